@@ -1,0 +1,178 @@
+"""Seeded synthetic inputs for the indexer -> exact top-k -> sparse-attention path.
+
+This module is shared by the CPU oracle's tests, the GPU parity tests and the
+benchmark.  It holds shapes and random draws only: none of the method's
+arithmetic lives here, so neither side can borrow the other's through it.
+
+Value distributions (the workloads described for the path):
+  * index queries / keys: int8, uniform over the integers -64..64 inclusive;
+  * indexer head weights w_h: int32, uniform over 1..16 inclusive;
+  * attention Q, K, V: fp32 draws from N(0, 1), cast to bf16 with
+    round-to-nearest-even.
+
+Each tensor has its own torch.Generator seeded with ``seed * 16 + id``
+(q_idx=1, k_idx=2, w=3, q=4, k=5, v=6), so a tensor does not depend on which
+others were drawn.  Draws are made on the device the caller names; CPU and GPU
+streams differ, so a test always hands the oracle a host copy of exactly the
+tensors the GPU consumed.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+IDS = {"q_idx": 1, "k_idx": 2, "w": 3, "q": 4, "k": 5, "v": 6}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shape of one workload of the path.
+
+    ``q_pos0`` is the absolute position of the first query of the chunk; query
+    i of every sequence sits at ``q_pos0 + i`` and sees keys 0..q_pos0+i.
+    ``L`` is the number of cached tokens (keys) per sequence.
+    """
+    name: str
+    B: int
+    n_q: int
+    L: int
+    q_pos0: int
+    H_I: int
+    d_I: int
+    k: int
+    H_q: int
+    d: int = 128
+    two_stage: bool = False
+    block_size: int = 128
+    n_keep: int = 64
+    seed: int = 0
+
+    @property
+    def decode(self) -> bool:
+        return self.n_q == 1 and self.B > 1
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(self.d) ** 0.5
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads of the path.  Names say what each one is.
+WORKLOADS = {
+    # tiny causal prefill: small enough for the oracle to check every row
+    "tiny_prefill_1k": Workload("tiny_prefill_1k", B=1, n_q=1024, L=1024, q_pos0=0,
+                                H_I=4, d_I=64, k=64, H_q=8),
+    # causal prefill of a 32K-token context
+    "prefill_32k": Workload("prefill_32k", B=1, n_q=32768, L=32768, q_pos0=0,
+                            H_I=64, d_I=128, k=2048, H_q=16),
+    # decode: 64 sequences, 131072 cached tokens + the new one each
+    "decode_128k": Workload("decode_128k", B=64, n_q=1, L=131073, q_pos0=131072,
+                            H_I=64, d_I=128, k=2048, H_q=16),
+    # last 16384-query chunk of a 262144-token context (one GPU's share)
+    "chunk_256k": Workload("chunk_256k", B=1, n_q=16384, L=262144, q_pos0=245760,
+                           H_I=64, d_I=128, k=2048, H_q=16),
+    # two-stage (block prefilter, then tokens) on the final 8192 queries of 128K
+    "two_stage_128k": Workload("two_stage_128k", B=1, n_q=8192, L=131072, q_pos0=122880,
+                               H_I=64, d_I=128, k=2048, H_q=16, two_stage=True,
+                               block_size=128, n_keep=64),
+}
+
+
+def _gen(seed: int, tid: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 16 + tid)
+    return g
+
+
+def _randint(shape, lo, hi_incl, dtype, seed, tid, device, chunk_rows=1 << 26):
+    """Uniform integers in [lo, hi_incl], drawn row-chunk by row-chunk."""
+    g = _gen(seed, tid, device)
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    n = flat.numel()
+    step = chunk_rows
+    for s in range(0, n, step):
+        e = min(n, s + step)
+        flat[s:e] = torch.randint(lo, hi_incl + 1, (e - s,), generator=g,
+                                  device=device, dtype=torch.int32).to(dtype)
+    return out
+
+
+def _randn_bf16(shape, seed, tid, device, chunk=1 << 26):
+    g = _gen(seed, tid, device)
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    flat = out.view(-1)
+    n = flat.numel()
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        flat[s:e] = torch.randn((e - s,), generator=g, device=device,
+                                dtype=torch.float32).to(torch.bfloat16)
+    return out
+
+
+def q_positions(wl: Workload, device="cpu") -> torch.Tensor:
+    """int32 [B, n_q]: absolute position of every query."""
+    pos = torch.arange(wl.n_q, dtype=torch.int32, device=device) + wl.q_pos0
+    return pos.unsqueeze(0).expand(wl.B, wl.n_q).contiguous()
+
+
+def make_inputs(wl: Workload, device="cpu", with_attn: bool = True,
+                seed: Optional[int] = None) -> dict:
+    """Draw every input of ``wl`` on ``device``.
+
+    Returns a dict of contiguous tensors:
+      q_idx int8 [B, n_q, H_I, d_I], k_idx int8 [B, L, d_I], w int32 [H_I],
+      q_pos int32 [B, n_q] and, if ``with_attn``, q bf16 [B, n_q, H_q, d],
+      k / v bf16 [B, L, d].
+    """
+    s = wl.seed if seed is None else seed
+    out = {
+        "q_idx": _randint((wl.B, wl.n_q, wl.H_I, wl.d_I), -64, 64, torch.int8, s, IDS["q_idx"], device),
+        "k_idx": _randint((wl.B, wl.L, wl.d_I), -64, 64, torch.int8, s, IDS["k_idx"], device),
+        "w": _randint((wl.H_I,), 1, 16, torch.int32, s, IDS["w"], device),
+        "q_pos": q_positions(wl, device),
+    }
+    if with_attn:
+        out["q"] = _randn_bf16((wl.B, wl.n_q, wl.H_q, wl.d), s, IDS["q"], device)
+        out["k"] = _randn_bf16((wl.B, wl.L, wl.d), s, IDS["k"], device)
+        out["v"] = _randn_bf16((wl.B, wl.L, wl.d), s, IDS["v"], device)
+    return out
+
+
+def checked_rows(wl: Workload, n_random: int = 56, seed: int = 0) -> list:
+    """Seeded subset of (b, i) query rows for the large workloads.
+
+    Always includes the first and last row of the chunk; for prefills starting
+    at position 0 also the rows at positions k-2, k-1, k (where the candidate
+    count crosses the budget); for two-stage workloads rows at the first and
+    last position of a key block.
+    """
+    rng = torch.Generator().manual_seed(seed * 16 + 15)
+    rows = set()
+    if wl.n_q == 1:
+        # decode: whole sequences; 0 and B-1 plus seeded others
+        picks = torch.randperm(wl.B, generator=rng)[: max(0, min(n_random, wl.B) - 2)].tolist()
+        for b in [0, wl.B - 1] + picks:
+            rows.add((b, 0))
+        return sorted(rows)
+    for i in [0, wl.n_q - 1]:
+        rows.add((0, i))
+    if wl.q_pos0 == 0:
+        for p in (wl.k - 2, wl.k - 1, wl.k):
+            if 0 <= p < wl.n_q:
+                rows.add((0, p))
+    if wl.two_stage:
+        bs = wl.block_size
+        for p in (wl.q_pos0 + 5 * bs, wl.q_pos0 + 5 * bs + bs - 1):
+            i = p - wl.q_pos0
+            if 0 <= i < wl.n_q:
+                rows.add((0, i))
+    b_idx = torch.randint(0, wl.B, (n_random,), generator=rng).tolist()
+    i_idx = torch.randint(0, wl.n_q, (n_random,), generator=rng).tolist()
+    for b, i in zip(b_idx, i_idx):
+        rows.add((b, i))
+    return sorted(rows)

@@ -1,0 +1,356 @@
+"""Pins of the CPU oracle: checks that do not re-derive the oracle's own code.
+
+Each ``check_*`` takes the implementation under test as an argument and returns
+``(ok, message)``.  ``test_oracle_pins.py`` runs them on the real oracle (all
+must pass) and on planted mistakes of it (each mutant must fail at least one),
+which shows that a plausible slip in the oracle -- a dropped term, a wrong sign
+or index, ReLU in the wrong place, the wrong tie-break -- would not go unseen.
+
+Kinds of pin used (nothing here calls the oracle to produce its own expected
+values):
+  * hand-worked examples (tests/golden/hand_worked.json);
+  * closed forms of special inputs (one head / one dim; constant vectors);
+  * invariances the definition implies (head / dim permutation, linearity in w);
+  * brute force by a different route (rank counting instead of sorting);
+  * library routines (torch scaled_dot_product_attention in fp64, scipy logsumexp);
+  * reductions of the two-stage indexer to the flat one.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_worked.json")
+
+
+def _load_golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _ok(cond, msg):
+    return (bool(cond), msg)
+
+
+def _all(results):
+    for ok, msg in results:
+        if not ok:
+            return False, msg
+    return True, "ok"
+
+
+# ----------------------------------------------------------------------------- scores
+def check_scores_hand(impl):
+    g = _load_golden()["indexer"]
+    q, w, K = np.array(g["q"]), np.array(g["w"]), np.array(g["k_idx"])
+    r = []
+    r.append(_ok(np.array_equal(impl.index_scores(q, K, w, 5), g["scores_p5"]), "hand scores p=5"))
+    r.append(_ok(np.array_equal(impl.index_scores(q, K, w, 3), g["scores_p3"]), "hand scores p=3"))
+    return _all(r)
+
+
+def check_scores_closed_forms(impl, seed=0):
+    rng = np.random.default_rng(seed)
+    r = []
+    # one head, one dim, unit weight: S_j = max(0, q * k_j)
+    for _ in range(5):
+        L = int(rng.integers(1, 40))
+        q = rng.integers(-64, 65, size=(1, 1))
+        K = rng.integers(-64, 65, size=(L, 1))
+        p = int(rng.integers(0, L))
+        want = [max(0, int(q[0, 0]) * int(K[j, 0])) for j in range(p + 1)]
+        r.append(_ok(np.array_equal(impl.index_scores(q, K, np.array([1]), p), want), "H=d=1 closed form"))
+    # q = +1 everywhere, k_j = c_j * ones: S_j = d * max(0, c_j) * sum(w)
+    for H, d in ((3, 5), (4, 64), (64, 128)):
+        w = rng.integers(1, 17, size=H)
+        c = rng.integers(-64, 65, size=50)
+        K = np.repeat(c[:, None], d, axis=1)
+        q = np.ones((H, d), dtype=np.int64)
+        want = [d * max(0, int(cj)) * int(w.sum()) for cj in c]
+        r.append(_ok(np.array_equal(impl.index_scores(q, K, w, 49), want), f"constant vectors H={H} d={d}"))
+    return _all(r)
+
+
+def check_scores_invariances(impl, seed=1):
+    rng = np.random.default_rng(seed)
+    H, d, L = 8, 16, 60
+    q = rng.integers(-64, 65, size=(H, d))
+    K = rng.integers(-64, 65, size=(L, d))
+    w = rng.integers(1, 17, size=H)
+    p = L - 1
+    s = impl.index_scores(q, K, w, p)
+    r = []
+    ph = rng.permutation(H)
+    r.append(_ok(np.array_equal(impl.index_scores(q[ph], K, w[ph], p), s), "head permutation"))
+    pd = rng.permutation(d)
+    r.append(_ok(np.array_equal(impl.index_scores(q[:, pd], K[:, pd], w, p), s), "dim permutation"))
+    r.append(_ok(np.array_equal(impl.index_scores(-q, -K, w, p), s), "joint negation"))
+    w2 = rng.integers(1, 17, size=H)
+    s2 = impl.index_scores(q, K, w2, p)
+    r.append(_ok(np.array_equal(impl.index_scores(q, K, w + w2, p), s + s2), "additive in w"))
+    r.append(_ok(np.array_equal(impl.index_scores(q, K, 3 * w, p), 3 * s), "homogeneous in w"))
+    # one head alone: S = w * max(0, dot) where dot = sum of elementwise products
+    for h in range(H):
+        e = np.zeros(H, dtype=np.int64)
+        e[h] = 1
+        dots = [sum(int(q[h, t]) * int(K[j, t]) for t in range(d)) for j in range(L)]
+        r.append(_ok(np.array_equal(impl.index_scores(q, K, e, p), [max(0, x) for x in dots]), f"single head {h}"))
+    # causality: p+1 keys, prefix-consistent, p clipped to the cache, p < 0 empty
+    r.append(_ok(len(impl.index_scores(q, K, w, 10)) == 11, "length p+1"))
+    r.append(_ok(np.array_equal(impl.index_scores(q, K, w, 10), s[:11]), "prefix consistency"))
+    r.append(_ok(len(impl.index_scores(q, K, w, L + 5)) == L, "p clipped to L-1"))
+    r.append(_ok(len(impl.index_scores(q, K, w, -1)) == 0, "p<0 empty"))
+    return _all(r)
+
+
+def check_scores_bound(impl, seed=2):
+    """Extreme inputs of the workloads' ranges stay below 2^31 (int32 scores are exact)."""
+    H, d = 64, 128
+    q = np.full((H, d), 64)
+    K = np.full((4, d), 64)
+    w = np.full(H, 16)
+    s = impl.index_scores(q, K, w, 3)
+    want = H * 16 * d * 64 * 64
+    return _all([_ok(np.all(s == want), "extreme score value"), _ok(want < 2 ** 31, "int32 bound")])
+
+
+# ----------------------------------------------------------------------------- top-k
+def _bruteforce_topk(scores, cand, k):
+    """Selected iff fewer than k candidates beat it (higher score, or equal score and lower index)."""
+    sel = []
+    n = len(cand)
+    for a in range(n):
+        beat = 0
+        for b in range(n):
+            if scores[b] > scores[a] or (scores[b] == scores[a] and cand[b] < cand[a]):
+                beat += 1
+        if beat < k:
+            sel.append(int(cand[a]))
+    sel.sort()
+    return sel + [-1] * (k - len(sel))
+
+
+def check_topk_hand(impl):
+    g = _load_golden()["indexer"]
+    s5 = np.array(g["scores_p5"])
+    r = []
+    for c in g["topk_cases"]:
+        s = s5[: c["p"] + 1]
+        J, cnt = impl.topk(s, np.arange(c["p"] + 1), c["k"])
+        r.append(_ok(list(J) == c["J"] and cnt == c["count"], f"hand top-k p={c['p']} k={c['k']}"))
+    return _all(r)
+
+
+def check_topk_bruteforce(impl, seed=3):
+    rng = np.random.default_rng(seed)
+    r = []
+    for trial in range(40):
+        n = int(rng.integers(1, 200))
+        hi = int(rng.choice([1, 2, 5, 1000, 2 ** 30]))
+        scores = rng.integers(-hi, hi + 1, size=n)
+        cand = np.sort(rng.choice(4 * n + 10, size=n, replace=False))
+        for k in sorted({1, 7, 64, n, max(1, n // 2)}):
+            J, cnt = impl.topk(scores, cand, k)
+            r.append(_ok(list(J) == _bruteforce_topk(scores, cand, k) and cnt == min(k, n),
+                         f"brute force n={n} k={k} trial={trial}"))
+    return _all(r)
+
+
+def check_topk_special(impl):
+    r = []
+    n = 100
+    ar = np.arange(n)
+    J, _ = impl.topk(np.zeros(n, dtype=np.int64), ar, 10)
+    r.append(_ok(list(J) == list(range(10)), "all equal -> lowest indices"))
+    J, _ = impl.topk(ar.copy(), ar, 10)
+    r.append(_ok(list(J) == list(range(n - 10, n)), "increasing -> last k"))
+    J, _ = impl.topk(-ar, ar, 10)
+    r.append(_ok(list(J) == list(range(10)), "decreasing -> first k"))
+    J, cnt = impl.topk(ar[:5], ar[:5], 8)
+    r.append(_ok(list(J) == [0, 1, 2, 3, 4, -1, -1, -1] and cnt == 5, "t < k pads with -1"))
+    J, cnt = impl.topk(np.zeros(0, dtype=np.int64), np.zeros(0, dtype=np.int64), 3)
+    r.append(_ok(list(J) == [-1, -1, -1] and cnt == 0, "empty row"))
+    s = np.array([1, 0, 1, 0, 1, -1, 0, 1])
+    J, _ = impl.topk(s, np.arange(8), 5)
+    r.append(_ok(list(J) == [0, 1, 2, 4, 7], "{-1,0,1} ties"))
+    return _all(r)
+
+
+# ----------------------------------------------------------------------------- blocks
+def check_blocks_hand(impl):
+    g = _load_golden()
+    gi, gt = g["indexer"], g["two_stage"]
+    q, w, K = np.array(gi["q"]), np.array(gi["w"]), np.array(gi["k_idx"])
+    bs = gt["block_size"]
+    r = [_ok(np.array_equal(impl.block_reps(K, bs), gt["reps"]), "hand reps")]
+    reps = impl.block_reps(K, bs)
+    r.append(_ok(np.array_equal(impl.block_scores(q, reps, w, 2), gt["block_scores_p5"]), "hand block scores"))
+    for c in gt["cases"]:
+        kept, _ = impl.block_keep(q, reps, w, c["p"], bs, c["n_keep"])
+        res = impl.forward_row(q, K, w, c["p"], c["k"], two_stage=True, block_size=bs, n_keep=c["n_keep"])
+        r.append(_ok(list(kept) == c["kept"], f"hand kept p={c['p']} n_keep={c['n_keep']}"))
+        r.append(_ok(list(res["J"]) == c["J"], f"hand two-stage J p={c['p']} k={c['k']}"))
+    return _all(r)
+
+
+def check_block_reps_sum(impl, seed=4):
+    rng = np.random.default_rng(seed)
+    K = rng.integers(-64, 65, size=(16 * 7 + 5, 6))
+    R = impl.block_reps(K, 16)
+    r = [_ok(R.shape == (7, 6), "complete blocks only")]
+    for m in range(7):
+        want = [sum(int(K[16 * m + t, c]) for t in range(16)) for c in range(6)]
+        r.append(_ok(list(R[m]) == want, f"block {m} sum"))
+    return _all(r)
+
+
+def check_block_keep_bruteforce(impl, seed=5):
+    """Kept set = own + blocks that fewer than n_keep-1 earlier blocks beat."""
+    rng = np.random.default_rng(seed)
+    r = []
+    for trial in range(12):
+        T, bs, n_keep, H, d = 512, 16, 4, 3, 8
+        K = rng.integers(-2, 3, size=(T, d))           # narrow range: many ties
+        q = rng.integers(-2, 3, size=(H, d))
+        w = rng.integers(1, 4, size=H)
+        R = impl.block_reps(K, bs)
+        for p in (0, 15, 16, 47, 63, 64, 200, 511):
+            own = p // bs
+            bsc = []
+            for m in range(own):
+                tot = 0
+                for h in range(H):
+                    dot = sum(int(q[h, t]) * int(R[m, t]) for t in range(d))
+                    tot += int(w[h]) * max(0, dot)
+                bsc.append(tot)
+            want = [own]
+            for m in range(own):
+                beat = sum(1 for m2 in range(own) if bsc[m2] > bsc[m] or (bsc[m2] == bsc[m] and m2 < m))
+                if beat < n_keep - 1:
+                    want.append(m)
+            kept, _ = impl.block_keep(q, R, w, p, bs, n_keep)
+            r.append(_ok(list(kept) == sorted(want), f"block keep brute force p={p} trial={trial}"))
+    return _all(r)
+
+
+def check_two_stage_reductions(impl, seed=6):
+    rng = np.random.default_rng(seed)
+    r = []
+    H, d, T = 4, 16, 300
+    K = rng.integers(-64, 65, size=(T, d))
+    w = rng.integers(1, 17, size=H)
+    for p in (0, 5, 63, 127, 255, 299):
+        q = rng.integers(-64, 65, size=(H, d))
+        flat = impl.forward_row(q, K, w, p, 24)["J"]
+        # 1) every causal block kept (own < n_keep): two-stage equals flat
+        two = impl.forward_row(q, K, w, p, 24, two_stage=True, block_size=16, n_keep=T // 16 + 1)["J"]
+        r.append(_ok(np.array_equal(flat, two), f"all blocks kept p={p}"))
+        # 2) block size 1 and n_keep >= k+1: two-stage equals flat
+        two1 = impl.forward_row(q, K, w, p, 24, two_stage=True, block_size=1, n_keep=25)["J"]
+        r.append(_ok(np.array_equal(flat, two1), f"block size 1 p={p}"))
+    return _all(r)
+
+
+def check_two_stage_invariants(impl, seed=7):
+    rng = np.random.default_rng(seed)
+    H, d, T, bs, n_keep = 4, 16, 2048, 16, 8
+    K = rng.integers(-64, 65, size=(T, d))
+    w = rng.integers(1, 17, size=H)
+    R = impl.block_reps(K, bs)
+    r = []
+    for p in (3, 16 * 5, 16 * 7 + 3, 16 * 8, 1000, 2047):
+        q = rng.integers(-64, 65, size=(H, d))
+        kept, _ = impl.block_keep(q, R, w, p, bs, n_keep)
+        own = p // bs
+        r.append(_ok(len(kept) == min(n_keep, own + 1), f"kept count p={p}"))
+        r.append(_ok(own in set(kept.tolist()), f"own kept p={p}"))
+        r.append(_ok(np.all(np.diff(kept) > 0), f"kept ascending p={p}"))
+    return _all(r)
+
+
+# ----------------------------------------------------------------------------- attention
+def check_attention_hand(impl):
+    g = _load_golden()["attention"]
+    r = []
+    for name in ("case_weighted", "case_zero_query"):
+        c = g[name]
+        q, k, v = np.array(c["q"]), np.array(c["k"]), np.array(c["v"])
+        out, lse = impl.sparse_attention(q, k, v, np.array(c["J"]), 1.0 / math.sqrt(2.0))
+        r.append(_ok(np.allclose(out, c["out"], atol=1e-12, rtol=0), f"hand attention {name} out"))
+        r.append(_ok(np.allclose(lse, c["lse"], atol=1e-12, rtol=0), f"hand attention {name} lse"))
+    return _all(r)
+
+
+def check_attention_dense(impl, seed=8):
+    """k >= t+1: sparse attention over all causal keys equals dense causal attention (torch SDPA, fp64)."""
+    import torch
+    import torch.nn.functional as F
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(seed)
+    T, H, d = 40, 4, 16
+    q = rng.standard_normal((T, H, d))
+    k = rng.standard_normal((T, d))
+    v = rng.standard_normal((T, d))
+    scale = 1.0 / math.sqrt(d)
+    tq = torch.from_numpy(q).permute(1, 0, 2).unsqueeze(0)         # [1, H, T, d]
+    tk = torch.from_numpy(k)[None, None].expand(1, H, T, d)
+    tv = torch.from_numpy(v)[None, None].expand(1, H, T, d)
+    dense = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale)[0].permute(1, 0, 2).numpy()
+    r = []
+    for t in range(T):
+        J = np.concatenate([np.arange(t + 1), -np.ones(T + 3 - (t + 1), dtype=np.int64)])
+        out, lse = impl.sparse_attention(q[t], k, v, J, scale)
+        r.append(_ok(np.max(np.abs(out - dense[t])) < 1e-12, f"dense equality t={t}"))
+        want_lse = logsumexp((q[t] @ k[: t + 1].T) * scale, axis=1)
+        r.append(_ok(np.max(np.abs(lse - want_lse)) < 1e-12, f"lse t={t}"))
+    return _all(r)
+
+
+def check_attention_special(impl, seed=9):
+    rng = np.random.default_rng(seed)
+    H, d, L = 4, 32, 50
+    q = rng.standard_normal((H, d))
+    k = rng.standard_normal((L, d))
+    v = rng.standard_normal((L, d))
+    scale = 1.0 / math.sqrt(d)
+    r = []
+    out, _ = impl.sparse_attention(q, k, v, np.array([7, -1, -1]), scale)
+    r.append(_ok(np.array_equal(out, np.repeat(v[7][None], H, 0)), "single key -> V[j]"))
+    J = np.array([1, 4, 9, 20, 33, -1])
+    out, _ = impl.sparse_attention(np.zeros((H, d)), k, v, J, scale)
+    r.append(_ok(np.allclose(out, np.repeat(v[[1, 4, 9, 20, 33]].mean(0)[None], H, 0), atol=1e-14), "zero query -> mean"))
+    out1, lse1 = impl.sparse_attention(q, k, v, J, scale)
+    out2, lse2 = impl.sparse_attention(q, k, v, J[[3, 0, 5, 2, 4, 1]], scale)
+    r.append(_ok(np.allclose(out1, out2, atol=1e-14) and np.allclose(lse1, lse2, atol=1e-14), "permutation invariance"))
+    qq = np.repeat(q[:1], H, 0)
+    out, _ = impl.sparse_attention(qq, k, v, J, scale)
+    r.append(_ok(all(np.array_equal(out[0], out[h]) for h in range(H)), "identical heads"))
+    # split-and-merge by log-sum-exp equals the whole (the decode split combine)
+    Ja, Jb = J[:2], J[2:5]
+    oa, la = impl.sparse_attention(q, k, v, Ja, scale)
+    ob, lb = impl.sparse_attention(q, k, v, Jb, scale)
+    m = np.maximum(la, lb)
+    wa, wb = np.exp(la - m), np.exp(lb - m)
+    merged = (oa * wa[:, None] + ob * wb[:, None]) / (wa + wb)[:, None]
+    r.append(_ok(np.allclose(merged, out1, atol=1e-13), "LSE split merge"))
+    r.append(_ok(np.allclose(m + np.log(wa + wb), lse1, atol=1e-13), "LSE merge of lse"))
+    out, lse = impl.sparse_attention(q, k, v, np.array([-1, -1]), scale)
+    r.append(_ok(np.all(out == 0) and np.all(np.isneginf(lse)), "empty list -> zeros, -inf"))
+    # a sharp query: attention goes to the argmax key
+    J2 = np.array([3, 8, 13])
+    qs = np.repeat((k[8] * 200.0)[None], H, 0)
+    out, _ = impl.sparse_attention(qs, k, v, J2, scale)
+    r.append(_ok(np.allclose(out, np.repeat(v[8][None], H, 0), atol=1e-9), "sharp query -> argmax key"))
+    return _all(r)
+
+
+ALL_CHECKS = [
+    check_scores_hand, check_scores_closed_forms, check_scores_invariances, check_scores_bound,
+    check_topk_hand, check_topk_bruteforce, check_topk_special,
+    check_blocks_hand, check_block_reps_sum, check_block_keep_bruteforce,
+    check_two_stage_reductions, check_two_stage_invariants,
+    check_attention_hand, check_attention_dense, check_attention_special,
+]

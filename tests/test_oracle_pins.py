@@ -1,0 +1,176 @@
+"""The CPU oracle against its pins (no GPU).  See oracle_pins.py for what each pin is."""
+from unittest import mock
+
+import numpy as np
+import pytest
+
+from oracle import lsa_oracle as O
+from tests import oracle_pins as P
+
+
+@pytest.mark.parametrize("check", P.ALL_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_passes_pin(check):
+    ok, msg = check(O)
+    assert ok, msg
+
+
+# ---------------------------------------------------------------- planted mistakes
+# Each mutant is a plausible slip in the oracle.  Patched into the oracle module
+# (so forward_row and friends use it too), it must fail at least one pin.
+
+def _relu_after_sum(q_row, k_idx, w, p):
+    n = min(int(p), k_idx.shape[0] - 1) + 1
+    if n <= 0:
+        return np.zeros((0,), np.int64)
+    dots = O._int_dots(q_row, k_idx[:n])
+    return np.maximum((np.asarray(w, np.int64)[:, None] * dots).sum(0), 0)
+
+
+def _no_relu(q_row, k_idx, w, p):
+    n = min(int(p), k_idx.shape[0] - 1) + 1
+    if n <= 0:
+        return np.zeros((0,), np.int64)
+    dots = O._int_dots(q_row, k_idx[:n])
+    return (np.asarray(w, np.int64)[:, None] * dots).sum(0)
+
+
+def _exclusive_causal(q_row, k_idx, w, p):
+    n = min(int(p), k_idx.shape[0])
+    if n <= 0:
+        return np.zeros((0,), np.int64)
+    return O._weighted_relu_sum(O._int_dots(q_row, k_idx[:n]), w)
+
+
+_orig_index_scores = O.index_scores
+_orig_topk = O.topk
+_orig_block_keep = O.block_keep
+_orig_attn = O.sparse_attention
+
+
+def _topk_high_index_ties(scores, cand, k):
+    scores = np.asarray(scores, np.int64)
+    cand = np.asarray(cand, np.int64)
+    n = min(k, cand.shape[0])
+    order = np.lexsort((-cand, -scores))
+    J = np.full((k,), -1, np.int64)
+    J[:n] = np.sort(cand[order[:n]])
+    return J, n
+
+
+def _topk_rank_order(scores, cand, k):
+    scores = np.asarray(scores, np.int64)
+    cand = np.asarray(cand, np.int64)
+    n = min(k, cand.shape[0])
+    order = np.lexsort((cand, -scores))
+    J = np.full((k,), -1, np.int64)
+    J[:n] = cand[order[:n]]
+    return J, n
+
+
+def _topk_smallest(scores, cand, k):
+    return _orig_topk(-np.asarray(scores, np.int64), cand, k)
+
+
+def _topk_off_by_one(scores, cand, k):
+    J, n = _orig_topk(scores, cand, max(k - 1, 0))
+    return np.concatenate([J, [-1]]), n
+
+
+def _reps_mean(k_idx, block_size):
+    k = np.asarray(k_idx, np.int64)
+    n_blk = k.shape[0] // block_size
+    return k[: n_blk * block_size].reshape(n_blk, block_size, k.shape[1]).sum(1) // block_size
+
+
+def _reps_shifted(k_idx, block_size):
+    k = np.asarray(k_idx, np.int64)[1:]
+    n_blk = k.shape[0] // block_size
+    return k[: n_blk * block_size].reshape(n_blk, block_size, k.shape[1]).sum(1)
+
+
+def _keep_without_forcing_own(q_row, reps, w, p, block_size, n_keep):
+    own = int(p) // block_size
+    bs = O.block_scores(q_row, reps, w, own)
+    m = np.arange(own)
+    order = np.lexsort((m, -bs))
+    best = m[order[: min(n_keep, own)]]
+    kept = np.sort(np.concatenate([best, [own]]))
+    return kept, bs
+
+
+def _keep_high_index_ties(q_row, reps, w, p, block_size, n_keep):
+    own = int(p) // block_size
+    bs = O.block_scores(q_row, reps, w, own)
+    m = np.arange(own)
+    order = np.lexsort((-m, -bs))
+    best = m[order[: min(n_keep - 1, own)]]
+    return np.sort(np.concatenate([best, [own]])), bs
+
+
+def _attn_wrong_scale(q_row, k_cache, v_cache, J, scale):
+    return _orig_attn(q_row, k_cache, v_cache, J, 1.0 / scale)
+
+
+def _attn_values_from_keys(q_row, k_cache, v_cache, J, scale):
+    return _orig_attn(q_row, k_cache, k_cache, J, scale)
+
+
+def _attn_padding_as_key(q_row, k_cache, v_cache, J, scale):
+    J = np.asarray(J, np.int64)
+    q = O._f64(q_row)
+    Kj, Vj = O._f64(k_cache[J]), O._f64(v_cache[J])
+    s = (q @ Kj.T) * scale
+    m = s.max(1, keepdims=True)
+    e = np.exp(s - m)
+    return (e @ Vj) / e.sum(1, keepdims=True), (m + np.log(e.sum(1, keepdims=True)))[:, 0]
+
+
+def _attn_lse_without_max(q_row, k_cache, v_cache, J, scale):
+    out, lse = _orig_attn(q_row, k_cache, v_cache, J, scale)
+    Jv = np.asarray(J)
+    Jv = Jv[Jv >= 0]
+    if Jv.size == 0:
+        return out, lse
+    m = ((O._f64(q_row) @ O._f64(k_cache[Jv]).T) * scale).max(1)
+    return out, lse - m
+
+
+def _cands_past_p(kept, p, block_size, L):
+    keys = (np.asarray(kept, np.int64)[:, None] * block_size + np.arange(block_size)[None, :]).reshape(-1)
+    return keys[keys < L]
+
+
+MUTANTS = {
+    "relu_after_sum": ("index_scores", _relu_after_sum),
+    "no_relu": ("index_scores", _no_relu),
+    "exclusive_causal": ("index_scores", _exclusive_causal),
+    "weights_dropped": ("index_scores", lambda q, k, w, p: _orig_index_scores(q, k, np.ones_like(np.asarray(w)), p)),
+    "topk_high_index_ties": ("topk", _topk_high_index_ties),
+    "topk_rank_order": ("topk", _topk_rank_order),
+    "topk_smallest": ("topk", _topk_smallest),
+    "topk_off_by_one": ("topk", _topk_off_by_one),
+    "reps_mean": ("block_reps", _reps_mean),
+    "reps_shifted": ("block_reps", _reps_shifted),
+    "keep_without_forcing_own": ("block_keep", _keep_without_forcing_own),
+    "keep_high_index_ties": ("block_keep", _keep_high_index_ties),
+    "attn_wrong_scale": ("sparse_attention", _attn_wrong_scale),
+    "attn_values_from_keys": ("sparse_attention", _attn_values_from_keys),
+    "attn_padding_as_key": ("sparse_attention", _attn_padding_as_key),
+    "attn_lse_without_max": ("sparse_attention", _attn_lse_without_max),
+    "cands_past_p": ("two_stage_candidates", _cands_past_p),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name):
+    attr, fn = MUTANTS[name]
+    failed = []
+    with mock.patch.object(O, attr, fn):
+        for check in P.ALL_CHECKS:
+            try:
+                ok, _ = check(O)
+            except Exception:       # a crash also counts as caught
+                ok = False
+            if not ok:
+                failed.append(check.__name__)
+    assert failed, f"mutant {name} passed every pin"
