@@ -1,0 +1,218 @@
+/*
+ * lsa.h -- C ABI of the learned top-k sparse attention hot path on MI355X (gfx950).
+ *
+ * The path (indexer -> exact top-k -> sparse attention):
+ *   1. a lightweight int8 indexer scores every causally preceding key of each query;
+ *   2. an exact per-query top-k keeps k keys (ties: lowest key index);
+ *   3. bf16 attention with an fp32 online softmax runs over only those keys;
+ *   optionally a two-stage indexer first keeps the best key blocks and scores
+ *   tokens only inside them.
+ *
+ * Sources (pages on learned sparse attention):
+ *   [LSA]  "Latent Sparse Attention (LSA)" (paperpeel.com/paper/2610.42147):
+ *          §2 "Sparse Attention" -- cost O(Tk) to prefill, O(k) per decoded token;
+ *          §2.1 "Design Choices", "Token Sparse Attention" -- an indexer with fewer
+ *          heads, smaller dimension and lower precision scores every preceding key;
+ *          §3.1 "Pooling" -- a pooled key is the sum of consecutive index keys;
+ *          §3.2 "Attention" -- one index list J_i serves every query head;
+ *          App. F.1 "Selection by threshold" -- packed (score, inverted id) keys:
+ *          better score first, lower id first at equal score; order of J_i is free;
+ *          App. F.1 "Attention kernels" -- J_i is a row of int32 cache slots padded
+ *          with -1, read by attention like a page table;
+ *          App. F.1 "CUDA graphs" -- decode steps are replayed from graphs, so a
+ *          step must not read anything back on the host.
+ *   [HISA] summary "HISA: Efficient Hierarchical Indexing for Fine-Grained Sparse
+ *          Attention" (theflow.svmpsp.dev related-papers page): block-level coarse
+ *          filter, then the token indexer only inside the kept blocks.
+ *   [HyTopK] HyScale summary on the same page: exact per-query top-k.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE memory owned by the caller (e.g. torch tensors' data_ptr),
+ *     contiguous row-major, at least 16-byte aligned.  The library never allocates,
+ *     frees or synchronises; scratch memory is the caller's workspace `ws` of
+ *     `ws_bytes`, sized by the matching *_workspace_size call.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream).  Outputs are valid once the caller synchronises;
+ *     inputs must not change before then.  No call reads anything back to the
+ *     host, so every call can be captured in a HIP graph.
+ *   - Errors: arguments are validated on the host first; on error the call returns
+ *     a negative status, launches nothing and leaves outputs untouched.  A failed
+ *     launch returns LSA_ERR_HIP.  Device-side faults surface at the caller's sync.
+ *   - q_pos[b*n_q + i] is the absolute position p of query i of sequence b; it
+ *     sees keys 0..p (its own key included).  Keys j >= L_max are never read:
+ *     p is clipped to L_max-1, and p < 0 gives a query with no candidates.
+ *   - Thread safety: reentrant, no global state.  Concurrent calls need distinct
+ *     workspaces.
+ *   - Exactness preconditions (device data cannot be checked on the host):
+ *     |w_h| < 2^23, and |sum_h w_h * max(0, q_h.k_j)| < 2^31 for token scores
+ *     (true for int8 in [-64, 64], 1 <= w <= 16, H_I <= 64, d_I <= 128); block
+ *     scores are int64 and need |sum| < 2^63.
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int lsa_status;
+enum {
+  LSA_OK = 0,
+  LSA_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent shapes */
+  LSA_ERR_UNSUPPORTED = -2, /* shape outside the compiled variants (see each call) */
+  LSA_ERR_WORKSPACE = -3,   /* ws too small (query *_workspace_size) or misaligned */
+  LSA_ERR_HIP = -4,         /* a kernel launch failed */
+  LSA_ERR_INTERNAL = -5
+};
+
+enum { LSA_MODE_PREFILL = 0, LSA_MODE_DECODE = 1 };
+
+/* Human-readable name of a status code (static storage). */
+const char* lsa_status_string(lsa_status s);
+/* Library version: major*10000 + minor*100 + patch. */
+int lsa_version(void);
+
+/*
+ * Token-indexer scores ([LSA] §2.1 "Token Sparse Attention"; the weighted-ReLU
+ * form used here is this library's reading of the indexer the pages leave open):
+ *     S[b,i,j] = sum_h w_h * max(0, sum_d q_idx[b,i,h,d] * k_idx[b,j,d])
+ * exact in int32, for every key j <= q_pos[b,i] (entries for later keys are
+ * left unspecified; they may or may not be written).
+ *   q_idx  int8  [B, n_q, H_I, d_I]     index queries (H_I heads each)
+ *   k_idx  int8  [B, L_max, d_I]        one index key per token, shared by heads
+ *   w      int32 [H_I] (w_per_query=0) or [B, n_q, H_I] (w_per_query=1)
+ *   q_pos  int32 [B, n_q]
+ *   kept_blocks int32 [B, n_q, n_keep] or NULL.
+ *     NULL: flat mode, scores[(b*n_q+i)*ld_scores + j] for keys j.
+ *     non-NULL: two-stage token stage ([HISA]); only keys of the listed blocks
+ *     (block m = keys m*block_size .. m*block_size+block_size-1; -1 = unused
+ *     entry) are scored, into compact slots:
+ *       scores[(b*n_q+i)*ld_scores + s], key(s) = kept[s / block_size]*block_size
+ *                                                + s % block_size,
+ *     for s < n_keep*block_size (ld_scores >= n_keep*block_size).  Slots whose
+ *     block is -1 or whose key is past q_pos are left unspecified.
+ * Supported: d_I in {64, 128}; 1 <= H_I <= 64; ld_scores >= L_max (flat).
+ * No workspace.
+ */
+lsa_status lsa_index_scores(const int8_t* q_idx, const int8_t* k_idx, const int32_t* w,
+                            int32_t w_per_query, const int32_t* q_pos,
+                            const int32_t* kept_blocks, int32_t block_size, int32_t n_keep,
+                            int32_t B, int32_t n_q, int32_t L_max, int32_t H_I, int32_t d_I,
+                            int32_t* scores, int64_t ld_scores, void* stream);
+
+/*
+ * Block representatives ([LSA] §3.1 "Pooling": a pooled key is the sum of its
+ * consecutive index keys; [HISA] scores such block summaries):
+ *     reps[b,m,:] = sum_{t < block_size} k_idx[b, m*block_size + t, :]   (int32)
+ * for m < n_blocks; requires n_blocks*block_size <= L_max (complete blocks only).
+ * Supported: d_I in {64, 128}; 1 <= block_size <= 128.  No workspace.
+ */
+lsa_status lsa_block_reps(const int8_t* k_idx, int32_t B, int32_t L_max, int32_t d_I,
+                          int32_t block_size, int32_t n_blocks, int32_t* reps, void* stream);
+
+/*
+ * Two-stage block prefilter ([HISA]; [LSA] §2.2 "Related Work": score blocks
+ * first, then only the keys inside the selected blocks).  For each query with
+ * own block o = floor(q_pos/block_size):
+ *     BS[m] = sum_h w_h * max(0, q_h . reps[m])   (int64), for blocks m < o,
+ *     kept  = {o} U the best min(n_keep-1, o) blocks by (BS desc, m asc),
+ * written ascending into kept_blocks[b,i,0..] and padded with -1 to n_keep.
+ *   reps          int32 [B, n_blocks, d_I] from lsa_block_reps (n_blocks must
+ *                 cover every own block: floor(max q_pos / block_size) <= n_blocks)
+ *   block_scores  optional int64 [B, n_q, n_blocks] output (entries m < o valid) or NULL
+ * Supported: d_I in {64,128}; 1 <= H_I <= 64; 1 <= block_size <= 128;
+ * 1 <= n_keep <= 256; n_blocks <= 65536.  Workspace: lsa_block_prefilter_workspace_size.
+ */
+lsa_status lsa_block_prefilter_workspace_size(int32_t B, int32_t n_q, int32_t n_blocks,
+                                              int32_t d_I, size_t* bytes);
+lsa_status lsa_block_prefilter(const int8_t* q_idx, const int32_t* reps, const int32_t* w,
+                               int32_t w_per_query, const int32_t* q_pos, int32_t B, int32_t n_q,
+                               int32_t n_blocks, int32_t H_I, int32_t d_I, int32_t block_size,
+                               int32_t n_keep, int32_t* kept_blocks, int64_t* block_scores,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Exact per-query top-k ([HyTopK]; tie rule of [LSA] App. F.1 "Selection by
+ * threshold"): idx[b,i,:] = the min(k, n_cand) candidates with the largest
+ * scores, equal scores ranked by lower key index first, written in ASCENDING
+ * key order and padded with -1 ([LSA] App. F.1 "Attention kernels").
+ * Candidates: flat mode (kept_blocks == NULL) keys 0..min(q_pos, L_max-1) with
+ * scores[(b*n_q+i)*ld_scores + j]; two-stage mode the compact slots written by
+ * lsa_index_scores with kept_blocks (keys <= q_pos and < L_max of listed blocks).
+ *   count  optional int32 [B, n_q] = number of indices written (or NULL).
+ * Supported: 1 <= k <= 4096.  Workspace: lsa_topk_workspace_size.
+ */
+lsa_status lsa_topk_workspace_size(int32_t B, int32_t n_q, int32_t L_max, int32_t k, size_t* bytes);
+lsa_status lsa_topk(const int32_t* scores, int64_t ld_scores, const int32_t* q_pos,
+                    const int32_t* kept_blocks, int32_t block_size, int32_t n_keep,
+                    int32_t B, int32_t n_q, int32_t L_max, int32_t k,
+                    int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Sparse attention over the index lists ([LSA] §3.2 "Attention": one list per
+ * query shared by all heads; §2: O(k) per query):
+ *     out[b,i,h,:] = sum_{j in J} softmax_j(scale * q[b,i,h,:].k[b,j,:]) v[b,j,:]
+ * with J = the entries of idx[b,i,:] in [0, L_max) (-1 and out-of-range entries
+ * are skipped; order does not matter).  bf16 MFMA products, fp32 online softmax,
+ * bf16 output (round to nearest even).  An empty list gives out = 0, lse = -inf.
+ *   q   bf16 [B, n_q, H_q, d];  k, v  bf16 [B, L_max, d] (one KV head)
+ *   idx int32 [B, n_q, k]
+ *   out bf16 [B, n_q, H_q, d];  lse optional fp32 [B, n_q, H_q] (natural log) or NULL
+ * n_split > 1 splits each list into n_split parts merged by log-sum-exp (the
+ * split-KV form used for decode); n_split = 0 picks automatically.
+ * Supported: d = 128; 1 <= H_q <= 16; 1 <= k <= 65536.
+ * Workspace: lsa_sparse_attn_workspace_size (0 when n_split resolves to 1).
+ */
+lsa_status lsa_sparse_attn_workspace_size(int32_t B, int32_t n_q, int32_t H_q, int32_t d, int32_t k,
+                                          int32_t n_split, size_t* bytes);
+lsa_status lsa_sparse_attn(const void* q, const void* k, const void* v, const int32_t* idx,
+                           int32_t B, int32_t n_q, int32_t L_max, int32_t H_q, int32_t d, int32_t k_top,
+                           float scale, int32_t n_split, void* out, float* lse,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole path in one call ([LSA] §2; [HISA] for two_stage):
+ *   PREFILL flat:      per chunk of query rows: index_scores -> topk -> sparse_attn
+ *   PREFILL two_stage: block_reps (once) -> block_prefilter -> index_scores (kept)
+ *                      -> topk (kept) -> sparse_attn
+ *   DECODE:            as PREFILL with one query per sequence (n_q = 1); the
+ *                      caller appends the new token's k/v/k_idx first and passes
+ *                      q_pos = its position.  Attention is split over keys.
+ * Score rows are materialised chunk by chunk in the workspace; chunk_rows = 0
+ * picks the largest chunk that fits ws_bytes.
+ */
+typedef struct lsa_forward_args {
+  int32_t mode;          /* LSA_MODE_PREFILL or LSA_MODE_DECODE */
+  int32_t two_stage;     /* 0 flat, 1 block prefilter then tokens */
+  const int8_t* q_idx;   /* int8 [B, n_q, H_I, d_I] */
+  const int8_t* k_idx;   /* int8 [B, L_max, d_I] */
+  const int32_t* w;      /* int32 [H_I] or [B, n_q, H_I] */
+  int32_t w_per_query;
+  const int32_t* q_pos;  /* int32 [B, n_q] */
+  const void* q;         /* bf16 [B, n_q, H_q, d] */
+  const void* k;         /* bf16 [B, L_max, d] */
+  const void* v;         /* bf16 [B, L_max, d] */
+  int32_t B, n_q, L_max, H_I, d_I, H_q, d, k_top;
+  int32_t block_size, n_keep; /* two-stage only */
+  float scale;           /* softmax scale, e.g. 1/sqrt(d) */
+  int32_t attn_split;    /* 0 = automatic */
+  int64_t chunk_rows;    /* query rows per score chunk; 0 = automatic */
+  int32_t* idx;          /* out int32 [B, n_q, k_top] */
+  int32_t* count;        /* out int32 [B, n_q] or NULL */
+  void* out;             /* out bf16 [B, n_q, H_q, d] */
+  float* lse;            /* out fp32 [B, n_q, H_q] or NULL */
+  int32_t* kept_blocks;  /* out int32 [B, n_q, n_keep] (two-stage) or NULL */
+} lsa_forward_args;
+
+/* Workspace for lsa_forward.  With a->chunk_rows = 0 it sizes score chunks of
+   at most ~1 GiB; lsa_forward then uses whatever chunk fits the ws it gets. */
+lsa_status lsa_forward_workspace_size(const lsa_forward_args* a, size_t* bytes);
+lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSA_H */

@@ -1,0 +1,301 @@
+"""ctypes binding of liblsa.so with the C ABI's names (see include/lsa.h).
+
+Argument marshalling only: dtype / device / contiguity checks, output and
+workspace allocation through torch, raw device pointers, the current stream.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+# every symbol include/lsa.h declares
+EXPORTED = [
+    "lsa_status_string", "lsa_version", "lsa_index_scores", "lsa_block_reps",
+    "lsa_block_prefilter_workspace_size", "lsa_block_prefilter", "lsa_topk_workspace_size",
+    "lsa_topk", "lsa_sparse_attn_workspace_size", "lsa_sparse_attn",
+    "lsa_forward_workspace_size", "lsa_forward",
+]
+
+P = C.c_void_p
+I32 = C.c_int32
+I64 = C.c_int64
+SZ = C.c_size_t
+
+
+class LsaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({lsa_status_string(status)})")
+        self.status = status
+
+
+class ForwardArgs(C.Structure):
+    _fields_ = [
+        ("mode", I32), ("two_stage", I32),
+        ("q_idx", P), ("k_idx", P), ("w", P), ("w_per_query", I32),
+        ("q_pos", P), ("q", P), ("k", P), ("v", P),
+        ("B", I32), ("n_q", I32), ("L_max", I32), ("H_I", I32), ("d_I", I32), ("H_q", I32),
+        ("d", I32), ("k_top", I32), ("block_size", I32), ("n_keep", I32),
+        ("scale", C.c_float), ("attn_split", I32), ("chunk_rows", I64),
+        ("idx", P), ("count", P), ("out", P), ("lse", P), ("kept_blocks", P),
+    ]
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "liblsa.so")
+
+
+def lib():
+    """The loaded liblsa.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                               "(hipcc --offload-arch=gfx950); there is no fallback path")
+        L = C.CDLL(path)
+        L.lsa_status_string.restype = C.c_char_p
+        L.lsa_status_string.argtypes = [C.c_int]
+        L.lsa_version.restype = C.c_int
+        L.lsa_version.argtypes = []
+        L.lsa_index_scores.argtypes = [P, P, P, I32, P, P, I32, I32, I32, I32, I32, I32, I32, P, I64, P]
+        L.lsa_block_reps.argtypes = [P, I32, I32, I32, I32, I32, P, P]
+        L.lsa_block_prefilter_workspace_size.argtypes = [I32, I32, I32, I32, C.POINTER(SZ)]
+        L.lsa_block_prefilter.argtypes = [P, P, P, I32, P, I32, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
+        L.lsa_topk_workspace_size.argtypes = [I32, I32, I32, I32, C.POINTER(SZ)]
+        L.lsa_topk.argtypes = [P, I64, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
+        L.lsa_sparse_attn_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, C.POINTER(SZ)]
+        L.lsa_sparse_attn.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, C.c_float, I32, P, P, P, SZ, P]
+        L.lsa_forward_workspace_size.argtypes = [C.POINTER(ForwardArgs), C.POINTER(SZ)]
+        L.lsa_forward.argtypes = [C.POINTER(ForwardArgs), P, SZ, P]
+        for name in EXPORTED:
+            if name not in ("lsa_status_string", "lsa_version"):
+                getattr(L, name).restype = C.c_int
+        _LIB = L
+    return _LIB
+
+
+def lsa_status_string(status: int) -> str:
+    return lib().lsa_status_string(int(status)).decode()
+
+
+def lsa_version() -> int:
+    return int(lib().lsa_version())
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise LsaError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> C.c_void_p:
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty((nbytes,), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------------- calls
+def lsa_index_scores(q_idx, k_idx, w, q_pos, scores=None, ld: Optional[int] = None,
+                     kept_blocks=None, block_size: int = 0, n_keep: int = 0):
+    """Indexer scores.  Flat: int32 [B, n_q, ld >= L]; two-stage (kept_blocks):
+    compact slots [B, n_q, ld >= n_keep*block_size].  Returns the score tensor."""
+    dev = q_idx.device
+    _need(q_idx, "q_idx", torch.int8)
+    _need(k_idx, "k_idx", torch.int8, dev)
+    _need(w, "w", torch.int32, dev)
+    _need(q_pos, "q_pos", torch.int32, dev)
+    B, n_q, H_I, d_I = q_idx.shape
+    L = k_idx.shape[1]
+    if k_idx.shape != (B, L, d_I):
+        raise ValueError("k_idx must be [B, L, d_I]")
+    w_pq = 1 if w.dim() == 3 else 0
+    if (w_pq and tuple(w.shape) != (B, n_q, H_I)) or (not w_pq and tuple(w.shape) != (H_I,)):
+        raise ValueError("w must be [H_I] or [B, n_q, H_I]")
+    if kept_blocks is not None:
+        _need(kept_blocks, "kept_blocks", torch.int32, dev)
+        n_keep = kept_blocks.shape[-1]
+        width = n_keep * block_size
+    else:
+        width = L
+    if ld is None:
+        ld = width
+    if scores is None:
+        scores = torch.empty((B, n_q, ld), dtype=torch.int32, device=dev)
+    _need(scores, "scores", torch.int32, dev)
+    st = lib().lsa_index_scores(_ptr(q_idx), _ptr(k_idx), _ptr(w), w_pq, _ptr(q_pos), _ptr(kept_blocks),
+                                block_size, n_keep, B, n_q, L, H_I, d_I, _ptr(scores), ld, _stream(dev))
+    _check("lsa_index_scores", st)
+    return scores
+
+
+def lsa_block_reps(k_idx, block_size: int, n_blocks: Optional[int] = None):
+    dev = k_idx.device
+    _need(k_idx, "k_idx", torch.int8)
+    B, L, d_I = k_idx.shape
+    if n_blocks is None:
+        n_blocks = L // block_size
+    reps = torch.empty((B, n_blocks, d_I), dtype=torch.int32, device=dev)
+    st = lib().lsa_block_reps(_ptr(k_idx), B, L, d_I, block_size, n_blocks, _ptr(reps), _stream(dev))
+    _check("lsa_block_reps", st)
+    return reps
+
+
+def lsa_block_prefilter(q_idx, reps, w, q_pos, block_size: int, n_keep: int, return_scores: bool = False):
+    """Kept blocks int32 [B, n_q, n_keep] (ascending, -1 padded); optionally block scores int64."""
+    dev = q_idx.device
+    _need(q_idx, "q_idx", torch.int8)
+    _need(reps, "reps", torch.int32, dev)
+    _need(w, "w", torch.int32, dev)
+    _need(q_pos, "q_pos", torch.int32, dev)
+    B, n_q, H_I, d_I = q_idx.shape
+    n_blocks = reps.shape[1]
+    w_pq = 1 if w.dim() == 3 else 0
+    kept = torch.empty((B, n_q, n_keep), dtype=torch.int32, device=dev)
+    bs = torch.empty((B, n_q, n_blocks), dtype=torch.int64, device=dev) if return_scores else None
+    nb = SZ(0)
+    _check("lsa_block_prefilter_workspace_size",
+           lib().lsa_block_prefilter_workspace_size(B, n_q, n_blocks, d_I, C.byref(nb)))
+    ws = _workspace(nb.value, dev)
+    st = lib().lsa_block_prefilter(_ptr(q_idx), _ptr(reps), _ptr(w), w_pq, _ptr(q_pos), B, n_q, n_blocks, H_I,
+                                   d_I, block_size, n_keep, _ptr(kept), _ptr(bs), _ptr(ws), nb.value,
+                                   _stream(dev))
+    _check("lsa_block_prefilter", st)
+    return (kept, bs) if return_scores else kept
+
+
+def lsa_topk(scores, q_pos, k: int, L_max: int, kept_blocks=None, block_size: int = 0):
+    """Exact top-k: (idx int32 [B, n_q, k] ascending and -1 padded, count int32 [B, n_q])."""
+    dev = scores.device
+    _need(scores, "scores", torch.int32)
+    _need(q_pos, "q_pos", torch.int32, dev)
+    B, n_q, ld = scores.shape
+    n_keep = 0
+    if kept_blocks is not None:
+        _need(kept_blocks, "kept_blocks", torch.int32, dev)
+        n_keep = kept_blocks.shape[-1]
+    idx = torch.empty((B, n_q, k), dtype=torch.int32, device=dev)
+    count = torch.empty((B, n_q), dtype=torch.int32, device=dev)
+    nb = SZ(0)
+    _check("lsa_topk_workspace_size", lib().lsa_topk_workspace_size(B, n_q, L_max, k, C.byref(nb)))
+    ws = _workspace(nb.value, dev)
+    st = lib().lsa_topk(_ptr(scores), ld, _ptr(q_pos), _ptr(kept_blocks), block_size, n_keep, B, n_q, L_max, k,
+                        _ptr(idx), _ptr(count), _ptr(ws), nb.value, _stream(dev))
+    _check("lsa_topk", st)
+    return idx, count
+
+
+def lsa_sparse_attn(q, k, v, idx, scale: Optional[float] = None, n_split: int = 0, return_lse: bool = True):
+    """Sparse attention: (out bf16 [B, n_q, H_q, d], lse fp32 [B, n_q, H_q] or None)."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, dev)
+    _need(v, "v", torch.bfloat16, dev)
+    _need(idx, "idx", torch.int32, dev)
+    B, n_q, H_q, d = q.shape
+    L = k.shape[1]
+    k_top = idx.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, n_q, H_q), dtype=torch.float32, device=dev) if return_lse else None
+    nb = SZ(0)
+    _check("lsa_sparse_attn_workspace_size",
+           lib().lsa_sparse_attn_workspace_size(B, n_q, H_q, d, k_top, n_split, C.byref(nb)))
+    ws = _workspace(nb.value, dev)
+    st = lib().lsa_sparse_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), B, n_q, L, H_q, d, k_top, float(scale),
+                               n_split, _ptr(out), _ptr(lse), _ptr(ws), nb.value, _stream(dev))
+    _check("lsa_sparse_attn", st)
+    return out, lse
+
+
+def _forward_args(inp: dict, k_top: int, two_stage: bool, block_size: int, n_keep: int, scale, attn_split: int,
+                  chunk_rows: int, out: dict):
+    q_idx, k_idx, w, q_pos, q, k, v = (inp[n] for n in ("q_idx", "k_idx", "w", "q_pos", "q", "k", "v"))
+    B, n_q, H_I, d_I = q_idx.shape
+    _, _, H_q, d = q.shape
+    L = k_idx.shape[1]
+    a = ForwardArgs()
+    a.mode = 1 if (n_q == 1 and B > 1) else 0
+    a.two_stage = 1 if two_stage else 0
+    a.q_idx, a.k_idx, a.w = q_idx.data_ptr(), k_idx.data_ptr(), w.data_ptr()
+    a.w_per_query = 1 if w.dim() == 3 else 0
+    a.q_pos, a.q, a.k, a.v = q_pos.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.B, a.n_q, a.L_max, a.H_I, a.d_I, a.H_q, a.d, a.k_top = B, n_q, L, H_I, d_I, H_q, d, k_top
+    a.block_size, a.n_keep = block_size, n_keep
+    a.scale = float(1.0 / math.sqrt(d) if scale is None else scale)
+    a.attn_split = attn_split
+    a.chunk_rows = chunk_rows
+    a.idx = out["idx"].data_ptr()
+    a.count = out["count"].data_ptr() if out.get("count") is not None else None
+    a.out = out["out"].data_ptr()
+    a.lse = out["lse"].data_ptr() if out.get("lse") is not None else None
+    a.kept_blocks = out["kept"].data_ptr() if out.get("kept") is not None else None
+    return a
+
+
+def lsa_forward_workspace_size(inp: dict, k_top: int, two_stage: bool = False, block_size: int = 128,
+                               n_keep: int = 64, attn_split: int = 0, chunk_rows: int = 0) -> int:
+    dummy = {"idx": inp["q_pos"], "out": inp["q"]}
+    a = _forward_args(inp, k_top, two_stage, block_size, n_keep, None, attn_split, chunk_rows, dummy)
+    nb = SZ(0)
+    _check("lsa_forward_workspace_size", lib().lsa_forward_workspace_size(C.byref(a), C.byref(nb)))
+    return nb.value
+
+
+def lsa_forward(inp: dict, k_top: int, two_stage: bool = False, block_size: int = 128, n_keep: int = 64,
+                scale: Optional[float] = None, attn_split: int = 0, chunk_rows: int = 0,
+                out: Optional[dict] = None, ws: Optional[torch.Tensor] = None) -> dict:
+    """The whole path.  ``inp`` holds q_idx, k_idx, w, q_pos, q, k, v (device tensors).
+    Returns dict(idx, count, out, lse[, kept]); pass ``out`` / ``ws`` to reuse buffers."""
+    q_idx, q = inp["q_idx"], inp["q"]
+    dev = q_idx.device
+    for name, dt in (("q_idx", torch.int8), ("k_idx", torch.int8), ("w", torch.int32), ("q_pos", torch.int32),
+                     ("q", torch.bfloat16), ("k", torch.bfloat16), ("v", torch.bfloat16)):
+        _need(inp[name], name, dt, dev)
+    B, n_q = q_idx.shape[:2]
+    H_q = q.shape[2]
+    if out is None:
+        out = {
+            "idx": torch.empty((B, n_q, k_top), dtype=torch.int32, device=dev),
+            "count": torch.empty((B, n_q), dtype=torch.int32, device=dev),
+            "out": torch.empty_like(q),
+            "lse": torch.empty((B, n_q, H_q), dtype=torch.float32, device=dev),
+        }
+        if two_stage:
+            out["kept"] = torch.empty((B, n_q, n_keep), dtype=torch.int32, device=dev)
+    a = _forward_args(inp, k_top, two_stage, block_size, n_keep, scale, attn_split, chunk_rows, out)
+    if ws is None:
+        nb = SZ(0)
+        _check("lsa_forward_workspace_size", lib().lsa_forward_workspace_size(C.byref(a), C.byref(nb)))
+        ws = _workspace(nb.value, dev)
+    nbytes = 0 if ws is None else ws.numel()
+    st = lib().lsa_forward(C.byref(a), _ptr(ws), nbytes, _stream(dev))
+    _check("lsa_forward", st)
+    return out

@@ -1,0 +1,493 @@
+// lsa_api.cpp -- the C ABI of include/lsa.h: host-side validation, workspace
+// sizing and kernel orchestration.  Nothing here allocates, frees or waits.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstdint>
+
+#include "lsa.h"
+#include "lsa_internal.h"
+
+#define LSA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline lsa_status hip_status(hipError_t e) { return e == hipSuccess ? LSA_OK : LSA_ERR_HIP; }
+
+// default score-row leading dimension used by lsa_forward
+inline int64_t score_ld(int32_t L) { return ((int64_t)L + 63) / 64 * 64; }
+
+// keys per workgroup span of the flat indexer
+inline int flat_span(int32_t L_max, bool direct) {
+  if (direct) return 2048;
+  return L_max > 65536 ? 8192 : 4096;
+}
+
+// automatic split count of the sparse attention
+inline int attn_split_auto(long long rows, int32_t k_top) {
+  const int n_tiles = (k_top + 31) / 32;
+  if (rows >= 2048) return 1;
+  long long s = (2048 + rows - 1) / rows;
+  return (int)std::max<long long>(1, std::min<long long>(s, n_tiles));
+}
+
+lsa_status check_index_args(const int8_t* q_idx, const int8_t* k_idx, const int32_t* w, const int32_t* q_pos,
+                            const int32_t* kept, int32_t block_size, int32_t n_keep, int32_t B, int32_t n_q,
+                            int32_t L_max, int32_t H_I, int32_t d_I, const int32_t* scores, int64_t ld) {
+  if (B < 0 || n_q < 0 || L_max < 0 || H_I < 0) return LSA_ERR_INVALID_ARG;
+  if ((long long)B * n_q == 0) return LSA_OK;
+  if (!q_idx || !k_idx || !w || !q_pos || !scores) return LSA_ERR_INVALID_ARG;
+  if (L_max < 1) return LSA_ERR_INVALID_ARG;
+  if (d_I != 64 && d_I != 128) return LSA_ERR_UNSUPPORTED;
+  if (H_I < 1 || H_I > 64) return LSA_ERR_UNSUPPORTED;
+  if (kept) {
+    if (block_size < 1 || n_keep < 1) return LSA_ERR_INVALID_ARG;
+    if (n_keep > 256 || block_size > 65536) return LSA_ERR_UNSUPPORTED;
+    if (ld < (int64_t)n_keep * block_size) return LSA_ERR_INVALID_ARG;
+  } else {
+    if (ld < L_max) return LSA_ERR_INVALID_ARG;
+  }
+  return LSA_OK;
+}
+
+}  // namespace
+
+LSA_API const char* lsa_status_string(lsa_status s) {
+  switch (s) {
+    case LSA_OK: return "LSA_OK";
+    case LSA_ERR_INVALID_ARG: return "LSA_ERR_INVALID_ARG: invalid argument";
+    case LSA_ERR_UNSUPPORTED: return "LSA_ERR_UNSUPPORTED: shape outside the compiled variants";
+    case LSA_ERR_WORKSPACE: return "LSA_ERR_WORKSPACE: workspace too small or misaligned";
+    case LSA_ERR_HIP: return "LSA_ERR_HIP: kernel launch failed";
+    case LSA_ERR_INTERNAL: return "LSA_ERR_INTERNAL";
+    default: return "unknown lsa_status";
+  }
+}
+
+LSA_API int lsa_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+LSA_API lsa_status lsa_index_scores(const int8_t* q_idx, const int8_t* k_idx, const int32_t* w,
+                                    int32_t w_per_query, const int32_t* q_pos, const int32_t* kept_blocks,
+                                    int32_t block_size, int32_t n_keep, int32_t B, int32_t n_q, int32_t L_max,
+                                    int32_t H_I, int32_t d_I, int32_t* scores, int64_t ld_scores,
+                                    void* stream) {
+  lsa_status st = check_index_args(q_idx, k_idx, w, q_pos, kept_blocks, block_size, n_keep, B, n_q, L_max,
+                                   H_I, d_I, scores, ld_scores);
+  if (st != LSA_OK || (long long)B * n_q == 0) return st;
+  lsa::IdxArgs a{};
+  a.q_idx = q_idx;
+  a.k_idx = k_idx;
+  a.w = w;
+  a.w_per_query = w_per_query ? 1 : 0;
+  a.q_pos = q_pos;
+  a.kept = kept_blocks;
+  a.block_size = block_size;
+  a.n_keep = n_keep;
+  a.B = B;
+  a.n_q = n_q;
+  a.L_max = L_max;
+  a.H_I = H_I;
+  a.d_I = d_I;
+  a.scores = scores;
+  a.ld = ld_scores;
+  a.use_direct = n_q < 8;
+  a.span = flat_span(L_max, a.use_direct);
+  return hip_status(lsa::launch_index_scores(a, as_stream(stream)));
+}
+
+LSA_API lsa_status lsa_block_reps(const int8_t* k_idx, int32_t B, int32_t L_max, int32_t d_I, int32_t block_size,
+                                  int32_t n_blocks, int32_t* reps, void* stream) {
+  if (B < 0 || L_max < 0 || n_blocks < 0 || block_size < 1) return LSA_ERR_INVALID_ARG;
+  if (d_I != 64 && d_I != 128) return LSA_ERR_UNSUPPORTED;
+  if (block_size > 128) return LSA_ERR_UNSUPPORTED;
+  if ((long long)n_blocks * block_size > L_max) return LSA_ERR_INVALID_ARG;
+  if ((long long)B * n_blocks == 0) return LSA_OK;
+  if (!k_idx || !reps) return LSA_ERR_INVALID_ARG;
+  return hip_status(lsa::launch_block_reps(k_idx, B, L_max, d_I, block_size, n_blocks, reps, as_stream(stream)));
+}
+
+static size_t prefilter_ws_bytes(int32_t B, int32_t n_q, int32_t n_blocks, int32_t d_I) {
+  return align_up((size_t)B * n_blocks * 2 * d_I) + align_up((size_t)B * n_q * n_blocks * 8);
+}
+
+LSA_API lsa_status lsa_block_prefilter_workspace_size(int32_t B, int32_t n_q, int32_t n_blocks, int32_t d_I,
+                                                      size_t* bytes) {
+  if (!bytes || B < 0 || n_q < 0 || n_blocks < 0) return LSA_ERR_INVALID_ARG;
+  *bytes = prefilter_ws_bytes(B, n_q, n_blocks, d_I);
+  return LSA_OK;
+}
+
+// block scores + keep for rows whose limbs are already in `limbs`
+static lsa_status run_prefilter(const int8_t* q_idx, const int8_t* limbs, const int32_t* w, int32_t w_per_query,
+                                const int32_t* q_pos, int32_t B, int32_t n_q, int32_t n_blocks, int32_t H_I,
+                                int32_t d_I, int32_t block_size, int32_t n_keep, int32_t* kept,
+                                long long* bscores, hipStream_t s) {
+  lsa::BlkArgs ba{};
+  ba.q_idx = q_idx;
+  ba.limbs = limbs;
+  ba.w = w;
+  ba.w_per_query = w_per_query ? 1 : 0;
+  ba.q_pos = q_pos;
+  ba.B = B;
+  ba.n_q = n_q;
+  ba.n_blocks = n_blocks;
+  ba.L_max = INT_MAX;
+  ba.H_I = H_I;
+  ba.d_I = d_I;
+  ba.block_size = block_size;
+  ba.bscores = bscores;
+  ba.ld = n_blocks;
+  ba.span = 512;
+  hipError_t e = lsa::launch_block_scores(ba, s);
+  if (e != hipSuccess) return LSA_ERR_HIP;
+  lsa::BlkSelArgs sa{};
+  sa.bscores = bscores;
+  sa.ld = n_blocks;
+  sa.q_pos = q_pos;
+  sa.B = B;
+  sa.n_q = n_q;
+  sa.n_blocks = n_blocks;
+  sa.block_size = block_size;
+  sa.n_keep = n_keep;
+  sa.kept = kept;
+  return hip_status(lsa::launch_block_select(sa, s));
+}
+
+LSA_API lsa_status lsa_block_prefilter(const int8_t* q_idx, const int32_t* reps, const int32_t* w,
+                                       int32_t w_per_query, const int32_t* q_pos, int32_t B, int32_t n_q,
+                                       int32_t n_blocks, int32_t H_I, int32_t d_I, int32_t block_size,
+                                       int32_t n_keep, int32_t* kept_blocks, int64_t* block_scores, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  if (B < 0 || n_q < 0 || n_blocks < 0 || block_size < 1 || n_keep < 1) return LSA_ERR_INVALID_ARG;
+  if (d_I != 64 && d_I != 128) return LSA_ERR_UNSUPPORTED;
+  if (H_I < 1 || H_I > 64 || block_size > 128 || n_keep > 256 || n_blocks > 65536) return LSA_ERR_UNSUPPORTED;
+  if ((long long)B * n_q == 0) return LSA_OK;
+  if (!q_idx || !w || !q_pos || !kept_blocks || (n_blocks > 0 && !reps)) return LSA_ERR_INVALID_ARG;
+  if (ws_bytes < prefilter_ws_bytes(B, n_q, n_blocks, d_I) || (ws_bytes > 0 && !ws)) return LSA_ERR_WORKSPACE;
+  if (((uintptr_t)ws) % 16 != 0) return LSA_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  int8_t* limbs = static_cast<int8_t*>(ws);
+  long long* bs = block_scores ? reinterpret_cast<long long*>(block_scores)
+                               : reinterpret_cast<long long*>(static_cast<char*>(ws) +
+                                                              align_up((size_t)B * n_blocks * 2 * d_I));
+  if (n_blocks > 0) {
+    hipError_t e = lsa::launch_block_limbs(reps, B, n_blocks, d_I, limbs, s);
+    if (e != hipSuccess) return LSA_ERR_HIP;
+  }
+  return run_prefilter(q_idx, limbs, w, w_per_query, q_pos, B, n_q, n_blocks, H_I, d_I, block_size, n_keep,
+                       kept_blocks, bs, s);
+}
+
+LSA_API lsa_status lsa_topk_workspace_size(int32_t B, int32_t n_q, int32_t L_max, int32_t k, size_t* bytes) {
+  if (!bytes || B < 0 || n_q < 0 || L_max < 0 || k < 0) return LSA_ERR_INVALID_ARG;
+  *bytes = 0;
+  return LSA_OK;
+}
+
+LSA_API lsa_status lsa_topk(const int32_t* scores, int64_t ld_scores, const int32_t* q_pos,
+                            const int32_t* kept_blocks, int32_t block_size, int32_t n_keep, int32_t B, int32_t n_q,
+                            int32_t L_max, int32_t k, int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
+                            void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (B < 0 || n_q < 0 || L_max < 0) return LSA_ERR_INVALID_ARG;
+  if (k < 1) return LSA_ERR_INVALID_ARG;
+  if (k > 4096) return LSA_ERR_UNSUPPORTED;
+  if ((long long)B * n_q == 0) return LSA_OK;
+  if (!scores || !q_pos || !idx || L_max < 1) return LSA_ERR_INVALID_ARG;
+  if (kept_blocks) {
+    if (block_size < 1 || n_keep < 1) return LSA_ERR_INVALID_ARG;
+    if (n_keep > 256) return LSA_ERR_UNSUPPORTED;
+    if (ld_scores < (int64_t)n_keep * block_size) return LSA_ERR_INVALID_ARG;
+  } else if (ld_scores < L_max) {
+    return LSA_ERR_INVALID_ARG;
+  }
+  lsa::TopkArgs a{};
+  a.scores = scores;
+  a.ld = ld_scores;
+  a.q_pos = q_pos;
+  a.kept = kept_blocks;
+  a.block_size = block_size;
+  a.n_keep = n_keep;
+  a.B = B;
+  a.n_q = n_q;
+  a.L_max = L_max;
+  a.k = k;
+  a.idx = idx;
+  a.count = count;
+  return hip_status(lsa::launch_topk(a, as_stream(stream)));
+}
+
+static int resolve_split(int32_t B, int32_t n_q, int32_t k_top, int32_t n_split) {
+  const long long rows = (long long)B * n_q;
+  const int n_tiles = (k_top + 31) / 32;
+  if (n_split <= 0) return attn_split_auto(rows, k_top);
+  return std::max(1, std::min(n_split, n_tiles));
+}
+
+static size_t attn_ws_bytes(long long rows, int32_t H_q, int32_t d, int split) {
+  if (split <= 1) return 0;
+  const long long units = rows * split;
+  return align_up((size_t)units * H_q * d * 4) + align_up((size_t)units * H_q * 4);
+}
+
+LSA_API lsa_status lsa_sparse_attn_workspace_size(int32_t B, int32_t n_q, int32_t H_q, int32_t d, int32_t k,
+                                                  int32_t n_split, size_t* bytes) {
+  if (!bytes || B < 0 || n_q < 0 || H_q < 0 || d < 0 || k < 1) return LSA_ERR_INVALID_ARG;
+  const int split = resolve_split(B, n_q, k, n_split);
+  *bytes = attn_ws_bytes((long long)B * n_q, H_q, d, split);
+  return LSA_OK;
+}
+
+static lsa_status run_attn(const void* q, const void* k, const void* v, const int32_t* idx, int32_t B, int32_t n_q,
+                           int32_t L_max, int32_t H_q, int32_t d, int32_t k_top, float scale, int split, void* out,
+                           float* lse, void* ws, hipStream_t s) {
+  lsa::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.B = B;
+  a.n_q = n_q;
+  a.L_max = L_max;
+  a.H_q = H_q;
+  a.d = d;
+  a.k_top = k_top;
+  a.scale = scale;
+  a.n_split = split;
+  a.out = out;
+  a.lse = lse;
+  a.ws = static_cast<float*>(ws);
+  return hip_status(lsa::launch_sparse_attn(a, s));
+}
+
+LSA_API lsa_status lsa_sparse_attn(const void* q, const void* k, const void* v, const int32_t* idx, int32_t B,
+                                   int32_t n_q, int32_t L_max, int32_t H_q, int32_t d, int32_t k_top, float scale,
+                                   int32_t n_split, void* out, float* lse, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  if (B < 0 || n_q < 0 || L_max < 0 || k_top < 1 || H_q < 1) return LSA_ERR_INVALID_ARG;
+  if (d != 128) return LSA_ERR_UNSUPPORTED;
+  if (H_q > 16 || k_top > 65536) return LSA_ERR_UNSUPPORTED;
+  if ((long long)B * n_q == 0) return LSA_OK;
+  if (!q || !k || !v || !idx || !out || L_max < 1) return LSA_ERR_INVALID_ARG;
+  const int split = resolve_split(B, n_q, k_top, n_split);
+  const size_t need = attn_ws_bytes((long long)B * n_q, H_q, d, split);
+  if (ws_bytes < need || (need > 0 && !ws)) return LSA_ERR_WORKSPACE;
+  if (((uintptr_t)ws) % 16 != 0) return LSA_ERR_WORKSPACE;
+  return run_attn(q, k, v, idx, B, n_q, L_max, H_q, d, k_top, scale, split, out, lse, ws, as_stream(stream));
+}
+
+// ------------------------------------------------------------------------------------------ forward
+namespace {
+
+struct FwdPlan {
+  bool decode_like;     // n_q == 1: chunks are groups of sequences
+  long long per_row;    // workspace bytes per chunk row
+  size_t fixed;         // workspace bytes independent of the chunk
+  int64_t ld;           // score row stride
+  int32_t n_blocks;
+};
+
+lsa_status check_forward(const lsa_forward_args* a) {
+  if (!a) return LSA_ERR_INVALID_ARG;
+  if (a->mode != LSA_MODE_PREFILL && a->mode != LSA_MODE_DECODE) return LSA_ERR_INVALID_ARG;
+  if (a->B < 0 || a->n_q < 0 || a->L_max < 1 || a->k_top < 1) return LSA_ERR_INVALID_ARG;
+  if (a->mode == LSA_MODE_DECODE && a->n_q != 1) return LSA_ERR_INVALID_ARG;
+  if (a->d_I != 64 && a->d_I != 128) return LSA_ERR_UNSUPPORTED;
+  if (a->H_I < 1 || a->H_I > 64 || a->d != 128 || a->H_q < 1 || a->H_q > 16) return LSA_ERR_UNSUPPORTED;
+  if (a->k_top > 4096) return LSA_ERR_UNSUPPORTED;
+  if (a->two_stage) {
+    if (a->block_size < 1 || a->n_keep < 1) return LSA_ERR_INVALID_ARG;
+    if (a->block_size > 128 || a->n_keep > 256 || a->L_max / a->block_size > 65536) return LSA_ERR_UNSUPPORTED;
+  }
+  if ((long long)a->B * a->n_q == 0) return LSA_OK;
+  if (!a->q_idx || !a->k_idx || !a->w || !a->q_pos || !a->q || !a->k || !a->v || !a->idx || !a->out)
+    return LSA_ERR_INVALID_ARG;
+  return LSA_OK;
+}
+
+FwdPlan plan_forward(const lsa_forward_args* a) {
+  FwdPlan p{};
+  p.decode_like = a->n_q == 1;
+  if (a->two_stage) {
+    p.n_blocks = a->L_max / a->block_size;
+    p.ld = (int64_t)a->n_keep * a->block_size;
+    p.per_row = p.ld * 4 + (long long)p.n_blocks * 8 + (a->kept_blocks ? 0 : (long long)a->n_keep * 4) + 64;
+    p.fixed = align_up((size_t)a->B * p.n_blocks * a->d_I * 4) + align_up((size_t)a->B * p.n_blocks * 2 * a->d_I);
+  } else {
+    p.n_blocks = 0;
+    p.ld = score_ld(a->L_max);
+    p.per_row = p.ld * 4;
+    p.fixed = 0;
+  }
+  return p;
+}
+
+// workspace for a chunk of `rows` rows
+size_t chunk_bytes(const lsa_forward_args* a, const FwdPlan& p, long long rows) {
+  size_t s = p.fixed;
+  s += align_up((size_t)rows * p.ld * 4);                                   // scores
+  if (a->two_stage) {
+    s += align_up((size_t)rows * p.n_blocks * 8);                           // block scores
+    if (!a->kept_blocks) s += align_up((size_t)rows * a->n_keep * 4);       // kept lists
+  }
+  const int split = resolve_split(1, (int32_t)rows, a->k_top, a->attn_split);
+  s += attn_ws_bytes(rows, a->H_q, a->d, split);
+  return s;
+}
+
+long long total_rows(const lsa_forward_args* a) { return a->n_q == 1 ? (long long)a->B : (long long)a->n_q; }
+
+}  // namespace
+
+LSA_API lsa_status lsa_forward_workspace_size(const lsa_forward_args* a, size_t* bytes) {
+  if (!bytes) return LSA_ERR_INVALID_ARG;
+  lsa_status st = check_forward(a);
+  if (st != LSA_OK) return st;
+  if ((long long)a->B * a->n_q == 0) {
+    *bytes = 0;
+    return LSA_OK;
+  }
+  const FwdPlan p = plan_forward(a);
+  long long rows = a->chunk_rows > 0 ? a->chunk_rows : std::max<long long>(1, (1ll << 30) / p.per_row);
+  rows = std::min(rows, total_rows(a));
+  *bytes = chunk_bytes(a, p, rows);
+  return LSA_OK;
+}
+
+LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_bytes, void* stream) {
+  lsa_status st = check_forward(a);
+  if (st != LSA_OK) return st;
+  if ((long long)a->B * a->n_q == 0) return LSA_OK;
+  if (((uintptr_t)ws) % 16 != 0) return LSA_ERR_WORKSPACE;
+  const FwdPlan p = plan_forward(a);
+  hipStream_t s = as_stream(stream);
+  const long long n_rows = total_rows(a);
+
+  // rows per chunk: requested, else the most that fit
+  long long rows = a->chunk_rows > 0 ? std::min<long long>(a->chunk_rows, n_rows) : n_rows;
+  if (chunk_bytes(a, p, rows) > ws_bytes) {
+    if (a->chunk_rows > 0) return LSA_ERR_WORKSPACE;
+    long long lo = 1, hi = rows;
+    if (chunk_bytes(a, p, 1) > ws_bytes || !ws) return LSA_ERR_WORKSPACE;
+    while (lo < hi) {
+      const long long mid = (lo + hi + 1) / 2;
+      if (chunk_bytes(a, p, mid) <= ws_bytes) lo = mid;
+      else hi = mid - 1;
+    }
+    rows = lo;
+  }
+
+  // workspace carve-up
+  char* base = static_cast<char*>(ws);
+  size_t off = 0;
+  int32_t* reps = nullptr;
+  int8_t* limbs = nullptr;
+  if (a->two_stage) {
+    reps = reinterpret_cast<int32_t*>(base + off);
+    off += align_up((size_t)a->B * p.n_blocks * a->d_I * 4);
+    limbs = reinterpret_cast<int8_t*>(base + off);
+    off += align_up((size_t)a->B * p.n_blocks * 2 * a->d_I);
+  }
+  int32_t* sc = reinterpret_cast<int32_t*>(base + off);
+  off += align_up((size_t)rows * p.ld * 4);
+  long long* bsc = nullptr;
+  int32_t* kept_ws = nullptr;
+  if (a->two_stage) {
+    bsc = reinterpret_cast<long long*>(base + off);
+    off += align_up((size_t)rows * p.n_blocks * 8);
+    if (!a->kept_blocks) {
+      kept_ws = reinterpret_cast<int32_t*>(base + off);
+      off += align_up((size_t)rows * a->n_keep * 4);
+    }
+  }
+  void* attn_ws = base + off;
+
+  const int32_t d_I = a->d_I, H_I = a->H_I, H_q = a->H_q, d = a->d, L = a->L_max, kt = a->k_top;
+  // one split count for every chunk, so no chunk needs more attention workspace than sized
+  const int split = resolve_split(1, (int32_t)rows, kt, a->attn_split);
+  if (a->two_stage && p.n_blocks > 0) {
+    if (lsa::launch_block_reps(a->k_idx, a->B, L, d_I, a->block_size, p.n_blocks, reps, s) != hipSuccess)
+      return LSA_ERR_HIP;
+    if (lsa::launch_block_limbs(reps, a->B, p.n_blocks, d_I, limbs, s) != hipSuccess) return LSA_ERR_HIP;
+  }
+
+  // one chunk: sequences [b0, b0+nb) x queries [i0, i0+ni) (either nb == 1 or ni == n_q == 1)
+  auto run_chunk = [&](int32_t b0, int32_t nb, int32_t i0, int32_t ni) -> lsa_status {
+    const long long r0 = (long long)b0 * a->n_q + i0;  // first flattened row
+    const int8_t* qi = a->q_idx + r0 * H_I * d_I;
+    const int8_t* ki = a->k_idx + (long long)b0 * L * d_I;
+    const int32_t* wq = a->w_per_query ? a->w + r0 * H_I : a->w;
+    const int32_t* qp = a->q_pos + r0;
+    const char* qq = static_cast<const char*>(a->q) + r0 * H_q * d * 2;
+    const char* kk = static_cast<const char*>(a->k) + (long long)b0 * L * d * 2;
+    const char* vv = static_cast<const char*>(a->v) + (long long)b0 * L * d * 2;
+    int32_t* ix = a->idx + r0 * kt;
+    int32_t* cnt = a->count ? a->count + r0 : nullptr;
+    char* oo = static_cast<char*>(a->out) + r0 * H_q * d * 2;
+    float* ls = a->lse ? a->lse + r0 * H_q : nullptr;
+    const int32_t* kept = nullptr;
+    lsa::IdxArgs ia{};
+    ia.q_idx = qi;
+    ia.k_idx = ki;
+    ia.w = wq;
+    ia.w_per_query = a->w_per_query ? 1 : 0;
+    ia.q_pos = qp;
+    ia.B = nb;
+    ia.n_q = ni;
+    ia.L_max = L;
+    ia.H_I = H_I;
+    ia.d_I = d_I;
+    ia.scores = sc;
+    ia.ld = p.ld;
+    if (a->two_stage) {
+      int32_t* kout = a->kept_blocks ? a->kept_blocks + r0 * a->n_keep : kept_ws;
+      lsa_status st2 = run_prefilter(qi, limbs + (long long)b0 * p.n_blocks * 2 * d_I, wq, a->w_per_query, qp, nb,
+                                     ni, p.n_blocks, H_I, d_I, a->block_size, a->n_keep, kout, bsc, s);
+      if (st2 != LSA_OK) return st2;
+      kept = kout;
+      ia.kept = kept;
+      ia.block_size = a->block_size;
+      ia.n_keep = a->n_keep;
+    }
+    ia.use_direct = a->two_stage ? true : ni < 8;
+    ia.span = flat_span(L, ia.use_direct);
+    if (lsa::launch_index_scores(ia, s) != hipSuccess) return LSA_ERR_HIP;
+    lsa::TopkArgs ta{};
+    ta.scores = sc;
+    ta.ld = p.ld;
+    ta.q_pos = qp;
+    ta.kept = kept;
+    ta.block_size = a->block_size;
+    ta.n_keep = a->n_keep;
+    ta.B = nb;
+    ta.n_q = ni;
+    ta.L_max = L;
+    ta.k = kt;
+    ta.idx = ix;
+    ta.count = cnt;
+    if (lsa::launch_topk(ta, s) != hipSuccess) return LSA_ERR_HIP;
+    return run_attn(qq, kk, vv, ix, nb, ni, L, H_q, d, kt, a->scale, split, oo, ls, attn_ws, s);
+  };
+
+  if (p.decode_like) {
+    for (long long b0 = 0; b0 < a->B; b0 += rows) {
+      const int32_t nb = (int32_t)std::min<long long>(rows, a->B - b0);
+      lsa_status st2 = run_chunk((int32_t)b0, nb, 0, 1);
+      if (st2 != LSA_OK) return st2;
+    }
+  } else {
+    for (int32_t b = 0; b < a->B; ++b) {
+      for (long long i0 = 0; i0 < a->n_q; i0 += rows) {
+        const int32_t ni = (int32_t)std::min<long long>(rows, a->n_q - i0);
+        lsa_status st2 = run_chunk(b, 1, (int32_t)i0, ni);
+        if (st2 != LSA_OK) return st2;
+      }
+    }
+  }
+  return LSA_OK;
+}

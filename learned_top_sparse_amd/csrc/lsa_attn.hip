@@ -1,0 +1,284 @@
+// lsa_attn.hip -- sparse attention over per-query index lists (gfx950, bf16 MFMA).
+//
+//     out[b,i,h,:] = sum_{j in J_i} softmax_j(scale * q[b,i,h,:] . k[b,j,:]) v[b,j,:]
+// "Latent Sparse Attention (LSA)" §3.2 "Attention": attention runs only over the
+// keys of J_i, one list for every query head; §2: O(k) work per query.  App. F.1
+// "Attention kernels": J_i is read like a page table of single-slot pages, -1 =
+// no key.  The split form (J_i cut into n_split parts merged by log-sum-exp) is
+// the split-KV decode kernel the same appendix mentions.
+//
+// One wave per (query row, split).  Per tile of 32 listed keys:
+//   * the 32 K rows are gathered straight into MFMA A fragments and multiplied by
+//     the query's heads (B fragments, loaded once): S^T[key][head] = K Q^T with
+//     v_mfma_f32_16x16x32_bf16 -- lane l then owns head (l & 15);
+//   * the 32 V rows are gathered and written transposed to LDS (key pairs per
+//     dword, rows padded to 18 dwords: conflict-free writes and b64 reads);
+//   * fp32 online softmax in the exp2 domain (rescale of O only when a head's
+//     running max moves); P goes to bf16 and is used directly as the B fragment
+//     of O^T[d][head] += V^T P^T, since the lanes already hold P in the key order
+//     that the A fragment (read from the transposed V tile) uses.
+#include "lsa_device.h"
+#include "lsa_internal.h"
+
+namespace lsa {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int KT = 32;      // keys per tile
+constexpr int RSD = 18;     // dwords per transposed V row (16 key pairs + 2 pad)
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+typedef unsigned int u32;
+typedef u32 v4u __attribute__((ext_vector_type(4)));
+typedef u32 v2u __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float xhalf32_maxf(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xrow16_maxf(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf32_sumf(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xrow16_sumf(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite)
+__device__ __forceinline__ u32 bf16_bits(float f) {
+  const u32 u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ u32 pack_bf16(float lo, float hi) { return bf16_bits(lo) | (bf16_bits(hi) << 16); }
+
+union Frag8 {
+  v8bf v;
+  v4u u;
+};
+
+// One 64-thread workgroup = one wave = one (row, split) unit.
+__global__ __launch_bounds__(64) void sparse_attn_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const int32_t* __restrict__ idx, int n_q, int L_max, int H_q, int k_top, float scale_log2,
+    int n_split, __bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) u32 vt[D * RSD];
+
+  const int lane = threadIdx.x, g = lane >> 4, r16 = lane & 15;
+  const long long unit = blockIdx.x;
+  const long long row = unit / n_split;
+  const int split = (int)(unit % n_split);
+  const int b = (int)(row / n_q);
+  const int32_t* jrow = idx + row * (long long)k_top;
+  const __bf16* kb = k + (long long)b * L_max * D;
+  const __bf16* vb = v + (long long)b * L_max * D;
+
+  // query heads as B fragments: lane (h = l&15, g) holds d = 32g + 8s .. +8 at step s
+  Frag8 Qb[4];
+  {
+    const bool hv = r16 < H_q;
+    const __bf16* qr = q + (row * H_q + (hv ? r16 : 0)) * D + 32 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (hv) Qb[s].u = *(const v4u*)(qr + 8 * s);
+      else Qb[s].u = v4u{0u, 0u, 0u, 0u};
+    }
+  }
+
+  v4f O[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) O[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  const int n_tiles = (k_top + KT - 1) / KT;
+  const int t_begin = (int)((long long)n_tiles * split / n_split);
+  const int t_end = (int)((long long)n_tiles * (split + 1) / n_split);
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int base = t * KT;
+    // indices: keys (l&15) and 16+(l&15) for the K fragments, pair 2*(l&15)+{0,1} for V
+    auto load_j = [&](int pos) -> int {
+      if (pos >= k_top) return -1;
+      const int j = jrow[pos];
+      return (j >= 0 && j < L_max) ? j : -1;
+    };
+    const int jA = load_j(base + r16), jB = load_j(base + 16 + r16);
+    const int j0 = load_j(base + 2 * r16), j1 = load_j(base + 2 * r16 + 1);
+    const unsigned long long vA = __ballot(jA >= 0), vB = __ballot(jB >= 0);
+    if ((vA | vB) == 0ull) continue;
+
+    // gathers
+    Frag8 Ka[2][4];
+    {
+      const __bf16* ra = kb + (long long)(jA < 0 ? 0 : jA) * D + 32 * g;
+      const __bf16* rb = kb + (long long)(jB < 0 ? 0 : jB) * D + 32 * g;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        Ka[0][s].u = (jA >= 0) ? *(const v4u*)(ra + 8 * s) : v4u{0u, 0u, 0u, 0u};
+        Ka[1][s].u = (jB >= 0) ? *(const v4u*)(rb + 8 * s) : v4u{0u, 0u, 0u, 0u};
+      }
+    }
+    v4u V0[4], V1[4];  // rows j0 / j1, d = 8g + 32m .. +8
+    {
+      const __bf16* r0 = vb + (long long)(j0 < 0 ? 0 : j0) * D + 8 * g;
+      const __bf16* r1 = vb + (long long)(j1 < 0 ? 0 : j1) * D + 8 * g;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        V0[m] = (j0 >= 0) ? *(const v4u*)(r0 + 32 * m) : v4u{0u, 0u, 0u, 0u};
+        V1[m] = (j1 >= 0) ? *(const v4u*)(r1 + 32 * m) : v4u{0u, 0u, 0u, 0u};
+      }
+    }
+
+    // S^T = K Q^T : lane holds keys 16*mt + 4g + i for head r16
+    v4f S[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      S[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) S[mt] = mfma_bf16(Ka[mt][s].v, Qb[s].v, S[mt]);
+    }
+
+    // V^T into LDS: dword [d][kp] = (V[2kp][d], V[2kp+1][d]), d = 8g + 32m + e
+    __syncthreads();  // previous tile's reads of vt are done
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const u32 a = V0[m][w2], c = V1[m][w2];
+        const int d = 8 * g + 32 * m + 2 * w2;
+        vt[d * RSD + r16] = __builtin_amdgcn_perm(c, a, 0x05040100u);        // low halves
+        vt[(d + 1) * RSD + r16] = __builtin_amdgcn_perm(c, a, 0x07060302u);  // high halves
+      }
+    }
+
+    // online softmax (exp2 domain)
+    float sv[2][4];
+    float mt_max = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const unsigned long long vm = mt ? vB : vA;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 4 * g + i;
+        const bool ok = (vm >> key) & 1ull;
+        sv[mt][i] = ok ? S[mt][i] * scale_log2 : -INFINITY;
+        mt_max = fmaxf(mt_max, sv[mt][i]);
+      }
+    }
+    mt_max = xhalf32_maxf(mt_max);
+    mt_max = xrow16_maxf(mt_max);
+    const float m_new = fmaxf(m_run, mt_max);
+    if (__ballot(m_new > m_run) != 0ull) {
+      const float alpha = exp2f(m_run - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int t2 = 0; t2 < 8; ++t2) O[t2] *= alpha;
+      m_run = m_new;
+    }
+    Frag8 Pb;
+    {
+      float pv[8];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pp = exp2f(sv[mt][i] - m_run);
+          pv[4 * mt + i] = pp;
+          l_part += pp;
+        }
+      Pb.u = v4u{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
+                 pack_bf16(pv[6], pv[7])};
+    }
+
+    __syncthreads();  // vt written
+    // O^T[d][h] += V^T[d][keys] P^T[keys][h]; A rows d = 16*dt + r16, keys 4g..4g+3, 16+4g..
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d = 16 * dt + r16;
+      Frag8 Va;
+      const v2u lo = *(const v2u*)(&vt[d * RSD + 2 * g]);
+      const v2u hi = *(const v2u*)(&vt[d * RSD + 8 + 2 * g]);
+      Va.u = v4u{lo[0], lo[1], hi[0], hi[1]};
+      O[dt] = mfma_bf16(Va.v, Pb.v, O[dt]);
+    }
+  }
+
+  float l_tot = xhalf32_sumf(l_part);
+  l_tot = xrow16_sumf(l_tot);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse_v = l_tot > 0.f ? (m_run + log2f(l_tot)) * LN2 : -INFINITY;
+  const int h = r16;
+  if (h >= H_q) return;
+  if (n_split == 1) {
+    __bf16* orow = out + (row * H_q + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d = 16 * dt + 4 * g;
+      v2u pk;
+      pk[0] = pack_bf16(O[dt][0] * inv, O[dt][1] * inv);
+      pk[1] = pack_bf16(O[dt][2] * inv, O[dt][3] * inv);
+      *(v2u*)(orow + d) = pk;
+    }
+    if (lse != nullptr && g == 0) lse[row * H_q + h] = lse_v;
+  } else {
+    float* po = ws + ((row * n_split + split) * H_q + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d = 16 * dt + 4 * g;
+      *(v4f*)(po + d) = O[dt] * inv;
+    }
+    if (g == 0) {
+      float* pl = ws + (long long)gridDim.x * H_q * D;  // lse parts after the outputs
+      pl[(row * n_split + split) * H_q + h] = lse_v;
+    }
+  }
+}
+
+// Merge of the n_split partial results of each (row, head) by log-sum-exp.
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ ws, long long n_units,
+                                                          int n_split, int H_q, __bf16* __restrict__ out,
+                                                          float* __restrict__ lse) {
+  const long long rh = blockIdx.x;  // row * H_q + h
+  const long long row = rh / H_q;
+  const int h = (int)(rh % H_q);
+  const int d = threadIdx.x;
+  const float* pl = ws + n_units * H_q * D;
+  float M = -INFINITY;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pl[(row * n_split + s) * H_q + h]);
+  float num = 0.f, den = 0.f;
+  if (M > -INFINITY) {
+    for (int s = 0; s < n_split; ++s) {
+      const float ls = pl[(row * n_split + s) * H_q + h];
+      const float wgt = expf(ls - M);
+      den += wgt;
+      num += wgt * ws[((row * n_split + s) * H_q + h) * D + d];
+    }
+  }
+  const float o = den > 0.f ? num / den : 0.f;
+  out[rh * D + d] = (__bf16)o;
+  if (lse != nullptr && d == 0) lse[rh] = den > 0.f ? M + logf(den) : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
+  const long long rows = (long long)a.B * a.n_q;
+  if (rows == 0) return hipSuccess;
+  const long long units = rows * a.n_split;
+  hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)units), dim3(64), 0, st, (const __bf16*)a.q,
+                     (const __bf16*)a.k, (const __bf16*)a.v, a.idx, a.n_q, a.L_max, a.H_q, a.k_top,
+                     a.scale * LOG2E, a.n_split, (__bf16*)a.out, a.lse, a.ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_split == 1) return e;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(rows * a.H_q)), dim3(128), 0, st, a.ws, units,
+                     a.n_split, a.H_q, (__bf16*)a.out, a.lse);
+  return hipGetLastError();
+}
+
+}  // namespace lsa

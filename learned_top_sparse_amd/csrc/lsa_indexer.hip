@@ -1,0 +1,544 @@
+// lsa_indexer.hip -- int8 MFMA indexer kernels for gfx950.
+//
+// Token scores ("Latent Sparse Attention (LSA)", §2.1 "Token Sparse Attention":
+// a low-precision indexer with few heads scores every preceding key):
+//     S[b,i,j] = sum_h w_h * max(0, q_idx[b,i,h,:] . k_idx[b,j,:])      (exact int32)
+// Block scores of the two-stage indexer (HISA summary: block filter first; LSA
+// §3.1 "Pooling": a block summary is the sum of its index keys):
+//     BS[b,i,m] = sum_h w_h * max(0, q_idx[b,i,h,:] . reps[b,m,:])      (exact int64)
+//
+// Mapping onto the matrix cores: a query's H_I heads are the M dimension of
+// v_mfma_i32_16x16x64_i8 (tiles of 16 heads), keys are N (16 per tile), d_I is K.
+// Output lane l then holds heads 4*(l>>4)+e of key (l&15), so the weighted ReLU
+// head sum is lane-local (v_max_i32 + v_mad_i32_i24 per element) and only the
+// final sum over the four 16-lane rows crosses lanes (permlane swaps, no LDS).
+#include "lsa_device.h"
+#include "lsa_internal.h"
+
+namespace lsa {
+
+// 16-byte chunk of the d_I bytes supplied by lane row g at K-step ks.  A and B
+// use the same assignment, so the product is the full dot product.
+template <int D>
+__device__ __forceinline__ int kchunk(int g, int ks) { return g * (D / 64) + ks; }
+
+// XOR swizzle of 16-byte chunk c of row r in an LDS key tile whose rows are RB
+// bytes: 8 consecutive rows read at one logical chunk hit 8 distinct bank groups,
+// and 8 consecutive chunks of one row (the staging writes) do too.
+template <int RB>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (RB >= 128) return c ^ (r & 7);
+  else return c ^ ((r >> 1) & 3);
+}
+
+// Reduce-scatter of 8 per-lane partial sums (value v = 4*q + nt) over the four
+// 16-lane rows: afterwards lane row g holds the full sums of values
+// 4*(g>>1) + 2*(g&1) + {0,1}, i.e. query q = g>>1, key tiles nt = 2*(g&1) + {0,1}.
+__device__ __forceinline__ void reduce_scatter8(const int (&v)[8], int (&out)[2]) {
+  int r1[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) r1[t] = xhalf32_sum(v[t], v[4 + t]);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) out[t] = xrow16_sum(r1[t], r1[2 + t]);
+}
+// Four values: lane row g ends with the full sum of value g.
+__device__ __forceinline__ int reduce_scatter4(const int (&v)[4]) {
+  int r0 = xhalf32_sum(v[0], v[2]);
+  int r1 = xhalf32_sum(v[1], v[3]);
+  return xrow16_sum(r0, r1);
+}
+__device__ __forceinline__ void reduce_scatter8_64(const long long (&v)[8], long long (&out)[2]) {
+  long long r1[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) r1[t] = xhalf32_sum64(v[t], v[4 + t]);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) out[t] = xrow16_sum64(r1[t], r1[2 + t]);
+}
+
+// Load the A fragments (index-query heads) and head weights of one query.
+template <int D, int MT>
+__device__ __forceinline__ void load_query(const int8_t* __restrict__ q_idx, const int32_t* __restrict__ w,
+                                           int w_per_query, long long row, int H_I, bool valid,
+                                           v4i (&A)[MT][D / 64], int (&wt)[MT][4]) {
+  const int lane = lane_id(), g = lane >> 4, r16 = lane & 15;
+  const int32_t* wr = w + (w_per_query ? row * H_I : 0);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int h = 16 * mt + r16;
+    const bool ok = valid && h < H_I;
+    const int8_t* qr = q_idx + (row * H_I + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks)
+      A[mt][ks] = ok ? *(const v4i*)(qr + 16 * kchunk<D>(g, ks)) : v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int hh = 16 * mt + 4 * g + e;
+      wt[mt][e] = (valid && hh < H_I) ? wr[hh] : 0;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Flat scores, prefill: a workgroup of 4 waves holds 4*QW queries in registers and
+// streams a span of keys through LDS in 64-key tiles shared by all its queries.
+// Grid: x = n_qtiles * n_spans (longest query tiles first), y = B.
+template <int D, int MT, int QW>
+__global__ __launch_bounds__(256, 2) void idx_flat_kernel(
+    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
+    int w_per_query, const int32_t* __restrict__ q_pos, int n_q, int L_max, int H_I, int span,
+    int n_spans, int n_qtiles, int32_t* __restrict__ scores, long long ld) {
+  static_assert(QW == 2, "reduce_scatter8 assumes two queries per wave");
+  constexpr int KS = D / 64, KT = 64, QT = 4 * QW, CH = D / 16;
+  constexpr int LOADS = KT * CH / 256;
+  __shared__ __attribute__((aligned(16))) int8_t tile[2][KT * D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int b = blockIdx.y;
+  const int s = blockIdx.x % n_spans;
+  const int qt = n_qtiles - 1 - blockIdx.x / n_spans;
+  const int i0 = qt * QT;
+  const int32_t* qp = q_pos + (long long)b * n_q;
+
+  int pmax = -1;
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    const int i = i0 + t;
+    if (i < n_q) pmax = max(pmax, min(qp[i], L_max - 1));
+  }
+  const int j_begin = s * span;
+  if (j_begin > pmax) return;
+  const int j_end = min(j_begin + span, pmax + 1);
+
+  v4i A[QW][MT][KS];
+  int wt[QW][MT][4];
+  int pq[QW];
+  long long srow[QW];
+#pragma unroll
+  for (int q = 0; q < QW; ++q) {
+    const int i = i0 + wave * QW + q;
+    const bool valid = i < n_q;
+    const long long row = (long long)b * n_q + (valid ? i : 0);
+    pq[q] = valid ? min(qp[i], L_max - 1) : -1;
+    srow[q] = row * ld;
+    load_query<D, MT>(q_idx, w, w_per_query, row, H_I, valid, A[q], wt[q]);
+  }
+
+  const int8_t* kb = k_idx + (long long)b * L_max * D;
+  v4i stage[LOADS];
+  auto gload = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int cid = tid + 256 * u, r = cid / CH, c = cid % CH, j = j0 + r;
+      stage[u] = (j < L_max) ? *(const v4i*)(kb + (long long)j * D + 16 * c) : v4i{0, 0, 0, 0};
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int cid = tid + 256 * u, r = cid / CH, c = cid % CH;
+      *(v4i*)(&tile[buf][r * D + 16 * swz<D>(r, c)]) = stage[u];
+    }
+  };
+
+  const int n_tiles = (j_end - j_begin + KT - 1) / KT;
+  gload(j_begin);
+  swrite(0);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int j0 = j_begin + t * KT;
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) gload(j0 + KT);
+    int part[8];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      v4i Bf[KS];
+      const int r = 16 * nt + r16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        Bf[ks] = *(const v4i*)(&tile[buf][r * D + 16 * swz<D>(r, kchunk<D>(g, ks))]);
+#pragma unroll
+      for (int q = 0; q < QW; ++q) {
+        v4i acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          acc[mt] = v4i{0, 0, 0, 0};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc[mt] = mfma_i8(A[q][mt][ks], Bf[ks], acc[mt]);
+        }
+        int ps = 0;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ps += __mul24(max(acc[mt][e], 0), wt[q][mt][e]);
+        part[4 * q + nt] = ps;
+      }
+    }
+    int res[2];
+    reduce_scatter8(part, res);
+    {
+      const int q = g >> 1;
+      const int p_sel = q ? pq[1] : pq[0];
+      const long long base = q ? srow[1] : srow[0];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int j = j0 + 16 * (2 * (g & 1) + e) + r16;
+        if (j <= p_sel) scores[base + j] = res[e];
+      }
+    }
+    if (t + 1 < n_tiles) swrite(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Direct scores: one query per workgroup, each wave takes 64-slot groups and loads
+// its key rows straight into MFMA B fragments (no LDS).  Used for decode (flat,
+// whole context split into spans over grid.x) and for the two-stage token stage
+// (KEPT: slot s is key kept[s / bs] * bs + s % bs; one workgroup covers all slots).
+// Grid: x = n_spans (1 for KEPT), y = B * n_q.
+template <int D, int MT, bool KEPT>
+__global__ __launch_bounds__(256) void idx_direct_kernel(
+    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
+    int w_per_query, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ kept, int bs,
+    int n_keep, int n_q, int L_max, int H_I, int span, int32_t* __restrict__ scores, long long ld) {
+  constexpr int KS = D / 64;
+  __shared__ int kept_s[KEPT ? 256 : 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const long long row = blockIdx.y;
+  const int b = (int)(row / n_q);
+  const int p = min(q_pos[row], L_max - 1);
+  if (p < 0) return;
+
+  int s_begin, s_end;
+  if constexpr (KEPT) {
+    for (int t = tid; t < n_keep; t += 256) kept_s[t] = kept[row * n_keep + t];
+    __syncthreads();
+    s_begin = 0;
+    s_end = n_keep * bs;
+  } else {
+    s_begin = blockIdx.x * span;
+    s_end = min(s_begin + span, p + 1);
+    if (s_begin >= s_end) return;
+  }
+
+  v4i A[MT][KS];
+  int wt[MT][4];
+  load_query<D, MT>(q_idx, w, w_per_query, row, H_I, true, A, wt);
+  const int8_t* kb = k_idx + (long long)b * L_max * D;
+  const long long srow = row * ld;
+
+  // key of a slot, or -1 if the slot is not a candidate of this query
+  auto key_of = [&](int s) -> int {
+    if (s >= s_end) return -1;
+    if constexpr (KEPT) {
+      const int blk = kept_s[s / bs];
+      if (blk < 0) return -1;
+      const int j = blk * bs + s % bs;
+      return (j <= p) ? j : -1;
+    } else {
+      return s;
+    }
+  };
+
+  const int n_groups = (s_end - s_begin + 63) / 64;
+  for (int grp = wave; grp < n_groups; grp += 4) {
+    const int sg = s_begin + 64 * grp;
+    v4i Bf[4][KS];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int j = key_of(sg + 16 * nt + r16);
+      const int8_t* kr = kb + (long long)(j < 0 ? 0 : j) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        Bf[nt][ks] = (j >= 0) ? *(const v4i*)(kr + 16 * kchunk<D>(g, ks)) : v4i{0, 0, 0, 0};
+    }
+    int part[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      v4i acc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[mt] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc[mt] = mfma_i8(A[mt][ks], Bf[nt][ks], acc[mt]);
+      }
+      int ps = 0;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ps += __mul24(max(acc[mt][e], 0), wt[mt][e]);
+      part[nt] = ps;
+    }
+    const int res = reduce_scatter4(part);
+    const int s = sg + 16 * g + r16;
+    if (key_of(s) >= 0) scores[srow + s] = res;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Block representatives: reps[b,m,c] = sum over the block's keys of k_idx[b,j,c].
+__global__ void blk_reps_kernel(const int8_t* __restrict__ k_idx, int L_max, int D, int bs, int n_blocks,
+                                long long total, int32_t* __restrict__ reps) {
+  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  const int c = (int)(e % D);
+  const long long bm = e / D;
+  const int m = (int)(bm % n_blocks);
+  const long long b = bm / n_blocks;
+  const int8_t* src = k_idx + (b * L_max + (long long)m * bs) * D + c;
+  int acc = 0;
+  for (int t = 0; t < bs; ++t) acc += src[(long long)t * D];
+  reps[e] = acc;
+}
+
+// Two int8 limbs of each representative, r = 128*hi + lo with lo in [-64, 63]:
+// for blocks of at most 128 int8 keys |r| <= 16384, so hi fits int8 as well.
+// Row layout [hi (D bytes) | lo (D bytes)].
+__global__ void blk_limbs_kernel(const int32_t* __restrict__ reps, int D, long long total,
+                                 int8_t* __restrict__ limbs) {
+  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  const int c = (int)(e % D);
+  const long long rowi = e / D;
+  const int r = reps[e];
+  const int hi = (r + 64) >> 7;
+  const int lo = r - (hi << 7);
+  limbs[rowi * 2 * D + c] = (int8_t)hi;
+  limbs[rowi * 2 * D + D + c] = (int8_t)lo;
+}
+
+// Block scores with the flat kernel's tiling: the "keys" are block limb rows of
+// 2*D bytes; q.r = 128*(q.hi) + (q.lo) is exact in int32 (|q.r| < 2^29), then
+// ReLU and the weighted head sum accumulate in int64.  Block m is scored for a
+// query iff m < floor(q_pos / bs) (its own block is never scored).
+template <int D, int MT, int QW>
+__global__ __launch_bounds__(256, 2) void blk_scores_kernel(
+    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ limbs, const int32_t* __restrict__ w,
+    int w_per_query, const int32_t* __restrict__ q_pos, int n_q, int n_blocks, int L_max, int H_I,
+    int bs, int span, int n_spans, int n_qtiles, long long* __restrict__ bscores, long long ld) {
+  static_assert(QW == 2, "reduce_scatter8_64 assumes two queries per wave");
+  constexpr int KS = D / 64, KT = 64, QT = 4 * QW, RB = 2 * D, CH = RB / 16;
+  constexpr int LOADS = KT * CH / 256;
+  __shared__ __attribute__((aligned(16))) int8_t tile[2][KT * RB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int b = blockIdx.y;
+  const int s = blockIdx.x % n_spans;
+  const int qt = n_qtiles - 1 - blockIdx.x / n_spans;
+  const int i0 = qt * QT;
+  const int32_t* qp = q_pos + (long long)b * n_q;
+
+  int omax = 0;  // blocks [0, omax) are scored by some query of the tile
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    const int i = i0 + t;
+    if (i < n_q) {
+      const int pp = min(qp[i], L_max - 1);
+      if (pp >= 0) omax = max(omax, min(pp / bs, n_blocks));
+    }
+  }
+  const int m_begin = s * span;
+  if (m_begin >= omax) return;
+  const int m_end = min(m_begin + span, omax);
+
+  v4i A[QW][MT][KS];
+  int wt[QW][MT][4];
+  int own[QW];
+  long long srow[QW];
+#pragma unroll
+  for (int q = 0; q < QW; ++q) {
+    const int i = i0 + wave * QW + q;
+    const bool valid = i < n_q;
+    const long long row = (long long)b * n_q + (valid ? i : 0);
+    const int pp = valid ? min(qp[i], L_max - 1) : -1;
+    own[q] = pp >= 0 ? min(pp / bs, n_blocks) : 0;
+    srow[q] = row * ld;
+    load_query<D, MT>(q_idx, w, w_per_query, row, H_I, valid, A[q], wt[q]);
+  }
+
+  const int8_t* lb = limbs + (long long)b * n_blocks * RB;
+  v4i stage[LOADS];
+  auto gload = [&](int m0) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int cid = tid + 256 * u, r = cid / CH, c = cid % CH, m = m0 + r;
+      stage[u] = (m < n_blocks) ? *(const v4i*)(lb + (long long)m * RB + 16 * c) : v4i{0, 0, 0, 0};
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int cid = tid + 256 * u, r = cid / CH, c = cid % CH;
+      *(v4i*)(&tile[buf][r * RB + 16 * swz<RB>(r, c)]) = stage[u];
+    }
+  };
+
+  const int n_tiles = (m_end - m_begin + KT - 1) / KT;
+  gload(m_begin);
+  swrite(0);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int m0 = m_begin + t * KT;
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) gload(m0 + KT);
+    long long part[8];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      v4i Bh[KS], Bl[KS];
+      const int r = 16 * nt + r16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int c = kchunk<D>(g, ks);
+        Bh[ks] = *(const v4i*)(&tile[buf][r * RB + 16 * swz<RB>(r, c)]);
+        Bl[ks] = *(const v4i*)(&tile[buf][r * RB + 16 * swz<RB>(r, c + D / 16)]);
+      }
+#pragma unroll
+      for (int q = 0; q < QW; ++q) {
+        long long ps = 0;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          v4i ah = v4i{0, 0, 0, 0}, al = v4i{0, 0, 0, 0};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            ah = mfma_i8(A[q][mt][ks], Bh[ks], ah);
+            al = mfma_i8(A[q][mt][ks], Bl[ks], al);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int x = (ah[e] << 7) + al[e];
+            ps += (long long)wt[q][mt][e] * (long long)max(x, 0);
+          }
+        }
+        part[4 * q + nt] = ps;
+      }
+    }
+    long long res[2];
+    reduce_scatter8_64(part, res);
+    {
+      const int q = g >> 1;
+      const int o = q ? own[1] : own[0];
+      const long long base = q ? srow[1] : srow[0];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int m = m0 + 16 * (2 * (g & 1) + e) + r16;
+        if (m < o) bscores[base + m] = res[e];
+      }
+    }
+    if (t + 1 < n_tiles) swrite(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// host-side launchers
+template <int D, int MT>
+static hipError_t launch_flat_t(const IdxArgs& a, hipStream_t st) {
+  const int QT = 8;
+  const int n_qtiles = (a.n_q + QT - 1) / QT;
+  const int span = a.span;
+  const int n_spans = (a.L_max + span - 1) / span;
+  dim3 grid((unsigned)(n_qtiles * n_spans), (unsigned)a.B);
+  hipLaunchKernelGGL((idx_flat_kernel<D, MT, 2>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.w,
+                     a.w_per_query, a.q_pos, a.n_q, a.L_max, a.H_I, span, n_spans, n_qtiles, a.scores,
+                     (long long)a.ld);
+  return hipGetLastError();
+}
+template <int D, int MT, bool KEPT>
+static hipError_t launch_direct_t(const IdxArgs& a, hipStream_t st) {
+  const int n_spans = KEPT ? 1 : (a.L_max + a.span - 1) / a.span;
+  dim3 grid((unsigned)n_spans, (unsigned)(a.B * a.n_q));
+  hipLaunchKernelGGL((idx_direct_kernel<D, MT, KEPT>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.w,
+                     a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I,
+                     a.span, a.scores, (long long)a.ld);
+  return hipGetLastError();
+}
+
+#define LSA_DISPATCH_MT(H, CALL)            \
+  switch (((H) + 15) / 16) {                \
+    case 1: return CALL(1);                 \
+    case 2: return CALL(2);                 \
+    case 3: return CALL(3);                 \
+    case 4: return CALL(4);                 \
+    default: return hipErrorInvalidValue;   \
+  }
+
+hipError_t launch_index_scores(const IdxArgs& a, hipStream_t st) {
+  const bool kept = a.kept != nullptr;
+  const bool direct = kept || a.use_direct;
+  if (a.d_I == 128) {
+    if (kept) {
+#define C(MT) launch_direct_t<128, MT, true>(a, st)
+      LSA_DISPATCH_MT(a.H_I, C)
+#undef C
+    } else if (direct) {
+#define C(MT) launch_direct_t<128, MT, false>(a, st)
+      LSA_DISPATCH_MT(a.H_I, C)
+#undef C
+    } else {
+#define C(MT) launch_flat_t<128, MT>(a, st)
+      LSA_DISPATCH_MT(a.H_I, C)
+#undef C
+    }
+  } else {
+    if (kept) {
+#define C(MT) launch_direct_t<64, MT, true>(a, st)
+      LSA_DISPATCH_MT(a.H_I, C)
+#undef C
+    } else if (direct) {
+#define C(MT) launch_direct_t<64, MT, false>(a, st)
+      LSA_DISPATCH_MT(a.H_I, C)
+#undef C
+    } else {
+#define C(MT) launch_flat_t<64, MT>(a, st)
+      LSA_DISPATCH_MT(a.H_I, C)
+#undef C
+    }
+  }
+}
+
+hipError_t launch_block_reps(const int8_t* k_idx, int B, int L_max, int d_I, int bs, int n_blocks,
+                             int32_t* reps, hipStream_t st) {
+  const long long total = (long long)B * n_blocks * d_I;
+  if (total == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  hipLaunchKernelGGL(blk_reps_kernel, dim3(blocks), dim3(256), 0, st, k_idx, L_max, d_I, bs, n_blocks,
+                     total, reps);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_limbs(const int32_t* reps, int B, int n_blocks, int d_I, int8_t* limbs,
+                              hipStream_t st) {
+  const long long total = (long long)B * n_blocks * d_I;
+  if (total == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  hipLaunchKernelGGL(blk_limbs_kernel, dim3(blocks), dim3(256), 0, st, reps, d_I, total, limbs);
+  return hipGetLastError();
+}
+
+template <int D, int MT>
+static hipError_t launch_blk_scores_t(const BlkArgs& a, hipStream_t st) {
+  const int QT = 8;
+  const int n_qtiles = (a.n_q + QT - 1) / QT;
+  const int span = a.span;
+  const int n_spans = (a.n_blocks + span - 1) / span;
+  if (n_spans == 0) return hipSuccess;
+  dim3 grid((unsigned)(n_qtiles * n_spans), (unsigned)a.B);
+  hipLaunchKernelGGL((blk_scores_kernel<D, MT, 2>), grid, dim3(256), 0, st, a.q_idx, a.limbs, a.w,
+                     a.w_per_query, a.q_pos, a.n_q, a.n_blocks, a.L_max, a.H_I, a.block_size, span,
+                     n_spans, n_qtiles, a.bscores, (long long)a.ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_scores(const BlkArgs& a, hipStream_t st) {
+  if (a.d_I == 128) {
+#define C(MT) launch_blk_scores_t<128, MT>(a, st)
+    LSA_DISPATCH_MT(a.H_I, C)
+#undef C
+  } else {
+#define C(MT) launch_blk_scores_t<64, MT>(a, st)
+    LSA_DISPATCH_MT(a.H_I, C)
+#undef C
+  }
+}
+
+}  // namespace lsa

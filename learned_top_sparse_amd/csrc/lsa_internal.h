@@ -1,0 +1,78 @@
+// lsa_internal.h -- host-side launcher interface between the C ABI (lsa_api.cpp)
+// and the kernel translation units.  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lsa {
+
+struct IdxArgs {
+  const int8_t* q_idx;
+  const int8_t* k_idx;
+  const int32_t* w;
+  int w_per_query;
+  const int32_t* q_pos;
+  const int32_t* kept;  // nullptr = flat
+  int block_size, n_keep;
+  int B, n_q, L_max, H_I, d_I;
+  int32_t* scores;
+  long long ld;
+  int span;        // keys per workgroup span (flat)
+  bool use_direct; // flat scores with one query per workgroup (decode-shaped)
+};
+
+struct BlkArgs {
+  const int8_t* q_idx;
+  const int8_t* limbs;
+  const int32_t* w;
+  int w_per_query;
+  const int32_t* q_pos;
+  int B, n_q, n_blocks, L_max, H_I, d_I, block_size;
+  long long* bscores;
+  long long ld;
+  int span;
+};
+
+struct TopkArgs {
+  const int32_t* scores;
+  long long ld;
+  const int32_t* q_pos;
+  const int32_t* kept;
+  int block_size, n_keep;
+  int B, n_q, L_max, k;
+  int32_t* idx;
+  int32_t* count;
+};
+
+struct BlkSelArgs {
+  const long long* bscores;
+  long long ld;
+  const int32_t* q_pos;
+  int B, n_q, n_blocks, block_size, n_keep;
+  int32_t* kept;
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* idx;
+  int B, n_q, L_max, H_q, d, k_top;
+  float scale;
+  int n_split;
+  void* out;
+  float* lse;
+  float* ws;  // n_split > 1: partial outputs [rows, n_split, H_q, d] then lse [rows, n_split, H_q]
+};
+
+hipError_t launch_index_scores(const IdxArgs& a, hipStream_t st);
+hipError_t launch_block_reps(const int8_t* k_idx, int B, int L_max, int d_I, int bs, int n_blocks,
+                             int32_t* reps, hipStream_t st);
+hipError_t launch_block_limbs(const int32_t* reps, int B, int n_blocks, int d_I, int8_t* limbs,
+                              hipStream_t st);
+hipError_t launch_block_scores(const BlkArgs& a, hipStream_t st);
+hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
+
+}  // namespace lsa
