@@ -1,0 +1,359 @@
+"""Benchmark of the learned top-k sparse attention hot path on one MI355X.
+
+Headline: decode tok/s at 128K context, k = 2048 (64 sequences, 131072 cached
+tokens + the new one each; one query per sequence per step).  A step is one
+pass of the whole decode path over the batch: int8 indexer scan of every
+cached index key -> exact top-k -> split-KV sparse attention.  The same JSON
+line also carries the 128K prefill figure (the final 8192-query chunk of a
+131072-token context through the two-stage path: block reps -> block
+prefilter -> token scores in kept blocks -> top-k -> sparse attention).
+
+Each step calls the C-ABI entry points in the order lsa_forward runs them
+(checked bit-identical to lsa_forward before timing), with HIP events recorded
+on the launch stream between calls, so every kernel's duration is measured live.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       [--no-cpu-baseline] [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill queries/s & decode tok/s at 128K ctx, k=2048; % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published (5.0 POPS)
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+
+def _describe(wl):
+    s = (f"{wl.name}: B={wl.B} x n_q={wl.n_q} queries at positions {wl.q_pos0}..{wl.q_pos0 + wl.n_q - 1}, "
+         f"{wl.L} cached keys, indexer H_I={wl.H_I} d_I={wl.d_I} int8, k={wl.k}, "
+         f"attention {wl.H_q} bf16 query heads / 1 KV head d={wl.d}")
+    if wl.two_stage:
+        s += f", two-stage blocks of {wl.block_size} keep {wl.n_keep}"
+    return s
+
+
+class Step:
+    """One pass of the path through the C ABI, chunked exactly as lsa_forward chunks it
+    (lsa_forward_plan), with HIP events recorded on the launch stream between calls."""
+
+    def __init__(self, lsa, torch, wl, inp):
+        self.lsa, self.torch, self.wl, self.inp = lsa, torch, wl, inp
+        dev = inp["q_idx"].device
+        B, n_q, L = wl.B, wl.n_q, wl.L
+        kw = dict(two_stage=wl.two_stage, block_size=wl.block_size, n_keep=wl.n_keep)
+        ws_bytes = lsa.lsa_forward_workspace_size(inp, wl.k, **kw)
+        self.rows, self.split = lsa.lsa_forward_plan(inp, wl.k, ws_bytes, **kw)
+        if n_q == 1:
+            self.chunks = [(b0, min(self.rows, B - b0), 0, 1) for b0 in range(0, B, self.rows)]
+        else:
+            self.chunks = [(b, 1, i0, min(self.rows, n_q - i0)) for b in range(B) for i0 in range(0, n_q, self.rows)]
+        self.ld = ((L + 63) // 64) * 64 if not wl.two_stage else wl.n_keep * wl.block_size
+        self.scores = torch.empty((self.rows * self.ld,), dtype=torch.int32, device=dev)
+        self.idx = torch.empty((B, n_q, wl.k), dtype=torch.int32, device=dev)
+        self.count = torch.empty((B, n_q), dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(inp["q"])
+        self.lse = torch.empty((B, n_q, wl.H_q), dtype=torch.float32, device=dev)
+        if wl.two_stage:
+            self.n_blocks = L // wl.block_size
+            self.reps = torch.empty((B, self.n_blocks, wl.d_I), dtype=torch.int32, device=dev)
+            self.kept = torch.empty((B, n_q, wl.n_keep), dtype=torch.int32, device=dev)
+        import ctypes as C
+        Lb = lsa.lib()
+        nb = C.c_size_t(0)
+        Lb.lsa_sparse_attn_workspace_size(1, self.rows, wl.H_q, wl.d, wl.k, self.split, C.byref(nb))
+        self.attn_ws = torch.empty((max(nb.value, 16),), dtype=torch.uint8, device=dev)
+        if wl.two_stage:
+            Lb.lsa_block_prefilter_workspace_size(1, self.rows, self.n_blocks, wl.d_I, C.byref(nb))
+            self.pf_ws = torch.empty((max(nb.value, 16),), dtype=torch.uint8, device=dev)
+        self.names = (["block_reps", "block_prefilter", "index_scores", "topk", "sparse_attn"]
+                      if wl.two_stage else ["index_scores", "topk", "sparse_attn"])
+        self.steps = []   # per recorded step: list of (name, start_event, end_event)
+
+    def run(self, record: bool):
+        import ctypes as C
+        lsa, torch, wl, g = self.lsa, self.torch, self.wl, self.inp
+        L = lsa.lib()
+        stream = torch.cuda.current_stream()
+        st = C.c_void_p(stream.cuda_stream)
+        ev = []
+        last = [None]
+
+        def mark(name):
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                if name is not None:
+                    ev.append((name, last[0], e))
+                last[0] = e
+
+        ptr = lambda t: C.c_void_p(t.data_ptr())
+        mark(None)
+        if wl.two_stage:
+            rc = L.lsa_block_reps(ptr(g["k_idx"]), wl.B, wl.L, wl.d_I, wl.block_size, self.n_blocks, ptr(self.reps), st)
+            assert rc == 0, rc
+            mark("block_reps")
+        for (b0, nb, i0, ni) in self.chunks:
+            sl = lambda t: t[b0: b0 + nb, i0: i0 + ni]
+            kept = None
+            if wl.two_stage:
+                rc = L.lsa_block_prefilter(ptr(sl(g["q_idx"])), ptr(self.reps[b0: b0 + nb]), ptr(g["w"]), 0,
+                                           ptr(sl(g["q_pos"])), nb, ni, self.n_blocks, wl.H_I, wl.d_I,
+                                           wl.block_size, wl.n_keep, ptr(sl(self.kept)), None, ptr(self.pf_ws),
+                                           self.pf_ws.numel(), st)
+                assert rc == 0, rc
+                mark("block_prefilter")
+                kept = ptr(sl(self.kept))
+            rc = L.lsa_index_scores(ptr(sl(g["q_idx"])), ptr(g["k_idx"][b0: b0 + nb]), ptr(g["w"]), 0,
+                                    ptr(sl(g["q_pos"])), kept, wl.block_size, wl.n_keep, nb, ni, wl.L, wl.H_I,
+                                    wl.d_I, ptr(self.scores), self.ld, st)
+            assert rc == 0, rc
+            mark("index_scores")
+            rc = L.lsa_topk(ptr(self.scores), self.ld, ptr(sl(g["q_pos"])), kept, wl.block_size, wl.n_keep, nb, ni,
+                            wl.L, wl.k, ptr(sl(self.idx)), ptr(sl(self.count)), None, 0, st)
+            assert rc == 0, rc
+            mark("topk")
+            rc = L.lsa_sparse_attn(ptr(sl(g["q"])), ptr(g["k"][b0: b0 + nb]), ptr(g["v"][b0: b0 + nb]),
+                                   ptr(sl(self.idx)), nb, ni, wl.L, wl.H_q, wl.d, wl.k, wl.scale, self.split,
+                                   ptr(sl(self.out)), ptr(sl(self.lse)), ptr(self.attn_ws), self.attn_ws.numel(), st)
+            assert rc == 0, rc
+            mark("sparse_attn")
+        if record:
+            self.steps.append(ev)
+
+    def kernel_ms(self):
+        """Per call: mean total ms per step, launches per step, mean ms per launch."""
+        tot = {n: 0.0 for n in self.names}
+        cnt = {n: 0 for n in self.names}
+        for ev in self.steps:
+            for name, a, b in ev:
+                tot[name] += a.elapsed_time(b)
+                cnt[name] += 1
+        n_steps = max(1, len(self.steps))
+        return {n: {"ms_per_step": tot[n] / n_steps, "launches_per_step": cnt[n] / n_steps,
+                    "ms_per_launch": tot[n] / max(1, cnt[n])} for n in self.names}
+
+
+def algorithmic(wl):
+    """Algorithmic work of one step (what the method must compute / move), per kernel."""
+    B, n_q, H_I, d_I, H_q, d, k = wl.B, wl.n_q, wl.H_I, wl.d_I, wl.H_q, wl.d, wl.k
+    pos = [wl.q_pos0 + i for i in range(n_q)]
+    vis = [min(p, wl.L - 1) + 1 for p in pos]
+    if wl.two_stage:
+        bs, nk = wl.block_size, wl.n_keep
+        blk_pairs = sum(p // bs for p in pos) * B
+        tok_pairs = 0
+        for p in pos:
+            own = p // bs
+            n_full = min(nk - 1, own)
+            tok_pairs += n_full * bs + (p - own * bs + 1)
+        tok_pairs *= B
+        att_pairs = B * sum(min(k, c) for c in [min(nk - 1, p // bs) * bs + (p - (p // bs) * bs + 1) for p in pos])
+        return {
+            "index_ops": 2 * H_I * d_I * tok_pairs,
+            "block_ops": 2 * H_I * d_I * blk_pairs,
+            "attn_flops": 4 * H_q * d * att_pairs,
+            "attn_gather_bytes": att_pairs * 2 * d * 2,
+            "tok_pairs": tok_pairs,
+        }
+    pairs = B * sum(vis)
+    att_pairs = B * sum(min(k, c) for c in vis)
+    return {
+        "index_ops": 2 * H_I * d_I * pairs,
+        "index_bytes": B * (wl.L * d_I + n_q * H_I * d_I),   # every index key + the index queries, read once
+        "topk_bytes": 4 * pairs,                             # every score read once
+        "attn_flops": 4 * H_q * d * att_pairs,
+        "attn_gather_bytes": att_pairs * 2 * d * 2,          # one K and one V bf16 row per listed key
+        "pairs": pairs,
+    }
+
+
+def cpu_baseline(wl, inp, budget_s=10.0):
+    """The oracle as it stands, on a bounded sample of the same workload's rows."""
+    import numpy as np
+    import oracle
+    import synthetic
+    rows = synthetic.checked_rows(wl, n_random=56)
+    done = 0
+    t_work = 0.0
+    batches = {}
+    # cycle over the seeded rows until about budget_s of oracle time has been spent
+    order = [rows[t % len(rows)] for t in range(100000)]
+    for (b, i) in order:
+        if b not in batches:
+            batches[b] = {
+                "k_idx": inp["k_idx"][b].cpu().numpy(),
+                "k": inp["k"][b].float().cpu().numpy().astype(np.float64),
+                "v": inp["v"][b].float().cpu().numpy().astype(np.float64),
+            }
+            if len(batches) > 3:
+                batches.pop(next(iter(batches)))
+        hb = batches[b]
+        qi = inp["q_idx"][b, i].cpu().numpy()
+        q = inp["q"][b, i].float().cpu().numpy().astype(np.float64)
+        w = inp["w"].cpu().numpy()
+        p = int(inp["q_pos"][b, i])
+        t0 = time.perf_counter()
+        oracle.forward_row(qi, hb["k_idx"], w, p, wl.k, q_row=q, k_cache=hb["k"], v_cache=hb["v"],
+                           scale=wl.scale, two_stage=wl.two_stage, block_size=wl.block_size, n_keep=wl.n_keep)
+        t_work += time.perf_counter() - t0
+        done += 1
+        if t_work > budget_s:
+            break
+    rate = done / t_work
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    unit = "tok/s" if wl.n_q == 1 else "queries/s"
+    return {"value": rate, "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"{done} row evaluations cycling over {len(rows)} seeded rows of {wl.name} (incl. boundary "
+                      f"rows), {t_work:.1f}s of oracle time "
+                      f"(numpy fp64 BLAS, int64 scores); rate = rows / time"}
+
+
+def copy_calibration(torch, nbytes=1 << 30, reps=5):
+    """Plain device copy of a known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    a = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def measure(lsa, torch, wl, steps, warmup):
+    import synthetic
+    inp = synthetic.make_inputs(wl, torch.device("cuda:0"))
+    torch.cuda.synchronize()
+    step = Step(lsa, torch, wl, inp)
+    # the C-ABI sequence is the lsa_forward path: identical outputs
+    ref = lsa.lsa_forward(inp, k_top=wl.k, two_stage=wl.two_stage, block_size=wl.block_size, n_keep=wl.n_keep)
+    step.run(record=False)
+    torch.cuda.synchronize()
+    if not (torch.equal(ref["idx"], step.idx) and torch.equal(ref["out"], step.out)):
+        raise SystemExit("bench step differs from lsa_forward")
+    del ref
+    for _ in range(warmup):
+        step.run(record=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step.run(record=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
+    return inp, step, ms
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="time only this workload (no headline line)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU "
+              "sharding of the path is designed but not built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import learned_top_sparse_amd as lsa
+    import synthetic
+    lsa.lib()
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    if args.workload:
+        names = list(synthetic.WORKLOADS) if args.workload == "all" else [args.workload]
+        for name in names:
+            wl = synthetic.WORKLOADS[name]
+            inp, step, ms = measure(lsa, torch, wl, args.steps, args.warmup)
+            print(json.dumps({"workload": wl.name, "ms_per_step": ms, "kernel_ms": step.kernel_ms(),
+                              "algorithmic": algorithmic(wl)}), flush=True)
+            del inp, step
+            torch.cuda.empty_cache()
+        return
+
+    # ---- headline: decode at 128K
+    wl = synthetic.WORKLOADS["decode_128k"]
+    inp, step, ms = measure(lsa, torch, wl, args.steps, args.warmup)
+    kms = step.kernel_ms()
+    alg = algorithmic(wl)
+    tok_s = wl.B * wl.n_q / (ms * 1e-3)
+    idx_ms = kms["index_scores"]["ms_per_launch"]
+    launches = kms["index_scores"]["launches_per_step"]
+    achieved = alg["index_bytes"] / launches / (idx_ms * 1e-3) / 1e9
+    roof_t_ms = max(alg["index_bytes"] + alg["attn_gather_bytes"], 0) / (HBM_PEAK_GBS * 1e9) * 1e3
+    res = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+bf16",
+        "data": "synthetic",
+        "config": {"workload": _describe(wl), "global_batch": wl.B, "seq_len": wl.L, "parallelism": "none"},
+        "roofline": {
+            "bound": "hbm", "kernel": "index_scores (decode scan, idx_direct_kernel)",
+            "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": alg["index_bytes"] / launches, "launch_ms": idx_ms,
+        },
+        "kernel_ms": kms,
+        "step_roofline_frac": roof_t_ms / ms,
+        "decode_attn": {
+            "achieved_GBs": alg["attn_gather_bytes"] / (kms["sparse_attn"]["ms_per_step"] * 1e-3) / 1e9,
+            "frac_hbm": alg["attn_gather_bytes"] / (kms["sparse_attn"]["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "gather_bytes": alg["attn_gather_bytes"],
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, inp)
+    del inp, step
+    torch.cuda.empty_cache()
+
+    # ---- prefill at 128K (two-stage chunk)
+    wp = synthetic.WORKLOADS["two_stage_128k"]
+    inp, step, ms_p = measure(lsa, torch, wp, args.steps, args.warmup)
+    kp = step.kernel_ms()
+    ap_ = algorithmic(wp)
+    res["prefill_128k"] = {
+        "workload": _describe(wp),
+        "value": wp.n_q / (ms_p * 1e-3), "unit": "queries/s", "ms_per_step": ms_p,
+        "kernel_ms": kp,
+        "roofline": {
+            "bound": "mfma", "kernel": "index_scores (token stage in kept blocks)",
+            "achieved": ap_["index_ops"] / (kp["index_scores"]["ms_per_step"] * 1e-3) / 1e12,
+            "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+            "frac": ap_["index_ops"] / (kp["index_scores"]["ms_per_step"] * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["prefill_128k"]["cpu_baseline"] = cpu_baseline(wp, inp, budget_s=10.0)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -208,9 +208,15 @@ typedef struct lsa_forward_args {
 } lsa_forward_args;
 
 /* Workspace for lsa_forward.  With a->chunk_rows = 0 it sizes score chunks of
-   at most ~1 GiB; lsa_forward then uses whatever chunk fits the ws it gets. */
+   at most ~4 GiB; lsa_forward then uses whatever chunk fits the ws it gets. */
 lsa_status lsa_forward_workspace_size(const lsa_forward_args* a, size_t* bytes);
 lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_bytes, void* stream);
+/* The launch plan lsa_forward uses with a workspace of ws_bytes: query rows per
+   score chunk (sequences per chunk when n_q == 1) and the attention split count.
+   Calling lsa_index_scores / lsa_topk / lsa_sparse_attn chunk by chunk with
+   these values (ld_scores = L_max rounded up to 64, or n_keep*block_size for
+   two_stage) reproduces lsa_forward's results bit for bit. */
+lsa_status lsa_forward_plan(const lsa_forward_args* a, size_t ws_bytes, int64_t* chunk_rows, int32_t* attn_split);
 
 #ifdef __cplusplus
 }

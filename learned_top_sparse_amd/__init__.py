@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     lsa_block_prefilter,
     lsa_block_reps,
     lsa_forward,
+    lsa_forward_plan,
     lsa_forward_workspace_size,
     lsa_index_scores,
     lsa_sparse_attn,

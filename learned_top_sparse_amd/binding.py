@@ -20,7 +20,7 @@ EXPORTED = [
     "lsa_status_string", "lsa_version", "lsa_index_scores", "lsa_block_reps",
     "lsa_block_prefilter_workspace_size", "lsa_block_prefilter", "lsa_topk_workspace_size",
     "lsa_topk", "lsa_sparse_attn_workspace_size", "lsa_sparse_attn",
-    "lsa_forward_workspace_size", "lsa_forward",
+    "lsa_forward_workspace_size", "lsa_forward", "lsa_forward_plan",
 ]
 
 P = C.c_void_p
@@ -74,6 +74,7 @@ def lib():
         L.lsa_sparse_attn.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, C.c_float, I32, P, P, P, SZ, P]
         L.lsa_forward_workspace_size.argtypes = [C.POINTER(ForwardArgs), C.POINTER(SZ)]
         L.lsa_forward.argtypes = [C.POINTER(ForwardArgs), P, SZ, P]
+        L.lsa_forward_plan.argtypes = [C.POINTER(ForwardArgs), SZ, C.POINTER(I64), C.POINTER(I32)]
         for name in EXPORTED:
             if name not in ("lsa_status_string", "lsa_version"):
                 getattr(L, name).restype = C.c_int
@@ -267,6 +268,16 @@ def lsa_forward_workspace_size(inp: dict, k_top: int, two_stage: bool = False, b
     nb = SZ(0)
     _check("lsa_forward_workspace_size", lib().lsa_forward_workspace_size(C.byref(a), C.byref(nb)))
     return nb.value
+
+
+def lsa_forward_plan(inp: dict, k_top: int, ws_bytes: int, two_stage: bool = False, block_size: int = 128,
+                     n_keep: int = 64, attn_split: int = 0, chunk_rows: int = 0):
+    """(rows per chunk, attention split) that lsa_forward uses with ws_bytes of workspace."""
+    dummy = {"idx": inp["q_pos"], "out": inp["q"]}
+    a = _forward_args(inp, k_top, two_stage, block_size, n_keep, None, attn_split, chunk_rows, dummy)
+    rows, split = I64(0), I32(0)
+    _check("lsa_forward_plan", lib().lsa_forward_plan(C.byref(a), ws_bytes, C.byref(rows), C.byref(split)))
+    return rows.value, split.value
 
 
 def lsa_forward(inp: dict, k_top: int, two_stage: bool = False, block_size: int = 128, n_keep: int = 64,

@@ -30,7 +30,7 @@ inline int flat_span(int32_t L_max, bool direct) {
 // automatic split count of the sparse attention
 inline int attn_split_auto(long long rows, int32_t k_top) {
   const int n_tiles = (k_top + 31) / 32;
-  if (rows >= 2048) return 1;
+  if (rows >= 512) return 1;
   long long s = (2048 + rows - 1) / rows;
   return (int)std::max<long long>(1, std::min<long long>(s, n_tiles));
 }
@@ -342,6 +342,23 @@ size_t chunk_bytes(const lsa_forward_args* a, const FwdPlan& p, long long rows) 
 
 long long total_rows(const lsa_forward_args* a) { return a->n_q == 1 ? (long long)a->B : (long long)a->n_q; }
 
+constexpr long long kChunkBudget = 4ll << 30;  // default score-chunk budget (bytes)
+
+// rows per chunk for a workspace of ws_bytes (0 if even one row does not fit)
+long long plan_rows(const lsa_forward_args* a, const FwdPlan& p, size_t ws_bytes) {
+  const long long n_rows = total_rows(a);
+  long long rows = a->chunk_rows > 0 ? std::min<long long>(a->chunk_rows, n_rows) : n_rows;
+  if (chunk_bytes(a, p, rows) <= ws_bytes) return rows;
+  if (a->chunk_rows > 0 || chunk_bytes(a, p, 1) > ws_bytes) return 0;
+  long long lo = 1, hi = rows;
+  while (lo < hi) {
+    const long long mid = (lo + hi + 1) / 2;
+    if (chunk_bytes(a, p, mid) <= ws_bytes) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 }  // namespace
 
 LSA_API lsa_status lsa_forward_workspace_size(const lsa_forward_args* a, size_t* bytes) {
@@ -353,7 +370,7 @@ LSA_API lsa_status lsa_forward_workspace_size(const lsa_forward_args* a, size_t*
     return LSA_OK;
   }
   const FwdPlan p = plan_forward(a);
-  long long rows = a->chunk_rows > 0 ? a->chunk_rows : std::max<long long>(1, (1ll << 30) / p.per_row);
+  long long rows = a->chunk_rows > 0 ? a->chunk_rows : std::max<long long>(1, kChunkBudget / p.per_row);
   rows = std::min(rows, total_rows(a));
   *bytes = chunk_bytes(a, p, rows);
   return LSA_OK;
@@ -369,18 +386,9 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
   const long long n_rows = total_rows(a);
 
   // rows per chunk: requested, else the most that fit
-  long long rows = a->chunk_rows > 0 ? std::min<long long>(a->chunk_rows, n_rows) : n_rows;
-  if (chunk_bytes(a, p, rows) > ws_bytes) {
-    if (a->chunk_rows > 0) return LSA_ERR_WORKSPACE;
-    long long lo = 1, hi = rows;
-    if (chunk_bytes(a, p, 1) > ws_bytes || !ws) return LSA_ERR_WORKSPACE;
-    while (lo < hi) {
-      const long long mid = (lo + hi + 1) / 2;
-      if (chunk_bytes(a, p, mid) <= ws_bytes) lo = mid;
-      else hi = mid - 1;
-    }
-    rows = lo;
-  }
+  const long long rows = plan_rows(a, p, ws_bytes);
+  if (rows == 0 || (!ws && chunk_bytes(a, p, rows) > 0)) return LSA_ERR_WORKSPACE;
+  (void)n_rows;
 
   // workspace carve-up
   char* base = static_cast<char*>(ws);
@@ -489,5 +497,23 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
       }
     }
   }
+  return LSA_OK;
+}
+
+LSA_API lsa_status lsa_forward_plan(const lsa_forward_args* a, size_t ws_bytes, int64_t* chunk_rows,
+                                    int32_t* attn_split) {
+  if (!chunk_rows || !attn_split) return LSA_ERR_INVALID_ARG;
+  lsa_status st = check_forward(a);
+  if (st != LSA_OK) return st;
+  if ((long long)a->B * a->n_q == 0) {
+    *chunk_rows = 0;
+    *attn_split = 1;
+    return LSA_OK;
+  }
+  const FwdPlan p = plan_forward(a);
+  const long long rows = plan_rows(a, p, ws_bytes);
+  if (rows == 0) return LSA_ERR_WORKSPACE;
+  *chunk_rows = rows;
+  *attn_split = resolve_split(1, (int32_t)rows, a->k_top, a->attn_split);
   return LSA_OK;
 }
