@@ -75,6 +75,11 @@ class Step:
         if wl.two_stage:
             Lb.lsa_block_prefilter_workspace_size(1, self.rows, self.n_blocks, wl.d_I, C.byref(nb))
             self.pf_ws = torch.empty((max(nb.value, 16),), dtype=torch.uint8, device=dev)
+            self.topk_ws_bytes = 0
+        else:
+            Lb.lsa_topk_workspace_size(1, self.rows, L, wl.k, C.byref(nb))
+            self.topk_ws_bytes = nb.value
+        self.topk_ws = torch.empty((max(self.topk_ws_bytes, 16),), dtype=torch.uint8, device=dev)
         self.names = (["block_reps", "block_prefilter", "index_scores", "topk", "sparse_attn"]
                       if wl.two_stage else ["index_scores", "topk", "sparse_attn"])
         self.steps = []   # per recorded step: list of (name, start_event, end_event)
@@ -119,7 +124,8 @@ class Step:
             assert rc == 0, rc
             mark("index_scores")
             rc = L.lsa_topk(ptr(self.scores), self.ld, ptr(sl(g["q_pos"])), kept, wl.block_size, wl.n_keep, nb, ni,
-                            wl.L, wl.k, ptr(sl(self.idx)), ptr(sl(self.count)), None, 0, st)
+                            wl.L, wl.k, ptr(sl(self.idx)), ptr(sl(self.count)), ptr(self.topk_ws),
+                            self.topk_ws_bytes, st)
             assert rc == 0, rc
             mark("topk")
             rc = L.lsa_sparse_attn(ptr(sl(g["q"])), ptr(g["k"][b0: b0 + nb]), ptr(g["v"][b0: b0 + nb]),

@@ -143,7 +143,10 @@ lsa_status lsa_block_prefilter(const int8_t* q_idx, const int32_t* reps, const i
  * scores[(b*n_q+i)*ld_scores + j]; two-stage mode the compact slots written by
  * lsa_index_scores with kept_blocks (keys <= q_pos and < L_max of listed blocks).
  *   count  optional int32 [B, n_q] = number of indices written (or NULL).
- * Supported: 1 <= k <= 4096.  Workspace: lsa_topk_workspace_size.
+ * Supported: 1 <= k <= 4096.  Workspace: lsa_topk_workspace_size returns a
+ * nonzero size when few long flat rows are better split over several
+ * workgroups each (decode-shaped calls); with a smaller or NULL workspace the
+ * one-workgroup-per-row algorithm runs instead.  Results are identical.
  */
 lsa_status lsa_topk_workspace_size(int32_t B, int32_t n_q, int32_t L_max, int32_t k, size_t* bytes);
 lsa_status lsa_topk(const int32_t* scores, int64_t ld_scores, const int32_t* q_pos,

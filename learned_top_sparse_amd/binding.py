@@ -191,7 +191,7 @@ def lsa_block_prefilter(q_idx, reps, w, q_pos, block_size: int, n_keep: int, ret
     return (kept, bs) if return_scores else kept
 
 
-def lsa_topk(scores, q_pos, k: int, L_max: int, kept_blocks=None, block_size: int = 0):
+def lsa_topk(scores, q_pos, k: int, L_max: int, kept_blocks=None, block_size: int = 0, use_ws: bool = True):
     """Exact top-k: (idx int32 [B, n_q, k] ascending and -1 padded, count int32 [B, n_q])."""
     dev = scores.device
     _need(scores, "scores", torch.int32)
@@ -205,9 +205,10 @@ def lsa_topk(scores, q_pos, k: int, L_max: int, kept_blocks=None, block_size: in
     count = torch.empty((B, n_q), dtype=torch.int32, device=dev)
     nb = SZ(0)
     _check("lsa_topk_workspace_size", lib().lsa_topk_workspace_size(B, n_q, L_max, k, C.byref(nb)))
-    ws = _workspace(nb.value, dev)
+    ws = _workspace(nb.value, dev) if use_ws else None
+    nbytes = nb.value if use_ws else 0
     st = lib().lsa_topk(_ptr(scores), ld, _ptr(q_pos), _ptr(kept_blocks), block_size, n_keep, B, n_q, L_max, k,
-                        _ptr(idx), _ptr(count), _ptr(ws), nb.value, _stream(dev))
+                        _ptr(idx), _ptr(count), _ptr(ws), nbytes, _stream(dev))
     _check("lsa_topk", st)
     return idx, count
 

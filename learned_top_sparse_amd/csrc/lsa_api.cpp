@@ -27,12 +27,14 @@ inline int flat_span(int32_t L_max, bool direct) {
   return L_max > 65536 ? 8192 : 4096;
 }
 
-// automatic split count of the sparse attention
+// automatic split count of the sparse attention: with few rows, cut each list so the
+// launch holds about 2048 waves, all resident at once (at least one 32-key tile per wave)
 inline int attn_split_auto(long long rows, int32_t k_top) {
-  const int n_tiles = (k_top + 31) / 32;
-  if (rows >= 512) return 1;
-  long long s = (2048 + rows - 1) / rows;
-  return (int)std::max<long long>(1, std::min<long long>(s, n_tiles));
+  const long long n_tiles = (k_top + 31) / 32;
+  const long long max_split = std::max<long long>(1, n_tiles / lsa::ATTN_WAVES);
+  if (rows * lsa::ATTN_WAVES >= 2048) return 1;
+  const long long s = (2048 + rows * lsa::ATTN_WAVES - 1) / (rows * lsa::ATTN_WAVES);
+  return (int)std::max<long long>(1, std::min<long long>(s, max_split));
 }
 
 lsa_status check_index_args(const int8_t* q_idx, const int8_t* k_idx, const int32_t* w, const int32_t* q_pos,
@@ -184,7 +186,7 @@ LSA_API lsa_status lsa_block_prefilter(const int8_t* q_idx, const int32_t* reps,
 
 LSA_API lsa_status lsa_topk_workspace_size(int32_t B, int32_t n_q, int32_t L_max, int32_t k, size_t* bytes) {
   if (!bytes || B < 0 || n_q < 0 || L_max < 0 || k < 0) return LSA_ERR_INVALID_ARG;
-  *bytes = 0;
+  *bytes = lsa::topk_ws_bytes((long long)B * n_q, L_max);
   return LSA_OK;
 }
 
@@ -192,9 +194,8 @@ LSA_API lsa_status lsa_topk(const int32_t* scores, int64_t ld_scores, const int3
                             const int32_t* kept_blocks, int32_t block_size, int32_t n_keep, int32_t B, int32_t n_q,
                             int32_t L_max, int32_t k, int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
                             void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (B < 0 || n_q < 0 || L_max < 0) return LSA_ERR_INVALID_ARG;
+  if (((uintptr_t)ws) % 16 != 0) return LSA_ERR_WORKSPACE;
   if (k < 1) return LSA_ERR_INVALID_ARG;
   if (k > 4096) return LSA_ERR_UNSUPPORTED;
   if ((long long)B * n_q == 0) return LSA_OK;
@@ -219,6 +220,8 @@ LSA_API lsa_status lsa_topk(const int32_t* scores, int64_t ld_scores, const int3
   a.k = k;
   a.idx = idx;
   a.count = count;
+  a.ws = ws;
+  a.ws_bytes = ws_bytes;
   return hip_status(lsa::launch_topk(a, as_stream(stream)));
 }
 
@@ -226,7 +229,7 @@ static int resolve_split(int32_t B, int32_t n_q, int32_t k_top, int32_t n_split)
   const long long rows = (long long)B * n_q;
   const int n_tiles = (k_top + 31) / 32;
   if (n_split <= 0) return attn_split_auto(rows, k_top);
-  return std::max(1, std::min(n_split, n_tiles));
+  return std::max(1, std::min(std::min(n_split, n_tiles), 64));
 }
 
 static size_t attn_ws_bytes(long long rows, int32_t H_q, int32_t d, int split) {
@@ -337,6 +340,7 @@ size_t chunk_bytes(const lsa_forward_args* a, const FwdPlan& p, long long rows) 
   }
   const int split = resolve_split(1, (int32_t)rows, a->k_top, a->attn_split);
   s += attn_ws_bytes(rows, a->H_q, a->d, split);
+  if (!a->two_stage) s += align_up(lsa::topk_ws_bytes(rows, a->L_max));
   return s;
 }
 
@@ -414,6 +418,9 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
     }
   }
   void* attn_ws = base + off;
+  off += attn_ws_bytes(rows, a->H_q, a->d, resolve_split(1, (int32_t)rows, a->k_top, a->attn_split));
+  void* topk_ws = a->two_stage ? nullptr : static_cast<void*>(base + off);
+  const size_t topk_ws_size = a->two_stage ? 0 : lsa::topk_ws_bytes(rows, a->L_max);
 
   const int32_t d_I = a->d_I, H_I = a->H_I, H_q = a->H_q, d = a->d, L = a->L_max, kt = a->k_top;
   // one split count for every chunk, so no chunk needs more attention workspace than sized
@@ -478,6 +485,8 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
     ta.k = kt;
     ta.idx = ix;
     ta.count = cnt;
+    ta.ws = topk_ws;
+    ta.ws_bytes = topk_ws_size;
     if (lsa::launch_topk(ta, s) != hipSuccess) return LSA_ERR_HIP;
     return run_attn(qq, kk, vv, ix, nb, ni, L, H_q, d, kt, a->scale, split, oo, ls, attn_ws, s);
   };

@@ -63,14 +63,28 @@ union Frag8 {
   v4u u;
 };
 
-// One 64-thread workgroup = one wave = one (row, split) unit.
-__global__ __launch_bounds__(64) void sparse_attn_kernel(
+// LDS ordering between lanes of one wave: LDS operations of a wave complete in
+// issue order, so keeping the compiler from moving them across this point is enough.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int WAVE_LDS = D * RSD;  // dwords of LDS per wave: the transposed V tile, later its partial state
+
+// A workgroup of NW waves handles one (row, split) unit: the split's 32-key tiles are
+// dealt to the waves round-robin, each wave keeps an online-softmax state for the 16
+// heads, and at the end the NW states are merged through LDS.  n_split == 1 writes
+// the bf16 output and LSE; otherwise a normalised fp32 partial and its LSE go to ws.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ idx, int n_q, int L_max, int H_q, int k_top, float scale_log2,
     int n_split, __bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws) {
-  __shared__ __attribute__((aligned(16))) u32 vt[D * RSD];
+  __shared__ __attribute__((aligned(16))) u32 lds[NW * WAVE_LDS];
 
-  const int lane = threadIdx.x, g = lane >> 4, r16 = lane & 15;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
   const long long unit = blockIdx.x;
   const long long row = unit / n_split;
   const int split = (int)(unit % n_split);
@@ -78,15 +92,16 @@ __global__ __launch_bounds__(64) void sparse_attn_kernel(
   const int32_t* jrow = idx + row * (long long)k_top;
   const __bf16* kb = k + (long long)b * L_max * D;
   const __bf16* vb = v + (long long)b * L_max * D;
+  u32* vt = lds + wave * WAVE_LDS;
 
-  // query heads as B fragments: lane (h = l&15, g) holds d = 32g + 8s .. +8 at step s
+  // query heads as B fragments: lane (h = l&15, g) holds d = 32s + 8g .. +8 at step s
   Frag8 Qb[4];
   {
     const bool hv = r16 < H_q;
-    const __bf16* qr = q + (row * H_q + (hv ? r16 : 0)) * D + 32 * g;
+    const __bf16* qr = q + (row * H_q + (hv ? r16 : 0)) * D + 8 * g;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if (hv) Qb[s].u = *(const v4u*)(qr + 8 * s);
+      if (hv) Qb[s].u = *(const v4u*)(qr + 32 * s);
       else Qb[s].u = v4u{0u, 0u, 0u, 0u};
     }
   }
@@ -100,7 +115,7 @@ __global__ __launch_bounds__(64) void sparse_attn_kernel(
   const int t_begin = (int)((long long)n_tiles * split / n_split);
   const int t_end = (int)((long long)n_tiles * (split + 1) / n_split);
 
-  for (int t = t_begin; t < t_end; ++t) {
+  for (int t = t_begin + wave; t < t_end; t += NW) {
     const int base = t * KT;
     // indices: keys (l&15) and 16+(l&15) for the K fragments, pair 2*(l&15)+{0,1} for V
     auto load_j = [&](int pos) -> int {
@@ -108,30 +123,42 @@ __global__ __launch_bounds__(64) void sparse_attn_kernel(
       const int j = jrow[pos];
       return (j >= 0 && j < L_max) ? j : -1;
     };
-    const int jA = load_j(base + r16), jB = load_j(base + 16 + r16);
-    const int j0 = load_j(base + 2 * r16), j1 = load_j(base + 2 * r16 + 1);
+    int jA = load_j(base + r16), jB = load_j(base + 16 + r16);
+    int j0 = load_j(base + 2 * r16), j1 = load_j(base + 2 * r16 + 1);
     const unsigned long long vA = __ballot(jA >= 0), vB = __ballot(jB >= 0);
     if ((vA | vB) == 0ull) continue;
+    // Entries without a key read the rows of a listed key of this tile instead: loads
+    // stay unconditional (all in flight together), the key's score is masked to -inf,
+    // so its weight is exactly 0 and the borrowed V row (finite, or listed anyway)
+    // adds nothing.
+    {
+      const int src = vA ? __ffsll((long long)vA) - 1 : __ffsll((long long)vB) - 1;
+      const int jfill = vA ? __shfl(jA, src) : __shfl(jB, src);
+      jA = jA < 0 ? jfill : jA;
+      jB = jB < 0 ? jfill : jB;
+      j0 = j0 < 0 ? jfill : j0;
+      j1 = j1 < 0 ? jfill : j1;
+    }
 
-    // gathers
+    // gathers: every load instruction reads whole 64-byte pieces of 16 rows
     Frag8 Ka[2][4];
     {
-      const __bf16* ra = kb + (long long)(jA < 0 ? 0 : jA) * D + 32 * g;
-      const __bf16* rb = kb + (long long)(jB < 0 ? 0 : jB) * D + 32 * g;
+      const __bf16* ra = kb + (long long)jA * D + 8 * g;
+      const __bf16* rb = kb + (long long)jB * D + 8 * g;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        Ka[0][s].u = (jA >= 0) ? *(const v4u*)(ra + 8 * s) : v4u{0u, 0u, 0u, 0u};
-        Ka[1][s].u = (jB >= 0) ? *(const v4u*)(rb + 8 * s) : v4u{0u, 0u, 0u, 0u};
+        Ka[0][s].u = *(const v4u*)(ra + 32 * s);
+        Ka[1][s].u = *(const v4u*)(rb + 32 * s);
       }
     }
     v4u V0[4], V1[4];  // rows j0 / j1, d = 8g + 32m .. +8
     {
-      const __bf16* r0 = vb + (long long)(j0 < 0 ? 0 : j0) * D + 8 * g;
-      const __bf16* r1 = vb + (long long)(j1 < 0 ? 0 : j1) * D + 8 * g;
+      const __bf16* r0 = vb + (long long)j0 * D + 8 * g;
+      const __bf16* r1 = vb + (long long)j1 * D + 8 * g;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        V0[m] = (j0 >= 0) ? *(const v4u*)(r0 + 32 * m) : v4u{0u, 0u, 0u, 0u};
-        V1[m] = (j1 >= 0) ? *(const v4u*)(r1 + 32 * m) : v4u{0u, 0u, 0u, 0u};
+        V0[m] = *(const v4u*)(r0 + 32 * m);
+        V1[m] = *(const v4u*)(r1 + 32 * m);
       }
     }
 
@@ -144,8 +171,8 @@ __global__ __launch_bounds__(64) void sparse_attn_kernel(
       for (int s = 0; s < 4; ++s) S[mt] = mfma_bf16(Ka[mt][s].v, Qb[s].v, S[mt]);
     }
 
-    // V^T into LDS: dword [d][kp] = (V[2kp][d], V[2kp+1][d]), d = 8g + 32m + e
-    __syncthreads();  // previous tile's reads of vt are done
+    // V^T into this wave's LDS tile: dword [d][kp] = (V[2kp][d], V[2kp+1][d]), d = 8g + 32m + e
+    wave_lds_sync();  // previous tile's reads of vt are done
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -196,7 +223,7 @@ __global__ __launch_bounds__(64) void sparse_attn_kernel(
                  pack_bf16(pv[6], pv[7])};
     }
 
-    __syncthreads();  // vt written
+    wave_lds_sync();  // vt written
     // O^T[d][h] += V^T[d][keys] P^T[keys][h]; A rows d = 16*dt + r16, keys 4g..4g+3, 16+4g..
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -209,60 +236,92 @@ __global__ __launch_bounds__(64) void sparse_attn_kernel(
     }
   }
 
+  // ---- merge the NW wave states through LDS: region of wave w = O[16][128] | m[16] | l[16]
   float l_tot = xhalf32_sumf(l_part);
   l_tot = xrow16_sumf(l_tot);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse_v = l_tot > 0.f ? (m_run + log2f(l_tot)) * LN2 : -INFINITY;
-  const int h = r16;
-  if (h >= H_q) return;
-  if (n_split == 1) {
-    __bf16* orow = out + (row * H_q + h) * D;
+  wave_lds_sync();
+  {
+    float* st = reinterpret_cast<float*>(vt);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const int d = 16 * dt + 4 * g;
-      v2u pk;
-      pk[0] = pack_bf16(O[dt][0] * inv, O[dt][1] * inv);
-      pk[1] = pack_bf16(O[dt][2] * inv, O[dt][3] * inv);
-      *(v2u*)(orow + d) = pk;
-    }
-    if (lse != nullptr && g == 0) lse[row * H_q + h] = lse_v;
-  } else {
-    float* po = ws + ((row * n_split + split) * H_q + h) * D;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int d = 16 * dt + 4 * g;
-      *(v4f*)(po + d) = O[dt] * inv;
+      *(v4f*)(st + r16 * D + d) = O[dt];
     }
     if (g == 0) {
-      float* pl = ws + (long long)gridDim.x * H_q * D;  // lse parts after the outputs
-      pl[(row * n_split + split) * H_q + h] = lse_v;
+      st[16 * D + r16] = m_run;
+      st[16 * D + 16 + r16] = l_tot;
+    }
+  }
+  __syncthreads();
+  const float* all = reinterpret_cast<const float*>(lds);
+  for (int e = threadIdx.x; e < 16 * D; e += 64 * NW) {
+    const int h = e / D, d = e % D;
+    if (h >= H_q) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, all[w * WAVE_LDS + 16 * D + h]);
+    float num = 0.f, den = 0.f;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float* st = all + w * WAVE_LDS;
+        const float mw = st[16 * D + h];
+        const float sc = mw > -INFINITY ? exp2f(mw - M) : 0.f;
+        num += sc * st[h * D + d];
+        den += sc * st[16 * D + 16 + h];
+      }
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    const float lse_v = den > 0.f ? (M + log2f(den)) * LN2 : -INFINITY;
+    if (n_split == 1) {
+      reinterpret_cast<unsigned short*>(out)[(row * H_q + h) * D + d] = (unsigned short)bf16_bits(num * inv);
+      if (lse != nullptr && d == 0) lse[row * H_q + h] = lse_v;
+    } else {
+      ws[((row * n_split + split) * H_q + h) * D + d] = num * inv;
+      if (d == 0) ws[(long long)gridDim.x * H_q * D + (row * n_split + split) * H_q + h] = lse_v;
     }
   }
 }
 
-// Merge of the n_split partial results of each (row, head) by log-sum-exp.
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ ws, long long n_units,
+// Merge of the n_split partial results of each row by log-sum-exp: one workgroup
+// per row, 8 outputs per thread, weights computed once per (split, head) in LDS.
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ ws, long long n_units,
                                                           int n_split, int H_q, __bf16* __restrict__ out,
                                                           float* __restrict__ lse) {
-  const long long rh = blockIdx.x;  // row * H_q + h
-  const long long row = rh / H_q;
-  const int h = (int)(rh % H_q);
-  const int d = threadIdx.x;
-  const float* pl = ws + n_units * H_q * D;
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pl[(row * n_split + s) * H_q + h]);
-  float num = 0.f, den = 0.f;
-  if (M > -INFINITY) {
+  __shared__ float wgt[64 * 16];
+  __shared__ float Mh[16], inv_den[16];
+  const long long row = blockIdx.x;
+  const float* pl = ws + n_units * H_q * D + row * n_split * H_q;  // lse parts of this row [split][h]
+  const int tid = threadIdx.x;
+  if (tid < H_q) {
+    float M = -INFINITY;
+    for (int s = 0; s < n_split; ++s) M = fmaxf(M, pl[s * H_q + tid]);
+    float den = 0.f;
     for (int s = 0; s < n_split; ++s) {
-      const float ls = pl[(row * n_split + s) * H_q + h];
-      const float wgt = expf(ls - M);
-      den += wgt;
-      num += wgt * ws[((row * n_split + s) * H_q + h) * D + d];
+      const float ls = pl[s * H_q + tid];
+      const float w = (M > -INFINITY && ls > -INFINITY) ? expf(ls - M) : 0.f;
+      wgt[s * 16 + tid] = w;
+      den += w;
     }
+    Mh[tid] = M;
+    inv_den[tid] = den > 0.f ? 1.f / den : 0.f;
+    if (lse != nullptr) lse[row * H_q + tid] = den > 0.f ? M + logf(den) : -INFINITY;
   }
-  const float o = den > 0.f ? num / den : 0.f;
-  out[rh * D + d] = (__bf16)o;
-  if (lse != nullptr && d == 0) lse[rh] = den > 0.f ? M + logf(den) : -INFINITY;
+  __syncthreads();
+  const int n_out = H_q * D;
+  for (int e0 = tid * 4; e0 < n_out; e0 += 256 * 4) {
+    const int h = e0 / D;
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < n_split; ++s) {
+      const v4f x = *(const v4f*)(ws + (row * n_split + s) * n_out + e0);
+      acc += x * wgt[s * 16 + h];
+    }
+    acc *= inv_den[h];
+    v2u pk;
+    pk[0] = pack_bf16(acc[0], acc[1]);
+    pk[1] = pack_bf16(acc[2], acc[3]);
+    *(v2u*)(out + row * n_out + e0) = pk;
+  }
 }
 
 }  // namespace
@@ -271,13 +330,13 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
   const long long rows = (long long)a.B * a.n_q;
   if (rows == 0) return hipSuccess;
   const long long units = rows * a.n_split;
-  hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)units), dim3(64), 0, st, (const __bf16*)a.q,
-                     (const __bf16*)a.k, (const __bf16*)a.v, a.idx, a.n_q, a.L_max, a.H_q, a.k_top,
-                     a.scale * LOG2E, a.n_split, (__bf16*)a.out, a.lse, a.ws);
+  hipLaunchKernelGGL((sparse_attn_kernel<ATTN_WAVES>), dim3((unsigned)units), dim3(64 * ATTN_WAVES), 0, st,
+                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.idx, a.n_q, a.L_max, a.H_q,
+                     a.k_top, a.scale * LOG2E, a.n_split, (__bf16*)a.out, a.lse, a.ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(rows * a.H_q)), dim3(128), 0, st, a.ws, units,
-                     a.n_split, a.H_q, (__bf16*)a.out, a.lse);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)rows), dim3(256), 0, st, a.ws, units, a.n_split, a.H_q,
+                     (__bf16*)a.out, a.lse);
   return hipGetLastError();
 }
 

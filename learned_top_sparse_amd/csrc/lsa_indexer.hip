@@ -18,9 +18,11 @@
 namespace lsa {
 
 // 16-byte chunk of the d_I bytes supplied by lane row g at K-step ks.  A and B
-// use the same assignment, so the product is the full dot product.
+// use the same assignment, so the product is the full dot product.  At one K-step
+// the four lane rows read four consecutive chunks, so every load instruction takes
+// whole 64-byte pieces of its 16 key rows.
 template <int D>
-__device__ __forceinline__ int kchunk(int g, int ks) { return g * (D / 64) + ks; }
+__device__ __forceinline__ int kchunk(int g, int ks) { return ks * 4 + g; }
 
 // XOR swizzle of 16-byte chunk c of row r in an LDS key tile whose rows are RB
 // bytes: 8 consecutive rows read at one logical chunk hit 8 distinct bank groups,
@@ -60,20 +62,21 @@ template <int D, int MT>
 __device__ __forceinline__ void load_query(const int8_t* __restrict__ q_idx, const int32_t* __restrict__ w,
                                            int w_per_query, long long row, int H_I, bool valid,
                                            v4i (&A)[MT][D / 64], int (&wt)[MT][4]) {
+  // Loads are unconditional (clamped to a valid head) so they are all in flight at
+  // once; a padding head gets weight 0, which cancels whatever its row produces.
   const int lane = lane_id(), g = lane >> 4, r16 = lane & 15;
   const int32_t* wr = w + (w_per_query ? row * H_I : 0);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int h = 16 * mt + r16;
-    const bool ok = valid && h < H_I;
+    const int h = min(16 * mt + r16, H_I - 1);
     const int8_t* qr = q_idx + (row * H_I + h) * D;
 #pragma unroll
-    for (int ks = 0; ks < D / 64; ++ks)
-      A[mt][ks] = ok ? *(const v4i*)(qr + 16 * kchunk<D>(g, ks)) : v4i{0, 0, 0, 0};
+    for (int ks = 0; ks < D / 64; ++ks) A[mt][ks] = *(const v4i*)(qr + 16 * kchunk<D>(g, ks));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int hh = 16 * mt + 4 * g + e;
-      wt[mt][e] = (valid && hh < H_I) ? wr[hh] : 0;
+      const int wv = wr[min(hh, H_I - 1)];
+      wt[mt][e] = (valid && hh < H_I) ? wv : 0;
     }
   }
 }
@@ -128,8 +131,10 @@ __global__ __launch_bounds__(256, 2) void idx_flat_kernel(
   auto gload = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
-      const int cid = tid + 256 * u, r = cid / CH, c = cid % CH, j = j0 + r;
-      stage[u] = (j < L_max) ? *(const v4i*)(kb + (long long)j * D + 16 * c) : v4i{0, 0, 0, 0};
+      // rows past the cache are clamped, not skipped: their scores are never stored, and
+      // unconditional loads keep every load of the tile in flight at once
+      const int cid = tid + 256 * u, r = cid / CH, c = cid % CH, j = min(j0 + r, L_max - 1);
+      stage[u] = *(const v4i*)(kb + (long long)j * D + 16 * c);
     }
   };
   auto swrite = [&](int buf) {
@@ -241,17 +246,25 @@ __global__ __launch_bounds__(256) void idx_direct_kernel(
   };
 
   const int n_groups = (s_end - s_begin + 63) / 64;
-  for (int grp = wave; grp < n_groups; grp += 4) {
+  // B fragments of one 64-slot group (4 key tiles of 16)
+  auto load_group = [&](int grp, v4i (&Bf)[4][KS]) {
     const int sg = s_begin + 64 * grp;
-    v4i Bf[4][KS];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const int j = key_of(sg + 16 * nt + r16);
-      const int8_t* kr = kb + (long long)(j < 0 ? 0 : j) * D;
+      // a slot without a key reads key 0: its column's score is never stored, and the
+      // unconditional loads stay in flight together
+      const int j = max(key_of(sg + 16 * nt + r16), 0);
+      const int8_t* kr = kb + (long long)j * D;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        Bf[nt][ks] = (j >= 0) ? *(const v4i*)(kr + 16 * kchunk<D>(g, ks)) : v4i{0, 0, 0, 0};
+      for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
     }
+  };
+  // software pipeline: the next group's loads are in flight while this one is multiplied
+  v4i Bf[4][KS], Bn[4][KS];
+  if (wave < n_groups) load_group(wave, Bf);
+  for (int grp = wave; grp < n_groups; grp += 4) {
+    const int sg = s_begin + 64 * grp;
+    if (grp + 4 < n_groups) load_group(grp + 4, Bn);
     int part[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
@@ -272,6 +285,10 @@ __global__ __launch_bounds__(256) void idx_direct_kernel(
     const int res = reduce_scatter4(part);
     const int s = sg + 16 * g + r16;
     if (key_of(s) >= 0) scores[srow + s] = res;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = Bn[nt][ks];
   }
 }
 
@@ -361,8 +378,8 @@ __global__ __launch_bounds__(256, 2) void blk_scores_kernel(
   auto gload = [&](int m0) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
-      const int cid = tid + 256 * u, r = cid / CH, c = cid % CH, m = m0 + r;
-      stage[u] = (m < n_blocks) ? *(const v4i*)(lb + (long long)m * RB + 16 * c) : v4i{0, 0, 0, 0};
+      const int cid = tid + 256 * u, r = cid / CH, c = cid % CH, m = min(m0 + r, n_blocks - 1);
+      stage[u] = *(const v4i*)(lb + (long long)m * RB + 16 * c);
     }
   };
   auto swrite = [&](int buf) {

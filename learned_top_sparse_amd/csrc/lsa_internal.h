@@ -42,6 +42,8 @@ struct TopkArgs {
   int B, n_q, L_max, k;
   int32_t* idx;
   int32_t* count;
+  void* ws;          // optional: enables the several-workgroups-per-row path
+  size_t ws_bytes;
 };
 
 struct BlkSelArgs {
@@ -51,6 +53,9 @@ struct BlkSelArgs {
   int B, n_q, n_blocks, block_size, n_keep;
   int32_t* kept;
 };
+
+// waves per sparse-attention workgroup (each with its own 32-key tile state)
+constexpr int ATTN_WAVES = 4;
 
 struct AttnArgs {
   const void* q;
@@ -73,6 +78,8 @@ hipError_t launch_block_limbs(const int32_t* reps, int B, int n_blocks, int d_I,
 hipError_t launch_block_scores(const BlkArgs& a, hipStream_t st);
 hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+// workspace that lets lsa_topk split each row over several workgroups (0 = not used)
+size_t topk_ws_bytes(long long rows, int L_max);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
 
 }  // namespace lsa

@@ -30,21 +30,20 @@ namespace {
 
 constexpr int NBINS = 8192;
 constexpr int CAP = NBINS / 2;  // LDS list entries (slot, score), reusing the histogram storage
+constexpr int SEG = 8192;       // slots per workgroup in the several-workgroups-per-row path
 
 __device__ __forceinline__ unsigned okey(int s) { return (unsigned)s ^ 0x80000000u; }
 
 // Monotone 13-bit bin: non-negative scores map to 4096 + g(s), negative ones to
-// 4095 - g(~s), where g keeps the exponent and the top 7 mantissa bits.
+// 4095 - g(~s), where g keeps the exponent and the top 7 mantissa bits:
+//   u = |s| folded (s ^ sign), shift = max(0, 24 - clz(u)), g = (shift << 7) + (u >> shift).
+// For u < 128 this is u itself; above, each power of two is split into 128 bins.
 __device__ __forceinline__ int coarse_bin(int s) {
-  const unsigned u = s >= 0 ? (unsigned)s : ~(unsigned)s;
-  int gv;
-  if (u < 128u) {
-    gv = (int)u;
-  } else {
-    const int e = 31 - __clz((int)u);
-    gv = ((e - 6) << 7) + (int)((u >> (e - 7)) & 127u);
-  }
-  return s >= 0 ? 4096 + gv : 4095 - gv;
+  const int sign = s >> 31;
+  const unsigned u = (unsigned)(s ^ sign);
+  const int shift = max(0, 24 - (int)__clz((int)(u | 1u)));
+  const int gv = (shift << 7) + (int)(u >> shift);
+  return (gv ^ sign) + 4096;
 }
 
 // Ordered compaction over positions [0, n): pred(pos, payload&) selects; emit(rank,
@@ -98,9 +97,10 @@ __device__ __forceinline__ int ordered_compact(int n, int* wcnt, Pred pred, Emit
 // sets *need_eq to how many entries equal to T are selected.  All threads call.
 template <int NT, int V, typename Pred>
 __device__ __forceinline__ unsigned radix_select32(int n, int need, int* h256, int* scan_tmp, int* sh,
-                                                   Pred pred, int* need_eq) {
-  unsigned pref = 0u, pmask = 0u;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+                                                   Pred pred, int* need_eq, int shift0 = 24, unsigned pref0 = 0u,
+                                                   unsigned pmask0 = 0u) {
+  unsigned pref = pref0, pmask = pmask0;
+  for (int shift = shift0; shift >= 0; shift -= 8) {
     for (int t = threadIdx.x; t < 256; t += NT) h256[t] = 0;
     __syncthreads();
     for (int base = 0; base < n; base += V * NT) {
@@ -134,14 +134,361 @@ __device__ __forceinline__ unsigned radix_select32(int n, int need, int* h256, i
   return pref;
 }
 
+// ---------------------------------------------------------------------------------
+// One query row as seen by the selection: candidate slots [0, n_slots), their
+// scores in global memory, and (two-stage mode) the kept-block table in LDS.
+template <bool KEPT>
+struct RowView {
+  const int32_t* srow;
+  const int* kept_s;  // KEPT: block table in LDS
+  int n_slots, p, bs;
+  bool vec;           // 16-byte aligned row: vector loads
+
+  __device__ __forceinline__ int key_of(int s) const {
+    if constexpr (KEPT) return kept_s[s / bs] * bs + s % bs;
+    else return s;
+  }
+  __device__ __forceinline__ bool valid(int s) const {
+    if (s >= n_slots) return false;
+    if constexpr (KEPT) {
+      const int blk = kept_s[s / bs];
+      return blk >= 0 && blk * bs + s % bs <= p;
+    } else {
+      return true;
+    }
+  }
+  // scores of slots s0..s0+3 (s0 % 4 == 0) and a 4-bit candidate mask
+  __device__ __forceinline__ unsigned load4(int s0, int (&sc)[4]) const {
+    if (vec && s0 + 3 < n_slots) {
+      const v4i x = *(const v4i*)(srow + s0);
+      sc[0] = x[0]; sc[1] = x[1]; sc[2] = x[2]; sc[3] = x[3];
+      if constexpr (!KEPT) return 0xFu;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sc[c] = (s0 + c < n_slots) ? srow[s0 + c] : 0;
+    }
+    unsigned m = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) m |= (valid(s0 + c) ? 1u : 0u) << c;
+    return m;
+  }
+};
+
+// Ordered compaction over positions [lo, hi) (lo % 4 == 0) taken four at a time:
+// f4(pos4, payload[4]) returns a 4-bit selection mask; emit(rank, pos, payload) gets
+// each selected position with its rank in position order, starting at `running`.
+// One barrier per 4*V*NT positions.  All threads call; returns running + count.
+template <int NT, int V, typename F4, typename Emit>
+__device__ __forceinline__ int ordered_compact4(int lo, int hi, int* wcnt, int running, F4 f4, Emit emit) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int parity = 0;
+  for (int base = lo; base < hi; base += 4 * V * NT) {
+    unsigned m[V];
+    int pl[V][4];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int pos4 = base + 4 * (v * NT + (int)threadIdx.x);
+      m[v] = 0;
+      if (pos4 < hi) {
+        m[v] = f4(pos4, pl[v]);
+        const int left = hi - pos4;
+        if (left < 4) m[v] &= (1u << left) - 1u;
+      }
+    }
+    unsigned long long bal[V][4];
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bal[v][c] = __ballot((m[v] >> c) & 1u);
+    int* wc = wcnt + parity * V * NW;
+    if (lane == 0) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        wc[v * NW + wave] = __popcll(bal[v][0]) + __popcll(bal[v][1]) + __popcll(bal[v][2]) + __popcll(bal[v][3]);
+    }
+    __syncthreads();
+    int off = running;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      int pre = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int c = wc[v * NW + w];
+        pre += (w < wave) ? c : 0;
+        tot += c;
+      }
+      if (m[v]) {
+        int r = off + pre;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r += lanes_below(bal[v][c]);
+        const int pos4 = base + 4 * (v * NT + (int)threadIdx.x);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if ((m[v] >> c) & 1u) emit(r++, pos4 + c, pl[v][c]);
+      }
+      off += tot;
+    }
+    running = off;
+    parity ^= 1;
+  }
+  __syncthreads();
+  return running;
+}
+
+// Coarse-bin histogram of the candidates in slots [lo, hi) into LDS `hist`.
+template <int NT, int V, bool KEPT>
+__device__ __forceinline__ void row_histogram(const RowView<KEPT> rv, int lo, int hi, int* hist) {
+  for (int base = lo; base < hi; base += 4 * V * NT) {
+    int sc[V][4];
+    unsigned m[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int s0 = base + 4 * (v * NT + (int)threadIdx.x);
+      m[v] = 0;
+      if (s0 < hi) {
+        m[v] = rv.load4(s0, sc[v]);
+        const int left = hi - s0;
+        if (left < 4) m[v] &= (1u << left) - 1u;
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((m[v] >> c) & 1u) atomicAdd(&hist[coarse_bin(sc[v][c])], 1);
+  }
+}
+
+// Bin b* holding the k-th best entry of `hist` (NBINS counters, LDS or global):
+// writes sh[4] = b*, sh[5] = entries in bins above b*, sh[6] = entries in b*.
 template <int NT>
+__device__ __forceinline__ void find_cut_bin(const int* hist, int k, int* scan_tmp, int* sh) {
+  constexpr int C = NBINS / NT;
+  const int hi = NBINS - (int)threadIdx.x * C;
+  int csum = 0;
+  // skewed visiting order: at step i lane t reads bin (i + t) % C of its range, so the
+  // lanes of a wave touch distinct LDS banks
+#pragma unroll 8
+  for (int i = 0; i < C; ++i) csum += hist[hi - C + ((i + (int)threadIdx.x) & (C - 1))];
+  int tot;
+  const int excl = block_exclusive_scan<NT>(csum, scan_tmp, &tot);
+  if (excl < k && excl + csum >= k) {
+    int acc = excl;
+    for (int b = hi - 1; b >= hi - C; --b) {
+      const int h = hist[b];
+      if (acc + h >= k) {
+        sh[4] = b;
+        sh[5] = acc;
+        sh[6] = h;
+        break;
+      }
+      acc += h;
+    }
+  }
+  __syncthreads();
+}
+
+// Steps 4-5 once the entries of bins >= b* sit in slot order in the LDS list
+// (lslot, lval; Lc entries): exact threshold inside b*, then the output row.
+template <int NT, bool KEPT>
+__device__ __forceinline__ void finish_from_list(const RowView<KEPT> rv, int Lc, int* lslot, int* lval, int bstar,
+                                                 int above, int k, int* wcnt, int* h256, int* scan_tmp, int* sh,
+                                                 int32_t* out) {
+  // bits shared by every entry of b*: the radix starts at the byte of the highest differing bit
+  unsigned mx = 0u, mn = 0xFFFFFFFFu;
+  for (int e = threadIdx.x; e < Lc; e += NT) {
+    const int sc = lval[e];
+    if (coarse_bin(sc) == bstar) {
+      const unsigned u = okey(sc);
+      mx = u > mx ? u : mx;
+      mn = u < mn ? u : mn;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    mx = max(mx, (unsigned)__shfl_xor((int)mx, o));
+    mn = min(mn, (unsigned)__shfl_xor((int)mn, o));
+  }
+  if (threadIdx.x == 0) {
+    sh[2] = 0;
+    sh[3] = -1;
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    atomicMax((unsigned*)&sh[2], mx);
+    atomicMin((unsigned*)&sh[3], mn);
+  }
+  __syncthreads();
+  mx = (unsigned)sh[2];
+  mn = (unsigned)sh[3];
+  __syncthreads();
+  int need_eq;
+  unsigned T;
+  if (mx == mn) {  // every entry of b* has the same score
+    T = mx;
+    need_eq = k - above;
+  } else {
+    const int hb = 31 - __clz((int)(mx ^ mn));
+    const int shift0 = (hb / 8) * 8;
+    const unsigned pmask0 = shift0 + 8 >= 32 ? 0u : ~((1u << (shift0 + 8)) - 1u);
+    T = radix_select32<NT, 4>(
+        Lc, k - above, h256, scan_tmp, sh,
+        [&](int e, int& sc) {
+          sc = lval[e];
+          return coarse_bin(sc) == bstar;
+        },
+        &need_eq, shift0, mx & pmask0, pmask0);
+  }
+  ordered_compact<NT, 4>(
+      Lc, wcnt, [&](int e, int&) { return okey(lval[e]) == T; },
+      [&](int r, int e, int) {
+        if (r >= need_eq) lslot[e] = -1 - lslot[e];  // equal to T but not taken
+      });
+  ordered_compact<NT, 4>(
+      Lc, wcnt, [&](int e, int&) { return lslot[e] >= 0 && okey(lval[e]) >= T; },
+      [&](int r, int e, int) {
+        if (r < k) out[r] = rv.key_of(lslot[e]);
+      });
+}
+
+// Exact selection straight from global memory (heavy ties): 8-bit radix passes
+// over the row, then a stable compaction chunk by chunk.  `scratch` holds NBINS ints.
+template <int NT, bool KEPT>
+__device__ __forceinline__ void fallback_select(const RowView<KEPT> rv, int k, int* scratch, int* wcnt, int* h256,
+                                                int* scan_tmp, int* sh, int32_t* out) {
+  constexpr int VF = NBINS / (4 * NT) < 4 ? NBINS / (4 * NT) : 4;  // chunk of 4*VF*NT <= NBINS positions
+  unsigned pref = 0u, pmask = 0u;
+  int need = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int t = threadIdx.x; t < 256; t += NT) h256[t] = 0;
+    __syncthreads();
+    for (int base = 0; base < rv.n_slots; base += 16 * NT) {
+      int sc[4][4];
+      unsigned m[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int s0 = base + 4 * (v * NT + (int)threadIdx.x);
+        m[v] = s0 < rv.n_slots ? rv.load4(s0, sc[v]) : 0u;
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if ((m[v] >> c) & 1u) {
+            const unsigned u = okey(sc[v][c]);
+            if ((u & pmask) == pref) atomicAdd(&h256[(u >> shift) & 255u], 1);
+          }
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    const int c = t < 256 ? h256[255 - t] : 0;
+    int tot;
+    const int excl = block_exclusive_scan<NT>(c, scan_tmp, &tot);
+    if (t < 256 && excl < need && excl + c >= need) {
+      sh[0] = 255 - t;
+      sh[1] = excl;
+    }
+    __syncthreads();
+    need -= sh[1];
+    pref |= (unsigned)sh[0] << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  const unsigned T = pref;
+  const int need_eq = need;
+  int eq_before = 0, written = 0;
+  for (int base = 0; base < rv.n_slots; base += 4 * VF * NT) {
+    const int hi = min(base + 4 * VF * NT, rv.n_slots);
+    int* eq_rank = scratch;  // indexed by position - base
+    const int neq = ordered_compact4<NT, VF>(
+        base, hi, wcnt, 0,
+        [&](int s0, int (&pl)[4]) {
+          int sc[4];
+          unsigned m = rv.load4(s0, sc), r = 0;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) r |= (((m >> c) & 1u) && okey(sc[c]) == T ? 1u : 0u) << c;
+          return r;
+        },
+        [&](int r, int s, int) { eq_rank[s - base] = r; });
+    const int wr = ordered_compact4<NT, VF>(
+        base, hi, wcnt, 0,
+        [&](int s0, int (&pl)[4]) {
+          int sc[4];
+          unsigned m = rv.load4(s0, sc), r = 0;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const unsigned u = okey(sc[c]);
+            const bool take = ((m >> c) & 1u) && (u > T || (u == T && eq_before + eq_rank[s0 + c - base] < need_eq));
+            r |= (take ? 1u : 0u) << c;
+          }
+          return r;
+        },
+        [&](int r, int s, int) {
+          if (written + r < k) out[written + r] = rv.key_of(s);
+        });
+    eq_before += neq;
+    written += wr;
+  }
+}
+
+// Rows with no more candidates than k: all of them, in order, then -1 padding.
+template <int NT, bool KEPT>
+__device__ __forceinline__ void select_all(const RowView<KEPT> rv, int n_valid, int k, int* wcnt, int32_t* out) {
+  ordered_compact4<NT, 4>(
+      0, rv.n_slots, wcnt, 0,
+      [&](int s0, int (&pl)[4]) {
+        unsigned m = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) m |= (rv.valid(s0 + c) ? 1u : 0u) << c;
+        return m;
+      },
+      [&](int r, int s, int) {
+        if (r < k) out[r] = rv.key_of(s);
+      });
+  for (int t = n_valid + (int)threadIdx.x; t < k; t += NT) out[t] = -1;
+}
+
+// Row setup shared by the kernels: position, slot count, kept table, candidate count.
+template <int NT, bool KEPT>
+__device__ __forceinline__ RowView<KEPT> make_row(const int32_t* scores, long long ld, const int32_t* q_pos,
+                                                  const int32_t* kept, int bs, int n_keep, int L_max, long long row,
+                                                  int* kept_s, int* scan_tmp, int* n_valid) {
+  RowView<KEPT> rv;
+  rv.p = min(q_pos[row], L_max - 1);
+  rv.srow = scores + row * ld;
+  rv.vec = (((uintptr_t)rv.srow) & 15u) == 0;
+  rv.bs = bs;
+  if constexpr (KEPT) {
+    for (int t = threadIdx.x; t < n_keep; t += NT) kept_s[t] = kept[row * n_keep + t];
+    __syncthreads();
+    rv.kept_s = kept_s;
+    rv.n_slots = (rv.p >= 0) ? n_keep * bs : 0;
+    int c = 0;
+    if ((int)threadIdx.x < n_keep && rv.p >= 0) {
+      const int blk = kept_s[threadIdx.x];
+      if (blk >= 0) c = max(0, min(bs, rv.p - blk * bs + 1));
+    }
+    int tot;
+    (void)block_exclusive_scan<NT>(c, scan_tmp, &tot);
+    *n_valid = tot;
+  } else {
+    rv.kept_s = nullptr;
+    rv.n_slots = max(rv.p + 1, 0);
+    *n_valid = rv.n_slots;
+  }
+  return rv;
+}
+
+// ---------------------------------------------------------------------------------
+// Single workgroup per row (many rows: prefill chunks).
+template <int NT, bool KEPT>
 __global__ __launch_bounds__(NT) void topk_kernel(const int32_t* __restrict__ scores, long long ld,
                                                   const int32_t* __restrict__ q_pos,
                                                   const int32_t* __restrict__ kept, int bs, int n_keep,
                                                   int L_max, int k, int32_t* __restrict__ idx,
                                                   int32_t* __restrict__ count) {
   constexpr int NW = NT / 64;
-  constexpr int VG = 16;  // entries per thread per pass over global memory
+  constexpr int VG = 4;  // groups of 4 slots per thread per pass
   __shared__ int lds_big[NBINS];  // histogram, then the candidate list (slots | scores)
   __shared__ int wcnt[2 * VG * NW];
   __shared__ int scan_tmp[NW + 1];
@@ -150,117 +497,31 @@ __global__ __launch_bounds__(NT) void topk_kernel(const int32_t* __restrict__ sc
   __shared__ int sh[8];
 
   const long long row = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int p = min(q_pos[row], L_max - 1);
-  const int32_t* srow = scores + row * ld;
   int32_t* out = idx + row * (long long)k;
-  const bool is_kept = kept != nullptr;
-
-  int n_slots;
   int n_valid;
-  if (is_kept) {
-    for (int t = tid; t < n_keep; t += NT) kept_s[t] = kept[row * n_keep + t];
-    __syncthreads();
-    n_slots = (p >= 0) ? n_keep * bs : 0;
-    int c = 0;
-    if (tid < n_keep && p >= 0) {
-      const int blk = kept_s[tid];
-      if (blk >= 0) c = max(0, min(bs, p - blk * bs + 1));
-    }
-    int tot;
-    (void)block_exclusive_scan<NT>(c, scan_tmp, &tot);
-    n_valid = tot;
-  } else {
-    n_slots = max(p + 1, 0);
-    n_valid = n_slots;
-  }
-
-  auto key_of = [&](int s) -> int {
-    if (!is_kept) return s;
-    return kept_s[s / bs] * bs + s % bs;
-  };
-  // candidate test + score load for slot s
-  auto cand = [&](int s, int& sc) -> bool {
-    if (is_kept) {
-      const int blk = kept_s[s / bs];
-      if (blk < 0) return false;
-      const int j = blk * bs + s % bs;
-      if (j > p) return false;
-    }
-    sc = srow[s];
-    return true;
-  };
-
-  if (count != nullptr && tid == 0) count[row] = min(k, n_valid);
-
-  // ---- fewer candidates than k: every candidate, in order, then -1 padding
+  const RowView<KEPT> rv = make_row<NT, KEPT>(scores, ld, q_pos, kept, bs, n_keep, L_max, row, kept_s, scan_tmp, &n_valid);
+  if (count != nullptr && threadIdx.x == 0) count[row] = min(k, n_valid);
   if (n_valid <= k) {
-    ordered_compact<NT, VG>(n_slots, wcnt, [&](int s, int& pl) { int sc; return cand(s, sc); },
-                            [&](int r, int s, int) {
-                              if (r < k) out[r] = key_of(s);
-                            });
-    for (int t = n_valid + tid; t < k; t += NT) out[t] = -1;
+    select_all<NT, KEPT>(rv, n_valid, k, wcnt, out);
     return;
   }
-
-  // ---- 1. coarse histogram
-  for (int t = tid; t < NBINS; t += NT) lds_big[t] = 0;
+  for (int t = threadIdx.x; t < NBINS; t += NT) lds_big[t] = 0;
   __syncthreads();
-  for (int base = 0; base < n_slots; base += VG * NT) {
-    int sc[VG];
-    bool ok[VG];
-#pragma unroll
-    for (int v = 0; v < VG; ++v) {
-      const int s = base + v * NT + tid;
-      sc[v] = 0;
-      ok[v] = (s < n_slots) && cand(s, sc[v]);
-    }
-#pragma unroll
-    for (int v = 0; v < VG; ++v)
-      if (ok[v]) atomicAdd(&lds_big[coarse_bin(sc[v])], 1);
-  }
+  row_histogram<NT, VG, KEPT>(rv, 0, rv.n_slots, lds_big);
   __syncthreads();
-
-  // ---- 2. bin holding the k-th best: thread t owns bins [NBINS-(t+1)C, NBINS-tC)
-  {
-    constexpr int C = NBINS / NT;
-    const int hi = NBINS - tid * C;
-    int csum = 0;
-#pragma unroll 8
-    for (int b = hi - C; b < hi; ++b) csum += lds_big[b];
-    int tot;
-    const int excl = block_exclusive_scan<NT>(csum, scan_tmp, &tot);
-    if (excl < k && excl + csum >= k) {
-      int acc = excl;
-      for (int b = hi - 1; b >= hi - C; --b) {
-        const int h = lds_big[b];
-        if (acc + h >= k) {
-          sh[4] = b;
-          sh[5] = acc;
-          sh[6] = h;
-          break;
-        }
-        acc += h;
-      }
-    }
-    __syncthreads();
-  }
+  find_cut_bin<NT>(lds_big, k, scan_tmp, sh);
   const int bstar = sh[4], above = sh[5], cnt_star = sh[6];
   __syncthreads();
-
-  unsigned T;
-  int need_eq;
   if (above + cnt_star <= CAP) {
-    // ---- 3. list of entries in bins >= b*, in slot order
     int* lslot = lds_big;
     int* lval = lds_big + CAP;
-    const int Lc = ordered_compact<NT, VG>(
-        n_slots, wcnt,
-        [&](int s, int& pl) {
-          int sc;
-          if (!cand(s, sc)) return false;
-          pl = sc;
-          return coarse_bin(sc) >= bstar;
+    const int Lc = ordered_compact4<NT, VG>(
+        0, rv.n_slots, wcnt, 0,
+        [&](int s0, int (&pl)[4]) {
+          unsigned m = rv.load4(s0, pl), r = 0;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) r |= (((m >> c) & 1u) && coarse_bin(pl[c]) >= bstar ? 1u : 0u) << c;
+          return r;
         },
         [&](int r, int s, int sc) {
           if (r < CAP) {
@@ -268,63 +529,182 @@ __global__ __launch_bounds__(NT) void topk_kernel(const int32_t* __restrict__ sc
             lval[r] = sc;
           }
         });
-    // ---- 4. exact threshold among the b* entries
-    T = radix_select32<NT, 4>(
-        Lc, k - above, h256, scan_tmp, sh,
-        [&](int e, int& sc) {
-          sc = lval[e];
-          return coarse_bin(sc) == bstar;
-        },
-        &need_eq);
-    // ---- 5. eq-rank of entries equal to T, then the output compaction
-    ordered_compact<NT, 4>(
-        Lc, wcnt, [&](int e, int&) { return okey(lval[e]) == T; },
-        [&](int r, int e, int) {
-          if (r >= need_eq) lslot[e] = -1 - lslot[e];  // mark: equal to T but not taken
-        });
-    ordered_compact<NT, 4>(
-        Lc, wcnt,
-        [&](int e, int&) {
-          return lslot[e] >= 0 && okey(lval[e]) >= T;
-        },
-        [&](int r, int e, int) {
-          if (r < k) out[r] = key_of(lslot[e]);
-        });
+    finish_from_list<NT, KEPT>(rv, Lc, lslot, lval, bstar, above, k, wcnt, h256, scan_tmp, sh, out);
   } else {
-    // ---- fallback: exact radix passes and compaction over the row in global memory
-    T = radix_select32<NT, VG>(n_slots, k, h256, scan_tmp, sh,
-                               [&](int s, int& sc) { return cand(s, sc); }, &need_eq);
-    // rank among entries equal to T is needed in slot order: count them chunk by chunk
-    constexpr int VF = (NBINS / NT < VG) ? NBINS / NT : VG;  // chunk fits lds_big
-    int eq_before = 0;
-    const int need = need_eq;
-    int written = 0;
-    for (int base = 0; base < n_slots; base += VF * NT) {
-      const int n_here = min(VF * NT, n_slots - base);
-      // entries equal to T in this chunk, in order
-      int* eq_rank = lds_big;
-      const int neq = ordered_compact<NT, VF>(
-          n_here, wcnt,
-          [&](int e, int&) {
-            int sc;
-            return cand(base + e, sc) && okey(sc) == T;
-          },
-          [&](int r, int e, int) { eq_rank[e] = r; });
-      const int wr = ordered_compact<NT, VF>(
-          n_here, wcnt,
-          [&](int e, int&) {
-            int sc;
-            if (!cand(base + e, sc)) return false;
-            const unsigned u = okey(sc);
-            return u > T || (u == T && eq_before + eq_rank[e] < need);
-          },
-          [&](int r, int e, int) {
-            if (written + r < k) out[written + r] = key_of(base + e);
-          });
-      eq_before += neq;
-      written += wr;
+    fallback_select<NT, KEPT>(rv, k, lds_big, wcnt, h256, scan_tmp, sh, out);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Several workgroups per row (few long rows: decode).  Workspace per row:
+//   hist[NBINS] | info[8] = {b*, above, cnt*, overflow, arrivals, -, -, -} | cnt[n_seg] |
+//   cand[n_seg][CAP] (slot, score)
+constexpr int INFO = 8;
+struct SegWs {
+  int* base;
+  int n_seg;
+  __device__ __forceinline__ long long row_ints() const { return NBINS + INFO + n_seg + 2ll * n_seg * CAP; }
+  __device__ __forceinline__ int* hist(long long r) const { return base + r * row_ints(); }
+  __device__ __forceinline__ int* info(long long r) const { return hist(r) + NBINS; }
+  __device__ __forceinline__ int* cnt(long long r) const { return info(r) + INFO; }
+  __device__ __forceinline__ int* cand(long long r, int seg) const { return cnt(r) + n_seg + 2ll * seg * CAP; }
+};
+
+// clears the histogram and the arrival counter of every row
+__global__ void topk_seg_zero_kernel(int* ws, long long row_ints, long long rows) {
+  const long long r = blockIdx.y;
+  if (r >= rows) return;
+  int* h = ws + r * row_ints;
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < NBINS + INFO; t += gridDim.x * blockDim.x) h[t] = 0;
+}
+
+template <int NT, bool KEPT>
+__global__ __launch_bounds__(NT) void topk_seg_hist_kernel(const int32_t* __restrict__ scores, long long ld,
+                                                           const int32_t* __restrict__ q_pos,
+                                                           const int32_t* __restrict__ kept, int bs, int n_keep,
+                                                           int L_max, int k, SegWs ws) {
+  constexpr int NW = NT / 64;
+  __shared__ int hist[NBINS];
+  __shared__ int scan_tmp[NW + 1];
+  __shared__ int kept_s[256];
+  const long long row = blockIdx.y;
+  const int seg = blockIdx.x;
+  int n_valid;
+  const RowView<KEPT> rv = make_row<NT, KEPT>(scores, ld, q_pos, kept, bs, n_keep, L_max, row, kept_s, scan_tmp, &n_valid);
+  const int lo = seg * SEG, hi = min(lo + SEG, rv.n_slots);
+  if (n_valid <= k) return;
+  const int n_seg_row = (rv.n_slots + SEG - 1) / SEG;
+  if (lo >= hi) return;  // segments past the row's end do not take part
+  for (int t = threadIdx.x; t < NBINS; t += NT) hist[t] = 0;
+  __syncthreads();
+  row_histogram<NT, 8, KEPT>(rv, lo, hi, hist);
+  __syncthreads();
+  int* gh = ws.hist(row);
+  for (int t = threadIdx.x; t < NBINS; t += NT) {
+    const int h = hist[t];
+    if (h) atomicAdd(&gh[t], h);
+  }
+  // The last segment of the row to finish finds the cut bin for everyone.  Each
+  // workgroup waits for its own histogram atomics to be performed (s_waitcnt, no
+  // cache write-back fence) before it counts itself in; the last one reads the
+  // totals back with device-scope atomic loads.
+  __shared__ int last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) last = (atomicAdd(&ws.info(row)[4], 1) == n_seg_row - 1);
+  __syncthreads();
+  if (!last) return;
+  for (int t = threadIdx.x; t < NBINS; t += NT)
+    hist[t] = __hip_atomic_load(&gh[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  __shared__ int sh[8];
+  find_cut_bin<NT>(hist, k, scan_tmp, sh);
+  if (threadIdx.x == 0) {
+    int* info = ws.info(row);
+    info[0] = sh[4];
+    info[1] = sh[5];
+    info[2] = sh[6];
+    info[3] = (sh[5] + sh[6] > CAP) ? 1 : 0;
+  }
+}
+
+template <int NT, bool KEPT>
+__global__ __launch_bounds__(NT) void topk_seg_select_kernel(const int32_t* __restrict__ scores, long long ld,
+                                                             const int32_t* __restrict__ q_pos,
+                                                             const int32_t* __restrict__ kept, int bs, int n_keep,
+                                                             int L_max, int k, SegWs ws) {
+  constexpr int NW = NT / 64;
+  constexpr int V = 8;
+  __shared__ int wcnt[2 * V * NW];
+  __shared__ int scan_tmp[NW + 1];
+  __shared__ int kept_s[256];
+  const long long row = blockIdx.y;
+  const int seg = blockIdx.x;
+  int n_valid;
+  const RowView<KEPT> rv = make_row<NT, KEPT>(scores, ld, q_pos, kept, bs, n_keep, L_max, row, kept_s, scan_tmp, &n_valid);
+  if (n_valid <= k) return;
+  const int lo = seg * SEG, hi = min(lo + SEG, rv.n_slots);
+  if (lo >= hi) return;
+  const int* info = ws.info(row);
+  const int bstar = info[0];
+  if (info[3]) return;  // overflow: the finish kernel selects from global memory
+  int* cand = ws.cand(row, seg);
+  const int n = ordered_compact4<NT, V>(
+      lo, hi, wcnt, 0,
+      [&](int s0, int (&pl)[4]) {
+        unsigned m = rv.load4(s0, pl), r = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r |= (((m >> c) & 1u) && coarse_bin(pl[c]) >= bstar ? 1u : 0u) << c;
+        return r;
+      },
+      [&](int r, int s, int sc) {
+        if (r < CAP) {
+          cand[2 * r] = s;
+          cand[2 * r + 1] = sc;
+        }
+      });
+  if (threadIdx.x == 0) ws.cnt(row)[seg] = n;
+}
+
+template <int NT, bool KEPT>
+__global__ __launch_bounds__(NT) void topk_seg_finish_kernel(const int32_t* __restrict__ scores, long long ld,
+                                                             const int32_t* __restrict__ q_pos,
+                                                             const int32_t* __restrict__ kept, int bs, int n_keep,
+                                                             int L_max, int k, SegWs ws, int32_t* __restrict__ idx,
+                                                             int32_t* __restrict__ count) {
+  constexpr int NW = NT / 64;
+  __shared__ int lds_big[NBINS];
+  __shared__ int wcnt[2 * 4 * NW];
+  __shared__ int scan_tmp[NW + 1];
+  __shared__ int h256[256];
+  __shared__ int kept_s[256];
+  __shared__ int sh[8];
+  __shared__ int seg_off[1025];
+  const long long row = blockIdx.x;
+  int32_t* out = idx + row * (long long)k;
+  int n_valid;
+  const RowView<KEPT> rv = make_row<NT, KEPT>(scores, ld, q_pos, kept, bs, n_keep, L_max, row, kept_s, scan_tmp, &n_valid);
+  if (count != nullptr && threadIdx.x == 0) count[row] = min(k, n_valid);
+  if (n_valid <= k) {
+    select_all<NT, KEPT>(rv, n_valid, k, wcnt, out);
+    return;
+  }
+  const int* info = ws.info(row);
+  const int bstar = info[0], above = info[1];
+  if (info[3]) {
+    fallback_select<NT, KEPT>(rv, k, lds_big, wcnt, h256, scan_tmp, sh, out);
+    return;
+  }
+  // segment offsets (n_seg <= 1024, scanned NT at a time), then the candidates in slot order
+  const int n_seg = (rv.n_slots + SEG - 1) / SEG;
+  {
+    int carry = 0;
+    for (int s0 = 0; s0 < n_seg; s0 += NT) {
+      const int s = s0 + (int)threadIdx.x;
+      const int c = s < n_seg ? ws.cnt(row)[s] : 0;
+      int tot;
+      const int ex = block_exclusive_scan<NT>(c, scan_tmp, &tot);
+      if (s < n_seg) seg_off[s] = carry + ex;
+      carry += tot;
+    }
+    if (threadIdx.x == 0) seg_off[n_seg] = carry;
+    __syncthreads();
+  }
+  const int Lc = min(seg_off[n_seg], CAP);
+  int* lslot = lds_big;
+  int* lval = lds_big + CAP;
+  for (int s = 0; s < n_seg; ++s) {
+    const int o = seg_off[s], c = seg_off[s + 1] - o;
+    const int* cand = ws.cand(row, s);
+    for (int e = threadIdx.x; e < c; e += NT) {
+      if (o + e < CAP) {
+        lslot[o + e] = cand[2 * e];
+        lval[o + e] = cand[2 * e + 1];
+      }
     }
   }
+  __syncthreads();
+  finish_from_list<NT, KEPT>(rv, Lc, lslot, lval, bstar, above, k, wcnt, h256, scan_tmp, sh, out);
 }
 
 // Block keep of the two-stage indexer: own block + the best n_keep-1 earlier blocks
@@ -446,16 +826,45 @@ __global__ __launch_bounds__(NT) void blk_select_kernel(const long long* __restr
 
 }  // namespace
 
+size_t topk_ws_bytes(long long rows, int L_max) {
+  if (rows == 0 || rows > 512 || L_max < 4 * SEG) return 0;
+  const long long n_seg = (L_max + SEG - 1) / SEG;
+  if (n_seg > 1024) return 0;
+  return (size_t)rows * (size_t)(NBINS + 8 + n_seg + 2 * n_seg * CAP) * sizeof(int);
+}
+
+template <bool KEPT>
+static void launch_topk_t(const TopkArgs& a, hipStream_t st, long long rows) {
+  const size_t need = topk_ws_bytes(rows, a.L_max);
+  if (!KEPT && need > 0 && a.ws != nullptr && a.ws_bytes >= need) {
+    // several workgroups per row: histogram and candidate compaction split over segments
+    SegWs w;
+    w.base = static_cast<int*>(a.ws);
+    w.n_seg = (a.L_max + SEG - 1) / SEG;
+    const long long row_ints = NBINS + INFO + w.n_seg + 2ll * w.n_seg * CAP;
+    hipLaunchKernelGGL(topk_seg_zero_kernel, dim3(8, (unsigned)rows), dim3(256), 0, st, w.base, row_ints, rows);
+    hipLaunchKernelGGL((topk_seg_hist_kernel<256, KEPT>), dim3((unsigned)w.n_seg, (unsigned)rows), dim3(256), 0, st,
+                       a.scores, a.ld, a.q_pos, a.kept, a.block_size, a.n_keep, a.L_max, a.k, w);
+    hipLaunchKernelGGL((topk_seg_select_kernel<256, KEPT>), dim3((unsigned)w.n_seg, (unsigned)rows), dim3(256), 0,
+                       st, a.scores, a.ld, a.q_pos, a.kept, a.block_size, a.n_keep, a.L_max, a.k, w);
+    hipLaunchKernelGGL((topk_seg_finish_kernel<256, KEPT>), dim3((unsigned)rows), dim3(256), 0, st, a.scores,
+                       a.ld, a.q_pos, a.kept, a.block_size, a.n_keep, a.L_max, a.k, w, a.idx, a.count);
+    return;
+  }
+  if (rows <= 1024 && a.L_max >= 16384) {
+    hipLaunchKernelGGL((topk_kernel<1024, KEPT>), dim3((unsigned)rows), dim3(1024), 0, st, a.scores, a.ld, a.q_pos,
+                       a.kept, a.block_size, a.n_keep, a.L_max, a.k, a.idx, a.count);
+  } else {
+    hipLaunchKernelGGL((topk_kernel<256, KEPT>), dim3((unsigned)rows), dim3(256), 0, st, a.scores, a.ld, a.q_pos,
+                       a.kept, a.block_size, a.n_keep, a.L_max, a.k, a.idx, a.count);
+  }
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   const long long rows = (long long)a.B * a.n_q;
   if (rows == 0) return hipSuccess;
-  if (rows <= 1024 && a.L_max >= 16384) {
-    hipLaunchKernelGGL(topk_kernel<1024>, dim3((unsigned)rows), dim3(1024), 0, st, a.scores, a.ld, a.q_pos,
-                       a.kept, a.block_size, a.n_keep, a.L_max, a.k, a.idx, a.count);
-  } else {
-    hipLaunchKernelGGL(topk_kernel<256>, dim3((unsigned)rows), dim3(256), 0, st, a.scores, a.ld, a.q_pos,
-                       a.kept, a.block_size, a.n_keep, a.L_max, a.k, a.idx, a.count);
-  }
+  if (a.kept != nullptr) launch_topk_t<true>(a, st, rows);
+  else launch_topk_t<false>(a, st, rows);
   return hipGetLastError();
 }
 

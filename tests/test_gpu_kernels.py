@@ -159,6 +159,25 @@ def test_topk_long_rows(lsa, kind, L, k):
         assert np.array_equal(J[r], want), f"{kind} row {r}"
 
 
+@pytest.mark.parametrize("kind", ["indexer_like", "equal", "ties3", "random"])
+def test_topk_split_rows_match_single_workgroup(lsa, kind):
+    """Decode-shaped rows: the several-workgroups-per-row path equals the one-workgroup path and the oracle."""
+    rng = np.random.default_rng(13)
+    L, k, n_rows = 131073, 2048, 9
+    S = _topk_case(kind, n_rows, L, rng)
+    pos = np.array([L - 1, L - 2, 100000, 40000, 32767, 8191, 2047, 2048, 0], np.int32)
+    Sg = torch.from_numpy(S).reshape(1, n_rows, L).to(dev())
+    pg = torch.from_numpy(pos).reshape(1, n_rows).to(dev())
+    J1, c1 = lsa.lsa_topk(Sg, pg, k, L, use_ws=True)
+    J2, c2 = lsa.lsa_topk(Sg, pg, k, L, use_ws=False)
+    assert torch.equal(J1, J2) and torch.equal(c1, c2)
+    J1 = J1.cpu().numpy()[0]
+    for r in range(n_rows):
+        p = int(pos[r])
+        want, _ = oracle.topk(S[r, : p + 1], np.arange(p + 1), k)
+        assert np.array_equal(J1[r], want), f"{kind} row {r}"
+
+
 def test_topk_many_rows_workgroup_variants(lsa):
     """Same rows through the 256-thread and the 1024-thread variants give identical lists."""
     rng = np.random.default_rng(7)
