@@ -11,8 +11,8 @@
  * Sources (pages on learned sparse attention):
  *   [LSA]  "Latent Sparse Attention (LSA)" (paperpeel.com/paper/2610.42147):
  *          §2 "Sparse Attention" -- cost O(Tk) to prefill, O(k) per decoded token;
- *          §2.1 "Design Choices", "Token Sparse Attention" -- an indexer with fewer
- *          heads, smaller dimension and lower precision scores every preceding key;
+ *          §2.1 "Design Choices", "Token Sparse Attention" -- a cheap, narrow,
+ *          low-precision scorer rates every earlier key;
  *          §3.1 "Pooling" -- a pooled key is the sum of consecutive index keys;
  *          §3.2 "Attention" -- one index list J_i serves every query head;
  *          App. F.1 "Selection by threshold" -- packed (score, inverted id) keys:

@@ -7,9 +7,9 @@ library routines, brute force); nothing here is "parity unpinned".
 Sources (the pages this follows; all under the subject "learned sparse attention"):
   [LSA]  "Latent Sparse Attention (LSA)", paperpeel.com/paper/2610.42147:
          §2 "Sparse Attention" (cost model: O(Tk) prefill / O(k) decode),
-         §2.1 "Design Choices", paragraph "Token Sparse Attention" (an indexer
-         with fewer heads, smaller dimension and lower precision scores every
-         preceding key; attention runs over the selected ones),
+         §2.1 "Design Choices", paragraph "Token Sparse Attention" (a cheap,
+         narrow, low-precision scorer rates each earlier key; attention then
+         uses only the chosen keys),
          §2.2 "Related Work" (two-stage block-then-token indexers),
          §3.1 "Semantic Clustering", paragraph "Pooling" (a pool key is the SUM
          of consecutive index keys),
