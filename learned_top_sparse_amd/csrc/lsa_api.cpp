@@ -23,7 +23,7 @@ inline int64_t score_ld(int32_t L) { return ((int64_t)L + 63) / 64 * 64; }
 
 // keys per workgroup span of the flat indexer
 inline int flat_span(int32_t L_max, bool direct) {
-  if (direct) return 2048;
+  if (direct) return 2048;  // matches the LDS score buffer of the direct kernel
   return L_max > 65536 ? 8192 : 4096;
 }
 

@@ -17,6 +17,9 @@
 
 namespace lsa {
 
+// keys per workgroup of the direct (decode-shaped) flat indexer
+constexpr int DIRECT_SPAN = 2048;
+
 // 16-byte chunk of the d_I bytes supplied by lane row g at K-step ks.  A and B
 // use the same assignment, so the product is the full dot product.  At one K-step
 // the four lane rows read four consecutive chunks, so every load instruction takes
@@ -200,14 +203,22 @@ __global__ __launch_bounds__(256, 2) void idx_flat_kernel(
 // its key rows straight into MFMA B fragments (no LDS).  Used for decode (flat,
 // whole context split into spans over grid.x) and for the two-stage token stage
 // (KEPT: slot s is key kept[s / bs] * bs + s % bs; one workgroup covers all slots).
+// The scan is bound by HBM, so each wave keeps a ring of RING groups of fragments:
+// RING-1 groups of loads are in flight while one group is multiplied (2 waves/SIMD).
 // Grid: x = n_spans (1 for KEPT), y = B * n_q.
 template <int D, int MT, bool KEPT>
-__global__ __launch_bounds__(256) void idx_direct_kernel(
+__global__ __launch_bounds__(256, 2) void idx_direct_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
     int w_per_query, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ kept, int bs,
     int n_keep, int n_q, int L_max, int H_I, int span, int32_t* __restrict__ scores, long long ld) {
   constexpr int KS = D / 64;
+  constexpr int RING = 4;
+  // Scores collect in LDS and leave in one burst at the end: a global store between
+  // the ring's loads makes the next wait drain every load in flight (loads and stores
+  // share one counter and may complete out of order).
+  constexpr int SBUF = KEPT ? 8192 : DIRECT_SPAN;
   __shared__ int kept_s[KEPT ? 256 : 1];
+  __shared__ __attribute__((aligned(16))) int sbuf[SBUF];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
   const long long row = blockIdx.y;
   const int b = (int)(row / n_q);
@@ -245,50 +256,64 @@ __global__ __launch_bounds__(256) void idx_direct_kernel(
     }
   };
 
-  const int n_groups = (s_end - s_begin + 63) / 64;
-  // B fragments of one 64-slot group (4 key tiles of 16)
-  auto load_group = [&](int grp, v4i (&Bf)[4][KS]) {
-    const int sg = s_begin + 64 * grp;
+  v4i ring[RING][4][KS];
+  // Slots are processed in chunks of SBUF; the chunk's scores leave LDS after its ring
+  // loop.  The ring loop is branch-free so the compiler's wait counts stay exact: every
+  // wave runs the same number of iterations (a multiple of RING) and loads past its
+  // last group re-read a row already in cache.
+  for (int c0 = s_begin; c0 < s_end; c0 += SBUF) {
+    const int c1 = min(c0 + SBUF, s_end);
+    const int n_groups = (c1 - c0 + 63) / 64;
+    const int n_iter = ((n_groups + 3) / 4 + RING - 1) / RING * RING;  // groups per wave, padded
+    auto load_group = [&](int i, v4i (&Bf)[4][KS]) {
+      const int sg = c0 + 64 * (wave + 4 * i);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      // a slot without a key reads key 0: its column's score is never stored, and the
-      // unconditional loads stay in flight together
-      const int j = max(key_of(sg + 16 * nt + r16), 0);
-      const int8_t* kr = kb + (long long)j * D;
+      for (int nt = 0; nt < 4; ++nt) {
+        // a slot without a key (or past the chunk) reads a fallback row: its column's
+        // score is never stored, and unconditional loads stay in flight together
+        const int s = min(sg + 16 * nt + r16, c1 - 1);
+        const int j = max(key_of(s), 0);
+        const int8_t* kr = kb + (long long)j * D;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
-    }
-  };
-  // software pipeline: the next group's loads are in flight while this one is multiplied
-  v4i Bf[4][KS], Bn[4][KS];
-  if (wave < n_groups) load_group(wave, Bf);
-  for (int grp = wave; grp < n_groups; grp += 4) {
-    const int sg = s_begin + 64 * grp;
-    if (grp + 4 < n_groups) load_group(grp + 4, Bn);
-    int part[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      v4i acc[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        acc[mt] = v4i{0, 0, 0, 0};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc[mt] = mfma_i8(A[mt][ks], Bf[nt][ks], acc[mt]);
+        for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
       }
-      int ps = 0;
+    };
+    auto compute_group = [&](int i, const v4i (&Bf)[4][KS]) {
+      const int sg = c0 + 64 * (wave + 4 * i);
+      int part[4];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int nt = 0; nt < 4; ++nt) {
+        v4i acc[MT];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ps += __mul24(max(acc[mt][e], 0), wt[mt][e]);
-      part[nt] = ps;
+        for (int mt = 0; mt < MT; ++mt) {
+          acc[mt] = v4i{0, 0, 0, 0};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc[mt] = mfma_i8(A[mt][ks], Bf[nt][ks], acc[mt]);
+        }
+        int ps = 0;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ps += __mul24(max(acc[mt][e], 0), wt[mt][e]);
+        part[nt] = ps;
+      }
+      const int res = reduce_scatter4(part);
+      const int s = sg + 16 * g + r16;
+      if (s < c1) sbuf[s - c0] = res;
+    };
+#pragma unroll
+    for (int r = 0; r < RING - 1; ++r) load_group(r, ring[r]);
+    for (int i0 = 0; i0 < n_iter; i0 += RING) {
+#pragma unroll
+      for (int r = 0; r < RING; ++r) {
+        load_group(i0 + r + RING - 1, ring[(r + RING - 1) % RING]);
+        compute_group(i0 + r, ring[r]);
+      }
     }
-    const int res = reduce_scatter4(part);
-    const int s = sg + 16 * g + r16;
-    if (key_of(s) >= 0) scores[srow + s] = res;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = Bn[nt][ks];
+    __syncthreads();
+    for (int t = tid; t < c1 - c0; t += 256)
+      if (key_of(c0 + t) >= 0) scores[srow + c0 + t] = sbuf[t];
+    __syncthreads();
   }
 }
 
