@@ -95,6 +95,9 @@ int lsa_version(void);
  *     for s < n_keep*block_size (ld_scores >= n_keep*block_size).  Slots whose
  *     block is -1 or whose key is past q_pos are left unspecified.
  * Supported: d_I in {64, 128}; 1 <= H_I <= 64; ld_scores >= L_max (flat).
+ * Exactness: each w_h must lie in [-2^23, 2^23) (the weight product uses 24-bit
+ * signed multiplies; a ReLU'd dot is at most 2^21) and every score must fit in
+ * int32; weights are device data and are not checked.
  * No workspace.
  */
 lsa_status lsa_index_scores(const int8_t* q_idx, const int8_t* k_idx, const int32_t* w,

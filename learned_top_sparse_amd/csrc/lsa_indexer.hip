@@ -36,16 +36,6 @@ __device__ __forceinline__ int swz(int r, int c) {
   else return c ^ ((r >> 1) & 3);
 }
 
-// Reduce-scatter of 8 per-lane partial sums (value v = 4*q + nt) over the four
-// 16-lane rows: afterwards lane row g holds the full sums of values
-// 4*(g>>1) + 2*(g&1) + {0,1}, i.e. query q = g>>1, key tiles nt = 2*(g&1) + {0,1}.
-__device__ __forceinline__ void reduce_scatter8(const int (&v)[8], int (&out)[2]) {
-  int r1[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) r1[t] = xhalf32_sum(v[t], v[4 + t]);
-#pragma unroll
-  for (int t = 0; t < 2; ++t) out[t] = xrow16_sum(r1[t], r1[2 + t]);
-}
 // Four values: lane row g ends with the full sum of value g.
 __device__ __forceinline__ int reduce_scatter4(const int (&v)[4]) {
   int r0 = xhalf32_sum(v[0], v[2]);
@@ -84,30 +74,58 @@ __device__ __forceinline__ void load_query(const int8_t* __restrict__ q_idx, con
   }
 }
 
+constexpr int BUF_RSRC_WORD3 = 0x00020000;  // 32-bit data format, raw (untyped) access
+
+// acc + max(x, 0) * w as one v_mad_i32_i24 (24-bit signed operands, 32-bit add).
+// Written out because the compiler otherwise splits the chain into multiplies and
+// three-way adds, which costs a quarter more VALU issue in the indexer epilogue --
+// the part of the indexer that bounds it, since each VALU op here takes about as
+// long to issue as a quarter of an int8 MFMA.
+__device__ __forceinline__ int relu_mad24(int x, int w, int acc) {
+  const int r = max(x, 0);
+  asm("v_mad_i32_i24 %0, %1, %2, %0" : "+v"(acc) : "v"(r), "v"(w));
+  return acc;
+}
+
 // ---------------------------------------------------------------------------------
-// Flat scores, prefill: a workgroup of 4 waves holds 4*QW queries in registers and
-// streams a span of keys through LDS in 64-key tiles shared by all its queries.
+// Flat scores, prefill: a workgroup of NW waves, one query per wave, shares each
+// 64-key tile of a span of keys through LDS.  A wave holds only its query's A
+// fragments and head weights, so four waves fit on every SIMD.
+//   * Key tiles travel through a ring of R register stages, issued R-1 tiles
+//     ahead; the loads are unconditional (clamped past the end) and the loop is
+//     unrolled by R so no stage is copied.
+//   * Inside a tile the MFMAs of key group nt+1 are issued before the ReLU/weight
+//     epilogue of group nt, so the matrix cores and the VALU work side by side.
+//   * A tile's 64 scores end up one per lane (lane l = key l of the tile) and leave
+//     as one buffer store per lane whose range check (records = the query's valid
+//     keys) drops what the query may not see: no branch around a store, so the
+//     memory counter the loads share with the stores stays exact.
 // Grid: x = n_qtiles * n_spans (longest query tiles first), y = B.
-template <int D, int MT, int QW>
-__global__ __launch_bounds__(256, 2) void idx_flat_kernel(
+template <int D, int MT, int NW>
+__global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
     int w_per_query, const int32_t* __restrict__ q_pos, int n_q, int L_max, int H_I, int span,
     int n_spans, int n_qtiles, int32_t* __restrict__ scores, long long ld) {
-  static_assert(QW == 2, "reduce_scatter8 assumes two queries per wave");
-  constexpr int KS = D / 64, KT = 64, QT = 4 * QW, CH = D / 16;
-  constexpr int LOADS = KT * CH / 256;
+  constexpr int KS = D / 64, KT = 64, CH = D / 16;
+  constexpr int R = 3;  // register stages of key tiles
+  static_assert(KT * CH <= 64 * NW, "one 16-byte chunk of a key tile per thread");
   __shared__ __attribute__((aligned(16))) int8_t tile[2][KT * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.y;
-  const int s = blockIdx.x % n_spans;
-  const int qt = n_qtiles - 1 - blockIdx.x / n_spans;
-  const int i0 = qt * QT;
+  const int qt_rev = blockIdx.x / n_spans;
+  // consecutive workgroups go to the XCDs in turn: rotating the span by the query
+  // tile spreads every span (the first one is the busiest under a causal mask) over
+  // all XCDs instead of pinning span s to XCD s % 8
+  const int s = (blockIdx.x + qt_rev) % n_spans;
+  const int qt = n_qtiles - 1 - qt_rev;
+  const int i0 = qt * NW;
   const int32_t* qp = q_pos + (long long)b * n_q;
 
   int pmax = -1;
 #pragma unroll
-  for (int t = 0; t < QT; ++t) {
+  for (int t = 0; t < NW; ++t) {
     const int i = i0 + t;
     if (i < n_q) pmax = max(pmax, min(qp[i], L_max - 1));
   }
@@ -115,86 +133,81 @@ __global__ __launch_bounds__(256, 2) void idx_flat_kernel(
   if (j_begin > pmax) return;
   const int j_end = min(j_begin + span, pmax + 1);
 
-  v4i A[QW][MT][KS];
-  int wt[QW][MT][4];
-  int pq[QW];
-  long long srow[QW];
-#pragma unroll
-  for (int q = 0; q < QW; ++q) {
-    const int i = i0 + wave * QW + q;
-    const bool valid = i < n_q;
-    const long long row = (long long)b * n_q + (valid ? i : 0);
-    pq[q] = valid ? min(qp[i], L_max - 1) : -1;
-    srow[q] = row * ld;
-    load_query<D, MT>(q_idx, w, w_per_query, row, H_I, valid, A[q], wt[q]);
-  }
+  const int i = i0 + wave;
+  const bool valid = i < n_q;
+  const long long row = (long long)b * n_q + (valid ? i : 0);
+  const int lim = valid ? min(min(qp[i], L_max - 1) + 1, j_end) : 0;
+  const __amdgpu_buffer_rsrc_t row_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(scores + row * ld, (short)0, lim * 4, BUF_RSRC_WORD3);
+
+  v4i A[MT][KS];
+  int wt[MT][4];
+  load_query<D, MT>(q_idx, w, w_per_query, row, H_I, valid, A, wt);
 
   const int8_t* kb = k_idx + (long long)b * L_max * D;
-  v4i stage[LOADS];
-  auto gload = [&](int j0) {
+  const int n_tiles = (j_end - j_begin + KT - 1) / KT;
+  // thread -> (row, chunk) of the key tile; with fewer chunks than threads the extra
+  // threads repeat a chunk and write the same bytes to the same place
+  const int cid = tid % (KT * CH), cr = cid / CH, cc = cid % CH;
+  const int tile_off = cr * D + 16 * swz<D>(cr, cc);
+  auto gload = [&](int t) -> v4i {
+    const int j = min(j_begin + min(t, n_tiles - 1) * KT + cr, L_max - 1);
+    return *(const v4i*)(kb + (long long)j * D + 16 * cc);
+  };
+  // dot products of the query's heads with the 16 keys of group nt
+  auto mfmas = [&](int buf, int nt, v4i (&acc)[MT]) {
+    v4i Bf[KS];
+    const int r = 16 * nt + r16;
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      // rows past the cache are clamped, not skipped: their scores are never stored, and
-      // unconditional loads keep every load of the tile in flight at once
-      const int cid = tid + 256 * u, r = cid / CH, c = cid % CH, j = min(j0 + r, L_max - 1);
-      stage[u] = *(const v4i*)(kb + (long long)j * D + 16 * c);
+    for (int ks = 0; ks < KS; ++ks)
+      Bf[ks] = *(const v4i*)(&tile[buf][r * D + 16 * swz<D>(r, kchunk<D>(g, ks))]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      acc[mt] = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc[mt] = mfma_i8(A[mt][ks], Bf[ks], acc[mt]);
     }
   };
-  auto swrite = [&](int buf) {
+  // this lane's share of sum_h w_h * max(0, dot_h) for its key column
+  auto epilogue = [&](const v4i (&acc)[MT]) -> int {
+    int ps = 0;
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int cid = tid + 256 * u, r = cid / CH, c = cid % CH;
-      *(v4i*)(&tile[buf][r * D + 16 * swz<D>(r, c)]) = stage[u];
-    }
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) ps = relu_mad24(acc[mt][e], wt[mt][e], ps);
+    return ps;
+  };
+  auto compute = [&](int buf) -> int {
+    int part[4];
+    v4i acc0[MT], acc1[MT];
+    mfmas(buf, 0, acc0);
+    mfmas(buf, 1, acc1);
+    part[0] = epilogue(acc0);
+    mfmas(buf, 2, acc0);
+    part[1] = epilogue(acc1);
+    mfmas(buf, 3, acc1);
+    part[2] = epilogue(acc0);
+    part[3] = epilogue(acc1);
+    return reduce_scatter4(part);  // lane l: key l of the tile
   };
 
-  const int n_tiles = (j_end - j_begin + KT - 1) / KT;
-  gload(j_begin);
-  swrite(0);
+  v4i st[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) st[u] = gload(u);
+  *(v4i*)(&tile[0][tile_off]) = st[0];
   __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const int j0 = j_begin + t * KT;
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) gload(j0 + KT);
-    int part[8];
+  const int n_pad = (n_tiles + R - 1) / R * R;
+  for (int t0 = 0; t0 < n_pad; t0 += R) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      v4i Bf[KS];
-      const int r = 16 * nt + r16;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        Bf[ks] = *(const v4i*)(&tile[buf][r * D + 16 * swz<D>(r, kchunk<D>(g, ks))]);
-#pragma unroll
-      for (int q = 0; q < QW; ++q) {
-        v4i acc[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          acc[mt] = v4i{0, 0, 0, 0};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) acc[mt] = mfma_i8(A[q][mt][ks], Bf[ks], acc[mt]);
-        }
-        int ps = 0;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ps += __mul24(max(acc[mt][e], 0), wt[q][mt][e]);
-        part[4 * q + nt] = ps;
-      }
+    for (int u = 0; u < R; ++u) {
+      const int t = t0 + u, buf = t & 1;
+      st[u] = gload(t + R);  // stage u held tile t, already in LDS
+      int res = 0;
+      if (t < n_tiles) res = compute(buf);
+      __builtin_amdgcn_raw_buffer_store_b32(res, row_rsrc, (j_begin + t * KT + lane) * 4, 0, 0);
+      *(v4i*)(&tile[buf ^ 1][tile_off]) = st[(u + 1) % R];  // tile t+1
+      __syncthreads();
     }
-    int res[2];
-    reduce_scatter8(part, res);
-    {
-      const int q = g >> 1;
-      const int p_sel = q ? pq[1] : pq[0];
-      const long long base = q ? srow[1] : srow[0];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int j = j0 + 16 * (2 * (g & 1) + e) + r16;
-        if (j <= p_sel) scores[base + j] = res[e];
-      }
-    }
-    if (t + 1 < n_tiles) swrite(buf ^ 1);
-    __syncthreads();
   }
 }
 
@@ -292,9 +305,9 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
         }
         int ps = 0;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ps += __mul24(max(acc[mt][e], 0), wt[mt][e]);
+          for (int mt = 0; mt < MT; ++mt) ps = relu_mad24(acc[mt][e], wt[mt][e], ps);
         part[nt] = ps;
       }
       const int res = reduce_scatter4(part);
@@ -365,8 +378,12 @@ __global__ __launch_bounds__(256, 2) void blk_scores_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
   const int b = blockIdx.y;
-  const int s = blockIdx.x % n_spans;
-  const int qt = n_qtiles - 1 - blockIdx.x / n_spans;
+  const int qt_rev = blockIdx.x / n_spans;
+  // consecutive workgroups go to the XCDs in turn: rotating the span by the query
+  // tile spreads every span (the first one is the busiest under a causal mask) over
+  // all XCDs instead of pinning span s to XCD s % 8
+  const int s = (blockIdx.x + qt_rev) % n_spans;
+  const int qt = n_qtiles - 1 - qt_rev;
   const int i0 = qt * QT;
   const int32_t* qp = q_pos + (long long)b * n_q;
 
@@ -475,14 +492,13 @@ __global__ __launch_bounds__(256, 2) void blk_scores_kernel(
 // host-side launchers
 template <int D, int MT>
 static hipError_t launch_flat_t(const IdxArgs& a, hipStream_t st) {
-  const int QT = 8;
-  const int n_qtiles = (a.n_q + QT - 1) / QT;
-  const int span = a.span;
-  const int n_spans = (a.L_max + span - 1) / span;
+  constexpr int NW = 8;  // queries (= waves) per workgroup
+  const int n_qtiles = (a.n_q + NW - 1) / NW;
+  const int n_spans = (a.L_max + a.span - 1) / a.span;
   dim3 grid((unsigned)(n_qtiles * n_spans), (unsigned)a.B);
-  hipLaunchKernelGGL((idx_flat_kernel<D, MT, 2>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.w,
-                     a.w_per_query, a.q_pos, a.n_q, a.L_max, a.H_I, span, n_spans, n_qtiles, a.scores,
-                     (long long)a.ld);
+  hipLaunchKernelGGL((idx_flat_kernel<D, MT, NW>), grid, dim3(64 * NW), 0, st, a.q_idx, a.k_idx, a.w,
+                     a.w_per_query, a.q_pos, a.n_q, a.L_max, a.H_I, a.span, n_spans, n_qtiles,
+                     a.scores, (long long)a.ld);
   return hipGetLastError();
 }
 template <int D, int MT, bool KEPT>
