@@ -8,9 +8,9 @@ line also carries the 128K prefill figure (the final 8192-query chunk of a
 131072-token context through the two-stage path: block reps -> block
 prefilter -> token scores in kept blocks -> top-k -> sparse attention).
 
-Each step calls the C-ABI entry points in the order lsa_forward runs them
-(checked bit-identical to lsa_forward before timing), with HIP events recorded
-on the launch stream between calls, so every kernel's duration is measured live.
+Each step is one lsa_forward call; it records a HIP event on its launch stream
+after every stage (lsa_forward_stages lists them), so every stage's kernels are
+timed live inside the timed region.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--no-cpu-baseline] [--copy-calibration]
@@ -43,101 +43,48 @@ def _describe(wl):
 
 
 class Step:
-    """One pass of the path through the C ABI, chunked exactly as lsa_forward chunks it
-    (lsa_forward_plan), with HIP events recorded on the launch stream between calls."""
+    """One pass of the path: one lsa_forward call, which records a HIP event on its
+    launch stream after every stage (lsa_forward_stages names them), so every
+    stage's kernels are timed live."""
 
     def __init__(self, lsa, torch, wl, inp):
         self.lsa, self.torch, self.wl, self.inp = lsa, torch, wl, inp
         dev = inp["q_idx"].device
-        B, n_q, L = wl.B, wl.n_q, wl.L
-        kw = dict(two_stage=wl.two_stage, block_size=wl.block_size, n_keep=wl.n_keep)
-        ws_bytes = lsa.lsa_forward_workspace_size(inp, wl.k, **kw)
-        self.rows, self.split = lsa.lsa_forward_plan(inp, wl.k, ws_bytes, **kw)
-        if n_q == 1:
-            self.chunks = [(b0, min(self.rows, B - b0), 0, 1) for b0 in range(0, B, self.rows)]
-        else:
-            self.chunks = [(b, 1, i0, min(self.rows, n_q - i0)) for b in range(B) for i0 in range(0, n_q, self.rows)]
-        self.ld = ((L + 63) // 64) * 64 if not wl.two_stage else wl.n_keep * wl.block_size
-        self.scores = torch.empty((self.rows * self.ld,), dtype=torch.int32, device=dev)
-        self.idx = torch.empty((B, n_q, wl.k), dtype=torch.int32, device=dev)
-        self.count = torch.empty((B, n_q), dtype=torch.int32, device=dev)
-        self.out = torch.empty_like(inp["q"])
-        self.lse = torch.empty((B, n_q, wl.H_q), dtype=torch.float32, device=dev)
+        B, n_q = wl.B, wl.n_q
+        self.kw = dict(two_stage=wl.two_stage, block_size=wl.block_size, n_keep=wl.n_keep)
+        ws_bytes = lsa.lsa_forward_workspace_size(inp, wl.k, **self.kw)
+        self.ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
+        self.stages = lsa.lsa_forward_stages(inp, wl.k, self.ws.numel(), **self.kw)
+        self.names = list(dict.fromkeys(self.stages))
+        self.out = {
+            "idx": torch.empty((B, n_q, wl.k), dtype=torch.int32, device=dev),
+            "count": torch.empty((B, n_q), dtype=torch.int32, device=dev),
+            "out": torch.empty_like(inp["q"]),
+            "lse": torch.empty((B, n_q, wl.H_q), dtype=torch.float32, device=dev),
+        }
         if wl.two_stage:
-            self.n_blocks = L // wl.block_size
-            self.reps = torch.empty((B, self.n_blocks, wl.d_I), dtype=torch.int32, device=dev)
-            self.kept = torch.empty((B, n_q, wl.n_keep), dtype=torch.int32, device=dev)
-        import ctypes as C
-        Lb = lsa.lib()
-        nb = C.c_size_t(0)
-        Lb.lsa_sparse_attn_workspace_size(1, self.rows, wl.H_q, wl.d, wl.k, self.split, C.byref(nb))
-        self.attn_ws = torch.empty((max(nb.value, 16),), dtype=torch.uint8, device=dev)
-        if wl.two_stage:
-            Lb.lsa_block_prefilter_workspace_size(1, self.rows, self.n_blocks, wl.d_I, C.byref(nb))
-            self.pf_ws = torch.empty((max(nb.value, 16),), dtype=torch.uint8, device=dev)
-            self.topk_ws_bytes = 0
-        else:
-            Lb.lsa_topk_workspace_size(1, self.rows, L, wl.k, C.byref(nb))
-            self.topk_ws_bytes = nb.value
-        self.topk_ws = torch.empty((max(self.topk_ws_bytes, 16),), dtype=torch.uint8, device=dev)
-        self.names = (["block_reps", "block_prefilter", "index_scores", "topk", "sparse_attn"]
-                      if wl.two_stage else ["index_scores", "topk", "sparse_attn"])
-        self.steps = []   # per recorded step: list of (name, start_event, end_event)
+            self.out["kept"] = torch.empty((B, n_q, wl.n_keep), dtype=torch.int32, device=dev)
+        self.pool = []    # event sets for recorded steps, created (recorded once) ahead of time
+        self.steps = []   # per recorded step: list of (stage, start_event, end_event)
+
+    def make_events(self, n_steps):
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        for _ in range(n_steps):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(self.stages) + 1)]
+            for e in evs:
+                e.record(stream)   # creates the HIP event
+            self.pool.append(evs)
+        torch.cuda.synchronize()
 
     def run(self, record: bool):
-        import ctypes as C
-        lsa, torch, wl, g = self.lsa, self.torch, self.wl, self.inp
-        L = lsa.lib()
-        stream = torch.cuda.current_stream()
-        st = C.c_void_p(stream.cuda_stream)
-        ev = []
-        last = [None]
-
-        def mark(name):
-            if record:
-                e = torch.cuda.Event(enable_timing=True)
-                e.record(stream)
-                if name is not None:
-                    ev.append((name, last[0], e))
-                last[0] = e
-
-        ptr = lambda t: C.c_void_p(t.data_ptr())
-        mark(None)
-        if wl.two_stage:
-            rc = L.lsa_block_reps(ptr(g["k_idx"]), wl.B, wl.L, wl.d_I, wl.block_size, self.n_blocks, ptr(self.reps), st)
-            assert rc == 0, rc
-            mark("block_reps")
-        for (b0, nb, i0, ni) in self.chunks:
-            sl = lambda t: t[b0: b0 + nb, i0: i0 + ni]
-            kept = None
-            if wl.two_stage:
-                rc = L.lsa_block_prefilter(ptr(sl(g["q_idx"])), ptr(self.reps[b0: b0 + nb]), ptr(g["w"]), 0,
-                                           ptr(sl(g["q_pos"])), nb, ni, self.n_blocks, wl.H_I, wl.d_I,
-                                           wl.block_size, wl.n_keep, ptr(sl(self.kept)), None, ptr(self.pf_ws),
-                                           self.pf_ws.numel(), st)
-                assert rc == 0, rc
-                mark("block_prefilter")
-                kept = ptr(sl(self.kept))
-            rc = L.lsa_index_scores(ptr(sl(g["q_idx"])), ptr(g["k_idx"][b0: b0 + nb]), ptr(g["w"]), 0,
-                                    ptr(sl(g["q_pos"])), kept, wl.block_size, wl.n_keep, nb, ni, wl.L, wl.H_I,
-                                    wl.d_I, ptr(self.scores), self.ld, st)
-            assert rc == 0, rc
-            mark("index_scores")
-            rc = L.lsa_topk(ptr(self.scores), self.ld, ptr(sl(g["q_pos"])), kept, wl.block_size, wl.n_keep, nb, ni,
-                            wl.L, wl.k, ptr(sl(self.idx)), ptr(sl(self.count)), ptr(self.topk_ws),
-                            self.topk_ws_bytes, st)
-            assert rc == 0, rc
-            mark("topk")
-            rc = L.lsa_sparse_attn(ptr(sl(g["q"])), ptr(g["k"][b0: b0 + nb]), ptr(g["v"][b0: b0 + nb]),
-                                   ptr(sl(self.idx)), nb, ni, wl.L, wl.H_q, wl.d, wl.k, wl.scale, self.split,
-                                   ptr(sl(self.out)), ptr(sl(self.lse)), ptr(self.attn_ws), self.attn_ws.numel(), st)
-            assert rc == 0, rc
-            mark("sparse_attn")
+        evs = self.pool[len(self.steps)] if record else None
+        self.lsa.lsa_forward(self.inp, k_top=self.wl.k, out=self.out, ws=self.ws, stage_events=evs, **self.kw)
         if record:
-            self.steps.append(ev)
+            self.steps.append([(name, evs[i], evs[i + 1]) for i, name in enumerate(self.stages)])
 
     def kernel_ms(self):
-        """Per call: mean total ms per step, launches per step, mean ms per launch."""
+        """Per stage: mean total ms per step, launches per step, mean ms per launch."""
         tot = {n: 0.0 for n in self.names}
         cnt = {n: 0 for n in self.names}
         for ev in self.steps:
@@ -245,13 +192,7 @@ def measure(lsa, torch, wl, steps, warmup):
     inp = synthetic.make_inputs(wl, torch.device("cuda:0"))
     torch.cuda.synchronize()
     step = Step(lsa, torch, wl, inp)
-    # the C-ABI sequence is the lsa_forward path: identical outputs
-    ref = lsa.lsa_forward(inp, k_top=wl.k, two_stage=wl.two_stage, block_size=wl.block_size, n_keep=wl.n_keep)
-    step.run(record=False)
-    torch.cuda.synchronize()
-    if not (torch.equal(ref["idx"], step.idx) and torch.equal(ref["out"], step.out)):
-        raise SystemExit("bench step differs from lsa_forward")
-    del ref
+    step.make_events(steps)
     for _ in range(warmup):
         step.run(record=False)
     torch.cuda.synchronize()

@@ -211,6 +211,13 @@ typedef struct lsa_forward_args {
   void* out;             /* out bf16 [B, n_q, H_q, d] */
   float* lse;            /* out fp32 [B, n_q, H_q] or NULL */
   int32_t* kept_blocks;  /* out int32 [B, n_q, n_keep] (two-stage) or NULL */
+  /* Optional stage timing: hipEvent_t handles created by the caller.  lsa_forward
+     records stage_events[0] on `stream` before its first launch and
+     stage_events[e] after its e-th stage, in launch order (lsa_forward_stages
+     lists the stages).  n_stage_events must be at least 1 + that count, else
+     LSA_ERR_INVALID_ARG and nothing is launched.  NULL: no events. */
+  void* const* stage_events;
+  int32_t n_stage_events;
 } lsa_forward_args;
 
 /* Workspace for lsa_forward.  With a->chunk_rows = 0 it sizes score chunks of
@@ -223,6 +230,29 @@ lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_bytes, voi
    these values (ld_scores = L_max rounded up to 64, or n_keep*block_size for
    two_stage) reproduces lsa_forward's results bit for bit. */
 lsa_status lsa_forward_plan(const lsa_forward_args* a, size_t ws_bytes, int64_t* chunk_rows, int32_t* attn_split);
+
+/* Stages of lsa_forward, in launch order, for a workspace of ws_bytes.  A stage is
+   one kernel or a short fixed sequence of them:
+     BLOCK_REPS       block representatives (two_stage, once per call)
+     BLOCK_PREFILTER  block scores and kept blocks of a chunk (two_stage)
+     TOPK_RESET       clears the selection state of a chunk's rows (flat rows of
+                      one query per sequence with the several-workgroups top-k:
+                      the indexer then builds each row's score histogram itself
+                      and TOPK skips its histogram pass)
+     INDEX_SCORES     the indexer over a chunk
+     TOPK             the exact top-k of a chunk
+     SPARSE_ATTN      sparse attention of a chunk (split-KV combine included)
+   Writes min(n, max_codes) codes to `codes` (may be NULL) and n to *n_stages. */
+enum {
+  LSA_STAGE_BLOCK_REPS = 1,
+  LSA_STAGE_BLOCK_PREFILTER = 2,
+  LSA_STAGE_TOPK_RESET = 3,
+  LSA_STAGE_INDEX_SCORES = 4,
+  LSA_STAGE_TOPK = 5,
+  LSA_STAGE_SPARSE_ATTN = 6
+};
+lsa_status lsa_forward_stages(const lsa_forward_args* a, size_t ws_bytes, int32_t* codes, int32_t max_codes,
+                              int32_t* n_stages);
 
 #ifdef __cplusplus
 }

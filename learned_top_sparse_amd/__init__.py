@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     lsa_block_reps,
     lsa_forward,
     lsa_forward_plan,
+    lsa_forward_stages,
     lsa_forward_workspace_size,
     lsa_index_scores,
     lsa_sparse_attn,
@@ -21,4 +22,5 @@ from .binding import (  # noqa: F401
     lsa_topk,
     lsa_version,
     EXPORTED,
+    STAGE_NAMES,
 )

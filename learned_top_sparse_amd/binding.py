@@ -20,8 +20,11 @@ EXPORTED = [
     "lsa_status_string", "lsa_version", "lsa_index_scores", "lsa_block_reps",
     "lsa_block_prefilter_workspace_size", "lsa_block_prefilter", "lsa_topk_workspace_size",
     "lsa_topk", "lsa_sparse_attn_workspace_size", "lsa_sparse_attn",
-    "lsa_forward_workspace_size", "lsa_forward", "lsa_forward_plan",
+    "lsa_forward_workspace_size", "lsa_forward", "lsa_forward_plan", "lsa_forward_stages",
 ]
+
+STAGE_NAMES = {1: "block_reps", 2: "block_prefilter", 3: "topk_reset", 4: "index_scores", 5: "topk",
+               6: "sparse_attn"}
 
 P = C.c_void_p
 I32 = C.c_int32
@@ -44,6 +47,7 @@ class ForwardArgs(C.Structure):
         ("d", I32), ("k_top", I32), ("block_size", I32), ("n_keep", I32),
         ("scale", C.c_float), ("attn_split", I32), ("chunk_rows", I64),
         ("idx", P), ("count", P), ("out", P), ("lse", P), ("kept_blocks", P),
+        ("stage_events", P), ("n_stage_events", I32),
     ]
 
 
@@ -75,6 +79,7 @@ def lib():
         L.lsa_forward_workspace_size.argtypes = [C.POINTER(ForwardArgs), C.POINTER(SZ)]
         L.lsa_forward.argtypes = [C.POINTER(ForwardArgs), P, SZ, P]
         L.lsa_forward_plan.argtypes = [C.POINTER(ForwardArgs), SZ, C.POINTER(I64), C.POINTER(I32)]
+        L.lsa_forward_stages.argtypes = [C.POINTER(ForwardArgs), SZ, C.POINTER(I32), I32, C.POINTER(I32)]
         for name in EXPORTED:
             if name not in ("lsa_status_string", "lsa_version"):
                 getattr(L, name).restype = C.c_int
@@ -281,11 +286,25 @@ def lsa_forward_plan(inp: dict, k_top: int, ws_bytes: int, two_stage: bool = Fal
     return rows.value, split.value
 
 
+def lsa_forward_stages(inp: dict, k_top: int, ws_bytes: int, two_stage: bool = False, block_size: int = 128,
+                       n_keep: int = 64, attn_split: int = 0, chunk_rows: int = 0) -> list:
+    """Names of the stages lsa_forward runs with ws_bytes of workspace, in launch order."""
+    dummy = {"idx": inp["q_pos"], "out": inp["q"]}
+    a = _forward_args(inp, k_top, two_stage, block_size, n_keep, None, attn_split, chunk_rows, dummy)
+    n = I32(0)
+    _check("lsa_forward_stages", lib().lsa_forward_stages(C.byref(a), ws_bytes, None, 0, C.byref(n)))
+    codes = (I32 * max(n.value, 1))()
+    _check("lsa_forward_stages", lib().lsa_forward_stages(C.byref(a), ws_bytes, codes, n.value, C.byref(n)))
+    return [STAGE_NAMES[codes[i]] for i in range(n.value)]
+
+
 def lsa_forward(inp: dict, k_top: int, two_stage: bool = False, block_size: int = 128, n_keep: int = 64,
                 scale: Optional[float] = None, attn_split: int = 0, chunk_rows: int = 0,
-                out: Optional[dict] = None, ws: Optional[torch.Tensor] = None) -> dict:
+                out: Optional[dict] = None, ws: Optional[torch.Tensor] = None, stage_events=None) -> dict:
     """The whole path.  ``inp`` holds q_idx, k_idx, w, q_pos, q, k, v (device tensors).
-    Returns dict(idx, count, out, lse[, kept]); pass ``out`` / ``ws`` to reuse buffers."""
+    Returns dict(idx, count, out, lse[, kept]); pass ``out`` / ``ws`` to reuse buffers.
+    ``stage_events``: optional torch.cuda.Event list (1 + len(lsa_forward_stages(...)));
+    each must have been recorded once (so its HIP event exists)."""
     q_idx, q = inp["q_idx"], inp["q"]
     dev = q_idx.device
     for name, dt in (("q_idx", torch.int8), ("k_idx", torch.int8), ("w", torch.int32), ("q_pos", torch.int32),
@@ -308,6 +327,14 @@ def lsa_forward(inp: dict, k_top: int, two_stage: bool = False, block_size: int 
         _check("lsa_forward_workspace_size", lib().lsa_forward_workspace_size(C.byref(a), C.byref(nb)))
         ws = _workspace(nb.value, dev)
     nbytes = 0 if ws is None else ws.numel()
+    if stage_events is not None:
+        handles = (P * len(stage_events))()
+        for i, e in enumerate(stage_events):
+            if not e.cuda_event:
+                raise LsaError("stage_events: record each event once before passing it")
+            handles[i] = e.cuda_event
+        a.stage_events = C.cast(handles, P)
+        a.n_stage_events = len(stage_events)
     st = lib().lsa_forward(C.byref(a), _ptr(ws), nbytes, _stream(dev))
     _check("lsa_forward", st)
     return out

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <vector>
 #include <climits>
 #include <cstdint>
 
@@ -365,6 +366,53 @@ long long plan_rows(const lsa_forward_args* a, const FwdPlan& p, size_t ws_bytes
 
 }  // namespace
 
+namespace {
+
+// A chunk of flat, one-query-per-sequence rows whose top-k splits each row over
+// several workgroups: the indexer builds the rows' score histograms itself.
+bool chunk_fused(const lsa_forward_args* a, int32_t nb, int32_t ni, void* topk_ws, size_t topk_ws_size) {
+  if (a->two_stage || ni >= 8) return false;
+  lsa::TopkArgs ta{};
+  ta.B = nb;
+  ta.n_q = ni;
+  ta.L_max = a->L_max;
+  ta.ws = topk_ws;
+  ta.ws_bytes = topk_ws_size;
+  int* hist = nullptr;
+  long long row_ints = 0;
+  return lsa::topk_split_rows(ta, &hist, &row_ints);
+}
+
+// chunks of lsa_forward for `rows` rows per chunk, as (b0, nb, i0, ni)
+template <typename F>
+void for_each_chunk(const lsa_forward_args* a, long long rows, F f) {
+  if (a->n_q == 1) {
+    for (long long b0 = 0; b0 < a->B; b0 += rows) f((int32_t)b0, (int32_t)std::min<long long>(rows, a->B - b0), 0, 1);
+  } else {
+    for (int32_t b = 0; b < a->B; ++b)
+      for (long long i0 = 0; i0 < a->n_q; i0 += rows)
+        f(b, 1, (int32_t)i0, (int32_t)std::min<long long>(rows, a->n_q - i0));
+  }
+}
+
+// stage codes of lsa_forward in launch order (rows per chunk already planned)
+std::vector<int32_t> forward_stages(const lsa_forward_args* a, const FwdPlan& p, long long rows) {
+  std::vector<int32_t> st;
+  if (a->two_stage && p.n_blocks > 0) st.push_back(LSA_STAGE_BLOCK_REPS);
+  const size_t topk_ws_size = a->two_stage ? 0 : lsa::topk_ws_bytes(rows, a->L_max);
+  alignas(16) char dummy[16];
+  for_each_chunk(a, rows, [&](int32_t, int32_t nb, int32_t, int32_t ni) {
+    if (a->two_stage) st.push_back(LSA_STAGE_BLOCK_PREFILTER);
+    if (chunk_fused(a, nb, ni, dummy, topk_ws_size)) st.push_back(LSA_STAGE_TOPK_RESET);
+    st.push_back(LSA_STAGE_INDEX_SCORES);
+    st.push_back(LSA_STAGE_TOPK);
+    st.push_back(LSA_STAGE_SPARSE_ATTN);
+  });
+  return st;
+}
+
+}  // namespace
+
 LSA_API lsa_status lsa_forward_workspace_size(const lsa_forward_args* a, size_t* bytes) {
   if (!bytes) return LSA_ERR_INVALID_ARG;
   lsa_status st = check_forward(a);
@@ -393,6 +441,16 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
   const long long rows = plan_rows(a, p, ws_bytes);
   if (rows == 0 || (!ws && chunk_bytes(a, p, rows) > 0)) return LSA_ERR_WORKSPACE;
   (void)n_rows;
+  if (a->stage_events != nullptr &&
+      (long long)a->n_stage_events < 1 + (long long)forward_stages(a, p, rows).size())
+    return LSA_ERR_INVALID_ARG;
+  int32_t n_marked = 0;
+  // records the next stage event (if the caller asked for them)
+  auto mark = [&]() -> bool {
+    if (a->stage_events == nullptr) return true;
+    return hipEventRecord(static_cast<hipEvent_t>(a->stage_events[n_marked++]), s) == hipSuccess;
+  };
+  if (!mark()) return LSA_ERR_HIP;
 
   // workspace carve-up
   char* base = static_cast<char*>(ws);
@@ -429,6 +487,7 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
     if (lsa::launch_block_reps(a->k_idx, a->B, L, d_I, a->block_size, p.n_blocks, reps, s) != hipSuccess)
       return LSA_ERR_HIP;
     if (lsa::launch_block_limbs(reps, a->B, p.n_blocks, d_I, limbs, s) != hipSuccess) return LSA_ERR_HIP;
+    if (!mark()) return LSA_ERR_HIP;
   }
 
   // one chunk: sequences [b0, b0+nb) x queries [i0, i0+ni) (either nb == 1 or ni == n_q == 1)
@@ -468,10 +527,10 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
       ia.kept = kept;
       ia.block_size = a->block_size;
       ia.n_keep = a->n_keep;
+      if (!mark()) return LSA_ERR_HIP;
     }
     ia.use_direct = a->two_stage ? true : ni < 8;
     ia.span = flat_span(L, ia.use_direct);
-    if (lsa::launch_index_scores(ia, s) != hipSuccess) return LSA_ERR_HIP;
     lsa::TopkArgs ta{};
     ta.scores = sc;
     ta.ld = p.ld;
@@ -487,25 +546,40 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
     ta.count = cnt;
     ta.ws = topk_ws;
     ta.ws_bytes = topk_ws_size;
-    if (lsa::launch_topk(ta, s) != hipSuccess) return LSA_ERR_HIP;
-    return run_attn(qq, kk, vv, ix, nb, ni, L, H_q, d, kt, a->scale, split, oo, ls, attn_ws, s);
+    if (chunk_fused(a, nb, ni, topk_ws, topk_ws_size)) {
+      // the indexer adds each row's score histogram into the selection state
+      if (lsa::launch_topk_reset(ta, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
+      if (!lsa::topk_split_rows(ta, &ia.sel_hist, &ia.sel_row_ints)) return LSA_ERR_INTERNAL;
+      ia.k_top = kt;
+      ta.hist_ready = true;
+    }
+    if (lsa::launch_index_scores(ia, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
+    if (lsa::launch_topk(ta, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
+    lsa_status sa = run_attn(qq, kk, vv, ix, nb, ni, L, H_q, d, kt, a->scale, split, oo, ls, attn_ws, s);
+    if (sa != LSA_OK) return sa;
+    return mark() ? LSA_OK : LSA_ERR_HIP;
   };
 
-  if (p.decode_like) {
-    for (long long b0 = 0; b0 < a->B; b0 += rows) {
-      const int32_t nb = (int32_t)std::min<long long>(rows, a->B - b0);
-      lsa_status st2 = run_chunk((int32_t)b0, nb, 0, 1);
-      if (st2 != LSA_OK) return st2;
-    }
-  } else {
-    for (int32_t b = 0; b < a->B; ++b) {
-      for (long long i0 = 0; i0 < a->n_q; i0 += rows) {
-        const int32_t ni = (int32_t)std::min<long long>(rows, a->n_q - i0);
-        lsa_status st2 = run_chunk(b, 1, (int32_t)i0, ni);
-        if (st2 != LSA_OK) return st2;
-      }
-    }
-  }
+  lsa_status result = LSA_OK;
+  for_each_chunk(a, rows, [&](int32_t b0, int32_t nb, int32_t i0, int32_t ni) {
+    if (result == LSA_OK) result = run_chunk(b0, nb, i0, ni);
+  });
+  return result;
+}
+
+LSA_API lsa_status lsa_forward_stages(const lsa_forward_args* a, size_t ws_bytes, int32_t* codes, int32_t max_codes,
+                                      int32_t* n_stages) {
+  if (!n_stages || max_codes < 0) return LSA_ERR_INVALID_ARG;
+  lsa_status st = check_forward(a);
+  if (st != LSA_OK) return st;
+  *n_stages = 0;
+  if ((long long)a->B * a->n_q == 0) return LSA_OK;
+  const FwdPlan p = plan_forward(a);
+  const long long rows = plan_rows(a, p, ws_bytes);
+  if (rows == 0) return LSA_ERR_WORKSPACE;
+  const std::vector<int32_t> v = forward_stages(a, p, rows);
+  for (size_t i = 0; codes != nullptr && i < v.size() && (long long)i < max_codes; ++i) codes[i] = v[i];
+  *n_stages = (int32_t)v.size();
   return LSA_OK;
 }
 

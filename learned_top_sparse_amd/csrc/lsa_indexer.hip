@@ -14,6 +14,7 @@
 // final sum over the four 16-lane rows crosses lanes (permlane swaps, no LDS).
 #include "lsa_device.h"
 #include "lsa_internal.h"
+#include "lsa_select.h"
 
 namespace lsa {
 
@@ -218,12 +219,18 @@ __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
 // (KEPT: slot s is key kept[s / bs] * bs + s % bs; one workgroup covers all slots).
 // The scan is bound by HBM, so each wave keeps a ring of RING groups of fragments:
 // RING-1 groups of loads are in flight while one group is multiplied (2 waves/SIMD).
+// HIST (flat only): the workgroup also counts its scores into an LDS histogram of
+// the selection's coarse bins and adds it to the row's histogram in device memory
+// (sel_hist + row * sel_row_ints, cleared beforehand), so the exact top-k that
+// follows needs no histogram pass of its own over the row.
 // Grid: x = n_spans (1 for KEPT), y = B * n_q.
-template <int D, int MT, bool KEPT>
+template <int D, int MT, bool KEPT, bool HIST>
 __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
     int w_per_query, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ kept, int bs,
-    int n_keep, int n_q, int L_max, int H_I, int span, int32_t* __restrict__ scores, long long ld) {
+    int n_keep, int n_q, int L_max, int H_I, int span, int32_t* __restrict__ scores, long long ld,
+    int* __restrict__ sel_hist, long long sel_row_ints, int k_top) {
+  static_assert(!(KEPT && HIST), "the histogram is built for flat rows only");
   constexpr int KS = D / 64;
   constexpr int RING = 4;
   // Scores collect in LDS and leave in one burst at the end: a global store between
@@ -232,6 +239,7 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
   constexpr int SBUF = KEPT ? 8192 : DIRECT_SPAN;
   __shared__ int kept_s[KEPT ? 256 : 1];
   __shared__ __attribute__((aligned(16))) int sbuf[SBUF];
+  __shared__ int lhist[HIST ? NBINS : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
   const long long row = blockIdx.y;
   const int b = (int)(row / n_q);
@@ -248,6 +256,13 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
     s_begin = blockIdx.x * span;
     s_end = min(s_begin + span, p + 1);
     if (s_begin >= s_end) return;
+  }
+
+  // a row with no more candidates than k takes them all: no histogram needed
+  const bool hist = HIST && p + 1 > k_top;
+  if (hist) {
+    for (int t = tid; t < NBINS; t += 256) lhist[t] = 0;
+    __syncthreads();
   }
 
   v4i A[MT][KS];
@@ -312,7 +327,11 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
       }
       const int res = reduce_scatter4(part);
       const int s = sg + 16 * g + r16;
-      if (s < c1) sbuf[s - c0] = res;
+      if (s < c1) {
+        sbuf[s - c0] = res;
+        // LDS only, inside the ring loop where the waves mostly wait on HBM anyway
+        if (hist) atomicAdd(&lhist[coarse_bin(res)], 1);
+      }
     };
 #pragma unroll
     for (int r = 0; r < RING - 1; ++r) load_group(r, ring[r]);
@@ -327,6 +346,13 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
     for (int t = tid; t < c1 - c0; t += 256)
       if (key_of(c0 + t) >= 0) scores[srow + c0 + t] = sbuf[t];
     __syncthreads();
+  }
+  if (hist) {
+    int* gh = sel_hist + row * sel_row_ints;
+    for (int t = tid; t < NBINS; t += 256) {
+      const int h = lhist[t];
+      if (h) atomicAdd(&gh[t], h);
+    }
   }
 }
 
@@ -505,9 +531,17 @@ template <int D, int MT, bool KEPT>
 static hipError_t launch_direct_t(const IdxArgs& a, hipStream_t st) {
   const int n_spans = KEPT ? 1 : (a.L_max + a.span - 1) / a.span;
   dim3 grid((unsigned)n_spans, (unsigned)(a.B * a.n_q));
-  hipLaunchKernelGGL((idx_direct_kernel<D, MT, KEPT>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.w,
+  if constexpr (!KEPT) {
+    if (a.sel_hist != nullptr) {
+      hipLaunchKernelGGL((idx_direct_kernel<D, MT, false, true>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.w,
+                         a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I,
+                         a.span, a.scores, (long long)a.ld, a.sel_hist, a.sel_row_ints, a.k_top);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((idx_direct_kernel<D, MT, KEPT, false>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.w,
                      a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I,
-                     a.span, a.scores, (long long)a.ld);
+                     a.span, a.scores, (long long)a.ld, nullptr, 0ll, 0);
   return hipGetLastError();
 }
 

@@ -23,28 +23,15 @@
 // stable compaction over the row in global memory.  Every path is exact.
 #include "lsa_device.h"
 #include "lsa_internal.h"
+#include "lsa_select.h"
 
 namespace lsa {
 
 namespace {
 
-constexpr int NBINS = 8192;
-constexpr int CAP = NBINS / 2;  // LDS list entries (slot, score), reusing the histogram storage
 constexpr int SEG = 8192;       // slots per workgroup in the several-workgroups-per-row path
 
 __device__ __forceinline__ unsigned okey(int s) { return (unsigned)s ^ 0x80000000u; }
-
-// Monotone 13-bit bin: non-negative scores map to 4096 + g(s), negative ones to
-// 4095 - g(~s), where g keeps the exponent and the top 7 mantissa bits:
-//   u = |s| folded (s ^ sign), shift = max(0, 24 - clz(u)), g = (shift << 7) + (u >> shift).
-// For u < 128 this is u itself; above, each power of two is split into 128 bins.
-__device__ __forceinline__ int coarse_bin(int s) {
-  const int sign = s >> 31;
-  const unsigned u = (unsigned)(s ^ sign);
-  const int shift = max(0, 24 - (int)__clz((int)(u | 1u)));
-  const int gv = (shift << 7) + (int)(u >> shift);
-  return (gv ^ sign) + 4096;
-}
 
 // Ordered compaction over positions [0, n): pred(pos, payload&) selects; emit(rank,
 // pos, payload) is called for selected positions with their rank in position order.
@@ -258,35 +245,6 @@ __device__ __forceinline__ void row_histogram(const RowView<KEPT> rv, int lo, in
       for (int c = 0; c < 4; ++c)
         if ((m[v] >> c) & 1u) atomicAdd(&hist[coarse_bin(sc[v][c])], 1);
   }
-}
-
-// Bin b* holding the k-th best entry of `hist` (NBINS counters, LDS or global):
-// writes sh[4] = b*, sh[5] = entries in bins above b*, sh[6] = entries in b*.
-template <int NT>
-__device__ __forceinline__ void find_cut_bin(const int* hist, int k, int* scan_tmp, int* sh) {
-  constexpr int C = NBINS / NT;
-  const int hi = NBINS - (int)threadIdx.x * C;
-  int csum = 0;
-  // skewed visiting order: at step i lane t reads bin (i + t) % C of its range, so the
-  // lanes of a wave touch distinct LDS banks
-#pragma unroll 8
-  for (int i = 0; i < C; ++i) csum += hist[hi - C + ((i + (int)threadIdx.x) & (C - 1))];
-  int tot;
-  const int excl = block_exclusive_scan<NT>(csum, scan_tmp, &tot);
-  if (excl < k && excl + csum >= k) {
-    int acc = excl;
-    for (int b = hi - 1; b >= hi - C; --b) {
-      const int h = hist[b];
-      if (acc + h >= k) {
-        sh[4] = b;
-        sh[5] = acc;
-        sh[6] = h;
-        break;
-      }
-      acc += h;
-    }
-  }
-  __syncthreads();
 }
 
 // Steps 4-5 once the entries of bins >= b* sit in slot order in the LDS list
@@ -539,11 +497,14 @@ __global__ __launch_bounds__(NT) void topk_kernel(const int32_t* __restrict__ sc
 // Several workgroups per row (few long rows: decode).  Workspace per row:
 //   hist[NBINS] | info[8] = {b*, above, cnt*, overflow, arrivals, -, -, -} | cnt[n_seg] |
 //   cand[n_seg][CAP] (slot, score)
-constexpr int INFO = 8;
+// ints per row of the workspace, a multiple of 4 so every row's histogram is 16-byte aligned
+__host__ __device__ constexpr long long seg_row_ints(long long n_seg) {
+  return (NBINS + INFO + n_seg + 2 * n_seg * CAP + 3) / 4 * 4;
+}
 struct SegWs {
   int* base;
   int n_seg;
-  __device__ __forceinline__ long long row_ints() const { return NBINS + INFO + n_seg + 2ll * n_seg * CAP; }
+  __device__ __forceinline__ long long row_ints() const { return seg_row_ints(n_seg); }
   __device__ __forceinline__ int* hist(long long r) const { return base + r * row_ints(); }
   __device__ __forceinline__ int* info(long long r) const { return hist(r) + NBINS; }
   __device__ __forceinline__ int* cnt(long long r) const { return info(r) + INFO; }
@@ -579,36 +540,14 @@ __global__ __launch_bounds__(NT) void topk_seg_hist_kernel(const int32_t* __rest
   __syncthreads();
   row_histogram<NT, 8, KEPT>(rv, lo, hi, hist);
   __syncthreads();
-  int* gh = ws.hist(row);
-  for (int t = threadIdx.x; t < NBINS; t += NT) {
-    const int h = hist[t];
-    if (h) atomicAdd(&gh[t], h);
-  }
-  // The last segment of the row to finish finds the cut bin for everyone.  Each
-  // workgroup waits for its own histogram atomics to be performed (s_waitcnt, no
-  // cache write-back fence) before it counts itself in; the last one reads the
-  // totals back with device-scope atomic loads.
-  __shared__ int last;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) last = (atomicAdd(&ws.info(row)[4], 1) == n_seg_row - 1);
-  __syncthreads();
-  if (!last) return;
-  for (int t = threadIdx.x; t < NBINS; t += NT)
-    hist[t] = __hip_atomic_load(&gh[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
   __shared__ int sh[8];
-  find_cut_bin<NT>(hist, k, scan_tmp, sh);
-  if (threadIdx.x == 0) {
-    int* info = ws.info(row);
-    info[0] = sh[4];
-    info[1] = sh[5];
-    info[2] = sh[6];
-    info[3] = (sh[5] + sh[6] > CAP) ? 1 : 0;
-  }
+  merge_row_histogram<NT>(hist, ws.hist(row), ws.info(row), n_seg_row, k, scan_tmp, sh);
 }
 
-template <int NT, bool KEPT>
+// CUT: the row's histogram is complete but its cut is not known yet (the indexer
+// built the histogram); every segment finds the cut itself and segment 0 records
+// it for the finish kernel.
+template <int NT, bool KEPT, bool CUT>
 __global__ __launch_bounds__(NT) void topk_seg_select_kernel(const int32_t* __restrict__ scores, long long ld,
                                                              const int32_t* __restrict__ q_pos,
                                                              const int32_t* __restrict__ kept, int bs, int n_keep,
@@ -618,6 +557,7 @@ __global__ __launch_bounds__(NT) void topk_seg_select_kernel(const int32_t* __re
   __shared__ int wcnt[2 * V * NW];
   __shared__ int scan_tmp[NW + 1];
   __shared__ int kept_s[256];
+  __shared__ int sh[8];
   const long long row = blockIdx.y;
   const int seg = blockIdx.x;
   int n_valid;
@@ -625,9 +565,31 @@ __global__ __launch_bounds__(NT) void topk_seg_select_kernel(const int32_t* __re
   if (n_valid <= k) return;
   const int lo = seg * SEG, hi = min(lo + SEG, rv.n_slots);
   if (lo >= hi) return;
-  const int* info = ws.info(row);
-  const int bstar = info[0];
-  if (info[3]) return;  // overflow: the finish kernel selects from global memory
+  int* info = ws.info(row);
+  int bstar, overflow;
+  if constexpr (CUT) {
+    __shared__ __attribute__((aligned(16))) int hcopy[NBINS];
+    const v4i* gh = reinterpret_cast<const v4i*>(ws.hist(row));
+    v4i hv[NBINS / 4 / NT];
+#pragma unroll
+    for (int u = 0; u < NBINS / 4 / NT; ++u) hv[u] = gh[u * NT + threadIdx.x];
+#pragma unroll
+    for (int u = 0; u < NBINS / 4 / NT; ++u) reinterpret_cast<v4i*>(hcopy)[u * NT + threadIdx.x] = hv[u];
+    __syncthreads();
+    find_cut_bin<NT>(hcopy, k, scan_tmp, sh);
+    bstar = sh[4];
+    overflow = (sh[5] + sh[6] > CAP) ? 1 : 0;
+    if (seg == 0 && threadIdx.x == 0) {
+      info[0] = sh[4];
+      info[1] = sh[5];
+      info[2] = sh[6];
+      info[3] = overflow;
+    }
+  } else {
+    bstar = info[0];
+    overflow = info[3];
+  }
+  if (overflow) return;  // the finish kernel selects from global memory
   int* cand = ws.cand(row, seg);
   const int n = ordered_compact4<NT, V>(
       lo, hi, wcnt, 0,
@@ -693,13 +655,31 @@ __global__ __launch_bounds__(NT) void topk_seg_finish_kernel(const int32_t* __re
   const int Lc = min(seg_off[n_seg], CAP);
   int* lslot = lds_big;
   int* lval = lds_big + CAP;
-  for (int s = 0; s < n_seg; ++s) {
-    const int o = seg_off[s], c = seg_off[s + 1] - o;
-    const int* cand = ws.cand(row, s);
-    for (int e = threadIdx.x; e < c; e += NT) {
-      if (o + e < CAP) {
-        lslot[o + e] = cand[2 * e];
-        lval[o + e] = cand[2 * e + 1];
+  // all candidates of the row in one flat pass, each entry's segment found by binary
+  // search in seg_off, G entries per thread in flight (a loop over segments would
+  // wait out one memory latency per segment)
+  constexpr int G = 8;
+  for (int e0 = 0; e0 < Lc; e0 += G * NT) {
+    int gs[G], gv[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int ec = min(e0 + u * NT + (int)threadIdx.x, Lc - 1);  // clamped: loads stay unconditional
+      int lo = 0, hi = n_seg;  // seg_off[lo] <= ec < seg_off[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (seg_off[mid] <= ec) lo = mid;
+        else hi = mid;
+      }
+      const int* cand = ws.cand(row, lo) + 2 * (ec - seg_off[lo]);
+      gs[u] = cand[0];
+      gv[u] = cand[1];
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int e = e0 + u * NT + (int)threadIdx.x;
+      if (e < Lc) {
+        lslot[e] = gs[u];
+        lval[e] = gv[u];
       }
     }
   }
@@ -830,23 +810,36 @@ size_t topk_ws_bytes(long long rows, int L_max) {
   if (rows == 0 || rows > 512 || L_max < 4 * SEG) return 0;
   const long long n_seg = (L_max + SEG - 1) / SEG;
   if (n_seg > 1024) return 0;
-  return (size_t)rows * (size_t)(NBINS + 8 + n_seg + 2 * n_seg * CAP) * sizeof(int);
+  return (size_t)rows * (size_t)seg_row_ints(n_seg) * sizeof(int);
+}
+
+static bool split_rows(const TopkArgs& a, SegWs* w, long long* row_ints) {
+  const long long rows = (long long)a.B * a.n_q;
+  const size_t need = topk_ws_bytes(rows, a.L_max);
+  if (a.kept != nullptr || need == 0 || a.ws == nullptr || a.ws_bytes < need) return false;
+  w->base = static_cast<int*>(a.ws);
+  w->n_seg = (a.L_max + SEG - 1) / SEG;
+  *row_ints = seg_row_ints(w->n_seg);
+  return true;
 }
 
 template <bool KEPT>
 static void launch_topk_t(const TopkArgs& a, hipStream_t st, long long rows) {
-  const size_t need = topk_ws_bytes(rows, a.L_max);
-  if (!KEPT && need > 0 && a.ws != nullptr && a.ws_bytes >= need) {
+  SegWs w;
+  long long row_ints;
+  if (!KEPT && split_rows(a, &w, &row_ints)) {
     // several workgroups per row: histogram and candidate compaction split over segments
-    SegWs w;
-    w.base = static_cast<int*>(a.ws);
-    w.n_seg = (a.L_max + SEG - 1) / SEG;
-    const long long row_ints = NBINS + INFO + w.n_seg + 2ll * w.n_seg * CAP;
-    hipLaunchKernelGGL(topk_seg_zero_kernel, dim3(8, (unsigned)rows), dim3(256), 0, st, w.base, row_ints, rows);
-    hipLaunchKernelGGL((topk_seg_hist_kernel<256, KEPT>), dim3((unsigned)w.n_seg, (unsigned)rows), dim3(256), 0, st,
-                       a.scores, a.ld, a.q_pos, a.kept, a.block_size, a.n_keep, a.L_max, a.k, w);
-    hipLaunchKernelGGL((topk_seg_select_kernel<256, KEPT>), dim3((unsigned)w.n_seg, (unsigned)rows), dim3(256), 0,
-                       st, a.scores, a.ld, a.q_pos, a.kept, a.block_size, a.n_keep, a.L_max, a.k, w);
+    const dim3 grid((unsigned)w.n_seg, (unsigned)rows);
+    if (a.hist_ready) {
+      hipLaunchKernelGGL((topk_seg_select_kernel<256, KEPT, true>), grid, dim3(256), 0, st, a.scores, a.ld,
+                         a.q_pos, a.kept, a.block_size, a.n_keep, a.L_max, a.k, w);
+    } else {
+      hipLaunchKernelGGL(topk_seg_zero_kernel, dim3(8, (unsigned)rows), dim3(256), 0, st, w.base, row_ints, rows);
+      hipLaunchKernelGGL((topk_seg_hist_kernel<256, KEPT>), grid, dim3(256), 0, st, a.scores, a.ld, a.q_pos,
+                         a.kept, a.block_size, a.n_keep, a.L_max, a.k, w);
+      hipLaunchKernelGGL((topk_seg_select_kernel<256, KEPT, false>), grid, dim3(256), 0, st, a.scores, a.ld,
+                         a.q_pos, a.kept, a.block_size, a.n_keep, a.L_max, a.k, w);
+    }
     hipLaunchKernelGGL((topk_seg_finish_kernel<256, KEPT>), dim3((unsigned)rows), dim3(256), 0, st, a.scores,
                        a.ld, a.q_pos, a.kept, a.block_size, a.n_keep, a.L_max, a.k, w, a.idx, a.count);
     return;
@@ -858,6 +851,22 @@ static void launch_topk_t(const TopkArgs& a, hipStream_t st, long long rows) {
     hipLaunchKernelGGL((topk_kernel<256, KEPT>), dim3((unsigned)rows), dim3(256), 0, st, a.scores, a.ld, a.q_pos,
                        a.kept, a.block_size, a.n_keep, a.L_max, a.k, a.idx, a.count);
   }
+}
+
+bool topk_split_rows(const TopkArgs& a, int** hist, long long* row_ints) {
+  SegWs w;
+  if (!split_rows(a, &w, row_ints)) return false;
+  *hist = w.base;
+  return true;
+}
+
+hipError_t launch_topk_reset(const TopkArgs& a, hipStream_t st) {
+  SegWs w;
+  long long row_ints;
+  const long long rows = (long long)a.B * a.n_q;
+  if (rows == 0 || !split_rows(a, &w, &row_ints)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_seg_zero_kernel, dim3(8, (unsigned)rows), dim3(256), 0, st, w.base, row_ints, rows);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {

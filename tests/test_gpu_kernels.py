@@ -389,6 +389,39 @@ def test_forward_decode_small(lsa):
     err.check()
 
 
+@pytest.mark.parametrize("H_I", [64, 20])
+def test_forward_decode_fused_selection(lsa, H_I):
+    """Decode rows long enough for the split top-k: lsa_forward lets the indexer build
+    the rows' histograms (stages topk_reset, index_scores, topk, sparse_attn).  Its
+    lists equal the separate calls' (histogram pass inside lsa_topk) bit for bit, and
+    the oracle's on sampled rows; rows of at most k candidates mix in."""
+    L, k = 40000, 1024
+    pos = [39999, 30000, 1023, 500, 33333, 39998]
+    wl = synthetic.Workload("decfused", B=len(pos), n_q=1, L=L, q_pos0=0, H_I=H_I, d_I=128, k=k, H_q=16)
+    inp, g = _inputs(wl, seed=11, pos=pos)
+    ws_bytes = lsa.lsa_forward_workspace_size(g, k)
+    assert lsa.lsa_forward_stages(g, k, ws_bytes) == ["topk_reset", "index_scores", "topk", "sparse_attn"]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    for e in evs:
+        e.record()
+    res = lsa.lsa_forward(g, k_top=k, stage_events=evs)
+    torch.cuda.synchronize()
+    assert all(evs[i].elapsed_time(evs[i + 1]) >= 0 for i in range(4))
+    ld = ((L + 63) // 64) * 64
+    sc = lsa.lsa_index_scores(g["q_idx"], g["k_idx"], g["w"], g["q_pos"], ld=ld)
+    for use_ws in (True, False):
+        idx, cnt = lsa.lsa_topk(sc, g["q_pos"], k, L, use_ws=use_ws)
+        assert torch.equal(idx, res["idx"]), f"use_ws={use_ws}"
+        assert torch.equal(cnt, res["count"])
+    want = _flat_oracle_rows(inp, k, rows=[(0, 0), (2, 0), (3, 0), (4, 0)])
+    J, out = res["idx"].cpu().numpy(), np64(res["out"])
+    err = AttnErr()
+    for (b, i), r in want.items():
+        assert np.array_equal(J[b, i], r["J"]), f"seq {b}"
+        err.add(out[b, i], r["out"], (b, i))
+    err.check()
+
+
 @pytest.mark.parametrize("T,bs,n_keep,k", [(4096, 128, 8, 256), (2048, 16, 6, 40)])
 def test_forward_two_stage_small(lsa, T, bs, n_keep, k):
     n_q = 64

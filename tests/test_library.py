@@ -47,3 +47,56 @@ def test_host_validation_without_gpu():
     assert L.lsa_block_reps(None, 1, 100, 128, 200, 1, None, None) == -2    # block_size > 128
     # zero-size work is a no-op success
     assert L.lsa_topk(None, 0, None, None, 0, 0, 0, 5, 10, 8, None, None, None, 0, None) == 0
+
+
+def _fake_inputs(B, n_q, L, H_I=64, d_I=128, H_q=16, d=128):
+    """CPU tensors with the path's shapes: only their pointers reach the host-side planning."""
+    import torch
+    return {
+        "q_idx": torch.zeros((B, n_q, H_I, d_I), dtype=torch.int8),
+        "k_idx": torch.zeros((B, L, d_I), dtype=torch.int8),
+        "w": torch.ones((H_I,), dtype=torch.int32),
+        "q_pos": torch.zeros((B, n_q), dtype=torch.int32),
+        "q": torch.zeros((B, n_q, H_q, d), dtype=torch.bfloat16),
+        "k": torch.zeros((B, L, d), dtype=torch.bfloat16),
+        "v": torch.zeros((B, L, d), dtype=torch.bfloat16),
+    }
+
+
+def test_forward_stages_listing():
+    """lsa_forward_stages: the stage sequence of each mode (host planning only)."""
+    import learned_top_sparse_amd as lsa
+    # decode-shaped, long rows: the indexer builds the histograms, so a reset stage comes first
+    inp = _fake_inputs(64, 1, 131073)
+    ws = lsa.lsa_forward_workspace_size(inp, 2048)
+    assert lsa.lsa_forward_stages(inp, 2048, ws) == ["topk_reset", "index_scores", "topk", "sparse_attn"]
+    # decode-shaped but short rows (below four selection segments): no split top-k, no reset
+    inp = _fake_inputs(8, 1, 20000)
+    ws = lsa.lsa_forward_workspace_size(inp, 2048)
+    assert lsa.lsa_forward_stages(inp, 2048, ws) == ["index_scores", "topk", "sparse_attn"]
+    # prefill in three chunks
+    inp = _fake_inputs(1, 3000, 4096)
+    ws = lsa.lsa_forward_workspace_size(inp, 512, chunk_rows=1000)
+    assert lsa.lsa_forward_stages(inp, 512, ws, chunk_rows=1000) == ["index_scores", "topk", "sparse_attn"] * 3
+    # two-stage: block representatives once, then four stages per chunk
+    inp = _fake_inputs(1, 512, 8192)
+    ws = lsa.lsa_forward_workspace_size(inp, 512, two_stage=True, chunk_rows=256)
+    st = lsa.lsa_forward_stages(inp, 512, ws, two_stage=True, chunk_rows=256)
+    assert st == ["block_reps"] + ["block_prefilter", "index_scores", "topk", "sparse_attn"] * 2
+
+
+def test_forward_rejects_too_few_stage_events():
+    """Too few stage events: LSA_ERR_INVALID_ARG before anything is launched."""
+    import learned_top_sparse_amd as lsa
+    from learned_top_sparse_amd.binding import ForwardArgs, _forward_args
+    inp = _fake_inputs(4, 1, 40000)
+    out = {"idx": inp["q_pos"], "out": inp["q"]}
+    a = _forward_args(inp, 2048, False, 128, 64, None, 0, 0, out)
+    n = ctypes.c_int32(0)
+    ws = lsa.lsa_forward_workspace_size(inp, 2048)
+    assert lsa.lib().lsa_forward_stages(ctypes.byref(a), ws, None, 0, ctypes.byref(n)) == 0 and n.value == 4
+    handles = (ctypes.c_void_p * n.value)()   # one short of 1 + n
+    a.stage_events = ctypes.cast(handles, ctypes.c_void_p)
+    a.n_stage_events = n.value
+    fake_ws = ctypes.c_void_p(1 << 20)   # never dereferenced: the call returns before any launch
+    assert lsa.lib().lsa_forward(ctypes.byref(a), fake_ws, ws, None) == -1
