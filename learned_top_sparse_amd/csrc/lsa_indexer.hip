@@ -348,11 +348,19 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
     __syncthreads();
   }
   if (hist) {
+    // bins go out in lane order (a wave's atomics touch few cache lines); thread t
+    // also sums group t in LDS (skewed order: the lanes of a wave read distinct banks)
+    static_assert(NGRP == 256, "one group per thread");
     int* gh = sel_hist + row * sel_row_ints;
+    int* gsum = gh + NBINS + INFO;
+    int sum = 0;
+#pragma unroll 8
+    for (int i = 0; i < GRP; ++i) sum += lhist[tid * GRP + ((i + tid) & (GRP - 1))];
     for (int t = tid; t < NBINS; t += 256) {
       const int h = lhist[t];
       if (h) atomicAdd(&gh[t], h);
     }
+    if (sum) atomicAdd(&gsum[tid], sum);
   }
 }
 

@@ -50,8 +50,12 @@ __device__ __forceinline__ void find_cut_bin(const int* hist, int k, int* scan_t
 }
 
 // Per-row selection state kept in device memory between the kernels of a row:
-//   hist[NBINS] | info[8] = {b*, above, cnt*, overflow, arrivals, -, -, -}
+//   hist[NBINS] | info[8] = {b*, above, cnt*, overflow, arrivals, -, -, -} |
+//   gsum[NGRP] (sums of GRP consecutive bins; kept only where the indexer builds
+//   the histogram) | ...
 constexpr int INFO = 8;
+constexpr int GRP = 32;
+constexpr int NGRP = NBINS / GRP;
 
 // Adds a workgroup's LDS histogram `hist` (NBINS counters, complete when called) into
 // the row's device histogram `gh`.  The last of the row's `n_parts` workgroups to

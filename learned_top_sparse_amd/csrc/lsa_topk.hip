@@ -161,6 +161,51 @@ struct RowView {
   }
 };
 
+// Ordered emission of one pass of 4*V*NT positions starting at `base`: thread t
+// holds positions base + 4*(v*NT + t) + c (c < 4) with selection bits m[v] and
+// payloads pl[v][c]; emit(rank, pos, payload) gets every selected position with its
+// rank in position order, starting at `running`.  wcnt: LDS int[V * NT/64].  One
+// barrier; all threads call; returns running + count.
+template <int NT, int V, typename Emit>
+__device__ __forceinline__ int ordered_emit4(int base, const unsigned (&m)[V], const int (&pl)[V][4], int* wc,
+                                             int running, Emit emit) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  unsigned long long bal[V][4];
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bal[v][c] = __ballot((m[v] >> c) & 1u);
+  if (lane == 0) {
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      wc[v * NW + wave] = __popcll(bal[v][0]) + __popcll(bal[v][1]) + __popcll(bal[v][2]) + __popcll(bal[v][3]);
+  }
+  __syncthreads();
+  int off = running;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int c = wc[v * NW + w];
+      pre += (w < wave) ? c : 0;
+      tot += c;
+    }
+    if (m[v]) {
+      int r = off + pre;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) r += lanes_below(bal[v][c]);
+      const int pos4 = base + 4 * (v * NT + (int)threadIdx.x);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((m[v] >> c) & 1u) emit(r++, pos4 + c, pl[v][c]);
+    }
+    off += tot;
+  }
+  return off;
+}
+
 // Ordered compaction over positions [lo, hi) (lo % 4 == 0) taken four at a time:
 // f4(pos4, payload[4]) returns a 4-bit selection mask; emit(rank, pos, payload) gets
 // each selected position with its rank in position order, starting at `running`.
@@ -168,7 +213,6 @@ struct RowView {
 template <int NT, int V, typename F4, typename Emit>
 __device__ __forceinline__ int ordered_compact4(int lo, int hi, int* wcnt, int running, F4 f4, Emit emit) {
   constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int parity = 0;
   for (int base = lo; base < hi; base += 4 * V * NT) {
     unsigned m[V];
@@ -183,40 +227,7 @@ __device__ __forceinline__ int ordered_compact4(int lo, int hi, int* wcnt, int r
         if (left < 4) m[v] &= (1u << left) - 1u;
       }
     }
-    unsigned long long bal[V][4];
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) bal[v][c] = __ballot((m[v] >> c) & 1u);
-    int* wc = wcnt + parity * V * NW;
-    if (lane == 0) {
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-        wc[v * NW + wave] = __popcll(bal[v][0]) + __popcll(bal[v][1]) + __popcll(bal[v][2]) + __popcll(bal[v][3]);
-    }
-    __syncthreads();
-    int off = running;
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      int pre = 0, tot = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const int c = wc[v * NW + w];
-        pre += (w < wave) ? c : 0;
-        tot += c;
-      }
-      if (m[v]) {
-        int r = off + pre;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) r += lanes_below(bal[v][c]);
-        const int pos4 = base + 4 * (v * NT + (int)threadIdx.x);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if ((m[v] >> c) & 1u) emit(r++, pos4 + c, pl[v][c]);
-      }
-      off += tot;
-    }
-    running = off;
+    running = ordered_emit4<NT, V>(base, m, pl, wcnt + parity * V * NW, running, emit);
     parity ^= 1;
   }
   __syncthreads();
@@ -499,7 +510,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const int32_t* __restrict__ sc
 //   cand[n_seg][CAP] (slot, score)
 // ints per row of the workspace, a multiple of 4 so every row's histogram is 16-byte aligned
 __host__ __device__ constexpr long long seg_row_ints(long long n_seg) {
-  return (NBINS + INFO + n_seg + 2 * n_seg * CAP + 3) / 4 * 4;
+  return (NBINS + INFO + NGRP + n_seg + 2 * n_seg * CAP + 3) / 4 * 4;
 }
 struct SegWs {
   int* base;
@@ -507,16 +518,18 @@ struct SegWs {
   __device__ __forceinline__ long long row_ints() const { return seg_row_ints(n_seg); }
   __device__ __forceinline__ int* hist(long long r) const { return base + r * row_ints(); }
   __device__ __forceinline__ int* info(long long r) const { return hist(r) + NBINS; }
-  __device__ __forceinline__ int* cnt(long long r) const { return info(r) + INFO; }
+  __device__ __forceinline__ int* gsum(long long r) const { return info(r) + INFO; }
+  __device__ __forceinline__ int* cnt(long long r) const { return gsum(r) + NGRP; }
   __device__ __forceinline__ int* cand(long long r, int seg) const { return cnt(r) + n_seg + 2ll * seg * CAP; }
 };
 
-// clears the histogram and the arrival counter of every row
+// clears the histogram, the group sums and the arrival counter of every row
 __global__ void topk_seg_zero_kernel(int* ws, long long row_ints, long long rows) {
   const long long r = blockIdx.y;
   if (r >= rows) return;
   int* h = ws + r * row_ints;
-  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < NBINS + INFO; t += gridDim.x * blockDim.x) h[t] = 0;
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < NBINS + INFO + NGRP; t += gridDim.x * blockDim.x)
+    h[t] = 0;
 }
 
 template <int NT, bool KEPT>
@@ -544,39 +557,85 @@ __global__ __launch_bounds__(NT) void topk_seg_hist_kernel(const int32_t* __rest
   merge_row_histogram<NT>(hist, ws.hist(row), ws.info(row), n_seg_row, k, scan_tmp, sh);
 }
 
+// One segment of a flat row: the entries of bins >= b* go, in slot order, to the
+// segment's candidate list in the workspace.  Every load the workgroup needs is
+// issued before any of them is used -- the row's position, its histogram (CUT) and
+// the segment's scores (read up to L_max and masked by the position afterwards) --
+// so the kernel waits out one memory latency instead of three.
 // CUT: the row's histogram is complete but its cut is not known yet (the indexer
 // built the histogram); every segment finds the cut itself and segment 0 records
 // it for the finish kernel.
-template <int NT, bool KEPT, bool CUT>
+template <int NT, bool CUT>
 __global__ __launch_bounds__(NT) void topk_seg_select_kernel(const int32_t* __restrict__ scores, long long ld,
-                                                             const int32_t* __restrict__ q_pos,
-                                                             const int32_t* __restrict__ kept, int bs, int n_keep,
-                                                             int L_max, int k, SegWs ws) {
+                                                             const int32_t* __restrict__ q_pos, int L_max, int k,
+                                                             SegWs ws) {
   constexpr int NW = NT / 64;
-  constexpr int V = 8;
-  __shared__ int wcnt[2 * V * NW];
+  constexpr int V = SEG / (4 * NT);  // one pass covers the segment
+  static_assert(4 * V * NT == SEG, "segment = one compaction pass");
+  static_assert(!CUT || NT == NGRP, "one group sum per thread");
+  __shared__ int wcnt[V * NW];
   __shared__ int scan_tmp[NW + 1];
-  __shared__ int kept_s[256];
   __shared__ int sh[8];
   const long long row = blockIdx.y;
   const int seg = blockIdx.x;
-  int n_valid;
-  const RowView<KEPT> rv = make_row<NT, KEPT>(scores, ld, q_pos, kept, bs, n_keep, L_max, row, kept_s, scan_tmp, &n_valid);
-  if (n_valid <= k) return;
-  const int lo = seg * SEG, hi = min(lo + SEG, rv.n_slots);
-  if (lo >= hi) return;
+  const int lo = seg * SEG, hi_max = min(lo + SEG, L_max);
+  const int32_t* srow = scores + row * ld;
   int* info = ws.info(row);
+
+  const int p_raw = q_pos[row];
+  int gs = 0, info0 = 0, info3 = 0;
+  if constexpr (CUT) {
+    gs = ws.gsum(row)[NGRP - 1 - (int)threadIdx.x];  // highest group first
+  } else {
+    info0 = info[0];
+    info3 = info[3];
+  }
+  const bool vec = (((uintptr_t)srow) & 15u) == 0;
+  int sc[V][4];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int pos4 = lo + 4 * (v * NT + (int)threadIdx.x);
+    if (vec && pos4 + 3 < hi_max) {
+      const v4i x = *(const v4i*)(srow + pos4);
+      sc[v][0] = x[0]; sc[v][1] = x[1]; sc[v][2] = x[2]; sc[v][3] = x[3];
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sc[v][c] = pos4 + c < hi_max ? srow[pos4 + c] : 0;
+    }
+  }
+
+  const int n_slots = max(min(p_raw, L_max - 1) + 1, 0);
+  if (n_slots <= k) return;  // every candidate is taken: the finish kernel lists them
+  const int hi = min(hi_max, n_slots);
+  if (lo >= hi) return;
   int bstar, overflow;
   if constexpr (CUT) {
-    __shared__ __attribute__((aligned(16))) int hcopy[NBINS];
-    const v4i* gh = reinterpret_cast<const v4i*>(ws.hist(row));
-    v4i hv[NBINS / 4 / NT];
-#pragma unroll
-    for (int u = 0; u < NBINS / 4 / NT; ++u) hv[u] = gh[u * NT + threadIdx.x];
-#pragma unroll
-    for (int u = 0; u < NBINS / 4 / NT; ++u) reinterpret_cast<v4i*>(hcopy)[u * NT + threadIdx.x] = hv[u];
+    // group holding the k-th best entry, then the bin inside it (one wave)
+    int tot;
+    const int excl = block_exclusive_scan<NT>(gs, scan_tmp, &tot);
+    if (excl < k && excl + gs >= k) {
+      sh[0] = NGRP - 1 - (int)threadIdx.x;
+      sh[1] = excl;
+    }
     __syncthreads();
-    find_cut_bin<NT>(hcopy, k, scan_tmp, sh);
+    if (threadIdx.x < 64) {
+      const int g = sh[0], lane = (int)threadIdx.x;
+      const int hb = lane < GRP ? ws.hist(row)[g * GRP + GRP - 1 - lane] : 0;  // highest bin first
+      int incl = hb;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      const unsigned long long hit = __ballot(sh[1] + incl >= k);
+      const int first = (int)__ffsll((long long)hit) - 1;
+      if (lane == first) {
+        sh[4] = g * GRP + GRP - 1 - lane;
+        sh[5] = sh[1] + incl - hb;
+        sh[6] = hb;
+      }
+    }
+    __syncthreads();
     bstar = sh[4];
     overflow = (sh[5] + sh[6] > CAP) ? 1 : 0;
     if (seg == 0 && threadIdx.x == 0) {
@@ -586,25 +645,25 @@ __global__ __launch_bounds__(NT) void topk_seg_select_kernel(const int32_t* __re
       info[3] = overflow;
     }
   } else {
-    bstar = info[0];
-    overflow = info[3];
+    bstar = info0;
+    overflow = info3;
   }
   if (overflow) return;  // the finish kernel selects from global memory
-  int* cand = ws.cand(row, seg);
-  const int n = ordered_compact4<NT, V>(
-      lo, hi, wcnt, 0,
-      [&](int s0, int (&pl)[4]) {
-        unsigned m = rv.load4(s0, pl), r = 0;
+  unsigned m[V];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) r |= (((m >> c) & 1u) && coarse_bin(pl[c]) >= bstar ? 1u : 0u) << c;
-        return r;
-      },
-      [&](int r, int s, int sc) {
-        if (r < CAP) {
-          cand[2 * r] = s;
-          cand[2 * r + 1] = sc;
-        }
-      });
+  for (int v = 0; v < V; ++v) {
+    const int pos4 = lo + 4 * (v * NT + (int)threadIdx.x);
+    m[v] = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) m[v] |= (pos4 + c < hi && coarse_bin(sc[v][c]) >= bstar ? 1u : 0u) << c;
+  }
+  int* cand = ws.cand(row, seg);
+  const int n = ordered_emit4<NT, V>(lo, m, sc, wcnt, 0, [&](int r, int s, int v) {
+    if (r < CAP) {
+      cand[2 * r] = s;
+      cand[2 * r + 1] = v;
+    }
+  });
   if (threadIdx.x == 0) ws.cnt(row)[seg] = n;
 }
 
@@ -624,6 +683,12 @@ __global__ __launch_bounds__(NT) void topk_seg_finish_kernel(const int32_t* __re
   __shared__ int seg_off[1025];
   const long long row = blockIdx.x;
   int32_t* out = idx + row * (long long)k;
+  // loads that do not depend on each other go out together: the row's cut and its
+  // first NT segment counts (read for every segment of the workspace; only the
+  // row's own are used), then the row's position
+  const int* info = ws.info(row);
+  const int bstar = info[0], above = info[1], overflow = info[3];
+  const int cnt0 = (int)threadIdx.x < ws.n_seg ? ws.cnt(row)[threadIdx.x] : 0;
   int n_valid;
   const RowView<KEPT> rv = make_row<NT, KEPT>(scores, ld, q_pos, kept, bs, n_keep, L_max, row, kept_s, scan_tmp, &n_valid);
   if (count != nullptr && threadIdx.x == 0) count[row] = min(k, n_valid);
@@ -631,9 +696,7 @@ __global__ __launch_bounds__(NT) void topk_seg_finish_kernel(const int32_t* __re
     select_all<NT, KEPT>(rv, n_valid, k, wcnt, out);
     return;
   }
-  const int* info = ws.info(row);
-  const int bstar = info[0], above = info[1];
-  if (info[3]) {
+  if (overflow) {
     fallback_select<NT, KEPT>(rv, k, lds_big, wcnt, h256, scan_tmp, sh, out);
     return;
   }
@@ -643,7 +706,7 @@ __global__ __launch_bounds__(NT) void topk_seg_finish_kernel(const int32_t* __re
     int carry = 0;
     for (int s0 = 0; s0 < n_seg; s0 += NT) {
       const int s = s0 + (int)threadIdx.x;
-      const int c = s < n_seg ? ws.cnt(row)[s] : 0;
+      const int c = s < n_seg ? (s0 == 0 ? cnt0 : ws.cnt(row)[s]) : 0;
       int tot;
       const int ex = block_exclusive_scan<NT>(c, scan_tmp, &tot);
       if (s < n_seg) seg_off[s] = carry + ex;
@@ -831,14 +894,14 @@ static void launch_topk_t(const TopkArgs& a, hipStream_t st, long long rows) {
     // several workgroups per row: histogram and candidate compaction split over segments
     const dim3 grid((unsigned)w.n_seg, (unsigned)rows);
     if (a.hist_ready) {
-      hipLaunchKernelGGL((topk_seg_select_kernel<256, KEPT, true>), grid, dim3(256), 0, st, a.scores, a.ld,
-                         a.q_pos, a.kept, a.block_size, a.n_keep, a.L_max, a.k, w);
+      hipLaunchKernelGGL((topk_seg_select_kernel<256, true>), grid, dim3(256), 0, st, a.scores, a.ld, a.q_pos,
+                         a.L_max, a.k, w);
     } else {
       hipLaunchKernelGGL(topk_seg_zero_kernel, dim3(8, (unsigned)rows), dim3(256), 0, st, w.base, row_ints, rows);
       hipLaunchKernelGGL((topk_seg_hist_kernel<256, KEPT>), grid, dim3(256), 0, st, a.scores, a.ld, a.q_pos,
                          a.kept, a.block_size, a.n_keep, a.L_max, a.k, w);
-      hipLaunchKernelGGL((topk_seg_select_kernel<256, KEPT, false>), grid, dim3(256), 0, st, a.scores, a.ld,
-                         a.q_pos, a.kept, a.block_size, a.n_keep, a.L_max, a.k, w);
+      hipLaunchKernelGGL((topk_seg_select_kernel<256, false>), grid, dim3(256), 0, st, a.scores, a.ld, a.q_pos,
+                         a.L_max, a.k, w);
     }
     hipLaunchKernelGGL((topk_seg_finish_kernel<256, KEPT>), dim3((unsigned)rows), dim3(256), 0, st, a.scores,
                        a.ld, a.q_pos, a.kept, a.block_size, a.n_keep, a.L_max, a.k, w, a.idx, a.count);
