@@ -51,13 +51,15 @@ __device__ __forceinline__ void reduce_scatter8_64(const long long (&v)[8], long
   for (int t = 0; t < 2; ++t) out[t] = xrow16_sum64(r1[t], r1[2 + t]);
 }
 
-// Load the A fragments (index-query heads) and head weights of one query.
+// Requests the A fragments (index-query heads) and the raw head weights of one
+// query.  Loads are unconditional (clamped to a valid head) so they are all in
+// flight at once; query_weights() then gives a padding head weight 0, which
+// cancels whatever its row produces.  Split in two so a caller can put more loads
+// in flight before the weights are first used.
 template <int D, int MT>
-__device__ __forceinline__ void load_query(const int8_t* __restrict__ q_idx, const int32_t* __restrict__ w,
-                                           int w_per_query, long long row, int H_I, bool valid,
-                                           v4i (&A)[MT][D / 64], int (&wt)[MT][4]) {
-  // Loads are unconditional (clamped to a valid head) so they are all in flight at
-  // once; a padding head gets weight 0, which cancels whatever its row produces.
+__device__ __forceinline__ void issue_query(const int8_t* __restrict__ q_idx, const int32_t* __restrict__ w,
+                                            int w_per_query, long long row, int H_I, v4i (&A)[MT][D / 64],
+                                            int (&wv)[MT][4]) {
   const int lane = lane_id(), g = lane >> 4, r16 = lane & 15;
   const int32_t* wr = w + (w_per_query ? row * H_I : 0);
 #pragma unroll
@@ -67,12 +69,24 @@ __device__ __forceinline__ void load_query(const int8_t* __restrict__ q_idx, con
 #pragma unroll
     for (int ks = 0; ks < D / 64; ++ks) A[mt][ks] = *(const v4i*)(qr + 16 * kchunk<D>(g, ks));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int hh = 16 * mt + 4 * g + e;
-      const int wv = wr[min(hh, H_I - 1)];
-      wt[mt][e] = (valid && hh < H_I) ? wv : 0;
-    }
+    for (int e = 0; e < 4; ++e) wv[mt][e] = wr[min(16 * mt + 4 * (lane >> 4) + e, H_I - 1)];
   }
+}
+template <int MT>
+__device__ __forceinline__ void query_weights(const int (&wv)[MT][4], int H_I, bool valid, int (&wt)[MT][4]) {
+  const int g = lane_id() >> 4;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wt[mt][e] = (valid && 16 * mt + 4 * g + e < H_I) ? wv[mt][e] : 0;
+}
+template <int D, int MT>
+__device__ __forceinline__ void load_query(const int8_t* __restrict__ q_idx, const int32_t* __restrict__ w,
+                                           int w_per_query, long long row, int H_I, bool valid,
+                                           v4i (&A)[MT][D / 64], int (&wt)[MT][4]) {
+  int wv[MT][4];
+  issue_query<D, MT>(q_idx, w, w_per_query, row, H_I, A, wv);
+  query_weights<MT>(wv, H_I, valid, wt);
 }
 
 constexpr int BUF_RSRC_WORD3 = 0x00020000;  // 32-bit data format, raw (untyped) access
@@ -242,70 +256,81 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
   __shared__ int lhist[HIST ? NBINS : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
   const long long row = blockIdx.y;
-  const int b = (int)(row / n_q);
-  const int p = min(q_pos[row], L_max - 1);
-  if (p < 0) return;
-
-  int s_begin, s_end;
+  const int b = (int)blockIdx.y / n_q;
+  // Flat rows: the span's keys are loaded (clamped to the cache) and scored whatever
+  // the query's position; the position only decides which scores are kept.  So the
+  // position, the query and the first key groups are all requested before any of
+  // them is waited for -- one memory latency at start-up instead of three.
+  const int p_raw = q_pos[row];
+  int p = 0, s_begin, s_lim, s_end;  // slots [s_begin, s_lim) are scored, [s_begin, s_end) kept
   if constexpr (KEPT) {
+    p = min(p_raw, L_max - 1);
+    if (p < 0) return;
     for (int t = tid; t < n_keep; t += 256) kept_s[t] = kept[row * n_keep + t];
     __syncthreads();
     s_begin = 0;
-    s_end = n_keep * bs;
+    s_lim = s_end = n_keep * bs;
   } else {
     s_begin = blockIdx.x * span;
-    s_end = min(s_begin + span, p + 1);
-    if (s_begin >= s_end) return;
+    s_lim = min(s_begin + span, L_max);
+    s_end = s_lim;  // narrowed to the position once it has arrived
   }
-
-  // a row with no more candidates than k takes them all: no histogram needed
-  const bool hist = HIST && p + 1 > k_top;
-  if (hist) {
-    for (int t = tid; t < NBINS; t += 256) lhist[t] = 0;
-    __syncthreads();
-  }
+  bool hist = false;
+  int bmin = NBINS, bmax = -1;  // bins this thread counted into
+  __shared__ int brange[2];
 
   v4i A[MT][KS];
-  int wt[MT][4];
-  load_query<D, MT>(q_idx, w, w_per_query, row, H_I, true, A, wt);
+  int wv[MT][4];
+  issue_query<D, MT>(q_idx, w, w_per_query, row, H_I, A, wv);
   const int8_t* kb = k_idx + (long long)b * L_max * D;
   const long long srow = row * ld;
 
-  // key of a slot, or -1 if the slot is not a candidate of this query
-  auto key_of = [&](int s) -> int {
-    if (s >= s_end) return -1;
+  // key a slot's scores come from (any slot below s_lim), and whether it is a
+  // candidate of this query
+  auto key_load = [&](int s) -> int {
     if constexpr (KEPT) {
-      const int blk = kept_s[s / bs];
-      if (blk < 0) return -1;
-      const int j = blk * bs + s % bs;
-      return (j <= p) ? j : -1;
+      const int blk = kept_s[s / bs];  // the query's own block may run past the cache
+      return blk >= 0 ? min(blk * bs + s % bs, L_max - 1) : 0;
     } else {
       return s;
     }
   };
+  auto is_cand = [&](int s) -> bool {
+    if (s >= s_end) return false;
+    if constexpr (KEPT) {
+      const int blk = kept_s[s / bs];
+      return blk >= 0 && blk * bs + s % bs <= p;
+    } else {
+      return true;
+    }
+  };
 
+  // Slots are processed in chunks of SBUF (one chunk for flat rows); the chunk's
+  // scores leave LDS after its ring loop.  The ring loop is branch-free so the
+  // compiler's wait counts stay exact: every wave runs the same number of iterations
+  // (a multiple of RING) and loads past its last group re-read a row already in cache.
   v4i ring[RING][4][KS];
-  // Slots are processed in chunks of SBUF; the chunk's scores leave LDS after its ring
-  // loop.  The ring loop is branch-free so the compiler's wait counts stay exact: every
-  // wave runs the same number of iterations (a multiple of RING) and loads past its
-  // last group re-read a row already in cache.
-  for (int c0 = s_begin; c0 < s_end; c0 += SBUF) {
-    const int c1 = min(c0 + SBUF, s_end);
+  auto load_group = [&](int c0, int c1, int i, v4i (&Bf)[4][KS]) {
+    const int sg = c0 + 64 * (wave + 4 * i);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      // a slot past the chunk (or without a kept block) reads a fallback row: its
+      // score is never kept, and unconditional loads stay in flight together
+      const int s = min(sg + 16 * nt + r16, c1 - 1);
+      const int8_t* kr = kb + (long long)key_load(s) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
+    }
+  };
+  auto prologue = [&](int c0, int c1) {
+#pragma unroll
+    for (int r = 0; r < RING - 1; ++r) load_group(c0, c1, r, ring[r]);
+  };
+  int wt[MT][4];
+  // the ring loop and score flush of one chunk whose prologue has been issued
+  auto run_chunk = [&](int c0, int c1) {
     const int n_groups = (c1 - c0 + 63) / 64;
     const int n_iter = ((n_groups + 3) / 4 + RING - 1) / RING * RING;  // groups per wave, padded
-    auto load_group = [&](int i, v4i (&Bf)[4][KS]) {
-      const int sg = c0 + 64 * (wave + 4 * i);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        // a slot without a key (or past the chunk) reads a fallback row: its column's
-        // score is never stored, and unconditional loads stay in flight together
-        const int s = min(sg + 16 * nt + r16, c1 - 1);
-        const int j = max(key_of(s), 0);
-        const int8_t* kr = kb + (long long)j * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
-      }
-    };
     auto compute_group = [&](int i, const v4i (&Bf)[4][KS]) {
       const int sg = c0 + 64 * (wave + 4 * i);
       int part[4];
@@ -330,37 +355,91 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
       if (s < c1) {
         sbuf[s - c0] = res;
         // LDS only, inside the ring loop where the waves mostly wait on HBM anyway
-        if (hist) atomicAdd(&lhist[coarse_bin(res)], 1);
+        if (hist && s < s_end) {
+          const int bin = coarse_bin(res);
+          atomicAdd(&lhist[bin], 1);
+          bmin = min(bmin, bin);
+          bmax = max(bmax, bin);
+        }
       }
     };
-#pragma unroll
-    for (int r = 0; r < RING - 1; ++r) load_group(r, ring[r]);
     for (int i0 = 0; i0 < n_iter; i0 += RING) {
 #pragma unroll
       for (int r = 0; r < RING; ++r) {
-        load_group(i0 + r + RING - 1, ring[(r + RING - 1) % RING]);
+        load_group(c0, c1, i0 + r + RING - 1, ring[(r + RING - 1) % RING]);
         compute_group(i0 + r, ring[r]);
       }
     }
     __syncthreads();
-    for (int t = tid; t < c1 - c0; t += 256)
-      if (key_of(c0 + t) >= 0) scores[srow + c0 + t] = sbuf[t];
+    if (!KEPT && (reinterpret_cast<uintptr_t>(scores + srow + c0) & 15) == 0) {
+      // flat rows: the whole chunk in 16-byte non-temporal stores (scores of keys past
+      // the query's position may be written: they are unspecified), which disturb the
+      // key stream less than dword stores
+      const int n4 = (c1 - c0) / 4;
+      for (int t = tid; t < n4; t += 256)
+        __builtin_nontemporal_store(*(const v4i*)&sbuf[4 * t], (v4i*)(scores + srow + c0 + 4 * t));
+      for (int t = 4 * n4 + tid; t < c1 - c0; t += 256) scores[srow + c0 + t] = sbuf[t];
+    } else {
+      for (int t = tid; t < c1 - c0; t += 256)
+        if (is_cand(c0 + t)) scores[srow + c0 + t] = sbuf[t];
+    }
     __syncthreads();
+  };
+
+  if constexpr (KEPT) {
+    query_weights<MT>(wv, H_I, true, wt);
+    for (int c0 = s_begin; c0 < s_lim; c0 += SBUF) {
+      const int c1 = min(c0 + SBUF, s_lim);
+      prologue(c0, c1);
+      run_chunk(c0, c1);
+    }
+  } else {
+    // the first key groups go out with the query and the position, before any wait
+    prologue(s_begin, s_lim);
+    query_weights<MT>(wv, H_I, true, wt);
+    p = min(p_raw, L_max - 1);
+    s_end = min(s_lim, p + 1);
+    if (s_begin >= s_end) return;  // nothing of this span is a candidate (uniform)
+    // a row with no more candidates than k takes them all: no histogram needed
+    hist = HIST && p + 1 > k_top;
+    if (hist) {
+      for (int t = tid; t < NBINS; t += 256) lhist[t] = 0;
+      if (tid == 0) {
+        brange[0] = NBINS;
+        brange[1] = -1;
+      }
+      __syncthreads();
+    }
+    run_chunk(s_begin, s_lim);
   }
   if (hist) {
-    // bins go out in lane order (a wave's atomics touch few cache lines); thread t
-    // also sums group t in LDS (skewed order: the lanes of a wave read distinct banks)
+    // Only the bins this workgroup touched are visited (a row's scores fill a narrow
+    // band of bins).  Bins go out in lane order (a wave's atomics touch few cache
+    // lines); thread t also sums group t in LDS if the group meets the band (skewed
+    // order: the lanes of a wave read distinct banks).
     static_assert(NGRP == 256, "one group per thread");
+    for (int o = 32; o > 0; o >>= 1) {
+      bmin = min(bmin, __shfl_xor(bmin, o));
+      bmax = max(bmax, __shfl_xor(bmax, o));
+    }
+    if (lane == 0) {
+      atomicMin(&brange[0], bmin);
+      atomicMax(&brange[1], bmax);
+    }
+    __syncthreads();
+    const int lo = brange[0], hi = brange[1];
     int* gh = sel_hist + row * sel_row_ints;
     int* gsum = gh + NBINS + INFO;
-    int sum = 0;
+    if (tid * GRP <= hi && tid * GRP + GRP > lo) {
+      int sum = 0;
 #pragma unroll 8
-    for (int i = 0; i < GRP; ++i) sum += lhist[tid * GRP + ((i + tid) & (GRP - 1))];
-    for (int t = tid; t < NBINS; t += 256) {
+      for (int i = 0; i < GRP; ++i) sum += lhist[tid * GRP + ((i + tid) & (GRP - 1))];
+      if (sum) atomicAdd(&gsum[tid], sum);
+    }
+    for (int t = lo + tid; t <= hi; t += 256) {
       const int h = lhist[t];
       if (h) atomicAdd(&gh[t], h);
     }
-    if (sum) atomicAdd(&gsum[tid], sum);
   }
 }
 
@@ -537,6 +616,8 @@ static hipError_t launch_flat_t(const IdxArgs& a, hipStream_t st) {
 }
 template <int D, int MT, bool KEPT>
 static hipError_t launch_direct_t(const IdxArgs& a, hipStream_t st) {
+  // flat rows: one span per workgroup, exactly the LDS score buffer
+  if (!KEPT && a.span != DIRECT_SPAN) return hipErrorInvalidValue;
   const int n_spans = KEPT ? 1 : (a.L_max + a.span - 1) / a.span;
   dim3 grid((unsigned)n_spans, (unsigned)(a.B * a.n_q));
   if constexpr (!KEPT) {
