@@ -29,12 +29,14 @@ inline int flat_span(int32_t L_max, bool direct) {
 }
 
 // automatic split count of the sparse attention: with few rows, cut each list so the
-// launch holds about 2048 waves, all resident at once (at least one 32-key tile per wave)
+// launch holds about 1024 waves (one per SIMD; each wave pipelines its tiles, so
+// more, shorter waves only add merge work), at least one 32-key tile per wave
 inline int attn_split_auto(long long rows, int32_t k_top) {
+  constexpr long long kWaves = 1024;
   const long long n_tiles = (k_top + 31) / 32;
   const long long max_split = std::max<long long>(1, n_tiles / lsa::ATTN_WAVES);
-  if (rows * lsa::ATTN_WAVES >= 2048) return 1;
-  const long long s = (2048 + rows * lsa::ATTN_WAVES - 1) / (rows * lsa::ATTN_WAVES);
+  if (rows * lsa::ATTN_WAVES >= kWaves) return 1;
+  const long long s = (kWaves + rows * lsa::ATTN_WAVES - 1) / (rows * lsa::ATTN_WAVES);
   return (int)std::max<long long>(1, std::min<long long>(s, max_split));
 }
 

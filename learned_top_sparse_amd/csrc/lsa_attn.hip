@@ -78,7 +78,7 @@ constexpr int WAVE_LDS = D * RSD;  // dwords of LDS per wave: the transposed V t
 // heads, and at the end the NW states are merged through LDS.  n_split == 1 writes
 // the bf16 output and LSE; otherwise a normalised fp32 partial and its LSE go to ws.
 template <int NW>
-__global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(
+__global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ idx, int n_q, int L_max, int H_q, int k_top, float scale_log2,
     int n_split, __bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws) {
@@ -114,61 +114,67 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(
   const int n_tiles = (k_top + KT - 1) / KT;
   const int t_begin = (int)((long long)n_tiles * split / n_split);
   const int t_end = (int)((long long)n_tiles * (split + 1) / n_split);
+  // this wave's tiles: t_begin + wave + NW*i for i < n_my
+  const int first = t_begin + wave;
+  const int n_my = first < t_end ? (t_end - first + NW - 1) / NW : 0;
 
-  for (int t = t_begin + wave; t < t_end; t += NW) {
-    const int base = t * KT;
-    // indices: keys (l&15) and 16+(l&15) for the K fragments, pair 2*(l&15)+{0,1} for V
-    auto load_j = [&](int pos) -> int {
-      if (pos >= k_top) return -1;
-      const int j = jrow[pos];
-      return (j >= 0 && j < L_max) ? j : -1;
-    };
-    int jA = load_j(base + r16), jB = load_j(base + 16 + r16);
-    int j0 = load_j(base + 2 * r16), j1 = load_j(base + 2 * r16 + 1);
-    const unsigned long long vA = __ballot(jA >= 0), vB = __ballot(jB >= 0);
-    if ((vA | vB) == 0ull) continue;
-    // Entries without a key read the rows of a listed key of this tile instead: loads
-    // stay unconditional (all in flight together), the key's score is masked to -inf,
-    // so its weight is exactly 0 and the borrowed V row (finite, or listed anyway)
-    // adds nothing.
-    {
-      const int src = vA ? __ffsll((long long)vA) - 1 : __ffsll((long long)vB) - 1;
-      const int jfill = vA ? __shfl(jA, src) : __shfl(jB, src);
-      jA = jA < 0 ? jfill : jA;
-      jB = jB < 0 ? jfill : jB;
-      j0 = j0 < 0 ? jfill : j0;
-      j1 = j1 < 0 ? jfill : j1;
-    }
-
-    // gathers: every load instruction reads whole 64-byte pieces of 16 rows
+  // Software pipeline over the wave's tiles: index entries two tiles ahead, K/V
+  // gathers one tile ahead, ping-pong register sets (no copies).  Every load is
+  // unconditional -- tiles past the wave's last one re-read that tile and are not
+  // computed -- so the compiler's wait counts stay exact.
+  struct Idx {
+    int jA, jB, j0, j1;
+  };
+  struct Gat {
     Frag8 Ka[2][4];
-    {
-      const __bf16* ra = kb + (long long)jA * D + 8 * g;
-      const __bf16* rb = kb + (long long)jB * D + 8 * g;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        Ka[0][s].u = *(const v4u*)(ra + 32 * s);
-        Ka[1][s].u = *(const v4u*)(rb + 32 * s);
-      }
+    v4u V0[4], V1[4];
+    unsigned long long vA, vB;
+  };
+  auto load_idx = [&](int i) -> Idx {
+    const int base = (first + NW * min(i, n_my - 1)) * KT;
+    auto e = [&](int pos) -> int { return jrow[min(pos, k_top - 1)] | (pos < k_top ? 0 : -1); };
+    return Idx{e(base + r16), e(base + 16 + r16), e(base + 2 * r16), e(base + 2 * r16 + 1)};
+  };
+  auto gather = [&](Idx x, Gat& G) {
+    auto ok = [&](int j) { return j >= 0 && j < L_max; };
+    G.vA = __ballot(ok(x.jA));
+    G.vB = __ballot(ok(x.jB));
+    // Entries without a key read the rows of a listed key of this tile instead (row 0
+    // if none is listed; the tile is then skipped): its score is masked to -inf, so
+    // its weight is exactly 0 and the borrowed V row (finite, or listed anyway) adds
+    // nothing.
+    int jfill = 0;
+    if (G.vA | G.vB) {
+      const int src = G.vA ? __ffsll((long long)G.vA) - 1 : __ffsll((long long)G.vB) - 1;
+      jfill = G.vA ? __shfl(x.jA, src) : __shfl(x.jB, src);
     }
-    v4u V0[4], V1[4];  // rows j0 / j1, d = 8g + 32m .. +8
-    {
-      const __bf16* r0 = vb + (long long)j0 * D + 8 * g;
-      const __bf16* r1 = vb + (long long)j1 * D + 8 * g;
+    const int jA = ok(x.jA) ? x.jA : jfill, jB = ok(x.jB) ? x.jB : jfill;
+    const int j0 = ok(x.j0) ? x.j0 : jfill, j1 = ok(x.j1) ? x.j1 : jfill;
+    // every load instruction reads whole 64-byte pieces of 16 rows
+    const __bf16* ra = kb + (long long)jA * D + 8 * g;
+    const __bf16* rb = kb + (long long)jB * D + 8 * g;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        V0[m] = *(const v4u*)(r0 + 32 * m);
-        V1[m] = *(const v4u*)(r1 + 32 * m);
-      }
+    for (int s = 0; s < 4; ++s) {
+      G.Ka[0][s].u = *(const v4u*)(ra + 32 * s);
+      G.Ka[1][s].u = *(const v4u*)(rb + 32 * s);
     }
-
+    const __bf16* r0 = vb + (long long)j0 * D + 8 * g;  // rows j0 / j1, d = 8g + 32m .. +8
+    const __bf16* r1 = vb + (long long)j1 * D + 8 * g;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      G.V0[m] = *(const v4u*)(r0 + 32 * m);
+      G.V1[m] = *(const v4u*)(r1 + 32 * m);
+    }
+  };
+  auto compute = [&](const Gat& G) {
+    if ((G.vA | G.vB) == 0ull) return;
     // S^T = K Q^T : lane holds keys 16*mt + 4g + i for head r16
     v4f S[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       S[mt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) S[mt] = mfma_bf16(Ka[mt][s].v, Qb[s].v, S[mt]);
+      for (int s = 0; s < 4; ++s) S[mt] = mfma_bf16(G.Ka[mt][s].v, Qb[s].v, S[mt]);
     }
 
     // V^T into this wave's LDS tile: dword [d][kp] = (V[2kp][d], V[2kp+1][d]), d = 8g + 32m + e
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
       for (int w2 = 0; w2 < 4; ++w2) {
-        const u32 a = V0[m][w2], c = V1[m][w2];
+        const u32 a = G.V0[m][w2], c = G.V1[m][w2];
         const int d = 8 * g + 32 * m + 2 * w2;
         vt[d * RSD + r16] = __builtin_amdgcn_perm(c, a, 0x05040100u);        // low halves
         vt[(d + 1) * RSD + r16] = __builtin_amdgcn_perm(c, a, 0x07060302u);  // high halves
@@ -189,12 +195,12 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(
     float mt_max = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const unsigned long long vm = mt ? vB : vA;
+      const unsigned long long vm = mt ? G.vB : G.vA;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = 4 * g + i;
-        const bool ok = (vm >> key) & 1ull;
-        sv[mt][i] = ok ? S[mt][i] * scale_log2 : -INFINITY;
+        const bool okk = (vm >> key) & 1ull;
+        sv[mt][i] = okk ? S[mt][i] * scale_log2 : -INFINITY;
         mt_max = fmaxf(mt_max, sv[mt][i]);
       }
     }
@@ -233,6 +239,21 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(
       const v2u hi = *(const v2u*)(&vt[d * RSD + 8 + 2 * g]);
       Va.u = v4u{lo[0], lo[1], hi[0], hi[1]};
       O[dt] = mfma_bf16(Va.v, Pb.v, O[dt]);
+    }
+  };
+
+  if (n_my > 0) {
+    Idx x0 = load_idx(0), x1 = load_idx(1);
+    Gat G0, G1;
+    gather(x0, G0);
+    x0 = load_idx(2);
+    for (int i = 0; i < n_my; i += 2) {
+      gather(x1, G1);  // tile i+1
+      x1 = load_idx(i + 3);
+      compute(G0);     // tile i
+      gather(x0, G0);  // tile i+2
+      x0 = load_idx(i + 4);
+      if (i + 1 < n_my) compute(G1);
     }
   }
 
