@@ -175,6 +175,31 @@ def cpu_baseline(wl, inp, budget_s=10.0):
                       f"(numpy fp64 BLAS, int64 scores); rate = rows / time"}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_128k_index_traffic.md")
+TRAFFIC_SOURCES = ["learned_top_sparse_amd/csrc/lsa_indexer.hip", "learned_top_sparse_amd/csrc/lsa_device.h",
+                   "learned_top_sparse_amd/csrc/lsa_select.h"]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode indexer from the committed rocprofv3 counter
+    runs (FETCH_SIZE + WRITE_SIZE, each scaled by a 1 GiB copy's reading), or None if the
+    kernel's sources changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        txt = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"^traffic_bytes_per_launch: (\d+)$", txt, re.M)
+    h = re.search(r"^kernel_sources_sha256: ([0-9a-f]{64})$", txt, re.M)
+    if not (m and h):
+        return None
+    d = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        d.update(open(os.path.join(ROOT, f), "rb").read())
+    return int(m.group(1)) if d.hexdigest() == h.group(1) else None
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=5):
     """Plain device copy of a known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
     a = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
@@ -265,7 +290,7 @@ def main():
         "roofline": {
             "bound": "hbm", "kernel": "index_scores (decode scan, idx_direct_kernel)",
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": alg["index_bytes"] / launches, "launch_ms": idx_ms,
         },
         "kernel_ms": kms,
