@@ -373,16 +373,17 @@ namespace {
 // A chunk of flat, one-query-per-sequence rows whose top-k splits each row over
 // several workgroups: the indexer builds the rows' score histograms itself.
 bool chunk_fused(const lsa_forward_args* a, int32_t nb, int32_t ni, void* topk_ws, size_t topk_ws_size) {
-  if (a->two_stage || ni >= 8) return false;
+  // the per-row finish reads one span list per thread: at most 256 spans of 2048 keys
+  if (a->two_stage || ni >= 8 || a->L_max > 256 * 2048) return false;
   lsa::TopkArgs ta{};
   ta.B = nb;
   ta.n_q = ni;
   ta.L_max = a->L_max;
   ta.ws = topk_ws;
   ta.ws_bytes = topk_ws_size;
-  int* hist = nullptr;
-  long long row_ints = 0;
-  return lsa::topk_split_rows(ta, &hist, &row_ints);
+  int* base = nullptr;
+  int n_seg = 0, n_lst = 0;
+  return lsa::topk_split_rows(ta, &base, &n_seg, &n_lst);
 }
 
 // chunks of lsa_forward for `rows` rows per chunk, as (b0, nb, i0, ni)
@@ -549,9 +550,9 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
     ta.ws = topk_ws;
     ta.ws_bytes = topk_ws_size;
     if (chunk_fused(a, nb, ni, topk_ws, topk_ws_size)) {
-      // the indexer adds each row's score histogram into the selection state
+      // the indexer builds each row's selection state (histogram, span candidate lists)
       if (lsa::launch_topk_reset(ta, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
-      if (!lsa::topk_split_rows(ta, &ia.sel_hist, &ia.sel_row_ints)) return LSA_ERR_INTERNAL;
+      if (!lsa::topk_split_rows(ta, &ia.sel_base, &ia.sel_n_seg, &ia.sel_n_lst)) return LSA_ERR_INTERNAL;
       ia.k_top = kt;
       ta.hist_ready = true;
     }

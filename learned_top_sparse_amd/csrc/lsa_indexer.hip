@@ -18,9 +18,6 @@
 
 namespace lsa {
 
-// keys per workgroup of the direct (decode-shaped) flat indexer
-constexpr int DIRECT_SPAN = 2048;
-
 // 16-byte chunk of the d_I bytes supplied by lane row g at K-step ks.  A and B
 // use the same assignment, so the product is the full dot product.  At one K-step
 // the four lane rows read four consecutive chunks, so every load instruction takes
@@ -233,17 +230,19 @@ __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
 // (KEPT: slot s is key kept[s / bs] * bs + s % bs; one workgroup covers all slots).
 // The scan is bound by HBM, so each wave keeps a ring of RING groups of fragments:
 // RING-1 groups of loads are in flight while one group is multiplied (2 waves/SIMD).
-// HIST (flat only): the workgroup also counts its scores into an LDS histogram of
-// the selection's coarse bins and adds it to the row's histogram in device memory
-// (sel_hist + row * sel_row_ints, cleared beforehand), so the exact top-k that
-// follows needs no histogram pass of its own over the row.
+// HIST (flat only): the workgroup also builds its share of the row's selection
+// state in the split top-k's workspace (SegWs, cleared beforehand): it counts its
+// scores into an LDS histogram of the selection's coarse bins, adds the bins it
+// touched to the row's histogram (device-scope atomics), and writes its span's
+// candidate list -- the entries of its highest bins, in slot order -- so the exact
+// top-k that follows reads neither the score table nor a histogram pass.
 // Grid: x = n_spans (1 for KEPT), y = B * n_q.
 template <int D, int MT, bool KEPT, bool HIST>
 __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
     int w_per_query, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ kept, int bs,
     int n_keep, int n_q, int L_max, int H_I, int span, int32_t* __restrict__ scores, long long ld,
-    int* __restrict__ sel_hist, long long sel_row_ints, int k_top) {
+    SegWs sel, int k_top) {
   static_assert(!(KEPT && HIST), "the histogram is built for flat rows only");
   constexpr int KS = D / 64;
   constexpr int RING = 4;
@@ -278,6 +277,9 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
   bool hist = false;
   int bmin = NBINS, bmax = -1;  // bins this thread counted into
   __shared__ int brange[2];
+  __shared__ int wcnt_l[2 * 4 * 4];
+  __shared__ int scan_l[5];
+  __shared__ int lsh[2];
 
   v4i A[MT][KS];
   int wv[MT][4];
@@ -414,9 +416,7 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
   }
   if (hist) {
     // Only the bins this workgroup touched are visited (a row's scores fill a narrow
-    // band of bins).  Bins go out in lane order (a wave's atomics touch few cache
-    // lines); thread t also sums group t in LDS if the group meets the band (skewed
-    // order: the lanes of a wave read distinct banks).
+    // band of bins).
     static_assert(NGRP == 256, "one group per thread");
     for (int o = 32; o > 0; o >>= 1) {
       bmin = min(bmin, __shfl_xor(bmin, o));
@@ -428,8 +428,58 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
     }
     __syncthreads();
     const int lo = brange[0], hi = brange[1];
-    int* gh = sel_hist + row * sel_row_ints;
-    int* gsum = gh + NBINS + INFO;
+
+    // The span's candidate list: lowest bin bw such that bins >= bw hold at least
+    // need = min(LIST_MIN, entries) entries; if that bin would overflow LIST_CAP the
+    // list stops above it (fewer entries; the top-k then checks bw against its cut).
+    // Thread t sums a chunk of CB bins from the top of the band, a block scan finds
+    // the chunk where the count crosses need, and that thread walks its chunk.
+    {
+      const int n_ent = s_end - s_begin, need = min(LIST_MIN, n_ent);
+      const int CB = (hi - lo + 256) / 256;
+      const int top = hi - tid * CB;  // this thread's bins: top, top-1, ..., top-CB+1 (>= lo)
+      int csum = 0;
+      for (int i = 0; i < CB; ++i) csum += top - i >= lo ? lhist[top - i] : 0;
+      int tot;
+      const int excl = block_exclusive_scan<256>(csum, scan_l, &tot);
+      if (excl < need && excl + csum >= need) {
+        int acc = excl;
+        for (int i = 0; i < CB; ++i) {
+          const int b = top - i;
+          const int h = b >= lo ? lhist[b] : 0;
+          if (acc + h >= need) {
+            lsh[0] = acc + h <= LIST_CAP ? b : b + 1;
+            break;
+          }
+          acc += h;
+        }
+      }
+      __syncthreads();
+      const int bw = lsh[0];
+      int* lc = sel.lcand(row, blockIdx.x);
+      const int n_list = ordered_compact<256, 4>(
+          n_ent, wcnt_l,
+          [&](int t, int& v) {
+            v = sbuf[t];
+            return coarse_bin(v) >= bw;
+          },
+          [&](int r, int t, int v) {
+            if (r < LIST_CAP) {
+              lc[2 * r] = s_begin + t;
+              lc[2 * r + 1] = v;
+            }
+          });
+      if (tid == 0) {
+        sel.lcnt(row)[blockIdx.x] = min(n_list, LIST_CAP);
+        sel.lbw(row)[blockIdx.x] = bw;
+      }
+    }
+
+    // histogram: bins go out in lane order (a wave's atomics touch few cache lines);
+    // thread t also sums group t in LDS if the group meets the band (skewed order:
+    // the lanes of a wave read distinct banks)
+    int* gh = sel.hist(row);
+    int* gsum = sel.gsum(row);
     if (tid * GRP <= hi && tid * GRP + GRP > lo) {
       int sum = 0;
 #pragma unroll 8
@@ -621,16 +671,21 @@ static hipError_t launch_direct_t(const IdxArgs& a, hipStream_t st) {
   const int n_spans = KEPT ? 1 : (a.L_max + a.span - 1) / a.span;
   dim3 grid((unsigned)n_spans, (unsigned)(a.B * a.n_q));
   if constexpr (!KEPT) {
-    if (a.sel_hist != nullptr) {
+    if (a.sel_base != nullptr) {
+      SegWs sel;
+      sel.base = a.sel_base;
+      sel.n_seg = a.sel_n_seg;
+      sel.n_lst = a.sel_n_lst;
+      if (n_spans > sel.n_lst) return hipErrorInvalidValue;
       hipLaunchKernelGGL((idx_direct_kernel<D, MT, false, true>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.w,
                          a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I,
-                         a.span, a.scores, (long long)a.ld, a.sel_hist, a.sel_row_ints, a.k_top);
+                         a.span, a.scores, (long long)a.ld, sel, a.k_top);
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((idx_direct_kernel<D, MT, KEPT, false>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.w,
                      a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I,
-                     a.span, a.scores, (long long)a.ld, nullptr, 0ll, 0);
+                     a.span, a.scores, (long long)a.ld, SegWs{}, 0);
   return hipGetLastError();
 }
 

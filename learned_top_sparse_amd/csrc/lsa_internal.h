@@ -19,10 +19,11 @@ struct IdxArgs {
   long long ld;
   int span;        // keys per workgroup span (flat)
   bool use_direct; // flat scores with one query per workgroup (decode-shaped)
-  // optional (direct flat only): also add each row's coarse score histogram into
-  // the selection state of the row (cleared beforehand by launch_topk_reset)
-  int* sel_hist;
-  long long sel_row_ints;
+  // optional (direct flat only): also build each row's selection state -- its
+  // coarse score histogram and one candidate list per span -- in the split top-k's
+  // workspace (cleared beforehand by launch_topk_reset)
+  int* sel_base;
+  int sel_n_seg, sel_n_lst;
   int k_top;
 };
 
@@ -87,8 +88,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 // workspace that lets lsa_topk split each row over several workgroups (0 = not used)
 size_t topk_ws_bytes(long long rows, int L_max);
 // The several-workgroups path applies to these arguments (flat rows, workspace big
-// enough): returns the per-row histogram base and row stride for the indexer.
-bool topk_split_rows(const TopkArgs& a, int** hist, long long* row_ints);
+// enough): returns the workspace layout the indexer fills (base, segments, lists).
+bool topk_split_rows(const TopkArgs& a, int** base, int* n_seg, int* n_lst);
 // clears the selection state (histograms, counters) of every row of `a`
 hipError_t launch_topk_reset(const TopkArgs& a, hipStream_t st);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);

@@ -49,13 +49,92 @@ __device__ __forceinline__ void find_cut_bin(const int* hist, int k, int* scan_t
   __syncthreads();
 }
 
-// Per-row selection state kept in device memory between the kernels of a row:
-//   hist[NBINS] | info[8] = {b*, above, cnt*, overflow, arrivals, -, -, -} |
-//   gsum[NGRP] (sums of GRP consecutive bins; kept only where the indexer builds
-//   the histogram) | ...
 constexpr int INFO = 8;
 constexpr int GRP = 32;
 constexpr int NGRP = NBINS / GRP;
+// keys per workgroup of the direct (decode-shaped) flat indexer
+constexpr int DIRECT_SPAN = 2048;
+// slots per workgroup in the several-workgroups-per-row top-k
+constexpr int SEG = 8192;
+// Candidate list the direct indexer keeps per span when it builds the row's
+// histogram: the span's entries in its highest coarse bins, in slot order -- at
+// least LIST_MIN of them (all, if the span has fewer), at most LIST_CAP -- and the
+// lowest bin it took (lbw).  Every entry of the span below lbw is out of the list.
+constexpr int LIST_MIN = 64;
+constexpr int LIST_CAP = 512;
+
+// Per-row selection state of the several-workgroups top-k in its workspace:
+//   hist[NBINS] | info[INFO] = {b*, above, cnt*, overflow, arrivals, -, -, -} |
+//   gsum[NGRP] (sums of GRP consecutive bins; kept where the indexer builds the
+//   histogram) | cnt[n_seg] | lcnt[n_lst] | lbw[n_lst] | cand
+// cand holds either n_seg segment candidate lists of CAP (slot, score) pairs or the
+// indexer's n_lst span lists of LIST_CAP pairs.  Rows are a multiple of 4 ints long,
+// so every row's histogram is 16-byte aligned.
+struct SegWs {
+  int* base;
+  int n_seg, n_lst;
+  __host__ __device__ static constexpr long long row_ints_for(long long n_seg, long long n_lst) {
+    return (NBINS + INFO + NGRP + n_seg + 2 * n_lst +
+            (2 * n_seg * CAP > 2 * n_lst * LIST_CAP ? 2 * n_seg * CAP : 2 * n_lst * LIST_CAP) + 3) / 4 * 4;
+  }
+  __host__ __device__ long long row_ints() const { return row_ints_for(n_seg, n_lst); }
+  __device__ __forceinline__ int* hist(long long r) const { return base + r * row_ints(); }
+  __device__ __forceinline__ int* info(long long r) const { return hist(r) + NBINS; }
+  __device__ __forceinline__ int* gsum(long long r) const { return info(r) + INFO; }
+  __device__ __forceinline__ int* cnt(long long r) const { return gsum(r) + NGRP; }
+  __device__ __forceinline__ int* lcnt(long long r) const { return cnt(r) + n_seg; }
+  __device__ __forceinline__ int* lbw(long long r) const { return lcnt(r) + n_lst; }
+  __device__ __forceinline__ int* cand(long long r, int seg) const { return lbw(r) + n_lst + 2ll * seg * CAP; }
+  __device__ __forceinline__ int* lcand(long long r, int w) const { return lbw(r) + n_lst + 2ll * w * LIST_CAP; }
+};
+
+// Ordered compaction over positions [0, n): pred(pos, payload&) selects; emit(rank,
+// pos, payload) is called for selected positions with their rank in position order.
+// wcnt: LDS int[2 * V * NT/64].  All threads must call; returns the count.
+template <int NT, int V, typename Pred, typename Emit>
+__device__ __forceinline__ int ordered_compact(int n, int* wcnt, Pred pred, Emit emit) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int running = 0, parity = 0;
+  for (int base = 0; base < n; base += V * NT) {
+    bool f[V];
+    int pl[V];
+    unsigned long long bal[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int pos = base + v * NT + (int)threadIdx.x;
+      pl[v] = 0;
+      f[v] = (pos < n) && pred(pos, pl[v]);
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) bal[v] = __ballot(f[v]);
+    int* wc = wcnt + parity * V * NW;
+    if (lane == 0) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) wc[v * NW + wave] = __popcll(bal[v]);
+    }
+    __syncthreads();
+    int off = running;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      int pre = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int c = wc[v * NW + w];
+        pre += (w < wave) ? c : 0;
+        tot += c;
+      }
+      if (f[v]) emit(off + pre + lanes_below(bal[v]), base + v * NT + (int)threadIdx.x, pl[v]);
+      off += tot;
+    }
+    running = off;
+    parity ^= 1;
+  }
+  __syncthreads();
+  return running;
+}
+
+
 
 // Adds a workgroup's LDS histogram `hist` (NBINS counters, complete when called) into
 // the row's device histogram `gh`.  The last of the row's `n_parts` workgroups to

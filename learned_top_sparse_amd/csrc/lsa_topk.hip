@@ -29,55 +29,8 @@ namespace lsa {
 
 namespace {
 
-constexpr int SEG = 8192;       // slots per workgroup in the several-workgroups-per-row path
 
 __device__ __forceinline__ unsigned okey(int s) { return (unsigned)s ^ 0x80000000u; }
-
-// Ordered compaction over positions [0, n): pred(pos, payload&) selects; emit(rank,
-// pos, payload) is called for selected positions with their rank in position order.
-// wcnt: LDS int[2 * V * NT/64].  All threads must call; returns the count.
-template <int NT, int V, typename Pred, typename Emit>
-__device__ __forceinline__ int ordered_compact(int n, int* wcnt, Pred pred, Emit emit) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int running = 0, parity = 0;
-  for (int base = 0; base < n; base += V * NT) {
-    bool f[V];
-    int pl[V];
-    unsigned long long bal[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const int pos = base + v * NT + (int)threadIdx.x;
-      pl[v] = 0;
-      f[v] = (pos < n) && pred(pos, pl[v]);
-    }
-#pragma unroll
-    for (int v = 0; v < V; ++v) bal[v] = __ballot(f[v]);
-    int* wc = wcnt + parity * V * NW;
-    if (lane == 0) {
-#pragma unroll
-      for (int v = 0; v < V; ++v) wc[v * NW + wave] = __popcll(bal[v]);
-    }
-    __syncthreads();
-    int off = running;
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      int pre = 0, tot = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const int c = wc[v * NW + w];
-        pre += (w < wave) ? c : 0;
-        tot += c;
-      }
-      if (f[v]) emit(off + pre + lanes_below(bal[v]), base + v * NT + (int)threadIdx.x, pl[v]);
-      off += tot;
-    }
-    running = off;
-    parity ^= 1;
-  }
-  __syncthreads();
-  return running;
-}
 
 // Among positions [0, n) accepted by pred (payload = score), find the need-th best
 // score by 8-bit radix passes on the order-preserving key.  Returns T (as key) and
@@ -166,8 +119,8 @@ struct RowView {
 // payloads pl[v][c]; emit(rank, pos, payload) gets every selected position with its
 // rank in position order, starting at `running`.  wcnt: LDS int[V * NT/64].  One
 // barrier; all threads call; returns running + count.
-template <int NT, int V, typename Emit>
-__device__ __forceinline__ int ordered_emit4(int base, const unsigned (&m)[V], const int (&pl)[V][4], int* wc,
+template <int NT, int V, typename P, typename Emit>
+__device__ __forceinline__ int ordered_emit4(int base, const unsigned (&m)[V], const P (&pl)[V][4], int* wc,
                                              int running, Emit emit) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -505,23 +458,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const int32_t* __restrict__ sc
 }
 
 // ---------------------------------------------------------------------------------
-// Several workgroups per row (few long rows: decode).  Workspace per row:
-//   hist[NBINS] | info[8] = {b*, above, cnt*, overflow, arrivals, -, -, -} | cnt[n_seg] |
-//   cand[n_seg][CAP] (slot, score)
-// ints per row of the workspace, a multiple of 4 so every row's histogram is 16-byte aligned
-__host__ __device__ constexpr long long seg_row_ints(long long n_seg) {
-  return (NBINS + INFO + NGRP + n_seg + 2 * n_seg * CAP + 3) / 4 * 4;
-}
-struct SegWs {
-  int* base;
-  int n_seg;
-  __device__ __forceinline__ long long row_ints() const { return seg_row_ints(n_seg); }
-  __device__ __forceinline__ int* hist(long long r) const { return base + r * row_ints(); }
-  __device__ __forceinline__ int* info(long long r) const { return hist(r) + NBINS; }
-  __device__ __forceinline__ int* gsum(long long r) const { return info(r) + INFO; }
-  __device__ __forceinline__ int* cnt(long long r) const { return gsum(r) + NGRP; }
-  __device__ __forceinline__ int* cand(long long r, int seg) const { return cnt(r) + n_seg + 2ll * seg * CAP; }
-};
+// Several workgroups per row (few long rows: decode); workspace layout: SegWs.
 
 // clears the histogram, the group sums and the arrival counter of every row
 __global__ void topk_seg_zero_kernel(int* ws, long long row_ints, long long rows) {
@@ -559,37 +496,24 @@ __global__ __launch_bounds__(NT) void topk_seg_hist_kernel(const int32_t* __rest
 
 // One segment of a flat row: the entries of bins >= b* go, in slot order, to the
 // segment's candidate list in the workspace.  Every load the workgroup needs is
-// issued before any of them is used -- the row's position, its histogram (CUT) and
-// the segment's scores (read up to L_max and masked by the position afterwards) --
-// so the kernel waits out one memory latency instead of three.
-// CUT: the row's histogram is complete but its cut is not known yet (the indexer
-// built the histogram); every segment finds the cut itself and segment 0 records
-// it for the finish kernel.
-template <int NT, bool CUT>
+// issued before any of them is used -- the row's position, its cut and the
+// segment's scores (read up to L_max and masked by the position afterwards).
+template <int NT>
 __global__ __launch_bounds__(NT) void topk_seg_select_kernel(const int32_t* __restrict__ scores, long long ld,
                                                              const int32_t* __restrict__ q_pos, int L_max, int k,
                                                              SegWs ws) {
   constexpr int NW = NT / 64;
   constexpr int V = SEG / (4 * NT);  // one pass covers the segment
   static_assert(4 * V * NT == SEG, "segment = one compaction pass");
-  static_assert(!CUT || NT == NGRP, "one group sum per thread");
   __shared__ int wcnt[V * NW];
-  __shared__ int scan_tmp[NW + 1];
-  __shared__ int sh[8];
   const long long row = blockIdx.y;
   const int seg = blockIdx.x;
   const int lo = seg * SEG, hi_max = min(lo + SEG, L_max);
   const int32_t* srow = scores + row * ld;
-  int* info = ws.info(row);
+  const int* info = ws.info(row);
 
   const int p_raw = q_pos[row];
-  int gs = 0, info0 = 0, info3 = 0;
-  if constexpr (CUT) {
-    gs = ws.gsum(row)[NGRP - 1 - (int)threadIdx.x];  // highest group first
-  } else {
-    info0 = info[0];
-    info3 = info[3];
-  }
+  const int bstar = info[0], overflow = info[3];
   const bool vec = (((uintptr_t)srow) & 15u) == 0;
   int sc[V][4];
 #pragma unroll
@@ -608,46 +532,6 @@ __global__ __launch_bounds__(NT) void topk_seg_select_kernel(const int32_t* __re
   if (n_slots <= k) return;  // every candidate is taken: the finish kernel lists them
   const int hi = min(hi_max, n_slots);
   if (lo >= hi) return;
-  int bstar, overflow;
-  if constexpr (CUT) {
-    // group holding the k-th best entry, then the bin inside it (one wave)
-    int tot;
-    const int excl = block_exclusive_scan<NT>(gs, scan_tmp, &tot);
-    if (excl < k && excl + gs >= k) {
-      sh[0] = NGRP - 1 - (int)threadIdx.x;
-      sh[1] = excl;
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      const int g = sh[0], lane = (int)threadIdx.x;
-      const int hb = lane < GRP ? ws.hist(row)[g * GRP + GRP - 1 - lane] : 0;  // highest bin first
-      int incl = hb;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-      }
-      const unsigned long long hit = __ballot(sh[1] + incl >= k);
-      const int first = (int)__ffsll((long long)hit) - 1;
-      if (lane == first) {
-        sh[4] = g * GRP + GRP - 1 - lane;
-        sh[5] = sh[1] + incl - hb;
-        sh[6] = hb;
-      }
-    }
-    __syncthreads();
-    bstar = sh[4];
-    overflow = (sh[5] + sh[6] > CAP) ? 1 : 0;
-    if (seg == 0 && threadIdx.x == 0) {
-      info[0] = sh[4];
-      info[1] = sh[5];
-      info[2] = sh[6];
-      info[3] = overflow;
-    }
-  } else {
-    bstar = info0;
-    overflow = info3;
-  }
   if (overflow) return;  // the finish kernel selects from global memory
   unsigned m[V];
 #pragma unroll
@@ -748,6 +632,151 @@ __global__ __launch_bounds__(NT) void topk_seg_finish_kernel(const int32_t* __re
   }
   __syncthreads();
   finish_from_list<NT, KEPT>(rv, Lc, lslot, lval, bstar, above, k, wcnt, h256, scan_tmp, sh, out);
+}
+
+// Flat rows whose histogram and span candidate lists the indexer built: one
+// workgroup per row, no pass over the score table in the usual case.  The cut b*
+// comes from the row's group sums and the bins of the cut group.  If every span's
+// list reaches down to b* (lbw <= b*), each entry in bins >= b* sits in its span's
+// list, so they are gathered in slot order straight from the lists; otherwise (a
+// span holds more of the top than its list kept, or the entries of bins >= b* do
+// not fit the LDS list) the row is selected from its score table.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_list_finish_kernel(const int32_t* __restrict__ scores, long long ld,
+                                                              const int32_t* __restrict__ q_pos, int L_max, int k,
+                                                              SegWs ws, int32_t* __restrict__ idx,
+                                                              int32_t* __restrict__ count) {
+  constexpr int NW = NT / 64;
+  constexpr int V = 2;
+  static_assert(NT >= NGRP, "one group sum per thread");
+  __shared__ int lds_big[NBINS];
+  __shared__ int wcnt[2 * 4 * NW];
+  __shared__ int scan_tmp[NW + 1];
+  __shared__ int h256[256];
+  __shared__ int sh[8];
+  __shared__ int loff[NT + 1];
+  const long long row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  int32_t* out = idx + row * (long long)k;
+
+  // independent loads together: position, group sums, the span lists' counts and lower bins
+  const int p_raw = q_pos[row];
+  const int gs = tid < NGRP ? ws.gsum(row)[NGRP - 1 - tid] : 0;  // highest group first
+  const int lc = tid < ws.n_lst ? ws.lcnt(row)[tid] : 0;
+  const int lb = tid < ws.n_lst ? ws.lbw(row)[tid] : 0;
+
+  RowView<false> rv;
+  rv.p = min(p_raw, L_max - 1);
+  rv.srow = scores + row * ld;
+  rv.vec = (((uintptr_t)rv.srow) & 15u) == 0;
+  rv.bs = 0;
+  rv.kept_s = nullptr;
+  rv.n_slots = max(rv.p + 1, 0);
+  const int n_valid = rv.n_slots;
+  if (count != nullptr && tid == 0) count[row] = min(k, n_valid);
+  if (n_valid <= k) {
+    select_all<NT, false>(rv, n_valid, k, wcnt, out);
+    return;
+  }
+
+  // cut: group holding the k-th best entry, then the bin inside it (one wave)
+  {
+    int tot;
+    const int excl = block_exclusive_scan<NT>(gs, scan_tmp, &tot);
+    if (excl < k && excl + gs >= k) {
+      sh[0] = NGRP - 1 - tid;
+      sh[1] = excl;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const int g = sh[0];
+      const int hb = lane < GRP ? ws.hist(row)[g * GRP + GRP - 1 - lane] : 0;  // highest bin first
+      int incl = hb;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      const unsigned long long hit = __ballot(sh[1] + incl >= k);
+      const int first = (int)__ffsll((long long)hit) - 1;
+      if (lane == first) {
+        sh[4] = g * GRP + GRP - 1 - lane;
+        sh[5] = sh[1] + incl - hb;
+        sh[6] = hb;
+      }
+    }
+    __syncthreads();
+  }
+  const int bstar = sh[4], above = sh[5], cnt_star = sh[6];
+  const int n_sp = (n_valid + DIRECT_SPAN - 1) / DIRECT_SPAN;  // spans of this row (each wrote a list)
+  const bool short_list = tid < n_sp && lb > bstar;
+  const bool from_table = __syncthreads_or(short_list) != 0;
+  int* lslot = lds_big;
+  int* lval = lds_big + CAP;
+  if (above + cnt_star > CAP) {
+    fallback_select<NT, false>(rv, k, lds_big, wcnt, h256, scan_tmp, sh, out);
+    return;
+  }
+  int Lc;
+  if (from_table) {
+    Lc = ordered_compact4<NT, 4>(
+        0, rv.n_slots, wcnt, 0,
+        [&](int s0, int (&pl)[4]) {
+          unsigned m = rv.load4(s0, pl), r = 0;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) r |= (((m >> c) & 1u) && coarse_bin(pl[c]) >= bstar ? 1u : 0u) << c;
+          return r;
+        },
+        [&](int r, int s, int sc) {
+          if (r < CAP) {
+            lslot[r] = s;
+            lval[r] = sc;
+          }
+        });
+  } else {
+    // offsets of the lists, then an ordered compaction over their concatenation
+    int n_all;
+    const int ex = block_exclusive_scan<NT>(tid < n_sp ? lc : 0, scan_tmp, &n_all);
+    if (tid < n_sp) loff[tid] = ex;
+    __syncthreads();
+    struct SP {
+      int slot, score;
+    };
+    int running = 0, parity = 0;
+    for (int base = 0; base < n_all; base += 4 * V * NT) {
+      unsigned m[V];
+      SP pl[V][4];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        m[v] = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int e = base + 4 * (v * NT + tid) + c;
+          const int ec = min(e, n_all - 1);  // clamped: the loads stay unconditional
+          int lo = 0, hi = n_sp;             // loff[lo] <= ec < loff[hi] (loff[n_sp] = n_all)
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (loff[mid] <= ec) lo = mid;
+            else hi = mid;
+          }
+          const int* L = ws.lcand(row, lo) + 2 * (ec - loff[lo]);
+          pl[v][c].slot = L[0];
+          pl[v][c].score = L[1];
+          m[v] |= (e < n_all && coarse_bin(pl[v][c].score) >= bstar ? 1u : 0u) << c;
+        }
+      }
+      running = ordered_emit4<NT, V>(base, m, pl, wcnt + parity * V * NW, running, [&](int r, int, SP x) {
+        if (r < CAP) {
+          lslot[r] = x.slot;
+          lval[r] = x.score;
+        }
+      });
+      parity ^= 1;
+    }
+    __syncthreads();
+    Lc = running;
+  }
+  finish_from_list<NT, false>(rv, min(Lc, CAP), lslot, lval, bstar, above, k, wcnt, h256, scan_tmp, sh, out);
 }
 
 // Block keep of the two-stage indexer: own block + the best n_keep-1 earlier blocks
@@ -872,37 +901,38 @@ __global__ __launch_bounds__(NT) void blk_select_kernel(const long long* __restr
 size_t topk_ws_bytes(long long rows, int L_max) {
   if (rows == 0 || rows > 512 || L_max < 4 * SEG) return 0;
   const long long n_seg = (L_max + SEG - 1) / SEG;
+  const long long n_lst = (L_max + DIRECT_SPAN - 1) / DIRECT_SPAN;
   if (n_seg > 1024) return 0;
-  return (size_t)rows * (size_t)seg_row_ints(n_seg) * sizeof(int);
+  return (size_t)rows * (size_t)SegWs::row_ints_for(n_seg, n_lst) * sizeof(int);
 }
 
-static bool split_rows(const TopkArgs& a, SegWs* w, long long* row_ints) {
+static bool split_rows(const TopkArgs& a, SegWs* w) {
   const long long rows = (long long)a.B * a.n_q;
   const size_t need = topk_ws_bytes(rows, a.L_max);
   if (a.kept != nullptr || need == 0 || a.ws == nullptr || a.ws_bytes < need) return false;
   w->base = static_cast<int*>(a.ws);
   w->n_seg = (a.L_max + SEG - 1) / SEG;
-  *row_ints = seg_row_ints(w->n_seg);
+  w->n_lst = (a.L_max + DIRECT_SPAN - 1) / DIRECT_SPAN;
   return true;
 }
 
 template <bool KEPT>
 static void launch_topk_t(const TopkArgs& a, hipStream_t st, long long rows) {
   SegWs w;
-  long long row_ints;
-  if (!KEPT && split_rows(a, &w, &row_ints)) {
+  if (!KEPT && split_rows(a, &w)) {
+    if (a.hist_ready) {
+      // the indexer built the histograms and the span lists: one kernel
+      hipLaunchKernelGGL((topk_list_finish_kernel<1024>), dim3((unsigned)rows), dim3(1024), 0, st, a.scores, a.ld,
+                         a.q_pos, a.L_max, a.k, w, a.idx, a.count);
+      return;
+    }
     // several workgroups per row: histogram and candidate compaction split over segments
     const dim3 grid((unsigned)w.n_seg, (unsigned)rows);
-    if (a.hist_ready) {
-      hipLaunchKernelGGL((topk_seg_select_kernel<256, true>), grid, dim3(256), 0, st, a.scores, a.ld, a.q_pos,
-                         a.L_max, a.k, w);
-    } else {
-      hipLaunchKernelGGL(topk_seg_zero_kernel, dim3(8, (unsigned)rows), dim3(256), 0, st, w.base, row_ints, rows);
-      hipLaunchKernelGGL((topk_seg_hist_kernel<256, KEPT>), grid, dim3(256), 0, st, a.scores, a.ld, a.q_pos,
-                         a.kept, a.block_size, a.n_keep, a.L_max, a.k, w);
-      hipLaunchKernelGGL((topk_seg_select_kernel<256, false>), grid, dim3(256), 0, st, a.scores, a.ld, a.q_pos,
-                         a.L_max, a.k, w);
-    }
+    hipLaunchKernelGGL(topk_seg_zero_kernel, dim3(8, (unsigned)rows), dim3(256), 0, st, w.base, w.row_ints(), rows);
+    hipLaunchKernelGGL((topk_seg_hist_kernel<256, KEPT>), grid, dim3(256), 0, st, a.scores, a.ld, a.q_pos, a.kept,
+                       a.block_size, a.n_keep, a.L_max, a.k, w);
+    hipLaunchKernelGGL((topk_seg_select_kernel<256>), grid, dim3(256), 0, st, a.scores, a.ld, a.q_pos, a.L_max,
+                       a.k, w);
     hipLaunchKernelGGL((topk_seg_finish_kernel<256, KEPT>), dim3((unsigned)rows), dim3(256), 0, st, a.scores,
                        a.ld, a.q_pos, a.kept, a.block_size, a.n_keep, a.L_max, a.k, w, a.idx, a.count);
     return;
@@ -916,19 +946,20 @@ static void launch_topk_t(const TopkArgs& a, hipStream_t st, long long rows) {
   }
 }
 
-bool topk_split_rows(const TopkArgs& a, int** hist, long long* row_ints) {
+bool topk_split_rows(const TopkArgs& a, int** base, int* n_seg, int* n_lst) {
   SegWs w;
-  if (!split_rows(a, &w, row_ints)) return false;
-  *hist = w.base;
+  if (!split_rows(a, &w)) return false;
+  *base = w.base;
+  *n_seg = w.n_seg;
+  *n_lst = w.n_lst;
   return true;
 }
 
 hipError_t launch_topk_reset(const TopkArgs& a, hipStream_t st) {
   SegWs w;
-  long long row_ints;
   const long long rows = (long long)a.B * a.n_q;
-  if (rows == 0 || !split_rows(a, &w, &row_ints)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(topk_seg_zero_kernel, dim3(8, (unsigned)rows), dim3(256), 0, st, w.base, row_ints, rows);
+  if (rows == 0 || !split_rows(a, &w)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_seg_zero_kernel, dim3(8, (unsigned)rows), dim3(256), 0, st, w.base, w.row_ints(), rows);
   return hipGetLastError();
 }
 

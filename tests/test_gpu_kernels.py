@@ -422,6 +422,44 @@ def test_forward_decode_fused_selection(lsa, H_I):
     err.check()
 
 
+@pytest.mark.parametrize("kind", ["one_span_distinct", "one_span_equal", "two_spans_ties"])
+def test_forward_decode_fused_selection_concentrated(lsa, kind):
+    """Decode rows whose top-k sits in one or two 2048-key spans: the indexer's span
+    lists cannot hold it (the list keeps ~128 entries of a span), so the top-k must
+    notice (list bin above the cut) and select from the score table -- still bit for
+    bit the separate calls' lists and the oracle's."""
+    L, k = 40000, 1024
+    pos = [39999, 39000, 35000, 20000]
+    wl = synthetic.Workload("deccon", B=len(pos), n_q=1, L=L, q_pos0=0, H_I=64, d_I=128, k=k, H_q=16)
+    inp, _ = _inputs(wl, seed=12, pos=pos)
+    q0 = inp["q_idx"][:, 0, 0, :].clone()           # head 0 of each query: keys aligned with it score high
+    gen = torch.Generator().manual_seed(3)
+    for b in range(wl.B):
+        if kind == "one_span_distinct":
+            lo, hi = 16384, 18432                     # exactly span 8
+            noise = torch.randint(-3, 4, (hi - lo, 128), generator=gen, dtype=torch.int64)
+            inp["k_idx"][b, lo:hi] = (q0[b].to(torch.int64) + noise).clamp(-128, 127).to(torch.int8)
+        elif kind == "one_span_equal":
+            lo, hi = 18432, 20000                     # part of span 9: 1568 identical keys (ties)
+            inp["k_idx"][b, lo:hi] = q0[b]
+        else:
+            for lo, hi in ((2048, 2600), (10240, 10900)):   # two spans, ties inside each
+                inp["k_idx"][b, lo:hi] = q0[b]
+    g = {kk: v.to(dev()) for kk, v in inp.items()}
+    assert lsa.lsa_forward_stages(g, k, lsa.lsa_forward_workspace_size(g, k))[0] == "topk_reset"
+    res = lsa.lsa_forward(g, k_top=k)
+    ld = ((L + 63) // 64) * 64
+    sc = lsa.lsa_index_scores(g["q_idx"], g["k_idx"], g["w"], g["q_pos"], ld=ld)
+    for use_ws in (True, False):
+        idx, cnt = lsa.lsa_topk(sc, g["q_pos"], k, L, use_ws=use_ws)
+        assert torch.equal(idx, res["idx"]), f"{kind} use_ws={use_ws}"
+        assert torch.equal(cnt, res["count"])
+    want = _flat_oracle_rows(inp, k, with_attn=False, rows=[(0, 0), (3, 0)])
+    J = res["idx"].cpu().numpy()
+    for (b, i), r in want.items():
+        assert np.array_equal(J[b, i], r["J"]), f"{kind} seq {b}"
+
+
 @pytest.mark.parametrize("T,bs,n_keep,k", [(4096, 128, 8, 256), (2048, 16, 6, 40)])
 def test_forward_two_stage_small(lsa, T, bs, n_keep, k):
     n_q = 64
