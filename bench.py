@@ -8,9 +8,10 @@ line also carries the 128K prefill figure (the final 8192-query chunk of a
 131072-token context through the two-stage path: block reps -> block
 prefilter -> token scores in kept blocks -> top-k -> sparse attention).
 
-Each step is one lsa_forward call; it records a HIP event on its launch stream
-after every stage (lsa_forward_stages lists them), so every stage's kernels are
-timed live inside the timed region.
+Each step is one lsa_forward call; every tenth timed step also records a HIP event
+on its launch stream after every stage (lsa_forward_stages lists them), so every
+stage's kernels are timed live inside the timed region without an event gap in
+every step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--no-cpu-baseline] [--copy-calibration]
@@ -42,10 +43,16 @@ def _describe(wl):
     return s
 
 
+# Stage events are recorded on every EVENTS_EVERY-th timed step only: an event recorded
+# between two kernels holds the next launch back by ~5-6 us on this GPU (measured in a
+# kernel trace), which would otherwise inflate every step by about one such gap per stage.
+EVENTS_EVERY = 10
+
+
 class Step:
-    """One pass of the path: one lsa_forward call, which records a HIP event on its
-    launch stream after every stage (lsa_forward_stages names them), so every
-    stage's kernels are timed live."""
+    """One pass of the path: one lsa_forward call; with record=True it also records a
+    HIP event on its launch stream after every stage (lsa_forward_stages names them),
+    so every stage's kernels are timed live."""
 
     def __init__(self, lsa, torch, wl, inp):
         self.lsa, self.torch, self.wl, self.inp = lsa, torch, wl, inp
@@ -82,6 +89,7 @@ class Step:
         self.lsa.lsa_forward(self.inp, k_top=self.wl.k, out=self.out, ws=self.ws, stage_events=evs, **self.kw)
         if record:
             self.steps.append([(name, evs[i], evs[i + 1]) for i, name in enumerate(self.stages)])
+
 
     def kernel_ms(self):
         """Per stage: mean total ms per step, launches per step, mean ms per launch."""
@@ -217,13 +225,13 @@ def measure(lsa, torch, wl, steps, warmup):
     inp = synthetic.make_inputs(wl, torch.device("cuda:0"))
     torch.cuda.synchronize()
     step = Step(lsa, torch, wl, inp)
-    step.make_events(steps)
+    step.make_events((steps + EVENTS_EVERY - 1) // EVENTS_EVERY)
     for _ in range(warmup):
         step.run(record=False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        step.run(record=True)
+    for i in range(steps):
+        step.run(record=(i % EVENTS_EVERY == 0))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / steps
@@ -257,7 +265,8 @@ def main():
         for name in names:
             wl = synthetic.WORKLOADS[name]
             inp, step, ms = measure(lsa, torch, wl, args.steps, args.warmup)
-            print(json.dumps({"workload": wl.name, "ms_per_step": ms, "kernel_ms": step.kernel_ms(),
+            print(json.dumps({"workload": wl.name, "ms_per_step": ms, "stage_events_every": EVENTS_EVERY,
+                              "kernel_ms": step.kernel_ms(),
                               "algorithmic": algorithmic(wl)}), flush=True)
             del inp, step
             torch.cuda.empty_cache()
@@ -281,6 +290,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "stage_events_every": EVENTS_EVERY,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

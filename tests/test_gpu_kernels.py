@@ -422,7 +422,7 @@ def test_forward_decode_fused_selection(lsa, H_I):
     err.check()
 
 
-@pytest.mark.parametrize("kind", ["one_span_distinct", "one_span_equal", "two_spans_ties"])
+@pytest.mark.parametrize("kind", ["one_span_distinct", "one_span_equal", "two_spans_ties", "all_equal"])
 def test_forward_decode_fused_selection_concentrated(lsa, kind):
     """Decode rows whose top-k sits in one or two 2048-key spans: the indexer's span
     lists cannot hold it (the list keeps ~128 entries of a span), so the top-k must
@@ -442,9 +442,11 @@ def test_forward_decode_fused_selection_concentrated(lsa, kind):
         elif kind == "one_span_equal":
             lo, hi = 18432, 20000                     # part of span 9: 1568 identical keys (ties)
             inp["k_idx"][b, lo:hi] = q0[b]
-        else:
+        elif kind == "two_spans_ties":
             for lo, hi in ((2048, 2600), (10240, 10900)):   # two spans, ties inside each
                 inp["k_idx"][b, lo:hi] = q0[b]
+        else:
+            inp["q_idx"][b] = 0                       # every score 0: the cut bin holds the whole row
     g = {kk: v.to(dev()) for kk, v in inp.items()}
     assert lsa.lsa_forward_stages(g, k, lsa.lsa_forward_workspace_size(g, k))[0] == "topk_reset"
     res = lsa.lsa_forward(g, k_top=k)
