@@ -555,6 +555,12 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
       if (!lsa::topk_split_rows(ta, &ia.sel_base, &ia.sel_n_seg, &ia.sel_n_lst)) return LSA_ERR_INTERNAL;
       ia.k_top = kt;
       ta.hist_ready = true;
+      ta.q_idx = qi;
+      ta.k_idx = ki;
+      ta.w = wq;
+      ta.w_per_query = a->w_per_query ? 1 : 0;
+      ta.H_I = H_I;
+      ta.d_I = d_I;
     }
     if (lsa::launch_index_scores(ia, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
     if (lsa::launch_topk(ta, s) != hipSuccess || !mark()) return LSA_ERR_HIP;

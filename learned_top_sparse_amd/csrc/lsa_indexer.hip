@@ -230,12 +230,13 @@ __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
 // (KEPT: slot s is key kept[s / bs] * bs + s % bs; one workgroup covers all slots).
 // The scan is bound by HBM, so each wave keeps a ring of RING groups of fragments:
 // RING-1 groups of loads are in flight while one group is multiplied (2 waves/SIMD).
-// HIST (flat only): the workgroup also builds its share of the row's selection
-// state in the split top-k's workspace (SegWs, cleared beforehand): it counts its
-// scores into an LDS histogram of the selection's coarse bins, adds the bins it
-// touched to the row's histogram (device-scope atomics), and writes its span's
-// candidate list -- the entries of its highest bins, in slot order -- so the exact
-// top-k that follows reads neither the score table nor a histogram pass.
+// HIST (flat only): instead of writing the score table, the workgroup builds its
+// share of the row's selection state in the split top-k's workspace (SegWs, cleared
+// beforehand): it counts its scores into an LDS histogram of the selection's coarse
+// bins, adds the bins it touched to the row's histogram (device-scope atomics), and
+// writes its span's candidate list -- the entries of its highest bins, in slot order.
+// Only a span whose list its own top bins cut short (heavy ties) writes its table
+// slice as well (marked lbw = -1).  The exact top-k that follows reads the lists.
 // Grid: x = n_spans (1 for KEPT), y = B * n_q.
 template <int D, int MT, bool KEPT, bool HIST>
 __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
@@ -329,7 +330,23 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
     for (int r = 0; r < RING - 1; ++r) load_group(c0, c1, r, ring[r]);
   };
   int wt[MT][4];
-  // the ring loop and score flush of one chunk whose prologue has been issued
+  // the chunk's scores (in sbuf) to the score table
+  auto store_chunk = [&](int c0, int c1) {
+    if (!KEPT && (reinterpret_cast<uintptr_t>(scores + srow + c0) & 15) == 0) {
+      // flat rows: the whole chunk in 16-byte non-temporal stores (scores of keys past
+      // the query's position may be written: they are unspecified), which disturb the
+      // key stream less than dword stores
+      const int n4 = (c1 - c0) / 4;
+      for (int t = tid; t < n4; t += 256)
+        __builtin_nontemporal_store(*(const v4i*)&sbuf[4 * t], (v4i*)(scores + srow + c0 + 4 * t));
+      for (int t = 4 * n4 + tid; t < c1 - c0; t += 256) scores[srow + c0 + t] = sbuf[t];
+    } else {
+      for (int t = tid; t < c1 - c0; t += 256)
+        if (is_cand(c0 + t)) scores[srow + c0 + t] = sbuf[t];
+    }
+  };
+  // the ring loop (and, unless the span's selection state is built, the score flush) of
+  // one chunk whose prologue has been issued
   auto run_chunk = [&](int c0, int c1) {
     const int n_groups = (c1 - c0 + 63) / 64;
     const int n_iter = ((n_groups + 3) / 4 + RING - 1) / RING * RING;  // groups per wave, padded
@@ -373,18 +390,7 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
       }
     }
     __syncthreads();
-    if (!KEPT && (reinterpret_cast<uintptr_t>(scores + srow + c0) & 15) == 0) {
-      // flat rows: the whole chunk in 16-byte non-temporal stores (scores of keys past
-      // the query's position may be written: they are unspecified), which disturb the
-      // key stream less than dword stores
-      const int n4 = (c1 - c0) / 4;
-      for (int t = tid; t < n4; t += 256)
-        __builtin_nontemporal_store(*(const v4i*)&sbuf[4 * t], (v4i*)(scores + srow + c0 + 4 * t));
-      for (int t = 4 * n4 + tid; t < c1 - c0; t += 256) scores[srow + c0 + t] = sbuf[t];
-    } else {
-      for (int t = tid; t < c1 - c0; t += 256)
-        if (is_cand(c0 + t)) scores[srow + c0 + t] = sbuf[t];
-    }
+    if (!hist) store_chunk(c0, c1);
     __syncthreads();
   };
 
@@ -449,6 +455,7 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
           const int h = b >= lo ? lhist[b] : 0;
           if (acc + h >= need) {
             lsh[0] = acc + h <= LIST_CAP ? b : b + 1;
+            lsh[1] = acc + h > LIST_CAP;
             break;
           }
           acc += h;
@@ -456,6 +463,10 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
       }
       __syncthreads();
       const int bw = lsh[0];
+      // A list cut short by its own top bins (more than LIST_CAP entries tie there)
+      // would leave the top-k to re-score the span: such a span writes its table slice
+      // instead and is marked lbw = -1.
+      const bool tied = lsh[1] != 0;
       int* lc = sel.lcand(row, blockIdx.x);
       const int n_list = ordered_compact<256, 4>(
           n_ent, wcnt_l,
@@ -469,9 +480,10 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
               lc[2 * r + 1] = v;
             }
           });
+      if (tied) store_chunk(s_begin, s_lim);
       if (tid == 0) {
         sel.lcnt(row)[blockIdx.x] = min(n_list, LIST_CAP);
-        sel.lbw(row)[blockIdx.x] = bw;
+        sel.lbw(row)[blockIdx.x] = tied ? -1 : bw;
       }
     }
 

@@ -50,7 +50,12 @@ struct TopkArgs {
   int32_t* count;
   void* ws;          // optional: enables the several-workgroups-per-row path
   size_t ws_bytes;
-  bool hist_ready;   // the indexer already built the rows' histograms in ws
+  bool hist_ready;   // the indexer built the rows' selection state in ws (no score table)
+  // with hist_ready: the indexer's inputs, to re-score spans whose list is too short
+  const int8_t* q_idx;
+  const int8_t* k_idx;
+  const int32_t* w;
+  int w_per_query, H_I, d_I;
 };
 
 struct BlkSelArgs {

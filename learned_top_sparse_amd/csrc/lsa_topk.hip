@@ -634,27 +634,64 @@ __global__ __launch_bounds__(NT) void topk_seg_finish_kernel(const int32_t* __re
   finish_from_list<NT, KEPT>(rv, Lc, lslot, lval, bstar, above, k, wcnt, h256, scan_tmp, sh, out);
 }
 
-// Flat rows whose histogram and span candidate lists the indexer built: one
-// workgroup per row, no pass over the score table in the usual case.  The cut b*
-// comes from the row's group sums and the bins of the cut group.  If every span's
-// list reaches down to b* (lbw <= b*), each entry in bins >= b* sits in its span's
-// list, so they are gathered in slot order straight from the lists; otherwise (a
-// span holds more of the top than its list kept, or the entries of bins >= b* do
-// not fit the LDS list) the row is selected from its score table.
+// Re-scores keys [j0, j1) of one flat row into its score-table slice: the indexer's
+// integer sum sum_h w_h * max(0, q_h . k_j), here with v_dot4_i32_i8 (4 int8 products
+// per op) instead of the MFMA -- identical integers, so identical selections.  The
+// rare path of the list-based selection; all NT threads call (two barriers).
+template <int NT, int DI>
+__device__ __forceinline__ void rescore_keys(const int8_t* __restrict__ q_row, const int32_t* __restrict__ w_row,
+                                             const int8_t* __restrict__ kb, int H_I, int j0, int j1,
+                                             int32_t* __restrict__ srow, int* q_lds, int* w_lds) {
+  constexpr int C = DI / 4;  // 4-byte words per index vector
+  for (int t = threadIdx.x; t < H_I * C; t += NT) q_lds[t] = reinterpret_cast<const int*>(q_row)[t];
+  for (int t = threadIdx.x; t < H_I; t += NT) w_lds[t] = w_row[t];
+  __syncthreads();
+  for (int j = j0 + (int)threadIdx.x; j < j1; j += NT) {
+    int kv[C];
+    const int* kr = reinterpret_cast<const int*>(kb + (long long)j * DI);
+#pragma unroll
+    for (int c = 0; c < C; ++c) kv[c] = kr[c];
+    int s = 0;
+    for (int h = 0; h < H_I; ++h) {
+      int dot = 0;
+#pragma unroll
+      for (int c = 0; c < C; ++c) dot = __builtin_amdgcn_sdot4(q_lds[h * C + c], kv[c], dot, false);
+      s += w_lds[h] * max(dot, 0);  // modulo 2^32, like the indexer's 24-bit multiply-adds
+    }
+    srow[j] = s;
+  }
+  __syncthreads();
+}
+
+// Flat rows whose selection state the indexer built (histogram, one candidate list
+// per 2048-key span, no score table): one workgroup per row.  The cut b* comes from
+// the row's group sums and the bins of the cut group.  A span is then
+//   L: its list reaches down to b* (lbw <= b*): all its entries of bins >= b* are in
+//      the list;
+//   T: it wrote its table slice (lbw = -1: its own top bins overflowed a list);
+//   S: its list stops above b* (the top is concentrated there): it is re-scored into
+//      its table slice here and then read like T.
+// The entries of bins >= b* are gathered in slot order from the lists and slices.
+// If they overflow the LDS list (heavy ties at b*), every span that is not T is
+// re-scored and the row goes through the exact radix fallback over its table.
 template <int NT>
-__global__ __launch_bounds__(NT) void topk_list_finish_kernel(const int32_t* __restrict__ scores, long long ld,
-                                                              const int32_t* __restrict__ q_pos, int L_max, int k,
-                                                              SegWs ws, int32_t* __restrict__ idx,
-                                                              int32_t* __restrict__ count) {
+__global__ __launch_bounds__(NT) void topk_list_finish_kernel(
+    int32_t* __restrict__ scores, long long ld, const int32_t* __restrict__ q_pos, int L_max, int k, SegWs ws,
+    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
+    int w_per_query, int n_q, int H_I, int d_I, int32_t* __restrict__ idx, int32_t* __restrict__ count) {
   constexpr int NW = NT / 64;
   constexpr int V = 2;
   static_assert(NT >= NGRP, "one group sum per thread");
+  enum { KIND_L = 0, KIND_T = 1, KIND_S = 2 };
   __shared__ int lds_big[NBINS];
   __shared__ int wcnt[2 * 4 * NW];
   __shared__ int scan_tmp[NW + 1];
   __shared__ int h256[256];
   __shared__ int sh[8];
   __shared__ int loff[NT + 1];
+  __shared__ int skind[NT], slen[NT];  // per span: kind and entries to gather
+  __shared__ int q_lds[64 * 128 / 4];
+  __shared__ int w_lds[64];
   const long long row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   int32_t* out = idx + row * (long long)k;
@@ -709,74 +746,81 @@ __global__ __launch_bounds__(NT) void topk_list_finish_kernel(const int32_t* __r
   }
   const int bstar = sh[4], above = sh[5], cnt_star = sh[6];
   const int n_sp = (n_valid + DIRECT_SPAN - 1) / DIRECT_SPAN;  // spans of this row (each wrote a list)
-  const bool short_list = tid < n_sp && lb > bstar;
-  const bool from_table = __syncthreads_or(short_list) != 0;
-  int* lslot = lds_big;
-  int* lval = lds_big + CAP;
-  if (above + cnt_star > CAP) {
+  const bool overflow = above + cnt_star > CAP;
+  // span kinds (with overflow every span that is not T is re-scored)
+  const bool resc = tid < n_sp && lb >= 0 && (overflow || lb > bstar);
+  if (tid < n_sp) {
+    const int len = min(n_valid, (tid + 1) * DIRECT_SPAN) - tid * DIRECT_SPAN;
+    skind[tid] = lb < 0 ? KIND_T : (resc ? KIND_S : KIND_L);
+    slen[tid] = (lb < 0 || resc) ? len : lc;
+  }
+  if (__syncthreads_count(resc) > 0) {
+    const int8_t* q_row = q_idx + row * (long long)H_I * d_I;
+    const int32_t* w_row = w + (w_per_query ? row * H_I : 0);
+    const int8_t* kb = k_idx + (row / n_q) * (long long)L_max * d_I;
+    for (int sp = 0; sp < n_sp; ++sp) {
+      if (skind[sp] != KIND_S) continue;  // uniform: LDS after a barrier
+      const int j0 = sp * DIRECT_SPAN, j1 = min(n_valid, j0 + DIRECT_SPAN);
+      if (d_I == 128) rescore_keys<NT, 128>(q_row, w_row, kb, H_I, j0, j1, scores + row * ld, q_lds, w_lds);
+      else rescore_keys<NT, 64>(q_row, w_row, kb, H_I, j0, j1, scores + row * ld, q_lds, w_lds);
+    }
+  }
+  if (overflow) {
     fallback_select<NT, false>(rv, k, lds_big, wcnt, h256, scan_tmp, sh, out);
     return;
   }
-  int Lc;
-  if (from_table) {
-    Lc = ordered_compact4<NT, 4>(
-        0, rv.n_slots, wcnt, 0,
-        [&](int s0, int (&pl)[4]) {
-          unsigned m = rv.load4(s0, pl), r = 0;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) r |= (((m >> c) & 1u) && coarse_bin(pl[c]) >= bstar ? 1u : 0u) << c;
-          return r;
-        },
-        [&](int r, int s, int sc) {
-          if (r < CAP) {
-            lslot[r] = s;
-            lval[r] = sc;
-          }
-        });
-  } else {
-    // offsets of the lists, then an ordered compaction over their concatenation
-    int n_all;
-    const int ex = block_exclusive_scan<NT>(tid < n_sp ? lc : 0, scan_tmp, &n_all);
+
+  // offsets of the spans' sources, then an ordered compaction over their concatenation
+  int* lslot = lds_big;
+  int* lval = lds_big + CAP;
+  int n_all;
+  {
+    const int ex = block_exclusive_scan<NT>(tid < n_sp ? slen[tid] : 0, scan_tmp, &n_all);
     if (tid < n_sp) loff[tid] = ex;
     __syncthreads();
-    struct SP {
-      int slot, score;
-    };
-    int running = 0, parity = 0;
-    for (int base = 0; base < n_all; base += 4 * V * NT) {
-      unsigned m[V];
-      SP pl[V][4];
+  }
+  struct SP {
+    int slot, score;
+  };
+  int running = 0, parity = 0;
+  for (int base = 0; base < n_all; base += 4 * V * NT) {
+    unsigned m[V];
+    SP pl[V][4];
 #pragma unroll
-      for (int v = 0; v < V; ++v) {
-        m[v] = 0;
+    for (int v = 0; v < V; ++v) {
+      m[v] = 0;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int e = base + 4 * (v * NT + tid) + c;
-          const int ec = min(e, n_all - 1);  // clamped: the loads stay unconditional
-          int lo = 0, hi = n_sp;             // loff[lo] <= ec < loff[hi] (loff[n_sp] = n_all)
-          while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (loff[mid] <= ec) lo = mid;
-            else hi = mid;
-          }
-          const int* L = ws.lcand(row, lo) + 2 * (ec - loff[lo]);
+      for (int c = 0; c < 4; ++c) {
+        const int e = base + 4 * (v * NT + tid) + c;
+        const int ec = min(e, n_all - 1);  // clamped: the loads stay unconditional
+        int lo = 0, hi = n_sp;             // loff[lo] <= ec < loff[hi] (loff[n_sp] = n_all)
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (loff[mid] <= ec) lo = mid;
+          else hi = mid;
+        }
+        const int j = ec - loff[lo];
+        if (skind[lo] == KIND_L) {
+          const int* L = ws.lcand(row, lo) + 2 * j;
           pl[v][c].slot = L[0];
           pl[v][c].score = L[1];
-          m[v] |= (e < n_all && coarse_bin(pl[v][c].score) >= bstar ? 1u : 0u) << c;
+        } else {
+          pl[v][c].slot = lo * DIRECT_SPAN + j;
+          pl[v][c].score = rv.srow[lo * DIRECT_SPAN + j];
         }
+        m[v] |= (e < n_all && coarse_bin(pl[v][c].score) >= bstar ? 1u : 0u) << c;
       }
-      running = ordered_emit4<NT, V>(base, m, pl, wcnt + parity * V * NW, running, [&](int r, int, SP x) {
-        if (r < CAP) {
-          lslot[r] = x.slot;
-          lval[r] = x.score;
-        }
-      });
-      parity ^= 1;
     }
-    __syncthreads();
-    Lc = running;
+    running = ordered_emit4<NT, V>(base, m, pl, wcnt + parity * V * NW, running, [&](int r, int, SP x) {
+      if (r < CAP) {
+        lslot[r] = x.slot;
+        lval[r] = x.score;
+      }
+    });
+    parity ^= 1;
   }
-  finish_from_list<NT, false>(rv, min(Lc, CAP), lslot, lval, bstar, above, k, wcnt, h256, scan_tmp, sh, out);
+  __syncthreads();
+  finish_from_list<NT, false>(rv, min(running, CAP), lslot, lval, bstar, above, k, wcnt, h256, scan_tmp, sh, out);
 }
 
 // Block keep of the two-stage indexer: own block + the best n_keep-1 earlier blocks
@@ -922,8 +966,9 @@ static void launch_topk_t(const TopkArgs& a, hipStream_t st, long long rows) {
   if (!KEPT && split_rows(a, &w)) {
     if (a.hist_ready) {
       // the indexer built the histograms and the span lists: one kernel
-      hipLaunchKernelGGL((topk_list_finish_kernel<1024>), dim3((unsigned)rows), dim3(1024), 0, st, a.scores, a.ld,
-                         a.q_pos, a.L_max, a.k, w, a.idx, a.count);
+      hipLaunchKernelGGL((topk_list_finish_kernel<1024>), dim3((unsigned)rows), dim3(1024), 0, st,
+                         const_cast<int32_t*>(a.scores), a.ld, a.q_pos, a.L_max, a.k, w, a.q_idx, a.k_idx, a.w,
+                         a.w_per_query, a.n_q, a.H_I, a.d_I, a.idx, a.count);
       return;
     }
     // several workgroups per row: histogram and candidate compaction split over segments

@@ -422,12 +422,14 @@ def test_forward_decode_fused_selection(lsa, H_I):
     err.check()
 
 
-@pytest.mark.parametrize("kind", ["one_span_distinct", "one_span_equal", "two_spans_ties", "all_equal"])
+@pytest.mark.parametrize("kind", ["one_span_distinct", "one_span_equal", "two_spans_ties", "all_equal",
+                                  "spread_ties"])
 def test_forward_decode_fused_selection_concentrated(lsa, kind):
-    """Decode rows whose top-k sits in one or two 2048-key spans: the indexer's span
-    lists cannot hold it (the list keeps ~128 entries of a span), so the top-k must
-    notice (list bin above the cut) and select from the score table -- still bit for
-    bit the separate calls' lists and the oracle's."""
+    """Decode rows whose top-k the indexer's span lists cannot hold: concentrated in
+    one or two 2048-key spans (a list keeps ~64 entries: re-scored spans), heavy ties
+    inside a span (the span writes its table slice), all scores equal or ties spread
+    over every span (the cut bin overflows: every span re-scored, exact radix
+    fallback) -- still bit for bit the separate calls' lists and the oracle's."""
     L, k = 40000, 1024
     pos = [39999, 39000, 35000, 20000]
     wl = synthetic.Workload("deccon", B=len(pos), n_q=1, L=L, q_pos0=0, H_I=64, d_I=128, k=k, H_q=16)
@@ -445,8 +447,10 @@ def test_forward_decode_fused_selection_concentrated(lsa, kind):
         elif kind == "two_spans_ties":
             for lo, hi in ((2048, 2600), (10240, 10900)):   # two spans, ties inside each
                 inp["k_idx"][b, lo:hi] = q0[b]
-        else:
+        elif kind == "all_equal":
             inp["q_idx"][b] = 0                       # every score 0: the cut bin holds the whole row
+        else:
+            inp["k_idx"][b, 0:L:8] = q0[b]            # ~5000 ties spread over every span
     g = {kk: v.to(dev()) for kk, v in inp.items()}
     assert lsa.lsa_forward_stages(g, k, lsa.lsa_forward_workspace_size(g, k))[0] == "topk_reset"
     res = lsa.lsa_forward(g, k_top=k)
