@@ -24,7 +24,7 @@ inline int64_t score_ld(int32_t L) { return ((int64_t)L + 63) / 64 * 64; }
 
 // keys per workgroup span of the flat indexer
 inline int flat_span(int32_t L_max, bool direct) {
-  if (direct) return 2048;  // matches the LDS score buffer of the direct kernel
+  if (direct) return lsa::DIRECT_SPAN;  // the LDS score buffer of the direct kernel
   return L_max > 65536 ? 8192 : 4096;
 }
 
@@ -373,8 +373,8 @@ namespace {
 // A chunk of flat, one-query-per-sequence rows whose top-k splits each row over
 // several workgroups: the indexer builds the rows' score histograms itself.
 bool chunk_fused(const lsa_forward_args* a, int32_t nb, int32_t ni, void* topk_ws, size_t topk_ws_size) {
-  // the per-row finish reads one span list per thread: at most 256 spans of 2048 keys
-  if (a->two_stage || ni >= 8 || a->L_max > 256 * 2048) return false;
+  // the per-row finish reads one span list per thread: at most 256 spans
+  if (a->two_stage || ni >= 8 || a->L_max > 256LL * lsa::DIRECT_SPAN) return false;
   lsa::TopkArgs ta{};
   ta.B = nb;
   ta.n_q = ni;

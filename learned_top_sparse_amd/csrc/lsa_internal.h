@@ -68,6 +68,9 @@ struct BlkSelArgs {
 
 // waves per sparse-attention workgroup (each with its own 32-key tile state)
 constexpr int ATTN_WAVES = 4;
+// keys per workgroup of the direct (decode-shaped) flat indexer, and per candidate
+// list of the decode selection
+constexpr int DIRECT_SPAN = 4096;
 
 struct AttnArgs {
   const void* q;

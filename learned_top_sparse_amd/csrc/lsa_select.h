@@ -2,6 +2,7 @@
 // kernels and the indexer that can build a row's score histogram as it goes.
 #pragma once
 #include "lsa_device.h"
+#include "lsa_internal.h"
 
 namespace lsa {
 
@@ -52,15 +53,13 @@ __device__ __forceinline__ void find_cut_bin(const int* hist, int k, int* scan_t
 constexpr int INFO = 8;
 constexpr int GRP = 32;
 constexpr int NGRP = NBINS / GRP;
-// keys per workgroup of the direct (decode-shaped) flat indexer
-constexpr int DIRECT_SPAN = 2048;
 // slots per workgroup in the several-workgroups-per-row top-k
 constexpr int SEG = 8192;
 // Candidate list the direct indexer keeps per span when it builds the row's
 // histogram: the span's entries in its highest coarse bins, in slot order -- at
 // least LIST_MIN of them (all, if the span has fewer), at most LIST_CAP -- and the
 // lowest bin it took (lbw).  Every entry of the span below lbw is out of the list.
-constexpr int LIST_MIN = 64;
+constexpr int LIST_MIN = 128;
 constexpr int LIST_CAP = 512;
 
 // Per-row selection state of the several-workgroups top-k in its workspace:

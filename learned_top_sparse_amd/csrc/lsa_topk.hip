@@ -664,7 +664,7 @@ __device__ __forceinline__ void rescore_keys(const int8_t* __restrict__ q_row, c
 }
 
 // Flat rows whose selection state the indexer built (histogram, one candidate list
-// per 2048-key span, no score table): one workgroup per row.  The cut b* comes from
+// per span of DIRECT_SPAN keys, no score table): one workgroup per row.  The cut b* comes from
 // the row's group sums and the bins of the cut group.  A span is then
 //   L: its list reaches down to b* (lbw <= b*): all its entries of bins >= b* are in
 //      the list;

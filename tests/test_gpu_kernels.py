@@ -426,7 +426,7 @@ def test_forward_decode_fused_selection(lsa, H_I):
                                   "spread_ties"])
 def test_forward_decode_fused_selection_concentrated(lsa, kind):
     """Decode rows whose top-k the indexer's span lists cannot hold: concentrated in
-    one or two 2048-key spans (a list keeps ~64 entries: re-scored spans), heavy ties
+    one or two indexer spans (a list keeps ~128 entries: re-scored spans), heavy ties
     inside a span (the span writes its table slice), all scores equal or ties spread
     over every span (the cut bin overflows: every span re-scored, exact radix
     fallback) -- still bit for bit the separate calls' lists and the oracle's."""
