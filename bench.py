@@ -278,8 +278,9 @@ def main():
     kms = step.kernel_ms()
     alg = algorithmic(wl)
     tok_s = wl.B * wl.n_q / (ms * 1e-3)
-    idx_ms = kms["index_scores"]["ms_per_launch"]
-    launches = kms["index_scores"]["launches_per_step"]
+    idx_stage = "index_select" if "index_select" in kms else "index_scores"
+    idx_ms = kms[idx_stage]["ms_per_launch"]
+    launches = kms[idx_stage]["launches_per_step"]
     achieved = alg["index_bytes"] / launches / (idx_ms * 1e-3) / 1e9
     roof_t_ms = max(alg["index_bytes"] + alg["attn_gather_bytes"], 0) / (HBM_PEAK_GBS * 1e9) * 1e3
     res = {
@@ -298,7 +299,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": _describe(wl), "global_batch": wl.B, "seq_len": wl.L, "parallelism": "none"},
         "roofline": {
-            "bound": "hbm", "kernel": "index_scores (decode scan, idx_direct_kernel)",
+            "bound": "hbm", "kernel": f"{idx_stage} (decode scan, idx_decode_kernel)",
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
             "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": alg["index_bytes"] / launches, "launch_ms": idx_ms,

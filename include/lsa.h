@@ -235,18 +235,19 @@ lsa_status lsa_forward_plan(const lsa_forward_args* a, size_t ws_bytes, int64_t*
    one kernel or a short fixed sequence of them:
      BLOCK_REPS       block representatives (two_stage, once per call)
      BLOCK_PREFILTER  block scores and kept blocks of a chunk (two_stage)
-     TOPK_RESET       clears the selection state of a chunk's rows (flat rows of
-                      one query per sequence with the several-workgroups top-k:
-                      the indexer then builds each row's score histogram itself
-                      and TOPK skips its histogram pass)
-     INDEX_SCORES     the indexer over a chunk
+     INDEX_SELECT     the indexer over a chunk of flat rows of few queries per
+                      sequence (fewer than 8) that leaves, instead of the score
+                      table, each key span's share of the selection state (coarse
+                      score histogram and candidate list); TOPK then finishes each
+                      row from it (the decode selection)
+     INDEX_SCORES     the indexer over a chunk, writing the score table
      TOPK             the exact top-k of a chunk
      SPARSE_ATTN      sparse attention of a chunk (split-KV combine included)
    Writes min(n, max_codes) codes to `codes` (may be NULL) and n to *n_stages. */
 enum {
   LSA_STAGE_BLOCK_REPS = 1,
   LSA_STAGE_BLOCK_PREFILTER = 2,
-  LSA_STAGE_TOPK_RESET = 3,
+  LSA_STAGE_INDEX_SELECT = 3,
   LSA_STAGE_INDEX_SCORES = 4,
   LSA_STAGE_TOPK = 5,
   LSA_STAGE_SPARSE_ATTN = 6

@@ -23,7 +23,7 @@ EXPORTED = [
     "lsa_forward_workspace_size", "lsa_forward", "lsa_forward_plan", "lsa_forward_stages",
 ]
 
-STAGE_NAMES = {1: "block_reps", 2: "block_prefilter", 3: "topk_reset", 4: "index_scores", 5: "topk",
+STAGE_NAMES = {1: "block_reps", 2: "block_prefilter", 3: "index_select", 4: "index_scores", 5: "topk",
                6: "sparse_attn"}
 
 P = C.c_void_p

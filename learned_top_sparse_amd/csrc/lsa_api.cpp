@@ -333,6 +333,17 @@ FwdPlan plan_forward(const lsa_forward_args* a) {
   return p;
 }
 
+// top-k workspace of chunks of `rows` rows: the split top-k's, and the decode
+// selection's state for every chunk of fewer than 8 queries per sequence that occurs
+// (all chunks when n_q == 1; a chunk of fewer rows needs no more)
+size_t topk_ws_for(const lsa_forward_args* a, long long rows) {
+  long long dec_rows = 0;
+  if (a->n_q == 1 || rows < 8) dec_rows = rows;
+  else if (a->n_q % rows > 0 && a->n_q % rows < 8) dec_rows = a->n_q % rows;  // the last, short chunk
+  const size_t dec = dec_rows > 0 ? lsa::dec_sel_ws_bytes(dec_rows, a->L_max, a->k_top) : 0;
+  return std::max(dec, lsa::topk_ws_bytes(rows, a->L_max));
+}
+
 // workspace for a chunk of `rows` rows
 size_t chunk_bytes(const lsa_forward_args* a, const FwdPlan& p, long long rows) {
   size_t s = p.fixed;
@@ -343,7 +354,7 @@ size_t chunk_bytes(const lsa_forward_args* a, const FwdPlan& p, long long rows) 
   }
   const int split = resolve_split(1, (int32_t)rows, a->k_top, a->attn_split);
   s += attn_ws_bytes(rows, a->H_q, a->d, split);
-  if (!a->two_stage) s += align_up(lsa::topk_ws_bytes(rows, a->L_max));
+  if (!a->two_stage) s += align_up(topk_ws_for(a, rows));
   return s;
 }
 
@@ -370,20 +381,13 @@ long long plan_rows(const lsa_forward_args* a, const FwdPlan& p, size_t ws_bytes
 
 namespace {
 
-// A chunk of flat, one-query-per-sequence rows whose top-k splits each row over
-// several workgroups: the indexer builds the rows' score histograms itself.
-bool chunk_fused(const lsa_forward_args* a, int32_t nb, int32_t ni, void* topk_ws, size_t topk_ws_size) {
-  // the per-row finish reads one span list per thread: at most 256 spans
-  if (a->two_stage || ni >= 8 || a->L_max > 256LL * lsa::DIRECT_SPAN) return false;
-  lsa::TopkArgs ta{};
-  ta.B = nb;
-  ta.n_q = ni;
-  ta.L_max = a->L_max;
-  ta.ws = topk_ws;
-  ta.ws_bytes = topk_ws_size;
-  int* base = nullptr;
-  int n_seg = 0, n_lst = 0;
-  return lsa::topk_split_rows(ta, &base, &n_seg, &n_lst);
+// A chunk of flat rows of few queries per sequence takes the decode selection: the
+// indexer builds each row's histogram and span candidate lists, and the top-k
+// finishes every row from them (no score table in between) -- where its state fits
+// the chunk's top-k workspace of topk_ws_size bytes.
+bool chunk_fused(const lsa_forward_args* a, int32_t nb, int32_t ni, size_t topk_ws_size) {
+  const size_t need = lsa::dec_sel_ws_bytes((long long)nb * ni, a->L_max, a->k_top);
+  return !a->two_stage && ni < 8 && need > 0 && need <= topk_ws_size;
 }
 
 // chunks of lsa_forward for `rows` rows per chunk, as (b0, nb, i0, ni)
@@ -402,12 +406,10 @@ void for_each_chunk(const lsa_forward_args* a, long long rows, F f) {
 std::vector<int32_t> forward_stages(const lsa_forward_args* a, const FwdPlan& p, long long rows) {
   std::vector<int32_t> st;
   if (a->two_stage && p.n_blocks > 0) st.push_back(LSA_STAGE_BLOCK_REPS);
-  const size_t topk_ws_size = a->two_stage ? 0 : lsa::topk_ws_bytes(rows, a->L_max);
-  alignas(16) char dummy[16];
+  const size_t topk_ws_size = a->two_stage ? 0 : topk_ws_for(a, rows);
   for_each_chunk(a, rows, [&](int32_t, int32_t nb, int32_t, int32_t ni) {
     if (a->two_stage) st.push_back(LSA_STAGE_BLOCK_PREFILTER);
-    if (chunk_fused(a, nb, ni, dummy, topk_ws_size)) st.push_back(LSA_STAGE_TOPK_RESET);
-    st.push_back(LSA_STAGE_INDEX_SCORES);
+    st.push_back(chunk_fused(a, nb, ni, topk_ws_size) ? LSA_STAGE_INDEX_SELECT : LSA_STAGE_INDEX_SCORES);
     st.push_back(LSA_STAGE_TOPK);
     st.push_back(LSA_STAGE_SPARSE_ATTN);
   });
@@ -481,7 +483,7 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
   void* attn_ws = base + off;
   off += attn_ws_bytes(rows, a->H_q, a->d, resolve_split(1, (int32_t)rows, a->k_top, a->attn_split));
   void* topk_ws = a->two_stage ? nullptr : static_cast<void*>(base + off);
-  const size_t topk_ws_size = a->two_stage ? 0 : lsa::topk_ws_bytes(rows, a->L_max);
+  const size_t topk_ws_size = a->two_stage ? 0 : topk_ws_for(a, rows);
 
   const int32_t d_I = a->d_I, H_I = a->H_I, H_q = a->H_q, d = a->d, L = a->L_max, kt = a->k_top;
   // one split count for every chunk, so no chunk needs more attention workspace than sized
@@ -549,18 +551,16 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
     ta.count = cnt;
     ta.ws = topk_ws;
     ta.ws_bytes = topk_ws_size;
-    if (chunk_fused(a, nb, ni, topk_ws, topk_ws_size)) {
+    if (chunk_fused(a, nb, ni, topk_ws_size)) {
       // the indexer builds each row's selection state (histogram, span candidate lists)
-      if (lsa::launch_topk_reset(ta, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
-      if (!lsa::topk_split_rows(ta, &ia.sel_base, &ia.sel_n_seg, &ia.sel_n_lst)) return LSA_ERR_INTERNAL;
-      ia.k_top = kt;
+      lsa::DecLayout dl;
+      if (!lsa::dec_sel_layout((long long)nb * ni, L, kt, &dl)) return LSA_ERR_INTERNAL;
       ta.hist_ready = true;
-      ta.q_idx = qi;
-      ta.k_idx = ki;
-      ta.w = wq;
-      ta.w_per_query = a->w_per_query ? 1 : 0;
-      ta.H_I = H_I;
-      ta.d_I = d_I;
+      ia.sel_base = static_cast<int*>(topk_ws);
+      ia.sel_rec_ints = dl.rec_ints;
+      ia.sel_parts = dl.parts;
+      ia.sel_lcap = dl.lcap;
+      ia.k_top = kt;
     }
     if (lsa::launch_index_scores(ia, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
     if (lsa::launch_topk(ta, s) != hipSuccess || !mark()) return LSA_ERR_HIP;

@@ -225,26 +225,18 @@ __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
 
 // ---------------------------------------------------------------------------------
 // Direct scores: one query per workgroup, each wave takes 64-slot groups and loads
-// its key rows straight into MFMA B fragments (no LDS).  Used for decode (flat,
-// whole context split into spans over grid.x) and for the two-stage token stage
-// (KEPT: slot s is key kept[s / bs] * bs + s % bs; one workgroup covers all slots).
-// The scan is bound by HBM, so each wave keeps a ring of RING groups of fragments:
-// RING-1 groups of loads are in flight while one group is multiplied (2 waves/SIMD).
-// HIST (flat only): instead of writing the score table, the workgroup builds its
-// share of the row's selection state in the split top-k's workspace (SegWs, cleared
-// beforehand): it counts its scores into an LDS histogram of the selection's coarse
-// bins, adds the bins it touched to the row's histogram (device-scope atomics), and
-// writes its span's candidate list -- the entries of its highest bins, in slot order.
-// Only a span whose list its own top bins cut short (heavy ties) writes its table
-// slice as well (marked lbw = -1).  The exact top-k that follows reads the lists.
+// its key rows straight into MFMA B fragments (no LDS).  Used for flat rows of few
+// queries (whole context split into spans over grid.x) and for the two-stage token
+// stage (KEPT: slot s is key kept[s / bs] * bs + s % bs; one workgroup covers all
+// slots).  The scan is bound by HBM, so each wave keeps a ring of RING groups of
+// fragments: RING-1 groups of loads are in flight while one group is multiplied
+// (2 waves/SIMD).
 // Grid: x = n_spans (1 for KEPT), y = B * n_q.
-template <int D, int MT, bool KEPT, bool HIST>
+template <int D, int MT, bool KEPT>
 __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
     int w_per_query, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ kept, int bs,
-    int n_keep, int n_q, int L_max, int H_I, int span, int32_t* __restrict__ scores, long long ld,
-    SegWs sel, int k_top) {
-  static_assert(!(KEPT && HIST), "the histogram is built for flat rows only");
+    int n_keep, int n_q, int L_max, int H_I, int span, int32_t* __restrict__ scores, long long ld) {
   constexpr int KS = D / 64;
   constexpr int RING = 4;
   // Scores collect in LDS and leave in one burst at the end: a global store between
@@ -253,7 +245,6 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
   constexpr int SBUF = KEPT ? 8192 : DIRECT_SPAN;
   __shared__ int kept_s[KEPT ? 256 : 1];
   __shared__ __attribute__((aligned(16))) int sbuf[SBUF];
-  __shared__ int lhist[HIST ? NBINS : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
   const long long row = blockIdx.y;
   const int b = (int)blockIdx.y / n_q;
@@ -275,12 +266,6 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
     s_lim = min(s_begin + span, L_max);
     s_end = s_lim;  // narrowed to the position once it has arrived
   }
-  bool hist = false;
-  int bmin = NBINS, bmax = -1;  // bins this thread counted into
-  __shared__ int brange[2];
-  __shared__ int wcnt_l[2 * 4 * 4];
-  __shared__ int scan_l[5];
-  __shared__ int lsh[2];
 
   v4i A[MT][KS];
   int wv[MT][4];
@@ -345,8 +330,7 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
         if (is_cand(c0 + t)) scores[srow + c0 + t] = sbuf[t];
     }
   };
-  // the ring loop (and, unless the span's selection state is built, the score flush) of
-  // one chunk whose prologue has been issued
+  // the ring loop and the score flush of one chunk whose prologue has been issued
   auto run_chunk = [&](int c0, int c1) {
     const int n_groups = (c1 - c0 + 63) / 64;
     const int n_iter = ((n_groups + 3) / 4 + RING - 1) / RING * RING;  // groups per wave, padded
@@ -371,16 +355,7 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
       }
       const int res = reduce_scatter4(part);
       const int s = sg + 16 * g + r16;
-      if (s < c1) {
-        sbuf[s - c0] = res;
-        // LDS only, inside the ring loop where the waves mostly wait on HBM anyway
-        if (hist && s < s_end) {
-          const int bin = coarse_bin(res);
-          atomicAdd(&lhist[bin], 1);
-          bmin = min(bmin, bin);
-          bmax = max(bmax, bin);
-        }
-      }
+      if (s < c1) sbuf[s - c0] = res;
     };
     for (int i0 = 0; i0 < n_iter; i0 += RING) {
 #pragma unroll
@@ -390,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
       }
     }
     __syncthreads();
-    if (!hist) store_chunk(c0, c1);
+    store_chunk(c0, c1);
     __syncthreads();
   };
 
@@ -408,101 +383,261 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
     p = min(p_raw, L_max - 1);
     s_end = min(s_lim, p + 1);
     if (s_begin >= s_end) return;  // nothing of this span is a candidate (uniform)
-    // a row with no more candidates than k takes them all: no histogram needed
-    hist = HIST && p + 1 > k_top;
-    if (hist) {
-      for (int t = tid; t < NBINS; t += 256) lhist[t] = 0;
-      if (tid == 0) {
-        brange[0] = NBINS;
-        brange[1] = -1;
-      }
-      __syncthreads();
-    }
     run_chunk(s_begin, s_lim);
   }
-  if (hist) {
-    // Only the bins this workgroup touched are visited (a row's scores fill a narrow
-    // band of bins).
-    static_assert(NGRP == 256, "one group per thread");
-    for (int o = 32; o > 0; o >>= 1) {
-      bmin = min(bmin, __shfl_xor(bmin, o));
-      bmax = max(bmax, __shfl_xor(bmax, o));
-    }
-    if (lane == 0) {
-      atomicMin(&brange[0], bmin);
-      atomicMax(&brange[1], bmax);
-    }
-    __syncthreads();
-    const int lo = brange[0], hi = brange[1];
+}
 
-    // The span's candidate list: lowest bin bw such that bins >= bw hold at least
-    // need = min(LIST_MIN, entries) entries; if that bin would overflow LIST_CAP the
-    // list stops above it (fewer entries; the top-k then checks bw against its cut).
-    // Thread t sums a chunk of CB bins from the top of the band, a block scan finds
-    // the chunk where the count crosses need, and that thread walks its chunk.
-    {
-      const int n_ent = s_end - s_begin, need = min(LIST_MIN, n_ent);
-      const int CB = (hi - lo + 256) / 256;
-      const int top = hi - tid * CB;  // this thread's bins: top, top-1, ..., top-CB+1 (>= lo)
-      int csum = 0;
-      for (int i = 0; i < CB; ++i) csum += top - i >= lo ? lhist[top - i] : 0;
-      int tot;
-      const int excl = block_exclusive_scan<256>(csum, scan_l, &tot);
-      if (excl < need && excl + csum >= need) {
-        int acc = excl;
-        for (int i = 0; i < CB; ++i) {
-          const int b = top - i;
-          const int h = b >= lo ? lhist[b] : 0;
-          if (acc + h >= need) {
-            lsh[0] = acc + h <= LIST_CAP ? b : b + 1;
-            lsh[1] = acc + h > LIST_CAP;
-            break;
-          }
-          acc += h;
-        }
-      }
-      __syncthreads();
-      const int bw = lsh[0];
-      // A list cut short by its own top bins (more than LIST_CAP entries tie there)
-      // would leave the top-k to re-score the span: such a span writes its table slice
-      // instead and is marked lbw = -1.
-      const bool tied = lsh[1] != 0;
-      int* lc = sel.lcand(row, blockIdx.x);
-      const int n_list = ordered_compact<256, 4>(
-          n_ent, wcnt_l,
-          [&](int t, int& v) {
-            v = sbuf[t];
-            return coarse_bin(v) >= bw;
-          },
-          [&](int r, int t, int v) {
-            if (r < LIST_CAP) {
-              lc[2 * r] = s_begin + t;
-              lc[2 * r + 1] = v;
-            }
-          });
-      if (tied) store_chunk(s_begin, s_lim);
-      if (tid == 0) {
-        sel.lcnt(row)[blockIdx.x] = min(n_list, LIST_CAP);
-        sel.lbw(row)[blockIdx.x] = tied ? -1 : bw;
-      }
-    }
+// ---------------------------------------------------------------------------------
+// Decode scores that leave each row's selection state instead of a score table (flat
+// rows of few queries, rows with more valid keys than k).  A row's n_valid keys are
+// cut into gridDim.x spans of dec_span(n_valid, gridDim.x) consecutive keys, one
+// 8-wave workgroup each, and the launch is sized to about one workgroup per compute
+// unit: start-up and the closing selection work are paid once per compute unit, not
+// once per few thousand keys.
+//   * Each wave streams 64-key groups straight into MFMA B fragments through a ring
+//     of RING register stages, as the direct kernel does; the groups are handed out
+//     by an LDS counter as ring slots free up, so the waves finish together.
+//   * The span's scores stay in LDS, and each is counted into a packed LDS histogram
+//     of the selection's coarse bins (16-bit counters: a span has < 65536 keys) as it
+//     is produced.
+//   * At the end the workgroup finds its list's lowest bin lbw -- the highest bin such
+//     that bins >= lbw hold at least min(entries, k) entries -- and writes its record
+//     (DecWs): the list (its entries of bins >= lbw in slot order), its group sums, the
+//     bins of its band and the header.  No span can hold k entries above the row's cut
+//     bin (fewer than k entries of the whole row are), so every list reaches down to
+//     the cut.  A list that would hold more than lcap entries (heavy ties in the bin
+//     that completes it) is replaced by the span's slice of the score table (lbw = -1).
+//     Only plain stores, issued last, which nothing waits for: no device-scope
+//     atomics (several workgroups on different XCDs would contend for the row's
+//     bins) and nothing to clear beforehand.
+// Grid: x = parts, y = B * n_q.
+template <int D, int MT>
+__global__ __launch_bounds__(512, 1) void idx_decode_kernel(
+    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
+    int w_per_query, const int32_t* __restrict__ q_pos, int n_q, int L_max, int H_I,
+    int32_t* __restrict__ scores, long long ld, DecWs sel, int k_top) {
+  constexpr int NT = 512, NWV = NT / 64, KS = D / 64, RING = 4;
+  static_assert(NGRP <= NT, "one group sum per thread");
+  __shared__ __attribute__((aligned(16))) int sbuf[DEC_SPAN_MAX];
+  __shared__ unsigned lh[NBINS / 2];  // bin b: 16-bit count at bit 16 * (b & 1) of word b / 2
+  __shared__ int brange[2];
+  __shared__ int scan_l[NWV + 1];
+  __shared__ int lsh[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const long long row = blockIdx.y;
+  const int part = blockIdx.x;
+  const int b = (int)blockIdx.y / n_q;
 
-    // histogram: bins go out in lane order (a wave's atomics touch few cache lines);
-    // thread t also sums group t in LDS if the group meets the band (skewed order:
-    // the lanes of a wave read distinct banks)
-    int* gh = sel.hist(row);
-    int* gsum = sel.gsum(row);
-    if (tid * GRP <= hi && tid * GRP + GRP > lo) {
-      int sum = 0;
-#pragma unroll 8
-      for (int i = 0; i < GRP; ++i) sum += lhist[tid * GRP + ((i + tid) & (GRP - 1))];
-      if (sum) atomicAdd(&gsum[tid], sum);
+  v4i A[MT][KS];
+  int wv[MT][4];
+  issue_query<D, MT>(q_idx, w, w_per_query, row, H_I, A, wv);
+  const int n_valid = max(min(q_pos[row], L_max - 1) + 1, 0);
+  // a row with no more valid keys than k takes them all: nothing to score
+  if (n_valid <= k_top) return;
+  const int span = dec_span(n_valid, gridDim.x);
+  const int s_begin = part * span, s_end = min(s_begin + span, n_valid);
+  if (s_begin >= s_end) return;  // uniform
+  const int n_ent = s_end - s_begin;
+  const int8_t* kb = k_idx + (long long)b * L_max * D;
+
+  // Ring of key fragments.  Loads past the span re-read its last key, so every load
+  // is unconditional.
+  v4i ring[RING][4][KS];
+  const int n_groups = (n_ent + 63) / 64;
+  auto load_group = [&](int grp, v4i (&Bf)[4][KS]) {
+    const int sg = s_begin + 64 * grp;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int8_t* kr = kb + (long long)min(sg + 16 * nt + r16, s_end - 1) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
     }
-    for (int t = lo + tid; t <= hi; t += 256) {
-      const int h = lhist[t];
-      if (h) atomicAdd(&gh[t], h);
+  };
+  // Groups go to the waves in the order they free a ring slot: the first RING-1 of
+  // each wave are fixed (wave, wave + 8, ...), the rest come from a shared counter.
+  int gi[RING];  // group in each ring slot (wave-uniform)
+#pragma unroll
+  for (int r = 0; r < RING - 1; ++r) {
+    gi[r] = wave + NWV * r;
+    load_group(gi[r], ring[r]);
+  }
+  __shared__ int next_grp;
+  int wt[MT][4];
+  query_weights<MT>(wv, H_I, true, wt);
+  for (int t = tid; t < NBINS / 2; t += NT) lh[t] = 0;
+  if (tid == 0) {
+    brange[0] = NBINS;
+    brange[1] = -1;
+    next_grp = NWV * (RING - 1);
+  }
+  __syncthreads();
+
+  int bmin = NBINS, bmax = -1;  // bins this thread counted into
+  auto compute_group = [&](int grp, const v4i (&Bf)[4][KS]) {
+    const int sg = s_begin + 64 * grp;
+    int part_s[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      v4i acc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[mt] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc[mt] = mfma_i8(A[mt][ks], Bf[nt][ks], acc[mt]);
+      }
+      int ps = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) ps = relu_mad24(acc[mt][e], wt[mt][e], ps);
+      part_s[nt] = ps;
+    }
+    const int res = reduce_scatter4(part_s);
+    const int s = sg + 16 * g + r16;
+    if (s < s_end) {
+      // LDS only, inside the ring loop where the waves mostly wait on HBM anyway
+      sbuf[s - s_begin] = res;
+      const int bin = coarse_bin(res);
+      atomicAdd(&lh[bin >> 1], 1u << ((bin & 1) << 4));
+      bmin = min(bmin, bin);
+      bmax = max(bmax, bin);
+    }
+  };
+  // Waves take groups from a shared counter as they free a ring slot, so a wave the
+  // memory system serves faster takes more of them (with a fixed share the waves of a
+  // workgroup drift far apart and the early ones idle).  A wave's groups only grow,
+  // so once the oldest slot holds a group past the span, every slot does.  The grab
+  // for the next slot is issued a step ahead, so its LDS latency is hidden.
+  auto grab = [&]() -> int {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&next_grp, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  int nx = grab();
+  for (bool live = true; live;) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      const int gl = nx;
+      nx = grab();
+      gi[(r + RING - 1) % RING] = gl;
+      load_group(gl, ring[(r + RING - 1) % RING]);
+      if (gi[r] >= n_groups) {
+        live = false;
+        break;
+      }
+      compute_group(gi[r], ring[r]);
     }
   }
+
+  // band of bins the workgroup touched (a span's scores fill a narrow band)
+  for (int o = 32; o > 0; o >>= 1) {
+    bmin = min(bmin, __shfl_xor(bmin, o));
+    bmax = max(bmax, __shfl_xor(bmax, o));
+  }
+  if (lane == 0) {
+    atomicMin(&brange[0], bmin);
+    atomicMax(&brange[1], bmax);
+  }
+  __syncthreads();
+  const int lo = brange[0], hi = brange[1];
+  auto bin_count = [&](int bb) -> int { return (int)((lh[bb >> 1] >> ((bb & 1) << 4)) & 0xffffu); };
+
+  // The list's lowest bin bw: thread t sums a chunk of CB bins from the top of the
+  // band, a block scan finds the chunk where the count reaches need, and that thread
+  // walks its chunk.
+  const int need = min(n_ent, k_top);
+  {
+    const int CB = (hi - lo + NT) / NT;
+    const int top = hi - tid * CB;  // this thread's bins: top, top-1, ..., top-CB+1 (>= lo)
+    int csum = 0;
+    for (int i = 0; i < CB; ++i) csum += top - i >= lo ? bin_count(top - i) : 0;
+    int tot;
+    const int excl = block_exclusive_scan<NT>(csum, scan_l, &tot);
+    if (excl < need && excl + csum >= need) {
+      int acc = excl;
+      for (int i = 0; i < CB; ++i) {
+        const int bb = top - i;
+        const int h = bb >= lo ? bin_count(bb) : 0;
+        if (acc + h >= need) {
+          lsh[0] = bb;
+          lsh[1] = acc + h > sel.lcap;
+          break;
+        }
+        acc += h;
+      }
+    }
+    __syncthreads();
+  }
+  const int bw = lsh[0];
+  const bool tied = lsh[1] != 0;
+  int n_list = 0;
+  if (tied) {
+    // heavy ties: the span's slice of the score table instead of a list
+    int32_t* srow = scores + row * ld;
+    for (int t = tid; t < n_ent; t += NT) srow[s_begin + t] = sbuf[t];
+  } else {
+    // The list: thread t takes C consecutive entries, reads them as 16-byte quads --
+    // all reads in flight together -- and marks the selected ones in a bit mask.  C/4
+    // is odd, so the lanes' first quads are an odd number of quads apart and any 16
+    // lanes' quads fall in distinct bank groups (an even count, e.g. C = 64, puts
+    // every lane of a read on the same banks).  A block scan of the counts gives each
+    // thread its first rank, and the thread writes its entries in slot order, one
+    // 8-byte (slot, score) store each.
+    constexpr int CQ = DEC_SPAN_MAX / NT / 4;  // quads per thread at most
+    static_assert(DEC_SPAN_MAX % (4 * NT) == 0 && CQ % 2 == 1, "whole quads per thread, an odd number at most");
+    constexpr int NWD = (4 * CQ + 31) / 32;
+    const int thr = bin_floor(bw);  // coarse_bin(v) >= bw  <=>  v >= thr
+    const int C = (((n_ent + 4 * NT - 1) / (4 * NT)) | 1) * 4;
+    const int c0 = min(tid * C, n_ent), len = min(C, n_ent - c0);
+    unsigned msk[NWD];  // bit j: entry c0 + j is in the list
+    {
+      v4i v[CQ];
+#pragma unroll
+      for (int q = 0; q < CQ; ++q) v[q] = *(const v4i*)&sbuf[min(c0 + 4 * q, DEC_SPAN_MAX - 4)];
+#pragma unroll
+      for (int wd = 0; wd < NWD; ++wd) msk[wd] = 0;
+#pragma unroll
+      for (int q = 0; q < CQ; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) msk[(4 * q + e) >> 5] |= (v[q][e] >= thr ? 1u : 0u) << ((4 * q + e) & 31);
+#pragma unroll
+      for (int wd = 0; wd < NWD; ++wd) {  // entries past the thread's own
+        const int nb = len - 32 * wd;
+        msk[wd] &= nb >= 32 ? ~0u : (nb <= 0 ? 0u : (1u << nb) - 1u);
+      }
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int wd = 0; wd < NWD; ++wd) cnt += __popc(msk[wd]);
+    int r = block_exclusive_scan<NT>(cnt, scan_l, &n_list);
+    int2* lc = reinterpret_cast<int2*>(sel.list(row, part));
+#pragma unroll
+    for (int wd = 0; wd < NWD; ++wd) {
+      unsigned m = msk[wd];
+      while (m) {
+        const int j = 32 * wd + __ffs(m) - 1;
+        m &= m - 1;
+        lc[r++] = make_int2(s_begin + c0 + j, sbuf[c0 + j]);
+      }
+    }
+  }
+
+  // the rest of the record: group sums (thread t sums group t; skewed order, so the
+  // lanes of a wave read distinct banks), the band's bins, the header
+  if (tid < NGRP) {
+    int sum = 0;
+    if (tid * GRP <= hi && tid * GRP + GRP > lo) {
+#pragma unroll
+      for (int i = 0; i < GRP / 2; ++i) {
+        const unsigned v = lh[tid * (GRP / 2) + ((i + tid) & (GRP / 2 - 1))];
+        sum += (int)(v & 0xffffu) + (int)(v >> 16);
+      }
+    }
+    sel.gsum(row, part)[tid] = sum;
+  }
+  int* hrec = sel.hist(row, part);
+  for (int t = lo + tid; t <= hi; t += NT) hrec[t] = bin_count(t);
+  if (tid == 0) *reinterpret_cast<int4*>(sel.hdr(row, part)) = make_int4(lo, hi, n_list, tied ? -1 : bw);
 }
 
 // ---------------------------------------------------------------------------------
@@ -678,26 +813,29 @@ static hipError_t launch_flat_t(const IdxArgs& a, hipStream_t st) {
 }
 template <int D, int MT, bool KEPT>
 static hipError_t launch_direct_t(const IdxArgs& a, hipStream_t st) {
+  if (a.sel_base != nullptr) {
+    // decode rows that build their selection state: one span per workgroup, the
+    // span lists in the layout the per-row finish reads
+    if (KEPT || a.sel_parts < 1 || a.sel_parts > DEC_MAX_PARTS || a.sel_lcap < 1 ||
+        dec_span(a.L_max, a.sel_parts) > DEC_SPAN_MAX)
+      return hipErrorInvalidValue;
+    DecWs sel;
+    sel.base = a.sel_base;
+    sel.rec_ints = a.sel_rec_ints;
+    sel.parts = a.sel_parts;
+    sel.lcap = a.sel_lcap;
+    hipLaunchKernelGGL((idx_decode_kernel<D, MT>), dim3((unsigned)a.sel_parts, (unsigned)(a.B * a.n_q)), dim3(512),
+                       0, st, a.q_idx, a.k_idx, a.w, a.w_per_query, a.q_pos, a.n_q, a.L_max, a.H_I, a.scores,
+                       (long long)a.ld, sel, a.k_top);
+    return hipGetLastError();
+  }
   // flat rows: one span per workgroup, exactly the LDS score buffer
   if (!KEPT && a.span != DIRECT_SPAN) return hipErrorInvalidValue;
   const int n_spans = KEPT ? 1 : (a.L_max + a.span - 1) / a.span;
   dim3 grid((unsigned)n_spans, (unsigned)(a.B * a.n_q));
-  if constexpr (!KEPT) {
-    if (a.sel_base != nullptr) {
-      SegWs sel;
-      sel.base = a.sel_base;
-      sel.n_seg = a.sel_n_seg;
-      sel.n_lst = a.sel_n_lst;
-      if (n_spans > sel.n_lst) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((idx_direct_kernel<D, MT, false, true>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.w,
-                         a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I,
-                         a.span, a.scores, (long long)a.ld, sel, a.k_top);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((idx_direct_kernel<D, MT, KEPT, false>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.w,
-                     a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I,
-                     a.span, a.scores, (long long)a.ld, SegWs{}, 0);
+  hipLaunchKernelGGL((idx_direct_kernel<D, MT, KEPT>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.w,
+                     a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I, a.span,
+                     a.scores, (long long)a.ld);
   return hipGetLastError();
 }
 

@@ -19,11 +19,12 @@ struct IdxArgs {
   long long ld;
   int span;        // keys per workgroup span (flat)
   bool use_direct; // flat scores with one query per workgroup (decode-shaped)
-  // optional (direct flat only): also build each row's selection state -- its
-  // coarse score histogram and one candidate list per span -- in the split top-k's
-  // workspace (cleared beforehand by launch_topk_reset)
+  // optional (direct flat only): leave each span's share of the row's selection
+  // state -- its coarse score histogram and candidate list -- in the decode
+  // selection's workspace (dec_sel_layout) instead of writing the score table
   int* sel_base;
-  int sel_n_seg, sel_n_lst;
+  long long sel_rec_ints;
+  int sel_parts, sel_lcap;
   int k_top;
 };
 
@@ -50,12 +51,7 @@ struct TopkArgs {
   int32_t* count;
   void* ws;          // optional: enables the several-workgroups-per-row path
   size_t ws_bytes;
-  bool hist_ready;   // the indexer built the rows' selection state in ws (no score table)
-  // with hist_ready: the indexer's inputs, to re-score spans whose list is too short
-  const int8_t* q_idx;
-  const int8_t* k_idx;
-  const int32_t* w;
-  int w_per_query, H_I, d_I;
+  bool hist_ready;   // the indexer built the rows' selection state in ws (dec_sel_layout)
 };
 
 struct BlkSelArgs {
@@ -68,8 +64,7 @@ struct BlkSelArgs {
 
 // waves per sparse-attention workgroup (each with its own 32-key tile state)
 constexpr int ATTN_WAVES = 4;
-// keys per workgroup of the direct (decode-shaped) flat indexer, and per candidate
-// list of the decode selection
+// keys per workgroup of the direct (decode-shaped) flat indexer that writes a score table
 constexpr int DIRECT_SPAN = 4096;
 
 struct AttnArgs {
@@ -95,11 +90,18 @@ hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 // workspace that lets lsa_topk split each row over several workgroups (0 = not used)
 size_t topk_ws_bytes(long long rows, int L_max);
-// The several-workgroups path applies to these arguments (flat rows, workspace big
-// enough): returns the workspace layout the indexer fills (base, segments, lists).
-bool topk_split_rows(const TopkArgs& a, int** base, int* n_seg, int* n_lst);
-// clears the selection state (histograms, counters) of every row of `a`
-hipError_t launch_topk_reset(const TopkArgs& a, hipStream_t st);
+// Decode selection: the indexer builds each row's selection state (histogram, one
+// candidate list per span) and one workgroup per row finishes the top-k from it.
+// Layout of `rows` rows of L_max keys and top-k size k: spans per row, list
+// capacity, ints per record.  Returns false where the path does not apply.
+struct DecLayout {
+  int parts, lcap;
+  long long rec_ints;  // ints per (row, span) record
+};
+bool dec_sel_layout(long long rows, int L_max, int k, DecLayout* out);
+// workspace of the decode selection (0 where it does not apply); a chunk of fewer
+// rows of the same L_max and k never needs more per row
+size_t dec_sel_ws_bytes(long long rows, int L_max, int k);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
 
 }  // namespace lsa

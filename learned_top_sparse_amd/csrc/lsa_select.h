@@ -55,36 +55,74 @@ constexpr int GRP = 32;
 constexpr int NGRP = NBINS / GRP;
 // slots per workgroup in the several-workgroups-per-row top-k
 constexpr int SEG = 8192;
-// Candidate list the direct indexer keeps per span when it builds the row's
-// histogram: the span's entries in its highest coarse bins, in slot order -- at
-// least LIST_MIN of them (all, if the span has fewer), at most LIST_CAP -- and the
-// lowest bin it took (lbw).  Every entry of the span below lbw is out of the list.
-constexpr int LIST_MIN = 128;
-constexpr int LIST_CAP = 512;
 
-// Per-row selection state of the several-workgroups top-k in its workspace:
+// Smallest score whose coarse bin is >= bw (bins 896..7295 are the ones coarse_bin
+// produces): coarse_bin(s) >= bw  <=>  s >= bin_floor(bw).  Inverts the mapping above:
+// g values below 256 are u itself; g >= 256 has shift g/128 - 1 and mantissa
+// 128 + g%128.  On the negative side the bin of ~u falls as u grows, so the bound is
+// -(smallest u of the next g value).
+__device__ __forceinline__ int bin_floor(int bw) {
+  auto umin_of = [](int gv) -> unsigned {
+    return gv < 256 ? (unsigned)gv : (unsigned)(128 + (gv & 127)) << ((gv >> 7) - 1);
+  };
+  if (bw >= 4096) return (int)umin_of(bw - 4096);
+  const int g1 = 4096 - bw;
+  return g1 > 3199 ? INT_MIN : -(int)umin_of(g1);
+}
+
+// Decode selection (flat rows, the indexer builds the selection state): every row's
+// n_valid keys are cut into `parts` spans of dec_span(n_valid, parts) consecutive keys,
+// one indexer workgroup each.  A span's scores stay in that workgroup's LDS, so a span
+// holds at most DEC_SPAN_MAX keys; the launch aims at DEC_WGS workgroups (one per
+// compute unit of an MI355X) with spans of at least DEC_SPAN_MIN keys.
+constexpr int DEC_SPAN_MAX = 34816;
+constexpr int DEC_WGS = 256;
+constexpr int DEC_SPAN_MIN = 2048;
+constexpr int DEC_MAX_PARTS = 1024;  // the per-row finish takes one span per thread
+__host__ __device__ __forceinline__ int dec_span(int n_valid, int parts) {
+  return ((n_valid + parts - 1) / parts + 63) / 64 * 64;
+}
+
+// What each decode-indexer workgroup leaves for the per-row finish, one record per
+// (row, span), written in full with plain stores (nothing to clear beforehand):
+//   hdr[4] = {lo, hi, lcnt, lbw}: the band of coarse bins its scores fall in, its
+//     list length and the lowest bin its list takes (-1: no list, its scores are in
+//     its slice of the score table);
+//   gsum[NGRP]: its counts per group of GRP bins;
+//   hist[NBINS]: its counts per bin, bins lo..hi only;
+//   list[2 * lcap]: (slot, score) pairs in slot order (16-byte aligned).
+// Records of one row are consecutive; rows are `parts` records apart.
+struct DecWs {
+  int* base;
+  long long rec_ints;
+  int parts, lcap;
+  __host__ __device__ static constexpr long long rec_ints_for(long long lcap) {
+    return (4 + NGRP + NBINS + 2 * lcap + 3) / 4 * 4;
+  }
+  __device__ __forceinline__ int* rec(long long row, int p) const { return base + (row * parts + p) * rec_ints; }
+  __device__ __forceinline__ int* hdr(long long row, int p) const { return rec(row, p); }
+  __device__ __forceinline__ int* gsum(long long row, int p) const { return rec(row, p) + 4; }
+  __device__ __forceinline__ int* hist(long long row, int p) const { return rec(row, p) + 4 + NGRP; }
+  __device__ __forceinline__ int* list(long long row, int p) const { return rec(row, p) + 4 + NGRP + NBINS; }
+};
+
+// Per-row selection state of the several-workgroups top-k in its workspace (rows
+// row_ints_for(n_seg) ints apart, a multiple of 4, so every row's histogram is
+// 16-byte aligned):
 //   hist[NBINS] | info[INFO] = {b*, above, cnt*, overflow, arrivals, -, -, -} |
-//   gsum[NGRP] (sums of GRP consecutive bins; kept where the indexer builds the
-//   histogram) | cnt[n_seg] | lcnt[n_lst] | lbw[n_lst] | cand
-// cand holds either n_seg segment candidate lists of CAP (slot, score) pairs or the
-// indexer's n_lst span lists of LIST_CAP pairs.  Rows are a multiple of 4 ints long,
-// so every row's histogram is 16-byte aligned.
+//   gsum[NGRP] (unused here) | cnt[n_seg] | cand[n_seg][CAP] (slot, score) pairs
 struct SegWs {
   int* base;
-  int n_seg, n_lst;
-  __host__ __device__ static constexpr long long row_ints_for(long long n_seg, long long n_lst) {
-    return (NBINS + INFO + NGRP + n_seg + 2 * n_lst +
-            (2 * n_seg * CAP > 2 * n_lst * LIST_CAP ? 2 * n_seg * CAP : 2 * n_lst * LIST_CAP) + 3) / 4 * 4;
+  int n_seg;
+  __host__ __device__ static constexpr long long row_ints_for(long long n_seg) {
+    return (NBINS + INFO + NGRP + n_seg + 2 * n_seg * CAP + 3) / 4 * 4;
   }
-  __host__ __device__ long long row_ints() const { return row_ints_for(n_seg, n_lst); }
+  __host__ __device__ long long row_ints() const { return row_ints_for(n_seg); }
   __device__ __forceinline__ int* hist(long long r) const { return base + r * row_ints(); }
   __device__ __forceinline__ int* info(long long r) const { return hist(r) + NBINS; }
   __device__ __forceinline__ int* gsum(long long r) const { return info(r) + INFO; }
   __device__ __forceinline__ int* cnt(long long r) const { return gsum(r) + NGRP; }
-  __device__ __forceinline__ int* lcnt(long long r) const { return cnt(r) + n_seg; }
-  __device__ __forceinline__ int* lbw(long long r) const { return lcnt(r) + n_lst; }
-  __device__ __forceinline__ int* cand(long long r, int seg) const { return lbw(r) + n_lst + 2ll * seg * CAP; }
-  __device__ __forceinline__ int* lcand(long long r, int w) const { return lbw(r) + n_lst + 2ll * w * LIST_CAP; }
+  __device__ __forceinline__ int* cand(long long r, int seg) const { return cnt(r) + n_seg + 2ll * seg * CAP; }
 };
 
 // Ordered compaction over positions [0, n): pred(pos, payload&) selects; emit(rank,

@@ -634,76 +634,42 @@ __global__ __launch_bounds__(NT) void topk_seg_finish_kernel(const int32_t* __re
   finish_from_list<NT, KEPT>(rv, Lc, lslot, lval, bstar, above, k, wcnt, h256, scan_tmp, sh, out);
 }
 
-// Re-scores keys [j0, j1) of one flat row into its score-table slice: the indexer's
-// integer sum sum_h w_h * max(0, q_h . k_j), here with v_dot4_i32_i8 (4 int8 products
-// per op) instead of the MFMA -- identical integers, so identical selections.  The
-// rare path of the list-based selection; all NT threads call (two barriers).
-template <int NT, int DI>
-__device__ __forceinline__ void rescore_keys(const int8_t* __restrict__ q_row, const int32_t* __restrict__ w_row,
-                                             const int8_t* __restrict__ kb, int H_I, int j0, int j1,
-                                             int32_t* __restrict__ srow, int* q_lds, int* w_lds) {
-  constexpr int C = DI / 4;  // 4-byte words per index vector
-  for (int t = threadIdx.x; t < H_I * C; t += NT) q_lds[t] = reinterpret_cast<const int*>(q_row)[t];
-  for (int t = threadIdx.x; t < H_I; t += NT) w_lds[t] = w_row[t];
-  __syncthreads();
-  for (int j = j0 + (int)threadIdx.x; j < j1; j += NT) {
-    int kv[C];
-    const int* kr = reinterpret_cast<const int*>(kb + (long long)j * DI);
-#pragma unroll
-    for (int c = 0; c < C; ++c) kv[c] = kr[c];
-    int s = 0;
-    for (int h = 0; h < H_I; ++h) {
-      int dot = 0;
-#pragma unroll
-      for (int c = 0; c < C; ++c) dot = __builtin_amdgcn_sdot4(q_lds[h * C + c], kv[c], dot, false);
-      s += w_lds[h] * max(dot, 0);  // modulo 2^32, like the indexer's 24-bit multiply-adds
-    }
-    srow[j] = s;
-  }
-  __syncthreads();
-}
-
-// Flat rows whose selection state the indexer built (histogram, one candidate list
-// per span of DIRECT_SPAN keys, no score table): one workgroup per row.  The cut b* comes from
-// the row's group sums and the bins of the cut group.  A span is then
-//   L: its list reaches down to b* (lbw <= b*): all its entries of bins >= b* are in
-//      the list;
-//   T: it wrote its table slice (lbw = -1: its own top bins overflowed a list);
-//   S: its list stops above b* (the top is concentrated there): it is re-scored into
-//      its table slice here and then read like T.
-// The entries of bins >= b* are gathered in slot order from the lists and slices.
-// If they overflow the LDS list (heavy ties at b*), every span that is not T is
-// re-scored and the row goes through the exact radix fallback over its table.
+// Flat rows whose selection state the decode indexer built (one record per span of
+// dec_span(n_valid, parts) keys: band, group sums, band bins, candidate list; no score
+// table): one workgroup per row.  The row's group sums are the sum of its spans'; the
+// cut group's bins likewise, and b* is the bin holding the k-th best entry.  Every
+// entry of bin >= b* is then in its span's list (lbw <= b*: no span holds k entries
+// above the cut) or, for a span whose list overflowed (lbw = -1), in its slice of the
+// score table; they are gathered in slot order from both.  If they overflow the LDS
+// list (heavy ties at b*), the row's table is completed instead -- a list span's
+// slice is set to INT_MIN, below every candidate, and its list entries are written
+// over it -- and the exact radix fallback runs over the table.
 template <int NT>
-__global__ __launch_bounds__(NT) void topk_list_finish_kernel(
-    int32_t* __restrict__ scores, long long ld, const int32_t* __restrict__ q_pos, int L_max, int k, SegWs ws,
-    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
-    int w_per_query, int n_q, int H_I, int d_I, int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+__global__ __launch_bounds__(NT) void topk_list_finish_kernel(int32_t* __restrict__ scores, long long ld,
+                                                              const int32_t* __restrict__ q_pos, int L_max, int k,
+                                                              DecWs ws, int32_t* __restrict__ idx,
+                                                              int32_t* __restrict__ count) {
   constexpr int NW = NT / 64;
   constexpr int V = 2;
-  static_assert(NT >= NGRP, "one group sum per thread");
-  enum { KIND_L = 0, KIND_T = 1, KIND_S = 2 };
+  static_assert(NT % NGRP == 0 && NT % GRP == 0, "whole groups of threads per group sum and per bin");
+  static_assert(NT >= DEC_MAX_PARTS, "one span per thread");
   __shared__ int lds_big[NBINS];
   __shared__ int wcnt[2 * 4 * NW];
   __shared__ int scan_tmp[NW + 1];
   __shared__ int h256[256];
   __shared__ int sh[8];
   __shared__ int loff[NT + 1];
-  __shared__ int skind[NT], slen[NT];  // per span: kind and entries to gather
-  __shared__ int q_lds[64 * 128 / 4];
-  __shared__ int w_lds[64];
+  __shared__ int slen[NT];   // per span: entries to gather
+  __shared__ int slist[NT];  // per span: 1 = list, 0 = table slice
+  __shared__ int sband[2][NT];
+  __shared__ int gs_l[NGRP];
+  __shared__ int bins_l[GRP];
   const long long row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   int32_t* out = idx + row * (long long)k;
 
-  // independent loads together: position, group sums, the span lists' counts and lower bins
-  const int p_raw = q_pos[row];
-  const int gs = tid < NGRP ? ws.gsum(row)[NGRP - 1 - tid] : 0;  // highest group first
-  const int lc = tid < ws.n_lst ? ws.lcnt(row)[tid] : 0;
-  const int lb = tid < ws.n_lst ? ws.lbw(row)[tid] : 0;
-
   RowView<false> rv;
-  rv.p = min(p_raw, L_max - 1);
+  rv.p = min(q_pos[row], L_max - 1);
   rv.srow = scores + row * ld;
   rv.vec = (((uintptr_t)rv.srow) & 15u) == 0;
   rv.bs = 0;
@@ -715,9 +681,31 @@ __global__ __launch_bounds__(NT) void topk_list_finish_kernel(
     select_all<NT, false>(rv, n_valid, k, wcnt, out);
     return;
   }
+  const int span = dec_span(n_valid, ws.parts);
+  const int n_sp = (n_valid + span - 1) / span;  // spans of this row (each left a record)
 
-  // cut: group holding the k-th best entry, then the bin inside it (one wave)
+  // the spans' headers, and the row's group sums: thread t adds group t % NGRP of
+  // spans t / NGRP, t / NGRP + NT / NGRP, ...
+  if (tid < n_sp) {
+    const int4 h = *reinterpret_cast<const int4*>(ws.hdr(row, tid));
+    sband[0][tid] = h.x;
+    sband[1][tid] = h.y;
+    slist[tid] = h.w >= 0;
+    slen[tid] = h.w >= 0 ? h.z : min(n_valid, (tid + 1) * span) - tid * span;
+  }
+  if (tid < NGRP) gs_l[tid] = 0;
+  if (tid < GRP) bins_l[tid] = 0;
   {
+    int acc = 0;
+    for (int sp = tid / NGRP; sp < n_sp; sp += NT / NGRP) acc += ws.gsum(row, sp)[tid % NGRP];
+    __syncthreads();
+    if (acc) atomicAdd(&gs_l[tid % NGRP], acc);
+  }
+  __syncthreads();
+
+  // cut: group holding the k-th best entry, then the bin inside it
+  {
+    const int gs = tid < NGRP ? gs_l[NGRP - 1 - tid] : 0;  // highest group first
     int tot;
     const int excl = block_exclusive_scan<NT>(gs, scan_tmp, &tot);
     if (excl < k && excl + gs >= k) {
@@ -725,9 +713,16 @@ __global__ __launch_bounds__(NT) void topk_list_finish_kernel(
       sh[1] = excl;
     }
     __syncthreads();
+    const int g = sh[0];
+    // bin g*GRP + tid % GRP of spans tid / GRP, tid / GRP + NT / GRP, ... (inside their bands)
+    const int bin = g * GRP + tid % GRP;
+    int acc = 0;
+    for (int sp = tid / GRP; sp < n_sp; sp += NT / GRP)
+      if (bin >= sband[0][sp] && bin <= sband[1][sp]) acc += ws.hist(row, sp)[bin];
+    if (acc) atomicAdd(&bins_l[tid % GRP], acc);
+    __syncthreads();
     if (tid < 64) {
-      const int g = sh[0];
-      const int hb = lane < GRP ? ws.hist(row)[g * GRP + GRP - 1 - lane] : 0;  // highest bin first
+      const int hb = lane < GRP ? bins_l[GRP - 1 - lane] : 0;  // highest bin first
       int incl = hb;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -745,27 +740,24 @@ __global__ __launch_bounds__(NT) void topk_list_finish_kernel(
     __syncthreads();
   }
   const int bstar = sh[4], above = sh[5], cnt_star = sh[6];
-  const int n_sp = (n_valid + DIRECT_SPAN - 1) / DIRECT_SPAN;  // spans of this row (each wrote a list)
-  const bool overflow = above + cnt_star > CAP;
-  // span kinds (with overflow every span that is not T is re-scored)
-  const bool resc = tid < n_sp && lb >= 0 && (overflow || lb > bstar);
-  if (tid < n_sp) {
-    const int len = min(n_valid, (tid + 1) * DIRECT_SPAN) - tid * DIRECT_SPAN;
-    skind[tid] = lb < 0 ? KIND_T : (resc ? KIND_S : KIND_L);
-    slen[tid] = (lb < 0 || resc) ? len : lc;
-  }
-  if (__syncthreads_count(resc) > 0) {
-    const int8_t* q_row = q_idx + row * (long long)H_I * d_I;
-    const int32_t* w_row = w + (w_per_query ? row * H_I : 0);
-    const int8_t* kb = k_idx + (row / n_q) * (long long)L_max * d_I;
+
+  if (above + cnt_star > CAP) {
+    int32_t* srow = scores + row * ld;
     for (int sp = 0; sp < n_sp; ++sp) {
-      if (skind[sp] != KIND_S) continue;  // uniform: LDS after a barrier
-      const int j0 = sp * DIRECT_SPAN, j1 = min(n_valid, j0 + DIRECT_SPAN);
-      if (d_I == 128) rescore_keys<NT, 128>(q_row, w_row, kb, H_I, j0, j1, scores + row * ld, q_lds, w_lds);
-      else rescore_keys<NT, 64>(q_row, w_row, kb, H_I, j0, j1, scores + row * ld, q_lds, w_lds);
+      if (!slist[sp]) continue;  // uniform: LDS after a barrier
+      const int j1 = min(n_valid, (sp + 1) * span);
+      for (int j = sp * span + tid; j < j1; j += NT) srow[j] = INT_MIN;
     }
-  }
-  if (overflow) {
+    __syncthreads();
+    for (int sp = 0; sp < n_sp; ++sp) {
+      if (!slist[sp]) continue;
+      const int2* L = reinterpret_cast<const int2*>(ws.list(row, sp));
+      for (int e = tid; e < slen[sp]; e += NT) {
+        const int2 x = L[e];
+        srow[x.x] = x.y;
+      }
+    }
+    __syncthreads();
     fallback_select<NT, false>(rv, k, lds_big, wcnt, h256, scan_tmp, sh, out);
     return;
   }
@@ -800,13 +792,13 @@ __global__ __launch_bounds__(NT) void topk_list_finish_kernel(
           else hi = mid;
         }
         const int j = ec - loff[lo];
-        if (skind[lo] == KIND_L) {
-          const int* L = ws.lcand(row, lo) + 2 * j;
-          pl[v][c].slot = L[0];
-          pl[v][c].score = L[1];
+        if (slist[lo]) {
+          const int2 x = reinterpret_cast<const int2*>(ws.list(row, lo))[j];
+          pl[v][c].slot = x.x;
+          pl[v][c].score = x.y;
         } else {
-          pl[v][c].slot = lo * DIRECT_SPAN + j;
-          pl[v][c].score = rv.srow[lo * DIRECT_SPAN + j];
+          pl[v][c].slot = lo * span + j;
+          pl[v][c].score = rv.srow[lo * span + j];
         }
         m[v] |= (e < n_all && coarse_bin(pl[v][c].score) >= bstar ? 1u : 0u) << c;
       }
@@ -945,9 +937,8 @@ __global__ __launch_bounds__(NT) void blk_select_kernel(const long long* __restr
 size_t topk_ws_bytes(long long rows, int L_max) {
   if (rows == 0 || rows > 512 || L_max < 4 * SEG) return 0;
   const long long n_seg = (L_max + SEG - 1) / SEG;
-  const long long n_lst = (L_max + DIRECT_SPAN - 1) / DIRECT_SPAN;
   if (n_seg > 1024) return 0;
-  return (size_t)rows * (size_t)SegWs::row_ints_for(n_seg, n_lst) * sizeof(int);
+  return (size_t)rows * (size_t)SegWs::row_ints_for(n_seg) * sizeof(int);
 }
 
 static bool split_rows(const TopkArgs& a, SegWs* w) {
@@ -956,21 +947,65 @@ static bool split_rows(const TopkArgs& a, SegWs* w) {
   if (a.kept != nullptr || need == 0 || a.ws == nullptr || a.ws_bytes < need) return false;
   w->base = static_cast<int*>(a.ws);
   w->n_seg = (a.L_max + SEG - 1) / SEG;
-  w->n_lst = (a.L_max + DIRECT_SPAN - 1) / DIRECT_SPAN;
+  return true;
+}
+
+// spans per row of the decode selection: about DEC_WGS workgroups in all, spans of at
+// least DEC_SPAN_MIN keys, and as many as a span of at most DEC_SPAN_MAX keys needs
+static long long dec_parts(long long rows, int L_max) {
+  const long long by_lds = (L_max + (DEC_SPAN_MAX - 64)) / (DEC_SPAN_MAX - 63);
+  const long long by_fill = (DEC_WGS + rows - 1) / rows;
+  const long long by_size = std::max<long long>(1, L_max / DEC_SPAN_MIN);
+  return std::max(by_lds, std::min(by_fill, by_size));
+}
+
+bool dec_sel_layout(long long rows, int L_max, int k, DecLayout* out) {
+  if (rows < 1 || rows > 65535 || L_max < 1 || k < 1) return false;
+  const long long parts = dec_parts(rows, L_max);
+  if (parts > DEC_MAX_PARTS) return false;
+  // a list holds at least min(span, k) entries, plus the rest of the bin that completes it
+  out->parts = (int)parts;
+  out->lcap = (int)std::min<long long>(2ll * k, DEC_SPAN_MAX);
+  out->rec_ints = DecWs::rec_ints_for(out->lcap);
+  return true;
+}
+
+size_t dec_sel_ws_bytes(long long rows, int L_max, int k) {
+  DecLayout d;
+  if (!dec_sel_layout(rows, L_max, k, &d)) return 0;
+  // records of a chunk of r <= rows rows: r * parts(r) <= r * max(by_lds, min(by_fill(r),
+  // by_size)), and r * by_fill(r) <= r + DEC_WGS - 1
+  const long long by_lds = (L_max + (DEC_SPAN_MAX - 64)) / (DEC_SPAN_MAX - 63);
+  const long long by_size = std::max<long long>(1, L_max / DEC_SPAN_MIN);
+  const long long recs = std::max(rows * by_lds, std::min(rows + DEC_WGS - 1, rows * by_size));
+  return (size_t)recs * (size_t)d.rec_ints * sizeof(int);
+}
+
+static bool dec_rows(const TopkArgs& a, DecWs* w) {
+  const long long rows = (long long)a.B * a.n_q;
+  DecLayout d;
+  if (a.kept != nullptr || a.ws == nullptr || !dec_sel_layout(rows, a.L_max, a.k, &d) ||
+      a.ws_bytes < (size_t)rows * d.parts * (size_t)d.rec_ints * sizeof(int))
+    return false;
+  w->base = static_cast<int*>(a.ws);
+  w->rec_ints = d.rec_ints;
+  w->parts = d.parts;
+  w->lcap = d.lcap;
   return true;
 }
 
 template <bool KEPT>
-static void launch_topk_t(const TopkArgs& a, hipStream_t st, long long rows) {
+static hipError_t launch_topk_t(const TopkArgs& a, hipStream_t st, long long rows) {
+  if (!KEPT && a.hist_ready) {
+    // the decode indexer left each span's histogram and list: one kernel
+    DecWs d;
+    if (!dec_rows(a, &d)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((topk_list_finish_kernel<1024>), dim3((unsigned)rows), dim3(1024), 0, st,
+                       const_cast<int32_t*>(a.scores), a.ld, a.q_pos, a.L_max, a.k, d, a.idx, a.count);
+    return hipGetLastError();
+  }
   SegWs w;
   if (!KEPT && split_rows(a, &w)) {
-    if (a.hist_ready) {
-      // the indexer built the histograms and the span lists: one kernel
-      hipLaunchKernelGGL((topk_list_finish_kernel<1024>), dim3((unsigned)rows), dim3(1024), 0, st,
-                         const_cast<int32_t*>(a.scores), a.ld, a.q_pos, a.L_max, a.k, w, a.q_idx, a.k_idx, a.w,
-                         a.w_per_query, a.n_q, a.H_I, a.d_I, a.idx, a.count);
-      return;
-    }
     // several workgroups per row: histogram and candidate compaction split over segments
     const dim3 grid((unsigned)w.n_seg, (unsigned)rows);
     hipLaunchKernelGGL(topk_seg_zero_kernel, dim3(8, (unsigned)rows), dim3(256), 0, st, w.base, w.row_ints(), rows);
@@ -980,7 +1015,7 @@ static void launch_topk_t(const TopkArgs& a, hipStream_t st, long long rows) {
                        a.k, w);
     hipLaunchKernelGGL((topk_seg_finish_kernel<256, KEPT>), dim3((unsigned)rows), dim3(256), 0, st, a.scores,
                        a.ld, a.q_pos, a.kept, a.block_size, a.n_keep, a.L_max, a.k, w, a.idx, a.count);
-    return;
+    return hipGetLastError();
   }
   if (rows <= 1024 && a.L_max >= 16384) {
     hipLaunchKernelGGL((topk_kernel<1024, KEPT>), dim3((unsigned)rows), dim3(1024), 0, st, a.scores, a.ld, a.q_pos,
@@ -989,31 +1024,13 @@ static void launch_topk_t(const TopkArgs& a, hipStream_t st, long long rows) {
     hipLaunchKernelGGL((topk_kernel<256, KEPT>), dim3((unsigned)rows), dim3(256), 0, st, a.scores, a.ld, a.q_pos,
                        a.kept, a.block_size, a.n_keep, a.L_max, a.k, a.idx, a.count);
   }
-}
-
-bool topk_split_rows(const TopkArgs& a, int** base, int* n_seg, int* n_lst) {
-  SegWs w;
-  if (!split_rows(a, &w)) return false;
-  *base = w.base;
-  *n_seg = w.n_seg;
-  *n_lst = w.n_lst;
-  return true;
-}
-
-hipError_t launch_topk_reset(const TopkArgs& a, hipStream_t st) {
-  SegWs w;
-  const long long rows = (long long)a.B * a.n_q;
-  if (rows == 0 || !split_rows(a, &w)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(topk_seg_zero_kernel, dim3(8, (unsigned)rows), dim3(256), 0, st, w.base, w.row_ints(), rows);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   const long long rows = (long long)a.B * a.n_q;
   if (rows == 0) return hipSuccess;
-  if (a.kept != nullptr) launch_topk_t<true>(a, st, rows);
-  else launch_topk_t<false>(a, st, rows);
-  return hipGetLastError();
+  return a.kept != nullptr ? launch_topk_t<true>(a, st, rows) : launch_topk_t<false>(a, st, rows);
 }
 
 hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st) {

@@ -391,22 +391,22 @@ def test_forward_decode_small(lsa):
 
 @pytest.mark.parametrize("H_I", [64, 20])
 def test_forward_decode_fused_selection(lsa, H_I):
-    """Decode rows long enough for the split top-k: lsa_forward lets the indexer build
-    the rows' histograms (stages topk_reset, index_scores, topk, sparse_attn).  Its
-    lists equal the separate calls' (histogram pass inside lsa_topk) bit for bit, and
-    the oracle's on sampled rows; rows of at most k candidates mix in."""
+    """Decode rows: lsa_forward lets the indexer leave each span's histogram and
+    candidate list (stages index_select, topk, sparse_attn).  Its lists equal the
+    separate calls' (score table, then lsa_topk) bit for bit, and the oracle's on
+    sampled rows; rows of at most k candidates mix in."""
     L, k = 40000, 1024
     pos = [39999, 30000, 1023, 500, 33333, 39998]
     wl = synthetic.Workload("decfused", B=len(pos), n_q=1, L=L, q_pos0=0, H_I=H_I, d_I=128, k=k, H_q=16)
     inp, g = _inputs(wl, seed=11, pos=pos)
     ws_bytes = lsa.lsa_forward_workspace_size(g, k)
-    assert lsa.lsa_forward_stages(g, k, ws_bytes) == ["topk_reset", "index_scores", "topk", "sparse_attn"]
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    assert lsa.lsa_forward_stages(g, k, ws_bytes) == ["index_select", "topk", "sparse_attn"]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     for e in evs:
         e.record()
     res = lsa.lsa_forward(g, k_top=k, stage_events=evs)
     torch.cuda.synchronize()
-    assert all(evs[i].elapsed_time(evs[i + 1]) >= 0 for i in range(4))
+    assert all(evs[i].elapsed_time(evs[i + 1]) >= 0 for i in range(3))
     ld = ((L + 63) // 64) * 64
     sc = lsa.lsa_index_scores(g["q_idx"], g["k_idx"], g["w"], g["q_pos"], ld=ld)
     for use_ws in (True, False):
@@ -422,14 +422,18 @@ def test_forward_decode_fused_selection(lsa, H_I):
     err.check()
 
 
-@pytest.mark.parametrize("kind", ["one_span_distinct", "one_span_equal", "two_spans_ties", "all_equal",
+@pytest.mark.parametrize("kind", ["one_span_distinct", "whole_span_equal", "two_spans_ties", "all_equal",
                                   "spread_ties"])
 def test_forward_decode_fused_selection_concentrated(lsa, kind):
-    """Decode rows whose top-k the indexer's span lists cannot hold: concentrated in
-    one or two indexer spans (a list keeps ~128 entries: re-scored spans), heavy ties
-    inside a span (the span writes its table slice), all scores equal or ties spread
-    over every span (the cut bin overflows: every span re-scored, exact radix
-    fallback) -- still bit for bit the separate calls' lists and the oracle's."""
+    """Decode rows with awkward score distributions for the indexer's span lists
+    (19 spans of <= 2112 keys per row here, lists of >= min(span, k) entries and at
+    most 2k): the top-k concentrated in about one span; a run of 3616 identical keys
+    that covers whole spans (such a span's list would overflow: it writes its table
+    slice, the row stays on the list path); ties in two spans; all scores equal (the
+    cut bin overflows the LDS list: the row's table is completed from lists and
+    slices, exact radix fallback, table slices and whole-span lists mixed); ~5000
+    ties spread over every span (the same fallback from lists only) -- still bit for
+    bit the separate calls' lists and the oracle's."""
     L, k = 40000, 1024
     pos = [39999, 39000, 35000, 20000]
     wl = synthetic.Workload("deccon", B=len(pos), n_q=1, L=L, q_pos0=0, H_I=64, d_I=128, k=k, H_q=16)
@@ -438,11 +442,11 @@ def test_forward_decode_fused_selection_concentrated(lsa, kind):
     gen = torch.Generator().manual_seed(3)
     for b in range(wl.B):
         if kind == "one_span_distinct":
-            lo, hi = 16384, 18432                     # exactly span 8
+            lo, hi = 16384, 18432                     # 2048 keys: about one span
             noise = torch.randint(-3, 4, (hi - lo, 128), generator=gen, dtype=torch.int64)
             inp["k_idx"][b, lo:hi] = (q0[b].to(torch.int64) + noise).clamp(-128, 127).to(torch.int8)
-        elif kind == "one_span_equal":
-            lo, hi = 18432, 20000                     # part of span 9: 1568 identical keys (ties)
+        elif kind == "whole_span_equal":
+            lo, hi = 16384, 20000                     # 3616 identical keys (ties), whole spans
             inp["k_idx"][b, lo:hi] = q0[b]
         elif kind == "two_spans_ties":
             for lo, hi in ((2048, 2600), (10240, 10900)):   # two spans, ties inside each
@@ -452,7 +456,7 @@ def test_forward_decode_fused_selection_concentrated(lsa, kind):
         else:
             inp["k_idx"][b, 0:L:8] = q0[b]            # ~5000 ties spread over every span
     g = {kk: v.to(dev()) for kk, v in inp.items()}
-    assert lsa.lsa_forward_stages(g, k, lsa.lsa_forward_workspace_size(g, k))[0] == "topk_reset"
+    assert lsa.lsa_forward_stages(g, k, lsa.lsa_forward_workspace_size(g, k))[0] == "index_select"
     res = lsa.lsa_forward(g, k_top=k)
     ld = ((L + 63) // 64) * 64
     sc = lsa.lsa_index_scores(g["q_idx"], g["k_idx"], g["w"], g["q_pos"], ld=ld)

@@ -66,14 +66,20 @@ def _fake_inputs(B, n_q, L, H_I=64, d_I=128, H_q=16, d=128):
 def test_forward_stages_listing():
     """lsa_forward_stages: the stage sequence of each mode (host planning only)."""
     import learned_top_sparse_amd as lsa
-    # decode-shaped, long rows: the indexer builds the histograms, so a reset stage comes first
+    # decode-shaped, long rows: the indexer leaves the selection state (no score table)
     inp = _fake_inputs(64, 1, 131073)
     ws = lsa.lsa_forward_workspace_size(inp, 2048)
-    assert lsa.lsa_forward_stages(inp, 2048, ws) == ["topk_reset", "index_scores", "topk", "sparse_attn"]
-    # decode-shaped but short rows (below four selection segments): no split top-k, no reset
+    assert lsa.lsa_forward_stages(inp, 2048, ws) == ["index_select", "topk", "sparse_attn"]
+    # short decode rows take the decode selection as well
     inp = _fake_inputs(8, 1, 20000)
     ws = lsa.lsa_forward_workspace_size(inp, 2048)
-    assert lsa.lsa_forward_stages(inp, 2048, ws) == ["index_scores", "topk", "sparse_attn"]
+    assert lsa.lsa_forward_stages(inp, 2048, ws) == ["index_select", "topk", "sparse_attn"]
+    # ten queries in chunks of eight: the score table for the first chunk, the decode
+    # selection for the last two queries (their state fits the chunk's top-k workspace)
+    inp = _fake_inputs(1, 10, 40000)
+    ws = lsa.lsa_forward_workspace_size(inp, 2048, chunk_rows=8)
+    assert lsa.lsa_forward_stages(inp, 2048, ws, chunk_rows=8) == [
+        "index_scores", "topk", "sparse_attn", "index_select", "topk", "sparse_attn"]
     # prefill in three chunks
     inp = _fake_inputs(1, 3000, 4096)
     ws = lsa.lsa_forward_workspace_size(inp, 512, chunk_rows=1000)
@@ -94,7 +100,7 @@ def test_forward_rejects_too_few_stage_events():
     a = _forward_args(inp, 2048, False, 128, 64, None, 0, 0, out)
     n = ctypes.c_int32(0)
     ws = lsa.lsa_forward_workspace_size(inp, 2048)
-    assert lsa.lib().lsa_forward_stages(ctypes.byref(a), ws, None, 0, ctypes.byref(n)) == 0 and n.value == 4
+    assert lsa.lib().lsa_forward_stages(ctypes.byref(a), ws, None, 0, ctypes.byref(n)) == 0 and n.value == 3
     handles = (ctypes.c_void_p * n.value)()   # one short of 1 + n
     a.stage_events = ctypes.cast(handles, ctypes.c_void_p)
     a.n_stage_events = n.value
