@@ -581,8 +581,8 @@ __global__ __launch_bounds__(512, 1) void idx_decode_kernel(
     // is odd, so the lanes' first quads are an odd number of quads apart and any 16
     // lanes' quads fall in distinct bank groups (an even count, e.g. C = 64, puts
     // every lane of a read on the same banks).  A block scan of the counts gives each
-    // thread its first rank, and the thread writes its entries in slot order, one
-    // 8-byte (slot, score) store each.
+    // thread its first rank, and the thread writes its entries' slots and scores in
+    // slot order.
     constexpr int CQ = DEC_SPAN_MAX / NT / 4;  // quads per thread at most
     static_assert(DEC_SPAN_MAX % (4 * NT) == 0 && CQ % 2 == 1, "whole quads per thread, an odd number at most");
     constexpr int NWD = (4 * CQ + 31) / 32;
@@ -610,14 +610,17 @@ __global__ __launch_bounds__(512, 1) void idx_decode_kernel(
 #pragma unroll
     for (int wd = 0; wd < NWD; ++wd) cnt += __popc(msk[wd]);
     int r = block_exclusive_scan<NT>(cnt, scan_l, &n_list);
-    int2* lc = reinterpret_cast<int2*>(sel.list(row, part));
+    int* lsl = sel.lslot(row, part);
+    int* lsc = sel.lscore(row, part);
 #pragma unroll
     for (int wd = 0; wd < NWD; ++wd) {
       unsigned m = msk[wd];
       while (m) {
         const int j = 32 * wd + __ffs(m) - 1;
         m &= m - 1;
-        lc[r++] = make_int2(s_begin + c0 + j, sbuf[c0 + j]);
+        lsl[r] = s_begin + c0 + j;
+        lsc[r] = sbuf[c0 + j];
+        ++r;
       }
     }
   }

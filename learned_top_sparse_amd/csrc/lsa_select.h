@@ -90,7 +90,9 @@ __host__ __device__ __forceinline__ int dec_span(int n_valid, int parts) {
 //     its slice of the score table);
 //   gsum[NGRP]: its counts per group of GRP bins;
 //   hist[NBINS]: its counts per bin, bins lo..hi only;
-//   list[2 * lcap]: (slot, score) pairs in slot order (16-byte aligned).
+//   lslot[lcap], lscore[lcap]: the list's slots and scores, in slot order (lcap is a
+//     multiple of 4, so both arrays are 16-byte aligned and a reader may take them a
+//     quad at a time up to the count rounded up to 4).
 // Records of one row are consecutive; rows are `parts` records apart.
 struct DecWs {
   int* base;
@@ -103,7 +105,8 @@ struct DecWs {
   __device__ __forceinline__ int* hdr(long long row, int p) const { return rec(row, p); }
   __device__ __forceinline__ int* gsum(long long row, int p) const { return rec(row, p) + 4; }
   __device__ __forceinline__ int* hist(long long row, int p) const { return rec(row, p) + 4 + NGRP; }
-  __device__ __forceinline__ int* list(long long row, int p) const { return rec(row, p) + 4 + NGRP + NBINS; }
+  __device__ __forceinline__ int* lslot(long long row, int p) const { return rec(row, p) + 4 + NGRP + NBINS; }
+  __device__ __forceinline__ int* lscore(long long row, int p) const { return lslot(row, p) + lcap; }
 };
 
 // Per-row selection state of the several-workgroups top-k in its workspace (rows

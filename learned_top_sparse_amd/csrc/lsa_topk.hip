@@ -213,11 +213,164 @@ __device__ __forceinline__ void row_histogram(const RowView<KEPT> rv, int lo, in
 
 // Steps 4-5 once the entries of bins >= b* sit in slot order in the LDS list
 // (lslot, lval; Lc entries): exact threshold inside b*, then the output row.
+// Bits shared by the (score, -slot) keys of every entry of coarse bin b: a bin is a
+// power-of-two aligned score range, so its scores agree above the range's width
+// (in the order-preserving unsigned form).  Returns the mask of those key bits and
+// sets *pref to their value.
+__device__ __forceinline__ unsigned long long bin_key_prefix(int b, unsigned long long* pref) {
+  const unsigned lo = okey(bin_floor(b));
+  const unsigned hi = b >= 7295 ? 0xFFFFFFFFu : okey(bin_floor(b + 1)) - 1u;
+  const unsigned d = lo ^ hi;
+  const unsigned long long m = d == 0u ? 0xFFFFFFFF00000000ull : ~((2ull << (63 - __clzll((long long)d << 32))) - 1ull);
+  *pref = ((unsigned long long)lo << 32) & m;
+  return m;
+}
+
+// The need-th largest of n <= 64*KPW 64-bit keys (1 <= need <= n), exactly, by one
+// wave holding KPW keys per lane in registers: a radix select over the bits where
+// the keys differ, 8 at a time from the highest, with its own 256-bucket histogram
+// in LDS (a wave's LDS operations take effect in order, so no barrier is needed),
+// stopping early once every key left in the chosen bucket is taken (the cutoff is
+// then the smallest of them).  key(i) gives key i (and may be called, its value
+// unused, for any i < 64*KPW); every key agrees with pref0 on the bits of pmask0 (0,
+// 0: nothing known), which the passes skip.
+template <int KPW, typename Key>
+__device__ __forceinline__ unsigned long long wave_select_kth(int n, int need, Key key, int* h256,
+                                                              unsigned long long pref0 = 0ull,
+                                                              unsigned long long pmask0 = 0ull) {
+  const int lane = threadIdx.x & 63;
+  auto wave_min = [&](unsigned long long v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long w = (unsigned long long)__shfl_xor((long long)v, o);
+      v = w < v ? w : v;
+    }
+    return v;
+  };
+  unsigned long long kv[KPW];  // read unconditionally (key(i) must be readable for i < 64*KPW)
+#pragma unroll
+  for (int j = 0; j < KPW; ++j) kv[j] = key(lane + 64 * j);
+  // the radix starts at the byte holding the highest bit not fixed by pmask0
+  const int hb = pmask0 == ~0ull ? -1 : 63 - __clzll((long long)~pmask0);
+  if (hb < 0) return pref0;
+  int shift = (hb / 8) * 8;
+  unsigned long long pmask = shift + 8 >= 64 ? 0ull : ~((1ull << (shift + 8)) - 1ull);
+  unsigned long long pref = pref0 & pmask;  // pmask0 is a prefix mask, so pmask is inside it
+  for (; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) h256[lane + 64 * j] = 0;
+#pragma unroll
+    for (int j = 0; j < KPW; ++j)
+      if (lane + 64 * j < n && (kv[j] & pmask) == pref) atomicAdd(&h256[(int)((kv[j] >> shift) & 255ull)], 1);
+    // lane l holds buckets 255-4l .. 252-4l (highest first); inclusive scan over lanes
+    int c[4], lsum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = h256[255 - 4 * lane - j];
+      lsum += c[j];
+    }
+    int incl = lsum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    const int excl = incl - lsum;
+    const unsigned long long hit = __ballot(excl < need && incl >= need);
+    const int src = (int)__ffsll((long long)hit) - 1;
+    int d = 0, before = 0, in_bucket = 0;
+    if (lane == src) {
+      int acc = excl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (acc + c[j] >= need) {
+          d = 255 - 4 * lane - j;
+          before = acc;
+          in_bucket = c[j];
+          break;
+        }
+        acc += c[j];
+      }
+    }
+    d = __shfl(d, src);
+    before = __shfl(before, src);
+    in_bucket = __shfl(in_bucket, src);
+    need -= before;
+    pref |= (unsigned long long)d << shift;
+    pmask |= 255ull << shift;
+    if (in_bucket == need) {  // every key left is taken
+      unsigned long long mn = ~0ull;
+#pragma unroll
+      for (int j = 0; j < KPW; ++j)
+        if (lane + 64 * j < n && (kv[j] & pmask) == pref && kv[j] < mn) mn = kv[j];
+      return wave_min(mn);
+    }
+  }
+  return pref;
+}
+
 template <int NT, bool KEPT>
 __device__ __forceinline__ void finish_from_list(const RowView<KEPT> rv, int Lc, int* lslot, int* lval, int bstar,
                                                  int above, int k, int* wcnt, int* h256, int* scan_tmp, int* sh,
                                                  int32_t* out) {
-  // bits shared by every entry of b*: the radix starts at the byte of the highest differing bit
+  // The entries of b* decide which of them are taken: need = k - above of them, by
+  // (score desc, slot asc).  Collect them (any order; one LDS atomic per wave), then
+  // one wave selects the need-th largest (score, -slot) key among them only: that is
+  // the cutoff (T, slot_T), and the taken entries are those with score > T, or
+  // score == T and slot <= slot_T.
+  constexpr int TMAX = 1024;
+  __shared__ int tb_score[TMAX], tb_slot[TMAX], tb_n;
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) tb_n = 0;
+  __syncthreads();
+  for (int e0 = 0; e0 < Lc; e0 += NT) {
+    const int e = e0 + (int)threadIdx.x;
+    const int sc = e < Lc ? lval[e] : 0;
+    const bool in = e < Lc && coarse_bin(sc) == bstar;
+    const unsigned long long bal = __ballot(in);
+    int wbase = 0;
+    if (lane == 0 && bal != 0ull) wbase = atomicAdd(&tb_n, __popcll(bal));
+    wbase = __shfl(wbase, 0);
+    if (in) {
+      const int i = wbase + lanes_below(bal);
+      if (i < TMAX) {
+        tb_score[i] = sc;
+        tb_slot[i] = lslot[e];
+      }
+    }
+  }
+  __syncthreads();
+  const int n_star = tb_n;
+  if (n_star <= TMAX) {
+    if (threadIdx.x < 64) {
+      unsigned long long kpref;
+      const unsigned long long kmask = bin_key_prefix(bstar, &kpref);
+      const auto key = [&](int i) {
+        return ((unsigned long long)okey(tb_score[i]) << 32) | (0xFFFFFFFFu - (unsigned)tb_slot[i]);
+      };
+      const unsigned long long cut =
+          n_star <= 256 ? wave_select_kth<4>(n_star, k - above, key, h256, kpref, kmask)
+                        : wave_select_kth<TMAX / 64>(n_star, k - above, key, h256, kpref, kmask);
+      if (threadIdx.x == 0) {
+        sh[0] = (int)((unsigned)(cut >> 32) ^ 0x80000000u);
+        sh[1] = (int)(0xFFFFFFFFu - (unsigned)cut);
+      }
+    }
+    __syncthreads();
+    const int T = sh[0], slot_T = sh[1];
+    ordered_compact<NT, 4>(
+        Lc, wcnt,
+        [&](int e, int&) {
+          const int sc = lval[e];
+          return sc > T || (sc == T && lslot[e] <= slot_T);
+        },
+        [&](int r, int e, int) {
+          if (r < k) out[r] = rv.key_of(lslot[e]);
+        });
+    return;
+  }
+  // Many ties: an exact radix selection over the entries of b*.  Bits shared by every
+  // entry of b*: the radix starts at the byte of the highest differing bit.
   unsigned mx = 0u, mn = 0xFFFFFFFFu;
   for (int e = threadIdx.x; e < Lc; e += NT) {
     const int sc = lval[e];
@@ -650,7 +803,7 @@ __global__ __launch_bounds__(NT) void topk_list_finish_kernel(int32_t* __restric
                                                               DecWs ws, int32_t* __restrict__ idx,
                                                               int32_t* __restrict__ count) {
   constexpr int NW = NT / 64;
-  constexpr int V = 2;
+  constexpr int V = 3;
   static_assert(NT % NGRP == 0 && NT % GRP == 0, "whole groups of threads per group sum and per bin");
   static_assert(NT >= DEC_MAX_PARTS, "one span per thread");
   __shared__ int lds_big[NBINS];
@@ -662,6 +815,11 @@ __global__ __launch_bounds__(NT) void topk_list_finish_kernel(int32_t* __restric
   __shared__ int slen[NT];   // per span: entries to gather
   __shared__ int slist[NT];  // per span: 1 = list, 0 = table slice
   __shared__ int sband[2][NT];
+  __shared__ const int* ssc[NT];  // per span: its scores (list or table slice)
+  __shared__ const int* ssl[NT];  // per span: its list's slots
+  __shared__ int sslot0[NT];      // per span: -1 (list) or its first slot (table slice)
+  constexpr int TMAX = 1024;      // entries of b* ranked directly
+  __shared__ int tb_score[TMAX], tb_slot[TMAX], tb_n;
   __shared__ int gs_l[NGRP];
   __shared__ int bins_l[GRP];
   const long long row = blockIdx.x;
@@ -751,31 +909,166 @@ __global__ __launch_bounds__(NT) void topk_list_finish_kernel(int32_t* __restric
     __syncthreads();
     for (int sp = 0; sp < n_sp; ++sp) {
       if (!slist[sp]) continue;
-      const int2* L = reinterpret_cast<const int2*>(ws.list(row, sp));
-      for (int e = tid; e < slen[sp]; e += NT) {
-        const int2 x = L[e];
-        srow[x.x] = x.y;
-      }
+      const int* Ls = ws.lslot(row, sp);
+      const int* Lv = ws.lscore(row, sp);
+      for (int e = tid; e < slen[sp]; e += NT) srow[Ls[e]] = Lv[e];
     }
     __syncthreads();
     fallback_select<NT, false>(rv, k, lds_big, wcnt, h256, scan_tmp, sh, out);
     return;
   }
 
-  // offsets of the spans' sources, then an ordered compaction over their concatenation
+  // Offsets of the spans' sources in their concatenation, each count rounded up to a
+  // multiple of 4 (so a thread's quad of consecutive entries lies in one span), and
+  // where the entries come from: a list's slot and score arrays, or a table slice of
+  // scores (slot = first slot + position).  Then an ordered compaction over the
+  // concatenation, a quad per thread and step: two 16-byte loads, all issued before
+  // any is used.  The padding entries, and the reads they make, stay inside the list
+  // (lcap is a multiple of 4) or the table row (a slice starts at a multiple of 64
+  // and the row is a multiple of 64 long).
   int* lslot = lds_big;
   int* lval = lds_big + CAP;
   int n_all;
   {
-    const int ex = block_exclusive_scan<NT>(tid < n_sp ? slen[tid] : 0, scan_tmp, &n_all);
-    if (tid < n_sp) loff[tid] = ex;
+    const int ex = block_exclusive_scan<NT>(tid < n_sp ? (slen[tid] + 3) & ~3 : 0, scan_tmp, &n_all);
+    if (tid < n_sp) {
+      loff[tid] = ex;
+      ssc[tid] = slist[tid] ? ws.lscore(row, tid) : rv.srow + tid * span;
+      ssl[tid] = slist[tid] ? ws.lslot(row, tid) : rv.srow + tid * span;  // slices: read, not used
+      sslot0[tid] = slist[tid] ? -1 : tid * span;
+    }
+    if (tid == 0) tb_n = 0;
     __syncthreads();
   }
   struct SP {
     int slot, score;
   };
+  // Each step gives a thread one quad of consecutive entries (4*V*NT entries a step):
+  // the span found by a binary search over the offsets, then two 16-byte loads
+  // (scores, and a list's slots), all issued before any is used.
+  constexpr int STEP = 4 * V * NT;
+  struct Quad {
+    v4i sc, sl;
+    int e0, j0, lim, s0;
+  };
+  auto load_step = [&](int base, Quad (&q)[V]) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      q[v].e0 = base + 4 * (v * NT + tid);
+      const int ec = min(q[v].e0, n_all - 4);  // clamped: the loads stay unconditional
+      int lo = 0, hi = n_sp;                    // last span with loff[lo] <= ec
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (loff[mid] <= ec) lo = mid;
+        else hi = mid;
+      }
+      q[v].j0 = ec - loff[lo];
+      q[v].lim = slen[lo];
+      q[v].s0 = sslot0[lo];
+      q[v].sc = *reinterpret_cast<const v4i*>(ssc[lo] + q[v].j0);
+      q[v].sl = *reinterpret_cast<const v4i*>(ssl[lo] + q[v].j0);
+    }
+  };
+  auto valid = [&](const Quad& q, int c) { return q.e0 < n_all && q.j0 + c < q.lim; };
+  auto slot_of = [&](const Quad& q, int c) { return q.s0 < 0 ? q.sl[c] : q.s0 + q.j0 + c; };
+
+  // Pass 1: collect the entries of b* (any order; one LDS atomic per wave and quad
+  // slot).  The first step's quads stay in registers for pass 2.
+  Quad q0[V];
+  load_step(0, q0);
+  auto collect = [&](const Quad (&q)[V]) {
+    unsigned in = 0;  // bit 4v+c: entry (v, c) is in b*
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) in |= (valid(q[v], c) && coarse_bin(q[v].sc[c]) == bstar ? 1u : 0u) << (4 * v + c);
+    // the wave's entries get consecutive places: a prefix sum over the lanes, one atomic
+    const int cnt = __popc(in);
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    int wb = 0;
+    if (lane == 63 && incl > 0) wb = atomicAdd(&tb_n, incl);
+    int i = __shfl(wb, 63) + incl - cnt;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((in >> (4 * v + c)) & 1u) {
+          if (i < TMAX) {
+            tb_score[i] = q[v].sc[c];
+            tb_slot[i] = slot_of(q[v], c);
+          }
+          ++i;
+        }
+  };
+  collect(q0);
+  for (int base = STEP; base < n_all; base += STEP) {
+    Quad q[V];
+    load_step(base, q);
+    collect(q);
+  }
+  __syncthreads();
+  const int n_star = tb_n;
   int running = 0, parity = 0;
-  for (int base = 0; base < n_all; base += 4 * V * NT) {
+  if (n_star > TMAX) {
+    // Heavy ties at b*: every entry of bin >= b* into the LDS list (fewer than CAP),
+    // then the exact selection over it.
+    const int thr = bin_floor(bstar);  // coarse_bin(v) >= b*  <=>  v >= thr
+    for (int base = 0; base < n_all; base += STEP) {
+      Quad q[V];
+      load_step(base, q);
+      unsigned m[V];
+      SP pl[V][4];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        m[v] = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          pl[v][c].slot = slot_of(q[v], c);
+          pl[v][c].score = q[v].sc[c];
+          m[v] |= (valid(q[v], c) && q[v].sc[c] >= thr ? 1u : 0u) << c;
+        }
+      }
+      running = ordered_emit4<NT, V>(base, m, pl, wcnt + parity * V * NW, running, [&](int r, int, SP x) {
+        if (r < CAP) {
+          lslot[r] = x.slot;
+          lval[r] = x.score;
+        }
+      });
+      parity ^= 1;
+    }
+    __syncthreads();
+    finish_from_list<NT, false>(rv, min(running, CAP), lslot, lval, bstar, above, k, wcnt, h256, scan_tmp, sh,
+                                out);
+    return;
+  }
+
+  // The cutoff: the (k - above)-th best entry of b* by (score desc, slot asc), found by
+  // one wave among the collected ones.
+  if (tid < 64) {
+    unsigned long long kpref;
+    const unsigned long long kmask = bin_key_prefix(bstar, &kpref);
+    const auto key = [&](int i) {
+      return ((unsigned long long)okey(tb_score[i]) << 32) | (0xFFFFFFFFu - (unsigned)tb_slot[i]);
+    };
+    const unsigned long long cut =
+        n_star <= 256 ? wave_select_kth<4>(n_star, k - above, key, h256, kpref, kmask)
+                      : wave_select_kth<TMAX / 64>(n_star, k - above, key, h256, kpref, kmask);
+    if (tid == 0) {
+      sh[0] = (int)((unsigned)(cut >> 32) ^ 0x80000000u);
+      sh[1] = (int)(0xFFFFFFFFu - (unsigned)cut);
+    }
+  }
+  __syncthreads();
+  const int T = sh[0], slot_T = sh[1];
+
+  // Pass 2: the taken entries -- score > T, or score == T and slot <= slot_T; exactly
+  // k of them -- straight to the output in slot order.
+  auto emit = [&](int base, const Quad (&q)[V]) {
     unsigned m[V];
     SP pl[V][4];
 #pragma unroll
@@ -783,36 +1076,23 @@ __global__ __launch_bounds__(NT) void topk_list_finish_kernel(int32_t* __restric
       m[v] = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int e = base + 4 * (v * NT + tid) + c;
-        const int ec = min(e, n_all - 1);  // clamped: the loads stay unconditional
-        int lo = 0, hi = n_sp;             // loff[lo] <= ec < loff[hi] (loff[n_sp] = n_all)
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (loff[mid] <= ec) lo = mid;
-          else hi = mid;
-        }
-        const int j = ec - loff[lo];
-        if (slist[lo]) {
-          const int2 x = reinterpret_cast<const int2*>(ws.list(row, lo))[j];
-          pl[v][c].slot = x.x;
-          pl[v][c].score = x.y;
-        } else {
-          pl[v][c].slot = lo * span + j;
-          pl[v][c].score = rv.srow[lo * span + j];
-        }
-        m[v] |= (e < n_all && coarse_bin(pl[v][c].score) >= bstar ? 1u : 0u) << c;
+        const int sc = q[v].sc[c], sl = slot_of(q[v], c);
+        pl[v][c].slot = sl;
+        pl[v][c].score = sc;
+        m[v] |= (valid(q[v], c) && (sc > T || (sc == T && sl <= slot_T)) ? 1u : 0u) << c;
       }
     }
     running = ordered_emit4<NT, V>(base, m, pl, wcnt + parity * V * NW, running, [&](int r, int, SP x) {
-      if (r < CAP) {
-        lslot[r] = x.slot;
-        lval[r] = x.score;
-      }
+      if (r < k) out[r] = x.slot;
     });
     parity ^= 1;
+  };
+  emit(0, q0);
+  for (int base = STEP; base < n_all; base += STEP) {
+    Quad q[V];
+    load_step(base, q);
+    emit(base, q);
   }
-  __syncthreads();
-  finish_from_list<NT, false>(rv, min(running, CAP), lslot, lval, bstar, above, k, wcnt, h256, scan_tmp, sh, out);
 }
 
 // Block keep of the two-stage indexer: own block + the best n_keep-1 earlier blocks
@@ -965,7 +1245,7 @@ bool dec_sel_layout(long long rows, int L_max, int k, DecLayout* out) {
   if (parts > DEC_MAX_PARTS) return false;
   // a list holds at least min(span, k) entries, plus the rest of the bin that completes it
   out->parts = (int)parts;
-  out->lcap = (int)std::min<long long>(2ll * k, DEC_SPAN_MAX);
+  out->lcap = (int)std::min<long long>((2ll * k + 3) / 4 * 4, DEC_SPAN_MAX);
   out->rec_ints = DecWs::rec_ints_for(out->lcap);
   return true;
 }
