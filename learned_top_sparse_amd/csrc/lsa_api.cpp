@@ -228,11 +228,13 @@ LSA_API lsa_status lsa_topk(const int32_t* scores, int64_t ld_scores, const int3
   return hip_status(lsa::launch_topk(a, as_stream(stream)));
 }
 
+// split count of the sparse attention: at most one 32-key tile per split, and at most
+// 64 splits (the merge keeps a weight per split and head in LDS)
 static int resolve_split(int32_t B, int32_t n_q, int32_t k_top, int32_t n_split) {
   const long long rows = (long long)B * n_q;
   const int n_tiles = (k_top + 31) / 32;
-  if (n_split <= 0) return attn_split_auto(rows, k_top);
-  return std::max(1, std::min(std::min(n_split, n_tiles), 64));
+  const int want = n_split <= 0 ? attn_split_auto(rows, k_top) : n_split;
+  return std::max(1, std::min(std::min(want, n_tiles), 64));
 }
 
 static size_t attn_ws_bytes(long long rows, int32_t H_q, int32_t d, int split) {

@@ -257,49 +257,55 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     }
   }
 
-  // ---- merge the NW wave states through LDS: region of wave w = O[16][128] | m[16] | l[16]
+  // ---- merge the NW wave states through LDS: region of wave w = O[16][OSTR] | m[16] | l[16]
+  // (OSTR = D + 4: the 16 head rows start 4 banks apart, so a wave's O writes do not
+  // collide); the per-head weights are computed once, then each output is NW FMAs.
+  constexpr int OSTR = D + 4;
+  static_assert(16 * OSTR + 32 <= WAVE_LDS, "a wave's state fits its LDS region");
   float l_tot = xhalf32_sumf(l_part);
   l_tot = xrow16_sumf(l_tot);
   wave_lds_sync();
   {
     float* st = reinterpret_cast<float*>(vt);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int d = 16 * dt + 4 * g;
-      *(v4f*)(st + r16 * D + d) = O[dt];
-    }
+    for (int dt = 0; dt < 8; ++dt) *(v4f*)(st + r16 * OSTR + 16 * dt + 4 * g) = O[dt];
     if (g == 0) {
-      st[16 * D + r16] = m_run;
-      st[16 * D + 16 + r16] = l_tot;
+      st[16 * OSTR + r16] = m_run;
+      st[16 * OSTR + 16 + r16] = l_tot;
     }
   }
   __syncthreads();
   const float* all = reinterpret_cast<const float*>(lds);
-  for (int e = threadIdx.x; e < 16 * D; e += 64 * NW) {
-    const int h = e / D, d = e % D;
-    if (h >= H_q) continue;
+  __shared__ float wsc[NW][16], hinv[16], hlse[16];  // per (wave, head) weight; per head 1/den, lse
+  if (threadIdx.x < 16) {
+    const int h = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, all[w * WAVE_LDS + 16 * D + h]);
-    float num = 0.f, den = 0.f;
-    if (M > -INFINITY) {
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, all[w * WAVE_LDS + 16 * OSTR + h]);
+    float den = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float* st = all + w * WAVE_LDS;
-        const float mw = st[16 * D + h];
-        const float sc = mw > -INFINITY ? exp2f(mw - M) : 0.f;
-        num += sc * st[h * D + d];
-        den += sc * st[16 * D + 16 + h];
-      }
+    for (int w = 0; w < NW; ++w) {
+      const float mw = all[w * WAVE_LDS + 16 * OSTR + h];
+      const float sc = (M > -INFINITY && mw > -INFINITY) ? exp2f(mw - M) : 0.f;
+      wsc[w][h] = sc;
+      den += sc * all[w * WAVE_LDS + 16 * OSTR + 16 + h];
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    const float lse_v = den > 0.f ? (M + log2f(den)) * LN2 : -INFINITY;
+    hinv[h] = den > 0.f ? 1.f / den : 0.f;
+    hlse[h] = den > 0.f ? (M + log2f(den)) * LN2 : -INFINITY;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < H_q * D; e += 64 * NW) {
+    const int h = e / D, d = e % D;
+    float num = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) num += wsc[w][h] * all[w * WAVE_LDS + h * OSTR + d];
+    const float o = num * hinv[h];
     if (n_split == 1) {
-      reinterpret_cast<unsigned short*>(out)[(row * H_q + h) * D + d] = (unsigned short)bf16_bits(num * inv);
-      if (lse != nullptr && d == 0) lse[row * H_q + h] = lse_v;
+      reinterpret_cast<unsigned short*>(out)[(row * H_q + h) * D + d] = (unsigned short)bf16_bits(o);
+      if (lse != nullptr && d == 0) lse[row * H_q + h] = hlse[h];
     } else {
-      ws[((row * n_split + split) * H_q + h) * D + d] = num * inv;
-      if (d == 0) ws[(long long)gridDim.x * H_q * D + (row * n_split + split) * H_q + h] = lse_v;
+      ws[(unit * H_q + h) * D + d] = o;
+      if (d == 0) ws[(long long)gridDim.x * H_q * D + unit * H_q + h] = hlse[h];
     }
   }
 }
@@ -350,6 +356,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
   const long long rows = (long long)a.B * a.n_q;
   if (rows == 0) return hipSuccess;
+  if (a.n_split < 1 || a.n_split > 64) return hipErrorInvalidValue;  // the merges hold 64 splits
   const long long units = rows * a.n_split;
   hipLaunchKernelGGL((sparse_attn_kernel<ATTN_WAVES>), dim3((unsigned)units), dim3(64 * ATTN_WAVES), 0, st,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.idx, a.n_q, a.L_max, a.H_q,
