@@ -313,64 +313,7 @@ template <int NT, bool KEPT>
 __device__ __forceinline__ void finish_from_list(const RowView<KEPT> rv, int Lc, int* lslot, int* lval, int bstar,
                                                  int above, int k, int* wcnt, int* h256, int* scan_tmp, int* sh,
                                                  int32_t* out) {
-  // The entries of b* decide which of them are taken: need = k - above of them, by
-  // (score desc, slot asc).  Collect them (any order; one LDS atomic per wave), then
-  // one wave selects the need-th largest (score, -slot) key among them only: that is
-  // the cutoff (T, slot_T), and the taken entries are those with score > T, or
-  // score == T and slot <= slot_T.
-  constexpr int TMAX = 1024;
-  __shared__ int tb_score[TMAX], tb_slot[TMAX], tb_n;
-  const int lane = threadIdx.x & 63;
-  if (threadIdx.x == 0) tb_n = 0;
-  __syncthreads();
-  for (int e0 = 0; e0 < Lc; e0 += NT) {
-    const int e = e0 + (int)threadIdx.x;
-    const int sc = e < Lc ? lval[e] : 0;
-    const bool in = e < Lc && coarse_bin(sc) == bstar;
-    const unsigned long long bal = __ballot(in);
-    int wbase = 0;
-    if (lane == 0 && bal != 0ull) wbase = atomicAdd(&tb_n, __popcll(bal));
-    wbase = __shfl(wbase, 0);
-    if (in) {
-      const int i = wbase + lanes_below(bal);
-      if (i < TMAX) {
-        tb_score[i] = sc;
-        tb_slot[i] = lslot[e];
-      }
-    }
-  }
-  __syncthreads();
-  const int n_star = tb_n;
-  if (n_star <= TMAX) {
-    if (threadIdx.x < 64) {
-      unsigned long long kpref;
-      const unsigned long long kmask = bin_key_prefix(bstar, &kpref);
-      const auto key = [&](int i) {
-        return ((unsigned long long)okey(tb_score[i]) << 32) | (0xFFFFFFFFu - (unsigned)tb_slot[i]);
-      };
-      const unsigned long long cut =
-          n_star <= 256 ? wave_select_kth<4>(n_star, k - above, key, h256, kpref, kmask)
-                        : wave_select_kth<TMAX / 64>(n_star, k - above, key, h256, kpref, kmask);
-      if (threadIdx.x == 0) {
-        sh[0] = (int)((unsigned)(cut >> 32) ^ 0x80000000u);
-        sh[1] = (int)(0xFFFFFFFFu - (unsigned)cut);
-      }
-    }
-    __syncthreads();
-    const int T = sh[0], slot_T = sh[1];
-    ordered_compact<NT, 4>(
-        Lc, wcnt,
-        [&](int e, int&) {
-          const int sc = lval[e];
-          return sc > T || (sc == T && lslot[e] <= slot_T);
-        },
-        [&](int r, int e, int) {
-          if (r < k) out[r] = rv.key_of(lslot[e]);
-        });
-    return;
-  }
-  // Many ties: an exact radix selection over the entries of b*.  Bits shared by every
-  // entry of b*: the radix starts at the byte of the highest differing bit.
+  // bits shared by every entry of b*: the radix starts at the byte of the highest differing bit
   unsigned mx = 0u, mn = 0xFFFFFFFFu;
   for (int e = threadIdx.x; e < Lc; e += NT) {
     const int sc = lval[e];
@@ -826,8 +769,16 @@ __global__ __launch_bounds__(NT) void topk_list_finish_kernel(int32_t* __restric
   const int tid = threadIdx.x, lane = tid & 63;
   int32_t* out = idx + row * (long long)k;
 
+  // The position, a span header per thread and the first group sums of every thread
+  // are requested together, before the position is known: records of spans past the
+  // row's last one (stale) are read but not used.  Thread t adds group t % NGRP of
+  // spans t / NGRP, t / NGRP + NT / NGRP, ...
+  const int p_raw = q_pos[row];
+  const int4 hdr = *reinterpret_cast<const int4*>(ws.hdr(row, min(tid, ws.parts - 1)));
+  const int gs0 = ws.gsum(row, min(tid / NGRP, ws.parts - 1))[tid % NGRP];
+
   RowView<false> rv;
-  rv.p = min(q_pos[row], L_max - 1);
+  rv.p = min(p_raw, L_max - 1);
   rv.srow = scores + row * ld;
   rv.vec = (((uintptr_t)rv.srow) & 15u) == 0;
   rv.bs = 0;
@@ -841,21 +792,17 @@ __global__ __launch_bounds__(NT) void topk_list_finish_kernel(int32_t* __restric
   }
   const int span = dec_span(n_valid, ws.parts);
   const int n_sp = (n_valid + span - 1) / span;  // spans of this row (each left a record)
-
-  // the spans' headers, and the row's group sums: thread t adds group t % NGRP of
-  // spans t / NGRP, t / NGRP + NT / NGRP, ...
   if (tid < n_sp) {
-    const int4 h = *reinterpret_cast<const int4*>(ws.hdr(row, tid));
-    sband[0][tid] = h.x;
-    sband[1][tid] = h.y;
-    slist[tid] = h.w >= 0;
-    slen[tid] = h.w >= 0 ? h.z : min(n_valid, (tid + 1) * span) - tid * span;
+    sband[0][tid] = hdr.x;
+    sband[1][tid] = hdr.y;
+    slist[tid] = hdr.w >= 0;
+    slen[tid] = hdr.w >= 0 ? hdr.z : min(n_valid, (tid + 1) * span) - tid * span;
   }
   if (tid < NGRP) gs_l[tid] = 0;
   if (tid < GRP) bins_l[tid] = 0;
   {
-    int acc = 0;
-    for (int sp = tid / NGRP; sp < n_sp; sp += NT / NGRP) acc += ws.gsum(row, sp)[tid % NGRP];
+    int acc = tid / NGRP < n_sp ? gs0 : 0;
+    for (int sp = tid / NGRP + NT / NGRP; sp < n_sp; sp += NT / NGRP) acc += ws.gsum(row, sp)[tid % NGRP];
     __syncthreads();
     if (acc) atomicAdd(&gs_l[tid % NGRP], acc);
   }
