@@ -218,10 +218,24 @@ typedef struct lsa_forward_args {
      LSA_ERR_INVALID_ARG and nothing is launched.  NULL: no events. */
   void* const* stage_events;
   int32_t n_stage_events;
+  /* Selection of flat rows of at least 8 queries per sequence (prefill):
+     LSA_SELECT_AUTO (0): rows longer than 4*k_top keys (k_top <= 2048, L_max <= 524288)
+       take the thresholded selection -- a sample of every row's keys gives it a
+       threshold, the indexer keeps only the entries that reach it, and the exact
+       top-k is taken from those; a row whose kept entries fall short of k_top or
+       overflow 4*k_top goes through the score table instead.  Other rows use the
+       score table.  The results are the same either way.
+     LSA_SELECT_TABLE (1): every row through the score table.
+     LSA_SELECT_FORCE_SHORT (2), LSA_SELECT_FORCE_OVERFLOW (3): as AUTO, but every
+       thresholded row's threshold is set above (below) all of its scores, so every
+       such row takes the fallback -- for testing that path. */
+  int32_t select_mode;
 } lsa_forward_args;
+enum { LSA_SELECT_AUTO = 0, LSA_SELECT_TABLE = 1, LSA_SELECT_FORCE_SHORT = 2, LSA_SELECT_FORCE_OVERFLOW = 3 };
 
-/* Workspace for lsa_forward.  With a->chunk_rows = 0 it sizes score chunks of
-   at most ~4 GiB; lsa_forward then uses whatever chunk fits the ws it gets. */
+/* Workspace for lsa_forward.  With a->chunk_rows = 0 it sizes chunks whose per-row
+   buffers (score table, sampled scores, candidate lists) come to at most ~8 GiB;
+   lsa_forward then uses whatever chunk fits the ws it gets. */
 lsa_status lsa_forward_workspace_size(const lsa_forward_args* a, size_t* bytes);
 lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_bytes, void* stream);
 /* The launch plan lsa_forward uses with a workspace of ws_bytes: query rows per
@@ -240,6 +254,11 @@ lsa_status lsa_forward_plan(const lsa_forward_args* a, size_t ws_bytes, int64_t*
                       table, each key span's share of the selection state (coarse
                       score histogram and candidate list); TOPK then finishes each
                       row from it (the decode selection)
+     SAMPLE           thresholded selection of flat prefill rows: the indexer over a
+                      sample of every row's keys and each row's threshold; then
+                      INDEX_SELECT keeps each row's entries that reach it (short
+                      rows write the score table) and TOPK takes the exact top-k
+                      from them (with the score-table fallback)
      INDEX_SCORES     the indexer over a chunk, writing the score table
      TOPK             the exact top-k of a chunk
      SPARSE_ATTN      sparse attention of a chunk (split-KV combine included)
@@ -250,7 +269,8 @@ enum {
   LSA_STAGE_INDEX_SELECT = 3,
   LSA_STAGE_INDEX_SCORES = 4,
   LSA_STAGE_TOPK = 5,
-  LSA_STAGE_SPARSE_ATTN = 6
+  LSA_STAGE_SPARSE_ATTN = 6,
+  LSA_STAGE_SAMPLE = 7
 };
 lsa_status lsa_forward_stages(const lsa_forward_args* a, size_t ws_bytes, int32_t* codes, int32_t max_codes,
                               int32_t* n_stages);

@@ -23,7 +23,7 @@ EXPORTED = [
     "lsa_forward_workspace_size", "lsa_forward", "lsa_forward_plan", "lsa_forward_stages",
 ]
 
-STAGE_NAMES = {1: "block_reps", 2: "block_prefilter", 3: "index_select", 4: "index_scores", 5: "topk",
+STAGE_NAMES = {1: "block_reps", 2: "block_prefilter", 3: "index_select", 4: "index_scores", 5: "topk", 7: "sample",
                6: "sparse_attn"}
 
 P = C.c_void_p
@@ -48,6 +48,7 @@ class ForwardArgs(C.Structure):
         ("scale", C.c_float), ("attn_split", I32), ("chunk_rows", I64),
         ("idx", P), ("count", P), ("out", P), ("lse", P), ("kept_blocks", P),
         ("stage_events", P), ("n_stage_events", I32),
+        ("select_mode", I32),
     ]
 
 
@@ -242,8 +243,12 @@ def lsa_sparse_attn(q, k, v, idx, scale: Optional[float] = None, n_split: int = 
     return out, lse
 
 
+# selection of flat prefill rows (lsa_forward_args.select_mode)
+SELECT_MODES = {"auto": 0, "table": 1, "force_short": 2, "force_overflow": 3}
+
+
 def _forward_args(inp: dict, k_top: int, two_stage: bool, block_size: int, n_keep: int, scale, attn_split: int,
-                  chunk_rows: int, out: dict):
+                  chunk_rows: int, out: dict, select: str = "auto"):
     q_idx, k_idx, w, q_pos, q, k, v = (inp[n] for n in ("q_idx", "k_idx", "w", "q_pos", "q", "k", "v"))
     B, n_q, H_I, d_I = q_idx.shape
     _, _, H_q, d = q.shape
@@ -264,33 +269,37 @@ def _forward_args(inp: dict, k_top: int, two_stage: bool, block_size: int, n_kee
     a.out = out["out"].data_ptr()
     a.lse = out["lse"].data_ptr() if out.get("lse") is not None else None
     a.kept_blocks = out["kept"].data_ptr() if out.get("kept") is not None else None
+    if select not in SELECT_MODES:
+        raise LsaError(f"select must be one of {sorted(SELECT_MODES)}")
+    a.select_mode = SELECT_MODES[select]
     return a
 
 
 def lsa_forward_workspace_size(inp: dict, k_top: int, two_stage: bool = False, block_size: int = 128,
-                               n_keep: int = 64, attn_split: int = 0, chunk_rows: int = 0) -> int:
+                               n_keep: int = 64, attn_split: int = 0, chunk_rows: int = 0,
+                               select: str = "auto") -> int:
     dummy = {"idx": inp["q_pos"], "out": inp["q"]}
-    a = _forward_args(inp, k_top, two_stage, block_size, n_keep, None, attn_split, chunk_rows, dummy)
+    a = _forward_args(inp, k_top, two_stage, block_size, n_keep, None, attn_split, chunk_rows, dummy, select)
     nb = SZ(0)
     _check("lsa_forward_workspace_size", lib().lsa_forward_workspace_size(C.byref(a), C.byref(nb)))
     return nb.value
 
 
 def lsa_forward_plan(inp: dict, k_top: int, ws_bytes: int, two_stage: bool = False, block_size: int = 128,
-                     n_keep: int = 64, attn_split: int = 0, chunk_rows: int = 0):
+                     n_keep: int = 64, attn_split: int = 0, chunk_rows: int = 0, select: str = "auto"):
     """(rows per chunk, attention split) that lsa_forward uses with ws_bytes of workspace."""
     dummy = {"idx": inp["q_pos"], "out": inp["q"]}
-    a = _forward_args(inp, k_top, two_stage, block_size, n_keep, None, attn_split, chunk_rows, dummy)
+    a = _forward_args(inp, k_top, two_stage, block_size, n_keep, None, attn_split, chunk_rows, dummy, select)
     rows, split = I64(0), I32(0)
     _check("lsa_forward_plan", lib().lsa_forward_plan(C.byref(a), ws_bytes, C.byref(rows), C.byref(split)))
     return rows.value, split.value
 
 
 def lsa_forward_stages(inp: dict, k_top: int, ws_bytes: int, two_stage: bool = False, block_size: int = 128,
-                       n_keep: int = 64, attn_split: int = 0, chunk_rows: int = 0) -> list:
+                       n_keep: int = 64, attn_split: int = 0, chunk_rows: int = 0, select: str = "auto") -> list:
     """Names of the stages lsa_forward runs with ws_bytes of workspace, in launch order."""
     dummy = {"idx": inp["q_pos"], "out": inp["q"]}
-    a = _forward_args(inp, k_top, two_stage, block_size, n_keep, None, attn_split, chunk_rows, dummy)
+    a = _forward_args(inp, k_top, two_stage, block_size, n_keep, None, attn_split, chunk_rows, dummy, select)
     n = I32(0)
     _check("lsa_forward_stages", lib().lsa_forward_stages(C.byref(a), ws_bytes, None, 0, C.byref(n)))
     codes = (I32 * max(n.value, 1))()
@@ -300,7 +309,8 @@ def lsa_forward_stages(inp: dict, k_top: int, ws_bytes: int, two_stage: bool = F
 
 def lsa_forward(inp: dict, k_top: int, two_stage: bool = False, block_size: int = 128, n_keep: int = 64,
                 scale: Optional[float] = None, attn_split: int = 0, chunk_rows: int = 0,
-                out: Optional[dict] = None, ws: Optional[torch.Tensor] = None, stage_events=None) -> dict:
+                out: Optional[dict] = None, ws: Optional[torch.Tensor] = None, stage_events=None,
+                select: str = "auto") -> dict:
     """The whole path.  ``inp`` holds q_idx, k_idx, w, q_pos, q, k, v (device tensors).
     Returns dict(idx, count, out, lse[, kept]); pass ``out`` / ``ws`` to reuse buffers.
     ``stage_events``: optional torch.cuda.Event list (1 + len(lsa_forward_stages(...)));
@@ -321,7 +331,7 @@ def lsa_forward(inp: dict, k_top: int, two_stage: bool = False, block_size: int 
         }
         if two_stage:
             out["kept"] = torch.empty((B, n_q, n_keep), dtype=torch.int32, device=dev)
-    a = _forward_args(inp, k_top, two_stage, block_size, n_keep, scale, attn_split, chunk_rows, out)
+    a = _forward_args(inp, k_top, two_stage, block_size, n_keep, scale, attn_split, chunk_rows, out, select)
     if ws is None:
         nb = SZ(0)
         _check("lsa_forward_workspace_size", lib().lsa_forward_workspace_size(C.byref(a), C.byref(nb)))

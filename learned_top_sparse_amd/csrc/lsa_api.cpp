@@ -308,6 +308,7 @@ lsa_status check_forward(const lsa_forward_args* a) {
   if (a->d_I != 64 && a->d_I != 128) return LSA_ERR_UNSUPPORTED;
   if (a->H_I < 1 || a->H_I > 64 || a->d != 128 || a->H_q < 1 || a->H_q > 16) return LSA_ERR_UNSUPPORTED;
   if (a->k_top > 4096) return LSA_ERR_UNSUPPORTED;
+  if (a->select_mode < LSA_SELECT_AUTO || a->select_mode > LSA_SELECT_FORCE_OVERFLOW) return LSA_ERR_INVALID_ARG;
   if (a->two_stage) {
     if (a->block_size < 1 || a->n_keep < 1) return LSA_ERR_INVALID_ARG;
     if (a->block_size > 128 || a->n_keep > 256 || a->L_max / a->block_size > 65536) return LSA_ERR_UNSUPPORTED;
@@ -316,6 +317,26 @@ lsa_status check_forward(const lsa_forward_args* a) {
   if (!a->q_idx || !a->k_idx || !a->w || !a->q_pos || !a->q || !a->k || !a->v || !a->idx || !a->out)
     return LSA_ERR_INVALID_ARG;
   return LSA_OK;
+}
+
+// Thresholded selection (the score table only for short rows and fallbacks) applies to
+// flat chunks of at least 8 queries per sequence whose rows may exceed thr_cap(k) keys.
+bool thr_applies(const lsa_forward_args* a) {
+  return !a->two_stage && a->select_mode != LSA_SELECT_TABLE && a->n_q >= 8 && a->k_top <= lsa::THR_MAX_K &&
+         a->L_max <= lsa::THR_MAX_L && a->L_max > lsa::thr_row_min(a->k_top);
+}
+// sampled scores per row (leading dimension)
+int64_t thr_ld(int32_t L_max, int32_t k) {
+  const int st = lsa::thr_stride(k);
+  return ((int64_t)(L_max - 1) / st + 1 + 63) / 64 * 64;
+}
+// its workspace for a chunk of `rows` rows: sampled scores, threshold, state and count
+// per row, and the candidate lists (slots, scores)
+size_t thr_ws_bytes(const lsa_forward_args* a, long long rows) {
+  if (!thr_applies(a)) return 0;
+  const size_t cap = (size_t)lsa::thr_cap(a->k_top);
+  return align_up((size_t)rows * thr_ld(a->L_max, a->k_top) * 4) + 3 * align_up((size_t)rows * 4) +
+         2 * align_up((size_t)rows * cap * 4);
 }
 
 FwdPlan plan_forward(const lsa_forward_args* a) {
@@ -330,6 +351,7 @@ FwdPlan plan_forward(const lsa_forward_args* a) {
     p.n_blocks = 0;
     p.ld = score_ld(a->L_max);
     p.per_row = p.ld * 4;
+    if (thr_applies(a)) p.per_row += thr_ld(a->L_max, a->k_top) * 4 + 2LL * lsa::thr_cap(a->k_top) * 4 + 12;
     p.fixed = 0;
   }
   return p;
@@ -357,12 +379,13 @@ size_t chunk_bytes(const lsa_forward_args* a, const FwdPlan& p, long long rows) 
   const int split = resolve_split(1, (int32_t)rows, a->k_top, a->attn_split);
   s += attn_ws_bytes(rows, a->H_q, a->d, split);
   if (!a->two_stage) s += align_up(topk_ws_for(a, rows));
+  s += thr_ws_bytes(a, rows);
   return s;
 }
 
 long long total_rows(const lsa_forward_args* a) { return a->n_q == 1 ? (long long)a->B : (long long)a->n_q; }
 
-constexpr long long kChunkBudget = 4ll << 30;  // default score-chunk budget (bytes)
+constexpr long long kChunkBudget = 8ll << 30;  // default chunk budget (bytes)
 
 // rows per chunk for a workspace of ws_bytes (0 if even one row does not fit)
 long long plan_rows(const lsa_forward_args* a, const FwdPlan& p, size_t ws_bytes) {
@@ -392,6 +415,10 @@ bool chunk_fused(const lsa_forward_args* a, int32_t nb, int32_t ni, size_t topk_
   return !a->two_stage && ni < 8 && need > 0 && need <= topk_ws_size;
 }
 
+bool chunk_thr(const lsa_forward_args* a, int32_t nb, int32_t ni, size_t topk_ws_size) {
+  return thr_applies(a) && !chunk_fused(a, nb, ni, topk_ws_size);
+}
+
 // chunks of lsa_forward for `rows` rows per chunk, as (b0, nb, i0, ni)
 template <typename F>
 void for_each_chunk(const lsa_forward_args* a, long long rows, F f) {
@@ -411,7 +438,9 @@ std::vector<int32_t> forward_stages(const lsa_forward_args* a, const FwdPlan& p,
   const size_t topk_ws_size = a->two_stage ? 0 : topk_ws_for(a, rows);
   for_each_chunk(a, rows, [&](int32_t, int32_t nb, int32_t, int32_t ni) {
     if (a->two_stage) st.push_back(LSA_STAGE_BLOCK_PREFILTER);
-    st.push_back(chunk_fused(a, nb, ni, topk_ws_size) ? LSA_STAGE_INDEX_SELECT : LSA_STAGE_INDEX_SCORES);
+    const bool thr = chunk_thr(a, nb, ni, topk_ws_size);
+    if (thr) st.push_back(LSA_STAGE_SAMPLE);
+    st.push_back(chunk_fused(a, nb, ni, topk_ws_size) || thr ? LSA_STAGE_INDEX_SELECT : LSA_STAGE_INDEX_SCORES);
     st.push_back(LSA_STAGE_TOPK);
     st.push_back(LSA_STAGE_SPARSE_ATTN);
   });
@@ -486,6 +515,27 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
   off += attn_ws_bytes(rows, a->H_q, a->d, resolve_split(1, (int32_t)rows, a->k_top, a->attn_split));
   void* topk_ws = a->two_stage ? nullptr : static_cast<void*>(base + off);
   const size_t topk_ws_size = a->two_stage ? 0 : topk_ws_for(a, rows);
+  if (!a->two_stage) off += align_up(topk_ws_size);
+  // thresholded selection: sampled scores, per-row threshold / state / count, candidate lists
+  int32_t* thr_samp = nullptr;
+  lsa::ThrArgs thr{};
+  const int64_t ld_s = thr_ld(a->L_max, a->k_top);
+  if (thr_applies(a)) {
+    thr.cap = lsa::thr_cap(a->k_top);
+    thr.row_min = lsa::thr_row_min(a->k_top);
+    thr_samp = reinterpret_cast<int32_t*>(base + off);
+    off += align_up((size_t)rows * ld_s * 4);
+    thr.theta = reinterpret_cast<int32_t*>(base + off);
+    off += align_up((size_t)rows * 4);
+    thr.rstate = reinterpret_cast<int32_t*>(base + off);
+    off += align_up((size_t)rows * 4);
+    thr.cnt = reinterpret_cast<int32_t*>(base + off);
+    off += align_up((size_t)rows * 4);
+    thr.lslot = reinterpret_cast<int32_t*>(base + off);
+    off += align_up((size_t)rows * thr.cap * 4);
+    thr.lscore = reinterpret_cast<int32_t*>(base + off);
+    off += align_up((size_t)rows * thr.cap * 4);
+  }
 
   const int32_t d_I = a->d_I, H_I = a->H_I, H_q = a->H_q, d = a->d, L = a->L_max, kt = a->k_top;
   // one split count for every chunk, so no chunk needs more attention workspace than sized
@@ -564,8 +614,36 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
       ia.sel_lcap = dl.lcap;
       ia.k_top = kt;
     }
-    if (lsa::launch_index_scores(ia, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
-    if (lsa::launch_topk(ta, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
+    if (chunk_thr(a, nb, ni, topk_ws_size)) {
+      // Thresholded selection: score a sample of every row's keys and set its
+      // threshold (short rows keep the table) ...
+      const long long rows_c = (long long)nb * ni;
+      const int mode = a->select_mode == LSA_SELECT_FORCE_SHORT ? 1 : a->select_mode == LSA_SELECT_FORCE_OVERFLOW ? 2 : 0;
+      lsa::IdxArgs sa = ia;
+      sa.stride = lsa::thr_stride(kt);
+      sa.row_min = thr.row_min;  // table rows need no threshold
+      sa.scores = thr_samp;
+      sa.ld = ld_s;
+      if (lsa::launch_index_scores(sa, s) != hipSuccess) return LSA_ERR_HIP;
+      if (lsa::launch_thresholds(thr_samp, ld_s, qp, rows_c, L, kt, sa.stride, mode, thr, s) != hipSuccess ||
+          !mark())
+        return LSA_ERR_HIP;
+      // ... the scan appends each list row's candidates (table rows store their scores) ...
+      ia.thr = thr;
+      if (lsa::launch_index_scores(ia, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
+      // ... the list rows' top-k from their lists; rows whose list fell short or
+      // overflowed are scored again into the table, and the top-k of the table rows
+      if (lsa::launch_list_topk(qp, rows_c, L, kt, thr, ix, cnt, s) != hipSuccess) return LSA_ERR_HIP;
+      lsa::IdxArgs fa = ia;
+      fa.thr = lsa::ThrArgs{};
+      fa.tile_filter = thr.rstate;
+      if (lsa::launch_index_scores(fa, s) != hipSuccess) return LSA_ERR_HIP;
+      ta.row_state = thr.rstate;
+      if (lsa::launch_topk(ta, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
+    } else {
+      if (lsa::launch_index_scores(ia, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
+      if (lsa::launch_topk(ta, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
+    }
     lsa_status sa = run_attn(qq, kk, vv, ix, nb, ni, L, H_q, d, kt, a->scale, split, oo, ls, attn_ws, s);
     if (sa != LSA_OK) return sa;
     return mark() ? LSA_OK : LSA_ERR_HIP;

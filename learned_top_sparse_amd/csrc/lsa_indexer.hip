@@ -112,16 +112,27 @@ __device__ __forceinline__ int relu_mad24(int x, int w, int acc) {
 //     as one buffer store per lane whose range check (records = the query's valid
 //     keys) drops what the query may not see: no branch around a store, so the
 //     memory counter the loads share with the stores stays exact.
+// Slot j scores key j * stride (a stride above 1 scores an evenly spaced sample of
+// the keys; slot j is valid for a query at position p iff j * stride <= p).
+// SEL (thresholded selection): a wave whose row is a list row instead appends the
+// (slot, score) of its scores >= the row's threshold to a buffer in LDS, and moves
+// the buffer to the row's candidate list (one device atomic reserves the places)
+// whenever it nears full and at the end; table rows store their scores as above.
+// tile_filter (optional): only query tiles holding a row of state 2 do any work;
+// row_min: only query tiles holding a row of more than row_min keys do.
 // Grid: x = n_qtiles * n_spans (longest query tiles first), y = B.
-template <int D, int MT, int NW>
+template <int D, int MT, int NW, bool SEL>
 __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
     int w_per_query, const int32_t* __restrict__ q_pos, int n_q, int L_max, int H_I, int span,
-    int n_spans, int n_qtiles, int32_t* __restrict__ scores, long long ld) {
+    int n_spans, int n_qtiles, int32_t* __restrict__ scores, long long ld, int stride,
+    const int32_t* __restrict__ tile_filter, int row_min, ThrArgs thr) {
   constexpr int KS = D / 64, KT = 64, CH = D / 16;
   constexpr int R = 3;  // register stages of key tiles
+  constexpr int WBUF = 512;  // SEL: candidates a wave buffers in LDS
   static_assert(KT * CH <= 64 * NW, "one 16-byte chunk of a key tile per thread");
   __shared__ __attribute__((aligned(16))) int8_t tile[2][KT * D];
+  __shared__ int wb_slot[SEL ? NW : 1][WBUF], wb_score[SEL ? NW : 1][WBUF];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -134,37 +145,75 @@ __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
   const int qt = n_qtiles - 1 - qt_rev;
   const int i0 = qt * NW;
   const int32_t* qp = q_pos + (long long)b * n_q;
+  // last valid slot of a query at position p (-1: none)
+  auto last_slot = [&](int p) { return p < 0 ? -1 : min(p, L_max - 1) / stride; };
 
-  int pmax = -1;
+  int pmax = -1, nmax = 0;
+  bool todo = tile_filter == nullptr;
 #pragma unroll
   for (int t = 0; t < NW; ++t) {
     const int i = i0 + t;
-    if (i < n_q) pmax = max(pmax, min(qp[i], L_max - 1));
+    if (i < n_q) {
+      const int p = qp[i];
+      pmax = max(pmax, last_slot(p));
+      nmax = max(nmax, p < 0 ? 0 : min(p, L_max - 1) + 1);
+      if (tile_filter != nullptr && tile_filter[(long long)b * n_q + i] == 2) todo = true;
+    }
   }
   const int j_begin = s * span;
-  if (j_begin > pmax) return;
+  if (j_begin > pmax || !todo || nmax <= row_min) return;
   const int j_end = min(j_begin + span, pmax + 1);
 
   const int i = i0 + wave;
   const bool valid = i < n_q;
   const long long row = (long long)b * n_q + (valid ? i : 0);
-  const int lim = valid ? min(min(qp[i], L_max - 1) + 1, j_end) : 0;
+  const int lim = valid ? min(last_slot(qp[i]) + 1, j_end) : 0;
   const __amdgpu_buffer_rsrc_t row_rsrc =
       __builtin_amdgcn_make_buffer_rsrc(scores + row * ld, (short)0, lim * 4, BUF_RSRC_WORD3);
 
   v4i A[MT][KS];
   int wt[MT][4];
   load_query<D, MT>(q_idx, w, w_per_query, row, H_I, valid, A, wt);
+  // SEL: this wave's row kind and threshold (a table row, or an invalid query, keeps
+  // the plain stores)
+  bool list_row = false;
+  int th = 0;
+  if constexpr (SEL) {
+    list_row = valid && thr.rstate[row] == 0;
+    th = thr.theta[row];
+  }
+  int wn = 0;  // SEL: candidates in this wave's LDS buffer (wave-uniform)
+  auto flush = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&thr.cnt[row], wn);
+    base = __shfl(base, 0);
+    int32_t* lsl = thr.lslot + row * thr.cap;
+    int32_t* lsc = thr.lscore + row * thr.cap;
+    for (int e = lane; e < wn; e += 64) {
+      if (base + e < thr.cap) {
+        lsl[base + e] = wb_slot[wave][e];
+        lsc[base + e] = wb_score[wave][e];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wn = 0;
+  };
 
   const int8_t* kb = k_idx + (long long)b * L_max * D;
   const int n_tiles = (j_end - j_begin + KT - 1) / KT;
+  const int smax = (L_max - 1) / stride;  // last slot with a key
   // thread -> (row, chunk) of the key tile; with fewer chunks than threads the extra
   // threads repeat a chunk and write the same bytes to the same place
   const int cid = tid % (KT * CH), cr = cid / CH, cc = cid % CH;
   const int tile_off = cr * D + 16 * swz<D>(cr, cc);
   auto gload = [&](int t) -> v4i {
-    const int j = min(j_begin + min(t, n_tiles - 1) * KT + cr, L_max - 1);
-    return *(const v4i*)(kb + (long long)j * D + 16 * cc);
+    const int js = min(j_begin + min(t, n_tiles - 1) * KT + cr, smax);
+    return *(const v4i*)(kb + (long long)js * stride * D + 16 * cc);
   };
   // dot products of the query's heads with the 16 keys of group nt
   auto mfmas = [&](int buf, int nt, v4i (&acc)[MT]) {
@@ -216,11 +265,27 @@ __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
       st[u] = gload(t + R);  // stage u held tile t, already in LDS
       int res = 0;
       if (t < n_tiles) res = compute(buf);
-      __builtin_amdgcn_raw_buffer_store_b32(res, row_rsrc, (j_begin + t * KT + lane) * 4, 0, 0);
+      const int js = j_begin + t * KT + lane;
+      if (!SEL || !list_row) {
+        __builtin_amdgcn_raw_buffer_store_b32(res, row_rsrc, js * 4, 0, 0);
+      } else {
+        const bool pass = js < lim && res >= th;
+        const unsigned long long bal = __ballot(pass);
+        if (bal != 0ull) {  // wave-uniform
+          const int r = wn + lanes_below(bal);
+          if (pass) {
+            wb_slot[wave][r] = js;
+            wb_score[wave][r] = res;
+          }
+          wn += __popcll(bal);
+          if (wn > WBUF - 64) flush();
+        }
+      }
       *(v4i*)(&tile[buf ^ 1][tile_off]) = st[(u + 1) % R];  // tile t+1
       __syncthreads();
     }
   }
+  if (SEL && list_row && wn > 0) flush();
 }
 
 // ---------------------------------------------------------------------------------
@@ -806,12 +871,23 @@ __global__ __launch_bounds__(256, 2) void blk_scores_kernel(
 template <int D, int MT>
 static hipError_t launch_flat_t(const IdxArgs& a, hipStream_t st) {
   constexpr int NW = 8;  // queries (= waves) per workgroup
+  const int stride = a.stride > 1 ? a.stride : 1;
   const int n_qtiles = (a.n_q + NW - 1) / NW;
-  const int n_spans = (a.L_max + a.span - 1) / a.span;
+  const int n_slots = (a.L_max - 1) / stride + 1;
+  const int n_spans = (n_slots + a.span - 1) / a.span;
   dim3 grid((unsigned)(n_qtiles * n_spans), (unsigned)a.B);
-  hipLaunchKernelGGL((idx_flat_kernel<D, MT, NW>), grid, dim3(64 * NW), 0, st, a.q_idx, a.k_idx, a.w,
-                     a.w_per_query, a.q_pos, a.n_q, a.L_max, a.H_I, a.span, n_spans, n_qtiles,
-                     a.scores, (long long)a.ld);
+  if (a.thr.theta != nullptr) {
+    if (a.thr.rstate == nullptr || a.thr.cnt == nullptr || a.thr.lslot == nullptr || a.thr.lscore == nullptr ||
+        a.thr.cap < 1)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL((idx_flat_kernel<D, MT, NW, true>), grid, dim3(64 * NW), 0, st, a.q_idx, a.k_idx, a.w,
+                       a.w_per_query, a.q_pos, a.n_q, a.L_max, a.H_I, a.span, n_spans, n_qtiles, a.scores,
+                       (long long)a.ld, stride, a.tile_filter, a.row_min, a.thr);
+  } else {
+    hipLaunchKernelGGL((idx_flat_kernel<D, MT, NW, false>), grid, dim3(64 * NW), 0, st, a.q_idx, a.k_idx, a.w,
+                       a.w_per_query, a.q_pos, a.n_q, a.L_max, a.H_I, a.span, n_spans, n_qtiles, a.scores,
+                       (long long)a.ld, stride, a.tile_filter, a.row_min, a.thr);
+  }
   return hipGetLastError();
 }
 template <int D, int MT, bool KEPT>

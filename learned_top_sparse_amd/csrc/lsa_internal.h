@@ -6,6 +6,22 @@
 
 namespace lsa {
 
+// Thresholded selection of flat rows (prefill): each row's threshold and state, and
+// its candidate list, in the workspace lsa_forward carves out.
+//   rstate: 0 = list row (its entries with score >= theta are appended to its list),
+//           1 = table row (short row: its scores go to the score table),
+//           2 = list row whose list fell short of k or overflowed cap (the score
+//               table path redoes it).
+struct ThrArgs {
+  const int32_t* theta;
+  int32_t* rstate;
+  int32_t* cnt;     // entries appended to the row's list (may exceed cap)
+  int32_t* lslot;   // [rows][cap]
+  int32_t* lscore;  // [rows][cap]
+  int cap;
+  int row_min;      // rows of at most row_min keys keep the score table
+};
+
 struct IdxArgs {
   const int8_t* q_idx;
   const int8_t* k_idx;
@@ -26,6 +42,11 @@ struct IdxArgs {
   long long sel_rec_ints;
   int sel_parts, sel_lcap;
   int k_top;
+  // flat, many queries (idx_flat_kernel):
+  int stride;                  // slot j scores key j * stride (0 or 1: every key)
+  ThrArgs thr;                 // thr.theta != nullptr: append candidates instead of writing the table
+  const int32_t* tile_filter;  // optional: only query tiles holding a row of state 2
+  int row_min;                 // only query tiles holding a row of more than row_min keys (0: all)
 };
 
 struct BlkArgs {
@@ -52,6 +73,7 @@ struct TopkArgs {
   void* ws;          // optional: enables the several-workgroups-per-row path
   size_t ws_bytes;
   bool hist_ready;   // the indexer built the rows' selection state in ws (dec_sel_layout)
+  const int32_t* row_state;  // optional (flat): only rows whose state (ThrArgs) is not 0
 };
 
 struct BlkSelArgs {
@@ -103,5 +125,29 @@ bool dec_sel_layout(long long rows, int L_max, int k, DecLayout* out);
 // rows of the same L_max and k never needs more per row
 size_t dec_sel_ws_bytes(long long rows, int L_max, int k);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
+
+// Thresholded selection of flat rows (prefill rows longer than thr_cap(k) keys): a
+// sample of every thr_stride(k)-th key gives each row a threshold that about 2k of
+// its entries reach -- about THR_ABOVE samples lie above it, so the count is known to
+// +-1/sqrt(THR_ABOVE) -- the scan appends those entries to the row's list (at most
+// thr_cap(k)); the exact top-k is taken from the list, and rows whose list fell short
+// of k or overflowed go through the score table.
+constexpr int THR_ABOVE = 64;       // sampled entries expected above a row's threshold
+constexpr int THR_MAX_K = 2048;     // list rows hold at most 4 * 2048 entries (LDS of the list top-k)
+constexpr int THR_MAX_L = 524288;   // the list top-k's slot bitmap (64 KB)
+inline int thr_cap(int k) { return 4 * k; }
+// Rows of at most 8k keys keep the score table: below that the table's round trip
+// costs less than the sample, the list and its selection (measured on MI355X: rows of
+// 8K..16K keys at k = 2048 ran 7 % slower through lists, rows past 24K keys faster).
+inline int thr_row_min(int k) { return 8 * k; }
+// 2k entries above the threshold for THR_ABOVE samples: one sample per 2k / THR_ABOVE keys
+inline int thr_stride(int k) { return k * 2 / THR_ABOVE > 1 ? k * 2 / THR_ABOVE : 1; }
+// modes of launch_thresholds: 0 sampled quantile; 1 threshold above every score (all
+// list rows fall short); 2 threshold below every score (list rows overflow)
+hipError_t launch_thresholds(const int32_t* samp, long long ld_s, const int32_t* q_pos, long long rows, int L_max,
+                             int k, int stride, int mode, const ThrArgs& t, hipStream_t st);
+// exact top-k of the list rows; marks rows whose list fell short or overflowed (state 2)
+hipError_t launch_list_topk(const int32_t* q_pos, long long rows, int L_max, int k, const ThrArgs& t,
+                            int32_t* idx, int32_t* count, hipStream_t st);
 
 }  // namespace lsa

@@ -504,7 +504,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(const int32_t* __restrict__ sc
                                                   const int32_t* __restrict__ q_pos,
                                                   const int32_t* __restrict__ kept, int bs, int n_keep,
                                                   int L_max, int k, int32_t* __restrict__ idx,
-                                                  int32_t* __restrict__ count) {
+                                                  int32_t* __restrict__ count,
+                                                  const int32_t* __restrict__ row_state) {
   constexpr int NW = NT / 64;
   constexpr int VG = 4;  // groups of 4 slots per thread per pass
   __shared__ int lds_big[NBINS];  // histogram, then the candidate list (slots | scores)
@@ -515,6 +516,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const int32_t* __restrict__ sc
   __shared__ int sh[8];
 
   const long long row = blockIdx.x;
+  if (row_state != nullptr && row_state[row] == 0) return;  // selected from its candidate list
   int32_t* out = idx + row * (long long)k;
   int n_valid;
   const RowView<KEPT> rv = make_row<NT, KEPT>(scores, ld, q_pos, kept, bs, n_keep, L_max, row, kept_s, scan_tmp, &n_valid);
@@ -1042,6 +1044,270 @@ __global__ __launch_bounds__(NT) void topk_list_finish_kernel(int32_t* __restric
   }
 }
 
+// Threshold of each flat row for the thresholded selection (one workgroup per row).
+// A row of at most t.row_min keys keeps the score table (state 1).  Otherwise its
+// threshold is the t-th best of its m sampled scores (keys 0, stride, 2*stride, ... up
+// to the query position), t = ceil(2k * m / n_valid) (at most m), so about 2k entries
+// of the row are expected to reach it; the selection stays exact whatever the sample
+// shows (rows that fall short of k or overflow take the table path).
+template <int NT>
+__global__ __launch_bounds__(NT) void thr_kernel(const int32_t* __restrict__ samp, long long ld_s,
+                                                 const int32_t* __restrict__ q_pos, int L_max, int k, int stride,
+                                                 int mode, ThrArgs t) {
+  constexpr int NW = NT / 64;
+  __shared__ int scan_tmp[NW + 1];
+  __shared__ int h256[256];
+  __shared__ int sh[8];
+  const long long row = blockIdx.x;
+  const int p = min(q_pos[row], L_max - 1);
+  const int n_valid = max(p + 1, 0);
+  int32_t* theta = const_cast<int32_t*>(t.theta);
+  if (n_valid <= t.row_min) {
+    if (threadIdx.x == 0) {
+      theta[row] = INT_MIN;
+      t.rstate[row] = 1;
+      t.cnt[row] = 0;
+    }
+    return;
+  }
+  int th;
+  if (mode == 1) {
+    th = INT_MAX;
+  } else if (mode == 2) {
+    th = INT_MIN;
+  } else {
+    const int m = p / stride + 1;
+    const long long tt = (2LL * k * m + n_valid - 1) / n_valid;
+    const int need = (int)min<long long>(m, max<long long>(1, tt));
+    const int32_t* srow = samp + row * ld_s;
+    int need_eq;
+    const unsigned T = radix_select32<NT, 4>(
+        m, need, h256, scan_tmp, sh,
+        [&](int pos, int& sc) {
+          sc = srow[pos];
+          return true;
+        },
+        &need_eq);
+    th = (int)(T ^ 0x80000000u);
+  }
+  if (threadIdx.x == 0) {
+    theta[row] = th;
+    t.rstate[row] = 0;
+    t.cnt[row] = 0;
+  }
+}
+
+// The need-th largest of the 64-bit keys kv[j][c] with bit 4j+c of take[j / 8] set
+// (1 <= need <= their count), exactly, by the whole workgroup: 8-bit radix passes
+// from the highest bit not fixed by pmask0 (every taken key agrees with pref0 there).
+template <int NT, int J>
+__device__ __forceinline__ unsigned long long block_select_kth64(const unsigned long long (&kv)[J][4],
+                                                                 const unsigned (&take)[(J + 7) / 8], int need,
+                                                                 int* h256, int* scan_tmp, int* sh,
+                                                                 unsigned long long pref0,
+                                                                 unsigned long long pmask0) {
+  static_assert(NT >= 256, "one bucket per thread in the scan");
+  const int hb = pmask0 == ~0ull ? -1 : 63 - __clzll((long long)~pmask0);
+  if (hb < 0) return pref0;
+  int shift = (hb / 8) * 8;
+  unsigned long long pmask = shift + 8 >= 64 ? 0ull : ~((1ull << (shift + 8)) - 1ull);
+  unsigned long long pref = pref0 & pmask;
+  const int t = threadIdx.x;
+  for (; shift >= 0; shift -= 8) {
+    if (t < 256) h256[t] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (((take[j / 8] >> (4 * (j % 8) + c)) & 1u) && (kv[j][c] & pmask) == pref)
+          atomicAdd(&h256[(int)((kv[j][c] >> shift) & 255ull)], 1);
+    __syncthreads();
+    const int cnt = t < 256 ? h256[255 - t] : 0;
+    int tot;
+    const int excl = block_exclusive_scan<NT>(cnt, scan_tmp, &tot);
+    if (t < 256 && excl < need && excl + cnt >= need) {
+      sh[0] = 255 - t;
+      sh[1] = excl;
+    }
+    __syncthreads();
+    need -= sh[1];
+    pref |= (unsigned long long)sh[0] << shift;
+    pmask |= 255ull << shift;
+    __syncthreads();
+  }
+  return pref;
+}
+
+// Exact top-k of a list row from its candidate list (one workgroup per row): every
+// entry of the row with score >= its threshold is in the list, and there are at
+// least k of them, so the row's top-k by (score desc, slot asc) is the list's.
+// The list stays in registers (thread t holds quads t, t + NT, ...).  One pass builds
+// the coarse-bin histogram and finds the bin b* of the k-th best; the entries of b*
+// are gathered in LDS and one wave finds the cutoff among them (the whole workgroup
+// when b* holds more than TMAX, i.e. heavy ties); the taken entries are marked in a
+// bitmap of the row's slots (sharing the histogram's LDS) and written in ascending
+// order.  A list that fell short of k or overflowed marks its row for the score table.
+// Dynamic LDS: max(NBINS, ceil(L_max / 32)) ints.
+template <int NT, int J>
+__global__ __launch_bounds__(NT) void list_topk_kernel(const int32_t* __restrict__ q_pos, int L_max, int k,
+                                                       ThrArgs t, int32_t* __restrict__ idx,
+                                                       int32_t* __restrict__ count) {
+  constexpr int NW = NT / 64;
+  constexpr int TMAX = 512;
+  constexpr int JW = (J + 7) / 8;
+  extern __shared__ int lds_dyn[];
+  __shared__ int tb_score[TMAX], tb_slot[TMAX];
+  __shared__ int scan_tmp[NW + 1];
+  __shared__ int h256[256];
+  __shared__ int sh[8];
+  __shared__ int tb_n;
+  int* hist = lds_dyn;
+  unsigned* bm = reinterpret_cast<unsigned*>(lds_dyn);
+  const long long row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (t.rstate[row] != 0) return;
+  const int n_valid = max(min(q_pos[row], L_max - 1) + 1, 0);
+  const int c = t.cnt[row];
+  if (c < k || c > t.cap) {
+    if (tid == 0) t.rstate[row] = 2;
+    return;
+  }
+  int32_t* out = idx + row * (long long)k;
+  if (count != nullptr && tid == 0) count[row] = k;  // a list row has more than cap >= k keys
+  // the list: cap is a multiple of 4, so each row's arrays are 16-byte aligned
+  const int32_t* lsl = t.lslot + row * t.cap;
+  const int32_t* lsc = t.lscore + row * t.cap;
+  v4i sc[J], sl[J];
+  unsigned valid[JW];
+#pragma unroll
+  for (int w = 0; w < JW; ++w) valid[w] = 0u;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e0 = 4 * (tid + NT * j);
+    if (e0 < c) {
+      sc[j] = *reinterpret_cast<const v4i*>(lsc + e0);
+      sl[j] = *reinterpret_cast<const v4i*>(lsl + e0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) valid[j / 8] |= (e0 + q < c ? 1u : 0u) << (4 * (j % 8) + q);
+    } else {
+      sc[j] = v4i{0, 0, 0, 0};
+      sl[j] = v4i{0, 0, 0, 0};
+    }
+  }
+  auto is_valid = [&](int j, int q) { return ((valid[j / 8] >> (4 * (j % 8) + q)) & 1u) != 0u; };
+  for (int b = tid; b < NBINS; b += NT) hist[b] = 0;
+  if (tid == 0) tb_n = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (is_valid(j, q)) atomicAdd(&hist[coarse_bin(sc[j][q])], 1);
+  __syncthreads();
+  find_cut_bin<NT>(hist, k, scan_tmp, sh);
+  const int bstar = sh[4], above = sh[5], n_star = sh[6];
+  const int need = k - above;  // 1 <= need <= n_star
+  unsigned long long kpref;
+  const unsigned long long kmask = bin_key_prefix(bstar, &kpref);
+  auto key_of = [](int score, int slot) {
+    return ((unsigned long long)okey(score) << 32) | (0xFFFFFFFFu - (unsigned)slot);
+  };
+  unsigned long long cut;
+  if (n_star <= TMAX) {
+    // gather b* (any order): a prefix sum over the wave's lanes, one LDS atomic a wave
+    unsigned in[JW];
+    int cnt = 0;
+#pragma unroll
+    for (int w = 0; w < JW; ++w) in[w] = 0u;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (is_valid(j, q) && coarse_bin(sc[j][q]) == bstar) {
+          in[j / 8] |= 1u << (4 * (j % 8) + q);
+          ++cnt;
+        }
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    int wb = 0;
+    if (lane == 63 && incl > 0) wb = atomicAdd(&tb_n, incl);
+    int i = __shfl(wb, 63) + incl - cnt;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if ((in[j / 8] >> (4 * (j % 8) + q)) & 1u) {
+          tb_score[i] = sc[j][q];
+          tb_slot[i] = sl[j][q];
+          ++i;
+        }
+    __syncthreads();
+    if (tid < 64) {
+      const auto key = [&](int e) { return key_of(tb_score[e], tb_slot[e]); };
+      const unsigned long long r = n_star <= 256 ? wave_select_kth<4>(n_star, need, key, h256, kpref, kmask)
+                                                 : wave_select_kth<TMAX / 64>(n_star, need, key, h256, kpref, kmask);
+      if (tid == 0) {
+        sh[0] = (int)(unsigned)(r >> 32);
+        sh[1] = (int)(unsigned)r;
+      }
+    }
+    __syncthreads();
+    cut = ((unsigned long long)(unsigned)sh[0] << 32) | (unsigned)sh[1];
+  } else {
+    // heavy ties: the keys of b* stay in registers for a workgroup-wide radix select
+    unsigned long long kv[J][4];
+    unsigned in[JW];
+#pragma unroll
+    for (int w = 0; w < JW; ++w) in[w] = 0u;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        kv[j][q] = key_of(sc[j][q], sl[j][q]);
+        if (is_valid(j, q) && coarse_bin(sc[j][q]) == bstar) in[j / 8] |= 1u << (4 * (j % 8) + q);
+      }
+    cut = block_select_kth64<NT, J>(kv, in, need, h256, scan_tmp, sh, kpref, kmask);
+  }
+  // the taken entries (key >= cut; exactly k of them) into the bitmap of slots
+  const int nw = (n_valid + 31) / 32;
+  for (int wd = tid; wd < nw; wd += NT) bm[wd] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (is_valid(j, q) && key_of(sc[j][q], sl[j][q]) >= cut) {
+        const int s = sl[j][q];
+        atomicOr(&bm[s >> 5], 1u << (s & 31));
+      }
+  __syncthreads();
+  // ascending output: thread tid takes words [tid * WPT, tid * WPT + WPT)
+  const int WPT = (nw + NT - 1) / NT;
+  int my = 0;
+  for (int i = 0; i < WPT; ++i) {
+    const int wd = tid * WPT + i;
+    if (wd < nw) my += __popc(bm[wd]);
+  }
+  int tot;
+  int r = block_exclusive_scan<NT>(my, scan_tmp, &tot);
+  for (int i = 0; i < WPT; ++i) {
+    const int wd = tid * WPT + i;
+    if (wd >= nw) break;
+    unsigned m = bm[wd];
+    while (m) {
+      const int bit = __ffs(m) - 1;
+      m &= m - 1;
+      if (r < k) out[r] = wd * 32 + bit;
+      ++r;
+    }
+  }
+}
+
 // Block keep of the two-stage indexer: own block + the best n_keep-1 earlier blocks
 // by (int64 score desc, block asc), ascending, -1 padded.
 template <int NT>
@@ -1232,7 +1498,7 @@ static hipError_t launch_topk_t(const TopkArgs& a, hipStream_t st, long long row
     return hipGetLastError();
   }
   SegWs w;
-  if (!KEPT && split_rows(a, &w)) {
+  if (!KEPT && a.row_state == nullptr && split_rows(a, &w)) {
     // several workgroups per row: histogram and candidate compaction split over segments
     const dim3 grid((unsigned)w.n_seg, (unsigned)rows);
     hipLaunchKernelGGL(topk_seg_zero_kernel, dim3(8, (unsigned)rows), dim3(256), 0, st, w.base, w.row_ints(), rows);
@@ -1246,11 +1512,32 @@ static hipError_t launch_topk_t(const TopkArgs& a, hipStream_t st, long long row
   }
   if (rows <= 1024 && a.L_max >= 16384) {
     hipLaunchKernelGGL((topk_kernel<1024, KEPT>), dim3((unsigned)rows), dim3(1024), 0, st, a.scores, a.ld, a.q_pos,
-                       a.kept, a.block_size, a.n_keep, a.L_max, a.k, a.idx, a.count);
+                       a.kept, a.block_size, a.n_keep, a.L_max, a.k, a.idx, a.count, a.row_state);
   } else {
     hipLaunchKernelGGL((topk_kernel<256, KEPT>), dim3((unsigned)rows), dim3(256), 0, st, a.scores, a.ld, a.q_pos,
-                       a.kept, a.block_size, a.n_keep, a.L_max, a.k, a.idx, a.count);
+                       a.kept, a.block_size, a.n_keep, a.L_max, a.k, a.idx, a.count, a.row_state);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_thresholds(const int32_t* samp, long long ld_s, const int32_t* q_pos, long long rows, int L_max,
+                             int k, int stride, int mode, const ThrArgs& t, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if (k < 1 || k > THR_MAX_K || t.cap != thr_cap(k) || t.row_min < t.cap || L_max > THR_MAX_L || stride < 1)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(thr_kernel<256>, dim3((unsigned)rows), dim3(256), 0, st, samp, ld_s, q_pos, L_max, k, stride,
+                     mode, t);
+  return hipGetLastError();
+}
+
+hipError_t launch_list_topk(const int32_t* q_pos, long long rows, int L_max, int k, const ThrArgs& t,
+                            int32_t* idx, int32_t* count, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if (k < 1 || k > THR_MAX_K || t.cap != thr_cap(k) || L_max > THR_MAX_L) return hipErrorInvalidValue;
+  constexpr int NT = 256, J = 4 * THR_MAX_K / (4 * NT);  // J quads a thread hold the longest list
+  const size_t dyn = (size_t)max(NBINS, (L_max + 31) / 32) * sizeof(int);
+  hipLaunchKernelGGL((list_topk_kernel<NT, J>), dim3((unsigned)rows), dim3(NT), dyn, st, q_pos, L_max, k, t, idx,
+                     count);
   return hipGetLastError();
 }
 

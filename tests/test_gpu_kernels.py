@@ -376,6 +376,44 @@ def test_forward_chunking_identical(lsa, chunk_rows):
     assert torch.equal(ref["out"], res["out"])
 
 
+@pytest.mark.parametrize("kind", ["random", "zero_queries", "concentrated"])
+def test_forward_thresholded_selection_modes(lsa, kind):
+    """Flat prefill rows longer than 8k keys take the thresholded selection (a threshold
+    from sampled scores, candidate lists, the exact top-k from the lists, the score table
+    for lists that fall short or overflow).  Every mode gives the score table's lists,
+    counts and outputs bit for bit, and the oracle's on sampled rows: auto; every
+    thresholded row forced to fall short; forced to overflow.  Rows up to 4096 keys
+    (the score table) mix in, the 4097-key row is the shortest list row; half the queries all-zero (every score 0: the lists
+    overflow); or every query's best keys in one 600-key window."""
+    k = 512
+    wl = synthetic.Workload("thr", B=2, n_q=96, L=24000, q_pos0=0, H_I=64, d_I=128, k=k, H_q=16)
+    pos = np.linspace(0, 23999, 96).astype(np.int64)
+    pos[:8] = [0, 300, 511, 512, 2047, 2048, 4095, 4096]
+    inp, _ = _inputs(wl, seed=21, pos=np.tile(pos, 2))
+    if kind == "zero_queries":
+        inp["q_idx"][:, ::2] = 0
+    elif kind == "concentrated":
+        gen = torch.Generator().manual_seed(8)
+        vdir = torch.randint(-64, 65, (128,), generator=gen, dtype=torch.int64)
+        inp["q_idx"][:, :, 0, :] = vdir.to(torch.int8)
+        noise = torch.randint(-3, 4, (600, 128), generator=gen, dtype=torch.int64)
+        inp["k_idx"][:, 5000:5600] = (vdir + noise).clamp(-128, 127).to(torch.int8)
+    g = {kk: v.to(dev()) for kk, v in inp.items()}
+    ws = lsa.lsa_forward_workspace_size(g, k)
+    assert lsa.lsa_forward_stages(g, k, ws)[0] == "sample"
+    ref = lsa.lsa_forward(g, k_top=k, select="table", attn_split=1)
+    for mode in ("auto", "force_short", "force_overflow"):
+        res = lsa.lsa_forward(g, k_top=k, select=mode, attn_split=1)
+        assert torch.equal(res["idx"], ref["idx"]), f"{kind} {mode}"
+        assert torch.equal(res["count"], ref["count"]), f"{kind} {mode}"
+        assert torch.equal(res["out"], ref["out"]), f"{kind} {mode}"
+    rows = [(0, 0), (0, 3), (0, 6), (0, 7), (1, 50), (1, 95)]
+    want = _flat_oracle_rows(inp, k, with_attn=False, rows=rows)
+    J = ref["idx"].cpu().numpy()
+    for (b, i), r in want.items():
+        assert np.array_equal(J[b, i], r["J"]), f"{kind} row {(b, i)}"
+
+
 def test_forward_decode_small(lsa):
     wl = synthetic.Workload("dec", B=5, n_q=1, L=9000, q_pos0=8999, H_I=64, d_I=128, k=512, H_q=16)
     inp, g = _inputs(wl, seed=5)

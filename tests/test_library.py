@@ -74,16 +74,25 @@ def test_forward_stages_listing():
     inp = _fake_inputs(8, 1, 20000)
     ws = lsa.lsa_forward_workspace_size(inp, 2048)
     assert lsa.lsa_forward_stages(inp, 2048, ws) == ["index_select", "topk", "sparse_attn"]
-    # ten queries in chunks of eight: the score table for the first chunk, the decode
-    # selection for the last two queries (their state fits the chunk's top-k workspace)
+    # ten queries in chunks of eight: the thresholded selection for the first chunk (rows
+    # may be longer than 8k keys), the decode selection for the last two queries
     inp = _fake_inputs(1, 10, 40000)
     ws = lsa.lsa_forward_workspace_size(inp, 2048, chunk_rows=8)
     assert lsa.lsa_forward_stages(inp, 2048, ws, chunk_rows=8) == [
+        "sample", "index_select", "topk", "sparse_attn", "index_select", "topk", "sparse_attn"]
+    # ... and with the score table asked for, the table for the first chunk
+    ws = lsa.lsa_forward_workspace_size(inp, 2048, chunk_rows=8, select="table")
+    assert lsa.lsa_forward_stages(inp, 2048, ws, chunk_rows=8, select="table") == [
         "index_scores", "topk", "sparse_attn", "index_select", "topk", "sparse_attn"]
-    # prefill in three chunks
-    inp = _fake_inputs(1, 3000, 4096)
+    # rows no longer than 8k keys keep the score table
+    inp = _fake_inputs(1, 64, 16384)
+    ws = lsa.lsa_forward_workspace_size(inp, 2048)
+    assert lsa.lsa_forward_stages(inp, 2048, ws) == ["index_scores", "topk", "sparse_attn"]
+    # prefill in three chunks (rows up to 8192 keys, k = 512: thresholded selection)
+    inp = _fake_inputs(1, 3000, 8192)
     ws = lsa.lsa_forward_workspace_size(inp, 512, chunk_rows=1000)
-    assert lsa.lsa_forward_stages(inp, 512, ws, chunk_rows=1000) == ["index_scores", "topk", "sparse_attn"] * 3
+    assert lsa.lsa_forward_stages(inp, 512, ws, chunk_rows=1000) == [
+        "sample", "index_select", "topk", "sparse_attn"] * 3
     # two-stage: block representatives once, then four stages per chunk
     inp = _fake_inputs(1, 512, 8192)
     ws = lsa.lsa_forward_workspace_size(inp, 512, two_stage=True, chunk_rows=256)
