@@ -40,6 +40,8 @@ def _describe(wl):
          f"attention {wl.H_q} bf16 query heads / 1 KV head d={wl.d}")
     if wl.two_stage:
         s += f", two-stage blocks of {wl.block_size} keep {wl.n_keep}"
+    if wl.page_size:
+        s += f", paged caches (pages of {wl.page_size} tokens in a shared pool, {wl.spare_pages} spare pages)"
     return s
 
 
@@ -314,6 +316,16 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, inp)
+    del inp, step
+    torch.cuda.empty_cache()
+
+    # ---- the same decode step over paged caches
+    wpg = synthetic.WORKLOADS["decode_128k_paged"]
+    inp, step, ms_g = measure(lsa, torch, wpg, args.steps, args.warmup)
+    res["decode_128k_paged"] = {
+        "workload": _describe(wpg), "value": wpg.B * wpg.n_q / (ms_g * 1e-3), "unit": "tok/s",
+        "ms_per_step": ms_g, "kernel_ms": step.kernel_ms(),
+    }
     del inp, step
     torch.cuda.empty_cache()
 

@@ -219,7 +219,7 @@ typedef struct lsa_forward_args {
   void* const* stage_events;
   int32_t n_stage_events;
   /* Selection of flat rows of at least 8 queries per sequence (prefill):
-     LSA_SELECT_AUTO (0): rows longer than 4*k_top keys (k_top <= 2048, L_max <= 524288)
+     LSA_SELECT_AUTO (0): rows longer than 8*k_top keys (k_top <= 2048, L_max <= 524288)
        take the thresholded selection -- a sample of every row's keys gives it a
        threshold, the indexer keeps only the entries that reach it, and the exact
        top-k is taken from those; a row whose kept entries fall short of k_top or
@@ -230,6 +230,25 @@ typedef struct lsa_forward_args {
        thresholded row's threshold is set above (below) all of its scores, so every
        such row takes the fallback -- for testing that path. */
   int32_t select_mode;
+  /* Paged caches (serving-style decode; [LSA] App. F.1 "Attention kernels": the index
+     list is read like a page table).  page_table != NULL: k_idx, k and v are pools of
+     n_slots rows shared by all sequences (int8 [n_slots, d_I], bf16 [n_slots, d]),
+     and logical key j of sequence b is pool row
+         page_table[b * max_pages + j / page_size] * page_size + j % page_size.
+     L_max must equal max_pages * page_size; page_size is a power of two >= 64 and
+     n_slots a multiple of it (at most 2^31).  Page ids outside [0, n_slots / page_size)
+     are clamped into that range (no fault; the result is then unspecified).  Selection
+     runs on logical keys (ties: lower logical index) and idx receives the pool rows of
+     the kept keys, in ascending logical order, -1 padded.  Supported for flat calls of
+     fewer than 8 queries per sequence (n_q < 8, two_stage = 0), else
+     LSA_ERR_UNSUPPORTED; a workspace too small for their selection state gives
+     LSA_ERR_WORKSPACE.  Sequences of different lengths share a call through q_pos;
+     with L_max fixed (one per range of context lengths) the launches keep one shape,
+     so a captured HIP graph replays for any positions and page tables.
+     page_table == NULL: contiguous caches [B, L_max, ...]. */
+  const int32_t* page_table;  /* int32 [B, max_pages] */
+  int32_t page_size, max_pages;
+  int64_t n_slots;
 } lsa_forward_args;
 enum { LSA_SELECT_AUTO = 0, LSA_SELECT_TABLE = 1, LSA_SELECT_FORCE_SHORT = 2, LSA_SELECT_FORCE_OVERFLOW = 3 };
 

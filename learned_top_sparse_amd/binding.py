@@ -49,6 +49,7 @@ class ForwardArgs(C.Structure):
         ("idx", P), ("count", P), ("out", P), ("lse", P), ("kept_blocks", P),
         ("stage_events", P), ("n_stage_events", I32),
         ("select_mode", I32),
+        ("page_table", P), ("page_size", I32), ("max_pages", I32), ("n_slots", I64),
     ]
 
 
@@ -252,7 +253,13 @@ def _forward_args(inp: dict, k_top: int, two_stage: bool, block_size: int, n_kee
     q_idx, k_idx, w, q_pos, q, k, v = (inp[n] for n in ("q_idx", "k_idx", "w", "q_pos", "q", "k", "v"))
     B, n_q, H_I, d_I = q_idx.shape
     _, _, H_q, d = q.shape
-    L = k_idx.shape[1]
+    pt = inp.get("page_table")
+    if pt is not None:
+        # paged caches: k_idx / k / v are pools [n_slots, .], keys reach them through pt
+        page_size = int(inp["page_size"])
+        L = pt.shape[1] * page_size
+    else:
+        L = k_idx.shape[1]
     a = ForwardArgs()
     a.mode = 1 if (n_q == 1 and B > 1) else 0
     a.two_stage = 1 if two_stage else 0
@@ -270,8 +277,13 @@ def _forward_args(inp: dict, k_top: int, two_stage: bool, block_size: int, n_kee
     a.lse = out["lse"].data_ptr() if out.get("lse") is not None else None
     a.kept_blocks = out["kept"].data_ptr() if out.get("kept") is not None else None
     if select not in SELECT_MODES:
-        raise LsaError(f"select must be one of {sorted(SELECT_MODES)}")
+        raise ValueError(f"select must be one of {sorted(SELECT_MODES)}")
     a.select_mode = SELECT_MODES[select]
+    if pt is not None:
+        a.page_table = pt.data_ptr()
+        a.page_size = page_size
+        a.max_pages = pt.shape[1]
+        a.n_slots = k_idx.shape[0]
     return a
 
 
@@ -312,6 +324,8 @@ def lsa_forward(inp: dict, k_top: int, two_stage: bool = False, block_size: int 
                 out: Optional[dict] = None, ws: Optional[torch.Tensor] = None, stage_events=None,
                 select: str = "auto") -> dict:
     """The whole path.  ``inp`` holds q_idx, k_idx, w, q_pos, q, k, v (device tensors).
+    Paged caches: ``inp`` also holds page_table (int32 [B, max_pages]) and page_size;
+    k_idx, k and v are then pools [n_slots, .] and idx receives pool rows.
     Returns dict(idx, count, out, lse[, kept]); pass ``out`` / ``ws`` to reuse buffers.
     ``stage_events``: optional torch.cuda.Event list (1 + len(lsa_forward_stages(...)));
     each must have been recorded once (so its HIP event exists)."""
@@ -320,6 +334,8 @@ def lsa_forward(inp: dict, k_top: int, two_stage: bool = False, block_size: int 
     for name, dt in (("q_idx", torch.int8), ("k_idx", torch.int8), ("w", torch.int32), ("q_pos", torch.int32),
                      ("q", torch.bfloat16), ("k", torch.bfloat16), ("v", torch.bfloat16)):
         _need(inp[name], name, dt, dev)
+    if inp.get("page_table") is not None:
+        _need(inp["page_table"], "page_table", torch.int32, dev)
     B, n_q = q_idx.shape[:2]
     H_q = q.shape[2]
     if out is None:

@@ -253,8 +253,9 @@ LSA_API lsa_status lsa_sparse_attn_workspace_size(int32_t B, int32_t n_q, int32_
 
 static lsa_status run_attn(const void* q, const void* k, const void* v, const int32_t* idx, int32_t B, int32_t n_q,
                            int32_t L_max, int32_t H_q, int32_t d, int32_t k_top, float scale, int split, void* out,
-                           float* lse, void* ws, hipStream_t s) {
+                           float* lse, void* ws, hipStream_t s, long long kv_pool = 0) {
   lsa::AttnArgs a{};
+  a.kv_pool = kv_pool;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -313,10 +314,28 @@ lsa_status check_forward(const lsa_forward_args* a) {
     if (a->block_size < 1 || a->n_keep < 1) return LSA_ERR_INVALID_ARG;
     if (a->block_size > 128 || a->n_keep > 256 || a->L_max / a->block_size > 65536) return LSA_ERR_UNSUPPORTED;
   }
+  if (a->page_table) {
+    if (a->page_size < 64 || (a->page_size & (a->page_size - 1)) != 0 || a->max_pages < 1 ||
+        (long long)a->max_pages * a->page_size != a->L_max || a->n_slots < a->page_size ||
+        a->n_slots % a->page_size != 0 || a->n_slots > (1ll << 31))
+      return LSA_ERR_INVALID_ARG;
+    if (a->two_stage || a->n_q >= 8) return LSA_ERR_UNSUPPORTED;
+  }
   if ((long long)a->B * a->n_q == 0) return LSA_OK;
   if (!a->q_idx || !a->k_idx || !a->w || !a->q_pos || !a->q || !a->k || !a->v || !a->idx || !a->out)
     return LSA_ERR_INVALID_ARG;
   return LSA_OK;
+}
+
+// pages of the chunk whose first sequence is b0 (page_table == nullptr: contiguous caches)
+lsa::Pages chunk_pages(const lsa_forward_args* a, int32_t b0) {
+  lsa::Pages pg{};
+  if (!a->page_table) return pg;
+  pg.page_table = a->page_table + (long long)b0 * a->max_pages;
+  pg.page_log2 = __builtin_ctz((unsigned)a->page_size);
+  pg.max_pages = a->max_pages;
+  pg.n_pages = (int)(a->n_slots / a->page_size);
+  return pg;
 }
 
 // Thresholded selection (the score table only for short rows and fallbacks) applies to
@@ -480,6 +499,14 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
   if (a->stage_events != nullptr &&
       (long long)a->n_stage_events < 1 + (long long)forward_stages(a, p, rows).size())
     return LSA_ERR_INVALID_ARG;
+  if (a->page_table) {
+    // paged caches: every chunk must take the decode selection
+    const size_t tws = topk_ws_for(a, rows);
+    bool fused = true;
+    for_each_chunk(a, rows,
+                   [&](int32_t, int32_t nb, int32_t, int32_t ni) { fused = fused && chunk_fused(a, nb, ni, tws); });
+    if (!fused) return LSA_ERR_WORKSPACE;
+  }
   int32_t n_marked = 0;
   // records the next stage event (if the caller asked for them)
   auto mark = [&]() -> bool {
@@ -551,12 +578,13 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
   auto run_chunk = [&](int32_t b0, int32_t nb, int32_t i0, int32_t ni) -> lsa_status {
     const long long r0 = (long long)b0 * a->n_q + i0;  // first flattened row
     const int8_t* qi = a->q_idx + r0 * H_I * d_I;
-    const int8_t* ki = a->k_idx + (long long)b0 * L * d_I;
+    const bool paged = a->page_table != nullptr;  // caches are pools: no per-sequence offset
+    const int8_t* ki = a->k_idx + (paged ? 0ll : (long long)b0 * L * d_I);
     const int32_t* wq = a->w_per_query ? a->w + r0 * H_I : a->w;
     const int32_t* qp = a->q_pos + r0;
     const char* qq = static_cast<const char*>(a->q) + r0 * H_q * d * 2;
-    const char* kk = static_cast<const char*>(a->k) + (long long)b0 * L * d * 2;
-    const char* vv = static_cast<const char*>(a->v) + (long long)b0 * L * d * 2;
+    const char* kk = static_cast<const char*>(a->k) + (paged ? 0ll : (long long)b0 * L * d * 2);
+    const char* vv = static_cast<const char*>(a->v) + (paged ? 0ll : (long long)b0 * L * d * 2);
     int32_t* ix = a->idx + r0 * kt;
     int32_t* cnt = a->count ? a->count + r0 : nullptr;
     char* oo = static_cast<char*>(a->out) + r0 * H_q * d * 2;
@@ -575,6 +603,7 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
     ia.d_I = d_I;
     ia.scores = sc;
     ia.ld = p.ld;
+    ia.pages = chunk_pages(a, b0);
     if (a->two_stage) {
       int32_t* kout = a->kept_blocks ? a->kept_blocks + r0 * a->n_keep : kept_ws;
       lsa_status st2 = run_prefilter(qi, limbs + (long long)b0 * p.n_blocks * 2 * d_I, wq, a->w_per_query, qp, nb,
@@ -642,9 +671,14 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
       if (lsa::launch_topk(ta, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
     } else {
       if (lsa::launch_index_scores(ia, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
-      if (lsa::launch_topk(ta, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
+      if (lsa::launch_topk(ta, s) != hipSuccess) return LSA_ERR_HIP;
+      // paged caches: the lists' logical keys become pool rows
+      if (paged && lsa::launch_map_slots(ix, (long long)nb * ni, ni, kt, ia.pages, s) != hipSuccess)
+        return LSA_ERR_HIP;
+      if (!mark()) return LSA_ERR_HIP;
     }
-    lsa_status sa = run_attn(qq, kk, vv, ix, nb, ni, L, H_q, d, kt, a->scale, split, oo, ls, attn_ws, s);
+    lsa_status sa = run_attn(qq, kk, vv, ix, nb, ni, L, H_q, d, kt, a->scale, split, oo, ls, attn_ws, s,
+                             paged ? (long long)a->n_slots : 0ll);
     if (sa != LSA_OK) return sa;
     return mark() ? LSA_OK : LSA_ERR_HIP;
   };

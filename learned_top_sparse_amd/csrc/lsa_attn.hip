@@ -80,8 +80,8 @@ constexpr int WAVE_LDS = D * RSD;  // dwords of LDS per wave: the transposed V t
 template <int NW>
 __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const int32_t* __restrict__ idx, int n_q, int L_max, int H_q, int k_top, float scale_log2,
-    int n_split, __bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws) {
+    const int32_t* __restrict__ idx, int n_q, long long kv_rows, long long j_lim, int H_q, int k_top,
+    float scale_log2, int n_split, __bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws) {
   __shared__ __attribute__((aligned(16))) u32 lds[NW * WAVE_LDS];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
@@ -90,8 +90,10 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
   const int split = (int)(unit % n_split);
   const int b = (int)(row / n_q);
   const int32_t* jrow = idx + row * (long long)k_top;
-  const __bf16* kb = k + (long long)b * L_max * D;
-  const __bf16* vb = v + (long long)b * L_max * D;
+  // sequence b's keys: rows [b * kv_rows, b * kv_rows + j_lim) of k and v (paged caches:
+  // kv_rows = 0 and the entries are rows of the shared pool)
+  const __bf16* kb = k + (long long)b * kv_rows * D;
+  const __bf16* vb = v + (long long)b * kv_rows * D;
   u32* vt = lds + wave * WAVE_LDS;
 
   // query heads as B fragments: lane (h = l&15, g) holds d = 32s + 8g .. +8 at step s
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     return Idx{e(base + r16), e(base + 16 + r16), e(base + 2 * r16), e(base + 2 * r16 + 1)};
   };
   auto gather = [&](Idx x, Gat& G) {
-    auto ok = [&](int j) { return j >= 0 && j < L_max; };
+    auto ok = [&](int j) { return j >= 0 && (long long)j < j_lim; };
     G.vA = __ballot(ok(x.jA));
     G.vB = __ballot(ok(x.jB));
     // Entries without a key read the rows of a listed key of this tile instead (row 0
@@ -359,8 +361,9 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
   if (a.n_split < 1 || a.n_split > 64) return hipErrorInvalidValue;  // the merges hold 64 splits
   const long long units = rows * a.n_split;
   hipLaunchKernelGGL((sparse_attn_kernel<ATTN_WAVES>), dim3((unsigned)units), dim3(64 * ATTN_WAVES), 0, st,
-                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.idx, a.n_q, a.L_max, a.H_q,
-                     a.k_top, a.scale * LOG2E, a.n_split, (__bf16*)a.out, a.lse, a.ws);
+                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.idx, a.n_q,
+                     a.kv_pool > 0 ? 0ll : (long long)a.L_max, a.kv_pool > 0 ? a.kv_pool : (long long)a.L_max,
+                     a.H_q, a.k_top, a.scale * LOG2E, a.n_split, (__bf16*)a.out, a.lse, a.ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)rows), dim3(256), 0, st, a.ws, units, a.n_split, a.H_q,

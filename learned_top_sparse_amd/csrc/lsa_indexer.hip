@@ -475,12 +475,15 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
 //     Only plain stores, issued last, which nothing waits for: no device-scope
 //     atomics (several workgroups on different XCDs would contend for the row's
 //     bins) and nothing to clear beforehand.
+//   * PAGED: k_idx is a pool of pages of 2^page_log2 >= 64 keys; the pool pages of
+//     the span are read into LDS once.  A 64-key group (spans start at multiples of
+//     64) lies inside one page, so its loads are those of the contiguous layout.
 // Grid: x = parts, y = B * n_q.
-template <int D, int MT>
+template <int D, int MT, bool PAGED>
 __global__ __launch_bounds__(512, 1) void idx_decode_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
     int w_per_query, const int32_t* __restrict__ q_pos, int n_q, int L_max, int H_I,
-    int32_t* __restrict__ scores, long long ld, DecWs sel, int k_top) {
+    int32_t* __restrict__ scores, long long ld, DecWs sel, int k_top, Pages pg) {
   constexpr int NT = 512, NWV = NT / 64, KS = D / 64, RING = 4;
   static_assert(NGRP <= NT, "one group sum per thread");
   __shared__ __attribute__((aligned(16))) int sbuf[DEC_SPAN_MAX];
@@ -503,7 +506,15 @@ __global__ __launch_bounds__(512, 1) void idx_decode_kernel(
   const int s_begin = part * span, s_end = min(s_begin + span, n_valid);
   if (s_begin >= s_end) return;  // uniform
   const int n_ent = s_end - s_begin;
-  const int8_t* kb = k_idx + (long long)b * L_max * D;
+  const int8_t* kb = k_idx + (PAGED ? 0ll : (long long)b * L_max * D);
+  __shared__ int span_pages[PAGED ? DEC_SPAN_MAX / 64 + 2 : 1];
+  const int pg0 = PAGED ? s_begin >> pg.page_log2 : 0;
+  if constexpr (PAGED) {
+    const int n_pg = ((s_end - 1) >> pg.page_log2) - pg0 + 1;
+    const int32_t* pt = pg.page_table + (long long)b * pg.max_pages + pg0;
+    for (int t = tid; t < n_pg; t += NT) span_pages[t] = min(max(pt[t], 0), pg.n_pages - 1);
+    __syncthreads();
+  }
 
   // Ring of key fragments.  Loads past the span re-read its last key, so every load
   // is unconditional.
@@ -511,9 +522,14 @@ __global__ __launch_bounds__(512, 1) void idx_decode_kernel(
   const int n_groups = (n_ent + 63) / 64;
   auto load_group = [&](int grp, v4i (&Bf)[4][KS]) {
     const int sg = s_begin + 64 * grp;
+    // PAGED: the pool row of key j of this group is (page << page_log2) | (j & mask);
+    // keys clamped to the span's last key stay in the group's page
+    long long prow = 0;
+    if constexpr (PAGED) prow = (long long)span_pages[(min(sg, s_end - 1) >> pg.page_log2) - pg0] << pg.page_log2;
+    const int pmask = PAGED ? (1 << pg.page_log2) - 1 : -1;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const int8_t* kr = kb + (long long)min(sg + 16 * nt + r16, s_end - 1) * D;
+      const int8_t* kr = kb + (prow + (min(sg + 16 * nt + r16, s_end - 1) & pmask)) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
     }
@@ -903,9 +919,19 @@ static hipError_t launch_direct_t(const IdxArgs& a, hipStream_t st) {
     sel.rec_ints = a.sel_rec_ints;
     sel.parts = a.sel_parts;
     sel.lcap = a.sel_lcap;
-    hipLaunchKernelGGL((idx_decode_kernel<D, MT>), dim3((unsigned)a.sel_parts, (unsigned)(a.B * a.n_q)), dim3(512),
-                       0, st, a.q_idx, a.k_idx, a.w, a.w_per_query, a.q_pos, a.n_q, a.L_max, a.H_I, a.scores,
-                       (long long)a.ld, sel, a.k_top);
+    const dim3 grid((unsigned)a.sel_parts, (unsigned)(a.B * a.n_q));
+    if (a.pages.page_table != nullptr) {
+      if (a.pages.page_log2 < 6 || a.pages.page_log2 > 30 || a.pages.n_pages < 1 ||
+          (long long)a.pages.max_pages << a.pages.page_log2 != a.L_max)
+        return hipErrorInvalidValue;
+      hipLaunchKernelGGL((idx_decode_kernel<D, MT, true>), grid, dim3(512), 0, st, a.q_idx, a.k_idx, a.w,
+                         a.w_per_query, a.q_pos, a.n_q, a.L_max, a.H_I, a.scores, (long long)a.ld, sel, a.k_top,
+                         a.pages);
+    } else {
+      hipLaunchKernelGGL((idx_decode_kernel<D, MT, false>), grid, dim3(512), 0, st, a.q_idx, a.k_idx, a.w,
+                         a.w_per_query, a.q_pos, a.n_q, a.L_max, a.H_I, a.scores, (long long)a.ld, sel, a.k_top,
+                         a.pages);
+    }
     return hipGetLastError();
   }
   // flat rows: one span per workgroup, exactly the LDS score buffer
@@ -928,6 +954,9 @@ static hipError_t launch_direct_t(const IdxArgs& a, hipStream_t st) {
   }
 
 hipError_t launch_index_scores(const IdxArgs& a, hipStream_t st) {
+  // paged caches: the decode selection only
+  if (a.pages.page_table != nullptr && (a.kept != nullptr || !a.use_direct || a.sel_base == nullptr))
+    return hipErrorInvalidValue;
   const bool kept = a.kept != nullptr;
   const bool direct = kept || a.use_direct;
   if (a.d_I == 128) {

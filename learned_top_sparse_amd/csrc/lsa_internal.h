@@ -22,6 +22,12 @@ struct ThrArgs {
   int row_min;      // rows of at most row_min keys keep the score table
 };
 
+// Paged caches: pool row of key j of sequence b (page_table == nullptr: contiguous).
+struct Pages {
+  const int32_t* page_table;  // [B, max_pages]
+  int page_log2, max_pages, n_pages;
+};
+
 struct IdxArgs {
   const int8_t* q_idx;
   const int8_t* k_idx;
@@ -47,6 +53,9 @@ struct IdxArgs {
   ThrArgs thr;                 // thr.theta != nullptr: append candidates instead of writing the table
   const int32_t* tile_filter;  // optional: only query tiles holding a row of state 2
   int row_min;                 // only query tiles holding a row of more than row_min keys (0: all)
+  // paged caches (decode selection only): k_idx is a pool of n_pages pages of
+  // 2^page_log2 keys; key j of sequence b is in page page_table[b * max_pages + (j >> page_log2)]
+  Pages pages;
 };
 
 struct BlkArgs {
@@ -95,6 +104,7 @@ struct AttnArgs {
   const void* v;
   const int32_t* idx;
   int B, n_q, L_max, H_q, d, k_top;
+  long long kv_pool;  // > 0: k, v are pools of kv_pool rows and idx holds pool rows
   float scale;
   int n_split;
   void* out;
@@ -110,6 +120,8 @@ hipError_t launch_block_limbs(const int32_t* reps, int B, int n_blocks, int d_I,
 hipError_t launch_block_scores(const BlkArgs& a, hipStream_t st);
 hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+// idx[row][e] (logical key of sequence row / n_q, or -1) -> its pool row, in place
+hipError_t launch_map_slots(int32_t* idx, long long rows, int n_q, int k, const Pages& pg, hipStream_t st);
 // workspace that lets lsa_topk split each row over several workgroups (0 = not used)
 size_t topk_ws_bytes(long long rows, int L_max);
 // Decode selection: the indexer builds each row's selection state (histogram, one

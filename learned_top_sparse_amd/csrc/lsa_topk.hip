@@ -1547,6 +1547,29 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   return a.kept != nullptr ? launch_topk_t<true>(a, st, rows) : launch_topk_t<false>(a, st, rows);
 }
 
+// Paged caches: each entry of the index lists (a logical key of its row's sequence, or
+// -1) becomes the key's pool row, page_table[b][j >> page_log2] << page_log2 | j & mask
+// (page ids clamped to the pool).
+__global__ __launch_bounds__(256) void map_slots_kernel(int32_t* __restrict__ idx, long long n, int n_q, int k,
+                                                        Pages pg) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n) return;
+  const int j = idx[t];
+  if (j < 0) return;
+  const int32_t* pt = pg.page_table + (t / k / n_q) * pg.max_pages;
+  idx[t] = (min(max(pt[j >> pg.page_log2], 0), pg.n_pages - 1) << pg.page_log2) | (j & ((1 << pg.page_log2) - 1));
+}
+
+hipError_t launch_map_slots(int32_t* idx, long long rows, int n_q, int k, const Pages& pg, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if (pg.page_table == nullptr || k < 1 || n_q < 1 || pg.n_pages < 1 ||
+      ((long long)pg.n_pages << pg.page_log2) > (1ll << 31))
+    return hipErrorInvalidValue;
+  const long long n = rows * k;
+  hipLaunchKernelGGL(map_slots_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, idx, n, n_q, k, pg);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st) {
   const long long rows = (long long)a.B * a.n_q;
   if (rows == 0) return hipSuccess;

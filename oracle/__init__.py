@@ -19,4 +19,6 @@ from .lsa_oracle import (  # noqa: F401
     topk,
     sparse_attention,
     forward_row,
+    paged_rows,
+    forward_row_paged,
 )

@@ -19,7 +19,8 @@ Sources (the pages this follows; all under the subject "learned sparse attention
          ranks a higher score first and, at equal score, the lower id first;
          attention does not depend on the order of J_i),
          App. F.1, paragraph "Attention kernels" (J_i is a row of int32 slots
-         padded with -1 when a query has fewer keys).
+         padded with -1 when a query has fewer keys; attention reads the list as
+         a page table -- with paged caches the slots are rows of the cache pool).
   [HISA] theflow.svmpsp.dev related-papers page, summary "HISA: Efficient
          Hierarchical Indexing for Fine-Grained Sparse Attention" (coarse block
          filter, then the original token indexer only inside kept blocks).
@@ -34,6 +35,9 @@ Readings where the pages are silent (each stated at its function):
     included), so |J| = min(k, p+1).
   * J is written in ascending key order and padded with -1.
   * attention: scale 1/sqrt(d), natural-base softmax, no extra mask.
+  * paged caches: logical key j of a sequence is pool row
+    page_table[j // page_size] * page_size + j % page_size; selection ranks
+    logical keys (ties: lower logical index) and J holds the pool rows.
 """
 from __future__ import annotations
 
@@ -191,4 +195,35 @@ def forward_row(q_idx_row, k_idx, w, p: int, k: int, q_row=None, k_cache=None,
         if scale is None:
             scale = 1.0 / np.sqrt(q_row.shape[-1])
         res["out"], res["lse"] = sparse_attention(q_row, k_cache, v_cache, J, scale)
+    return res
+
+
+def paged_rows(page_table_row, n_keys: int, page_size: int) -> np.ndarray:
+    """Pool row of each logical key 0..n_keys-1 of one sequence with paged caches.
+
+    [LSA] App. F.1 "Attention kernels": the index list is read like a page table.
+    Reading: logical key j sits at offset j % page_size of the page named by
+    entry j // page_size of the sequence's page table.
+    """
+    j = np.arange(n_keys, dtype=np.int64)
+    pt = np.asarray(page_table_row, np.int64)
+    return pt[j // page_size] * page_size + j % page_size
+
+
+def forward_row_paged(q_idx_row, k_idx_pool, w, p: int, k: int, page_table_row, page_size: int,
+                      q_row=None, k_pool=None, v_pool=None, scale: float | None = None):
+    """The flat path for one query row of a sequence whose caches are paged.
+
+    The sequence's logical caches are the pool rows its page table names
+    (paged_rows); scores, top-k and attention are those of forward_row on them,
+    and J then names the pool rows of the chosen logical keys (ascending logical
+    order, -1 padded).  J_logical keeps the logical keys.
+    """
+    rows = paged_rows(page_table_row, len(page_table_row) * page_size, page_size)
+    res = forward_row(q_idx_row, np.asarray(k_idx_pool)[rows], w, p, k, q_row=q_row,
+                      k_cache=None if k_pool is None else np.asarray(k_pool)[rows],
+                      v_cache=None if v_pool is None else np.asarray(v_pool)[rows], scale=scale)
+    J = res["J"]
+    res["J_logical"] = J
+    res["J"] = np.where(J >= 0, rows[np.maximum(J, 0)], -1)
     return res

@@ -23,7 +23,8 @@ from typing import Optional
 
 import torch
 
-IDS = {"q_idx": 1, "k_idx": 2, "w": 3, "q": 4, "k": 5, "v": 6}
+IDS = {"q_idx": 1, "k_idx": 2, "w": 3, "q": 4, "k": 5, "v": 6,
+       "pages": 7, "pool_k_idx": 8, "pool_k": 9, "pool_v": 10}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -48,6 +49,8 @@ class Workload:
     block_size: int = 128
     n_keep: int = 64
     seed: int = 0
+    page_size: int = 0      # > 0: caches scattered over a pool of pages (paged_pool)
+    spare_pages: int = 0    # unused pool pages besides the sequences' own
 
     @property
     def decode(self) -> bool:
@@ -61,7 +64,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads of the path.  Names say what each one is.
+# The workloads of the path.  Names say what each one is.
 WORKLOADS = {
     # tiny causal prefill: small enough for the oracle to check every row
     "tiny_prefill_1k": Workload("tiny_prefill_1k", B=1, n_q=1024, L=1024, q_pos0=0,
@@ -75,6 +78,9 @@ WORKLOADS = {
     # last 16384-query chunk of a 262144-token context (one GPU's share)
     "chunk_256k": Workload("chunk_256k", B=1, n_q=16384, L=262144, q_pos0=245760,
                            H_I=64, d_I=128, k=2048, H_q=16),
+    # decode_128k with its caches scattered over a pool of 64-token pages (serving layout)
+    "decode_128k_paged": Workload("decode_128k_paged", B=64, n_q=1, L=131073, q_pos0=131072,
+                                  H_I=64, d_I=128, k=2048, H_q=16, page_size=64, spare_pages=4096),
     # two-stage (block prefilter, then tokens) on the final 8192 queries of 128K
     "two_stage_128k": Workload("two_stage_128k", B=1, n_q=8192, L=131072, q_pos0=122880,
                                H_I=64, d_I=128, k=2048, H_q=16, two_stage=True,
@@ -140,6 +146,44 @@ def make_inputs(wl: Workload, device="cpu", with_attn: bool = True,
         out["q"] = _randn_bf16((wl.B, wl.n_q, wl.H_q, wl.d), s, IDS["q"], device)
         out["k"] = _randn_bf16((wl.B, wl.L, wl.d), s, IDS["k"], device)
         out["v"] = _randn_bf16((wl.B, wl.L, wl.d), s, IDS["v"], device)
+    if wl.page_size > 0:
+        return paged_pool(out, wl.page_size, wl.spare_pages, s)
+    return out
+
+
+def paged_pool(inp: dict, page_size: int, spare_pages: int = 0, seed: int = 0) -> dict:
+    """The caches of ``inp`` scattered over one shared pool of pages (serving layout).
+
+    Sequence b's L keys fill max_pages = ceil(L / page_size) pages.  Those B * max_pages
+    pages and ``spare_pages`` unused ones are laid out in a seeded random order, so
+    sequence b's page m sits at pool page page_table[b, m].  Returns a copy of ``inp``
+    whose k_idx, k and v are pools [n_slots, .] (n_slots = pages * page_size) holding
+    the keys of ``inp`` at the rows the page table names and seeded random values
+    elsewhere (spare pages, the tail of each last page), plus page_table (int32
+    [B, max_pages]) and page_size.  It moves data only.
+    """
+    k_idx = inp["k_idx"]
+    device = k_idx.device
+    B, L, d_I = k_idx.shape
+    max_pages = -(-L // page_size)
+    n_pages = B * max_pages + spare_pages
+    g = torch.Generator().manual_seed(seed * 16 + IDS["pages"])
+    order = torch.randperm(n_pages, generator=g)[: B * max_pages].to(torch.int32)
+    page_table = order.view(B, max_pages).contiguous().to(device)
+    n_slots = n_pages * page_size
+    j = torch.arange(L, device=device, dtype=torch.int64)
+    rows = (page_table.long()[:, j // page_size] * page_size + j % page_size).reshape(-1)
+    out = dict(inp)
+    out["k_idx"] = _randint((n_slots, d_I), -64, 64, torch.int8, seed, IDS["pool_k_idx"], device)
+    out["k_idx"].index_copy_(0, rows, k_idx.reshape(B * L, d_I))
+    for name in ("k", "v"):
+        if name in inp:
+            t = inp[name]
+            pool = _randn_bf16((n_slots, t.shape[-1]), seed, IDS["pool_" + name], device)
+            pool.index_copy_(0, rows, t.reshape(B * L, t.shape[-1]))
+            out[name] = pool
+    out["page_table"] = page_table
+    out["page_size"] = page_size
     return out
 
 

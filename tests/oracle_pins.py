@@ -347,10 +347,80 @@ def check_attention_special(impl, seed=9):
     return _all(r)
 
 
+def check_paged_hand(impl):
+    """Paged caches by hand: pool rows of logical keys, and one worked selection."""
+    r = []
+    r.append(_ok(np.array_equal(impl.paged_rows([2, 0, 1], 6, 2), [4, 5, 0, 1, 2, 3]), "rows, pages of 2"))
+    r.append(_ok(np.array_equal(impl.paged_rows([3, 1], 8, 4), [12, 13, 14, 15, 4, 5, 6, 7]), "rows, pages of 4"))
+    # one head, one dim, w = 1, q = 1: a key's score is max(0, its value).  Pool rows hold
+    # 5 1 7 3 2 9; the page table [1, 2, 0] makes the logical keys 7 3 2 9 5 1.
+    pool = np.array([[5], [1], [7], [3], [2], [9]], np.int64)
+    q = np.array([[1]], np.int64)
+    w = np.array([1], np.int64)
+    res = impl.forward_row_paged(q, pool, w, 5, 3, [1, 2, 0], 2)
+    # best three logical keys: 3 (9), 0 (7), 4 (5) -> logical [0, 3, 4] -> pool rows [2, 5, 0]
+    r.append(_ok(np.array_equal(res["J"], [2, 5, 0]) and res["count"] == 3, f"worked selection {res['J']}"))
+    res = impl.forward_row_paged(q, pool, w, 3, 2, [1, 2, 0], 2)
+    r.append(_ok(np.array_equal(res["J"], [2, 5]), f"causal limit {res['J']}"))
+    res = impl.forward_row_paged(q, pool, w, 1, 4, [1, 2, 0], 2)
+    r.append(_ok(np.array_equal(res["J"], [2, 3, -1, -1]), f"short row padded {res['J']}"))
+    return _all(r)
+
+
+def _paged_case(rng, n_pages_seq, page_size, spare, d_I=16, d=8, H=4):
+    L = n_pages_seq * page_size
+    k_idx = rng.integers(-64, 65, (L, d_I))
+    kc = rng.standard_normal((L, d))
+    vc = rng.standard_normal((L, d))
+    n_pool = n_pages_seq + spare
+    perm = rng.permutation(n_pool)[:n_pages_seq]
+    rows = (perm[:, None] * page_size + np.arange(page_size)[None, :]).reshape(-1)
+    pool_k_idx = rng.integers(-64, 65, (n_pool * page_size, d_I))
+    pool_kc = rng.standard_normal((n_pool * page_size, d))
+    pool_vc = rng.standard_normal((n_pool * page_size, d))
+    pool_k_idx[rows], pool_kc[rows], pool_vc[rows] = k_idx, kc, vc
+    q_idx = rng.integers(-64, 65, (H, d_I))
+    w = rng.integers(1, 17, (H,))
+    q = rng.standard_normal((H, d))
+    return L, k_idx, kc, vc, perm, pool_k_idx, pool_kc, pool_vc, q_idx, w, q
+
+
+def check_paged_identity(impl, seed=10):
+    """An identity page table is the contiguous cache itself."""
+    rng = np.random.default_rng(seed)
+    L, k_idx, kc, vc, _, _, _, _, q_idx, w, q = _paged_case(rng, 6, 8, 0)
+    r = []
+    for p, k in ((L - 1, 12), (20, 30), (0, 4)):
+        a = impl.forward_row(q_idx, k_idx, w, p, k, q_row=q, k_cache=kc, v_cache=vc)
+        b = impl.forward_row_paged(q_idx, k_idx, w, p, k, np.arange(6), 8, q_row=q, k_pool=kc, v_pool=vc)
+        r.append(_ok(np.array_equal(a["J"], b["J"]) and np.array_equal(a["out"], b["out"])
+                     and np.array_equal(a["lse"], b["lse"]), f"identity pages p={p}"))
+    return _all(r)
+
+
+def check_paged_permutation(impl, seed=11):
+    """Pages scattered over a larger pool: the same selection on logical keys, J mapped
+    through the page table, the same attention result."""
+    rng = np.random.default_rng(seed)
+    r = []
+    for page_size, n_pages, spare in ((4, 9, 5), (16, 5, 3)):
+        L, k_idx, kc, vc, perm, pk, pkc, pvc, q_idx, w, q = _paged_case(rng, n_pages, page_size, spare)
+        for p, k in ((L - 1, 10), (L // 2, 7), (3, 9)):
+            a = impl.forward_row(q_idx, k_idx, w, p, k, q_row=q, k_cache=kc, v_cache=vc)
+            b = impl.forward_row_paged(q_idx, pk, w, p, k, perm, page_size, q_row=q, k_pool=pkc, v_pool=pvc)
+            Ja = a["J"]
+            want = np.where(Ja >= 0, perm[np.maximum(Ja, 0) // page_size] * page_size + np.maximum(Ja, 0) % page_size, -1)
+            r.append(_ok(np.array_equal(b["J_logical"], Ja) and np.array_equal(b["J"], want)
+                         and np.array_equal(a["out"], b["out"]) and np.array_equal(a["lse"], b["lse"]),
+                         f"scattered pages P={page_size} p={p}"))
+    return _all(r)
+
+
 ALL_CHECKS = [
     check_scores_hand, check_scores_closed_forms, check_scores_invariances, check_scores_bound,
     check_topk_hand, check_topk_bruteforce, check_topk_special,
     check_blocks_hand, check_block_reps_sum, check_block_keep_bruteforce,
     check_two_stage_reductions, check_two_stage_invariants,
     check_attention_hand, check_attention_dense, check_attention_special,
+    check_paged_hand, check_paged_identity, check_paged_permutation,
 ]

@@ -460,6 +460,95 @@ def test_forward_decode_fused_selection(lsa, H_I):
     err.check()
 
 
+def _map_pages(J, page_table, page_size):
+    """Logical keys [B, n_q, k] (or -1) -> pool rows through page_table [B, max_pages]."""
+    J = J.long()
+    pt = page_table.long()
+    B, n_q, k = J.shape
+    Jc = J.clamp(min=0)
+    rows = torch.gather(pt, 1, (Jc // page_size).reshape(B, -1)).reshape(B, n_q, k) * page_size + Jc % page_size
+    return torch.where(J >= 0, rows, torch.full_like(J, -1))
+
+
+@pytest.mark.parametrize("page_size", [64, 256])
+def test_forward_decode_paged(lsa, page_size):
+    """Paged caches (decode): k_idx / k / v are pools shared by the sequences, each
+    sequence reaching its keys through a page table (pages scattered over the pool,
+    spare pages between them).  The lists name pool rows: they equal the contiguous
+    call's lists mapped through the page table, counts equal, outputs and LSE equal
+    bit for bit; the oracle's paged definition agrees on sampled rows.  Sequences of
+    different lengths share the call, rows of at most k keys included."""
+    L, k = 40000, 1024
+    pos = [39999, 30000, 1023, 500, 33333, 39998, 4095]
+    wl = synthetic.Workload("paged", B=len(pos), n_q=1, L=L, q_pos0=0, H_I=64, d_I=128, k=k, H_q=16)
+    inp, g = _inputs(wl, seed=13, pos=pos)
+    ref = lsa.lsa_forward(g, k_top=k)
+    pg = synthetic.paged_pool(g, page_size, spare_pages=37, seed=3)
+    ws_bytes = lsa.lsa_forward_workspace_size(pg, k)
+    assert lsa.lsa_forward_stages(pg, k, ws_bytes) == ["index_select", "topk", "sparse_attn"]
+    res = lsa.lsa_forward(pg, k_top=k)
+    torch.cuda.synchronize()
+    assert torch.equal(res["idx"].long(), _map_pages(ref["idx"], pg["page_table"], page_size))
+    assert torch.equal(res["count"], ref["count"])
+    assert torch.equal(res["out"], ref["out"])
+    assert torch.equal(res["lse"], ref["lse"])
+    # the oracle over the pool itself
+    pt = pg["page_table"].cpu().numpy()
+    pki, pk, pv = pg["k_idx"].cpu().numpy(), np64(pg["k"].cpu()), np64(pg["v"].cpu())
+    qi, w, q = inp["q_idx"].numpy(), inp["w"].numpy(), np64(inp["q"])
+    J, out = res["idx"].cpu().numpy(), np64(res["out"])
+    err = AttnErr()
+    for b in (0, 3, 6):
+        r = oracle.forward_row_paged(qi[b, 0], pki, w, pos[b], k, pt[b], page_size, q_row=q[b, 0],
+                                     k_pool=pk, v_pool=pv, scale=1.0 / math.sqrt(128))
+        assert np.array_equal(J[b, 0], r["J"]), f"seq {b}"
+        err.add(out[b, 0], r["out"], b)
+    err.check()
+
+
+def test_forward_decode_paged_graph_replay(lsa):
+    """A paged decode step captured once in a HIP graph (one graph per range of context
+    lengths: the page-table width fixes L_max and so every launch shape) replays for
+    new positions and new page tables written into the captured inputs; every replay
+    equals an eager call on the same inputs, bit for bit."""
+    P, k, L = 64, 512, 20000
+    pos = [19999, 12000, 511, 7000]
+    wl = synthetic.Workload("pgraph", B=len(pos), n_q=1, L=L, q_pos0=0, H_I=64, d_I=128, k=k, H_q=16)
+    _, g = _inputs(wl, seed=17, pos=pos)
+    pg = synthetic.paged_pool(g, P, spare_pages=64, seed=5)
+    ws = torch.empty((max(lsa.lsa_forward_workspace_size(pg, k), 16),), dtype=torch.uint8, device=dev())
+    B = len(pos)
+    out = {"idx": torch.empty((B, 1, k), dtype=torch.int32, device=dev()),
+           "count": torch.empty((B, 1), dtype=torch.int32, device=dev()),
+           "out": torch.empty_like(pg["q"]),
+           "lse": torch.empty((B, 1, 16), dtype=torch.float32, device=dev())}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lsa.lsa_forward(pg, k_top=k, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lsa.lsa_forward(pg, k_top=k, out=out, ws=ws)
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(99)
+    n_pool = pg["k_idx"].shape[0] // P
+    for trial in range(3):
+        new_pos = torch.randint(0, L, (B, 1), generator=gen, dtype=torch.int32)
+        new_pt = torch.randperm(n_pool, generator=gen)[: pg["page_table"].numel()].to(torch.int32)
+        pg["q_pos"].copy_(new_pos.to(dev()))
+        pg["page_table"].copy_(new_pt.view_as(pg["page_table"]).to(dev()))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {n: t.clone() for n, t in out.items()}
+        want = lsa.lsa_forward(pg, k_top=k)
+        torch.cuda.synchronize()
+        for n in ("idx", "count", "out", "lse"):
+            assert torch.equal(got[n], want[n]), f"replay {trial}: {n}"
+
+
 @pytest.mark.parametrize("kind", ["one_span_distinct", "whole_span_equal", "two_spans_ties", "all_equal",
                                   "spread_ties"])
 def test_forward_decode_fused_selection_concentrated(lsa, kind):

@@ -1,4 +1,4 @@
-"""The five workloads at full size, in the launch configuration the benchmark times
+"""The workloads at full size, in the launch configuration the benchmark times
 (lsa_forward with its automatic chunking): sampled rows against the CPU oracle
 (indices bit-exact, attention within tolerance) and, on every row the GPU memory
 allows, the O(n) top-k certificate over the GPU's own scores."""
@@ -88,6 +88,21 @@ def test_decode_128k(lsa):
     _check_rows(wl, g, res, synthetic.checked_rows(wl, n_random=10))
     S = lsa.lsa_index_scores(g["q_idx"], g["k_idx"], g["w"], g["q_pos"])
     topk_certificate(S[:, 0], res["idx"][:, 0], g["q_pos"][:, 0], wl.k)
+    del S
+    # the benchmark's paged variant (decode_128k_paged): the same caches scattered over a
+    # pool of 64-token pages give the same step, the lists naming pool rows
+    wp = synthetic.WORKLOADS["decode_128k_paged"]
+    pg = synthetic.paged_pool(g, wp.page_size, wp.spare_pages, wp.seed)
+    rp = lsa.lsa_forward(pg, k_top=wp.k)
+    torch.cuda.synchronize()
+    P = wp.page_size
+    J = res["idx"].long()
+    pt = pg["page_table"].long()
+    Jc = J.clamp(min=0)
+    rows = torch.gather(pt, 1, (Jc // P).reshape(wl.B, -1)).reshape(J.shape) * P + Jc % P
+    assert torch.equal(rp["idx"].long(), torch.where(J >= 0, rows, torch.full_like(J, -1)))
+    assert torch.equal(rp["out"], res["out"]) and torch.equal(rp["lse"], res["lse"])
+    print("[decode_128k_paged] equal to the contiguous step", flush=True)
 
 
 def test_chunk_256k(lsa):

@@ -100,6 +100,40 @@ def test_forward_stages_listing():
     assert st == ["block_reps"] + ["block_prefilter", "index_scores", "topk", "sparse_attn"] * 2
 
 
+def _fake_paged(B, n_q, max_pages, page_size, n_pages, H_I=64, d_I=128, H_q=16, d=128):
+    import torch
+    inp = _fake_inputs(B, n_q, 1, H_I, d_I, H_q, d)
+    inp["k_idx"] = torch.zeros((n_pages * page_size, d_I), dtype=torch.int8)
+    inp["k"] = torch.zeros((n_pages * page_size, d), dtype=torch.bfloat16)
+    inp["v"] = torch.zeros((n_pages * page_size, d), dtype=torch.bfloat16)
+    inp["page_table"] = torch.zeros((B, max_pages), dtype=torch.int32)
+    inp["page_size"] = page_size
+    return inp
+
+
+def test_forward_paged_arguments():
+    """Paged caches (host checks only): decode calls plan the decode selection; page
+    sizes below 64 or not powers of two, and pools not made of whole pages, are
+    invalid; prefill-shaped and two-stage calls are unsupported."""
+    import learned_top_sparse_amd as lsa
+    from learned_top_sparse_amd.binding import LsaError
+    inp = _fake_paged(64, 1, 2049, 64, 64 * 2049 + 100)
+    ws = lsa.lsa_forward_workspace_size(inp, 2048)
+    assert ws > 0
+    assert lsa.lsa_forward_stages(inp, 2048, ws) == ["index_select", "topk", "sparse_attn"]
+    for bad in (_fake_paged(4, 1, 16, 32, 80), _fake_paged(4, 1, 16, 96, 80)):
+        with pytest.raises(LsaError, match="INVALID_ARG"):
+            lsa.lsa_forward_workspace_size(bad, 256)
+    bad = _fake_paged(4, 1, 16, 64, 80)
+    bad["k_idx"] = bad["k_idx"][:-1]   # not whole pages
+    with pytest.raises(LsaError, match="INVALID_ARG"):
+        lsa.lsa_forward_workspace_size(bad, 256)
+    with pytest.raises(LsaError, match="UNSUPPORTED"):
+        lsa.lsa_forward_workspace_size(_fake_paged(1, 8, 16, 64, 80), 256)
+    with pytest.raises(LsaError, match="UNSUPPORTED"):
+        lsa.lsa_forward_workspace_size(_fake_paged(4, 1, 16, 64, 80), 256, two_stage=True)
+
+
 def test_forward_rejects_too_few_stage_events():
     """Too few stage events: LSA_ERR_INVALID_ARG before anything is launched."""
     import learned_top_sparse_amd as lsa

@@ -140,6 +140,25 @@ def _cands_past_p(kept, p, block_size, L):
     return keys[keys < L]
 
 
+_orig_paged_rows = O.paged_rows
+_orig_forward_row_paged = O.forward_row_paged
+
+
+def _paged_rows_no_offset(pt, n_keys, page_size):
+    j = np.arange(n_keys, dtype=np.int64)
+    return np.asarray(pt, np.int64)[j // page_size] * page_size
+
+
+def _paged_rows_ignore_table(pt, n_keys, page_size):
+    return np.arange(n_keys, dtype=np.int64)
+
+
+def _paged_J_logical(*args, **kw):
+    res = _orig_forward_row_paged(*args, **kw)
+    res["J"] = res["J_logical"]
+    return res
+
+
 MUTANTS = {
     "relu_after_sum": ("index_scores", _relu_after_sum),
     "no_relu": ("index_scores", _no_relu),
@@ -158,6 +177,9 @@ MUTANTS = {
     "attn_padding_as_key": ("sparse_attention", _attn_padding_as_key),
     "attn_lse_without_max": ("sparse_attention", _attn_lse_without_max),
     "cands_past_p": ("two_stage_candidates", _cands_past_p),
+    "paged_rows_no_offset": ("paged_rows", _paged_rows_no_offset),
+    "paged_rows_ignore_table": ("paged_rows", _paged_rows_ignore_table),
+    "paged_J_logical": ("forward_row_paged", _paged_J_logical),
 }
 
 
