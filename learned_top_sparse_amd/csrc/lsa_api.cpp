@@ -637,6 +637,7 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
       lsa::DecLayout dl;
       if (!lsa::dec_sel_layout((long long)nb * ni, L, kt, &dl)) return LSA_ERR_INTERNAL;
       ta.hist_ready = true;
+      ta.pages = ia.pages;  // paged caches: the finish writes pool rows
       ia.sel_base = static_cast<int*>(topk_ws);
       ia.sel_rec_ints = dl.rec_ints;
       ia.sel_parts = dl.parts;
@@ -671,11 +672,7 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
       if (lsa::launch_topk(ta, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
     } else {
       if (lsa::launch_index_scores(ia, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
-      if (lsa::launch_topk(ta, s) != hipSuccess) return LSA_ERR_HIP;
-      // paged caches: the lists' logical keys become pool rows
-      if (paged && lsa::launch_map_slots(ix, (long long)nb * ni, ni, kt, ia.pages, s) != hipSuccess)
-        return LSA_ERR_HIP;
-      if (!mark()) return LSA_ERR_HIP;
+      if (lsa::launch_topk(ta, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
     }
     lsa_status sa = run_attn(qq, kk, vv, ix, nb, ni, L, H_q, d, kt, a->scale, split, oo, ls, attn_ws, s,
                              paged ? (long long)a->n_slots : 0ll);

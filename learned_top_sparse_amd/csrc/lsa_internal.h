@@ -83,6 +83,7 @@ struct TopkArgs {
   size_t ws_bytes;
   bool hist_ready;   // the indexer built the rows' selection state in ws (dec_sel_layout)
   const int32_t* row_state;  // optional (flat): only rows whose state (ThrArgs) is not 0
+  Pages pages;               // hist_ready with paged caches: the lists receive pool rows
 };
 
 struct BlkSelArgs {
@@ -120,8 +121,6 @@ hipError_t launch_block_limbs(const int32_t* reps, int B, int n_blocks, int d_I,
 hipError_t launch_block_scores(const BlkArgs& a, hipStream_t st);
 hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
-// idx[row][e] (logical key of sequence row / n_q, or -1) -> its pool row, in place
-hipError_t launch_map_slots(int32_t* idx, long long rows, int n_q, int k, const Pages& pg, hipStream_t st);
 // workspace that lets lsa_topk split each row over several workgroups (0 = not used)
 size_t topk_ws_bytes(long long rows, int L_max);
 // Decode selection: the indexer builds each row's selection state (histogram, one

@@ -76,17 +76,25 @@ __device__ __forceinline__ unsigned radix_select32(int n, int need, int* h256, i
 
 // ---------------------------------------------------------------------------------
 // One query row as seen by the selection: candidate slots [0, n_slots), their
-// scores in global memory, and (two-stage mode) the kept-block table in LDS.
+// scores in global memory, and (two-stage mode) the kept-block table in LDS.  The
+// written list holds key_of(slot): the key (two-stage: through the kept blocks), or
+// with paged caches (flat rows, pt set) the key's pool row.
 template <bool KEPT>
 struct RowView {
   const int32_t* srow;
   const int* kept_s;  // KEPT: block table in LDS
   int n_slots, p, bs;
   bool vec;           // 16-byte aligned row: vector loads
+  const int32_t* pt = nullptr;  // paged caches: the row's page table (page ids clamped to n_pages)
+  int plog2 = 0, n_pages = 0;
 
   __device__ __forceinline__ int key_of(int s) const {
-    if constexpr (KEPT) return kept_s[s / bs] * bs + s % bs;
-    else return s;
+    if constexpr (KEPT) {
+      return kept_s[s / bs] * bs + s % bs;
+    } else {
+      if (pt == nullptr) return s;
+      return (min(max(pt[s >> plog2], 0), n_pages - 1) << plog2) | (s & ((1 << plog2) - 1));
+    }
   }
   __device__ __forceinline__ bool valid(int s) const {
     if (s >= n_slots) return false;
@@ -746,7 +754,7 @@ template <int NT>
 __global__ __launch_bounds__(NT) void topk_list_finish_kernel(int32_t* __restrict__ scores, long long ld,
                                                               const int32_t* __restrict__ q_pos, int L_max, int k,
                                                               DecWs ws, int32_t* __restrict__ idx,
-                                                              int32_t* __restrict__ count) {
+                                                              int32_t* __restrict__ count, int n_q, Pages pg) {
   constexpr int NW = NT / 64;
   constexpr int V = 3;
   static_assert(NT % NGRP == 0 && NT % GRP == 0, "whole groups of threads per group sum and per bin");
@@ -786,6 +794,11 @@ __global__ __launch_bounds__(NT) void topk_list_finish_kernel(int32_t* __restric
   rv.bs = 0;
   rv.kept_s = nullptr;
   rv.n_slots = max(rv.p + 1, 0);
+  if (pg.page_table != nullptr) {
+    rv.pt = pg.page_table + (row / n_q) * pg.max_pages;
+    rv.plog2 = pg.page_log2;
+    rv.n_pages = pg.n_pages;
+  }
   const int n_valid = rv.n_slots;
   if (count != nullptr && tid == 0) count[row] = min(k, n_valid);
   if (n_valid <= k) {
@@ -1032,7 +1045,7 @@ __global__ __launch_bounds__(NT) void topk_list_finish_kernel(int32_t* __restric
       }
     }
     running = ordered_emit4<NT, V>(base, m, pl, wcnt + parity * V * NW, running, [&](int r, int, SP x) {
-      if (r < k) out[r] = x.slot;
+      if (r < k) out[r] = rv.key_of(x.slot);
     });
     parity ^= 1;
   };
@@ -1494,7 +1507,8 @@ static hipError_t launch_topk_t(const TopkArgs& a, hipStream_t st, long long row
     DecWs d;
     if (!dec_rows(a, &d)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((topk_list_finish_kernel<1024>), dim3((unsigned)rows), dim3(1024), 0, st,
-                       const_cast<int32_t*>(a.scores), a.ld, a.q_pos, a.L_max, a.k, d, a.idx, a.count);
+                       const_cast<int32_t*>(a.scores), a.ld, a.q_pos, a.L_max, a.k, d, a.idx, a.count, a.n_q,
+                       a.pages);
     return hipGetLastError();
   }
   SegWs w;
@@ -1545,29 +1559,6 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   const long long rows = (long long)a.B * a.n_q;
   if (rows == 0) return hipSuccess;
   return a.kept != nullptr ? launch_topk_t<true>(a, st, rows) : launch_topk_t<false>(a, st, rows);
-}
-
-// Paged caches: each entry of the index lists (a logical key of its row's sequence, or
-// -1) becomes the key's pool row, page_table[b][j >> page_log2] << page_log2 | j & mask
-// (page ids clamped to the pool).
-__global__ __launch_bounds__(256) void map_slots_kernel(int32_t* __restrict__ idx, long long n, int n_q, int k,
-                                                        Pages pg) {
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (t >= n) return;
-  const int j = idx[t];
-  if (j < 0) return;
-  const int32_t* pt = pg.page_table + (t / k / n_q) * pg.max_pages;
-  idx[t] = (min(max(pt[j >> pg.page_log2], 0), pg.n_pages - 1) << pg.page_log2) | (j & ((1 << pg.page_log2) - 1));
-}
-
-hipError_t launch_map_slots(int32_t* idx, long long rows, int n_q, int k, const Pages& pg, hipStream_t st) {
-  if (rows == 0) return hipSuccess;
-  if (pg.page_table == nullptr || k < 1 || n_q < 1 || pg.n_pages < 1 ||
-      ((long long)pg.n_pages << pg.page_log2) > (1ll << 31))
-    return hipErrorInvalidValue;
-  const long long n = rows * k;
-  hipLaunchKernelGGL(map_slots_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, idx, n, n_q, k, pg);
-  return hipGetLastError();
 }
 
 hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st) {
