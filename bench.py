@@ -38,7 +38,10 @@ def _describe(wl):
     s = (f"{wl.name}: B={wl.B} x n_q={wl.n_q} queries at positions {wl.q_pos0}..{wl.q_pos0 + wl.n_q - 1}, "
          f"{wl.L} cached keys, indexer H_I={wl.H_I} d_I={wl.d_I} int8, k={wl.k}, "
          f"attention {wl.H_q} bf16 query heads / 1 KV head d={wl.d}")
-    if wl.two_stage:
+    if wl.pooled:
+        s += (f", pooled indexer: one key per {wl.block_size} keys (block-key cache resident), "
+              f"keep {wl.n_keep} blocks")
+    elif wl.two_stage:
         s += f", two-stage blocks of {wl.block_size} keep {wl.n_keep}"
     if wl.page_size:
         s += f", paged caches (pages of {wl.page_size} tokens in a shared pool, {wl.spare_pages} spare pages)"
@@ -60,7 +63,8 @@ class Step:
         self.lsa, self.torch, self.wl, self.inp = lsa, torch, wl, inp
         dev = inp["q_idx"].device
         B, n_q = wl.B, wl.n_q
-        self.kw = dict(two_stage=wl.two_stage, block_size=wl.block_size, n_keep=wl.n_keep)
+        self.kw = dict(two_stage="pooled" if wl.pooled else wl.two_stage, block_size=wl.block_size,
+                       n_keep=wl.n_keep)
         ws_bytes = lsa.lsa_forward_workspace_size(inp, wl.k, **self.kw)
         self.ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
         self.stages = lsa.lsa_forward_stages(inp, wl.k, self.ws.numel(), **self.kw)
@@ -111,6 +115,17 @@ def algorithmic(wl):
     B, n_q, H_I, d_I, H_q, d, k = wl.B, wl.n_q, wl.H_I, wl.d_I, wl.H_q, wl.d, wl.k
     pos = [wl.q_pos0 + i for i in range(n_q)]
     vis = [min(p, wl.L - 1) + 1 for p in pos]
+    if wl.pooled:
+        bs, nk = wl.block_size, wl.n_keep
+        nbl = wl.L // bs
+        blk_pairs = B * sum(min(p // bs, nbl) for p in pos)
+        att_pairs = B * sum(min(nk - 1, p // bs) * bs + (p - (p // bs) * bs + 1) for p in pos)
+        return {
+            "block_ops": 2 * H_I * d_I * blk_pairs * 2,           # two int8 parts per block key
+            "block_bytes": B * (nbl * 2 * d_I + n_q * H_I * d_I),  # the block-key cache + index queries
+            "attn_flops": 4 * H_q * d * att_pairs,
+            "attn_gather_bytes": att_pairs * 2 * d * 2,
+        }
     if wl.two_stage:
         bs, nk = wl.block_size, wl.n_keep
         blk_pairs = sum(p // bs for p in pos) * B
@@ -225,6 +240,10 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
 def measure(lsa, torch, wl, steps, warmup):
     import synthetic
     inp = synthetic.make_inputs(wl, torch.device("cuda:0"))
+    if wl.pooled:
+        # the block-key cache is kept with the caches (a serving loop updates one block per
+        # block_size tokens), so it is built before the timed steps
+        inp["block_keys"] = lsa.lsa_block_cache(inp["k_idx"], wl.block_size)
     torch.cuda.synchronize()
     step = Step(lsa, torch, wl, inp)
     step.make_events((steps + EVENTS_EVERY - 1) // EVENTS_EVERY)

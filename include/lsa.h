@@ -117,6 +117,20 @@ lsa_status lsa_block_reps(const int8_t* k_idx, int32_t B, int32_t L_max, int32_t
                           int32_t block_size, int32_t n_blocks, int32_t* reps, void* stream);
 
 /*
+ * Block-key cache of the block modes of lsa_forward (two_stage = 1 or 2): for blocks
+ * m in [first_block, first_block + n_update) of every sequence, the representative
+ * r = sum of the block's block_size index keys ([LSA] §3.1 "Pooling"), stored as two
+ * int8 parts r = 128 * hi + lo, lo in [-64, 63]:
+ *     block_keys[b, m, 0, :] = hi,  block_keys[b, m, 1, :] = lo   (int8 [B, n_blocks, 2, d_I])
+ * A serving loop builds it once and then updates only the block a new token
+ * completes (n_update = 1).  Requires (first_block + n_update) * block_size <= L_max.
+ * Supported: d_I in {64, 128}; 1 <= block_size <= 128.  No workspace.
+ */
+lsa_status lsa_block_cache(const int8_t* k_idx, int32_t B, int32_t L_max, int32_t d_I, int32_t block_size,
+                           int32_t n_blocks, int32_t first_block, int32_t n_update, int8_t* block_keys,
+                           void* stream);
+
+/*
  * Two-stage block prefilter ([HISA]; [LSA] §2.2 "Related Work": score blocks
  * first, then only the keys inside the selected blocks).  For each query with
  * own block o = floor(q_pos/block_size):
@@ -192,7 +206,7 @@ lsa_status lsa_sparse_attn(const void* q, const void* k, const void* v, const in
  */
 typedef struct lsa_forward_args {
   int32_t mode;          /* LSA_MODE_PREFILL or LSA_MODE_DECODE */
-  int32_t two_stage;     /* 0 flat, 1 block prefilter then tokens */
+  int32_t two_stage;     /* 0 flat; 1 block prefilter then tokens; 2 pooled blocks (below) */
   const int8_t* q_idx;   /* int8 [B, n_q, H_I, d_I] */
   const int8_t* k_idx;   /* int8 [B, L_max, d_I] */
   const int32_t* w;      /* int32 [H_I] or [B, n_q, H_I] */
@@ -249,6 +263,15 @@ typedef struct lsa_forward_args {
   const int32_t* page_table;  /* int32 [B, max_pages] */
   int32_t page_size, max_pages;
   int64_t n_slots;
+  /* Block modes: the block-key cache of lsa_block_cache for all L_max / block_size
+     blocks, or NULL (then lsa_forward builds it in its workspace, stage block_reps).
+     Pooled blocks (two_stage = 2; the "score every block of four keys" indexers of
+     [LSA] §2.2 "Related Work" and the LSA page's flat baseline): each query keeps its
+     own block and the best n_keep - 1 earlier complete blocks by their block score (as
+     two_stage = 1), and its list is every key of those blocks it may see, ascending,
+     -1 padded: k_top must equal n_keep * block_size.  Stages block_prefilter ->
+     expand -> sparse_attn per chunk. */
+  const int8_t* block_keys;
 } lsa_forward_args;
 enum { LSA_SELECT_AUTO = 0, LSA_SELECT_TABLE = 1, LSA_SELECT_FORCE_SHORT = 2, LSA_SELECT_FORCE_OVERFLOW = 3 };
 
@@ -266,8 +289,9 @@ lsa_status lsa_forward_plan(const lsa_forward_args* a, size_t ws_bytes, int64_t*
 
 /* Stages of lsa_forward, in launch order, for a workspace of ws_bytes.  A stage is
    one kernel or a short fixed sequence of them:
-     BLOCK_REPS       block representatives (two_stage, once per call)
-     BLOCK_PREFILTER  block scores and kept blocks of a chunk (two_stage)
+     BLOCK_REPS       the block-key cache (block modes without block_keys, once per call)
+     BLOCK_PREFILTER  block scores and kept blocks of a chunk (block modes)
+     EXPAND           pooled blocks: the keys of the kept blocks as the index lists
      INDEX_SELECT     the indexer over a chunk of flat rows of few queries per
                       sequence (fewer than 8) that leaves, instead of the score
                       table, each key span's share of the selection state (coarse
@@ -289,7 +313,8 @@ enum {
   LSA_STAGE_INDEX_SCORES = 4,
   LSA_STAGE_TOPK = 5,
   LSA_STAGE_SPARSE_ATTN = 6,
-  LSA_STAGE_SAMPLE = 7
+  LSA_STAGE_SAMPLE = 7,
+  LSA_STAGE_EXPAND = 8
 };
 lsa_status lsa_forward_stages(const lsa_forward_args* a, size_t ws_bytes, int32_t* codes, int32_t max_codes,
                               int32_t* n_stages);

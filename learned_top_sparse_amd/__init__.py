@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     LsaError,
     lib,
     lib_path,
+    lsa_block_cache,
     lsa_block_prefilter,
     lsa_block_reps,
     lsa_forward,

@@ -17,14 +17,14 @@ _LIB = None
 
 # every symbol include/lsa.h declares
 EXPORTED = [
-    "lsa_status_string", "lsa_version", "lsa_index_scores", "lsa_block_reps",
+    "lsa_status_string", "lsa_version", "lsa_index_scores", "lsa_block_reps", "lsa_block_cache",
     "lsa_block_prefilter_workspace_size", "lsa_block_prefilter", "lsa_topk_workspace_size",
     "lsa_topk", "lsa_sparse_attn_workspace_size", "lsa_sparse_attn",
     "lsa_forward_workspace_size", "lsa_forward", "lsa_forward_plan", "lsa_forward_stages",
 ]
 
 STAGE_NAMES = {1: "block_reps", 2: "block_prefilter", 3: "index_select", 4: "index_scores", 5: "topk", 7: "sample",
-               6: "sparse_attn"}
+               6: "sparse_attn", 8: "expand"}
 
 P = C.c_void_p
 I32 = C.c_int32
@@ -50,6 +50,7 @@ class ForwardArgs(C.Structure):
         ("stage_events", P), ("n_stage_events", I32),
         ("select_mode", I32),
         ("page_table", P), ("page_size", I32), ("max_pages", I32), ("n_slots", I64),
+        ("block_keys", P),
     ]
 
 
@@ -72,6 +73,7 @@ def lib():
         L.lsa_version.argtypes = []
         L.lsa_index_scores.argtypes = [P, P, P, I32, P, P, I32, I32, I32, I32, I32, I32, I32, P, I64, P]
         L.lsa_block_reps.argtypes = [P, I32, I32, I32, I32, I32, P, P]
+        L.lsa_block_cache.argtypes = [P, I32, I32, I32, I32, I32, I32, I32, P, P]
         L.lsa_block_prefilter_workspace_size.argtypes = [I32, I32, I32, I32, C.POINTER(SZ)]
         L.lsa_block_prefilter.argtypes = [P, P, P, I32, P, I32, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
         L.lsa_topk_workspace_size.argtypes = [I32, I32, I32, I32, C.POINTER(SZ)]
@@ -175,6 +177,26 @@ def lsa_block_reps(k_idx, block_size: int, n_blocks: Optional[int] = None):
     return reps
 
 
+def lsa_block_cache(k_idx, block_size: int, n_blocks: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                    first_block: int = 0, n_update: Optional[int] = None):
+    """Block-key cache int8 [B, n_blocks, 2, d_I] (hi, lo parts of each block's key sum);
+    with ``out`` given, only blocks [first_block, first_block + n_update) are (re)written."""
+    dev = k_idx.device
+    _need(k_idx, "k_idx", torch.int8)
+    B, L, d_I = k_idx.shape
+    if n_blocks is None:
+        n_blocks = L // block_size
+    if out is None:
+        out = torch.empty((B, n_blocks, 2, d_I), dtype=torch.int8, device=dev)
+    _need(out, "block_keys", torch.int8, dev)
+    if n_update is None:
+        n_update = n_blocks - first_block
+    st = lib().lsa_block_cache(_ptr(k_idx), B, L, d_I, block_size, n_blocks, first_block, n_update, _ptr(out),
+                               _stream(dev))
+    _check("lsa_block_cache", st)
+    return out
+
+
 def lsa_block_prefilter(q_idx, reps, w, q_pos, block_size: int, n_keep: int, return_scores: bool = False):
     """Kept blocks int32 [B, n_q, n_keep] (ascending, -1 padded); optionally block scores int64."""
     dev = q_idx.device
@@ -248,7 +270,7 @@ def lsa_sparse_attn(q, k, v, idx, scale: Optional[float] = None, n_split: int = 
 SELECT_MODES = {"auto": 0, "table": 1, "force_short": 2, "force_overflow": 3}
 
 
-def _forward_args(inp: dict, k_top: int, two_stage: bool, block_size: int, n_keep: int, scale, attn_split: int,
+def _forward_args(inp: dict, k_top: int, two_stage, block_size: int, n_keep: int, scale, attn_split: int,
                   chunk_rows: int, out: dict, select: str = "auto"):
     q_idx, k_idx, w, q_pos, q, k, v = (inp[n] for n in ("q_idx", "k_idx", "w", "q_pos", "q", "k", "v"))
     B, n_q, H_I, d_I = q_idx.shape
@@ -262,7 +284,8 @@ def _forward_args(inp: dict, k_top: int, two_stage: bool, block_size: int, n_kee
         L = k_idx.shape[1]
     a = ForwardArgs()
     a.mode = 1 if (n_q == 1 and B > 1) else 0
-    a.two_stage = 1 if two_stage else 0
+    # two_stage: False / True (block prefilter, then tokens) / "pooled" (kept blocks' keys)
+    a.two_stage = 2 if two_stage == "pooled" else (1 if two_stage else 0)
     a.q_idx, a.k_idx, a.w = q_idx.data_ptr(), k_idx.data_ptr(), w.data_ptr()
     a.w_per_query = 1 if w.dim() == 3 else 0
     a.q_pos, a.q, a.k, a.v = q_pos.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr()
@@ -279,6 +302,8 @@ def _forward_args(inp: dict, k_top: int, two_stage: bool, block_size: int, n_kee
     if select not in SELECT_MODES:
         raise ValueError(f"select must be one of {sorted(SELECT_MODES)}")
     a.select_mode = SELECT_MODES[select]
+    if inp.get("block_keys") is not None:
+        a.block_keys = inp["block_keys"].data_ptr()
     if pt is not None:
         a.page_table = pt.data_ptr()
         a.page_size = page_size
@@ -287,7 +312,7 @@ def _forward_args(inp: dict, k_top: int, two_stage: bool, block_size: int, n_kee
     return a
 
 
-def lsa_forward_workspace_size(inp: dict, k_top: int, two_stage: bool = False, block_size: int = 128,
+def lsa_forward_workspace_size(inp: dict, k_top: int, two_stage=False, block_size: int = 128,
                                n_keep: int = 64, attn_split: int = 0, chunk_rows: int = 0,
                                select: str = "auto") -> int:
     dummy = {"idx": inp["q_pos"], "out": inp["q"]}
@@ -297,7 +322,7 @@ def lsa_forward_workspace_size(inp: dict, k_top: int, two_stage: bool = False, b
     return nb.value
 
 
-def lsa_forward_plan(inp: dict, k_top: int, ws_bytes: int, two_stage: bool = False, block_size: int = 128,
+def lsa_forward_plan(inp: dict, k_top: int, ws_bytes: int, two_stage=False, block_size: int = 128,
                      n_keep: int = 64, attn_split: int = 0, chunk_rows: int = 0, select: str = "auto"):
     """(rows per chunk, attention split) that lsa_forward uses with ws_bytes of workspace."""
     dummy = {"idx": inp["q_pos"], "out": inp["q"]}
@@ -307,7 +332,7 @@ def lsa_forward_plan(inp: dict, k_top: int, ws_bytes: int, two_stage: bool = Fal
     return rows.value, split.value
 
 
-def lsa_forward_stages(inp: dict, k_top: int, ws_bytes: int, two_stage: bool = False, block_size: int = 128,
+def lsa_forward_stages(inp: dict, k_top: int, ws_bytes: int, two_stage=False, block_size: int = 128,
                        n_keep: int = 64, attn_split: int = 0, chunk_rows: int = 0, select: str = "auto") -> list:
     """Names of the stages lsa_forward runs with ws_bytes of workspace, in launch order."""
     dummy = {"idx": inp["q_pos"], "out": inp["q"]}
@@ -319,11 +344,14 @@ def lsa_forward_stages(inp: dict, k_top: int, ws_bytes: int, two_stage: bool = F
     return [STAGE_NAMES[codes[i]] for i in range(n.value)]
 
 
-def lsa_forward(inp: dict, k_top: int, two_stage: bool = False, block_size: int = 128, n_keep: int = 64,
+def lsa_forward(inp: dict, k_top: int, two_stage=False, block_size: int = 128, n_keep: int = 64,
                 scale: Optional[float] = None, attn_split: int = 0, chunk_rows: int = 0,
                 out: Optional[dict] = None, ws: Optional[torch.Tensor] = None, stage_events=None,
                 select: str = "auto") -> dict:
     """The whole path.  ``inp`` holds q_idx, k_idx, w, q_pos, q, k, v (device tensors).
+    ``two_stage``: False (flat), True (block prefilter, then tokens) or "pooled" (the keys
+    of the kept blocks; k_top = n_keep * block_size); ``inp["block_keys"]`` (optional,
+    from lsa_block_cache) spares the block modes rebuilding the block-key cache.
     Paged caches: ``inp`` also holds page_table (int32 [B, max_pages]) and page_size;
     k_idx, k and v are then pools [n_slots, .] and idx receives pool rows.
     Returns dict(idx, count, out, lse[, kept]); pass ``out`` / ``ws`` to reuse buffers.
@@ -336,6 +364,8 @@ def lsa_forward(inp: dict, k_top: int, two_stage: bool = False, block_size: int 
         _need(inp[name], name, dt, dev)
     if inp.get("page_table") is not None:
         _need(inp["page_table"], "page_table", torch.int32, dev)
+    if inp.get("block_keys") is not None:
+        _need(inp["block_keys"], "block_keys", torch.int8, dev)
     B, n_q = q_idx.shape[:2]
     H_q = q.shape[2]
     if out is None:

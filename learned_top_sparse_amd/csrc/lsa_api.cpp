@@ -187,6 +187,20 @@ LSA_API lsa_status lsa_block_prefilter(const int8_t* q_idx, const int32_t* reps,
                        kept_blocks, bs, s);
 }
 
+LSA_API lsa_status lsa_block_cache(const int8_t* k_idx, int32_t B, int32_t L_max, int32_t d_I, int32_t block_size,
+                                   int32_t n_blocks, int32_t first_block, int32_t n_update, int8_t* block_keys,
+                                   void* stream) {
+  if (B < 0 || L_max < 1 || block_size < 1 || n_blocks < 0 || first_block < 0 || n_update < 0 ||
+      (long long)first_block + n_update > n_blocks || ((long long)first_block + n_update) * block_size > L_max)
+    return LSA_ERR_INVALID_ARG;
+  if (d_I != 64 && d_I != 128) return LSA_ERR_UNSUPPORTED;
+  if (block_size > 128) return LSA_ERR_UNSUPPORTED;
+  if ((long long)B * n_update == 0) return LSA_OK;
+  if (!k_idx || !block_keys) return LSA_ERR_INVALID_ARG;
+  return hip_status(lsa::launch_block_cache(k_idx, B, L_max, d_I, block_size, n_blocks, first_block, n_update,
+                                            block_keys, as_stream(stream)));
+}
+
 LSA_API lsa_status lsa_topk_workspace_size(int32_t B, int32_t n_q, int32_t L_max, int32_t k, size_t* bytes) {
   if (!bytes || B < 0 || n_q < 0 || L_max < 0 || k < 0) return LSA_ERR_INVALID_ARG;
   *bytes = lsa::topk_ws_bytes((long long)B * n_q, L_max);
@@ -310,9 +324,15 @@ lsa_status check_forward(const lsa_forward_args* a) {
   if (a->H_I < 1 || a->H_I > 64 || a->d != 128 || a->H_q < 1 || a->H_q > 16) return LSA_ERR_UNSUPPORTED;
   if (a->k_top > 4096) return LSA_ERR_UNSUPPORTED;
   if (a->select_mode < LSA_SELECT_AUTO || a->select_mode > LSA_SELECT_FORCE_OVERFLOW) return LSA_ERR_INVALID_ARG;
+  if (a->two_stage < 0 || a->two_stage > 2) return LSA_ERR_INVALID_ARG;
   if (a->two_stage) {
     if (a->block_size < 1 || a->n_keep < 1) return LSA_ERR_INVALID_ARG;
-    if (a->block_size > 128 || a->n_keep > 256 || a->L_max / a->block_size > 65536) return LSA_ERR_UNSUPPORTED;
+    if (a->block_size > 128 || a->L_max / a->block_size > 65536) return LSA_ERR_UNSUPPORTED;
+    if (a->two_stage == 1 && a->n_keep > 256) return LSA_ERR_UNSUPPORTED;  // the token stage's kept table
+    // pooled blocks: the list is the keys of the kept blocks
+    if (a->two_stage == 2 && (long long)a->n_keep * a->block_size != a->k_top) return LSA_ERR_INVALID_ARG;
+  } else if (a->block_keys) {
+    return LSA_ERR_INVALID_ARG;
   }
   if (a->page_table) {
     if (a->page_size < 64 || (a->page_size & (a->page_size - 1)) != 0 || a->max_pages < 1 ||
@@ -363,9 +383,11 @@ FwdPlan plan_forward(const lsa_forward_args* a) {
   p.decode_like = a->n_q == 1;
   if (a->two_stage) {
     p.n_blocks = a->L_max / a->block_size;
-    p.ld = (int64_t)a->n_keep * a->block_size;
+    // the token stage's score rows (pooled blocks have none)
+    p.ld = a->two_stage == 2 ? 0 : (int64_t)a->n_keep * a->block_size;
     p.per_row = p.ld * 4 + (long long)p.n_blocks * 8 + (a->kept_blocks ? 0 : (long long)a->n_keep * 4) + 64;
-    p.fixed = align_up((size_t)a->B * p.n_blocks * a->d_I * 4) + align_up((size_t)a->B * p.n_blocks * 2 * a->d_I);
+    // the block-key cache, unless the caller keeps one
+    p.fixed = a->block_keys ? 0 : align_up((size_t)a->B * p.n_blocks * 2 * a->d_I);
   } else {
     p.n_blocks = 0;
     p.ld = score_ld(a->L_max);
@@ -453,10 +475,15 @@ void for_each_chunk(const lsa_forward_args* a, long long rows, F f) {
 // stage codes of lsa_forward in launch order (rows per chunk already planned)
 std::vector<int32_t> forward_stages(const lsa_forward_args* a, const FwdPlan& p, long long rows) {
   std::vector<int32_t> st;
-  if (a->two_stage && p.n_blocks > 0) st.push_back(LSA_STAGE_BLOCK_REPS);
+  if (a->two_stage && p.n_blocks > 0 && !a->block_keys) st.push_back(LSA_STAGE_BLOCK_REPS);
   const size_t topk_ws_size = a->two_stage ? 0 : topk_ws_for(a, rows);
   for_each_chunk(a, rows, [&](int32_t, int32_t nb, int32_t, int32_t ni) {
     if (a->two_stage) st.push_back(LSA_STAGE_BLOCK_PREFILTER);
+    if (a->two_stage == 2) {
+      st.push_back(LSA_STAGE_EXPAND);
+      st.push_back(LSA_STAGE_SPARSE_ATTN);
+      return;
+    }
     const bool thr = chunk_thr(a, nb, ni, topk_ws_size);
     if (thr) st.push_back(LSA_STAGE_SAMPLE);
     st.push_back(chunk_fused(a, nb, ni, topk_ws_size) || thr ? LSA_STAGE_INDEX_SELECT : LSA_STAGE_INDEX_SCORES);
@@ -518,12 +545,11 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
   // workspace carve-up
   char* base = static_cast<char*>(ws);
   size_t off = 0;
-  int32_t* reps = nullptr;
-  int8_t* limbs = nullptr;
-  if (a->two_stage) {
-    reps = reinterpret_cast<int32_t*>(base + off);
-    off += align_up((size_t)a->B * p.n_blocks * a->d_I * 4);
-    limbs = reinterpret_cast<int8_t*>(base + off);
+  const int8_t* limbs = a->block_keys;  // block-key cache: the caller's, else built here
+  int8_t* limbs_ws = nullptr;
+  if (a->two_stage && !a->block_keys) {
+    limbs_ws = reinterpret_cast<int8_t*>(base + off);
+    limbs = limbs_ws;
     off += align_up((size_t)a->B * p.n_blocks * 2 * a->d_I);
   }
   int32_t* sc = reinterpret_cast<int32_t*>(base + off);
@@ -567,11 +593,11 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
   const int32_t d_I = a->d_I, H_I = a->H_I, H_q = a->H_q, d = a->d, L = a->L_max, kt = a->k_top;
   // one split count for every chunk, so no chunk needs more attention workspace than sized
   const int split = resolve_split(1, (int32_t)rows, kt, a->attn_split);
-  if (a->two_stage && p.n_blocks > 0) {
-    if (lsa::launch_block_reps(a->k_idx, a->B, L, d_I, a->block_size, p.n_blocks, reps, s) != hipSuccess)
+  if (a->two_stage && p.n_blocks > 0 && limbs_ws) {
+    if (lsa::launch_block_cache(a->k_idx, a->B, L, d_I, a->block_size, p.n_blocks, 0, p.n_blocks, limbs_ws, s) !=
+            hipSuccess ||
+        !mark())
       return LSA_ERR_HIP;
-    if (lsa::launch_block_limbs(reps, a->B, p.n_blocks, d_I, limbs, s) != hipSuccess) return LSA_ERR_HIP;
-    if (!mark()) return LSA_ERR_HIP;
   }
 
   // one chunk: sequences [b0, b0+nb) x queries [i0, i0+ni) (either nb == 1 or ni == n_q == 1)
@@ -614,6 +640,15 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
       ia.block_size = a->block_size;
       ia.n_keep = a->n_keep;
       if (!mark()) return LSA_ERR_HIP;
+      if (a->two_stage == 2) {
+        // pooled blocks: the list is every key of the kept blocks the query may see
+        if (lsa::launch_expand(kept, qp, (long long)nb * ni, a->block_size, a->n_keep, kt, ix, cnt, s) != hipSuccess ||
+            !mark())
+          return LSA_ERR_HIP;
+        lsa_status sa = run_attn(qq, kk, vv, ix, nb, ni, L, H_q, d, kt, a->scale, split, oo, ls, attn_ws, s);
+        if (sa != LSA_OK) return sa;
+        return mark() ? LSA_OK : LSA_ERR_HIP;
+      }
     }
     ia.use_direct = a->two_stage ? true : ni < 8;
     ia.span = flat_span(L, ia.use_direct);

@@ -756,6 +756,26 @@ __global__ void blk_limbs_kernel(const int32_t* __restrict__ reps, int D, long l
   limbs[rowi * 2 * D + D + c] = (int8_t)lo;
 }
 
+// Block-key cache: blocks [m0, m0 + n_upd) of every sequence, each written as the
+// two int8 limbs of its representative (the sum of its bs keys), rows laid out as
+// blk_limbs_kernel writes them.  Thread e: one byte column c of block m.
+__global__ void blk_cache_kernel(const int8_t* __restrict__ k_idx, int L_max, int D, int bs, int n_blocks, int m0,
+                                 int n_upd, long long total, int8_t* __restrict__ limbs) {
+  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  const int c = (int)(e % D);
+  const long long bm = e / D;
+  const int m = m0 + (int)(bm % n_upd);
+  const long long b = bm / n_upd;
+  const int8_t* src = k_idx + (b * L_max + (long long)m * bs) * D + c;
+  int r = 0;
+  for (int t = 0; t < bs; ++t) r += src[(long long)t * D];
+  const int hi = (r + 64) >> 7;
+  int8_t* dst = limbs + (b * n_blocks + m) * 2 * D;
+  dst[c] = (int8_t)hi;
+  dst[D + c] = (int8_t)(r - (hi << 7));
+}
+
 // Block scores with the flat kernel's tiling: the "keys" are block limb rows of
 // 2*D bytes; q.r = 128*(q.hi) + (q.lo) is exact in int32 (|q.r| < 2^29), then
 // ReLU and the weighted head sum accumulate in int64.  Block m is scored for a
@@ -880,6 +900,97 @@ __global__ __launch_bounds__(256, 2) void blk_scores_kernel(
     if (t + 1 < n_tiles) swrite(buf ^ 1);
     __syncthreads();
   }
+}
+
+// ---------------------------------------------------------------------------------
+// Block scores of decode-shaped rows (few queries per sequence, many blocks): one
+// query per workgroup of 4 waves and a span of its blocks; each wave streams 32-block
+// groups of block-key rows (hi, lo parts) straight into MFMA B fragments through a
+// ring of RING register stages (loads unconditional, clamped to the span's last
+// block), as the flat decode scan does with index keys.  Per block: the two dot
+// products give q.r = 128 (q.hi) + q.lo exactly in int32, then ReLU and the weighted
+// head sum in int64; the sum over the four 16-lane rows ends with one value per block
+// in lanes of rows 0 and 2.  Blocks m < own = min(floor(q_pos / bs), n_blocks) are
+// scored.  The span's scores collect in LDS (span <= BLK_DEC_SPAN) and leave in one
+// burst at the end: a store between the ring's loads would make the next wait drain
+// the loads in flight (loads and stores share one counter).
+// Grid: x = spans, y = B * n_q.
+constexpr int BLK_DEC_SPAN = 4096;
+template <int D, int MT>
+__global__ __launch_bounds__(256, 2) void blk_decode_kernel(
+    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ limbs, const int32_t* __restrict__ w,
+    int w_per_query, const int32_t* __restrict__ q_pos, int n_q, int n_blocks, int H_I, int bs, int span,
+    long long* __restrict__ bscores, long long ld) {
+  constexpr int KS = D / 64, RB = 2 * D, RING = 4, GB = 32;  // GB blocks per group
+  __shared__ __attribute__((aligned(16))) long long sbuf[BLK_DEC_SPAN];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const long long row = blockIdx.y;
+  const int b = (int)(row / n_q);
+  v4i A[MT][KS];
+  int wv[MT][4];
+  issue_query<D, MT>(q_idx, w, w_per_query, row, H_I, A, wv);
+  const int p = q_pos[row];
+  if (p < 0) return;
+  const int own = min(p / bs, n_blocks);
+  const int m_begin = blockIdx.x * span, m_end = min(m_begin + span, own);
+  if (m_begin >= m_end) return;  // uniform
+  const int8_t* lb = limbs + (long long)b * n_blocks * RB;
+  const int n_groups = (m_end - m_begin + GB - 1) / GB;
+  // this wave's groups: wave, wave + 4, ...; padded to a multiple of RING (the extra
+  // loads re-read the span's last block and are not computed)
+  const int n_my = wave < n_groups ? (n_groups - wave + 3) / 4 : 0;
+  const int n_iter = (n_my + RING - 1) / RING * RING;
+  v4i ring[RING][2][2][KS];  // [stage][nt][part][ks]
+  auto load_group = [&](int i, v4i (&Bf)[2][2][KS]) {
+    const int sg = m_begin + GB * (wave + 4 * i);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int8_t* br = lb + (long long)min(sg + 16 * nt + r16, m_end - 1) * RB;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) Bf[nt][h][ks] = *(const v4i*)(br + h * D + 16 * kchunk<D>(g, ks));
+    }
+  };
+#pragma unroll
+  for (int r = 0; r < RING - 1; ++r) load_group(r, ring[r]);
+  int wt[MT][4];
+  query_weights<MT>(wv, H_I, true, wt);
+  auto compute_group = [&](int i, const v4i (&Bf)[2][2][KS]) {
+    long long part[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      long long ps = 0;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        v4i ah = v4i{0, 0, 0, 0}, al = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          ah = mfma_i8(A[mt][ks], Bf[nt][0][ks], ah);
+          al = mfma_i8(A[mt][ks], Bf[nt][1][ks], al);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ps += (long long)wt[mt][e] * (long long)max((ah[e] << 7) + al[e], 0);
+      }
+      part[nt] = ps;
+    }
+    // rows 0, 1 of the lower half end with block (nt 0, r16); rows 2, 3 with (nt 1, r16)
+    const long long hsum = xhalf32_sum64(part[0], part[1]);
+    const long long tot = xrow16_sum64(hsum, hsum);
+    const int m = m_begin + GB * (wave + 4 * i) + 16 * (g >> 1) + r16;
+    if ((g & 1) == 0 && m < m_end) sbuf[m - m_begin] = tot;
+  };
+  for (int i0 = 0; i0 < n_iter; i0 += RING) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      const int i = i0 + r;
+      load_group(min(i + RING - 1, n_my - 1), ring[(r + RING - 1) % RING]);
+      if (i < n_my) compute_group(i, ring[r]);
+    }
+  }
+  __syncthreads();
+  long long* srow = bscores + row * ld + m_begin;
+  for (int t = tid; t < m_end - m_begin; t += 256) srow[t] = sbuf[t];
 }
 
 // ---------------------------------------------------------------------------------
@@ -1009,6 +1120,16 @@ hipError_t launch_block_limbs(const int32_t* reps, int B, int n_blocks, int d_I,
   return hipGetLastError();
 }
 
+hipError_t launch_block_cache(const int8_t* k_idx, int B, int L_max, int d_I, int bs, int n_blocks, int m0,
+                              int n_upd, int8_t* limbs, hipStream_t st) {
+  const long long total = (long long)B * n_upd * d_I;
+  if (total == 0) return hipSuccess;
+  if (m0 < 0 || n_upd < 0 || m0 + n_upd > n_blocks || (long long)(m0 + n_upd) * bs > L_max) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(blk_cache_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, k_idx, L_max, d_I,
+                     bs, n_blocks, m0, n_upd, total, limbs);
+  return hipGetLastError();
+}
+
 template <int D, int MT>
 static hipError_t launch_blk_scores_t(const BlkArgs& a, hipStream_t st) {
   const int QT = 8;
@@ -1023,7 +1144,33 @@ static hipError_t launch_blk_scores_t(const BlkArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int D, int MT>
+static hipError_t launch_blk_decode_t(const BlkArgs& a, hipStream_t st) {
+  const long long rows = (long long)a.B * a.n_q;
+  // about 512 workgroups in all (two per compute unit, all resident at once), spans of
+  // at least 512 blocks
+  long long want = std::max(1ll, std::min((512 + rows - 1) / rows, (long long)(a.n_blocks + 511) / 512));
+  want = std::max(want, (long long)(a.n_blocks + BLK_DEC_SPAN - 1) / BLK_DEC_SPAN);  // spans fit the LDS buffer
+  const int span = (int)std::min<long long>(((a.n_blocks + want - 1) / want + 31) / 32 * 32, BLK_DEC_SPAN);
+  const int n_spans = (a.n_blocks + span - 1) / span;
+  hipLaunchKernelGGL((blk_decode_kernel<D, MT>), dim3((unsigned)n_spans, (unsigned)rows), dim3(256), 0, st,
+                     a.q_idx, a.limbs, a.w, a.w_per_query, a.q_pos, a.n_q, a.n_blocks, a.H_I, a.block_size, span,
+                     a.bscores, a.ld);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_scores(const BlkArgs& a, hipStream_t st) {
+  if (a.n_q < 8) {  // decode-shaped rows: one query per workgroup
+    if (a.d_I == 128) {
+#define C(MT) launch_blk_decode_t<128, MT>(a, st)
+      LSA_DISPATCH_MT(a.H_I, C)
+#undef C
+    } else {
+#define C(MT) launch_blk_decode_t<64, MT>(a, st)
+      LSA_DISPATCH_MT(a.H_I, C)
+#undef C
+    }
+  }
   if (a.d_I == 128) {
 #define C(MT) launch_blk_scores_t<128, MT>(a, st)
     LSA_DISPATCH_MT(a.H_I, C)

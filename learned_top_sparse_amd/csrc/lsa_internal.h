@@ -119,6 +119,12 @@ hipError_t launch_block_reps(const int8_t* k_idx, int B, int L_max, int d_I, int
 hipError_t launch_block_limbs(const int32_t* reps, int B, int n_blocks, int d_I, int8_t* limbs,
                               hipStream_t st);
 hipError_t launch_block_scores(const BlkArgs& a, hipStream_t st);
+// block-key cache (the limbs of the representatives) of blocks [m0, m0 + n_upd)
+hipError_t launch_block_cache(const int8_t* k_idx, int B, int L_max, int d_I, int bs, int n_blocks, int m0,
+                              int n_upd, int8_t* limbs, hipStream_t st);
+// pooled blocks: index lists = the keys of the kept blocks a query may see
+hipError_t launch_expand(const int32_t* kept, const int32_t* q_pos, long long rows, int bs, int n_keep, int k,
+                         int32_t* idx, int32_t* count, hipStream_t st);
 hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 // workspace that lets lsa_topk split each row over several workgroups (0 = not used)

@@ -1438,6 +1438,176 @@ __global__ __launch_bounds__(NT) void blk_select_kernel(const long long* __restr
   for (int t = written + 1 + tid; t < n_keep; t += NT) out[t] = -1;
 }
 
+// Block keep of rows with many blocks and one workgroup each (decode): the same result
+// as blk_select_kernel, with the row's scores held in registers (thread t: blocks
+// t, t + NT, ..., at most C of them) instead of re-read per pass.  The cut T (the
+// n_sel-th best key) comes from radix passes of DIG-bit digits over the bits below
+// the prefix all keys share, counted in an LDS histogram; then, in block order, the
+// blocks with key > T and the first need_eq blocks with key == T are kept (bitmaps of
+// the row's blocks, one scan for the ranks among equal keys and one for the output).
+template <int NT, int C>
+__global__ __launch_bounds__(NT) void blk_keep_rows_kernel(const long long* __restrict__ bscores, long long ld,
+                                                           const int32_t* __restrict__ q_pos, int n_blocks, int bs,
+                                                           int n_keep, int32_t* __restrict__ kept) {
+  constexpr int NW = NT / 64, DIG = 11, NBIN = 1 << DIG, BPT = NBIN / NT;
+  static_assert(NBIN % NT == 0, "whole bins per thread");
+  __shared__ int hist[NBIN];
+  __shared__ int scan_tmp[NW + 1];
+  __shared__ unsigned long long shu[2];
+  __shared__ int sh[2];
+  const long long row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int p = q_pos[row];
+  int32_t* out = kept + row * (long long)n_keep;
+  if (p < 0) {
+    for (int t = tid; t < n_keep; t += NT) out[t] = -1;
+    return;
+  }
+  const int own = p / bs;
+  const int n_sc = min(own, n_blocks);  // scored earlier blocks
+  const int n_sel = min(n_keep - 1, n_sc);
+  const long long* br = bscores + row * ld;
+  int written;
+  if (n_sel >= n_sc) {
+    for (int m = tid; m < n_sc; m += NT) out[m] = m;
+    written = n_sc;
+  } else {
+    unsigned long long key[C];
+    unsigned long long mx = 0ull, mn = ~0ull;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int m = c * NT + tid;
+      key[c] = m < n_sc ? (unsigned long long)br[m] ^ 0x8000000000000000ull : 0ull;
+      if (m < n_sc) {
+        mx = key[c] > mx ? key[c] : mx;
+        mn = key[c] < mn ? key[c] : mn;
+      }
+    }
+    auto valid = [&](int c) { return c * NT + tid < n_sc; };
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long a = __shfl_xor(mx, o), b = __shfl_xor(mn, o);
+      mx = a > mx ? a : mx;
+      mn = b < mn ? b : mn;
+    }
+    if (tid == 0) {
+      shu[0] = 0ull;
+      shu[1] = ~0ull;
+    }
+    __syncthreads();
+    if (lane == 0) {
+      atomicMax(&shu[0], mx);
+      atomicMin(&shu[1], mn);
+    }
+    __syncthreads();
+    mx = shu[0];
+    mn = shu[1];
+    int need = n_sel;
+    unsigned long long pref = mx, pmask = ~0ull;
+    if (mx != mn) {
+      const int hb = 63 - __clzll((long long)(mx ^ mn));  // highest bit where keys differ
+      pmask = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
+      pref = mx & pmask;
+      for (int top = hb; top >= 0; top -= DIG) {
+        const int lo = max(0, top - DIG + 1);
+        const int nb = 1 << (top - lo + 1);
+        for (int t = tid; t < nb; t += NT) hist[t] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+          if (valid(c) && (key[c] & pmask) == pref) atomicAdd(&hist[(int)((key[c] >> lo) & (nb - 1))], 1);
+        __syncthreads();
+        // thread t sums bins nb-1-BPT*t .. nb-BPT*(t+1) (from the top); the one whose range
+        // holds the need-th entry walks it
+        int csum = 0;
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+          const int bin = nb - 1 - BPT * tid - j;
+          csum += bin >= 0 ? hist[bin] : 0;
+        }
+        int tot;
+        const int excl = block_exclusive_scan<NT>(csum, scan_tmp, &tot);
+        if (excl < need && excl + csum >= need) {
+          int acc = excl;
+          for (int j = 0; j < BPT && nb - 1 - BPT * tid - j >= 0; ++j) {
+            const int bin = nb - 1 - BPT * tid - j;
+            const int h = hist[bin];
+            if (acc + h >= need) {
+              sh[0] = bin;
+              sh[1] = acc;
+              break;
+            }
+            acc += h;
+          }
+        }
+        __syncthreads();
+        need -= sh[1];
+        pref |= (unsigned long long)sh[0] << lo;
+        pmask |= (unsigned long long)(nb - 1) << lo;
+        __syncthreads();
+      }
+    }
+    const unsigned long long T = pref;
+    const int need_eq = need;  // blocks equal to T to keep, the lowest first
+    // bitmaps over the row's blocks: gt = key > T, eq = key == T; thread t then owns
+    // words [WPT t, WPT t + WPT) and keeps their gt bits and the eq bits whose rank among
+    // all eq bits (in block order) is below need_eq
+    constexpr int NWD = C * NT / 32, WPT = NWD / NT;
+    unsigned* gt = reinterpret_cast<unsigned*>(hist);  // NBIN ints: NWD words each
+    unsigned* eq = gt + NWD;
+    static_assert(2 * NWD <= NBIN, "both bitmaps in the histogram's LDS");
+    __syncthreads();
+    for (int t = tid; t < 2 * NWD; t += NT) gt[t] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      if (!valid(c)) continue;
+      const int m = c * NT + tid;
+      if (key[c] > T) atomicOr(&gt[m >> 5], 1u << (m & 31));
+      else if (key[c] == T) atomicOr(&eq[m >> 5], 1u << (m & 31));
+    }
+    __syncthreads();
+    unsigned wg[WPT], we[WPT];
+    int n_eq = 0;
+#pragma unroll
+    for (int j2 = 0; j2 < WPT; ++j2) {
+      wg[j2] = gt[WPT * tid + j2];
+      we[j2] = eq[WPT * tid + j2];
+      n_eq += __popc(we[j2]);
+    }
+    int tot;
+    int eq_before = block_exclusive_scan<NT>(n_eq, scan_tmp, &tot);
+    int n_take = 0;
+#pragma unroll
+    for (int j2 = 0; j2 < WPT; ++j2) {
+      // the eq bits of this word with rank < need_eq
+      unsigned keep = 0u, e = we[j2];
+      while (e != 0u && eq_before < need_eq) {
+        const unsigned low = e & (0u - e);
+        keep |= low;
+        e ^= low;
+        ++eq_before;
+      }
+      wg[j2] |= keep;
+      n_take += __popc(wg[j2]);
+    }
+    int r = block_exclusive_scan<NT>(n_take, scan_tmp, &tot);
+#pragma unroll
+    for (int j2 = 0; j2 < WPT; ++j2) {
+      unsigned bits = wg[j2];
+      while (bits != 0u) {
+        const int bit = __ffs(bits) - 1;
+        bits &= bits - 1u;
+        if (r < n_keep - 1) out[r] = 32 * (WPT * tid + j2) + bit;
+        ++r;
+      }
+    }
+    written = tot;
+  }
+  written = min(written, n_keep - 1);
+  if (tid == 0) out[written] = own;
+  for (int t = written + 1 + tid; t < n_keep; t += NT) out[t] = -1;
+}
+
 }  // namespace
 
 size_t topk_ws_bytes(long long rows, int L_max) {
@@ -1561,9 +1731,52 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   return a.kept != nullptr ? launch_topk_t<true>(a, st, rows) : launch_topk_t<false>(a, st, rows);
 }
 
+// Pooled blocks: the index list of a query is every key of its kept blocks that it
+// may see, idx[r] = kept[r / bs] * bs + r % bs if that block is kept and the key is
+// <= the query's position, else -1.  kept is ascending with the own block last, so
+// the valid keys form a prefix in ascending order; count = their number.
+template <int NT>
+__global__ __launch_bounds__(NT) void expand_kernel(const int32_t* __restrict__ kept, const int32_t* __restrict__ q_pos,
+                                                    int bs, int n_keep, int k, int32_t* __restrict__ idx,
+                                                    int32_t* __restrict__ count) {
+  __shared__ int scan_tmp[NT / 64 + 1];
+  const long long row = blockIdx.x;
+  const int p = q_pos[row];
+  const int32_t* kr = kept + row * (long long)n_keep;
+  int32_t* out = idx + row * (long long)k;
+  int n = 0;
+  for (int r = threadIdx.x; r < k; r += NT) {
+    const int blk = r / bs < n_keep ? kr[r / bs] : -1;
+    const int key = blk * bs + r % bs;
+    const bool ok = blk >= 0 && key <= p;
+    out[r] = ok ? key : -1;
+    n += ok ? 1 : 0;
+  }
+  if (count != nullptr) {
+    int tot;
+    block_exclusive_scan<NT>(n, scan_tmp, &tot);
+    if (threadIdx.x == 0) count[row] = tot;
+  }
+}
+
+hipError_t launch_expand(const int32_t* kept, const int32_t* q_pos, long long rows, int bs, int n_keep, int k,
+                         int32_t* idx, int32_t* count, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if (bs < 1 || n_keep < 1 || k < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(expand_kernel<256>, dim3((unsigned)rows), dim3(256), 0, st, kept, q_pos, bs, n_keep, k, idx,
+                     count);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st) {
   const long long rows = (long long)a.B * a.n_q;
   if (rows == 0) return hipSuccess;
+  if (a.n_q < 8 && a.n_blocks > 4096 && a.n_blocks <= 1024 * 32) {
+    // few long rows (decode): the row's scores in registers of one workgroup
+    hipLaunchKernelGGL((blk_keep_rows_kernel<1024, 32>), dim3((unsigned)rows), dim3(1024), 0, st, a.bscores, a.ld,
+                       a.q_pos, a.n_blocks, a.block_size, a.n_keep, a.kept);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(blk_select_kernel<256>, dim3((unsigned)rows), dim3(256), 0, st, a.bscores, a.ld,
                      a.q_pos, a.n_blocks, a.block_size, a.n_keep, a.kept);
   return hipGetLastError();

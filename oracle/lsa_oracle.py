@@ -167,12 +167,16 @@ def sparse_attention(q_row, k_cache, v_cache, J, scale: float):
 
 def forward_row(q_idx_row, k_idx, w, p: int, k: int, q_row=None, k_cache=None,
                 v_cache=None, scale: float | None = None, two_stage: bool = False,
-                block_size: int = 128, n_keep: int = 64, reps=None):
+                block_size: int = 128, n_keep: int = 64, reps=None, pooled: bool = False):
     """The whole path for one query row: candidates -> scores -> top-k -> attention.
 
     Flat: candidates are keys 0..p.  Two-stage ([HISA]): kept blocks first, then
-    the same token scores over the kept keys.  Returns a dict with J, count,
-    and (if q_row is given) out / lse; two-stage adds kept (padded to n_keep).
+    the same token scores over the kept keys.  Pooled (with two_stage; [LSA] §2.2
+    "Related Work": indexers that score one pooled key per block of consecutive
+    keys): the kept blocks' visible keys are the list itself, no token stage --
+    J = those keys ascending, padded with -1 to k (k = n_keep * block_size).
+    Returns a dict with J, count, and (if q_row is given) out / lse; the block modes
+    add kept (padded to n_keep).
     """
     L = k_idx.shape[0]
     res = {}
@@ -181,11 +185,20 @@ def forward_row(q_idx_row, k_idx, w, p: int, k: int, q_row=None, k_cache=None,
             reps = block_reps(k_idx, block_size)
         kept, _ = block_keep(q_idx_row, reps, w, p, block_size, n_keep)
         cand = two_stage_candidates(kept, p, block_size, L)
-        dots = _int_dots(q_idx_row, k_idx[cand]) if cand.size else np.zeros((len(w), 0), np.int64)
-        sc = _weighted_relu_sum(dots, w)
         kp = np.full((n_keep,), -1, dtype=np.int64)
         kp[: kept.size] = kept
         res["kept"] = kp
+        if pooled:
+            J = np.full((k,), -1, dtype=np.int64)
+            J[: cand.size] = cand
+            res["J"], res["count"] = J, int(cand.size)
+            if q_row is not None:
+                if scale is None:
+                    scale = 1.0 / np.sqrt(q_row.shape[-1])
+                res["out"], res["lse"] = sparse_attention(q_row, k_cache, v_cache, J, scale)
+            return res
+        dots = _int_dots(q_idx_row, k_idx[cand]) if cand.size else np.zeros((len(w), 0), np.int64)
+        sc = _weighted_relu_sum(dots, w)
     else:
         sc = index_scores(q_idx_row, k_idx, w, p)
         cand = np.arange(sc.shape[0], dtype=np.int64)

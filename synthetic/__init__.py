@@ -49,6 +49,7 @@ class Workload:
     block_size: int = 128
     n_keep: int = 64
     seed: int = 0
+    pooled: bool = False    # two_stage with the kept blocks' keys as the list (k = n_keep * block_size)
     page_size: int = 0      # > 0: caches scattered over a pool of pages (paged_pool)
     spare_pages: int = 0    # unused pool pages besides the sequences' own
 
@@ -81,6 +82,11 @@ WORKLOADS = {
     # decode_128k with its caches scattered over a pool of 64-token pages (serving layout)
     "decode_128k_paged": Workload("decode_128k_paged", B=64, n_q=1, L=131073, q_pos0=131072,
                                   H_I=64, d_I=128, k=2048, H_q=16, page_size=64, spare_pages=4096),
+    # decode_128k with a 4:1 pooled indexer: one pooled key per 4 keys, the best 512 blocks
+    # (own block included) give the 2048-key list
+    "decode_128k_pool4": Workload("decode_128k_pool4", B=64, n_q=1, L=131073, q_pos0=131072,
+                                  H_I=64, d_I=128, k=2048, H_q=16, two_stage=True, pooled=True,
+                                  block_size=4, n_keep=512),
     # two-stage (block prefilter, then tokens) on the final 8192 queries of 128K
     "two_stage_128k": Workload("two_stage_128k", B=1, n_q=8192, L=131072, q_pos0=122880,
                                H_I=64, d_I=128, k=2048, H_q=16, two_stage=True,

@@ -347,6 +347,51 @@ def check_attention_special(impl, seed=9):
     return _all(r)
 
 
+def check_pooled_hand(impl):
+    """Pooled blocks by hand: one head, one dim, w = 1, q = 1, so a block's score is
+    max(0, the sum of its keys)."""
+    k_idx = np.array([[3], [1], [0], [5], [2], [2], [4], [0], [1], [1]], np.int64)
+    q = np.array([[1]], np.int64)
+    w = np.array([1], np.int64)
+    r = []
+    # blocks of 2: sums 4 5 4 4 2.  p = 8: own block 4 (keys 8, 9; only 8 visible); the best
+    # two earlier blocks are 1 (5) and, among the ties at 4, block 0
+    res = impl.forward_row(q, k_idx, w, 8, 6, two_stage=True, block_size=2, n_keep=3, pooled=True)
+    r.append(_ok(np.array_equal(res["J"], [0, 1, 2, 3, 8, -1]) and res["count"] == 5
+                 and np.array_equal(res["kept"], [0, 1, 4]), f"p=8 {res['J']}"))
+    res = impl.forward_row(q, k_idx, w, 9, 6, two_stage=True, block_size=2, n_keep=3, pooled=True)
+    r.append(_ok(np.array_equal(res["J"], [0, 1, 2, 3, 8, 9]) and res["count"] == 6, f"p=9 {res['J']}"))
+    res = impl.forward_row(q, k_idx, w, 1, 6, two_stage=True, block_size=2, n_keep=3, pooled=True)
+    r.append(_ok(np.array_equal(res["J"], [0, 1, -1, -1, -1, -1]) and res["count"] == 2, f"p=1 {res['J']}"))
+    # a negative query: every block score is ReLU'd to 0, ties go to the lowest blocks
+    res = impl.forward_row(-q, k_idx, w, 7, 6, two_stage=True, block_size=2, n_keep=3, pooled=True)
+    r.append(_ok(np.array_equal(res["J"], [0, 1, 2, 3, 6, 7]), f"all ties {res['J']}"))
+    return _all(r)
+
+
+def check_pooled_dense(impl, seed=12):
+    """Enough kept blocks for every block up to the query's: the list is every key
+    0..p (the flat list with k > p), and attention is dense causal attention."""
+    rng = np.random.default_rng(seed)
+    L, d_I, d, H, bs = 40, 16, 8, 3, 4
+    k_idx = rng.integers(-64, 65, (L, d_I))
+    kc, vc = rng.standard_normal((L, d)), rng.standard_normal((L, d))
+    q_idx = rng.integers(-64, 65, (H, d_I))
+    w = rng.integers(1, 17, (H,))
+    q = rng.standard_normal((H, d))
+    r = []
+    for p in (0, 5, 17, 39):
+        res = impl.forward_row(q_idx, k_idx, w, p, 40, q_row=q, k_cache=kc, v_cache=vc, two_stage=True,
+                               block_size=bs, n_keep=10, pooled=True)
+        want = np.concatenate([np.arange(p + 1), np.full(40 - p - 1, -1)])
+        s = (q @ kc[: p + 1].T) / math.sqrt(d)
+        e = np.exp(s - s.max(1, keepdims=True))
+        dense = (e @ vc[: p + 1]) / e.sum(1, keepdims=True)
+        r.append(_ok(np.array_equal(res["J"], want) and res["count"] == p + 1
+                     and np.allclose(res["out"], dense, atol=1e-13), f"dense p={p}"))
+    return _all(r)
+
+
 def check_paged_hand(impl):
     """Paged caches by hand: pool rows of logical keys, and one worked selection."""
     r = []
@@ -423,4 +468,5 @@ ALL_CHECKS = [
     check_two_stage_reductions, check_two_stage_invariants,
     check_attention_hand, check_attention_dense, check_attention_special,
     check_paged_hand, check_paged_identity, check_paged_permutation,
+    check_pooled_hand, check_pooled_dense,
 ]

@@ -460,6 +460,88 @@ def test_forward_decode_fused_selection(lsa, H_I):
     err.check()
 
 
+def test_block_cache(lsa):
+    """The block-key cache: hi, lo int8 parts with 128 * hi + lo = the block's key sum
+    (lsa_block_reps) and lo in [-64, 63]; a cache built in two partial updates over a
+    stale buffer equals one built whole."""
+    wl = synthetic.Workload("bc", B=3, n_q=1, L=1000, q_pos0=999, H_I=4, d_I=128, k=16, H_q=8)
+    _, g = _inputs(wl, seed=23)
+    for bs in (4, 16, 128):
+        full = lsa.lsa_block_cache(g["k_idx"], bs)
+        reps = lsa.lsa_block_reps(g["k_idx"], bs)
+        hi, lo = full[:, :, 0].long(), full[:, :, 1].long()
+        assert torch.equal(128 * hi + lo, reps.long()), f"bs={bs}"
+        assert int(lo.min()) >= -64 and int(lo.max()) <= 63
+        n = full.shape[1]
+        part = torch.full_like(full, 77)
+        lsa.lsa_block_cache(g["k_idx"], bs, out=part, first_block=0, n_update=n // 2)
+        lsa.lsa_block_cache(g["k_idx"], bs, out=part, first_block=n // 2, n_update=n - n // 2)
+        assert torch.equal(part, full), f"bs={bs}"
+
+
+@pytest.mark.parametrize("case", [
+    # (B, n_q, L, positions, block_size, n_keep)
+    (2, 40, 3000, "random", 4, 64),     # prefill-shaped, own blocks partial and full
+    (5, 1, 9000, "decode", 4, 512),     # decode-shaped, 4:1 blocks, k = 2048
+    (4, 1, 40000, "decode", 4, 256),    # 10000 blocks a row: the register-resident keep
+    (3, 1, 40000, "zeros", 4, 256),     # every block score 0: the lowest blocks are kept
+    (1, 30, 700, "random", 16, 8),      # bigger blocks, few kept; early rows keep all
+])
+def test_forward_pooled_blocks(lsa, case):
+    """Pooled blocks (two_stage = "pooled"): each query keeps its own block and the
+    best n_keep - 1 earlier blocks by pooled-key score, and its list is every key of
+    them it may see.  Lists, kept blocks and counts equal the oracle's (attention within
+    tolerance); with a caller-built block-key cache the call skips block_reps and gives
+    the same bits; where n_keep allows the token stage (n_keep <= 256), the two-stage
+    path with k = n_keep * block_size gives the same bits too (its token top-k keeps
+    every candidate)."""
+    B, n_q, L, mode, bs, nk = case
+    k = nk * bs
+    wl = synthetic.Workload("pooled", B=B, n_q=n_q, L=L, q_pos0=0, H_I=64, d_I=128, k=k, H_q=16)
+    if mode in ("decode", "zeros"):
+        pos = [L - 1, L - 2, 5000, 4 * nk - 1, 3][:B]
+    else:
+        gen = np.random.default_rng(7)
+        pos = np.sort(gen.integers(0, L, (B, n_q)), axis=1)
+        pos[:, 0], pos[:, 1] = 0, bs - 1
+        pos = pos.reshape(-1).tolist()
+    inp, g = _inputs(wl, seed=29, pos=pos)
+    if mode == "zeros":
+        inp["q_idx"].zero_()
+        g["q_idx"].zero_()
+    res = lsa.lsa_forward(g, k_top=k, two_stage="pooled", block_size=bs, n_keep=nk, attn_split=1)
+    ws = lsa.lsa_forward_workspace_size(g, k, two_stage="pooled", block_size=bs, n_keep=nk)
+    assert lsa.lsa_forward_stages(g, k, ws, two_stage="pooled", block_size=bs, n_keep=nk)[:3] == [
+        "block_reps", "block_prefilter", "expand"]
+    gc = dict(g, block_keys=lsa.lsa_block_cache(g["k_idx"], bs))
+    ws = lsa.lsa_forward_workspace_size(gc, k, two_stage="pooled", block_size=bs, n_keep=nk)
+    assert lsa.lsa_forward_stages(gc, k, ws, two_stage="pooled", block_size=bs, n_keep=nk)[:2] == [
+        "block_prefilter", "expand"]
+    res_c = lsa.lsa_forward(gc, k_top=k, two_stage="pooled", block_size=bs, n_keep=nk, attn_split=1)
+    for n in ("idx", "count", "kept", "out", "lse"):
+        assert torch.equal(res[n], res_c[n]), n
+    if nk <= 256:
+        two = lsa.lsa_forward(g, k_top=k, two_stage=True, block_size=bs, n_keep=nk, attn_split=1)
+        for n in ("idx", "count", "kept", "out"):
+            assert torch.equal(res[n], two[n]), n
+    qi, ki, w = inp["q_idx"].numpy(), inp["k_idx"].numpy(), inp["w"].numpy()
+    q, kk, vv = np64(inp["q"]), np64(inp["k"]), np64(inp["v"])
+    J, kept, cnt, out = res["idx"].cpu().numpy(), res["kept"].cpu().numpy(), res["count"].cpu().numpy(), np64(res["out"])
+    qp = inp["q_pos"].numpy()
+    rows = [(b, i) for b in range(B) for i in range(n_q)]
+    if len(rows) > 12:
+        rows = rows[:4] + rows[-4:] + rows[len(rows) // 2: len(rows) // 2 + 4]
+    err = AttnErr()
+    for b, i in rows:
+        r = oracle.forward_row(qi[b, i], ki[b], w, int(qp[b, i]), k, q_row=q[b, i], k_cache=kk[b], v_cache=vv[b],
+                               scale=1.0 / math.sqrt(128), two_stage=True, block_size=bs, n_keep=nk, pooled=True)
+        assert np.array_equal(J[b, i], r["J"]), f"row {(b, i)}"
+        assert np.array_equal(kept[b, i], r["kept"]), f"kept {(b, i)}"
+        assert cnt[b, i] == r["count"]
+        err.add(out[b, i], r["out"], (b, i))
+    err.check()
+
+
 def _map_pages(J, page_table, page_size):
     """Logical keys [B, n_q, k] (or -1) -> pool rows through page_table [B, max_pages]."""
     J = J.long()

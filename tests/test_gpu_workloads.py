@@ -150,3 +150,29 @@ def test_two_stage_128k(lsa):
     max_oth = torch.where(oth, packed_lo, torch.full_like(packed_lo, -big - 1)).max(1).values
     assert bool(((min_sel >= max_oth) | (oth.sum(1) == 0)).all())
     assert bool((sel.sum(1) == torch.clamp(own, max=nk - 1)).all())
+
+
+def test_decode_128k_pool4(lsa):
+    """The pooled (4:1) decode workload at full size, with the block-key cache built
+    beforehand as the benchmark does: sampled rows against the oracle (lists, kept
+    blocks and counts exact, attention within tolerance)."""
+    wl = synthetic.WORKLOADS["decode_128k_pool4"]
+    g = synthetic.make_inputs(wl, dev())
+    g["block_keys"] = lsa.lsa_block_cache(g["k_idx"], wl.block_size)
+    t0 = time.time()
+    res = lsa.lsa_forward(g, k_top=wl.k, two_stage="pooled", block_size=wl.block_size, n_keep=wl.n_keep)
+    torch.cuda.synchronize()
+    print(f"[{wl.name}] forward {time.time() - t0:.3f}s", flush=True)
+    w = g["w"].cpu().numpy()
+    err = AttnErr()
+    for b, _ in synthetic.checked_rows(wl, n_random=6):
+        ki = g["k_idx"][b].cpu().numpy()
+        p = int(g["q_pos"][b, 0])
+        r = oracle.forward_row(g["q_idx"][b, 0].cpu().numpy(), ki, w, p, wl.k, q_row=np64(g["q"][b, 0]),
+                               k_cache=np64(g["k"][b].cpu()), v_cache=np64(g["v"][b].cpu()), scale=wl.scale,
+                               two_stage=True, block_size=wl.block_size, n_keep=wl.n_keep, pooled=True)
+        assert np.array_equal(res["idx"][b, 0].cpu().numpy(), r["J"]), f"seq {b}"
+        assert np.array_equal(res["kept"][b, 0].cpu().numpy(), r["kept"]), f"kept {b}"
+        assert int(res["count"][b, 0]) == r["count"]
+        err.add(np64(res["out"][b, 0]), r["out"], b)
+    err.check()
