@@ -348,6 +348,23 @@ def main():
     del inp, step
     torch.cuda.empty_cache()
 
+    # ---- decode at 128K with the pooled (4:1) indexer, block-key cache resident
+    wpo = synthetic.WORKLOADS["decode_128k_pool4"]
+    inp, step, ms_o = measure(lsa, torch, wpo, args.steps, args.warmup)
+    ko = step.kernel_ms()
+    ao = algorithmic(wpo)
+    res["decode_128k_pool4"] = {
+        "workload": _describe(wpo), "value": wpo.B * wpo.n_q / (ms_o * 1e-3), "unit": "tok/s",
+        "ms_per_step": ms_o, "kernel_ms": ko,
+        "block_scan": {
+            "bound": "hbm", "kernel": "block_prefilter (blk_decode_kernel + blk_keep_rows_kernel)",
+            "bytes_per_step": ao["block_bytes"],
+            "achieved_GBs": ao["block_bytes"] / (ko["block_prefilter"]["ms_per_step"] * 1e-3) / 1e9,
+        },
+    }
+    del inp, step
+    torch.cuda.empty_cache()
+
     # ---- prefill at 128K (two-stage chunk)
     wp = synthetic.WORKLOADS["two_stage_128k"]
     inp, step, ms_p = measure(lsa, torch, wp, args.steps, args.warmup)
