@@ -253,10 +253,10 @@ typedef struct lsa_forward_args {
      n_slots a multiple of it (at most 2^31).  Page ids outside [0, n_slots / page_size)
      are clamped into that range (no fault; the result is then unspecified).  Selection
      runs on logical keys (ties: lower logical index) and idx receives the pool rows of
-     the kept keys, in ascending logical order, -1 padded.  Supported for flat calls of
-     fewer than 8 queries per sequence (n_q < 8, two_stage = 0), else
-     LSA_ERR_UNSUPPORTED; a workspace too small for their selection state gives
-     LSA_ERR_WORKSPACE.  Sequences of different lengths share a call through q_pos;
+     the kept keys, in ascending logical order, -1 padded.  Supported for flat calls
+     (two_stage = 0, else LSA_ERR_UNSUPPORTED): decode and prefill chunks alike; a chunk
+     of fewer than 8 queries per sequence must fit its decode selection state in the
+     workspace (else LSA_ERR_WORKSPACE).  Sequences of different lengths share a call through q_pos;
      with L_max fixed (one per range of context lengths) the launches keep one shape,
      so a captured HIP graph replays for any positions and page tables.
      page_table == NULL: contiguous caches [B, L_max, ...]. */

@@ -339,7 +339,7 @@ lsa_status check_forward(const lsa_forward_args* a) {
         (long long)a->max_pages * a->page_size != a->L_max || a->n_slots < a->page_size ||
         a->n_slots % a->page_size != 0 || a->n_slots > (1ll << 31))
       return LSA_ERR_INVALID_ARG;
-    if (a->two_stage || a->n_q >= 8) return LSA_ERR_UNSUPPORTED;
+    if (a->two_stage) return LSA_ERR_UNSUPPORTED;
   }
   if ((long long)a->B * a->n_q == 0) return LSA_OK;
   if (!a->q_idx || !a->k_idx || !a->w || !a->q_pos || !a->q || !a->k || !a->v || !a->idx || !a->out)
@@ -527,12 +527,13 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
       (long long)a->n_stage_events < 1 + (long long)forward_stages(a, p, rows).size())
     return LSA_ERR_INVALID_ARG;
   if (a->page_table) {
-    // paged caches: every chunk must take the decode selection
+    // paged caches: chunks of fewer than 8 queries per sequence must take the decode selection
     const size_t tws = topk_ws_for(a, rows);
-    bool fused = true;
-    for_each_chunk(a, rows,
-                   [&](int32_t, int32_t nb, int32_t, int32_t ni) { fused = fused && chunk_fused(a, nb, ni, tws); });
-    if (!fused) return LSA_ERR_WORKSPACE;
+    bool ok = true;
+    for_each_chunk(a, rows, [&](int32_t, int32_t nb, int32_t, int32_t ni) {
+      ok = ok && (ni >= 8 || chunk_fused(a, nb, ni, tws));
+    });
+    if (!ok) return LSA_ERR_WORKSPACE;
   }
   int32_t n_marked = 0;
   // records the next stage event (if the caller asked for them)
@@ -661,6 +662,7 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
     ta.n_keep = a->n_keep;
     ta.B = nb;
     ta.n_q = ni;
+    ta.pages = ia.pages;  // paged caches: the top-k writes pool rows
     ta.L_max = L;
     ta.k = kt;
     ta.idx = ix;
@@ -672,7 +674,6 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
       lsa::DecLayout dl;
       if (!lsa::dec_sel_layout((long long)nb * ni, L, kt, &dl)) return LSA_ERR_INTERNAL;
       ta.hist_ready = true;
-      ta.pages = ia.pages;  // paged caches: the finish writes pool rows
       ia.sel_base = static_cast<int*>(topk_ws);
       ia.sel_rec_ints = dl.rec_ints;
       ia.sel_parts = dl.parts;
@@ -698,7 +699,7 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
       if (lsa::launch_index_scores(ia, s) != hipSuccess || !mark()) return LSA_ERR_HIP;
       // ... the list rows' top-k from their lists; rows whose list fell short or
       // overflowed are scored again into the table, and the top-k of the table rows
-      if (lsa::launch_list_topk(qp, rows_c, L, kt, thr, ix, cnt, s) != hipSuccess) return LSA_ERR_HIP;
+      if (lsa::launch_list_topk(qp, rows_c, L, kt, thr, ix, cnt, ni, ia.pages, s) != hipSuccess) return LSA_ERR_HIP;
       lsa::IdxArgs fa = ia;
       fa.thr = lsa::ThrArgs{};
       fa.tile_filter = thr.rstate;

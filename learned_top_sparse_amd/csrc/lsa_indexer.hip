@@ -120,13 +120,17 @@ __device__ __forceinline__ int relu_mad24(int x, int w, int acc) {
 // whenever it nears full and at the end; table rows store their scores as above.
 // tile_filter (optional): only query tiles holding a row of state 2 do any work;
 // row_min: only query tiles holding a row of more than row_min keys do.
+// PAGED: k_idx is a pool of pages of 2^page_log2 >= 64 keys; the pool pages of the
+// workgroup's keys (at most FLAT_PAGES of them: the launcher sizes the spans) are read
+// into LDS first, and each key's row is looked up there.
 // Grid: x = n_qtiles * n_spans (longest query tiles first), y = B.
-template <int D, int MT, int NW, bool SEL>
+constexpr int FLAT_PAGES = 4096;
+template <int D, int MT, int NW, bool SEL, bool PAGED>
 __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
     int w_per_query, const int32_t* __restrict__ q_pos, int n_q, int L_max, int H_I, int span,
     int n_spans, int n_qtiles, int32_t* __restrict__ scores, long long ld, int stride,
-    const int32_t* __restrict__ tile_filter, int row_min, ThrArgs thr) {
+    const int32_t* __restrict__ tile_filter, int row_min, ThrArgs thr, Pages pg) {
   constexpr int KS = D / 64, KT = 64, CH = D / 16;
   constexpr int R = 3;  // register stages of key tiles
   constexpr int WBUF = 512;  // SEL: candidates a wave buffers in LDS
@@ -204,16 +208,30 @@ __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
     wn = 0;
   };
 
-  const int8_t* kb = k_idx + (long long)b * L_max * D;
+  const int8_t* kb = k_idx + (PAGED ? 0ll : (long long)b * L_max * D);
   const int n_tiles = (j_end - j_begin + KT - 1) / KT;
   const int smax = (L_max - 1) / stride;  // last slot with a key
   // thread -> (row, chunk) of the key tile; with fewer chunks than threads the extra
   // threads repeat a chunk and write the same bytes to the same place
   const int cid = tid % (KT * CH), cr = cid / CH, cc = cid % CH;
   const int tile_off = cr * D + 16 * swz<D>(cr, cc);
+  __shared__ int span_pages[PAGED ? FLAT_PAGES : 1];
+  int pg0 = 0;
+  if constexpr (PAGED) {
+    // pages of the keys gload can touch: slots j_begin .. min(j_begin + n_tiles * KT - 1, smax)
+    pg0 = (int)(((long long)j_begin * stride) >> pg.page_log2);
+    const int pg1 = (int)(((long long)min(j_begin + n_tiles * KT - 1, smax) * stride) >> pg.page_log2);
+    const int32_t* pt = pg.page_table + (long long)b * pg.max_pages;
+    for (int t = tid; t <= pg1 - pg0; t += 64 * NW) span_pages[t] = min(max(pt[pg0 + t], 0), pg.n_pages - 1);
+    __syncthreads();
+  }
   auto gload = [&](int t) -> v4i {
     const int js = min(j_begin + min(t, n_tiles - 1) * KT + cr, smax);
-    return *(const v4i*)(kb + (long long)js * stride * D + 16 * cc);
+    long long key = (long long)js * stride;
+    if constexpr (PAGED)
+      key = ((long long)span_pages[(int)(key >> pg.page_log2) - pg0] << pg.page_log2) |
+            (key & ((1ll << pg.page_log2) - 1));
+    return *(const v4i*)(kb + key * D + 16 * cc);
   };
   // dot products of the query's heads with the 16 keys of group nt
   auto mfmas = [&](int buf, int nt, v4i (&acc)[MT]) {
@@ -1001,20 +1019,34 @@ static hipError_t launch_flat_t(const IdxArgs& a, hipStream_t st) {
   const int stride = a.stride > 1 ? a.stride : 1;
   const int n_qtiles = (a.n_q + NW - 1) / NW;
   const int n_slots = (a.L_max - 1) / stride + 1;
-  const int n_spans = (n_slots + a.span - 1) / a.span;
-  dim3 grid((unsigned)(n_qtiles * n_spans), (unsigned)a.B);
-  if (a.thr.theta != nullptr) {
-    if (a.thr.rstate == nullptr || a.thr.cnt == nullptr || a.thr.lslot == nullptr || a.thr.lscore == nullptr ||
-        a.thr.cap < 1)
+  const bool paged = a.pages.page_table != nullptr;
+  int span = a.span;
+  if (paged) {
+    if (a.pages.page_log2 < 6 || a.pages.n_pages < 1 || (long long)a.pages.max_pages << a.pages.page_log2 < a.L_max)
       return hipErrorInvalidValue;
-    hipLaunchKernelGGL((idx_flat_kernel<D, MT, NW, true>), grid, dim3(64 * NW), 0, st, a.q_idx, a.k_idx, a.w,
-                       a.w_per_query, a.q_pos, a.n_q, a.L_max, a.H_I, a.span, n_spans, n_qtiles, a.scores,
-                       (long long)a.ld, stride, a.tile_filter, a.row_min, a.thr);
-  } else {
-    hipLaunchKernelGGL((idx_flat_kernel<D, MT, NW, false>), grid, dim3(64 * NW), 0, st, a.q_idx, a.k_idx, a.w,
-                       a.w_per_query, a.q_pos, a.n_q, a.L_max, a.H_I, a.span, n_spans, n_qtiles, a.scores,
-                       (long long)a.ld, stride, a.tile_filter, a.row_min, a.thr);
+    // a workgroup's keys span at most FLAT_PAGES pages
+    const long long fit = ((long long)(FLAT_PAGES - 2) << a.pages.page_log2) / stride / 64 * 64;
+    if (fit < 64) return hipErrorInvalidValue;
+    span = (int)std::min<long long>(span, fit);
   }
+  const int n_spans = (n_slots + span - 1) / span;
+  dim3 grid((unsigned)(n_qtiles * n_spans), (unsigned)a.B);
+  const bool sel = a.thr.theta != nullptr;
+  if (sel && (a.thr.rstate == nullptr || a.thr.cnt == nullptr || a.thr.lslot == nullptr || a.thr.lscore == nullptr ||
+              a.thr.cap < 1))
+    return hipErrorInvalidValue;
+#define LSA_FLAT(SEL, PG)                                                                                         \
+  hipLaunchKernelGGL((idx_flat_kernel<D, MT, NW, SEL, PG>), grid, dim3(64 * NW), 0, st, a.q_idx, a.k_idx, a.w,     \
+                     a.w_per_query, a.q_pos, a.n_q, a.L_max, a.H_I, span, n_spans, n_qtiles, a.scores,             \
+                     (long long)a.ld, stride, a.tile_filter, a.row_min, a.thr, a.pages)
+  if (sel) {
+    if (paged) LSA_FLAT(true, true);
+    else LSA_FLAT(true, false);
+  } else {
+    if (paged) LSA_FLAT(false, true);
+    else LSA_FLAT(false, false);
+  }
+#undef LSA_FLAT
   return hipGetLastError();
 }
 template <int D, int MT, bool KEPT>
@@ -1065,8 +1097,8 @@ static hipError_t launch_direct_t(const IdxArgs& a, hipStream_t st) {
   }
 
 hipError_t launch_index_scores(const IdxArgs& a, hipStream_t st) {
-  // paged caches: the decode selection only
-  if (a.pages.page_table != nullptr && (a.kept != nullptr || !a.use_direct || a.sel_base == nullptr))
+  // paged caches: the decode selection and the flat prefill kernel
+  if (a.pages.page_table != nullptr && (a.kept != nullptr || (a.use_direct && a.sel_base == nullptr)))
     return hipErrorInvalidValue;
   const bool kept = a.kept != nullptr;
   const bool direct = kept || a.use_direct;

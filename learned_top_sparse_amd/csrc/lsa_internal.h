@@ -165,6 +165,6 @@ hipError_t launch_thresholds(const int32_t* samp, long long ld_s, const int32_t*
                              int k, int stride, int mode, const ThrArgs& t, hipStream_t st);
 // exact top-k of the list rows; marks rows whose list fell short or overflowed (state 2)
 hipError_t launch_list_topk(const int32_t* q_pos, long long rows, int L_max, int k, const ThrArgs& t,
-                            int32_t* idx, int32_t* count, hipStream_t st);
+                            int32_t* idx, int32_t* count, int n_q, const Pages& pg, hipStream_t st);
 
 }  // namespace lsa

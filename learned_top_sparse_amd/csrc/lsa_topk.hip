@@ -513,7 +513,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const int32_t* __restrict__ sc
                                                   const int32_t* __restrict__ kept, int bs, int n_keep,
                                                   int L_max, int k, int32_t* __restrict__ idx,
                                                   int32_t* __restrict__ count,
-                                                  const int32_t* __restrict__ row_state) {
+                                                  const int32_t* __restrict__ row_state, int n_q, Pages pg) {
   constexpr int NW = NT / 64;
   constexpr int VG = 4;  // groups of 4 slots per thread per pass
   __shared__ int lds_big[NBINS];  // histogram, then the candidate list (slots | scores)
@@ -527,7 +527,14 @@ __global__ __launch_bounds__(NT) void topk_kernel(const int32_t* __restrict__ sc
   if (row_state != nullptr && row_state[row] == 0) return;  // selected from its candidate list
   int32_t* out = idx + row * (long long)k;
   int n_valid;
-  const RowView<KEPT> rv = make_row<NT, KEPT>(scores, ld, q_pos, kept, bs, n_keep, L_max, row, kept_s, scan_tmp, &n_valid);
+  RowView<KEPT> rv = make_row<NT, KEPT>(scores, ld, q_pos, kept, bs, n_keep, L_max, row, kept_s, scan_tmp, &n_valid);
+  if constexpr (!KEPT) {
+    if (pg.page_table != nullptr) {  // paged caches: the list receives pool rows
+      rv.pt = pg.page_table + (row / n_q) * pg.max_pages;
+      rv.plog2 = pg.page_log2;
+      rv.n_pages = pg.n_pages;
+    }
+  }
   if (count != nullptr && threadIdx.x == 0) count[row] = min(k, n_valid);
   if (n_valid <= k) {
     select_all<NT, KEPT>(rv, n_valid, k, wcnt, out);
@@ -1165,7 +1172,7 @@ __device__ __forceinline__ unsigned long long block_select_kth64(const unsigned 
 template <int NT, int J>
 __global__ __launch_bounds__(NT) void list_topk_kernel(const int32_t* __restrict__ q_pos, int L_max, int k,
                                                        ThrArgs t, int32_t* __restrict__ idx,
-                                                       int32_t* __restrict__ count) {
+                                                       int32_t* __restrict__ count, int n_q, Pages pg) {
   constexpr int NW = NT / 64;
   constexpr int TMAX = 512;
   constexpr int JW = (J + 7) / 8;
@@ -1315,7 +1322,14 @@ __global__ __launch_bounds__(NT) void list_topk_kernel(const int32_t* __restrict
     while (m) {
       const int bit = __ffs(m) - 1;
       m &= m - 1;
-      if (r < k) out[r] = wd * 32 + bit;
+      if (r < k) {
+        const int key = wd * 32 + bit;
+        // paged caches: the key's pool row
+        out[r] = pg.page_table == nullptr
+                     ? key
+                     : (min(max(pg.page_table[(row / n_q) * pg.max_pages + (key >> pg.page_log2)], 0), pg.n_pages - 1)
+                        << pg.page_log2) | (key & ((1 << pg.page_log2) - 1));
+      }
       ++r;
     }
   }
@@ -1682,7 +1696,7 @@ static hipError_t launch_topk_t(const TopkArgs& a, hipStream_t st, long long row
     return hipGetLastError();
   }
   SegWs w;
-  if (!KEPT && a.row_state == nullptr && split_rows(a, &w)) {
+  if (!KEPT && a.row_state == nullptr && a.pages.page_table == nullptr && split_rows(a, &w)) {
     // several workgroups per row: histogram and candidate compaction split over segments
     const dim3 grid((unsigned)w.n_seg, (unsigned)rows);
     hipLaunchKernelGGL(topk_seg_zero_kernel, dim3(8, (unsigned)rows), dim3(256), 0, st, w.base, w.row_ints(), rows);
@@ -1696,10 +1710,10 @@ static hipError_t launch_topk_t(const TopkArgs& a, hipStream_t st, long long row
   }
   if (rows <= 1024 && a.L_max >= 16384) {
     hipLaunchKernelGGL((topk_kernel<1024, KEPT>), dim3((unsigned)rows), dim3(1024), 0, st, a.scores, a.ld, a.q_pos,
-                       a.kept, a.block_size, a.n_keep, a.L_max, a.k, a.idx, a.count, a.row_state);
+                       a.kept, a.block_size, a.n_keep, a.L_max, a.k, a.idx, a.count, a.row_state, a.n_q, a.pages);
   } else {
     hipLaunchKernelGGL((topk_kernel<256, KEPT>), dim3((unsigned)rows), dim3(256), 0, st, a.scores, a.ld, a.q_pos,
-                       a.kept, a.block_size, a.n_keep, a.L_max, a.k, a.idx, a.count, a.row_state);
+                       a.kept, a.block_size, a.n_keep, a.L_max, a.k, a.idx, a.count, a.row_state, a.n_q, a.pages);
   }
   return hipGetLastError();
 }
@@ -1715,13 +1729,13 @@ hipError_t launch_thresholds(const int32_t* samp, long long ld_s, const int32_t*
 }
 
 hipError_t launch_list_topk(const int32_t* q_pos, long long rows, int L_max, int k, const ThrArgs& t,
-                            int32_t* idx, int32_t* count, hipStream_t st) {
+                            int32_t* idx, int32_t* count, int n_q, const Pages& pg, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   if (k < 1 || k > THR_MAX_K || t.cap != thr_cap(k) || L_max > THR_MAX_L) return hipErrorInvalidValue;
   constexpr int NT = 256, J = 4 * THR_MAX_K / (4 * NT);  // J quads a thread hold the longest list
   const size_t dyn = (size_t)max(NBINS, (L_max + 31) / 32) * sizeof(int);
   hipLaunchKernelGGL((list_topk_kernel<NT, J>), dim3((unsigned)rows), dim3(NT), dyn, st, q_pos, L_max, k, t, idx,
-                     count);
+                     count, n_q, pg);
   return hipGetLastError();
 }
 

@@ -588,6 +588,29 @@ def test_forward_decode_paged(lsa, page_size):
     err.check()
 
 
+@pytest.mark.parametrize("page_size", [64, 256])
+def test_forward_prefill_paged(lsa, page_size):
+    """Paged caches in prefill chunks (the flat indexer reads keys through the page
+    table): every selection mode -- thresholded lists, forced fall-backs, the score
+    table -- gives the contiguous call's lists mapped through the page table, its counts
+    and outputs bit for bit; rows up to 4096 keys (the table) and a short last chunk of
+    two queries (the decode selection) mix in."""
+    k = 512
+    wl = synthetic.Workload("pgpre", B=2, n_q=98, L=24000, q_pos0=0, H_I=64, d_I=128, k=k, H_q=16)
+    pos = np.linspace(0, 23999, 98).astype(np.int64)
+    pos[:6] = [0, 300, 511, 512, 4095, 4096]
+    _, g = _inputs(wl, seed=31, pos=np.tile(pos, 2))
+    pg = synthetic.paged_pool(g, page_size, spare_pages=29, seed=7)
+    for mode in ("auto", "table", "force_short", "force_overflow"):
+        ref = lsa.lsa_forward(g, k_top=k, select=mode, attn_split=1, chunk_rows=48)
+        res = lsa.lsa_forward(pg, k_top=k, select=mode, attn_split=1, chunk_rows=48)
+        torch.cuda.synchronize()
+        assert torch.equal(res["idx"].long(), _map_pages(ref["idx"], pg["page_table"], page_size)), mode
+        assert torch.equal(res["count"], ref["count"]), mode
+        assert torch.equal(res["out"], ref["out"]), mode
+        assert torch.equal(res["lse"], ref["lse"]), mode
+
+
 def test_forward_decode_paged_graph_replay(lsa):
     """A paged decode step captured once in a HIP graph (one graph per range of context
     lengths: the page-table width fixes L_max and so every launch shape) replays for

@@ -112,9 +112,9 @@ def _fake_paged(B, n_q, max_pages, page_size, n_pages, H_I=64, d_I=128, H_q=16, 
 
 
 def test_forward_paged_arguments():
-    """Paged caches (host checks only): decode calls plan the decode selection; page
-    sizes below 64 or not powers of two, and pools not made of whole pages, are
-    invalid; prefill-shaped and two-stage calls are unsupported."""
+    """Paged caches (host checks only): decode calls plan the decode selection and
+    prefill calls the flat stages; page sizes below 64 or not powers of two, and pools
+    not made of whole pages, are invalid; two-stage calls are unsupported."""
     import learned_top_sparse_amd as lsa
     from learned_top_sparse_amd.binding import LsaError
     inp = _fake_paged(64, 1, 2049, 64, 64 * 2049 + 100)
@@ -128,8 +128,9 @@ def test_forward_paged_arguments():
     bad["k_idx"] = bad["k_idx"][:-1]   # not whole pages
     with pytest.raises(LsaError, match="INVALID_ARG"):
         lsa.lsa_forward_workspace_size(bad, 256)
-    with pytest.raises(LsaError, match="UNSUPPORTED"):
-        lsa.lsa_forward_workspace_size(_fake_paged(1, 8, 16, 64, 80), 256)
+    pre = _fake_paged(1, 64, 512, 64, 600)   # 32768-key prefill rows: thresholded selection
+    ws = lsa.lsa_forward_workspace_size(pre, 2048)
+    assert lsa.lsa_forward_stages(pre, 2048, ws) == ["sample", "index_select", "topk", "sparse_attn"]
     with pytest.raises(LsaError, match="UNSUPPORTED"):
         lsa.lsa_forward_workspace_size(_fake_paged(4, 1, 16, 64, 80), 256, two_stage=True)
 
