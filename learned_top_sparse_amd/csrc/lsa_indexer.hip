@@ -1179,6 +1179,7 @@ static hipError_t launch_blk_scores_t(const BlkArgs& a, hipStream_t st) {
 template <int D, int MT>
 static hipError_t launch_blk_decode_t(const BlkArgs& a, hipStream_t st) {
   const long long rows = (long long)a.B * a.n_q;
+  if (rows == 0 || a.n_blocks <= 0) return hipSuccess;  // no complete block to score
   // about 512 workgroups in all (two per compute unit, all resident at once), spans of
   // at least 512 blocks
   long long want = std::max(1ll, std::min((512 + rows - 1) / rows, (long long)(a.n_blocks + 511) / 512));

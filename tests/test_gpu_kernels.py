@@ -542,6 +542,26 @@ def test_forward_pooled_blocks(lsa, case):
     err.check()
 
 
+@pytest.mark.parametrize("mode", ["two_stage", "pooled"])
+def test_forward_block_modes_short_context(lsa, mode):
+    """Contexts shorter than one block (no complete block to score): every query keeps
+    only its own block, so its list is keys 0..p -- decode- and prefill-shaped rows."""
+    bs, nk = 64, 2
+    k = nk * bs
+    for B, n_q, pos in ((3, 1, [49, 0, 20]), (1, 9, list(range(0, 45, 5)))):
+        wl = synthetic.Workload("short", B=B, n_q=n_q, L=50, q_pos0=0, H_I=16, d_I=64, k=k, H_q=8)
+        inp, g = _inputs(wl, seed=37, pos=pos)
+        res = lsa.lsa_forward(g, k_top=k, two_stage="pooled" if mode == "pooled" else True, block_size=bs,
+                              n_keep=nk, attn_split=1)
+        J = res["idx"].cpu().numpy()
+        for b in range(B):
+            for i in range(n_q):
+                p = int(inp["q_pos"][b, i])
+                want = np.concatenate([np.arange(p + 1), np.full(k - p - 1, -1)])
+                assert np.array_equal(J[b, i], want), f"{mode} {(b, i)}"
+                assert int(res["count"][b, i]) == p + 1
+
+
 def _map_pages(J, page_table, page_size):
     """Logical keys [B, n_q, k] (or -1) -> pool rows through page_table [B, max_pages]."""
     J = J.long()
