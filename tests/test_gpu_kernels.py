@@ -486,6 +486,7 @@ def test_block_cache(lsa):
     (4, 1, 40000, "decode", 4, 256),    # 10000 blocks a row: the register-resident keep
     (3, 1, 40000, "zeros", 4, 256),     # every block score 0: the lowest blocks are kept
     (1, 30, 700, "random", 16, 8),      # bigger blocks, few kept; early rows keep all
+    (4, 1, 30000, "decode64", 4, 256),  # d_I = 64 and 20 heads (a partial head tile)
 ])
 def test_forward_pooled_blocks(lsa, case):
     """Pooled blocks (two_stage = "pooled"): each query keeps its own block and the
@@ -497,8 +498,9 @@ def test_forward_pooled_blocks(lsa, case):
     every candidate)."""
     B, n_q, L, mode, bs, nk = case
     k = nk * bs
-    wl = synthetic.Workload("pooled", B=B, n_q=n_q, L=L, q_pos0=0, H_I=64, d_I=128, k=k, H_q=16)
-    if mode in ("decode", "zeros"):
+    H_I, d_I = (20, 64) if mode == "decode64" else (64, 128)
+    wl = synthetic.Workload("pooled", B=B, n_q=n_q, L=L, q_pos0=0, H_I=H_I, d_I=d_I, k=k, H_q=16)
+    if mode in ("decode", "zeros", "decode64"):
         pos = [L - 1, L - 2, 5000, 4 * nk - 1, 3][:B]
     else:
         gen = np.random.default_rng(7)
