@@ -574,8 +574,8 @@ def _map_pages(J, page_table, page_size):
     return torch.where(J >= 0, rows, torch.full_like(J, -1))
 
 
-@pytest.mark.parametrize("page_size", [64, 256])
-def test_forward_decode_paged(lsa, page_size):
+@pytest.mark.parametrize("page_size,H_I,d_I", [(64, 64, 128), (256, 64, 128), (128, 20, 64)])
+def test_forward_decode_paged(lsa, page_size, H_I, d_I):
     """Paged caches (decode): k_idx / k / v are pools shared by the sequences, each
     sequence reaching its keys through a page table (pages scattered over the pool,
     spare pages between them).  The lists name pool rows: they equal the contiguous
@@ -584,7 +584,7 @@ def test_forward_decode_paged(lsa, page_size):
     different lengths share the call, rows of at most k keys included."""
     L, k = 40000, 1024
     pos = [39999, 30000, 1023, 500, 33333, 39998, 4095]
-    wl = synthetic.Workload("paged", B=len(pos), n_q=1, L=L, q_pos0=0, H_I=64, d_I=128, k=k, H_q=16)
+    wl = synthetic.Workload("paged", B=len(pos), n_q=1, L=L, q_pos0=0, H_I=H_I, d_I=d_I, k=k, H_q=16)
     inp, g = _inputs(wl, seed=13, pos=pos)
     ref = lsa.lsa_forward(g, k_top=k)
     pg = synthetic.paged_pool(g, page_size, spare_pages=37, seed=3)
