@@ -127,10 +127,16 @@ LSA_API lsa_status lsa_block_prefilter_workspace_size(int32_t B, int32_t n_q, in
 }
 
 // block scores + keep for rows whose limbs are already in `limbs`
+// Block scores and kept blocks.  scores_private: bscores is workspace nobody reads back,
+// so decode-shaped rows may keep span candidates there instead of the score table.
 static lsa_status run_prefilter(const int8_t* q_idx, const int8_t* limbs, const int32_t* w, int32_t w_per_query,
                                 const int32_t* q_pos, int32_t B, int32_t n_q, int32_t n_blocks, int32_t H_I,
                                 int32_t d_I, int32_t block_size, int32_t n_keep, int32_t* kept,
-                                long long* bscores, hipStream_t s) {
+                                long long* bscores, hipStream_t s, bool scores_private = false) {
+  lsa::BlkCand cand{};
+  if (scores_private && !lsa::blk_cand_layout((long long)B * n_q, n_q, n_blocks, n_keep, bscores,
+                                              (size_t)B * n_q * n_blocks * 8, &cand))
+    cand = lsa::BlkCand{};
   lsa::BlkArgs ba{};
   ba.q_idx = q_idx;
   ba.limbs = limbs;
@@ -147,6 +153,7 @@ static lsa_status run_prefilter(const int8_t* q_idx, const int8_t* limbs, const 
   ba.bscores = bscores;
   ba.ld = n_blocks;
   ba.span = 512;
+  ba.cand = cand;
   hipError_t e = lsa::launch_block_scores(ba, s);
   if (e != hipSuccess) return LSA_ERR_HIP;
   lsa::BlkSelArgs sa{};
@@ -159,6 +166,7 @@ static lsa_status run_prefilter(const int8_t* q_idx, const int8_t* limbs, const 
   sa.block_size = block_size;
   sa.n_keep = n_keep;
   sa.kept = kept;
+  sa.cand = cand;
   return hip_status(lsa::launch_block_select(sa, s));
 }
 
@@ -184,7 +192,7 @@ LSA_API lsa_status lsa_block_prefilter(const int8_t* q_idx, const int32_t* reps,
     if (e != hipSuccess) return LSA_ERR_HIP;
   }
   return run_prefilter(q_idx, limbs, w, w_per_query, q_pos, B, n_q, n_blocks, H_I, d_I, block_size, n_keep,
-                       kept_blocks, bs, s);
+                       kept_blocks, bs, s, block_scores == nullptr);
 }
 
 LSA_API lsa_status lsa_block_cache(const int8_t* k_idx, int32_t B, int32_t L_max, int32_t d_I, int32_t block_size,
@@ -634,7 +642,7 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
     if (a->two_stage) {
       int32_t* kout = a->kept_blocks ? a->kept_blocks + r0 * a->n_keep : kept_ws;
       lsa_status st2 = run_prefilter(qi, limbs + (long long)b0 * p.n_blocks * 2 * d_I, wq, a->w_per_query, qp, nb,
-                                     ni, p.n_blocks, H_I, d_I, a->block_size, a->n_keep, kout, bsc, s);
+                                     ni, p.n_blocks, H_I, d_I, a->block_size, a->n_keep, kout, bsc, s, true);
       if (st2 != LSA_OK) return st2;
       kept = kout;
       ia.kept = kept;

@@ -932,13 +932,17 @@ __global__ __launch_bounds__(256, 2) void blk_scores_kernel(
 // scored.  The span's scores collect in LDS (span <= BLK_DEC_SPAN) and leave in one
 // burst at the end: a store between the ring's loads would make the next wait drain
 // the loads in flight (loads and stores share one counter).
+// With cand.key set, the workgroup instead keeps its span's best min(n_keep - 1, its
+// blocks) by (score desc, block asc) -- every block the row keeps from this span is
+// among them -- and writes those candidates (BlkCand) in block order: a few KB per
+// span instead of the span's scores.
 // Grid: x = spans, y = B * n_q.
 constexpr int BLK_DEC_SPAN = 4096;
 template <int D, int MT>
 __global__ __launch_bounds__(256, 2) void blk_decode_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ limbs, const int32_t* __restrict__ w,
     int w_per_query, const int32_t* __restrict__ q_pos, int n_q, int n_blocks, int H_I, int bs, int span,
-    long long* __restrict__ bscores, long long ld) {
+    long long* __restrict__ bscores, long long ld, BlkCand cand, int n_keep) {
   constexpr int KS = D / 64, RB = 2 * D, RING = 4, GB = 32;  // GB blocks per group
   __shared__ __attribute__((aligned(16))) long long sbuf[BLK_DEC_SPAN];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
@@ -1007,8 +1011,40 @@ __global__ __launch_bounds__(256, 2) void blk_decode_kernel(
     }
   }
   __syncthreads();
-  long long* srow = bscores + row * ld + m_begin;
-  for (int t = tid; t < m_end - m_begin; t += 256) srow[t] = sbuf[t];
+  if (cand.key == nullptr) {
+    long long* srow = bscores + row * ld + m_begin;
+    for (int t = tid; t < m_end - m_begin; t += 256) srow[t] = sbuf[t];
+    return;
+  }
+  // the span's candidates: keys (score with the sign bit flipped: unsigned order) in
+  // registers, position c * 256 + tid = block m_begin + position
+  constexpr int CK = BLK_DEC_SPAN / 256;
+  __shared__ int hist[2048];
+  __shared__ unsigned bm[BLK_DEC_SPAN / 32], eqm[BLK_DEC_SPAN / 32];
+  __shared__ int scan_tmp[5], sh[2];
+  __shared__ unsigned long long shu[2];
+  const int n_e = m_end - m_begin;
+  unsigned long long key[CK];
+  unsigned vmask = 0u;
+#pragma unroll
+  for (int c = 0; c < CK; ++c) {
+    const int pos = c * 256 + tid;
+    key[c] = pos < n_e ? (unsigned long long)sbuf[pos] ^ 0x8000000000000000ull : 0ull;
+    vmask |= (pos < n_e ? 1u : 0u) << c;
+  }
+  const int need = min(min(n_keep - 1, own), n_e);
+  unsigned long long T = 0ull;  // need >= n_e: every block of the span
+  int need_eq = n_e;
+  if (need < n_e) T = radix_cut64<256, CK>(key, vmask, need, hist, scan_tmp, sh, shu, &need_eq);
+  mark_kept64<256, CK>(key, vmask, T, need_eq, bm, eqm, scan_tmp);
+  const long long base = (row * cand.spans + blockIdx.x) * (long long)cand.cap;
+  const int n_out = emit_marked<256>(bm, BLK_DEC_SPAN / 32, scan_tmp, [&](int r, int pos) {
+    if (r < cand.cap) {
+      cand.key[base + r] = sbuf[pos];
+      cand.blk[base + r] = m_begin + pos;
+    }
+  });
+  if (tid == 0) cand.cnt[row * cand.spans + blockIdx.x] = min(n_out, cand.cap);
 }
 
 // ---------------------------------------------------------------------------------
@@ -1176,19 +1212,41 @@ static hipError_t launch_blk_scores_t(const BlkArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Spans of the decode-shaped block scoring: about 512 workgroups in all (two per compute
+// unit, all resident at once), spans of at least 512 blocks and at most BLK_DEC_SPAN.
+static int blk_decode_span(long long rows, int n_blocks) {
+  long long want = std::max(1ll, std::min((512 + rows - 1) / rows, (long long)(n_blocks + 511) / 512));
+  want = std::max(want, (long long)(n_blocks + BLK_DEC_SPAN - 1) / BLK_DEC_SPAN);  // spans fit the LDS buffer
+  return (int)std::min<long long>(((n_blocks + want - 1) / want + 31) / 32 * 32, BLK_DEC_SPAN);
+}
+
+bool blk_cand_layout(long long rows, int n_q, int n_blocks, int n_keep, void* region, size_t region_bytes,
+                     BlkCand* c) {
+  if (n_q >= 8 || rows <= 0 || n_blocks <= 0 || n_keep < 2 || region == nullptr) return false;
+  c->span = blk_decode_span(rows, n_blocks);
+  c->spans = (n_blocks + c->span - 1) / c->span;
+  c->cap = n_keep - 1;
+  // the merge holds a row's candidates in registers of one workgroup: at most 8 per thread
+  if ((long long)c->spans * c->cap > 8 * 1024) return false;
+  const size_t n = (size_t)rows * c->spans * c->cap;
+  const size_t bytes = n * 8 + n * 4 + (size_t)rows * c->spans * 4;
+  if (bytes > region_bytes || (reinterpret_cast<uintptr_t>(region) & 7) != 0) return false;
+  c->key = static_cast<long long*>(region);
+  c->blk = reinterpret_cast<int*>(c->key + n);
+  c->cnt = c->blk + n;
+  return true;
+}
+
 template <int D, int MT>
 static hipError_t launch_blk_decode_t(const BlkArgs& a, hipStream_t st) {
   const long long rows = (long long)a.B * a.n_q;
   if (rows == 0 || a.n_blocks <= 0) return hipSuccess;  // no complete block to score
-  // about 512 workgroups in all (two per compute unit, all resident at once), spans of
-  // at least 512 blocks
-  long long want = std::max(1ll, std::min((512 + rows - 1) / rows, (long long)(a.n_blocks + 511) / 512));
-  want = std::max(want, (long long)(a.n_blocks + BLK_DEC_SPAN - 1) / BLK_DEC_SPAN);  // spans fit the LDS buffer
-  const int span = (int)std::min<long long>(((a.n_blocks + want - 1) / want + 31) / 32 * 32, BLK_DEC_SPAN);
+  const int span = a.cand.key != nullptr ? a.cand.span : blk_decode_span(rows, a.n_blocks);
   const int n_spans = (a.n_blocks + span - 1) / span;
+  if (a.cand.key != nullptr && (n_spans != a.cand.spans || span > BLK_DEC_SPAN)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((blk_decode_kernel<D, MT>), dim3((unsigned)n_spans, (unsigned)rows), dim3(256), 0, st,
                      a.q_idx, a.limbs, a.w, a.w_per_query, a.q_pos, a.n_q, a.n_blocks, a.H_I, a.block_size, span,
-                     a.bscores, a.ld);
+                     a.bscores, a.ld, a.cand, a.cand.cap + 1);
   return hipGetLastError();
 }
 

@@ -58,6 +58,16 @@ struct IdxArgs {
   Pages pages;
 };
 
+// Block candidates of decode-shaped rows: the scoring workgroup of span s (span blocks)
+// of row r leaves the best min(cap, its blocks) of its span by (score desc, block asc), in
+// block order: key[(r * spans + s) * cap + i] (int64 score), blk[...] (block), cnt[r * spans + s].
+struct BlkCand {
+  long long* key;
+  int* blk;
+  int* cnt;
+  int spans, span, cap;
+};
+
 struct BlkArgs {
   const int8_t* q_idx;
   const int8_t* limbs;
@@ -68,6 +78,7 @@ struct BlkArgs {
   long long* bscores;
   long long ld;
   int span;
+  BlkCand cand;  // decode-shaped rows: candidates instead of the score table (key == nullptr: table)
 };
 
 struct TopkArgs {
@@ -92,6 +103,7 @@ struct BlkSelArgs {
   const int32_t* q_pos;
   int B, n_q, n_blocks, block_size, n_keep;
   int32_t* kept;
+  BlkCand cand;  // key != nullptr: merge the scoring workgroups' candidates instead
 };
 
 // waves per sparse-attention workgroup (each with its own 32-key tile state)
@@ -119,6 +131,11 @@ hipError_t launch_block_reps(const int8_t* k_idx, int B, int L_max, int d_I, int
 hipError_t launch_block_limbs(const int32_t* reps, int B, int n_blocks, int d_I, int8_t* limbs,
                               hipStream_t st);
 hipError_t launch_block_scores(const BlkArgs& a, hipStream_t st);
+// Candidate layout of decode-shaped block rows (rows of fewer than 8 queries per sequence)
+// carved from `region` (region_bytes); false if it does not fit or the rows are not
+// decode-shaped (then the score table is used).
+bool blk_cand_layout(long long rows, int n_q, int n_blocks, int n_keep, void* region, size_t region_bytes,
+                     BlkCand* c);
 // block-key cache (the limbs of the representatives) of blocks [m0, m0 + n_upd)
 hipError_t launch_block_cache(const int8_t* k_idx, int B, int L_max, int d_I, int bs, int n_blocks, int m0,
                               int n_upd, int8_t* limbs, hipStream_t st);

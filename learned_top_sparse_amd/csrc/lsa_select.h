@@ -206,4 +206,168 @@ __device__ __forceinline__ void merge_row_histogram(int* hist, int* gh, int* inf
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Exact selection over 64-bit keys held in registers, C <= 32 per thread: key c of thread
+// t sits at position c * NT + t and counts iff bit c of vmask is set.  All threads call.
+
+// The need-th largest of the valid keys (1 <= need <= their number): radix passes of
+// 11-bit digits below the prefix shared by the largest and smallest valid key, counted
+// in an LDS histogram (hist: 2048 ints).  Returns T; *need_eq = how many keys equal to
+// T are among the need largest.
+template <int NT, int C>
+__device__ __forceinline__ unsigned long long radix_cut64(const unsigned long long (&key)[C], unsigned vmask,
+                                                          int need, int* hist, int* scan_tmp, int* sh,
+                                                          unsigned long long* shu, int* need_eq) {
+  static_assert(C <= 32, "a 32-bit validity mask");
+  constexpr int DIG = 11, NBIN = 1 << DIG;
+  constexpr int BPT = (NBIN + NT - 1) / NT;  // bins per thread in the scan
+  const int tid = threadIdx.x, lane = tid & 63;
+  unsigned long long mx = 0ull, mn = ~0ull;
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+    if ((vmask >> c) & 1u) {
+      mx = key[c] > mx ? key[c] : mx;
+      mn = key[c] < mn ? key[c] : mn;
+    }
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long a = __shfl_xor(mx, o), b = __shfl_xor(mn, o);
+    mx = a > mx ? a : mx;
+    mn = b < mn ? b : mn;
+  }
+  if (tid == 0) {
+    shu[0] = 0ull;
+    shu[1] = ~0ull;
+  }
+  __syncthreads();
+  if (lane == 0) {
+    atomicMax(&shu[0], mx);
+    atomicMin(&shu[1], mn);
+  }
+  __syncthreads();
+  mx = shu[0];
+  mn = shu[1];
+  unsigned long long pref = mx, pmask = ~0ull;
+  if (mx != mn) {
+    const int hb = 63 - __clzll((long long)(mx ^ mn));  // highest bit where keys differ
+    pmask = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
+    pref = mx & pmask;
+    for (int top = hb; top >= 0; top -= DIG) {
+      const int lo = max(0, top - DIG + 1);
+      const int nb = 1 << (top - lo + 1);
+      for (int t = tid; t < nb; t += NT) hist[t] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        if (((vmask >> c) & 1u) && (key[c] & pmask) == pref) atomicAdd(&hist[(int)((key[c] >> lo) & (nb - 1))], 1);
+      __syncthreads();
+      // thread t sums bins nb-1-BPT*t .. nb-BPT*(t+1) (from the top); the one whose range
+      // holds the need-th entry walks it
+      int csum = 0;
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {
+        const int bin = nb - 1 - BPT * tid - j;
+        csum += bin >= 0 ? hist[bin] : 0;
+      }
+      int tot;
+      const int excl = block_exclusive_scan<NT>(csum, scan_tmp, &tot);
+      if (excl < need && excl + csum >= need) {
+        int acc = excl;
+        for (int j = 0; j < BPT && nb - 1 - BPT * tid - j >= 0; ++j) {
+          const int bin = nb - 1 - BPT * tid - j;
+          const int h = hist[bin];
+          if (acc + h >= need) {
+            sh[0] = bin;
+            sh[1] = acc;
+            break;
+          }
+          acc += h;
+        }
+      }
+      __syncthreads();
+      need -= sh[1];
+      pref |= (unsigned long long)sh[0] << lo;
+      pmask |= (unsigned long long)(nb - 1) << lo;
+      __syncthreads();
+    }
+  }
+  *need_eq = need;
+  return pref;
+}
+
+// Marks, in an LDS bitmap of positions (bm: NT * C / 32 words), the keys kept by the cut:
+// key > T, and the first need_eq keys equal to T in position order (the lowest
+// positions win ties).  eqm: another NT * C / 32 words of LDS.  The bitmap is complete
+// when this returns.
+template <int NT, int C>
+__device__ __forceinline__ void mark_kept64(const unsigned long long (&key)[C], unsigned vmask,
+                                            unsigned long long T, int need_eq, unsigned* bm, unsigned* eqm,
+                                            int* scan_tmp) {
+  constexpr int NWD = NT * C / 32;
+  static_assert(NT * C % 32 == 0, "whole bitmap words");
+  const int tid = threadIdx.x;
+  __syncthreads();
+  for (int t = tid; t < NWD; t += NT) {
+    bm[t] = 0u;
+    eqm[t] = 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    if (!((vmask >> c) & 1u)) continue;
+    const int pos = c * NT + tid;
+    if (key[c] > T) atomicOr(&bm[pos >> 5], 1u << (pos & 31));
+    else if (key[c] == T) atomicOr(&eqm[pos >> 5], 1u << (pos & 31));
+  }
+  __syncthreads();
+  // each thread takes whole words in order: the rank of its first equal key among all
+  constexpr int WPT = (NWD + NT - 1) / NT;
+  int n_eq = 0;
+  for (int j = 0; j < WPT; ++j) {
+    const int wd = WPT * tid + j;
+    if (wd < NWD) n_eq += __popc(eqm[wd]);
+  }
+  int tot;
+  int before = block_exclusive_scan<NT>(n_eq, scan_tmp, &tot);
+  for (int j = 0; j < WPT; ++j) {
+    const int wd = WPT * tid + j;
+    if (wd >= NWD) break;
+    unsigned e = eqm[wd], keep = 0u;
+    while (e != 0u && before < need_eq) {
+      const unsigned low = e & (0u - e);
+      keep |= low;
+      e ^= low;
+      ++before;
+    }
+    bm[wd] |= keep;
+  }
+  __syncthreads();
+}
+
+// Writes the marked positions in ascending order: emit(rank, pos) for each; returns
+// their number.  Each thread takes whole words of the bitmap (NWD words).
+template <int NT, typename Emit>
+__device__ __forceinline__ int emit_marked(const unsigned* bm, int NWD, int* scan_tmp, Emit emit) {
+  const int tid = threadIdx.x;
+  const int WPT = (NWD + NT - 1) / NT;
+  int mine = 0;
+  for (int j = 0; j < WPT; ++j) {
+    const int wd = WPT * tid + j;
+    if (wd < NWD) mine += __popc(bm[wd]);
+  }
+  int tot;
+  int r = block_exclusive_scan<NT>(mine, scan_tmp, &tot);
+  for (int j = 0; j < WPT; ++j) {
+    const int wd = WPT * tid + j;
+    if (wd >= NWD) break;
+    unsigned bits = bm[wd];
+    while (bits != 0u) {
+      const int bit = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      emit(r, 32 * wd + bit);
+      ++r;
+    }
+  }
+  return tot;
+}
+
 }  // namespace lsa

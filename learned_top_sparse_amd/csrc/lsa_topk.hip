@@ -1454,23 +1454,19 @@ __global__ __launch_bounds__(NT) void blk_select_kernel(const long long* __restr
 
 // Block keep of rows with many blocks and one workgroup each (decode): the same result
 // as blk_select_kernel, with the row's scores held in registers (thread t: blocks
-// t, t + NT, ..., at most C of them) instead of re-read per pass.  The cut T (the
-// n_sel-th best key) comes from radix passes of DIG-bit digits over the bits below
-// the prefix all keys share, counted in an LDS histogram; then, in block order, the
-// blocks with key > T and the first need_eq blocks with key == T are kept (bitmaps of
-// the row's blocks, one scan for the ranks among equal keys and one for the output).
+// t, t + NT, ..., at most C of them) instead of re-read per pass: the cut (radix_cut64)
+// and, in block order, the blocks with a higher key and the first ones equal to the cut.
 template <int NT, int C>
 __global__ __launch_bounds__(NT) void blk_keep_rows_kernel(const long long* __restrict__ bscores, long long ld,
                                                            const int32_t* __restrict__ q_pos, int n_blocks, int bs,
                                                            int n_keep, int32_t* __restrict__ kept) {
-  constexpr int NW = NT / 64, DIG = 11, NBIN = 1 << DIG, BPT = NBIN / NT;
-  static_assert(NBIN % NT == 0, "whole bins per thread");
-  __shared__ int hist[NBIN];
-  __shared__ int scan_tmp[NW + 1];
+  constexpr int NW = NT / 64, NWD = NT * C / 32;
+  __shared__ int hist[2048];
+  __shared__ unsigned bm[NWD], eqm[NWD];
+  __shared__ int scan_tmp[NW + 1], sh[2];
   __shared__ unsigned long long shu[2];
-  __shared__ int sh[2];
   const long long row = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int p = q_pos[row];
   int32_t* out = kept + row * (long long)n_keep;
   if (p < 0) {
@@ -1487,135 +1483,93 @@ __global__ __launch_bounds__(NT) void blk_keep_rows_kernel(const long long* __re
     written = n_sc;
   } else {
     unsigned long long key[C];
-    unsigned long long mx = 0ull, mn = ~0ull;
+    unsigned vmask = 0u;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int m = c * NT + tid;
       key[c] = m < n_sc ? (unsigned long long)br[m] ^ 0x8000000000000000ull : 0ull;
-      if (m < n_sc) {
-        mx = key[c] > mx ? key[c] : mx;
-        mn = key[c] < mn ? key[c] : mn;
-      }
+      vmask |= (m < n_sc ? 1u : 0u) << c;
     }
-    auto valid = [&](int c) { return c * NT + tid < n_sc; };
-    for (int o = 32; o > 0; o >>= 1) {
-      const unsigned long long a = __shfl_xor(mx, o), b = __shfl_xor(mn, o);
-      mx = a > mx ? a : mx;
-      mn = b < mn ? b : mn;
-    }
+    int need_eq;
+    const unsigned long long T = radix_cut64<NT, C>(key, vmask, n_sel, hist, scan_tmp, sh, shu, &need_eq);
+    mark_kept64<NT, C>(key, vmask, T, need_eq, bm, eqm, scan_tmp);
+    written = emit_marked<NT>(bm, NWD, scan_tmp, [&](int r, int pos) {
+      if (r < n_keep - 1) out[r] = pos;
+    });
+  }
+  written = min(written, n_keep - 1);
+  if (tid == 0) out[written] = own;
+  for (int t = written + 1 + tid; t < n_keep; t += NT) out[t] = -1;
+}
+
+// Block keep of decode-shaped rows from the scoring workgroups' candidates (BlkCand):
+// every span holding scored blocks left its best min(n_keep - 1, its blocks) in block
+// order, so their concatenation is in block order and holds every block the row keeps;
+// the row's cut over it (at most NT * C entries, in registers) is the row's.
+template <int NT, int C>
+__global__ __launch_bounds__(NT) void blk_keep_merge_kernel(const int32_t* __restrict__ q_pos, int n_blocks, int bs,
+                                                            int n_keep, BlkCand cand, int32_t* __restrict__ kept) {
+  constexpr int NW = NT / 64, NWD = NT * C / 32;
+  constexpr int MAX_SPANS = 256;
+  __shared__ int hist[2048];
+  __shared__ unsigned bm[NWD], eqm[NWD];
+  __shared__ int blk_s[NT * C];
+  __shared__ int off_s[MAX_SPANS + 1];
+  __shared__ int scan_tmp[NW + 1], sh[2];
+  __shared__ unsigned long long shu[2];
+  const long long row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int p = q_pos[row];
+  int32_t* out = kept + row * (long long)n_keep;
+  if (p < 0) {
+    for (int t = tid; t < n_keep; t += NT) out[t] = -1;
+    return;
+  }
+  const int own = p / bs;
+  const int n_sc = min(own, n_blocks);  // scored earlier blocks
+  const int n_sel = min(n_keep - 1, n_sc);
+  int written;
+  if (n_sel >= n_sc) {
+    for (int m = tid; m < n_sc; m += NT) out[m] = m;
+    written = n_sc;
+  } else {
+    const int S = (n_sc + cand.span - 1) / cand.span;  // spans with scored blocks (each wrote its list)
+    const long long rs = row * cand.spans;
     if (tid == 0) {
-      shu[0] = 0ull;
-      shu[1] = ~0ull;
-    }
-    __syncthreads();
-    if (lane == 0) {
-      atomicMax(&shu[0], mx);
-      atomicMin(&shu[1], mn);
-    }
-    __syncthreads();
-    mx = shu[0];
-    mn = shu[1];
-    int need = n_sel;
-    unsigned long long pref = mx, pmask = ~0ull;
-    if (mx != mn) {
-      const int hb = 63 - __clzll((long long)(mx ^ mn));  // highest bit where keys differ
-      pmask = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
-      pref = mx & pmask;
-      for (int top = hb; top >= 0; top -= DIG) {
-        const int lo = max(0, top - DIG + 1);
-        const int nb = 1 << (top - lo + 1);
-        for (int t = tid; t < nb; t += NT) hist[t] = 0;
-        __syncthreads();
-#pragma unroll
-        for (int c = 0; c < C; ++c)
-          if (valid(c) && (key[c] & pmask) == pref) atomicAdd(&hist[(int)((key[c] >> lo) & (nb - 1))], 1);
-        __syncthreads();
-        // thread t sums bins nb-1-BPT*t .. nb-BPT*(t+1) (from the top); the one whose range
-        // holds the need-th entry walks it
-        int csum = 0;
-#pragma unroll
-        for (int j = 0; j < BPT; ++j) {
-          const int bin = nb - 1 - BPT * tid - j;
-          csum += bin >= 0 ? hist[bin] : 0;
-        }
-        int tot;
-        const int excl = block_exclusive_scan<NT>(csum, scan_tmp, &tot);
-        if (excl < need && excl + csum >= need) {
-          int acc = excl;
-          for (int j = 0; j < BPT && nb - 1 - BPT * tid - j >= 0; ++j) {
-            const int bin = nb - 1 - BPT * tid - j;
-            const int h = hist[bin];
-            if (acc + h >= need) {
-              sh[0] = bin;
-              sh[1] = acc;
-              break;
-            }
-            acc += h;
-          }
-        }
-        __syncthreads();
-        need -= sh[1];
-        pref |= (unsigned long long)sh[0] << lo;
-        pmask |= (unsigned long long)(nb - 1) << lo;
-        __syncthreads();
+      int o = 0;
+      for (int s2 = 0; s2 < S; ++s2) {
+        off_s[s2] = o;
+        o += cand.cnt[rs + s2];
       }
+      off_s[S] = o;
     }
-    const unsigned long long T = pref;
-    const int need_eq = need;  // blocks equal to T to keep, the lowest first
-    // bitmaps over the row's blocks: gt = key > T, eq = key == T; thread t then owns
-    // words [WPT t, WPT t + WPT) and keeps their gt bits and the eq bits whose rank among
-    // all eq bits (in block order) is below need_eq
-    constexpr int NWD = C * NT / 32, WPT = NWD / NT;
-    unsigned* gt = reinterpret_cast<unsigned*>(hist);  // NBIN ints: NWD words each
-    unsigned* eq = gt + NWD;
-    static_assert(2 * NWD <= NBIN, "both bitmaps in the histogram's LDS");
     __syncthreads();
-    for (int t = tid; t < 2 * NWD; t += NT) gt[t] = 0u;
-    __syncthreads();
+    const int total = off_s[S];
+    unsigned long long key[C];
+    unsigned vmask = 0u;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      if (!valid(c)) continue;
-      const int m = c * NT + tid;
-      if (key[c] > T) atomicOr(&gt[m >> 5], 1u << (m & 31));
-      else if (key[c] == T) atomicOr(&eq[m >> 5], 1u << (m & 31));
-    }
-    __syncthreads();
-    unsigned wg[WPT], we[WPT];
-    int n_eq = 0;
-#pragma unroll
-    for (int j2 = 0; j2 < WPT; ++j2) {
-      wg[j2] = gt[WPT * tid + j2];
-      we[j2] = eq[WPT * tid + j2];
-      n_eq += __popc(we[j2]);
-    }
-    int tot;
-    int eq_before = block_exclusive_scan<NT>(n_eq, scan_tmp, &tot);
-    int n_take = 0;
-#pragma unroll
-    for (int j2 = 0; j2 < WPT; ++j2) {
-      // the eq bits of this word with rank < need_eq
-      unsigned keep = 0u, e = we[j2];
-      while (e != 0u && eq_before < need_eq) {
-        const unsigned low = e & (0u - e);
-        keep |= low;
-        e ^= low;
-        ++eq_before;
-      }
-      wg[j2] |= keep;
-      n_take += __popc(wg[j2]);
-    }
-    int r = block_exclusive_scan<NT>(n_take, scan_tmp, &tot);
-#pragma unroll
-    for (int j2 = 0; j2 < WPT; ++j2) {
-      unsigned bits = wg[j2];
-      while (bits != 0u) {
-        const int bit = __ffs(bits) - 1;
-        bits &= bits - 1u;
-        if (r < n_keep - 1) out[r] = 32 * (WPT * tid + j2) + bit;
-        ++r;
+      const int e = c * NT + tid;
+      key[c] = 0ull;
+      if (e < total) {
+        int lo = 0, hi = S;  // the span whose list holds entry e: off_s[lo] <= e < off_s[lo + 1]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (off_s[mid] <= e) lo = mid;
+          else hi = mid;
+        }
+        const long long at = (rs + lo) * cand.cap + (e - off_s[lo]);
+        key[c] = (unsigned long long)cand.key[at] ^ 0x8000000000000000ull;
+        blk_s[e] = cand.blk[at];
+        vmask |= 1u << c;
       }
     }
-    written = tot;
+    int need_eq;
+    const unsigned long long T = radix_cut64<NT, C>(key, vmask, n_sel, hist, scan_tmp, sh, shu, &need_eq);
+    mark_kept64<NT, C>(key, vmask, T, need_eq, bm, eqm, scan_tmp);
+    written = emit_marked<NT>(bm, NWD, scan_tmp, [&](int r, int pos) {
+      if (r < n_keep - 1) out[r] = blk_s[pos];
+    });
   }
   written = min(written, n_keep - 1);
   if (tid == 0) out[written] = own;
@@ -1785,6 +1739,14 @@ hipError_t launch_expand(const int32_t* kept, const int32_t* q_pos, long long ro
 hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st) {
   const long long rows = (long long)a.B * a.n_q;
   if (rows == 0) return hipSuccess;
+  if (a.cand.key != nullptr) {
+    // decode-shaped rows whose scoring left span candidates
+    if (a.cand.spans > 256 || (long long)a.cand.spans * a.cand.cap > 8 * 1024 || a.cand.cap != a.n_keep - 1)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL((blk_keep_merge_kernel<1024, 8>), dim3((unsigned)rows), dim3(1024), 0, st, a.q_pos,
+                       a.n_blocks, a.block_size, a.n_keep, a.cand, a.kept);
+    return hipGetLastError();
+  }
   if (a.n_q < 8 && a.n_blocks > 4096 && a.n_blocks <= 1024 * 32) {
     // few long rows (decode): the row's scores in registers of one workgroup
     hipLaunchKernelGGL((blk_keep_rows_kernel<1024, 32>), dim3((unsigned)rows), dim3(1024), 0, st, a.bscores, a.ld,
