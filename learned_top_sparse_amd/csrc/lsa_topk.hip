@@ -1511,6 +1511,7 @@ __global__ __launch_bounds__(NT) void blk_keep_merge_kernel(const int32_t* __res
                                                             int n_keep, BlkCand cand, int32_t* __restrict__ kept) {
   constexpr int NW = NT / 64, NWD = NT * C / 32;
   constexpr int MAX_SPANS = 256;
+  static_assert(NT > MAX_SPANS, "one thread per span");
   __shared__ int hist[2048];
   __shared__ unsigned bm[NWD], eqm[NWD];
   __shared__ int blk_s[NT * C];
@@ -1535,16 +1536,12 @@ __global__ __launch_bounds__(NT) void blk_keep_merge_kernel(const int32_t* __res
   } else {
     const int S = (n_sc + cand.span - 1) / cand.span;  // spans with scored blocks (each wrote its list)
     const long long rs = row * cand.spans;
-    if (tid == 0) {
-      int o = 0;
-      for (int s2 = 0; s2 < S; ++s2) {
-        off_s[s2] = o;
-        o += cand.cnt[rs + s2];
-      }
-      off_s[S] = o;
-    }
+    // list offsets: the counts load in parallel, one thread per span, then one scan
+    const int my_cnt = tid < S ? cand.cnt[rs + tid] : 0;
+    int total;
+    const int my_off = block_exclusive_scan<NT>(my_cnt, scan_tmp, &total);
+    if (tid <= S) off_s[tid] = tid < S ? my_off : total;
     __syncthreads();
-    const int total = off_s[S];
     unsigned long long key[C];
     unsigned vmask = 0u;
 #pragma unroll
