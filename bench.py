@@ -202,7 +202,7 @@ def cpu_baseline(wl, inp, budget_s=10.0):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_128k_index_traffic.md")
 TRAFFIC_SOURCES = ["learned_top_sparse_amd/csrc/lsa_indexer.hip", "learned_top_sparse_amd/csrc/lsa_device.h",
-                   "learned_top_sparse_amd/csrc/lsa_select.h"]
+                   "learned_top_sparse_amd/csrc/lsa_select.h", "learned_top_sparse_amd/csrc/lsa_idx_tiles.h"]
 
 
 def measured_traffic():

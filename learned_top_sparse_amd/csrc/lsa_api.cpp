@@ -386,13 +386,19 @@ size_t thr_ws_bytes(const lsa_forward_args* a, long long rows) {
          2 * align_up((size_t)rows * cap * 4);
 }
 
+// Two-stage rows whose kept slots fit one workgroup's LDS: the token stage and its top-k
+// run as one kernel, with no token score table.
+bool kept_fused(const lsa_forward_args* a) {
+  return a->two_stage == 1 && a->n_keep <= 256 && (long long)a->n_keep * a->block_size <= lsa::KSEL_SLOTS;
+}
+
 FwdPlan plan_forward(const lsa_forward_args* a) {
   FwdPlan p{};
   p.decode_like = a->n_q == 1;
   if (a->two_stage) {
     p.n_blocks = a->L_max / a->block_size;
     // the token stage's score rows (pooled blocks have none)
-    p.ld = a->two_stage == 2 ? 0 : (int64_t)a->n_keep * a->block_size;
+    p.ld = (a->two_stage == 2 || kept_fused(a)) ? 0 : (int64_t)a->n_keep * a->block_size;
     p.per_row = p.ld * 4 + (long long)p.n_blocks * 8 + (a->kept_blocks ? 0 : (long long)a->n_keep * 4) + 64;
     // the block-key cache, unless the caller keeps one
     p.fixed = a->block_keys ? 0 : align_up((size_t)a->B * p.n_blocks * 2 * a->d_I);
@@ -487,8 +493,8 @@ std::vector<int32_t> forward_stages(const lsa_forward_args* a, const FwdPlan& p,
   const size_t topk_ws_size = a->two_stage ? 0 : topk_ws_for(a, rows);
   for_each_chunk(a, rows, [&](int32_t, int32_t nb, int32_t, int32_t ni) {
     if (a->two_stage) st.push_back(LSA_STAGE_BLOCK_PREFILTER);
-    if (a->two_stage == 2) {
-      st.push_back(LSA_STAGE_EXPAND);
+    if (a->two_stage == 2 || kept_fused(a)) {
+      st.push_back(a->two_stage == 2 ? LSA_STAGE_EXPAND : LSA_STAGE_INDEX_SELECT);
       st.push_back(LSA_STAGE_SPARSE_ATTN);
       return;
     }
@@ -649,11 +655,16 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
       ia.block_size = a->block_size;
       ia.n_keep = a->n_keep;
       if (!mark()) return LSA_ERR_HIP;
-      if (a->two_stage == 2) {
-        // pooled blocks: the list is every key of the kept blocks the query may see
-        if (lsa::launch_expand(kept, qp, (long long)nb * ni, a->block_size, a->n_keep, kt, ix, cnt, s) != hipSuccess ||
-            !mark())
-          return LSA_ERR_HIP;
+      if (a->two_stage == 2 || kept_fused(a)) {
+        hipError_t e;
+        if (a->two_stage == 2) {
+          // pooled blocks: the list is every key of the kept blocks the query may see
+          e = lsa::launch_expand(kept, qp, (long long)nb * ni, a->block_size, a->n_keep, kt, ix, cnt, s);
+        } else {
+          // the token stage and its top-k in one kernel
+          e = lsa::launch_kept_select(ia, kt, ix, cnt, s);
+        }
+        if (e != hipSuccess || !mark()) return LSA_ERR_HIP;
         lsa_status sa = run_attn(qq, kk, vv, ix, nb, ni, L, H_q, d, kt, a->scale, split, oo, ls, attn_ws, s);
         if (sa != LSA_OK) return sa;
         return mark() ? LSA_OK : LSA_ERR_HIP;

@@ -144,6 +144,9 @@ hipError_t launch_expand(const int32_t* kept, const int32_t* q_pos, long long ro
                          int32_t* idx, int32_t* count, hipStream_t st);
 hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+// two-stage token stage and its top-k in one kernel (rows of at most KSEL_SLOTS kept slots)
+constexpr int KSEL_SLOTS = 8192;
+hipError_t launch_kept_select(const IdxArgs& a, int k, int32_t* idx, int32_t* count, hipStream_t st);
 // workspace that lets lsa_topk split each row over several workgroups (0 = not used)
 size_t topk_ws_bytes(long long rows, int L_max);
 // Decode selection: the indexer builds each row's selection state (histogram, one

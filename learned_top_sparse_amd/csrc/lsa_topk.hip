@@ -23,6 +23,7 @@
 // stable compaction over the row in global memory.  Every path is exact.
 #include "lsa_device.h"
 #include "lsa_internal.h"
+#include "lsa_idx_tiles.h"
 #include "lsa_select.h"
 
 namespace lsa {
@@ -505,37 +506,13 @@ __device__ __forceinline__ RowView<KEPT> make_row(const int32_t* scores, long lo
   return rv;
 }
 
-// ---------------------------------------------------------------------------------
-// Single workgroup per row (many rows: prefill chunks).
+// The exact top-k of one row -- the k best candidates by (score desc, slot asc), written
+// as keys (rv.key_of) in ascending order, -1 padded -- by one workgroup, from the row's
+// scores behind rv (global memory or LDS).  lds_big: NBINS ints; wcnt: 2 * 4 * NT/64.
 template <int NT, bool KEPT>
-__global__ __launch_bounds__(NT) void topk_kernel(const int32_t* __restrict__ scores, long long ld,
-                                                  const int32_t* __restrict__ q_pos,
-                                                  const int32_t* __restrict__ kept, int bs, int n_keep,
-                                                  int L_max, int k, int32_t* __restrict__ idx,
-                                                  int32_t* __restrict__ count,
-                                                  const int32_t* __restrict__ row_state, int n_q, Pages pg) {
-  constexpr int NW = NT / 64;
+__device__ __forceinline__ void select_row(const RowView<KEPT>& rv, int n_valid, int k, int32_t* out,
+                                           int* lds_big, int* wcnt, int* scan_tmp, int* h256, int* sh) {
   constexpr int VG = 4;  // groups of 4 slots per thread per pass
-  __shared__ int lds_big[NBINS];  // histogram, then the candidate list (slots | scores)
-  __shared__ int wcnt[2 * VG * NW];
-  __shared__ int scan_tmp[NW + 1];
-  __shared__ int h256[256];
-  __shared__ int kept_s[256];
-  __shared__ int sh[8];
-
-  const long long row = blockIdx.x;
-  if (row_state != nullptr && row_state[row] == 0) return;  // selected from its candidate list
-  int32_t* out = idx + row * (long long)k;
-  int n_valid;
-  RowView<KEPT> rv = make_row<NT, KEPT>(scores, ld, q_pos, kept, bs, n_keep, L_max, row, kept_s, scan_tmp, &n_valid);
-  if constexpr (!KEPT) {
-    if (pg.page_table != nullptr) {  // paged caches: the list receives pool rows
-      rv.pt = pg.page_table + (row / n_q) * pg.max_pages;
-      rv.plog2 = pg.page_log2;
-      rv.n_pages = pg.n_pages;
-    }
-  }
-  if (count != nullptr && threadIdx.x == 0) count[row] = min(k, n_valid);
   if (n_valid <= k) {
     select_all<NT, KEPT>(rv, n_valid, k, wcnt, out);
     return;
@@ -568,6 +545,155 @@ __global__ __launch_bounds__(NT) void topk_kernel(const int32_t* __restrict__ sc
   } else {
     fallback_select<NT, KEPT>(rv, k, lds_big, wcnt, h256, scan_tmp, sh, out);
   }
+}
+
+// ---------------------------------------------------------------------------------
+// Single workgroup per row (many rows: prefill chunks).
+template <int NT, bool KEPT>
+__global__ __launch_bounds__(NT) void topk_kernel(const int32_t* __restrict__ scores, long long ld,
+                                                  const int32_t* __restrict__ q_pos,
+                                                  const int32_t* __restrict__ kept, int bs, int n_keep,
+                                                  int L_max, int k, int32_t* __restrict__ idx,
+                                                  int32_t* __restrict__ count,
+                                                  const int32_t* __restrict__ row_state, int n_q, Pages pg) {
+  constexpr int NW = NT / 64;
+  constexpr int VG = 4;  // groups of 4 slots per thread per pass
+  __shared__ int lds_big[NBINS];  // histogram, then the candidate list (slots | scores)
+  __shared__ int wcnt[2 * VG * NW];
+  __shared__ int scan_tmp[NW + 1];
+  __shared__ int h256[256];
+  __shared__ int kept_s[256];
+  __shared__ int sh[8];
+
+  const long long row = blockIdx.x;
+  if (row_state != nullptr && row_state[row] == 0) return;  // selected from its candidate list
+  int32_t* out = idx + row * (long long)k;
+  int n_valid;
+  RowView<KEPT> rv = make_row<NT, KEPT>(scores, ld, q_pos, kept, bs, n_keep, L_max, row, kept_s, scan_tmp, &n_valid);
+  if constexpr (!KEPT) {
+    if (pg.page_table != nullptr) {  // paged caches: the list receives pool rows
+      rv.pt = pg.page_table + (row / n_q) * pg.max_pages;
+      rv.plog2 = pg.page_log2;
+      rv.n_pages = pg.n_pages;
+    }
+  }
+  if (count != nullptr && threadIdx.x == 0) count[row] = min(k, n_valid);
+  select_row<NT, KEPT>(rv, n_valid, k, out, lds_big, wcnt, scan_tmp, h256, sh);
+}
+
+// ---------------------------------------------------------------------------------
+// Two-stage token stage and its top-k in one kernel: one query per workgroup scores the
+// slots of its kept blocks (slot s is key kept[s / bs] * bs + s % bs) as the direct
+// indexer kernel does -- 64-slot groups straight into MFMA B fragments through a register
+// ring, scores into LDS -- and then takes its exact top-k from those LDS scores with the
+// score-table kernel's row selection (select_row), so no score table is written or
+// read back.  Rows of at most KSEL_SLOTS slots (n_keep * bs).
+template <int D, int MT>
+__global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
+    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
+    int w_per_query, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ kept, int bs, int n_keep,
+    int n_q, int L_max, int H_I, int k, int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+  constexpr int NT = 256, NW = NT / 64, KS = D / 64, RING = 4;
+  __shared__ int kept_s[256];
+  __shared__ __attribute__((aligned(16))) int sbuf[KSEL_SLOTS];
+  __shared__ int lds_big[NBINS];
+  __shared__ int wcnt[2 * 4 * NW];
+  __shared__ int scan_tmp[NW + 1];
+  __shared__ int h256[256];
+  __shared__ int sh[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const long long row = blockIdx.x;
+  const int b = (int)(row / n_q);
+  int32_t* out = idx + row * (long long)k;
+  v4i A[MT][KS];
+  int wv[MT][4];
+  issue_query<D, MT>(q_idx, w, w_per_query, row, H_I, A, wv);
+  const int p = min(q_pos[row], L_max - 1);
+  if (p < 0) {  // no key to see (uniform)
+    for (int t = tid; t < k; t += NT) out[t] = -1;
+    if (count != nullptr && tid == 0) count[row] = 0;
+    return;
+  }
+  for (int t = tid; t < n_keep; t += NT) kept_s[t] = kept[row * n_keep + t];
+  __syncthreads();
+  const int n_slots = n_keep * bs;
+  int n_valid;  // candidates: keys of kept blocks at or below p
+  {
+    int c = 0;
+    if (tid < n_keep) {
+      const int blk = kept_s[tid];
+      if (blk >= 0) c = max(0, min(bs, p - blk * bs + 1));
+    }
+    (void)block_exclusive_scan<NT>(c, scan_tmp, &n_valid);
+  }
+  const int8_t* kb = k_idx + (long long)b * L_max * D;
+  // a slot without a kept block, or past the cache, reads a fallback row: its score is
+  // never a candidate, and the loads stay unconditional
+  auto key_load = [&](int sl) -> int {
+    const int blk = kept_s[sl / bs];
+    return blk >= 0 ? min(blk * bs + sl % bs, L_max - 1) : 0;
+  };
+  v4i ring[RING][4][KS];
+  auto load_group = [&](int i, v4i (&Bf)[4][KS]) {
+    const int sg = 64 * (wave + NW * i);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int8_t* kr = kb + (long long)key_load(min(sg + 16 * nt + r16, n_slots - 1)) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
+    }
+  };
+  const int n_groups = (n_slots + 63) / 64;
+  const int n_iter = ((n_groups + NW - 1) / NW + RING - 1) / RING * RING;  // groups per wave, padded
+#pragma unroll
+  for (int r = 0; r < RING - 1; ++r) load_group(r, ring[r]);
+  int wt[MT][4];
+  query_weights<MT>(wv, H_I, true, wt);
+  for (int i0 = 0; i0 < n_iter; i0 += RING) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      load_group(i0 + r + RING - 1, ring[(r + RING - 1) % RING]);
+      const int sg = 64 * (wave + NW * (i0 + r));
+      int part[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        v4i acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          acc[mt] = v4i{0, 0, 0, 0};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc[mt] = mfma_i8(A[mt][ks], ring[r][nt][ks], acc[mt]);
+        }
+        int ps = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) ps = relu_mad24(acc[mt][e], wt[mt][e], ps);
+        part[nt] = ps;
+      }
+      const int res = reduce_scatter4(part);
+      const int sl = sg + 16 * g + r16;
+      if (sl < n_slots) sbuf[sl] = res;
+    }
+  }
+  __syncthreads();
+  RowView<true> rv;
+  rv.srow = sbuf;
+  rv.kept_s = kept_s;
+  rv.n_slots = n_slots;
+  rv.p = p;
+  rv.bs = bs;
+  rv.vec = true;
+  if (count != nullptr && tid == 0) count[row] = min(k, n_valid);
+  select_row<NT, true>(rv, n_valid, k, out, lds_big, wcnt, scan_tmp, h256, sh);
+}
+
+template <int D, int MT>
+static hipError_t launch_kept_select_t(const IdxArgs& a, int k, int32_t* idx, int32_t* count, hipStream_t st) {
+  const long long rows = (long long)a.B * a.n_q;
+  hipLaunchKernelGGL((idx_kept_select_kernel<D, MT>), dim3((unsigned)rows), dim3(256), 0, st, a.q_idx, a.k_idx, a.w,
+                     a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I, k, idx, count);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------
@@ -1731,6 +1857,30 @@ hipError_t launch_expand(const int32_t* kept, const int32_t* q_pos, long long ro
   hipLaunchKernelGGL(expand_kernel<256>, dim3((unsigned)rows), dim3(256), 0, st, kept, q_pos, bs, n_keep, k, idx,
                      count);
   return hipGetLastError();
+}
+
+hipError_t launch_kept_select(const IdxArgs& a, int k, int32_t* idx, int32_t* count, hipStream_t st) {
+  const long long rows = (long long)a.B * a.n_q;
+  if (rows == 0) return hipSuccess;
+  if (a.kept == nullptr || a.block_size < 1 || a.n_keep < 1 || a.n_keep > 256 ||
+      (long long)a.n_keep * a.block_size > KSEL_SLOTS || k < 1 || (a.d_I != 64 && a.d_I != 128) || a.H_I < 1 ||
+      a.H_I > 64)
+    return hipErrorInvalidValue;
+  const int mt = (a.H_I + 15) / 16;
+  if (a.d_I == 128) {
+    switch (mt) {
+      case 1: return launch_kept_select_t<128, 1>(a, k, idx, count, st);
+      case 2: return launch_kept_select_t<128, 2>(a, k, idx, count, st);
+      case 3: return launch_kept_select_t<128, 3>(a, k, idx, count, st);
+      default: return launch_kept_select_t<128, 4>(a, k, idx, count, st);
+    }
+  }
+  switch (mt) {
+    case 1: return launch_kept_select_t<64, 1>(a, k, idx, count, st);
+    case 2: return launch_kept_select_t<64, 2>(a, k, idx, count, st);
+    case 3: return launch_kept_select_t<64, 3>(a, k, idx, count, st);
+    default: return launch_kept_select_t<64, 4>(a, k, idx, count, st);
+  }
 }
 
 hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st) {

@@ -724,13 +724,24 @@ def test_forward_decode_fused_selection_concentrated(lsa, kind):
         assert np.array_equal(J[b, i], r["J"]), f"{kind} seq {b}"
 
 
-@pytest.mark.parametrize("T,bs,n_keep,k", [(4096, 128, 8, 256), (2048, 16, 6, 40)])
+@pytest.mark.parametrize("T,bs,n_keep,k", [(4096, 128, 8, 256), (2048, 16, 6, 40), (20000, 128, 64, 2048),
+                                           (20000, 128, 100, 2048)])
 def test_forward_two_stage_small(lsa, T, bs, n_keep, k):
+    """Two-stage lsa_forward against the oracle, and bit for bit against the separate calls
+    (block prefilter, kept-slot scores, score-table top-k): with at most 8192 kept slots
+    the forward scores and selects in one kernel, above that through the score table."""
     n_q = 64
     wl = synthetic.Workload("ts", B=1, n_q=n_q, L=T, q_pos0=T - n_q, H_I=64, d_I=128, k=k, H_q=16,
                             two_stage=True, block_size=bs, n_keep=n_keep)
     inp, g = _inputs(wl, seed=6)
     res = lsa.lsa_forward(g, k_top=k, two_stage=True, block_size=bs, n_keep=n_keep)
+    kept_g = lsa.lsa_block_prefilter(g["q_idx"], lsa.lsa_block_reps(g["k_idx"], bs), g["w"], g["q_pos"], bs, n_keep)
+    sc = lsa.lsa_index_scores(g["q_idx"], g["k_idx"], g["w"], g["q_pos"], kept_blocks=kept_g, block_size=bs,
+                              n_keep=n_keep)
+    idx2, cnt2 = lsa.lsa_topk(sc, g["q_pos"], k, T, kept_blocks=kept_g, block_size=bs)
+    assert torch.equal(kept_g, res["kept"])
+    assert torch.equal(idx2, res["idx"])
+    assert torch.equal(cnt2, res["count"])
     qi, ki, w = inp["q_idx"].numpy(), inp["k_idx"].numpy(), inp["w"].numpy()
     q, kk, vv = np64(inp["q"]), np64(inp["k"]), np64(inp["v"])
     reps = oracle.block_reps(ki[0], bs)

@@ -93,10 +93,15 @@ def test_forward_stages_listing():
     ws = lsa.lsa_forward_workspace_size(inp, 512, chunk_rows=1000)
     assert lsa.lsa_forward_stages(inp, 512, ws, chunk_rows=1000) == [
         "sample", "index_select", "topk", "sparse_attn"] * 3
-    # two-stage: block representatives once, then four stages per chunk
+    # two-stage: the block-key cache once, then per chunk the block prefilter, the token
+    # stage with its top-k in one kernel (kept slots fit one workgroup), the attention
     inp = _fake_inputs(1, 512, 8192)
     ws = lsa.lsa_forward_workspace_size(inp, 512, two_stage=True, chunk_rows=256)
     st = lsa.lsa_forward_stages(inp, 512, ws, two_stage=True, chunk_rows=256)
+    assert st == ["block_reps"] + ["block_prefilter", "index_select", "sparse_attn"] * 2
+    # ... and with more kept slots than one workgroup holds, the token score table
+    ws = lsa.lsa_forward_workspace_size(inp, 512, two_stage=True, block_size=128, n_keep=100, chunk_rows=256)
+    st = lsa.lsa_forward_stages(inp, 512, ws, two_stage=True, block_size=128, n_keep=100, chunk_rows=256)
     assert st == ["block_reps"] + ["block_prefilter", "index_scores", "topk", "sparse_attn"] * 2
 
 
