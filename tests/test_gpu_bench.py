@@ -1,0 +1,32 @@
+"""The benchmark's default run, shortened: it finishes and prints one JSON line with
+the fields its readers rely on (metric, value, roofline, per-workload stage times)."""
+from __future__ import annotations
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = [pytest.mark.gpu]
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_headline_line():
+    p = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "3", "--warmup", "1",
+                        "--no-cpu-baseline"], cwd=ROOT, capture_output=True, text=True, timeout=400)
+    assert p.returncode == 0, p.stderr[-3000:]
+    lines = [l for l in p.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1, p.stdout[-3000:]
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "dtype", "config", "roofline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["value"] > 0
+    r = d["roofline"]
+    assert r["bound"] in ("hbm", "mfma", "alu") and 0 < r["frac"] < 1.5 and r["peak"] > 0
+    for wl in ("decode_128k_paged", "decode_128k_pool4", "prefill_128k"):
+        assert d[wl]["ms_per_step"] > 0 and d[wl]["kernel_ms"], wl
+    assert 0 < d["prefill_128k"]["roofline"]["frac"] < 1.5

@@ -155,3 +155,12 @@ def test_forward_rejects_too_few_stage_events():
     a.n_stage_events = n.value
     fake_ws = ctypes.c_void_p(1 << 20)   # never dereferenced: the call returns before any launch
     assert lsa.lib().lsa_forward(ctypes.byref(a), fake_ws, ws, None) == -1
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py runs on one GPU: asked for more it exits with a message before touching a device."""
+    import subprocess
+    import sys
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=60)
+    assert p.returncode == 2 and "one GPU" in p.stderr
