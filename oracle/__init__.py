@@ -21,4 +21,17 @@ from .lsa_oracle import (  # noqa: F401
     forward_row,
     paged_rows,
     forward_row_paged,
+    sem_bf16,
+    sem_normalize,
+    sem_pool_keys,
+    sem_ward_costs,
+    sem_ward,
+    sem_cluster_block,
+    bucket_cache,
+    sem_scores,
+    sem_order_key,
+    sem_top_buckets,
+    sem_expand,
+    semantic_select_row,
+    semantic_forward_row,
 )

@@ -240,3 +240,253 @@ def forward_row_paged(q_idx_row, k_idx_pool, w, p: int, k: int, page_table_row, 
     res["J_logical"] = J
     res["J"] = np.where(J >= 0, rows[np.maximum(J, 0)], -1)
     return res
+
+
+# =================================================================================
+# Semantic search, flat ([LSA] §3.1 "Semantic Clustering", §3.2 "Semantic Search",
+# App. F.1 "Kernels": "Selection by threshold", "Flat decode").
+#
+# Floating point decides integers here (which buckets merge, which are kept), so
+# every such decision is taken in fp32 with each operation rounded on its own and
+# sums over the index dimensions taken in order d = 0, 1, ...: the kernels follow
+# the same definition and reach the same bits.  Readings where the pages are silent
+# (listed again in the design notes):
+#   * normalisation: ss = sum_d x_d * x_d, norm = sqrt(ss), x_d / norm, all fp32; a
+#     zero vector stays zero;
+#   * pool keys are sums of the *normalised* keys (normalisation comes first in §3.1),
+#     summed in key order;
+#   * Ward's cost of buckets a, b with sums S and sizes n (in pool keys):
+#     |n_b S_a - n_a S_b|^2 / (n_a n_b (n_a + n_b)), the rise of the total squared
+#     distance of the pool keys from their bucket means;
+#   * a bucket's partner is its cheapest allowed merge, the lower id at equal cost;
+#     ids are pool-key indices and a merged bucket keeps the lower id (so an id is
+#     the lowest pool key a bucket holds);
+#   * when merging every mutual pair of a round would leave fewer than m buckets,
+#     only the cheapest pairs merge (cost, then lower id), so exactly m remain;
+#   * centroids and index queries are normalised in fp32 and rounded to bf16 (the
+#     pages score bf16 operands); a score is the fp32 sum of the exact products;
+#   * a bucket's keys are listed in ascending position; buckets of a cluster block
+#     by id.
+# =================================================================================
+
+_F32 = np.float32
+
+
+def sem_bf16(x) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest, ties to even); returned as fp32 values."""
+    u = np.ascontiguousarray(x, dtype=_F32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(_F32)
+
+
+def sem_normalize(x) -> np.ndarray:
+    """L2 normalisation of every row in fp32 ([LSA] §3.1 "Key normalisation", §3.2
+    "Query normalisation"): ss summed d = 0, 1, ..., each product and sum rounded;
+    sqrt and division correctly rounded; a zero row stays zero."""
+    x = np.asarray(x, _F32)
+    ss = np.zeros(x.shape[:-1], _F32)
+    for j in range(x.shape[-1]):
+        ss = ss + x[..., j] * x[..., j]
+    nrm = np.sqrt(ss)
+    safe = np.where(nrm > 0, nrm, _F32(1)).astype(_F32)
+    return np.where((nrm > 0)[..., None], x / safe[..., None], _F32(0)).astype(_F32)
+
+
+def sem_pool_keys(k_blk, n_pool: int) -> np.ndarray:
+    """Pool keys of a run of index keys ([LSA] §3.1 "Pooling"): every n_pool
+    consecutive normalised keys summed, ((y0 + y1) + y2) + ..., in fp32."""
+    y = sem_normalize(k_blk)
+    n = y.shape[0] // n_pool
+    y = y[: n * n_pool].reshape(n, n_pool, y.shape[-1])
+    P = y[:, 0].copy()
+    for i in range(1, n_pool):
+        P = P + y[:, i]
+    return P
+
+
+def sem_ward_costs(S, cnt) -> np.ndarray:
+    """Ward's merge cost of every pair of buckets ([LSA] §3.1 "Clustering", Ward's
+    criterion): |n_b S_a - n_a S_b|^2 / (n_a n_b (n_a + n_b)) for bucket sums S [n, d]
+    and sizes cnt [n] (pool keys), in fp32 with the squared norm summed d = 0, 1, ...
+    Equal to n_a n_b / (n_a + n_b) * |mean_a - mean_b|^2, and symmetric bit for bit."""
+    S = np.asarray(S, _F32)
+    n = np.asarray(cnt).astype(_F32)
+    na = n[:, None]
+    nb = n[None, :]
+    sq = np.zeros((S.shape[0], S.shape[0]), _F32)
+    for j in range(S.shape[1]):
+        dj = nb * S[:, None, j] - na * S[None, :, j]
+        sq = sq + dj * dj
+    return sq / (na * nb * (na + nb))
+
+
+def sem_ward(P, m: int, cap: int):
+    """Bottom-up Ward clustering of one cluster block's pool keys into m buckets
+    ([LSA] §3.1 "Clustering").
+
+    Every pool key starts as a bucket of its own (id = its index).  Each round, every
+    bucket finds its cheapest allowed partner (a merge is allowed if the two hold at
+    most ``cap`` pool keys together; lowest cost, then lowest id), and all pairs of
+    buckets that are each other's partner merge at once; the merged bucket keeps the
+    lower id and the sum of both sums.  If merging all of them would leave fewer than
+    m buckets, only the cheapest pairs merge (cost, then lower id).  Stops at m
+    buckets, or when no merge is allowed.
+
+    Returns (label of every pool key = its bucket id, bucket sums [n, d] (rows of
+    live ids), sizes [n], merge log [(round, a, b, cost)])."""
+    P = np.asarray(P, _F32)
+    n = P.shape[0]
+    S = P.copy()
+    cnt = np.ones(n, np.int64)
+    alive = np.ones(n, bool)
+    lab = np.arange(n)
+    log = []
+    live, rnd = n, 0
+    while live > m:
+        C = sem_ward_costs(S, cnt)
+        ok = alive[:, None] & alive[None, :] & ((cnt[:, None] + cnt[None, :]) <= cap)
+        np.fill_diagonal(ok, False)
+        Cm = np.where(ok, C, np.inf)
+        partner = np.where(ok.any(1), np.argmin(Cm, axis=1), -1)
+        pairs = [(a, int(partner[a])) for a in range(n)
+                 if alive[a] and partner[a] > a and partner[partner[a]] == a]
+        if not pairs:
+            break
+        if live - len(pairs) < m:
+            pairs.sort(key=lambda ab: (C[ab[0], ab[1]], ab[0]))
+            pairs = pairs[: live - m]
+        for a, b in pairs:
+            log.append((rnd, a, b, float(C[a, b])))
+            S[a] = S[a] + S[b]
+            cnt[a] += cnt[b]
+            alive[b] = False
+            lab[lab == b] = a
+        live -= len(pairs)
+        rnd += 1
+    return lab, S, cnt, log
+
+
+def sem_cluster_block(k_blk, n_pool: int, m: int, n_max: int, first_key: int = 0):
+    """One complete cluster block into its bucket-cache entry ([LSA] §3.1 "Clustering",
+    "Bucket cache").  k_blk: the block's n_cluster index keys [n_cluster, d] (bf16
+    values).  Returns (centroids [n_b, d]: each bucket's sum normalised and rounded to
+    bf16; table [n_cluster]: key positions, bucket after bucket in id order, each
+    bucket's keys ascending; offsets [n_b + 1] into the table).  n_b = m unless the
+    size cap stopped the merging early."""
+    P = sem_pool_keys(k_blk, n_pool)
+    lab, S, _, _ = sem_ward(P, m, n_max // n_pool)
+    ids = np.unique(lab)
+    cent = sem_bf16(sem_normalize(S[ids]))
+    table, off = [], [0]
+    for b in ids:
+        for u in np.nonzero(lab == b)[0]:
+            table.extend(range(first_key + int(u) * n_pool, first_key + (int(u) + 1) * n_pool))
+        off.append(len(table))
+    return cent, np.asarray(table, np.int64), np.asarray(off, np.int64)
+
+
+def bucket_cache(k_idx, n_cluster: int, n_pool: int, n_bavg: int, n_max: int, n_blocks=None) -> dict:
+    """Bucket cache of one sequence ([LSA] §3.1 "Bucket cache"): every complete cluster
+    block of k_idx [L, d] (or the first n_blocks) clustered into m = n_cluster / n_bavg
+    buckets.  Returns dict(centroids [NB, m, d], table [NB, n_cluster], offsets
+    [NB, m + 1], n_cluster)."""
+    k_idx = np.asarray(k_idx, _F32)
+    m = n_cluster // n_bavg
+    nb = k_idx.shape[0] // n_cluster if n_blocks is None else n_blocks
+    cents, tabs, offs = [], [], []
+    for blk in range(nb):
+        c, t, o = sem_cluster_block(k_idx[blk * n_cluster:(blk + 1) * n_cluster], n_pool, m, n_max,
+                                    first_key=blk * n_cluster)
+        assert c.shape[0] == m, "size cap left more than m buckets"
+        cents.append(c)
+        tabs.append(t)
+        offs.append(o)
+    d = k_idx.shape[1]
+    return {"centroids": np.asarray(cents, _F32).reshape(nb, m, d),
+            "table": np.asarray(tabs, np.int64).reshape(nb, n_cluster),
+            "offsets": np.asarray(offs, np.int64).reshape(nb, m + 1), "n_cluster": n_cluster}
+
+
+def sem_scores(qn, cent) -> np.ndarray:
+    """s_b = c_b . q for every bucket ([LSA] §3.2 "Scoring"): bf16 operands, every
+    product exact in fp32, the sum taken d = 0, 1, ... with each addition rounded."""
+    qn = np.asarray(qn, _F32)
+    cent = np.asarray(cent, _F32)
+    s = np.zeros(cent.shape[0], _F32)
+    for j in range(cent.shape[1]):
+        s = s + cent[:, j] * qn[j]
+    return s
+
+
+def sem_order_key(s) -> np.ndarray:
+    """Order-keeping unsigned image of fp32 scores (the upper half of the packed key of
+    [LSA] App. F.1 "Selection by threshold"): a higher score gives a larger key; -0
+    sits just below +0."""
+    u = np.asarray(s, _F32).view(np.uint32).astype(np.uint64)
+    return np.where((u >> 31) == 1, u ^ 0xFFFFFFFF, u | 0x80000000)
+
+
+def sem_top_buckets(s, p_top: int) -> np.ndarray:
+    """The top-p buckets of a row, best first: the larger packed key first, i.e. the
+    higher score, at equal keys the lower bucket id ([LSA] §3.2 "Scoring",
+    App. F.1 "Selection by threshold")."""
+    key = sem_order_key(s).astype(np.int64)
+    order = np.lexsort((np.arange(key.shape[0]), -key))
+    return order[:p_top]
+
+
+def sem_expand(best_first, table, offsets, p: int, k: int, n_sink: int, n_w: int) -> np.ndarray:
+    """Long-range keys of one query ([LSA] §3.2 "Expansion"): the selected buckets best
+    first, each bucket's keys in table order, skipping keys of the sink (j < n_sink) and
+    of the window (j > p - n_w), until k keys."""
+    m = offsets.shape[1] - 1
+    w0 = max(0, p - n_w + 1)
+    out = []
+    for b in best_first:
+        if len(out) >= k:
+            break
+        blk, loc = divmod(int(b), m)
+        for j in table[blk, offsets[blk, loc]:offsets[blk, loc + 1]]:
+            if j < n_sink or j >= w0:
+                continue
+            out.append(int(j))
+            if len(out) == k:
+                break
+    return np.asarray(out, np.int64)
+
+
+def semantic_select_row(q_idx_row, cache: dict, p: int, k: int, p_top: int, n_sink: int, n_w: int) -> dict:
+    """Index list J_i of one query under flat semantic search ([LSA] §3.2): the query
+    (normalised, bf16) scores every bucket of the cluster blocks before its own, keeps
+    the top-p, expands them into k long-range keys; J_i adds the sink keys and the
+    window (p - n_w, p].  Ascending, -1 padded to n_sink + k + n_w.
+    Returns dict(J, count, kept (best first), scores)."""
+    width = n_sink + k + n_w
+    J = np.full((width,), -1, np.int64)
+    if p < 0:
+        return {"J": J, "count": 0, "kept": np.zeros(0, np.int64), "scores": np.zeros(0, _F32)}
+    n_c = cache["n_cluster"]
+    cent = cache["centroids"]
+    m = cent.shape[1]
+    nb = p // n_c
+    assert nb <= cent.shape[0], "bucket cache lacks blocks before the query's own"
+    qn = sem_bf16(sem_normalize(np.asarray(q_idx_row, _F32)))
+    s = sem_scores(qn, cent[:nb].reshape(nb * m, cent.shape[2]))
+    kept = sem_top_buckets(s, p_top)
+    lr = sem_expand(kept, cache["table"], cache["offsets"], p, k, n_sink, n_w)
+    w0 = max(0, p - n_w + 1)
+    keys = sorted(set(range(min(n_sink, p + 1))) | set(range(w0, p + 1)) | set(lr.tolist()))
+    J[:len(keys)] = keys
+    return {"J": J, "count": len(keys), "kept": kept, "scores": s}
+
+
+def semantic_forward_row(q_idx_row, cache: dict, p: int, k: int, p_top: int, n_sink: int, n_w: int,
+                         q_row=None, k_cache=None, v_cache=None, scale: float | None = None) -> dict:
+    """Flat semantic search for one query, then attention over J_i ([LSA] §3.2
+    "Attention": one J_i for all heads)."""
+    r = semantic_select_row(q_idx_row, cache, p, k, p_top, n_sink, n_w)
+    if q_row is not None:
+        if scale is None:
+            scale = 1.0 / np.sqrt(np.asarray(q_row).shape[-1])
+        r["out"], r["lse"] = sparse_attention(q_row, k_cache, v_cache, r["J"], scale)
+    return r

@@ -461,6 +461,239 @@ def check_paged_permutation(impl, seed=11):
     return _all(r)
 
 
+# ---------------------------------------------------------------- semantic search (LSA Flat)
+# [LSA] §3.1 "Semantic Clustering", §3.2 "Semantic Search".  Pinned by: closed forms of the
+# normalisation and pooling, scipy's Ward linkage (the full hierarchy; Ward's criterion is
+# reducible, so merging mutual-cheapest pairs in rounds gives the same clusters as the
+# sequential algorithm), the rise of the sum of squared distances computed from the members
+# in fp64, hand-worked merge and expansion cases, and the reduction to token-level top-k.
+
+def _sem_keys(rng, n, d=64, scale=1.0):
+    return impl_bf16(rng.standard_normal((n, d)) * scale)
+
+
+def impl_bf16(x):
+    import torch
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def check_sem_normalize_pool(impl, seed=20):
+    rng = np.random.default_rng(seed)
+    r = []
+    x = _sem_keys(rng, 64, scale=3.0)
+    y = impl.sem_normalize(x)
+    n64 = np.sqrt((y.astype(np.float64) ** 2).sum(1))
+    r.append(_ok(np.abs(n64 - 1).max() < 1e-6, f"unit norm {np.abs(n64 - 1).max()}"))
+    cos = (y.astype(np.float64) * x).sum(1) / np.sqrt((x.astype(np.float64) ** 2).sum(1))
+    r.append(_ok(np.abs(cos - 1).max() < 1e-6, "direction kept"))
+    r.append(_ok(np.array_equal(impl.sem_normalize(2 * x), y), "scale by 2 changes no bit"))
+    z = np.zeros((3, 64), np.float32)
+    r.append(_ok(np.array_equal(impl.sem_normalize(z), z), "zero row stays zero"))
+    # pool keys: sums of the normalised keys, whatever the raw norms
+    raw = _sem_keys(rng, 32) * np.repeat(rng.integers(1, 50, 32)[:, None], 64, 1).astype(np.float32)
+    P = impl.sem_pool_keys(raw, 4)
+    x64 = raw.astype(np.float64)
+    want = (x64 / np.sqrt((x64 ** 2).sum(1, keepdims=True))).reshape(8, 4, 64).sum(1)
+    r.append(_ok(P.shape == (8, 64) and np.abs(P - want).max() < 1e-5, "pool = sum of normalised keys"))
+    r.append(_ok(np.array_equal(impl.sem_pool_keys(raw, 1), impl.sem_normalize(raw)), "n_pool 1"))
+    # bf16 rounding: nearest, ties to even
+    v = np.array([1.0, 1.00390625, 1.005859375, 1.0078125 + 2 ** -9, -3.0e-3], np.float32)
+    r.append(_ok(np.array_equal(impl.sem_bf16(v), impl_bf16(v)), "bf16 rounding"))
+    return _all(r)
+
+
+def _clusters_from_log(n, log):
+    members = {i: frozenset([i]) for i in range(n)}
+    out = {}
+    for _, a, b, cost in log:
+        members[a] = members[a] | members[b]
+        out[members[a]] = cost
+    return out
+
+
+def check_sem_ward_scipy(impl, seed=21):
+    from scipy.cluster.hierarchy import linkage
+    rng = np.random.default_rng(seed)
+    r = []
+    for n, d in ((24, 64), (40, 16), (33, 8)):
+        P = rng.standard_normal((n, d)).astype(np.float32)
+        lab, S, cnt, log = impl.sem_ward(P, 1, n)
+        got = _clusters_from_log(n, log)
+        Z = linkage(P.astype(np.float64), method="ward")
+        mem = {i: frozenset([i]) for i in range(n)}
+        want = {}
+        for i, (u, v, h, _) in enumerate(Z):
+            mem[n + i] = mem[int(u)] | mem[int(v)]
+            want[mem[n + i]] = h * h / 2
+        same = set(got) == set(want)
+        r.append(_ok(same, f"Ward hierarchy n={n}"))
+        if same:
+            rel = max(abs(got[c] - want[c]) / max(want[c], 1e-12) for c in got)
+            r.append(_ok(rel < 1e-3, f"merge costs vs heights n={n}: {rel}"))
+        r.append(_ok(len(set(lab.tolist())) == 1 and cnt[0] == n, "one bucket at m=1"))
+    return _all(r)
+
+
+def check_sem_ward_hand(impl):
+    # 1-D points on axis 0: mutual pairs (0,1) cost 0.5, (2,3) 0.125, (4,5) 2.
+    x = np.array([0, 1, 10, 10.5, 30, 32], np.float32)
+    P = np.zeros((6, 8), np.float32)
+    P[:, 0] = x
+    r = []
+    for m, cap, want in ((5, 6, [0, 1, 2, 2, 4, 5]), (4, 6, [0, 0, 2, 2, 4, 5]), (3, 6, [0, 0, 2, 2, 4, 4]),
+                         (2, 6, [0, 0, 0, 0, 4, 4]), (1, 6, [0] * 6), (2, 2, [0, 0, 2, 2, 4, 4])):
+        lab, S, cnt, log = impl.sem_ward(P, m, cap)
+        r.append(_ok(lab.tolist() == want, f"m={m} cap={cap}: {lab.tolist()}"))
+    lab, S, cnt, log = impl.sem_ward(P, 2, 6)
+    costs = [(a, b, c) for _, a, b, c in log]
+    r.append(_ok(costs[:3] == [(0, 1, 0.5), (2, 3, 0.125), (4, 5, 2.0)] and costs[3][:2] == (0, 2)
+                 and abs(costs[3][2] - 95.0625) < 1e-4, f"costs {costs}"))
+    r.append(_ok(S[0, 0] == 21.5 and cnt[0] == 4 and S[4, 0] == 62, "sums and sizes"))
+    return _all(r)
+
+
+def check_sem_ward_invariants(impl, seed=22):
+    rng = np.random.default_rng(seed)
+    r = []
+    P = impl.sem_pool_keys(_sem_keys(rng, 512), 4)
+    for m, cap in ((64, 8), (32, 8), (16, 32)):
+        lab, S, cnt, log = impl.sem_ward(P, m, cap)
+        ids = sorted(set(lab.tolist()))
+        sizes = [int((lab == b).sum()) for b in ids]
+        r.append(_ok(len(ids) == m and max(sizes) <= cap, f"m={m} cap={cap}: {len(ids)} {max(sizes)}"))
+        r.append(_ok(all(b == int(np.nonzero(lab == b)[0][0]) for b in ids), "id = lowest pool key"))
+        s64 = {b: P[lab == b].astype(np.float64).sum(0) for b in ids}
+        r.append(_ok(all(np.abs(S[b] - s64[b]).max() < 1e-4 for b in ids), "bucket sum = member sum"))
+        # each merge's cost = rise of the sum of squared distances of the members (fp64)
+        mem = {i: [i] for i in range(P.shape[0])}
+        worst = 0.0
+        for _, a, b, cost in log:
+            A, Bm = P[mem[a]].astype(np.float64), P[mem[b]].astype(np.float64)
+            U = np.vstack([A, Bm])
+            sse = lambda X: ((X - X.mean(0)) ** 2).sum()
+            rise = sse(U) - sse(A) - sse(Bm)
+            worst = max(worst, abs(cost - rise) / max(rise, 1e-6))
+            mem[a] = mem[a] + mem[b]
+        r.append(_ok(worst < 1e-3, f"cost = SSE rise ({worst})"))
+    # well separated blobs of `cap` pool keys come back as the buckets
+    cen = rng.standard_normal((8, 64)) * 10
+    order = rng.permutation(32)
+    Pb = (cen[np.arange(32) // 4] + 0.01 * rng.standard_normal((32, 64)))[order].astype(np.float32)
+    lab, _, _, _ = impl.sem_ward(Pb, 8, 4)
+    blob = (np.arange(32) // 4)[order]
+    r.append(_ok(all(len(set(blob[lab == b])) == 1 and (lab == b).sum() == 4 for b in set(lab.tolist())),
+                 "blobs recovered"))
+    return _all(r)
+
+
+def _hand_cache():
+    # 3 cluster blocks of 8 keys, 2 buckets each (the bucket cache written out by hand)
+    table = np.array([[0, 1, 4, 5, 2, 3, 6, 7], [8, 9, 10, 11, 12, 13, 14, 15],
+                      [16, 17, 20, 21, 18, 19, 22, 23]])
+    offsets = np.array([[0, 4, 8]] * 3)
+    a = np.array([0.125, 0.5, 0.875, 0.25, 0.875, 0.75], np.float32)
+    cent = np.zeros((3, 2, 4), np.float32)
+    cent[:, :, 0] = a.reshape(3, 2)
+    return {"centroids": cent, "table": table, "offsets": offsets, "n_cluster": 8}
+
+
+def check_sem_select_hand(impl):
+    c = _hand_cache()
+    q = np.array([3, 0, 0, 0], np.float32)
+    r = []
+    # p = 26: own block 3; window 19..26; b2 and b4 tie (0.875), the lower id first
+    got = impl.semantic_select_row(q, c, 26, 7, 4, 2, 8)
+    want = [0, 1, 8, 9, 10, 11, 16, 17, 18] + list(range(19, 27))
+    r.append(_ok(got["J"].tolist() == want and got["count"] == 17, f"p=26 k=7: {got['J'].tolist()}"))
+    r.append(_ok(got["kept"].tolist() == [2, 4, 5, 1], f"kept {got['kept'].tolist()}"))
+    got = impl.semantic_select_row(q, c, 26, 7, 2, 2, 8)
+    want = [0, 1, 8, 9, 10, 11, 16, 17] + list(range(19, 27)) + [-1]
+    r.append(_ok(got["J"].tolist() == want and got["count"] == 16, f"p=26 top-2: {got['J'].tolist()}"))
+    got = impl.semantic_select_row(q, c, 10, 7, 4, 2, 8)
+    want = [0, 1, 2] + list(range(3, 11)) + [-1] * 6
+    r.append(_ok(got["J"].tolist() == want and got["count"] == 11, f"p=10: {got['J'].tolist()}"))
+    got = impl.semantic_select_row(q, c, 5, 7, 4, 2, 8)
+    r.append(_ok(got["J"].tolist() == list(range(6)) + [-1] * 11 and got["count"] == 6, "p=5: window only"))
+    got = impl.semantic_select_row(q, c, -1, 7, 4, 2, 8)
+    r.append(_ok(got["count"] == 0 and (got["J"] == -1).all(), "padding row"))
+    s = impl.sem_scores(np.array([1, 0, 0, 0], np.float32), c["centroids"].reshape(6, 4))
+    r.append(_ok(s.tolist() == [0.125, 0.5, 0.875, 0.25, 0.875, 0.75], "scores"))
+    key = impl.sem_order_key(np.array([-2.0, -0.0, 0.0, 1e-30, 3.0], np.float32))
+    r.append(_ok(np.all(np.diff(key.astype(np.int64)) > 0), "order key"))
+    return _all(r)
+
+
+def check_sem_token_reduction(impl, seed=23):
+    """One key per bucket (n_pool = 1, m = n_cluster, no merge) and p = k: the long-range
+    keys are the exact top-k of the cosine scores over the keys of the earlier cluster
+    blocks, less those in the sink or the window."""
+    rng = np.random.default_rng(seed)
+    r = []
+    n_c, d = 32, 64
+    keys = _sem_keys(rng, 8 * n_c)
+    c = impl.bucket_cache(keys, n_c, 1, 1, 2)
+    k64 = keys.astype(np.float64)
+    kn = impl_bf16(k64 / np.sqrt((k64 ** 2).sum(1, keepdims=True)))
+    for p, k, n_sink, n_w in ((8 * n_c - 1, 20, 4, n_c), (5 * n_c + 3, 37, 0, n_c), (3 * n_c, 50, 2, 2 * n_c)):
+        q = _sem_keys(rng, 1)[0]
+        q64 = q.astype(np.float64)
+        qn = impl_bf16(q64 / np.sqrt((q64 ** 2).sum())).astype(np.float64)
+        nb = p // n_c
+        w0 = max(0, p - n_w + 1)
+        # the k best keys of the earlier blocks are the k selected buckets; the expansion
+        # then drops those in the sink or the window
+        sc = kn[: nb * n_c].astype(np.float64) @ qn
+        top = {j for j in np.argsort(-sc, kind="stable")[:k].tolist() if n_sink <= j < w0}
+        got = impl.semantic_select_row(q, c, p, k, k, n_sink, n_w)
+        J = got["J"][got["J"] >= 0]
+        lr = set(J.tolist()) - set(range(min(n_sink, p + 1))) - set(range(w0, p + 1))
+        r.append(_ok(lr == top, f"p={p} k={k}: {len(lr ^ top)} differ"))
+    return _all(r)
+
+
+def check_sem_invariants(impl, seed=24):
+    rng = np.random.default_rng(seed)
+    r = []
+    n_c = 512
+    keys = _sem_keys(rng, 6 * n_c)
+    c = impl.bucket_cache(keys, n_c, 4, 8, 32)
+    m = 64
+    r.append(_ok(all(sorted(c["table"][b].tolist()) == list(range(b * n_c, (b + 1) * n_c)) for b in range(6)),
+                 "table holds every key of its block once"))
+    sz = np.diff(c["offsets"], axis=1)
+    r.append(_ok(sz.min() >= 4 and sz.max() <= 32 and (sz % 4 == 0).all(), "bucket sizes"))
+    n64 = np.sqrt((c["centroids"].astype(np.float64) ** 2).sum(-1))
+    r.append(_ok(np.abs(n64 - 1).max() < 1e-2, "unit centroids"))
+    for p, k, pt in ((6 * n_c - 1, 300, 64), (6 * n_c - 1, 300, 16), (2 * n_c + 7, 200, 64), (n_c, 50, 8)):
+        q = _sem_keys(rng, 1)[0]
+        g = impl.semantic_select_row(q, c, p, k, pt, 4, n_c)
+        J = g["J"][: g["count"]]
+        w0 = max(0, p - n_c + 1)
+        ok = (np.all(np.diff(J) > 0) and (g["J"][g["count"]:] == -1).all() and J[-1] == p
+              and set(range(4)) <= set(J.tolist()) and set(range(w0, p + 1)) <= set(J.tolist()))
+        r.append(_ok(ok, f"J shape p={p}"))
+        lr = [j for j in J.tolist() if 4 <= j < w0]
+        kept = g["kept"]
+        bk = {}
+        for i, b in enumerate(kept):
+            blk, loc = divmod(int(b), m)
+            for j in c["table"][blk, c["offsets"][blk, loc]:c["offsets"][blk, loc + 1]]:
+                bk[int(j)] = i
+        avail = sum(1 for j in bk if 4 <= j < w0)
+        r.append(_ok(all(j in bk for j in lr) and len(lr) == min(k, avail), f"long-range keys p={p}"))
+        if lr:
+            # best first: every bucket ranked before the last one used is taken whole
+            last = max(bk[j] for j in lr)
+            whole = all(j in lr for j, i in bk.items() if i < last and 4 <= j < w0)
+            r.append(_ok(whole, f"buckets taken best first p={p}"))
+        s = g["scores"]
+        kk = impl.sem_order_key(s).astype(np.int64)
+        rest = np.setdiff1d(np.arange(s.shape[0]), kept)
+        r.append(_ok(len(kept) == min(pt, s.shape[0]) and (rest.size == 0 or kk[kept].min() >= kk[rest].max()),
+                     "top-p buckets"))
+    return _all(r)
+
+
 ALL_CHECKS = [
     check_scores_hand, check_scores_closed_forms, check_scores_invariances, check_scores_bound,
     check_topk_hand, check_topk_bruteforce, check_topk_special,
@@ -469,4 +702,6 @@ ALL_CHECKS = [
     check_attention_hand, check_attention_dense, check_attention_special,
     check_paged_hand, check_paged_identity, check_paged_permutation,
     check_pooled_hand, check_pooled_dense,
+    check_sem_normalize_pool, check_sem_ward_scipy, check_sem_ward_hand, check_sem_ward_invariants,
+    check_sem_select_hand, check_sem_token_reduction, check_sem_invariants,
 ]

@@ -159,6 +159,103 @@ def _paged_J_logical(*args, **kw):
     return res
 
 
+_orig_sem_ward_costs = O.sem_ward_costs
+_orig_sem_ward = O.sem_ward
+_orig_sem_expand = O.sem_expand
+
+
+def _sem_cost_unweighted(S, cnt):
+    S = np.asarray(S, np.float32)
+    d = S[:, None, :] - S[None, :, :]
+    return (d * d).sum(-1).astype(np.float32)
+
+
+def _sem_cost_no_denominator(S, cnt):
+    n = np.asarray(cnt).astype(np.float32)
+    den = n[:, None] * n[None, :] * (n[:, None] + n[None, :])
+    return (_orig_sem_ward_costs(S, cnt) * den).astype(np.float32)
+
+
+def _no_trim(P, m, cap):
+    # merges every mutual pair of the last round, so it may end below m buckets
+    P = np.asarray(P, np.float32)
+    n = P.shape[0]
+    S, cnt, alive, lab, log = P.copy(), np.ones(n, np.int64), np.ones(n, bool), np.arange(n), []
+    live, rnd = n, 0
+    while live > m:
+        C = O.sem_ward_costs(S, cnt)
+        ok = alive[:, None] & alive[None, :] & ((cnt[:, None] + cnt[None, :]) <= cap)
+        np.fill_diagonal(ok, False)
+        partner = np.where(ok.any(1), np.argmin(np.where(ok, C, np.inf), axis=1), -1)
+        pairs = [(a, int(partner[a])) for a in range(n) if alive[a] and partner[a] > a and partner[partner[a]] == a]
+        if not pairs:
+            break
+        for a, b in pairs:
+            log.append((rnd, a, b, float(C[a, b])))
+            S[a] = S[a] + S[b]
+            cnt[a] += cnt[b]
+            alive[b] = False
+            lab[lab == b] = a
+        live -= len(pairs)
+        rnd += 1
+    return lab, S, cnt, log
+
+
+def _sem_ward_greedy_nonmutual(P, m, cap):
+    # every bucket merges with its partner whether or not the choice is mutual
+    P = np.asarray(P, np.float32)
+    n = P.shape[0]
+    S, cnt, alive, lab, log = P.copy(), np.ones(n, np.int64), np.ones(n, bool), np.arange(n), []
+    live, rnd = n, 0
+    while live > m:
+        C = O.sem_ward_costs(S, cnt)
+        ok = alive[:, None] & alive[None, :] & ((cnt[:, None] + cnt[None, :]) <= cap)
+        np.fill_diagonal(ok, False)
+        if not ok.any():
+            break
+        a = int(np.nonzero(alive & ok.any(1))[0][0])
+        b = int(np.argmin(np.where(ok[a], C[a], np.inf)))
+        a, b = min(a, b), max(a, b)
+        log.append((rnd, a, b, float(C[a, b])))
+        S[a] = S[a] + S[b]
+        cnt[a] += cnt[b]
+        alive[b] = False
+        lab[lab == b] = a
+        live -= 1
+        rnd += 1
+    return lab, S, cnt, log
+
+
+def _sem_expand_no_window_skip(best_first, table, offsets, p, k, n_sink, n_w):
+    return _orig_sem_expand(best_first, table, offsets, p, k, n_sink, 0)
+
+
+def _sem_top_high_ties(s, p_top):
+    key = O.sem_order_key(s).astype(np.int64)
+    order = np.lexsort((-np.arange(key.shape[0]), -key))
+    return order[:p_top]
+
+
+def _sem_pool_raw(k_blk, n_pool):
+    y = np.asarray(k_blk, np.float32)
+    n = y.shape[0] // n_pool
+    return y[: n * n_pool].reshape(n, n_pool, -1).sum(1).astype(np.float32)
+
+
+_orig_sem_scores = O.sem_scores
+
+
+def _short(qn, cent):
+    # the last index dimension left out of the dot product
+    cent = np.asarray(cent, np.float32).copy()
+    cent[:, -1] = 0
+    return _orig_sem_scores(qn, cent)
+
+
+def _sem_order_raw_bits(s):
+    return np.asarray(s, np.float32).view(np.uint32).astype(np.uint64)
+
+
 MUTANTS = {
     "relu_after_sum": ("index_scores", _relu_after_sum),
     "no_relu": ("index_scores", _no_relu),
@@ -180,6 +277,15 @@ MUTANTS = {
     "paged_rows_no_offset": ("paged_rows", _paged_rows_no_offset),
     "paged_rows_ignore_table": ("paged_rows", _paged_rows_ignore_table),
     "paged_J_logical": ("forward_row_paged", _paged_J_logical),
+    "sem_cost_unweighted": ("sem_ward_costs", _sem_cost_unweighted),
+    "sem_cost_no_denominator": ("sem_ward_costs", _sem_cost_no_denominator),
+    "sem_ward_no_trim": ("sem_ward", _no_trim),
+    "sem_ward_greedy_nonmutual": ("sem_ward", _sem_ward_greedy_nonmutual),
+    "sem_expand_no_window_skip": ("sem_expand", _sem_expand_no_window_skip),
+    "sem_top_high_ties": ("sem_top_buckets", _sem_top_high_ties),
+    "sem_pool_raw_keys": ("sem_pool_keys", _sem_pool_raw),
+    "sem_scores_last_dim_dropped": ("sem_scores", _short),
+    "sem_order_raw_bits": ("sem_order_key", _sem_order_raw_bits),
 }
 
 
