@@ -237,6 +237,101 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+class SemStep:
+    """One pass of flat semantic search over the batch: lsa_semantic_select (index-query
+    normalisation, centroid scores, top-p and expansion) then lsa_sparse_attn over the
+    lists; with record=True a HIP event is recorded around each of the two calls on the
+    stream they run on.  The bucket cache is built before (a serving loop clusters each
+    block once, when it completes)."""
+
+    def __init__(self, lsa, torch, wl, inp, cache):
+        self.lsa, self.torch, self.wl, self.inp, self.cache = lsa, torch, wl, inp, cache
+        dev = inp["q_sem"].device
+        W = wl.n_sink + wl.k + wl.n_cluster
+        self.idx = torch.empty((wl.B, wl.n_q, W), dtype=torch.int32, device=dev)
+        self.count = torch.empty((wl.B, wl.n_q), dtype=torch.int32, device=dev)
+        self.ws = torch.empty((max(16, lsa.lsa_semantic_workspace_size(wl.B, wl.n_q, cache)),), dtype=torch.uint8,
+                              device=dev)
+        self.names = ["semantic_select", "sparse_attn"]
+        self.pool, self.steps = [], []
+
+    make_events = Step.make_events
+    kernel_ms = Step.kernel_ms
+
+    @property
+    def stages(self):
+        return self.names
+
+    def run(self, record: bool):
+        evs = self.pool[len(self.steps)] if record else None
+        st = self.torch.cuda.current_stream()
+        wl = self.wl
+        if record:
+            evs[0].record(st)
+        self.lsa.lsa_semantic_select(self.inp["q_sem"], self.inp["q_pos"], self.cache, wl.k, wl.p_top, wl.n_sink,
+                                     wl.n_cluster, idx=self.idx, count=self.count, ws=self.ws)
+        if record:
+            evs[1].record(st)
+        self.out, _ = self.lsa.lsa_sparse_attn(self.inp["q"], self.inp["k"], self.inp["v"], self.idx,
+                                               scale=wl.scale, return_lse=False)
+        if record:
+            evs[2].record(st)
+            self.steps.append([(n, evs[i], evs[i + 1]) for i, n in enumerate(self.names)])
+
+
+def sem_algorithmic(wl):
+    """Algorithmic work of one semantic step: centroids read (8 KB per cluster block
+    before each query's own), centroid scores, attention over the lists."""
+    pos = [wl.q_pos0 + i for i in range(wl.n_q)]
+    nbl = wl.L // wl.n_cluster
+    m = wl.n_cluster // wl.n_bavg
+    blocks = [min(p // wl.n_cluster, nbl) for p in pos]
+    lists = [min(wl.n_sink, p + 1) + (min(p, wl.n_cluster - 1) + 1) + min(wl.k, b * wl.n_cluster) for p, b in
+             zip(pos, blocks)]
+    att_pairs = wl.B * sum(lists)
+    return {
+        "centroid_bytes": wl.B * max(blocks) * m * 64 * 2 if wl.n_q == 1 else wl.B * nbl * m * 64 * 2,
+        "score_flops": wl.B * sum(blocks) * m * 64 * 2,
+        "attn_flops": 4 * wl.H_q * wl.d * att_pairs,
+        "attn_gather_bytes": att_pairs * 2 * wl.d * 2,
+    }
+
+
+def measure_sem(lsa, torch, wl, steps, warmup):
+    import synthetic
+    dev = torch.device("cuda:0")
+    inp = synthetic.make_inputs(wl, dev)
+    inp.update(synthetic.semantic_inputs(wl, dev))
+    del inp["q_idx"], inp["k_idx"]
+    prm = (wl.n_cluster, wl.n_pool, wl.n_bavg, wl.n_bmax)
+    torch.cuda.synchronize()
+    # the whole bucket cache once (every complete block of every sequence), then the
+    # launch a decode step pays every n_cluster tokens: one new block per sequence
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record()
+    cache = lsa.lsa_semantic_cache(inp["k_sem"], *prm)
+    e[1].record()
+    nb = cache["table"].shape[1]
+    lsa.lsa_semantic_cache(inp["k_sem"], cache=cache, first_block=nb - 1, n_update=1)
+    e[2].record()
+    torch.cuda.synchronize()
+    cluster = {"full_cache_ms": e[0].elapsed_time(e[1]), "blocks": wl.B * nb,
+               "one_block_per_sequence_ms": e[1].elapsed_time(e[2]),
+               "amortised_ms_per_decode_step": e[1].elapsed_time(e[2]) / wl.n_cluster}
+    step = SemStep(lsa, torch, wl, inp, cache)
+    step.make_events((steps + EVENTS_EVERY - 1) // EVENTS_EVERY)
+    for _ in range(warmup):
+        step.run(record=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step.run(record=(i % EVENTS_EVERY == 0))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
+    return inp, step, ms, cluster
+
+
 def measure(lsa, torch, wl, steps, warmup):
     import synthetic
     inp = synthetic.make_inputs(wl, torch.device("cuda:0"))
@@ -285,6 +380,14 @@ def main():
         names = list(synthetic.WORKLOADS) if args.workload == "all" else [args.workload]
         for name in names:
             wl = synthetic.WORKLOADS[name]
+            if wl.semantic:
+                inp, step, ms, cluster = measure_sem(lsa, torch, wl, args.steps, args.warmup)
+                print(json.dumps({"workload": wl.name, "ms_per_step": ms, "stage_events_every": EVENTS_EVERY,
+                                  "kernel_ms": step.kernel_ms(), "cluster": cluster,
+                                  "algorithmic": sem_algorithmic(wl)}), flush=True)
+                del inp, step
+                torch.cuda.empty_cache()
+                continue
             inp, step, ms = measure(lsa, torch, wl, args.steps, args.warmup)
             print(json.dumps({"workload": wl.name, "ms_per_step": ms, "stage_events_every": EVENTS_EVERY,
                               "kernel_ms": step.kernel_ms(),

@@ -319,6 +319,77 @@ enum {
 lsa_status lsa_forward_stages(const lsa_forward_args* a, size_t ws_bytes, int32_t* codes, int32_t max_codes,
                               int32_t* n_stages);
 
+/* ---------------------------------------------------------------------------------
+ * Flat semantic search ([LSA] §3.1 "Semantic Clustering", §3.2 "Semantic Search",
+ * App. F.1 "Kernels").  Index keys and queries are bf16 vectors of d_idx = 64.
+ *
+ * Cluster blocks are runs of n_cluster consecutive keys.  A complete block's keys are
+ * L2 normalised and summed n_pool at a time into pool keys; the pool keys are merged
+ * bottom up by Ward's criterion (every round, all pairs of buckets that are each
+ * other's cheapest allowed merge merge at once; a merge is allowed while the bucket
+ * holds at most n_bmax keys) until m = n_cluster / n_bavg buckets remain.  A bucket's
+ * centroid is its normalised key sum, in bf16.  A query (normalised, bf16) scores the
+ * centroids of every block before its own, keeps the top p_top buckets (higher score
+ * first, then lower bucket id) and expands them, best first, into k long-range keys,
+ * skipping keys of the sink (j < n_sink) and of the window (j > p - n_w); its list is
+ * the sink, those keys and the window.
+ *
+ * Every floating-point step that decides which buckets merge or are kept runs in fp32
+ * with each operation rounded on its own and sums over the dimensions taken in order,
+ * so results are deterministic and reproducible on any machine that rounds the same
+ * way (the CPU oracle does).
+ */
+typedef struct lsa_semantic_params {
+  int32_t n_cluster; /* keys per cluster block */
+  int32_t n_pool;    /* keys summed into one pool key; divides n_cluster and n_bmax */
+  int32_t n_bavg;    /* average keys per bucket; divides n_cluster (m = n_cluster / n_bavg) */
+  int32_t n_bmax;    /* largest bucket, in keys; at least 2 * n_bavg (so exactly m buckets form) */
+} lsa_semantic_params;
+
+/*
+ * Bucket cache of blocks [first_block, first_block + n_update) of every sequence
+ * ([LSA] §3.1 "Clustering", "Bucket cache"); the other blocks are left alone, so a
+ * serving loop clusters each block once, when it completes.  k_idx: bf16
+ * [B, L_max, 64]; (first_block + n_update) * n_cluster <= L_max; n_blocks: the
+ * blocks the cache holds per sequence.  Layout (device memory, caller-owned):
+ *   centroids bf16 [B, n_blocks, 8, 64, 8]: dims 8c..8c+7 of bucket s of a block at
+ *     [c][s][0..7]; buckets of a block in order of the lowest pool key each holds
+ *     (slots m..63 zero);
+ *   table int32 [B, n_blocks, n_cluster]: the block's key positions (absolute within
+ *     the sequence), bucket after bucket, ascending within a bucket;
+ *   offsets int32 [B, n_blocks, m + 1]: bucket starts in table (offsets[m] = n_cluster).
+ * Supported: d_idx = 64; n_cluster / n_pool <= 128 pool keys; m <= 64.  No workspace.
+ */
+lsa_status lsa_semantic_cluster(const void* k_idx, int32_t B, int32_t L_max, int32_t d_idx,
+                                const lsa_semantic_params* prm, int32_t n_blocks, int32_t first_block,
+                                int32_t n_update, void* centroids, int32_t* table, int32_t* offsets,
+                                void* stream);
+
+/* Workspace lsa_semantic_select needs to take all B * n_q queries in one pass: per
+   query its normalised index query and one score-table row of n_blocks * m floats.
+   Less (at least one query per sequence) is accepted: the call then runs in chunks of
+   queries. */
+lsa_status lsa_semantic_select_workspace_size(int32_t B, int32_t n_q, int32_t n_blocks,
+                                              const lsa_semantic_params* prm, size_t* bytes);
+
+/*
+ * Index lists of flat semantic search ([LSA] §3.2 "Scoring", "Expansion"): q_idx bf16
+ * [B, n_q, 64]; q_pos int32 [B, n_q] (-1: padding query, empty list).  A query at p
+ * scores the buckets of blocks 0 .. min(p / n_cluster, n_blocks) - 1 of the cache of
+ * lsa_semantic_cluster (those blocks must be clustered), takes the top p_top and
+ * expands them into at most k long-range keys.  idx int32 [B, n_q, n_sink + k + n_w]
+ * receives the sink keys (j < min(n_sink, p + 1)), the long-range keys and the window
+ * (max(0, p - n_w + 1) .. p), ascending and -1 padded; count int32 [B, n_q] their
+ * number.  The list is that of the oracle bit for bit.  Attention over it:
+ * lsa_sparse_attn with k_top = n_sink + k + n_w.
+ * Supported: d_idx = 64; 1 <= k <= 4096; 1 <= p_top <= 2048.  ws 16-byte aligned.
+ */
+lsa_status lsa_semantic_select(const void* q_idx, const int32_t* q_pos, int32_t B, int32_t n_q, int32_t d_idx,
+                               const lsa_semantic_params* prm, int32_t n_blocks, const void* centroids,
+                               const int32_t* table, const int32_t* offsets, int32_t k, int32_t p_top,
+                               int32_t n_sink, int32_t n_w, int32_t* idx, int32_t* count, void* ws,
+                               size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

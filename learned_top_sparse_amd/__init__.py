@@ -18,6 +18,11 @@ from .binding import (  # noqa: F401
     lsa_forward_stages,
     lsa_forward_workspace_size,
     lsa_index_scores,
+    lsa_semantic_cache,
+    lsa_semantic_forward,
+    lsa_semantic_select,
+    lsa_semantic_workspace_size,
+    SemanticParams,
     lsa_sparse_attn,
     lsa_status_string,
     lsa_topk,

@@ -21,6 +21,7 @@ EXPORTED = [
     "lsa_block_prefilter_workspace_size", "lsa_block_prefilter", "lsa_topk_workspace_size",
     "lsa_topk", "lsa_sparse_attn_workspace_size", "lsa_sparse_attn",
     "lsa_forward_workspace_size", "lsa_forward", "lsa_forward_plan", "lsa_forward_stages",
+    "lsa_semantic_cluster", "lsa_semantic_select_workspace_size", "lsa_semantic_select",
 ]
 
 STAGE_NAMES = {1: "block_reps", 2: "block_prefilter", 3: "index_select", 4: "index_scores", 5: "topk", 7: "sample",
@@ -84,6 +85,10 @@ def lib():
         L.lsa_forward.argtypes = [C.POINTER(ForwardArgs), P, SZ, P]
         L.lsa_forward_plan.argtypes = [C.POINTER(ForwardArgs), SZ, C.POINTER(I64), C.POINTER(I32)]
         L.lsa_forward_stages.argtypes = [C.POINTER(ForwardArgs), SZ, C.POINTER(I32), I32, C.POINTER(I32)]
+        SP = C.POINTER(SemanticParams)
+        L.lsa_semantic_cluster.argtypes = [P, I32, I32, I32, SP, I32, I32, I32, P, P, P, P]
+        L.lsa_semantic_select_workspace_size.argtypes = [I32, I32, I32, SP, C.POINTER(SZ)]
+        L.lsa_semantic_select.argtypes = [P, P, I32, I32, I32, SP, I32, P, P, P, I32, I32, I32, I32, P, P, P, SZ, P]
         for name in EXPORTED:
             if name not in ("lsa_status_string", "lsa_version"):
                 getattr(L, name).restype = C.c_int
@@ -394,3 +399,91 @@ def lsa_forward(inp: dict, k_top: int, two_stage=False, block_size: int = 128, n
     st = lib().lsa_forward(C.byref(a), _ptr(ws), nbytes, _stream(dev))
     _check("lsa_forward", st)
     return out
+
+
+# --------------------------------------------------------------------------- flat semantic search
+class SemanticParams(C.Structure):
+    """lsa_semantic_params of include/lsa.h."""
+    _fields_ = [("n_cluster", I32), ("n_pool", I32), ("n_bavg", I32), ("n_bmax", I32)]
+
+
+def lsa_semantic_cache(k_idx, n_cluster: int = 512, n_pool: int = 4, n_bavg: int = 8, n_bmax: int = 32,
+                       n_blocks: Optional[int] = None, cache: Optional[dict] = None, first_block: int = 0,
+                       n_update: Optional[int] = None) -> dict:
+    """Bucket cache of the complete cluster blocks of k_idx (bf16 [B, L_max, 64]) through
+    lsa_semantic_cluster.  With ``cache`` given, only blocks [first_block, first_block +
+    n_update) are (re)clustered into it.  Returns dict(centroids bf16 [B, NB, 8, 64, 8],
+    table int32 [B, NB, n_cluster], offsets int32 [B, NB, m + 1], params)."""
+    _need(k_idx, "k_idx", torch.bfloat16)
+    dev = k_idx.device
+    B, L, d = k_idx.shape
+    prm = SemanticParams(n_cluster, n_pool, n_bavg, n_bmax)
+    if cache is None:
+        NB = L // n_cluster if n_blocks is None else n_blocks
+        m = n_cluster // n_bavg
+        cache = {"centroids": torch.zeros((B, NB, 8, 64, 8), dtype=torch.bfloat16, device=dev),
+                 "table": torch.empty((B, NB, n_cluster), dtype=torch.int32, device=dev),
+                 "offsets": torch.empty((B, NB, m + 1), dtype=torch.int32, device=dev),
+                 "params": (n_cluster, n_pool, n_bavg, n_bmax)}
+    else:
+        prm = SemanticParams(*cache["params"])
+    NB = cache["table"].shape[1]
+    if n_update is None:
+        n_update = min(NB, L // prm.n_cluster) - first_block
+    _check("lsa_semantic_cluster",
+           lib().lsa_semantic_cluster(_ptr(k_idx), B, L, d, C.byref(prm), NB, first_block, n_update,
+                                      _ptr(cache["centroids"]), _ptr(cache["table"]), _ptr(cache["offsets"]),
+                                      _stream(dev)))
+    return cache
+
+
+def lsa_semantic_select(q_idx, q_pos, cache: dict, k: int, p_top: int, n_sink: int, n_w: int,
+                        idx=None, count=None, ws_bytes: Optional[int] = None, ws: Optional[torch.Tensor] = None):
+    """Index lists of flat semantic search: (idx int32 [B, n_q, n_sink + k + n_w], count
+    int32 [B, n_q]).  q_idx bf16 [B, n_q, 64]; q_pos int32 [B, n_q]."""
+    _need(q_idx, "q_idx", torch.bfloat16)
+    dev = q_idx.device
+    _need(q_pos, "q_pos", torch.int32, dev)
+    B, n_q, d = q_idx.shape
+    prm = SemanticParams(*cache["params"])
+    NB = cache["table"].shape[1]
+    W = n_sink + k + n_w
+    if idx is None:
+        idx = torch.empty((B, n_q, W), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((B, n_q), dtype=torch.int32, device=dev)
+    if ws is not None:
+        _need(ws, "ws", torch.uint8, dev)
+        ws_bytes = ws.numel()
+    else:
+        if ws_bytes is None:
+            nb = SZ(0)
+            _check("lsa_semantic_select_workspace_size",
+                   lib().lsa_semantic_select_workspace_size(B, n_q, NB, C.byref(prm), C.byref(nb)))
+            ws_bytes = nb.value
+        ws = _workspace(ws_bytes, dev)
+    _check("lsa_semantic_select",
+           lib().lsa_semantic_select(_ptr(q_idx), _ptr(q_pos), B, n_q, d, C.byref(prm), NB,
+                                     _ptr(cache["centroids"]), _ptr(cache["table"]), _ptr(cache["offsets"]),
+                                     k, p_top, n_sink, n_w, _ptr(idx), _ptr(count), _ptr(ws), ws_bytes,
+                                     _stream(dev)))
+    return idx, count
+
+
+def lsa_semantic_workspace_size(B: int, n_q: int, cache: dict) -> int:
+    """lsa_semantic_select_workspace_size for a cache of lsa_semantic_cache."""
+    nb = SZ(0)
+    prm = SemanticParams(*cache["params"])
+    _check("lsa_semantic_select_workspace_size",
+           lib().lsa_semantic_select_workspace_size(B, n_q, cache["table"].shape[1], C.byref(prm), C.byref(nb)))
+    return nb.value
+
+
+def lsa_semantic_forward(inp: dict, cache: dict, k: int, p_top: int, n_sink: int, n_w: int,
+                         scale: Optional[float] = None, attn_split: int = 0) -> dict:
+    """Flat semantic search then sparse attention over its lists: lsa_semantic_select
+    and lsa_sparse_attn.  inp: q_sem bf16 [B, n_q, 64], q_pos, q / k / v as for
+    lsa_sparse_attn.  Returns dict(idx, count, out, lse)."""
+    idx, count = lsa_semantic_select(inp["q_sem"], inp["q_pos"], cache, k, p_top, n_sink, n_w)
+    out, lse = lsa_sparse_attn(inp["q"], inp["k"], inp["v"], idx, scale=scale, n_split=attn_split)
+    return {"idx": idx, "count": count, "out": out, "lse": lse}

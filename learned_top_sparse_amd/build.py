@@ -18,7 +18,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblsa.so")
-SOURCES = ["lsa_indexer.hip", "lsa_topk.hip", "lsa_attn.hip", "lsa_api.cpp"]
+SOURCES = ["lsa_indexer.hip", "lsa_topk.hip", "lsa_attn.hip", "lsa_semantic.hip", "lsa_api.cpp"]
+# sources whose arithmetic decides integers (merges, kept buckets): no fused multiply-add
+# unless written out, so every value is rounded in the order the source gives
+NO_CONTRACT = {"lsa_semantic.hip"}
 
 ARCH = "gfx950"
 COMMON = [
@@ -37,6 +40,8 @@ def hipcc() -> str:
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON
+    if src in NO_CONTRACT:
+        cmd.append("-ffp-contract=off")
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -775,3 +775,89 @@ LSA_API lsa_status lsa_forward_plan(const lsa_forward_args* a, size_t ws_bytes, 
   *attn_split = resolve_split(1, (int32_t)rows, a->k_top, a->attn_split);
   return LSA_OK;
 }
+
+
+// ---------------------------------------------------------------------------------
+// flat semantic search
+
+static lsa_status check_sem_params(const lsa_semantic_params* prm, int d_idx, lsa::SemParams* sp) {
+  if (!prm) return LSA_ERR_INVALID_ARG;
+  const lsa_semantic_params& p = *prm;
+  if (p.n_cluster < 1 || p.n_pool < 1 || p.n_bavg < 1 || p.n_bmax < 1 || p.n_cluster % p.n_pool != 0 ||
+      p.n_cluster % p.n_bavg != 0 || p.n_bmax % p.n_pool != 0 || p.n_bmax < 2 * p.n_bavg ||
+      p.n_bavg < p.n_pool)
+    return LSA_ERR_INVALID_ARG;
+  if (d_idx != 64) return LSA_ERR_UNSUPPORTED;
+  if (p.n_cluster / p.n_pool > lsa::SEM_MAX_POOL_KEYS || p.n_cluster / p.n_bavg > lsa::SEM_MAX_BUCKETS)
+    return LSA_ERR_UNSUPPORTED;
+  sp->n_cluster = p.n_cluster;
+  sp->n_pool = p.n_pool;
+  sp->n_bavg = p.n_bavg;
+  sp->n_bmax = p.n_bmax;
+  return LSA_OK;
+}
+
+LSA_API lsa_status lsa_semantic_cluster(const void* k_idx, int32_t B, int32_t L_max, int32_t d_idx,
+                                        const lsa_semantic_params* prm, int32_t n_blocks, int32_t first_block,
+                                        int32_t n_update, void* centroids, int32_t* table, int32_t* offsets,
+                                        void* stream) {
+  lsa::SemParams sp;
+  if (B < 0 || L_max < 1 || n_blocks < 0 || first_block < 0 || n_update < 0) return LSA_ERR_INVALID_ARG;
+  lsa_status st = check_sem_params(prm, d_idx, &sp);
+  if (st != LSA_OK) return st;
+  if ((long long)first_block + n_update > n_blocks ||
+      ((long long)first_block + n_update) * sp.n_cluster > L_max)
+    return LSA_ERR_INVALID_ARG;
+  if ((long long)B * n_update == 0) return LSA_OK;
+  if (!k_idx || !centroids || !table || !offsets) return LSA_ERR_INVALID_ARG;
+  return hip_status(lsa::launch_sem_cluster(k_idx, B, L_max, sp, n_blocks, first_block, n_update, centroids, table,
+                                            offsets, as_stream(stream)));
+}
+
+LSA_API lsa_status lsa_semantic_select_workspace_size(int32_t B, int32_t n_q, int32_t n_blocks,
+                                                      const lsa_semantic_params* prm, size_t* bytes) {
+  lsa::SemParams sp;
+  if (!bytes || B < 0 || n_q < 0 || n_blocks < 0) return LSA_ERR_INVALID_ARG;
+  lsa_status st = check_sem_params(prm, 64, &sp);
+  if (st != LSA_OK) return st;
+  *bytes = (size_t)B * n_q * lsa::sem_select_row_bytes(n_blocks, sp.n_cluster / sp.n_bavg);
+  return LSA_OK;
+}
+
+LSA_API lsa_status lsa_semantic_select(const void* q_idx, const int32_t* q_pos, int32_t B, int32_t n_q, int32_t d_idx,
+                                       const lsa_semantic_params* prm, int32_t n_blocks, const void* centroids,
+                                       const int32_t* table, const int32_t* offsets, int32_t k, int32_t p_top,
+                                       int32_t n_sink, int32_t n_w, int32_t* idx, int32_t* count, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  lsa::SemParams sp;
+  if (B < 0 || n_q < 0 || n_blocks < 0 || k < 1 || p_top < 1 || n_sink < 0 || n_w < 0) return LSA_ERR_INVALID_ARG;
+  lsa_status st = check_sem_params(prm, d_idx, &sp);
+  if (st != LSA_OK) return st;
+  if (k > lsa::SEM_MAX_K || p_top > lsa::SEM_MAX_P) return LSA_ERR_UNSUPPORTED;
+  if ((long long)n_sink + k + n_w > (1LL << 30)) return LSA_ERR_INVALID_ARG;
+  if ((long long)B * n_q == 0) return LSA_OK;
+  if (!q_idx || !q_pos || !idx || !count || (n_blocks > 0 && (!centroids || !table || !offsets)))
+    return LSA_ERR_INVALID_ARG;
+  if (((uintptr_t)ws) % 16 != 0) return LSA_ERR_WORKSPACE;
+  const size_t row = lsa::sem_select_row_bytes(n_blocks, sp.n_cluster / sp.n_bavg);
+  if (!ws || ws_bytes < (size_t)B * row) return LSA_ERR_WORKSPACE;
+  lsa::SemSelectArgs a;
+  a.q_idx = q_idx;
+  a.q_pos = q_pos;
+  a.B = B;
+  a.n_q = n_q;
+  a.sp = sp;
+  a.NB = n_blocks;
+  a.cent = centroids;
+  a.table = table;
+  a.offs = offsets;
+  a.k = k;
+  a.p_top = p_top;
+  a.n_sink = n_sink;
+  a.n_w = n_w;
+  a.idx = idx;
+  a.count = count;
+  a.ws = ws;
+  a.ws_bytes = ws_bytes;
+  return hip_status(lsa::launch_sem_select(a, as_stream(stream)));
+}

@@ -187,4 +187,32 @@ hipError_t launch_thresholds(const int32_t* samp, long long ld_s, const int32_t*
 hipError_t launch_list_topk(const int32_t* q_pos, long long rows, int L_max, int k, const ThrArgs& t,
                             int32_t* idx, int32_t* count, int n_q, const Pages& pg, hipStream_t st);
 
+// ---- flat semantic search (Ward bucket cache, centroid scoring, top-p, expansion)
+struct SemParams {
+  int n_cluster, n_pool, n_bavg, n_bmax;
+};
+struct SemSelectArgs {
+  const void* q_idx;       // bf16 [B, n_q, 64]
+  const int32_t* q_pos;    // [B, n_q]
+  int B, n_q;
+  SemParams sp;
+  int NB;                  // cluster blocks the cache holds per sequence
+  const void* cent;
+  const int32_t* table;
+  const int32_t* offs;
+  int k, p_top, n_sink, n_w;
+  int32_t* idx;            // [B, n_q, n_sink + k + n_w]
+  int32_t* count;          // [B, n_q]
+  void* ws;
+  size_t ws_bytes;
+};
+constexpr int SEM_MAX_POOL_KEYS = 128;  // pool keys of a cluster block
+constexpr int SEM_MAX_BUCKETS = 64;     // buckets of a cluster block
+constexpr int SEM_MAX_P = 2048;
+constexpr int SEM_MAX_K = 4096;
+hipError_t launch_sem_cluster(const void* k_idx, int B, int L_max, const SemParams& sp, int NB, int first_block,
+                              int n_update, void* cent, int32_t* table, int32_t* offs, hipStream_t st);
+size_t sem_select_row_bytes(int NB, int m);
+hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st);
+
 }  // namespace lsa

@@ -1,0 +1,596 @@
+// lsa_semantic.hip -- flat semantic search: Ward clustering of cluster blocks into a
+// bucket cache, centroid scoring, exact top-p of the buckets and their expansion into
+// the index lists ("Latent Sparse Attention (LSA)" §3.1 "Semantic Clustering", §3.2
+// "Semantic Search", App. F.1 "Kernels").
+//
+// Floating point takes integer decisions here (which buckets merge, which are kept),
+// so this file is compiled with -ffp-contract=off: every sum and product is rounded on
+// its own, in the order written, and sums over the 64 index dimensions run d = 0, 1,
+// ...  The one fused multiply-add is explicit and adds exact products (bf16 x bf16 is
+// exact in fp32), so it rounds like the separate add.  Division and square root are
+// the correctly rounded ones.
+//
+// Bucket cache of sequence b, cluster block t (m <= 64 buckets per block, listed by the
+// lowest pool key each holds):
+//   centroids bf16 [B][NB][8][64][8]: dims 8c..8c+7 of bucket slot s at [c][s][0..7]
+//     (slots m..63 zero), so a wave reads one dim group of all 64 slots as 1 KB;
+//   table int32 [B][NB][n_cluster]: key positions, bucket after bucket, ascending
+//     within a bucket;
+//   offsets int32 [B][NB][m + 1]: bucket starts in the table (offsets[m] = n_cluster).
+#include <hip/hip_runtime.h>
+
+#include "lsa_device.h"
+#include "lsa_internal.h"
+
+namespace lsa {
+namespace {
+
+constexpr int SEM_D = 64;        // index dimension
+constexpr int SEM_NPK = 128;     // pool keys per cluster block, at most
+constexpr int SEM_SLOTS = 64;    // bucket slots per block in the centroid layout
+constexpr int SEL_NT = 512;      // threads of the selection workgroup
+
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, nearest with ties to even (finite inputs)
+__device__ __forceinline__ unsigned to_bf16(float x) {
+  const unsigned u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// order-keeping unsigned image of an fp32 score (-0 just below +0)
+__device__ __forceinline__ unsigned order_key(float s) {
+  const unsigned u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ void unpack8(uint4 v, float* x) {
+  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+
+// ---------------------------------------------------------------------------------
+// Clustering: one 256-thread workgroup per (cluster block, sequence).  The block's
+// pool keys (sums of its normalised keys), the bucket sums and the Ward cost of every
+// pair stay in LDS for all merge rounds; only the rows of merged buckets are
+// recomputed after a round.
+
+struct SemGeom {
+  int n_cluster, n_pool, npk, m, cap;  // cap: size cap in pool keys
+};
+
+// Ward's cost of buckets a, b: |n_b S_a - n_a S_b|^2 / (n_a n_b (n_a + n_b))
+__device__ __forceinline__ float ward_cost(const float (*S)[SEM_D + 1], const int* cnt, int a, int b) {
+  const float na = (float)cnt[a], nb = (float)cnt[b];
+  float sq = 0.f;
+#pragma unroll 16
+  for (int d = 0; d < SEM_D; ++d) {
+    const float df = nb * S[a][d] - na * S[b][d];
+    sq = sq + df * df;
+  }
+  return sq / (na * nb * (na + nb));
+}
+
+__global__ __launch_bounds__(256) void sem_cluster_kernel(const unsigned short* __restrict__ kidx, long long seq_elems,
+                                                          SemGeom g, int first_block, int NB,
+                                                          unsigned short* __restrict__ cent, int* __restrict__ table,
+                                                          int* __restrict__ offs) {
+  __shared__ float S[SEM_NPK][SEM_D + 1];
+  __shared__ float C[SEM_NPK][SEM_NPK + 1];
+  __shared__ int cnt[SEM_NPK], lab[SEM_NPK], partner[SEM_NPK], into[SEM_NPK], off_of[SEM_NPK];
+  __shared__ float pcost[SEM_NPK];
+  __shared__ int pa[SEM_NPK / 2], pb[SEM_NPK / 2], keep[SEM_NPK / 2];
+  __shared__ float pc[SEM_NPK / 2];
+  __shared__ int id_of_rank[SEM_SLOTS];
+  __shared__ int sh_np;
+
+  const int t = threadIdx.x;
+  const int blk = first_block + blockIdx.x;
+  const int b = blockIdx.y;
+  const int npk = g.npk;
+  const unsigned short* kb = kidx + (long long)b * seq_elems + (long long)blk * g.n_cluster * SEM_D;
+
+  // 1. pool keys: the block's keys normalised and summed n_pool at a time, in key order
+  if (t < npk) {
+    float P[SEM_D];
+    for (int i = 0; i < g.n_pool; ++i) {
+      const uint4* row = reinterpret_cast<const uint4*>(kb + (long long)(t * g.n_pool + i) * SEM_D);
+      float x[SEM_D];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) unpack8(row[c], x + 8 * c);
+      float ss = 0.f;
+#pragma unroll
+      for (int d = 0; d < SEM_D; ++d) ss = ss + x[d] * x[d];
+      const float nrm = sqrtf(ss);
+#pragma unroll
+      for (int d = 0; d < SEM_D; ++d) {
+        const float y = nrm > 0.f ? x[d] / nrm : 0.f;
+        P[d] = i == 0 ? y : P[d] + y;
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < SEM_D; ++d) S[t][d] = P[d];
+  }
+  if (t < SEM_NPK) {
+    cnt[t] = t < npk ? 1 : 0;
+    lab[t] = t;
+  }
+  __syncthreads();
+
+  // 2. cost of every ordered pair (both triangles; the formula is symmetric bit for bit)
+  {
+    const int a = t & (SEM_NPK - 1);
+    if (a < npk)
+      for (int bb = t >> 7; bb < npk; bb += 2)
+        if (bb != a) C[a][bb] = ward_cost(S, cnt, a, bb);
+  }
+  __syncthreads();
+
+  // 3. merge rounds
+  int live = npk;
+  while (live > g.m) {
+    if (t < npk) {
+      int bi = -1;
+      float best = 0.f;
+      const int ca = cnt[t];
+      if (ca > 0)
+        for (int bb = 0; bb < npk; ++bb) {
+          const int cb = cnt[bb];
+          if (bb == t || cb == 0 || ca + cb > g.cap) continue;
+          const float c = C[t][bb];
+          if (bi < 0 || c < best) {
+            best = c;
+            bi = bb;
+          }
+        }
+      partner[t] = bi;
+      pcost[t] = best;
+      into[t] = -1;
+    }
+    if (t == 0) sh_np = 0;
+    __syncthreads();
+    if (t < npk) {
+      const int bb = partner[t];
+      if (bb > t && partner[bb] == t) {
+        const int s = atomicAdd(&sh_np, 1);
+        pa[s] = t;
+        pb[s] = bb;
+        pc[s] = pcost[t];
+      }
+    }
+    __syncthreads();
+    const int np = sh_np;
+    if (np == 0) break;
+    const int need = live - g.m;
+    // all mutual pairs merge, unless that would leave fewer than m buckets: then the
+    // cheapest `need` (cost, then lower id)
+    if (t < np) {
+      int rk = 0;
+      if (np > need)
+        for (int j = 0; j < np; ++j) rk += (pc[j] < pc[t]) || (pc[j] == pc[t] && pa[j] < pa[t]);
+      keep[t] = rk < need;
+    }
+    __syncthreads();
+    for (int x = t; x < np * SEM_D; x += 256) {
+      const int s = x >> 6, d = x & (SEM_D - 1);
+      if (keep[s]) S[pa[s]][d] = S[pa[s]][d] + S[pb[s]][d];
+    }
+    if (t < np && keep[t]) {
+      into[pb[t]] = pa[t];
+      cnt[pa[t]] = cnt[pa[t]] + cnt[pb[t]];
+      cnt[pb[t]] = 0;
+    }
+    __syncthreads();
+    if (t < npk) {
+      const int l = into[lab[t]];
+      if (l >= 0) lab[t] = l;
+    }
+    live -= np < need ? np : need;
+    // costs of the merged buckets against every live bucket
+    for (int x = t; x < np * npk; x += 256) {
+      const int s = x / npk, j = x - s * npk;
+      const int a = pa[s];
+      if (keep[s] && cnt[j] > 0 && j != a) {
+        const float c = ward_cost(S, cnt, a, j);
+        C[a][j] = c;
+        C[j][a] = c;
+      }
+    }
+    __syncthreads();
+  }
+
+  // 4. the cache entry: buckets in id order, their keys ascending
+  if (t < npk && cnt[t] > 0) {
+    int r = 0, o = 0;
+    for (int j = 0; j < t; ++j)
+      if (cnt[j] > 0) {
+        ++r;
+        o += cnt[j];
+      }
+    off_of[t] = o * g.n_pool;
+    if (r < SEM_SLOTS) id_of_rank[r] = t;
+  }
+  __syncthreads();
+  const long long cb = (long long)b * NB + blk;
+  if (t < npk) {
+    const int a = lab[t];
+    int pos = 0;
+    for (int j = 0; j < t; ++j) pos += lab[j] == a;
+    int* tb = table + cb * g.n_cluster + off_of[a] + pos * g.n_pool;
+    for (int i = 0; i < g.n_pool; ++i) tb[i] = blk * g.n_cluster + t * g.n_pool + i;
+  }
+  int* ob = offs + cb * (g.m + 1);
+  if (t < g.m) ob[t] = off_of[id_of_rank[t]];
+  if (t == 0) ob[g.m] = g.n_cluster;
+  if (t < SEM_SLOTS) {
+    float v[SEM_D];
+    if (t < g.m) {
+      const int a = id_of_rank[t];
+      float ss = 0.f;
+#pragma unroll
+      for (int d = 0; d < SEM_D; ++d) ss = ss + S[a][d] * S[a][d];
+      const float nrm = sqrtf(ss);
+#pragma unroll
+      for (int d = 0; d < SEM_D; ++d) v[d] = nrm > 0.f ? S[a][d] / nrm : 0.f;
+    } else {
+#pragma unroll
+      for (int d = 0; d < SEM_D; ++d) v[d] = 0.f;
+    }
+    uint4* cp = reinterpret_cast<uint4*>(cent + cb * (SEM_D * SEM_SLOTS));
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      uint4 w;
+      w.x = to_bf16(v[8 * c + 0]) | (to_bf16(v[8 * c + 1]) << 16);
+      w.y = to_bf16(v[8 * c + 2]) | (to_bf16(v[8 * c + 3]) << 16);
+      w.z = to_bf16(v[8 * c + 4]) | (to_bf16(v[8 * c + 5]) << 16);
+      w.w = to_bf16(v[8 * c + 6]) | (to_bf16(v[8 * c + 7]) << 16);
+      cp[c * SEM_SLOTS + t] = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Index queries: normalised in fp32, rounded to bf16, kept as fp32 values.
+
+__global__ __launch_bounds__(256) void sem_qnorm_kernel(const unsigned short* __restrict__ q, int n_q, int i0, int nqc,
+                                                        int rows, float* __restrict__ qn) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  const int b = r / nqc, i = r - b * nqc;
+  const uint4* row = reinterpret_cast<const uint4*>(q + ((long long)b * n_q + i0 + i) * SEM_D);
+  float x[SEM_D];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) unpack8(row[c], x + 8 * c);
+  float ss = 0.f;
+#pragma unroll
+  for (int d = 0; d < SEM_D; ++d) ss = ss + x[d] * x[d];
+  const float nrm = sqrtf(ss);
+  float4* out = reinterpret_cast<float4*>(qn + (long long)r * SEM_D);
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = nrm > 0.f ? x[4 * c + e] / nrm : 0.f;
+      y[e] = __uint_as_float(to_bf16(v) << 16);
+    }
+    out[c] = make_float4(y[0], y[1], y[2], y[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Scores s_b = c_b . q: one wave per (cluster block, query tile), a lane per bucket
+// slot; the lane holds its centroid in registers and takes the tile's queries one by
+// one (wave-uniform).  Every score of the blocks before a query's own is written to
+// that query's row of the score table; the next block's centroids are loaded while
+// the current one is scored.
+
+template <int QT>
+__global__ __launch_bounds__(256) void sem_score_kernel(const float* __restrict__ qn, const int* __restrict__ q_pos,
+                                                        int n_q, int i0, int nqc,
+                                                        const unsigned short* __restrict__ cent, int NB, int m,
+                                                        int n_cluster, int bpw, float* __restrict__ S, long long ld) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b = blockIdx.z;
+  const int q0 = blockIdx.y * QT;
+  const int blk0 = (blockIdx.x * 4 + w) * bpw;
+  if (blk0 >= NB) return;
+  // the tile's furthest own block bounds the blocks worth loading
+  int own_max = 0;
+  for (int qi = 0; qi < QT && q0 + qi < nqc; ++qi) {
+    const int p = q_pos[(long long)b * n_q + i0 + q0 + qi];
+    const int o = p < 0 ? 0 : p / n_cluster;
+    own_max = o > own_max ? o : own_max;
+  }
+  int blk_end = blk0 + bpw;
+  blk_end = blk_end < NB ? blk_end : NB;
+  blk_end = blk_end < own_max ? blk_end : own_max;
+  if (blk0 >= blk_end) return;
+
+  const uint4* cb = reinterpret_cast<const uint4*>(cent + ((long long)b * NB) * (SEM_D * SEM_SLOTS));
+  uint4 nxt[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) nxt[c] = cb[(long long)blk0 * (SEM_D * SEM_SLOTS / 8) + c * SEM_SLOTS + lane];
+  for (int blk = blk0; blk < blk_end; ++blk) {
+    float cv[SEM_D];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) unpack8(nxt[c], cv + 8 * c);
+    if (blk + 1 < blk_end) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) nxt[c] = cb[(long long)(blk + 1) * (SEM_D * SEM_SLOTS / 8) + c * SEM_SLOTS + lane];
+    }
+    for (int qi = 0; qi < QT; ++qi) {
+      const int i = q0 + qi;
+      if (i >= nqc) break;
+      const int p = q_pos[(long long)b * n_q + i0 + i];
+      if (p < 0 || blk >= p / n_cluster) continue;
+      const float* q = qn + ((long long)b * nqc + i) * SEM_D;
+      float acc = 0.f;
+#pragma unroll
+      for (int d = 0; d < SEM_D; ++d) acc = fmaf(q[d], cv[d], acc);
+      if (lane < m) S[((long long)b * nqc + i) * ld + (long long)blk * m + lane] = acc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Selection and expansion: one workgroup per query.  The top-p buckets by packed key
+// (order key of the score above, inverted bucket id below) come from a radix select
+// over the score row (four 8-bit digits) and one ordered pass that takes every bucket
+// above the cut and the lowest-id ones at it.  They are sorted best first, their keys
+// outside the sink and the window counted, and the long-range keys written up to k
+// (the bucket at the cut in part); the list is sink, long-range keys ascending, window.
+
+constexpr int SEM_PMAX = 2048;
+constexpr int SEM_KMAX = 4096;
+
+__global__ __launch_bounds__(SEL_NT) void sem_select_kernel(const float* __restrict__ S, long long ld,
+                                                            const int* __restrict__ q_pos, int n_q, int i0, int nqc,
+                                                            const int* __restrict__ table, const int* __restrict__ offs,
+                                                            int NB, int m, int n_cluster, int k, int p_top, int n_sink,
+                                                            int n_w, int W, int* __restrict__ idx,
+                                                            int* __restrict__ count) {
+  __shared__ unsigned long long K[SEM_PMAX];
+  __shared__ int avail[SEM_PMAX];
+  __shared__ int excl[SEM_PMAX];
+  __shared__ int LR[SEM_KMAX];
+  __shared__ int hist[256];
+  __shared__ int scan_tmp[SEL_NT / 64];
+  __shared__ int sh[4];
+
+  const int t = threadIdx.x;
+  const int i = blockIdx.x, b = blockIdx.y;
+  const long long qrow = (long long)b * n_q + i0 + i;
+  const int p = q_pos[qrow];
+  int* out = idx + qrow * W;
+  if (p < 0) {
+    for (int j = t; j < W; j += SEL_NT) out[j] = -1;
+    if (t == 0) count[qrow] = 0;
+    return;
+  }
+  int nb = p / n_cluster;
+  nb = nb < NB ? nb : NB;
+  const int N = nb * m;
+  const float* row = S + ((long long)b * nqc + i) * ld;
+  const int w0 = p - n_w + 1 > 0 ? p - n_w + 1 : 0;
+
+  int nk;
+  if (N <= p_top) {
+    for (int j = t; j < N; j += SEL_NT)
+      K[j] = ((unsigned long long)order_key(row[j]) << 32) | (0xFFFFFFFFu - (unsigned)j);
+    nk = N;
+  } else {
+    unsigned prefix = 0;
+    int need = p_top;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int j = t; j < 256; j += SEL_NT) hist[j] = 0;
+      __syncthreads();
+      const unsigned hi_mask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+      for (int j = t; j < N; j += SEL_NT) {
+        const unsigned u = order_key(row[j]);
+        if ((u & hi_mask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
+      }
+      __syncthreads();
+      if (t == 0) {
+        int acc = 0, dg = 255;
+        for (; dg > 0; --dg) {
+          if (acc + hist[dg] >= need) break;
+          acc += hist[dg];
+        }
+        sh[0] = dg;
+        sh[1] = need - acc;
+      }
+      __syncthreads();
+      prefix |= (unsigned)sh[0] << shift;
+      need = sh[1];
+      __syncthreads();
+    }
+    // every key above `prefix`, and the `need` lowest-id keys equal to it
+    if (t == 0) {
+      sh[2] = 0;
+      sh[3] = 0;
+    }
+    __syncthreads();
+    for (int base = 0; base < N; base += SEL_NT) {
+      const int j = base + t;
+      unsigned u = 0;
+      if (j < N) u = order_key(row[j]);
+      const bool gt = j < N && u > prefix, eq = j < N && u == prefix;
+      int eq_total;
+      const int eq_rank = block_exclusive_scan<SEL_NT>(eq ? 1 : 0, scan_tmp, &eq_total);
+      const int eq_base = sh[3];
+      if (gt || (eq && eq_base + eq_rank < need)) {
+        const int s = atomicAdd(&sh[2], 1);
+        K[s] = ((unsigned long long)u << 32) | (0xFFFFFFFFu - (unsigned)j);
+      }
+      __syncthreads();
+      if (t == 0) sh[3] = eq_base + eq_total;
+      __syncthreads();
+    }
+    nk = p_top;
+  }
+
+  // best first: bitonic sort of the packed keys, descending (padding 0 sorts last)
+  int P2 = 1;
+  while (P2 < nk) P2 <<= 1;
+  for (int j = nk + t; j < P2; j += SEL_NT) K[j] = 0;
+  __syncthreads();
+  for (int kk = 2; kk <= P2; kk <<= 1)
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int x = t; x < P2; x += SEL_NT) {
+        const int y = x ^ jj;
+        if (y > x) {
+          const unsigned long long a0 = K[x], a1 = K[y];
+          const bool desc = (x & kk) == 0;
+          if (desc ? (a0 < a1) : (a0 > a1)) {
+            K[x] = a1;
+            K[y] = a0;
+          }
+        }
+      }
+      __syncthreads();
+    }
+
+  // keys each selected bucket offers outside the sink and the window
+  for (int r = t; r < nk; r += SEL_NT) {
+    const int gid = (int)(0xFFFFFFFFu - (unsigned)(K[r] & 0xFFFFFFFFull));
+    const int blk = gid / m, loc = gid - blk * m;
+    const int* ob = offs + ((long long)b * NB + blk) * (m + 1);
+    const int o0 = ob[loc], o1 = ob[loc + 1];
+    int av = o1 - o0;
+    if (blk * n_cluster < n_sink || (blk + 1) * n_cluster > w0) {
+      const int* tb = table + ((long long)b * NB + blk) * n_cluster;
+      av = 0;
+      for (int x = o0; x < o1; ++x) {
+        const int key = tb[x];
+        av += key >= n_sink && key < w0;
+      }
+    }
+    avail[r] = av;
+  }
+  __syncthreads();
+  // exclusive scan over the best-first order: each thread a contiguous run
+  const int per = (nk + SEL_NT - 1) / SEL_NT;
+  int run = 0;
+  for (int e = 0; e < per; ++e) {
+    const int r = t * per + e;
+    if (r < nk) run += avail[r];
+  }
+  int total;
+  int pre = block_exclusive_scan<SEL_NT>(run, scan_tmp, &total);
+  for (int e = 0; e < per; ++e) {
+    const int r = t * per + e;
+    if (r < nk) {
+      excl[r] = pre;
+      pre += avail[r];
+    }
+  }
+  __syncthreads();
+  const int n_lr = total < k ? total : k;
+  for (int r = t; r < nk; r += SEL_NT) {
+    const int e0 = excl[r];
+    if (e0 >= k) continue;
+    const int take = avail[r] < k - e0 ? avail[r] : k - e0;
+    const int gid = (int)(0xFFFFFFFFu - (unsigned)(K[r] & 0xFFFFFFFFull));
+    const int blk = gid / m, loc = gid - blk * m;
+    const int* ob = offs + ((long long)b * NB + blk) * (m + 1);
+    const int* tb = table + ((long long)b * NB + blk) * n_cluster;
+    int n = 0;
+    for (int x = ob[loc]; x < ob[loc + 1] && n < take; ++x) {
+      const int key = tb[x];
+      if (key >= n_sink && key < w0) LR[e0 + n++] = key;
+    }
+  }
+  // long-range keys ascending
+  int Q2 = 1;
+  while (Q2 < n_lr) Q2 <<= 1;
+  for (int j = n_lr + t; j < Q2; j += SEL_NT) LR[j] = 0x7FFFFFFF;
+  __syncthreads();
+  for (int kk = 2; kk <= Q2; kk <<= 1)
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int x = t; x < Q2; x += SEL_NT) {
+        const int y = x ^ jj;
+        if (y > x) {
+          const int a0 = LR[x], a1 = LR[y];
+          const bool asc = (x & kk) == 0;
+          if (asc ? (a0 > a1) : (a0 < a1)) {
+            LR[x] = a1;
+            LR[y] = a0;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  const int n_s = n_sink < w0 ? n_sink : w0;
+  const int n_win = p - w0 + 1;
+  const int cnt_all = n_s + n_lr + n_win;
+  for (int j = t; j < W; j += SEL_NT) {
+    int v = -1;
+    if (j < n_s) v = j;
+    else if (j < n_s + n_lr) v = LR[j - n_s];
+    else if (j < cnt_all) v = w0 + (j - n_s - n_lr);
+    out[j] = v;
+  }
+  if (t == 0) count[qrow] = cnt_all;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------
+
+hipError_t launch_sem_cluster(const void* k_idx, int B, int L_max, const SemParams& sp, int NB, int first_block,
+                              int n_update, void* cent, int32_t* table, int32_t* offs, hipStream_t st) {
+  SemGeom g;
+  g.n_cluster = sp.n_cluster;
+  g.n_pool = sp.n_pool;
+  g.npk = sp.n_cluster / sp.n_pool;
+  g.m = sp.n_cluster / sp.n_bavg;
+  g.cap = sp.n_bmax / sp.n_pool;
+  dim3 grid(n_update, B);
+  hipLaunchKernelGGL(sem_cluster_kernel, grid, dim3(256), 0, st, static_cast<const unsigned short*>(k_idx),
+                     (long long)L_max * SEM_D, g, first_block, NB, static_cast<unsigned short*>(cent), table, offs);
+  return hipGetLastError();
+}
+
+long long sem_ld(int NB, int m) { return (((long long)NB * m) + 3) / 4 * 4; }
+
+size_t sem_select_row_bytes(int NB, int m) { return (size_t)SEM_D * 4 + (size_t)sem_ld(NB, m) * 4; }
+
+hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
+  const int m = a.sp.n_cluster / a.sp.n_bavg;
+  const long long ld = sem_ld(a.NB, m);
+  const size_t row_bytes = sem_select_row_bytes(a.NB, m);
+  const long long rows_fit = (long long)(a.ws_bytes / row_bytes);
+  long long nqc_max = rows_fit / a.B;
+  if (nqc_max > a.n_q) nqc_max = a.n_q;
+  if (nqc_max < 1) return hipErrorInvalidValue;
+  const int W = a.n_sink + a.k + a.n_w;
+  for (int i0 = 0; i0 < a.n_q; i0 += (int)nqc_max) {
+    const int nqc = (int)(a.n_q - i0 < nqc_max ? a.n_q - i0 : nqc_max);
+    const int rows = a.B * nqc;
+    float* qn = static_cast<float*>(a.ws);
+    float* S = qn + (size_t)rows * SEM_D;
+    hipLaunchKernelGGL(sem_qnorm_kernel, dim3((rows + 255) / 256), dim3(256), 0, st,
+                       static_cast<const unsigned short*>(a.q_idx), a.n_q, i0, nqc, rows, qn);
+    if (nqc == 1) {
+      const int bpw = 4;
+      dim3 grid((a.NB + 4 * bpw - 1) / (4 * bpw), 1, a.B);
+      hipLaunchKernelGGL(sem_score_kernel<1>, grid, dim3(256), 0, st, qn, a.q_pos, a.n_q, i0, nqc,
+                         static_cast<const unsigned short*>(a.cent), a.NB, m, a.sp.n_cluster, bpw, S, ld);
+    } else {
+      constexpr int QT = 8;
+      const int bpw = 4;
+      dim3 grid((a.NB + 4 * bpw - 1) / (4 * bpw), (nqc + QT - 1) / QT, a.B);
+      hipLaunchKernelGGL(sem_score_kernel<QT>, grid, dim3(256), 0, st, qn, a.q_pos, a.n_q, i0, nqc,
+                         static_cast<const unsigned short*>(a.cent), a.NB, m, a.sp.n_cluster, bpw, S, ld);
+    }
+    hipLaunchKernelGGL(sem_select_kernel, dim3(nqc, a.B), dim3(SEL_NT), 0, st, S, ld, a.q_pos, a.n_q, i0, nqc,
+                       a.table, a.offs, a.NB, m, a.sp.n_cluster, a.k, a.p_top, a.n_sink, a.n_w, W, a.idx, a.count);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace lsa

@@ -24,7 +24,8 @@ from typing import Optional
 import torch
 
 IDS = {"q_idx": 1, "k_idx": 2, "w": 3, "q": 4, "k": 5, "v": 6,
-       "pages": 7, "pool_k_idx": 8, "pool_k": 9, "pool_v": 10}
+       "pages": 7, "pool_k_idx": 8, "pool_k": 9, "pool_v": 10,
+       "sem_topics": 11, "k_sem": 12, "q_sem": 13}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -52,6 +53,13 @@ class Workload:
     pooled: bool = False    # two_stage with the kept blocks' keys as the list (k = n_keep * block_size)
     page_size: int = 0      # > 0: caches scattered over a pool of pages (paged_pool)
     spare_pages: int = 0    # unused pool pages besides the sequences' own
+    semantic: bool = False  # flat semantic search: bf16 index keys / queries of 64 dims
+    n_cluster: int = 512    # keys per cluster block (the window is one block)
+    n_pool: int = 4         # keys per pool key
+    n_bavg: int = 8         # average keys per bucket
+    n_bmax: int = 32        # largest bucket (keys)
+    p_top: int = 512        # buckets kept per query (p * n_pool >= k)
+    n_sink: int = 4         # sink keys
 
     @property
     def decode(self) -> bool:
@@ -91,6 +99,14 @@ WORKLOADS = {
     "two_stage_128k": Workload("two_stage_128k", B=1, n_q=8192, L=131072, q_pos0=122880,
                                H_I=64, d_I=128, k=2048, H_q=16, two_stage=True,
                                block_size=128, n_keep=64),
+    # flat semantic search (bucket cache of 512-key blocks, 64 buckets each): decode of 64
+    # sequences at 128K, 2048 long-range keys from the best 512 buckets + 4 sinks + a
+    # 512-key window
+    "decode_128k_lsa": Workload("decode_128k_lsa", B=64, n_q=1, L=131073, q_pos0=131072,
+                                H_I=1, d_I=64, k=2048, H_q=16, semantic=True),
+    # the same search for the final 8192 queries of a 128K prefill
+    "prefill_128k_lsa": Workload("prefill_128k_lsa", B=1, n_q=8192, L=131072, q_pos0=122880,
+                                 H_I=1, d_I=64, k=2048, H_q=16, semantic=True),
 }
 
 
@@ -191,6 +207,34 @@ def paged_pool(inp: dict, page_size: int, spare_pages: int = 0, seed: int = 0) -
     out["page_table"] = page_table
     out["page_size"] = page_size
     return out
+
+
+def semantic_inputs(wl: Workload, device="cpu", seed: Optional[int] = None, n_topics: int = 64,
+                    noise: float = 0.5) -> dict:
+    """Index keys and queries of flat semantic search (bf16, 64 dims) with topic structure:
+    a sequence is a run of spans of 16..127 tokens, each on one of ``n_topics`` topics;
+    a key is its topic's centre (N(0, 1) per dim) plus N(0, noise^2) noise, a query the
+    centre of a random topic plus the same noise.  Returns dict(k_sem [B, L, 64],
+    q_sem [B, n_q, 64], q_pos)."""
+    s = wl.seed if seed is None else seed
+    gt = _gen(s, IDS["sem_topics"], "cpu")
+    centres = torch.randn((n_topics, 64), generator=gt)
+    topic = torch.empty((wl.B, wl.L), dtype=torch.int64)
+    for b in range(wl.B):
+        lens = torch.randint(16, 128, (wl.L // 16 + 1,), generator=gt)
+        tops = torch.randint(0, n_topics, (lens.shape[0],), generator=gt)
+        topic[b] = torch.repeat_interleave(tops, lens)[: wl.L]
+    q_topic = torch.randint(0, n_topics, (wl.B, wl.n_q), generator=gt)
+    gk = _gen(s, IDS["k_sem"], device)
+    gq = _gen(s, IDS["q_sem"], device)
+    c = centres.to(device)
+    k_sem = torch.empty((wl.B, wl.L, 64), dtype=torch.bfloat16, device=device)
+    for b in range(wl.B):
+        k_sem[b] = (c[topic[b].to(device)] + noise * torch.randn((wl.L, 64), generator=gk, device=device,
+                                                                 dtype=torch.float32)).to(torch.bfloat16)
+    q_sem = (c[q_topic.to(device)] + noise * torch.randn((wl.B, wl.n_q, 64), generator=gq, device=device,
+                                                         dtype=torch.float32)).to(torch.bfloat16)
+    return {"k_sem": k_sem, "q_sem": q_sem, "q_pos": q_positions(wl, device)}
 
 
 def checked_rows(wl: Workload, n_random: int = 56, seed: int = 0) -> list:

@@ -1,0 +1,197 @@
+"""Flat semantic search on the GPU against the CPU oracle: the bucket cache (centroid
+bits, key tables, offsets) and the index lists bit for bit, attention over the lists
+within tolerance, at small sizes spanning several blocks and ragged tails and on
+sampled rows of the full-size workloads."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from tests.gpu_util import AttnErr, dev, np64
+
+pytestmark = [pytest.mark.gpu]
+
+
+@pytest.fixture(scope="module")
+def lsa():
+    import learned_top_sparse_amd as m
+    m.lib()
+    return m
+
+
+def _f32(t):
+    return t.detach().float().cpu().numpy().astype(np.float32)
+
+
+def _gpu_cache_np(cache, b):
+    """The GPU cache of sequence b in the oracle's layout: centroids [NB, m, 64]."""
+    c = cache["centroids"][b].float().cpu().numpy()             # [NB, 8, 64, 8]
+    m = cache["offsets"].shape[-1] - 1
+    cent = c.transpose(0, 2, 1, 3).reshape(c.shape[0], 64, 64)[:, :m]
+    return cent, cache["table"][b].cpu().numpy(), cache["offsets"][b].cpu().numpy()
+
+
+def _oracle_cache(k_sem_b, prm, n_blocks=None):
+    n_cluster, n_pool, n_bavg, n_bmax = prm
+    return oracle.bucket_cache(_f32(k_sem_b), n_cluster, n_pool, n_bavg, n_bmax, n_blocks=n_blocks)
+
+
+def _check_cache(cache, k_sem, prm, blocks=None):
+    B = k_sem.shape[0]
+    for b in range(B):
+        cent, table, offs = _gpu_cache_np(cache, b)
+        NB = table.shape[0]
+        want = _oracle_cache(k_sem[b], prm, n_blocks=NB)
+        sel = range(NB) if blocks is None else blocks
+        for t in sel:
+            assert np.array_equal(offs[t], want["offsets"][t]), f"offsets b={b} block={t}"
+            assert np.array_equal(table[t], want["table"][t]), f"table b={b} block={t}"
+            assert np.array_equal(cent[t], want["centroids"][t]), f"centroids b={b} block={t}"
+        # unused slots of the centroid layout stay zero
+        m = offs.shape[-1] - 1
+        full = cache["centroids"][b].float().cpu().numpy().transpose(0, 2, 1, 3).reshape(NB, 64, 64)
+        assert not full[:, m:].any()
+    return want
+
+
+PARAMS = [(512, 4, 8, 32), (256, 2, 4, 16), (128, 1, 2, 8), (512, 8, 16, 64), (64, 2, 4, 8)]
+
+
+@pytest.mark.parametrize("prm", PARAMS, ids=lambda p: "c%d_p%d_a%d_x%d" % p)
+def test_cluster_matches_oracle(lsa, prm):
+    n_cluster = prm[0]
+    wl = synthetic.WORKLOADS["decode_128k_lsa"].replace(B=2, L=3 * n_cluster + 77, q_pos0=3 * n_cluster + 76)
+    inp = synthetic.semantic_inputs(wl, dev(), seed=3)
+    print(f"[cluster {prm}]", flush=True)
+    cache = lsa.lsa_semantic_cache(inp["k_sem"], *prm)
+    torch.cuda.synchronize()
+    assert cache["table"].shape[1] == wl.L // n_cluster
+    _check_cache(cache, inp["k_sem"], prm)
+
+
+def test_cluster_degenerate_keys(lsa):
+    """All-zero keys (zero pool keys: every cost 0, ties everywhere) and identical keys."""
+    prm = (512, 4, 8, 32)
+    k = torch.zeros((2, 1024, 64), dtype=torch.bfloat16, device=dev())
+    k[1] = torch.randn(64, device=dev()).to(torch.bfloat16)     # every key the same
+    k[0, 512:] = torch.randn((512, 64), device=dev()).to(torch.bfloat16)
+    cache = lsa.lsa_semantic_cache(k, *prm)
+    torch.cuda.synchronize()
+    _check_cache(cache, k, prm)
+
+
+def test_cluster_incremental(lsa):
+    """Clustering blocks one at a time into a cache sized for more gives the same cache."""
+    prm = (512, 4, 8, 32)
+    wl = synthetic.WORKLOADS["decode_128k_lsa"].replace(B=3, L=4 * 512, q_pos0=4 * 512 - 1)
+    inp = synthetic.semantic_inputs(wl, dev(), seed=4)
+    full = lsa.lsa_semantic_cache(inp["k_sem"], *prm)
+    inc = lsa.lsa_semantic_cache(inp["k_sem"][:, :512].contiguous(), *prm, n_blocks=4)
+    for t in range(1, 4):
+        inc = lsa.lsa_semantic_cache(inp["k_sem"], cache=inc, first_block=t, n_update=1)
+    torch.cuda.synchronize()
+    for name in ("centroids", "table", "offsets"):
+        assert torch.equal(full[name], inc[name]), name
+
+
+def _select_case(lsa, wl, prm, positions, k, p_top, n_sink, n_w, seed, ws_bytes=None):
+    inp = synthetic.semantic_inputs(wl, dev(), seed=seed)
+    B = wl.B
+    q_pos = torch.tensor(positions, dtype=torch.int32, device=dev()).view(B, -1).contiguous()
+    q = inp["q_sem"][:, :1].expand(B, q_pos.shape[1], 64).contiguous()
+    q = q + torch.randn(q.shape, device=dev(), generator=torch.Generator(dev()).manual_seed(seed)).to(q.dtype)
+    cache = lsa.lsa_semantic_cache(inp["k_sem"], *prm)
+    idx, cnt = lsa.lsa_semantic_select(q, q_pos, cache, k, p_top, n_sink, n_w, ws_bytes=ws_bytes)
+    torch.cuda.synchronize()
+    return inp, q, q_pos, cache, idx, cnt
+
+
+@pytest.mark.parametrize("prm,k,p_top,n_sink,n_w", [
+    ((512, 4, 8, 32), 300, 80, 4, 512),
+    ((512, 4, 8, 32), 2048, 512, 4, 512),
+    ((256, 2, 4, 16), 100, 64, 0, 300),
+    ((128, 1, 2, 8), 77, 2048, 9, 1),
+])
+def test_select_matches_oracle(lsa, prm, k, p_top, n_sink, n_w):
+    n_c = prm[0]
+    L = 9 * n_c + 5
+    wl = synthetic.WORKLOADS["decode_128k_lsa"].replace(B=2, L=L, q_pos0=L - 1)
+    positions = [[L - 1, n_c - 1, n_c, 2 * n_c + 3, 5 * n_c - 1, 0, -1, 8 * n_c + 100],
+                 [3, L - 2, 7 * n_c, n_c + 1, 4 * n_c + 17, 6 * n_c, 2 * n_c - 1, L - 1]]
+    inp, q, q_pos, cache, idx, cnt = _select_case(lsa, wl, prm, positions, k, p_top, n_sink, n_w, seed=5)
+    for b in range(2):
+        oc = _oracle_cache(inp["k_sem"][b], prm, n_blocks=cache["table"].shape[1])
+        for i, p in enumerate(positions[b]):
+            r = oracle.semantic_select_row(_f32(q[b, i]), oc, p, k, p_top, n_sink, n_w)
+            assert np.array_equal(idx[b, i].cpu().numpy(), r["J"]), f"b={b} p={p}"
+            assert int(cnt[b, i]) == r["count"], f"count b={b} p={p}"
+
+
+def test_select_in_chunks(lsa):
+    """A workspace for one query per sequence: the call runs in chunks, same lists."""
+    prm = (512, 4, 8, 32)
+    L = 6 * 512
+    wl = synthetic.WORKLOADS["decode_128k_lsa"].replace(B=2, L=L, q_pos0=L - 1)
+    positions = [[L - 1 - 37 * i for i in range(20)], [512 + 97 * i for i in range(20)]]
+    inp, q, q_pos, cache, idx, cnt = _select_case(lsa, wl, prm, positions, 200, 64, 4, 512, seed=6)
+    row = 64 * 4 + ((cache["table"].shape[1] * 64 + 3) // 4 * 4) * 4
+    idx2, cnt2 = lsa.lsa_semantic_select(q, q_pos, cache, 200, 64, 4, 512, ws_bytes=2 * row * 3)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
+
+
+def test_semantic_forward_small(lsa):
+    """Selection and attention together on a causal chunk against the oracle."""
+    prm = (512, 4, 8, 32)
+    wl = synthetic.Workload("sem_small", B=2, n_q=64, L=5 * 512 + 40, q_pos0=5 * 512 - 24, H_I=1, d_I=64,
+                            k=256, H_q=8, d=128, semantic=True, p_top=64, n_sink=4)
+    g = synthetic.make_inputs(wl.replace(d_I=64), dev())
+    g.update(synthetic.semantic_inputs(wl, dev(), seed=7))
+    cache = lsa.lsa_semantic_cache(g["k_sem"], *prm)
+    res = lsa.lsa_semantic_forward(g, cache, wl.k, wl.p_top, wl.n_sink, prm[0])
+    torch.cuda.synchronize()
+    err = AttnErr()
+    for b in range(2):
+        oc = _oracle_cache(g["k_sem"][b], prm, n_blocks=cache["table"].shape[1])
+        for i in range(0, 64, 5):
+            p = int(g["q_pos"][b, i])
+            r = oracle.semantic_forward_row(_f32(g["q_sem"][b, i]), oc, p, wl.k, wl.p_top, wl.n_sink, prm[0],
+                                            q_row=np64(g["q"][b, i]), k_cache=np64(g["k"][b]),
+                                            v_cache=np64(g["v"][b]), scale=wl.scale)
+            assert np.array_equal(res["idx"][b, i].cpu().numpy(), r["J"]), f"b={b} i={i}"
+            assert int(res["count"][b, i]) == r["count"]
+            err.add(np64(res["out"][b, i]), r["out"], (b, i))
+    err.check()
+
+
+@pytest.mark.slow
+def test_decode_128k_lsa_sampled(lsa):
+    """The decode workload at full size (64 sequences, 128K keys each), in the launch
+    configuration the benchmark times: sampled cache blocks and two sequences' lists
+    bit for bit against the oracle (which clusters those sequences itself)."""
+    wl = synthetic.WORKLOADS["decode_128k_lsa"]
+    prm = (wl.n_cluster, wl.n_pool, wl.n_bavg, wl.n_bmax)
+    inp = synthetic.semantic_inputs(wl, dev())
+    print("[decode_128k_lsa] clustering", flush=True)
+    cache = lsa.lsa_semantic_cache(inp["k_sem"], *prm)
+    idx, cnt = lsa.lsa_semantic_select(inp["q_sem"], inp["q_pos"], cache, wl.k, wl.p_top, wl.n_sink, wl.n_cluster)
+    torch.cuda.synchronize()
+    NB = cache["table"].shape[1]
+    assert NB == 256
+    for b in (0, 37, 63):
+        cent, table, offs = _gpu_cache_np(cache, b)
+        for t in (0, 1, 128, 255):
+            c, tb, of = oracle.sem_cluster_block(_f32(inp["k_sem"][b, t * 512:(t + 1) * 512]), wl.n_pool,
+                                                 512 // wl.n_bavg, wl.n_bmax, first_key=t * 512)
+            assert np.array_equal(cent[t], c) and np.array_equal(table[t], tb) and np.array_equal(offs[t], of), \
+                f"block b={b} t={t}"
+    for b in (0, 63):
+        print(f"[decode_128k_lsa] oracle cache of sequence {b}", flush=True)
+        oc = _oracle_cache(inp["k_sem"][b], prm, n_blocks=NB)
+        p = int(inp["q_pos"][b, 0])
+        r = oracle.semantic_select_row(_f32(inp["q_sem"][b, 0]), oc, p, wl.k, wl.p_top, wl.n_sink, wl.n_cluster)
+        assert np.array_equal(idx[b, 0].cpu().numpy(), r["J"]), f"seq {b}"
+        assert int(cnt[b, 0]) == r["count"] == wl.n_sink + wl.k + wl.n_cluster

@@ -49,6 +49,38 @@ def test_host_validation_without_gpu():
     assert L.lsa_topk(None, 0, None, None, 0, 0, 0, 5, 10, 8, None, None, None, 0, None) == 0
 
 
+def test_semantic_validation_without_gpu():
+    """Flat semantic search: parameter checks on the host, workspace sizes, no-op calls."""
+    import learned_top_sparse_amd as lsa
+    L = lsa.lib()
+    P = lsa.SemanticParams
+    ok = P(512, 4, 8, 32)
+    nb = ctypes.c_size_t(0)
+    assert L.lsa_semantic_select_workspace_size(64, 1, 256, ctypes.byref(ok), ctypes.byref(nb)) == 0
+    assert nb.value == 64 * (64 * 4 + 256 * 64 * 4)
+    for bad in (P(512, 4, 8, 15), P(512, 3, 8, 32), P(512, 4, 7, 32), P(512, 8, 4, 32), P(0, 1, 1, 2)):
+        assert L.lsa_semantic_cluster(None, 1, 4096, 64, ctypes.byref(bad), 8, 0, 8, None, None, None, None) == -1
+    assert L.lsa_semantic_cluster(None, 1, 4096, 128, ctypes.byref(ok), 8, 0, 8, None, None, None, None) == -2
+    # 512 pool keys per block, or more than 64 buckets: beyond the compiled limits
+    assert L.lsa_semantic_cluster(None, 1, 4096, 64, ctypes.byref(P(512, 1, 8, 32)), 8, 0, 8,
+                                  None, None, None, None) == -2
+    assert L.lsa_semantic_cluster(None, 1, 4096, 64, ctypes.byref(P(512, 2, 4, 8)), 8, 0, 8,
+                                  None, None, None, None) == -2
+    # blocks beyond the keys or the cache
+    assert L.lsa_semantic_cluster(None, 1, 4000, 64, ctypes.byref(ok), 8, 0, 8, None, None, None, None) == -1
+    assert L.lsa_semantic_cluster(None, 1, 4096, 64, ctypes.byref(ok), 4, 2, 3, None, None, None, None) == -1
+    assert L.lsa_semantic_cluster(None, 0, 4096, 64, ctypes.byref(ok), 8, 0, 8, None, None, None, None) == 0
+    sel = L.lsa_semantic_select
+    assert sel(None, None, 1, 1, 64, ctypes.byref(ok), 8, None, None, None, 0, 8, 4, 512,
+               None, None, None, 0, None) == -1                                       # k < 1
+    assert sel(None, None, 1, 1, 64, ctypes.byref(ok), 8, None, None, None, 5000, 8, 4, 512,
+               None, None, None, 0, None) == -2                                       # k > 4096
+    assert sel(None, None, 1, 1, 64, ctypes.byref(ok), 8, None, None, None, 64, 4096, 4, 512,
+               None, None, None, 0, None) == -2                                       # p_top > 2048
+    assert sel(None, None, 0, 1, 64, ctypes.byref(ok), 8, None, None, None, 64, 16, 4, 512,
+               None, None, None, 0, None) == 0                                        # nothing to do
+
+
 def _fake_inputs(B, n_q, L, H_I=64, d_I=128, H_q=16, d=128):
     """CPU tensors with the path's shapes: only their pointers reach the host-side planning."""
     import torch
