@@ -21,6 +21,7 @@
 
 #include "lsa_device.h"
 #include "lsa_internal.h"
+#include "lsa_select.h"
 
 namespace lsa {
 namespace {
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(256) void sem_score_kernel(const float* __restrict_
 constexpr int SEM_PMAX = 2048;
 constexpr int SEM_KMAX = 4096;
 
-__global__ __launch_bounds__(SEL_NT) void sem_select_kernel(const float* __restrict__ S, long long ld,
+__global__ __launch_bounds__(SEL_NT) void sem_select_stream_kernel(const float* __restrict__ S, long long ld,
                                                             const int* __restrict__ q_pos, int n_q, int i0, int nqc,
                                                             const int* __restrict__ table, const int* __restrict__ offs,
                                                             int NB, int m, int n_cluster, int k, int p_top, int n_sink,
@@ -535,6 +536,203 @@ __global__ __launch_bounds__(SEL_NT) void sem_select_kernel(const float* __restr
   if (t == 0) count[qrow] = cnt_all;
 }
 
+
+// Selection and expansion of rows of at most 1024 * C buckets whose long-range keys
+// lie below 32 * LBM(C) positions: one 1024-thread workgroup per query, the row's
+// order keys in registers (bucket c * 1024 + t in slot c of thread t).  The cut is a
+// radix select over them (11-bit digits below the bits all keys share; ties to the
+// lowest bucket id); each kept bucket's start in best-first order is the count of keys
+// the kept buckets with larger packed keys offer, and the long-range keys are marked
+// in an LDS bitmap of key positions, which yields them ascending.
+constexpr int SELR_NT = 1024;
+template <int C>
+struct SelLbm {
+  static constexpr int WORDS = 256 * C;  // positions < 8192 * C: n_bavg = 8 fills it
+};
+
+template <int C>
+__global__ __launch_bounds__(SELR_NT) void sem_select_kernel(const float* __restrict__ S, long long ld,
+                                                             const int* __restrict__ q_pos, int n_q, int i0, int nqc,
+                                                             const int* __restrict__ table,
+                                                             const int* __restrict__ offs, int NB, int m,
+                                                             int n_cluster, int n_bmax, int k, int p_top, int n_sink,
+                                                             int n_w, int W, int* __restrict__ idx,
+                                                             int* __restrict__ count) {
+  constexpr int NT = SELR_NT;
+  constexpr int NWD = NT * C / 32;
+  constexpr int LW = SelLbm<C>::WORDS;
+  __shared__ unsigned long long K[SEM_PMAX];
+  __shared__ int avail[SEM_PMAX];
+  __shared__ int excl[SEM_PMAX];
+  __shared__ int bstart[SEM_PMAX], bsize[SEM_PMAX];
+  __shared__ unsigned long long emask[SEM_PMAX];
+  __shared__ int hist[2048];
+  __shared__ unsigned bm[NWD], eqm[NWD];
+  __shared__ unsigned lbm[LW];
+  __shared__ int scan_tmp[NT / 64];
+  __shared__ int sh[4];
+  __shared__ unsigned long long shu[2];
+
+  const int t = threadIdx.x;
+  const int i = blockIdx.x, b = blockIdx.y;
+  const long long qrow = (long long)b * n_q + i0 + i;
+  const int p = q_pos[qrow];
+  int* out = idx + qrow * W;
+  if (p < 0) {
+    for (int j = t; j < W; j += NT) out[j] = -1;
+    if (t == 0) count[qrow] = 0;
+    return;
+  }
+  int nb = p / n_cluster;
+  nb = nb < NB ? nb : NB;
+  const int N = nb * m;
+  const float* row = S + ((long long)b * nqc + i) * ld;
+  const int w0 = p - n_w + 1 > 0 ? p - n_w + 1 : 0;
+
+  // 1. the kept buckets, marked in bm by bucket id
+  unsigned long long key[C];
+  unsigned vmask = 0u;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int j = c * NT + t;
+    key[c] = 0ull;
+    if (j < N) {
+      key[c] = order_key(row[j]);
+      vmask |= 1u << c;
+    }
+  }
+  if (N > p_top) {
+    int need_eq;
+    const unsigned long long T = radix_cut64<NT, C>(key, vmask, p_top, hist, scan_tmp, sh, shu, &need_eq);
+    mark_kept64<NT, C>(key, vmask, T, need_eq, bm, eqm, scan_tmp);
+  } else {
+    for (int wd = t; wd < NWD; wd += NT) {
+      const int lo = 32 * wd;
+      bm[wd] = lo + 32 <= N ? 0xFFFFFFFFu : (lo >= N ? 0u : ((1u << (N - lo)) - 1u));
+    }
+    __syncthreads();
+  }
+  const int nk = emit_marked<NT>(bm, NWD, scan_tmp, [&](int r, int pos) {
+    K[r] = ((unsigned long long)order_key(row[pos]) << 32) | (0xFFFFFFFFu - (unsigned)pos);
+  });
+  __syncthreads();
+
+  // 2. best first: bitonic sort of the packed keys, descending (padding 0 sorts last);
+  //    one key per thread, exchanges under 64 apart by lane shuffles, wider ones
+  //    through LDS
+  int P2 = 1;
+  while (P2 < nk) P2 <<= 1;
+  if (P2 <= NT) {
+    unsigned long long v = t < nk ? K[t] : 0ull;
+    for (int kk = 2; kk <= P2; kk <<= 1)
+      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+        unsigned long long pv;
+        if (jj >= 64) {
+          __syncthreads();
+          K[t] = v;
+          __syncthreads();
+          pv = K[t ^ jj];
+        } else {
+          pv = __shfl_xor(v, jj);
+        }
+        const bool desc = (t & kk) == 0, lower = (t & jj) == 0;
+        v = (desc == lower) ? (v > pv ? v : pv) : (v < pv ? v : pv);
+      }
+    __syncthreads();
+    if (t < P2) K[t] = v;
+  } else {
+    for (int j = nk + t; j < P2; j += NT) K[j] = 0;
+    __syncthreads();
+    for (int kk = 2; kk <= P2; kk <<= 1)
+      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+        for (int x = t; x < P2; x += NT) {
+          const int y = x ^ jj;
+          if (y > x) {
+            const unsigned long long a0 = K[x], a1 = K[y];
+            const bool desc = (x & kk) == 0;
+            if (desc ? (a0 < a1) : (a0 > a1)) {
+              K[x] = a1;
+              K[y] = a0;
+            }
+          }
+        }
+        __syncthreads();
+      }
+  }
+  __syncthreads();
+
+  // 3. each kept bucket: where its keys start in the table and how many (one load per
+  //    bucket), then which of them lie outside the sink and the window (one load per
+  //    key, all independent: a 64-bit mask per bucket), and the running count of those
+  //    in best-first order
+  const long long tseq = (long long)b * NB * n_cluster;
+  for (int r = t; r < nk; r += NT) {
+    const int gid = (int)(0xFFFFFFFFu - (unsigned)(K[r] & 0xFFFFFFFFull));
+    const int blk = gid / m, loc = gid - blk * m;
+    const int* ob = offs + ((long long)b * NB + blk) * (m + 1);
+    const int o0 = ob[loc], o1 = ob[loc + 1];
+    bstart[r] = blk * n_cluster + o0;
+    bsize[r] = o1 - o0;
+    emask[r] = 0ull;
+  }
+  // long-range keys lie below both the window and the end of the scored blocks
+  const int pos_lim = w0 < nb * n_cluster ? w0 : nb * n_cluster;
+  const int nlw = (pos_lim + 31) >> 5;
+  for (int wd = t; wd < nlw; wd += NT) lbm[wd] = 0u;
+  __syncthreads();
+  for (int x = t; x < nk * n_bmax; x += NT) {
+    const int r = x / n_bmax, sl = x - r * n_bmax;
+    if (sl >= bsize[r]) continue;
+    const int kx = table[tseq + bstart[r] + sl];
+    if (kx >= n_sink && kx < w0) atomicOr(&emask[r], 1ull << sl);
+  }
+  __syncthreads();
+  const int per = (nk + NT - 1) / NT;
+  int run = 0;
+  for (int e = 0; e < per; ++e) {
+    const int r = t * per + e;
+    if (r < nk) {
+      avail[r] = __popcll(emask[r]);
+      run += avail[r];
+    }
+  }
+  int total;
+  int pre = block_exclusive_scan<NT>(run, scan_tmp, &total);
+  for (int e = 0; e < per; ++e) {
+    const int r = t * per + e;
+    if (r < nk) {
+      excl[r] = pre;
+      pre += avail[r];
+    }
+  }
+  __syncthreads();
+
+  // 4. long-range keys: whole buckets before the cut, the first keys of the one at it
+  //    (a key's rank among its bucket's eligible keys is the mask's count below it)
+  const int n_lr = total < k ? total : k;
+  for (int x = t; x < nk * n_bmax; x += NT) {
+    const int r = x / n_bmax, sl = x - r * n_bmax;
+    const int e0 = excl[r];
+    if (e0 >= k) continue;
+    const unsigned long long em = emask[r];
+    if (!((em >> sl) & 1ull)) continue;
+    const int rank = __popcll(em & ((1ull << sl) - 1ull));
+    if (rank >= k - e0) continue;
+    const int kx = table[tseq + bstart[r] + sl];
+    atomicOr(&lbm[kx >> 5], 1u << (kx & 31));
+  }
+  __syncthreads();
+  const int n_s = n_sink < w0 ? n_sink : w0;
+  emit_marked<NT>(lbm, nlw, scan_tmp, [&](int r, int pos) { out[n_s + r] = pos; });
+  const int n_win = p - w0 + 1;
+  const int cnt_all = n_s + n_lr + n_win;
+  for (int j = t; j < W; j += NT) {
+    if (j < n_s) out[j] = j;
+    else if (j >= n_s + n_lr) out[j] = j < cnt_all ? w0 + (j - n_s - n_lr) : -1;
+  }
+  if (t == 0) count[qrow] = cnt_all;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------
@@ -585,8 +783,23 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(sem_score_kernel<QT>, grid, dim3(256), 0, st, qn, a.q_pos, a.n_q, i0, nqc,
                          static_cast<const unsigned short*>(a.cent), a.NB, m, a.sp.n_cluster, bpw, S, ld);
     }
-    hipLaunchKernelGGL(sem_select_kernel, dim3(nqc, a.B), dim3(SEL_NT), 0, st, S, ld, a.q_pos, a.n_q, i0, nqc,
-                       a.table, a.offs, a.NB, m, a.sp.n_cluster, a.k, a.p_top, a.n_sink, a.n_w, W, a.idx, a.count);
+    const long long n_max = (long long)a.NB * m, pos_max = (long long)a.NB * a.sp.n_cluster;
+    auto fits = [&](int C) {
+      return n_max <= (long long)SELR_NT * C && pos_max <= 32LL * 256 * C && a.sp.n_bmax <= 64;
+    };
+#define LSA_SEM_SEL(C)                                                                                          \
+  hipLaunchKernelGGL(sem_select_kernel<C>, dim3(nqc, a.B), dim3(SELR_NT), 0, st, S, ld, a.q_pos, a.n_q, i0, nqc, \
+                     a.table, a.offs, a.NB, m, a.sp.n_cluster, a.sp.n_bmax, a.k, a.p_top, a.n_sink, a.n_w, W, a.idx, \
+                     a.count)
+    if (fits(4)) LSA_SEM_SEL(4);
+    else if (fits(8)) LSA_SEM_SEL(8);
+    else if (fits(16)) LSA_SEM_SEL(16);
+    else if (fits(32)) LSA_SEM_SEL(32);
+    else
+      hipLaunchKernelGGL(sem_select_stream_kernel, dim3(nqc, a.B), dim3(SEL_NT), 0, st, S, ld, a.q_pos, a.n_q, i0,
+                         nqc, a.table, a.offs, a.NB, m, a.sp.n_cluster, a.k, a.p_top, a.n_sink, a.n_w, W, a.idx,
+                         a.count);
+#undef LSA_SEM_SEL
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -114,6 +114,7 @@ def _select_case(lsa, wl, prm, positions, k, p_top, n_sink, n_w, seed, ws_bytes=
     ((512, 4, 8, 32), 2048, 512, 4, 512),
     ((256, 2, 4, 16), 100, 64, 0, 300),
     ((128, 1, 2, 8), 77, 2048, 9, 1),
+    ((512, 4, 8, 32), 500, 128, 4, 1),
 ])
 def test_select_matches_oracle(lsa, prm, k, p_top, n_sink, n_w):
     n_c = prm[0]
@@ -165,6 +166,23 @@ def test_semantic_forward_small(lsa):
             assert int(res["count"][b, i]) == r["count"]
             err.add(np64(res["out"][b, i]), r["out"], (b, i))
     err.check()
+
+
+@pytest.mark.slow
+def test_select_long_rows(lsa):
+    """Rows of more buckets than the register-held selection takes (37440 > 32768): the
+    streaming selection, bit for bit; and buckets of 16 keys (key positions beyond the
+    smaller bitmaps)."""
+    for prm, L in (((512, 4, 8, 32), 585 * 512 + 3), ((512, 4, 16, 32), 300 * 512 + 9)):
+        wl = synthetic.WORKLOADS["decode_128k_lsa"].replace(B=1, L=L, q_pos0=L - 1)
+        positions = [[L - 1, L - 600, 200 * 512 + 5, 3 * 512]]
+        print(f"[long rows {prm} L={L}]", flush=True)
+        inp, q, q_pos, cache, idx, cnt = _select_case(lsa, wl, prm, positions, 2048, 512, 4, 512, seed=8)
+        oc = _oracle_cache(inp["k_sem"][0], prm, n_blocks=cache["table"].shape[1])
+        for i, p in enumerate(positions[0]):
+            r = oracle.semantic_select_row(_f32(q[0, i]), oc, p, 2048, 512, 4, 512)
+            assert np.array_equal(idx[0, i].cpu().numpy(), r["J"]), f"p={p}"
+            assert int(cnt[0, i]) == r["count"]
 
 
 @pytest.mark.slow
