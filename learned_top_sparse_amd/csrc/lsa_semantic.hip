@@ -287,6 +287,56 @@ __global__ __launch_bounds__(256) void sem_qnorm_kernel(const unsigned short* __
 // that query's row of the score table; the next block's centroids are loaded while
 // the current one is scored.
 
+// Decode (one query per sequence): the same scores, with the query normalised inside
+// each wave -- lane d holds x_d, the sum of squares is taken d = 0, 1, ... across the
+// lanes, and the 64 rounded values are then wave-uniform -- so no separate launch.
+__global__ __launch_bounds__(256) void sem_score_decode_kernel(const unsigned short* __restrict__ q_idx,
+                                                               const int* __restrict__ q_pos, int n_q, int i0,
+                                                               const unsigned short* __restrict__ cent, int NB,
+                                                               int m, int n_cluster, int bpw,
+                                                               float* __restrict__ S, long long ld) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b = blockIdx.z;
+  const int blk0 = (blockIdx.x * 4 + w) * bpw;
+  if (blk0 >= NB) return;
+  const int p = q_pos[(long long)b * n_q + i0];
+  const int own = p < 0 ? 0 : p / n_cluster;
+  int blk_end = blk0 + bpw;
+  blk_end = blk_end < NB ? blk_end : NB;
+  blk_end = blk_end < own ? blk_end : own;
+  if (blk0 >= blk_end) return;
+
+  const uint4* cb = reinterpret_cast<const uint4*>(cent + ((long long)b * NB) * (SEM_D * SEM_SLOTS));
+  uint4 nxt[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) nxt[c] = cb[(long long)blk0 * (SEM_D * SEM_SLOTS / 8) + c * SEM_SLOTS + lane];
+
+  const float x = __uint_as_float((unsigned)q_idx[((long long)b * n_q + i0) * SEM_D + lane] << 16);
+  const float sq = x * x;
+  float ss = 0.f;
+#pragma unroll
+  for (int d = 0; d < SEM_D; ++d) ss = ss + __shfl(sq, d);
+  const float nrm = sqrtf(ss);
+  const float y = __uint_as_float(to_bf16(nrm > 0.f ? x / nrm : 0.f) << 16);
+  float q[SEM_D];
+#pragma unroll
+  for (int d = 0; d < SEM_D; ++d) q[d] = __shfl(y, d);
+
+  for (int blk = blk0; blk < blk_end; ++blk) {
+    float cv[SEM_D];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) unpack8(nxt[c], cv + 8 * c);
+    if (blk + 1 < blk_end) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) nxt[c] = cb[(long long)(blk + 1) * (SEM_D * SEM_SLOTS / 8) + c * SEM_SLOTS + lane];
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int d = 0; d < SEM_D; ++d) acc = fmaf(q[d], cv[d], acc);
+    if (lane < m) S[(long long)b * ld + (long long)blk * m + lane] = acc;
+  }
+}
+
 template <int QT>
 __global__ __launch_bounds__(256) void sem_score_kernel(const float* __restrict__ qn, const int* __restrict__ q_pos,
                                                         int n_q, int i0, int nqc,
@@ -544,28 +594,22 @@ __global__ __launch_bounds__(SEL_NT) void sem_select_stream_kernel(const float* 
 // lowest bucket id); each kept bucket's start in best-first order is the count of keys
 // the kept buckets with larger packed keys offer, and the long-range keys are marked
 // in an LDS bitmap of key positions, which yields them ascending.
-constexpr int SELR_NT = 1024;
 template <int C>
 struct SelLbm {
   static constexpr int WORDS = 256 * C;  // positions < 8192 * C: n_bavg = 8 fills it
 };
 
-template <int C>
-__global__ __launch_bounds__(SELR_NT) void sem_select_kernel(const float* __restrict__ S, long long ld,
+template <int NT, int C>
+__global__ __launch_bounds__(NT) void sem_select_kernel(const float* __restrict__ S, long long ld,
                                                              const int* __restrict__ q_pos, int n_q, int i0, int nqc,
                                                              const int* __restrict__ table,
                                                              const int* __restrict__ offs, int NB, int m,
                                                              int n_cluster, int n_bmax, int k, int p_top, int n_sink,
                                                              int n_w, int W, int* __restrict__ idx,
                                                              int* __restrict__ count) {
-  constexpr int NT = SELR_NT;
   constexpr int NWD = NT * C / 32;
   constexpr int LW = SelLbm<C>::WORDS;
   __shared__ unsigned long long K[SEM_PMAX];
-  __shared__ int avail[SEM_PMAX];
-  __shared__ int excl[SEM_PMAX];
-  __shared__ int bstart[SEM_PMAX], bsize[SEM_PMAX];
-  __shared__ unsigned long long emask[SEM_PMAX];
   __shared__ int hist[2048];
   __shared__ unsigned bm[NWD], eqm[NWD];
   __shared__ unsigned lbm[LW];
@@ -605,17 +649,25 @@ __global__ __launch_bounds__(SELR_NT) void sem_select_kernel(const float* __rest
     int need_eq;
     const unsigned long long T = radix_cut64<NT, C>(key, vmask, p_top, hist, scan_tmp, sh, shu, &need_eq);
     mark_kept64<NT, C>(key, vmask, T, need_eq, bm, eqm, scan_tmp);
-  } else {
-    for (int wd = t; wd < NWD; wd += NT) {
-      const int lo = 32 * wd;
-      bm[wd] = lo + 32 <= N ? 0xFFFFFFFFu : (lo >= N ? 0u : ((1u << (N - lo)) - 1u));
-    }
-    __syncthreads();
   }
-  const int nk = emit_marked<NT>(bm, NWD, scan_tmp, [&](int r, int pos) {
-    K[r] = ((unsigned long long)order_key(row[pos]) << 32) | (0xFFFFFFFFu - (unsigned)pos);
-  });
+  // the kept buckets' packed keys, appended from the registers (wave-aggregated slots;
+  // their order is set by the sort below)
+  if (t == 0) sh[2] = 0;
   __syncthreads();
+  const int lane = t & 63;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int pos = c * NT + t;
+    const bool kept = ((vmask >> c) & 1u) && (N <= p_top || ((bm[pos >> 5] >> (pos & 31)) & 1u));
+    const unsigned long long ball = __ballot(kept);
+    if (ball == 0ull) continue;
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&sh[2], __popcll(ball));
+    base = __shfl(base, 0);
+    if (kept) K[base + lanes_below(ball)] = (key[c] << 32) | (0xFFFFFFFFu - (unsigned)pos);
+  }
+  __syncthreads();
+  const int nk = sh[2];
 
   // 2. best first: bitonic sort of the packed keys, descending (padding 0 sorts last);
   //    one key per thread, exchanges under 64 apart by lane shuffles, wider ones
@@ -661,65 +713,73 @@ __global__ __launch_bounds__(SELR_NT) void sem_select_kernel(const float* __rest
   }
   __syncthreads();
 
-  // 3. each kept bucket: where its keys start in the table and how many (one load per
-  //    bucket), then which of them lie outside the sink and the window (one load per
-  //    key, all independent: a 64-bit mask per bucket), and the running count of those
-  //    in best-first order
+  // 3. each kept bucket, by the thread owning its run of the best-first order: where
+  //    its keys start and how many (one load), which of them lie outside the sink and
+  //    the window (loads 8 at a time, a 64-bit mask kept in a register), and the
+  //    running count of those in best-first order (one scan)
   const long long tseq = (long long)b * NB * n_cluster;
-  for (int r = t; r < nk; r += NT) {
-    const int gid = (int)(0xFFFFFFFFu - (unsigned)(K[r] & 0xFFFFFFFFull));
-    const int blk = gid / m, loc = gid - blk * m;
-    const int* ob = offs + ((long long)b * NB + blk) * (m + 1);
-    const int o0 = ob[loc], o1 = ob[loc + 1];
-    bstart[r] = blk * n_cluster + o0;
-    bsize[r] = o1 - o0;
-    emask[r] = 0ull;
-  }
   // long-range keys lie below both the window and the end of the scored blocks
   const int pos_lim = w0 < nb * n_cluster ? w0 : nb * n_cluster;
   const int nlw = (pos_lim + 31) >> 5;
   for (int wd = t; wd < nlw; wd += NT) lbm[wd] = 0u;
-  __syncthreads();
-  for (int x = t; x < nk * n_bmax; x += NT) {
-    const int r = x / n_bmax, sl = x - r * n_bmax;
-    if (sl >= bsize[r]) continue;
-    const int kx = table[tseq + bstart[r] + sl];
-    if (kx >= n_sink && kx < w0) atomicOr(&emask[r], 1ull << sl);
-  }
-  __syncthreads();
+  constexpr int OWN = SEM_PMAX / NT;  // buckets a thread owns, at most
   const int per = (nk + NT - 1) / NT;
+  int o_start[OWN], o_size[OWN];
+  unsigned long long o_mask[OWN];
   int run = 0;
-  for (int e = 0; e < per; ++e) {
+#pragma unroll
+  for (int e = 0; e < OWN; ++e) {
     const int r = t * per + e;
-    if (r < nk) {
-      avail[r] = __popcll(emask[r]);
-      run += avail[r];
+    o_start[e] = 0;
+    o_size[e] = 0;
+    o_mask[e] = 0ull;
+    if (e >= per || r >= nk) continue;
+    const int gid = (int)(0xFFFFFFFFu - (unsigned)(K[r] & 0xFFFFFFFFull));
+    const int blk = gid / m, loc = gid - blk * m;
+    const int* ob = offs + ((long long)b * NB + blk) * (m + 1);
+    const int o0 = ob[loc], o1 = ob[loc + 1];
+    o_start[e] = blk * n_cluster + o0;
+    o_size[e] = o1 - o0;
+    const int* tb = table + tseq + o_start[e];
+    unsigned long long msk = 0ull;
+    for (int base = 0; base < o_size[e]; base += 8) {
+      int v[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) v[x] = base + x < o_size[e] ? tb[base + x] : -1;
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+        if (v[x] >= n_sink && v[x] < w0) msk |= 1ull << (base + x);
     }
+    o_mask[e] = msk;
+    run += __popcll(msk);
   }
   int total;
-  int pre = block_exclusive_scan<NT>(run, scan_tmp, &total);
-  for (int e = 0; e < per; ++e) {
-    const int r = t * per + e;
-    if (r < nk) {
-      excl[r] = pre;
-      pre += avail[r];
-    }
-  }
-  __syncthreads();
+  const int pre = block_exclusive_scan<NT>(run, scan_tmp, &total);
 
   // 4. long-range keys: whole buckets before the cut, the first keys of the one at it
   //    (a key's rank among its bucket's eligible keys is the mask's count below it)
   const int n_lr = total < k ? total : k;
-  for (int x = t; x < nk * n_bmax; x += NT) {
-    const int r = x / n_bmax, sl = x - r * n_bmax;
-    const int e0 = excl[r];
-    if (e0 >= k) continue;
-    const unsigned long long em = emask[r];
-    if (!((em >> sl) & 1ull)) continue;
-    const int rank = __popcll(em & ((1ull << sl) - 1ull));
-    if (rank >= k - e0) continue;
-    const int kx = table[tseq + bstart[r] + sl];
-    atomicOr(&lbm[kx >> 5], 1u << (kx & 31));
+  int e0 = pre;
+#pragma unroll
+  for (int e = 0; e < OWN; ++e) {
+    const unsigned long long msk = o_mask[e];
+    const int av = __popcll(msk);
+    if (e0 < k && msk != 0ull) {
+      const int take = av < k - e0 ? av : k - e0;
+      const int* tb = table + tseq + o_start[e];
+      for (int base = 0; base < o_size[e]; base += 8) {
+        int v[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) v[x] = base + x < o_size[e] ? tb[base + x] : -1;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int sl = base + x;
+          if (sl < o_size[e] && ((msk >> sl) & 1ull) && __popcll(msk & ((1ull << sl) - 1ull)) < take)
+            atomicOr(&lbm[v[x] >> 5], 1u << (v[x] & 31));
+        }
+      }
+    }
+    e0 += av;
   }
   __syncthreads();
   const int n_s = n_sink < w0 ? n_sink : w0;
@@ -769,32 +829,34 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
     const int rows = a.B * nqc;
     float* qn = static_cast<float*>(a.ws);
     float* S = qn + (size_t)rows * SEM_D;
-    hipLaunchKernelGGL(sem_qnorm_kernel, dim3((rows + 255) / 256), dim3(256), 0, st,
-                       static_cast<const unsigned short*>(a.q_idx), a.n_q, i0, nqc, rows, qn);
     if (nqc == 1) {
       const int bpw = 4;
       dim3 grid((a.NB + 4 * bpw - 1) / (4 * bpw), 1, a.B);
-      hipLaunchKernelGGL(sem_score_kernel<1>, grid, dim3(256), 0, st, qn, a.q_pos, a.n_q, i0, nqc,
+      hipLaunchKernelGGL(sem_score_decode_kernel, grid, dim3(256), 0, st,
+                         static_cast<const unsigned short*>(a.q_idx), a.q_pos, a.n_q, i0,
                          static_cast<const unsigned short*>(a.cent), a.NB, m, a.sp.n_cluster, bpw, S, ld);
     } else {
+      hipLaunchKernelGGL(sem_qnorm_kernel, dim3((rows + 255) / 256), dim3(256), 0, st,
+                         static_cast<const unsigned short*>(a.q_idx), a.n_q, i0, nqc, rows, qn);
       constexpr int QT = 8;
       const int bpw = 4;
       dim3 grid((a.NB + 4 * bpw - 1) / (4 * bpw), (nqc + QT - 1) / QT, a.B);
       hipLaunchKernelGGL(sem_score_kernel<QT>, grid, dim3(256), 0, st, qn, a.q_pos, a.n_q, i0, nqc,
                          static_cast<const unsigned short*>(a.cent), a.NB, m, a.sp.n_cluster, bpw, S, ld);
     }
+    // rows in registers: one 1024-thread workgroup per row
     const long long n_max = (long long)a.NB * m, pos_max = (long long)a.NB * a.sp.n_cluster;
-    auto fits = [&](int C) {
-      return n_max <= (long long)SELR_NT * C && pos_max <= 32LL * 256 * C && a.sp.n_bmax <= 64;
+    auto fits = [&](int nt, int C) {
+      return n_max <= (long long)nt * C && pos_max <= 32LL * 256 * C && a.sp.n_bmax <= 64;
     };
-#define LSA_SEM_SEL(C)                                                                                          \
-  hipLaunchKernelGGL(sem_select_kernel<C>, dim3(nqc, a.B), dim3(SELR_NT), 0, st, S, ld, a.q_pos, a.n_q, i0, nqc, \
-                     a.table, a.offs, a.NB, m, a.sp.n_cluster, a.sp.n_bmax, a.k, a.p_top, a.n_sink, a.n_w, W, a.idx, \
-                     a.count)
-    if (fits(4)) LSA_SEM_SEL(4);
-    else if (fits(8)) LSA_SEM_SEL(8);
-    else if (fits(16)) LSA_SEM_SEL(16);
-    else if (fits(32)) LSA_SEM_SEL(32);
+#define LSA_SEM_SEL(NT, C)                                                                                     \
+  hipLaunchKernelGGL((sem_select_kernel<NT, C>), dim3(nqc, a.B), dim3(NT), 0, st, S, ld, a.q_pos, a.n_q, i0,     \
+                     nqc, a.table, a.offs, a.NB, m, a.sp.n_cluster, a.sp.n_bmax, a.k, a.p_top, a.n_sink, a.n_w, W, \
+                     a.idx, a.count)
+    if (fits(1024, 4)) LSA_SEM_SEL(1024, 4);
+    else if (fits(1024, 8)) LSA_SEM_SEL(1024, 8);
+    else if (fits(1024, 16)) LSA_SEM_SEL(1024, 16);
+    else if (fits(1024, 32)) LSA_SEM_SEL(1024, 32);
     else
       hipLaunchKernelGGL(sem_select_stream_kernel, dim3(nqc, a.B), dim3(SEL_NT), 0, st, S, ld, a.q_pos, a.n_q, i0,
                          nqc, a.table, a.offs, a.NB, m, a.sp.n_cluster, a.k, a.p_top, a.n_sink, a.n_w, W, a.idx,
