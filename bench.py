@@ -247,11 +247,12 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
 
 
 class SemStep:
-    """One pass of flat semantic search over the batch: lsa_semantic_select (index-query
-    normalisation, centroid scores, top-p and expansion) then lsa_sparse_attn over the
-    lists; with record=True a HIP event is recorded around each of the two calls on the
-    stream they run on.  The bucket cache is built before (a serving loop clusters each
-    block once, when it completes)."""
+    """One pass of flat semantic search over the batch: for a prefill chunk, the clustering
+    of the cluster blocks its keys complete; lsa_semantic_select (index-query
+    normalisation, centroid scores, top-p and expansion); lsa_sparse_attn over the lists.
+    With record=True a HIP event is recorded around each call on the stream they run on.
+    The cache of the blocks before the chunk is built beforehand (a serving loop
+    clusters each block once, when it completes)."""
 
     def __init__(self, lsa, torch, wl, inp, cache):
         self.lsa, self.torch, self.wl, self.inp, self.cache = lsa, torch, wl, inp, cache
@@ -261,7 +262,16 @@ class SemStep:
         self.count = torch.empty((wl.B, wl.n_q), dtype=torch.int32, device=dev)
         self.ws = torch.empty((max(16, lsa.lsa_semantic_workspace_size(wl.B, wl.n_q, cache)),), dtype=torch.uint8,
                               device=dev)
-        self.names = ["semantic_select", "sparse_attn"]
+        # a prefill chunk first clusters the blocks its own keys complete (its later
+        # queries score them); decode clusters one block per n_cluster tokens, reported
+        # apart as an amortised cost
+        self.chunk_blocks = None
+        if wl.n_q > 1:
+            first = wl.q_pos0 // wl.n_cluster
+            last = min(wl.L, wl.q_pos0 + wl.n_q) // wl.n_cluster
+            if last > first:
+                self.chunk_blocks = (first, last - first)
+        self.names = (["cluster"] if self.chunk_blocks else []) + ["semantic_select", "sparse_attn"]
         self.pool, self.steps = [], []
 
     make_events = Step.make_events
@@ -275,16 +285,24 @@ class SemStep:
         evs = self.pool[len(self.steps)] if record else None
         st = self.torch.cuda.current_stream()
         wl = self.wl
+        e = 0
         if record:
-            evs[0].record(st)
+            evs[e].record(st)
+        if self.chunk_blocks:
+            self.lsa.lsa_semantic_cache(self.inp["k_sem"], cache=self.cache, first_block=self.chunk_blocks[0],
+                                        n_update=self.chunk_blocks[1])
+            if record:
+                e += 1
+                evs[e].record(st)
         self.lsa.lsa_semantic_select(self.inp["q_sem"], self.inp["q_pos"], self.cache, wl.k, wl.p_top, wl.n_sink,
                                      wl.n_cluster, idx=self.idx, count=self.count, ws=self.ws)
         if record:
-            evs[1].record(st)
+            e += 1
+            evs[e].record(st)
         self.out, _ = self.lsa.lsa_sparse_attn(self.inp["q"], self.inp["k"], self.inp["v"], self.idx,
                                                scale=wl.scale, return_lse=False)
         if record:
-            evs[2].record(st)
+            evs[e + 1].record(st)
             self.steps.append([(n, evs[i], evs[i + 1]) for i, n in enumerate(self.names)])
 
 

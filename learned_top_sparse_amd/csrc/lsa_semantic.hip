@@ -52,35 +52,47 @@ __device__ __forceinline__ void unpack8(uint4 v, float* x) {
 }
 
 // ---------------------------------------------------------------------------------
-// Clustering: one 256-thread workgroup per (cluster block, sequence).  The block's
-// pool keys (sums of its normalised keys), the bucket sums and the Ward cost of every
-// pair stay in LDS for all merge rounds; only the rows of merged buckets are
-// recomputed after a round.
+// Clustering: one 1024-thread workgroup per (cluster block, sequence), 8 threads per
+// pool key / bucket row.  The block's pool keys (sums of its normalised keys), the
+// bucket sums and the Ward cost of every pair stay in LDS for all merge rounds; only
+// the costs against merged buckets are recomputed after a round.
 
 struct SemGeom {
   int n_cluster, n_pool, npk, m, cap;  // cap: size cap in pool keys
 };
 
-// Ward's cost of buckets a, b: |n_b S_a - n_a S_b|^2 / (n_a n_b (n_a + n_b))
-__device__ __forceinline__ float ward_cost(const float (*S)[SEM_D + 1], const int* cnt, int a, int b) {
-  const float na = (float)cnt[a], nb = (float)cnt[b];
-  float sq = 0.f;
-#pragma unroll 16
+// Ward's cost of buckets a, b: |n_b S_a - n_a S_b|^2 / (n_a n_b (n_a + n_b)).  Four
+// costs of bucket a at once, each summed d = 0, 1, ... on its own chain, so the order
+// of every rounding is that of one cost at a time.
+__device__ __forceinline__ void ward_cost4(const float (*S)[SEM_D + 1], int a, float na, const int* bb,
+                                           const float* nb, float* out) {
+  float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int d = 0; d < SEM_D; ++d) {
-    const float df = nb * S[a][d] - na * S[b][d];
-    sq = sq + df * df;
+    const float sad = S[a][d];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float df = nb[e] * sad - na * S[bb[e]][d];
+      sq[e] = sq[e] + df * df;
+    }
   }
-  return sq / (na * nb * (na + nb));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[e] = sq[e] / (na * nb[e] * (na + nb[e]));
 }
 
-__global__ __launch_bounds__(256) void sem_cluster_kernel(const unsigned short* __restrict__ kidx, long long seq_elems,
-                                                          SemGeom g, int first_block, int NB,
-                                                          unsigned short* __restrict__ cent, int* __restrict__ table,
-                                                          int* __restrict__ offs) {
+constexpr int CL_NT = 1024;            // threads of the clustering workgroup
+constexpr int CL_SLOTS = CL_NT / SEM_NPK;  // threads per pool key / bucket row
+
+__global__ __launch_bounds__(CL_NT) void sem_cluster_kernel(const unsigned short* __restrict__ kidx,
+                                                            long long seq_elems, SemGeom g, int first_block, int NB,
+                                                            unsigned short* __restrict__ cent,
+                                                            int* __restrict__ table, int* __restrict__ offs) {
   __shared__ float S[SEM_NPK][SEM_D + 1];
   __shared__ float C[SEM_NPK][SEM_NPK + 1];
   __shared__ int cnt[SEM_NPK], lab[SEM_NPK], partner[SEM_NPK], into[SEM_NPK], off_of[SEM_NPK];
   __shared__ float pcost[SEM_NPK];
+  __shared__ float bcost[CL_SLOTS][SEM_NPK];
+  __shared__ int bidx[CL_SLOTS][SEM_NPK];
   __shared__ int pa[SEM_NPK / 2], pb[SEM_NPK / 2], keep[SEM_NPK / 2];
   __shared__ float pc[SEM_NPK / 2];
   __shared__ int id_of_rank[SEM_SLOTS];
@@ -90,28 +102,32 @@ __global__ __launch_bounds__(256) void sem_cluster_kernel(const unsigned short* 
   const int blk = first_block + blockIdx.x;
   const int b = blockIdx.y;
   const int npk = g.npk;
+  const int row = t & (SEM_NPK - 1), slot = t >> 7;  // a bucket row and one of its CL_SLOTS threads
   const unsigned short* kb = kidx + (long long)b * seq_elems + (long long)blk * g.n_cluster * SEM_D;
 
-  // 1. pool keys: the block's keys normalised and summed n_pool at a time, in key order
-  if (t < npk) {
-    float P[SEM_D];
+  // 1. pool keys: the block's keys normalised and summed n_pool at a time, in key order;
+  //    each of a pool key's 8 threads divides its 8 dims (the norm needs all 64)
+  if (row < npk) {
+    float P[8];
     for (int i = 0; i < g.n_pool; ++i) {
-      const uint4* row = reinterpret_cast<const uint4*>(kb + (long long)(t * g.n_pool + i) * SEM_D);
+      const uint4* kr = reinterpret_cast<const uint4*>(kb + (long long)(row * g.n_pool + i) * SEM_D);
       float x[SEM_D];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) unpack8(row[c], x + 8 * c);
+      for (int c = 0; c < 8; ++c) unpack8(kr[c], x + 8 * c);
       float ss = 0.f;
 #pragma unroll
       for (int d = 0; d < SEM_D; ++d) ss = ss + x[d] * x[d];
       const float nrm = sqrtf(ss);
+      float xs[8];  // this thread's 8 dims, reloaded (a runtime index into x would spill)
+      unpack8(kr[slot], xs);
 #pragma unroll
-      for (int d = 0; d < SEM_D; ++d) {
-        const float y = nrm > 0.f ? x[d] / nrm : 0.f;
-        P[d] = i == 0 ? y : P[d] + y;
+      for (int e = 0; e < 8; ++e) {
+        const float y = nrm > 0.f ? xs[e] / nrm : 0.f;
+        P[e] = i == 0 ? y : P[e] + y;
       }
     }
 #pragma unroll
-    for (int d = 0; d < SEM_D; ++d) S[t][d] = P[d];
+    for (int e = 0; e < 8; ++e) S[row][8 * slot + e] = P[e];
   }
   if (t < SEM_NPK) {
     cnt[t] = t < npk ? 1 : 0;
@@ -119,45 +135,76 @@ __global__ __launch_bounds__(256) void sem_cluster_kernel(const unsigned short* 
   }
   __syncthreads();
 
-  // 2. cost of every ordered pair (both triangles; the formula is symmetric bit for bit)
-  {
-    const int a = t & (SEM_NPK - 1);
-    if (a < npk)
-      for (int bb = t >> 7; bb < npk; bb += 2)
-        if (bb != a) C[a][bb] = ward_cost(S, cnt, a, bb);
+  // 2. cost of every ordered pair (both triangles; the formula is symmetric bit for bit):
+  //    thread (row, slot) takes columns slot, slot + 8, ..., four at a time
+  if (row < npk) {
+    for (int c0 = slot; c0 < npk; c0 += 4 * CL_SLOTS) {
+      int bb[4];
+      float nb[4], out[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = c0 + e * CL_SLOTS;
+        bb[e] = c < npk ? c : row;
+        nb[e] = 1.f;
+      }
+      ward_cost4(S, row, 1.f, bb, nb, out);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (bb[e] != row) C[row][bb[e]] = out[e];
+    }
   }
   __syncthreads();
 
   // 3. merge rounds
   int live = npk;
   while (live > g.m) {
-    if (t < npk) {
+    // cheapest allowed partner of every bucket: each of its 8 threads scans 16 columns
+    // in order, then the lowest (cost, column) of the 8 in slot order
+    if (row < npk) {
       int bi = -1;
       float best = 0.f;
-      const int ca = cnt[t];
-      if (ca > 0)
-        for (int bb = 0; bb < npk; ++bb) {
-          const int cb = cnt[bb];
-          if (bb == t || cb == 0 || ca + cb > g.cap) continue;
-          const float c = C[t][bb];
+      const int ca = cnt[row];
+      if (ca > 0) {
+        const int c_end = (slot + 1) * (SEM_NPK / CL_SLOTS) < npk ? (slot + 1) * (SEM_NPK / CL_SLOTS) : npk;
+        for (int bb = slot * (SEM_NPK / CL_SLOTS); bb < c_end; ++bb) {
+          const int cbb = cnt[bb];
+          if (bb == row || cbb == 0 || ca + cbb > g.cap) continue;
+          const float c = C[row][bb];
           if (bi < 0 || c < best) {
             best = c;
             bi = bb;
           }
         }
-      partner[t] = bi;
-      pcost[t] = best;
-      into[t] = -1;
+      }
+      bcost[slot][row] = best;
+      bidx[slot][row] = bi;
     }
     if (t == 0) sh_np = 0;
     __syncthreads();
     if (t < npk) {
+      int bi = -1;
+      float best = 0.f;
+      for (int sl = 0; sl < CL_SLOTS; ++sl) {
+        const int i2 = bidx[sl][t];
+        if (i2 < 0) continue;
+        const float c = bcost[sl][t];
+        if (bi < 0 || c < best) {
+          best = c;
+          bi = i2;
+        }
+      }
+      partner[t] = bi;
+      pcost[t] = best;
+      into[t] = -1;
+    }
+    __syncthreads();
+    if (t < npk) {
       const int bb = partner[t];
       if (bb > t && partner[bb] == t) {
-        const int s = atomicAdd(&sh_np, 1);
-        pa[s] = t;
-        pb[s] = bb;
-        pc[s] = pcost[t];
+        const int s2 = atomicAdd(&sh_np, 1);
+        pa[s2] = t;
+        pb[s2] = bb;
+        pc[s2] = pcost[t];
       }
     }
     __syncthreads();
@@ -173,9 +220,9 @@ __global__ __launch_bounds__(256) void sem_cluster_kernel(const unsigned short* 
       keep[t] = rk < need;
     }
     __syncthreads();
-    for (int x = t; x < np * SEM_D; x += 256) {
-      const int s = x >> 6, d = x & (SEM_D - 1);
-      if (keep[s]) S[pa[s]][d] = S[pa[s]][d] + S[pb[s]][d];
+    for (int x = t; x < np * SEM_D; x += CL_NT) {
+      const int s2 = x >> 6, d = x & (SEM_D - 1);
+      if (keep[s2]) S[pa[s2]][d] = S[pa[s2]][d] + S[pb[s2]][d];
     }
     if (t < np && keep[t]) {
       into[pb[t]] = pa[t];
@@ -188,19 +235,32 @@ __global__ __launch_bounds__(256) void sem_cluster_kernel(const unsigned short* 
       if (l >= 0) lab[t] = l;
     }
     live -= np < need ? np : need;
-    // costs of the merged buckets against every live bucket
-    for (int x = t; x < np * npk; x += 256) {
-      const int s = x / npk, j = x - s * npk;
-      const int a = pa[s];
-      if (keep[s] && cnt[j] > 0 && j != a) {
-        const float c = ward_cost(S, cnt, a, j);
-        C[a][j] = c;
-        C[j][a] = c;
+    // costs of every live bucket against the merged ones: thread (row, slot) takes
+    // merged pairs slot, slot + 8, ..., four at a time
+    if (row < npk && cnt[row] > 0) {
+      const float na = (float)cnt[row];
+      for (int s0 = slot; s0 < np; s0 += 4 * CL_SLOTS) {
+        int bb[4];
+        float nb[4], out[4];
+        bool use[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s2 = s0 + e * CL_SLOTS;
+          use[e] = s2 < np && keep[s2] && pa[s2] != row;
+          bb[e] = use[e] ? pa[s2] : row;
+          nb[e] = (float)cnt[bb[e]];
+        }
+        ward_cost4(S, row, na, bb, nb, out);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (use[e]) {
+            C[row][bb[e]] = out[e];
+            C[bb[e]][row] = out[e];
+          }
       }
     }
     __syncthreads();
   }
-
   // 4. the cache entry: buckets in id order, their keys ascending
   if (t < npk && cnt[t] > 0) {
     int r = 0, o = 0;
@@ -806,7 +866,7 @@ hipError_t launch_sem_cluster(const void* k_idx, int B, int L_max, const SemPara
   g.m = sp.n_cluster / sp.n_bavg;
   g.cap = sp.n_bmax / sp.n_pool;
   dim3 grid(n_update, B);
-  hipLaunchKernelGGL(sem_cluster_kernel, grid, dim3(256), 0, st, static_cast<const unsigned short*>(k_idx),
+  hipLaunchKernelGGL(sem_cluster_kernel, grid, dim3(CL_NT), 0, st, static_cast<const unsigned short*>(k_idx),
                      (long long)L_max * SEM_D, g, first_block, NB, static_cast<unsigned short*>(cent), table, offs);
   return hipGetLastError();
 }
