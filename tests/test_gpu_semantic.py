@@ -213,3 +213,55 @@ def test_decode_128k_lsa_sampled(lsa):
         r = oracle.semantic_select_row(_f32(inp["q_sem"][b, 0]), oc, p, wl.k, wl.p_top, wl.n_sink, wl.n_cluster)
         assert np.array_equal(idx[b, 0].cpu().numpy(), r["J"]), f"seq {b}"
         assert int(cnt[b, 0]) == r["count"] == wl.n_sink + wl.k + wl.n_cluster
+
+
+def test_semantic_decode_graph_replay(lsa):
+    """A semantic decode step (selection + attention) captured once in a HIP graph, with
+    the cache sized for the longest context, replays for new positions and new index
+    queries written into the captured inputs and after a block is clustered into the
+    cache between replays; every replay equals an eager call bit for bit."""
+    prm = (512, 4, 8, 32)
+    k, p_top, n_sink = 256, 64, 4
+    L = 24 * 512 + 1
+    wl = synthetic.Workload("sgraph", B=4, n_q=1, L=L, q_pos0=L - 1, H_I=1, d_I=64, k=k, H_q=16, semantic=True,
+                            p_top=p_top, n_sink=n_sink)
+    g = synthetic.make_inputs(wl, dev())
+    g.update(synthetic.semantic_inputs(wl, dev(), seed=9))
+    g["q_pos"].copy_(torch.tensor([[L - 1], [9000], [600], [5000]], dtype=torch.int32, device=dev()))
+    cache = lsa.lsa_semantic_cache(g["k_sem"][:, :20 * 512].contiguous(), *prm, n_blocks=24)
+    W = n_sink + k + prm[0]
+    idx = torch.empty((4, 1, W), dtype=torch.int32, device=dev())
+    cnt = torch.empty((4, 1), dtype=torch.int32, device=dev())
+    ws = torch.empty((lsa.lsa_semantic_workspace_size(4, 1, cache),), dtype=torch.uint8, device=dev())
+
+    def step():
+        lsa.lsa_semantic_select(g["q_sem"], g["q_pos"], cache, k, p_top, n_sink, prm[0], idx=idx, count=cnt, ws=ws)
+        return lsa.lsa_sparse_attn(g["q"], g["k"], g["v"], idx, scale=wl.scale)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out, lse = step()
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(11)
+    for trial in range(4):
+        if trial == 2:   # the next block completes: cluster it into the cache
+            lsa.lsa_semantic_cache(g["k_sem"], cache=cache, first_block=20, n_update=4)
+        hi = 20 * 512 if trial < 2 else L
+        g["q_pos"].copy_(torch.randint(0, hi, (4, 1), generator=gen, dtype=torch.int32).to(dev()))
+        g["q_sem"].copy_((g["q_sem"].float() + 0.25 * torch.randn(g["q_sem"].shape, generator=gen).to(dev()))
+                         .to(torch.bfloat16))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (idx.clone(), cnt.clone(), out.clone(), lse.clone())
+        want_idx, want_cnt = lsa.lsa_semantic_select(g["q_sem"], g["q_pos"], cache, k, p_top, n_sink, prm[0])
+        want_out, want_lse = lsa.lsa_sparse_attn(g["q"], g["k"], g["v"], want_idx, scale=wl.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], want_idx) and torch.equal(got[1], want_cnt), f"replay {trial}: lists"
+        assert torch.equal(got[2], want_out) and torch.equal(got[3], want_lse), f"replay {trial}: attention"
