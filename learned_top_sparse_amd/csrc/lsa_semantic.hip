@@ -659,8 +659,8 @@ struct SelLbm {
   static constexpr int WORDS = 256 * C;  // positions < 8192 * C: n_bavg = 8 fills it
 };
 
-template <int NT, int C>
-__global__ __launch_bounds__(NT) void sem_select_kernel(const float* __restrict__ S, long long ld,
+template <int NT, int C, int MINW>
+__global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __restrict__ S, long long ld,
                                                              const int* __restrict__ q_pos, int n_q, int i0, int nqc,
                                                              const int* __restrict__ table,
                                                              const int* __restrict__ offs, int NB, int m,
@@ -904,19 +904,25 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(sem_score_kernel<QT>, grid, dim3(256), 0, st, qn, a.q_pos, a.n_q, i0, nqc,
                          static_cast<const unsigned short*>(a.cent), a.NB, m, a.sp.n_cluster, bpw, S, ld);
     }
-    // rows in registers: one 1024-thread workgroup per row
+    // rows in registers: one 1024-thread workgroup per row; with enough rows to fill
+    // the chip twice, a variant held to 64 VGPRs (8 waves per SIMD) runs two
+    // workgroups per compute unit
+    const bool many = (long long)a.B * nqc >= 512;
     const long long n_max = (long long)a.NB * m, pos_max = (long long)a.NB * a.sp.n_cluster;
     auto fits = [&](int nt, int C) {
       return n_max <= (long long)nt * C && pos_max <= 32LL * 256 * C && a.sp.n_bmax <= 64;
     };
-#define LSA_SEM_SEL(NT, C)                                                                                     \
-  hipLaunchKernelGGL((sem_select_kernel<NT, C>), dim3(nqc, a.B), dim3(NT), 0, st, S, ld, a.q_pos, a.n_q, i0,     \
-                     nqc, a.table, a.offs, a.NB, m, a.sp.n_cluster, a.sp.n_bmax, a.k, a.p_top, a.n_sink, a.n_w, W, \
-                     a.idx, a.count)
-    if (fits(1024, 4)) LSA_SEM_SEL(1024, 4);
-    else if (fits(1024, 8)) LSA_SEM_SEL(1024, 8);
-    else if (fits(1024, 16)) LSA_SEM_SEL(1024, 16);
-    else if (fits(1024, 32)) LSA_SEM_SEL(1024, 32);
+#define LSA_SEM_SEL(NT, C, MINW)                                                                               \
+  hipLaunchKernelGGL((sem_select_kernel<NT, C, MINW>), dim3(nqc, a.B), dim3(NT), 0, st, S, ld, a.q_pos, a.n_q,   \
+                     i0, nqc, a.table, a.offs, a.NB, m, a.sp.n_cluster, a.sp.n_bmax, a.k, a.p_top, a.n_sink, a.n_w, \
+                     W, a.idx, a.count)
+    if (many && fits(1024, 4)) LSA_SEM_SEL(1024, 4, 8);
+    else if (many && fits(1024, 8)) LSA_SEM_SEL(1024, 8, 8);
+    else if (many && fits(1024, 16)) LSA_SEM_SEL(1024, 16, 8);
+    else if (fits(1024, 4)) LSA_SEM_SEL(1024, 4, 1);
+    else if (fits(1024, 8)) LSA_SEM_SEL(1024, 8, 1);
+    else if (fits(1024, 16)) LSA_SEM_SEL(1024, 16, 1);
+    else if (fits(1024, 32)) LSA_SEM_SEL(1024, 32, 1);
     else
       hipLaunchKernelGGL(sem_select_stream_kernel, dim3(nqc, a.B), dim3(SEL_NT), 0, st, S, ld, a.q_pos, a.n_q, i0,
                          nqc, a.table, a.offs, a.NB, m, a.sp.n_cluster, a.k, a.p_top, a.n_sink, a.n_w, W, a.idx,

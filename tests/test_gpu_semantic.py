@@ -168,6 +168,48 @@ def test_semantic_forward_small(lsa):
     err.check()
 
 
+def test_select_many_rows(lsa):
+    """A prefill chunk of 600 queries (enough rows for the two-workgroups-per-CU
+    selection): sampled rows, first and last included, bit for bit."""
+    prm = (512, 4, 8, 32)
+    L = 12 * 512 + 30
+    wl = synthetic.Workload("sem_chunk", B=1, n_q=600, L=L, q_pos0=L - 600, H_I=1, d_I=64, k=300, H_q=16,
+                            semantic=True, p_top=64, n_sink=4)
+    inp = synthetic.semantic_inputs(wl, dev(), seed=10)
+    cache = lsa.lsa_semantic_cache(inp["k_sem"], *prm)
+    idx, cnt = lsa.lsa_semantic_select(inp["q_sem"], inp["q_pos"], cache, wl.k, wl.p_top, wl.n_sink, prm[0])
+    torch.cuda.synchronize()
+    oc = _oracle_cache(inp["k_sem"][0], prm, n_blocks=cache["table"].shape[1])
+    for i in [0, 1, 77, 150, 299, 300, 451, 598, 599] + list(range(5, 600, 41)):
+        p = int(inp["q_pos"][0, i])
+        r = oracle.semantic_select_row(_f32(inp["q_sem"][0, i]), oc, p, wl.k, wl.p_top, wl.n_sink, prm[0])
+        assert np.array_equal(idx[0, i].cpu().numpy(), r["J"]), f"i={i} p={p}"
+        assert int(cnt[0, i]) == r["count"]
+
+
+@pytest.mark.slow
+def test_prefill_128k_lsa_sampled(lsa):
+    """The prefill workload at full size (8192 queries of a 128K context) as the benchmark
+    runs it: the cache of the blocks before the chunk, then the chunk's own 16 blocks
+    clustered into it, then the selection; sampled rows against the oracle's clustering."""
+    wl = synthetic.WORKLOADS["prefill_128k_lsa"]
+    prm = (wl.n_cluster, wl.n_pool, wl.n_bavg, wl.n_bmax)
+    inp = synthetic.semantic_inputs(wl, dev())
+    first = wl.q_pos0 // wl.n_cluster
+    cache = lsa.lsa_semantic_cache(inp["k_sem"][:, :wl.q_pos0].contiguous(), *prm, n_blocks=wl.L // wl.n_cluster)
+    cache = lsa.lsa_semantic_cache(inp["k_sem"], cache=cache, first_block=first,
+                                   n_update=wl.L // wl.n_cluster - first)
+    idx, cnt = lsa.lsa_semantic_select(inp["q_sem"], inp["q_pos"], cache, wl.k, wl.p_top, wl.n_sink, wl.n_cluster)
+    torch.cuda.synchronize()
+    print("[prefill_128k_lsa] oracle cache", flush=True)
+    oc = _oracle_cache(inp["k_sem"][0], prm, n_blocks=cache["table"].shape[1])
+    for i in (0, 1, 511, 512, 4000, 8190, 8191):
+        p = int(inp["q_pos"][0, i])
+        r = oracle.semantic_select_row(_f32(inp["q_sem"][0, i]), oc, p, wl.k, wl.p_top, wl.n_sink, wl.n_cluster)
+        assert np.array_equal(idx[0, i].cpu().numpy(), r["J"]), f"i={i} p={p}"
+        assert int(cnt[0, i]) == r["count"]
+
+
 @pytest.mark.slow
 def test_select_long_rows(lsa):
     """Rows of more buckets than the register-held selection takes (37440 > 32768): the
