@@ -889,7 +889,9 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
     const int rows = a.B * nqc;
     float* qn = static_cast<float*>(a.ws);
     float* S = qn + (size_t)rows * SEM_D;
-    if (nqc == 1) {
+    if (a.NB == 0) {
+      // an empty cache: nothing to score, every list is the sink and the window
+    } else if (nqc == 1) {
       const int bpw = 4;
       dim3 grid((a.NB + 4 * bpw - 1) / (4 * bpw), 1, a.B);
       hipLaunchKernelGGL(sem_score_decode_kernel, grid, dim3(256), 0, st,

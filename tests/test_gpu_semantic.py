@@ -131,6 +131,25 @@ def test_select_matches_oracle(lsa, prm, k, p_top, n_sink, n_w):
             assert int(cnt[b, i]) == r["count"], f"count b={b} p={p}"
 
 
+def test_select_empty_cache(lsa):
+    """A cache of no blocks (contexts shorter than one cluster block): every list is the
+    sink and the window, as the oracle's."""
+    prm = (512, 4, 8, 32)
+    wl = synthetic.WORKLOADS["decode_128k_lsa"].replace(B=2, L=500, q_pos0=499)
+    inp = synthetic.semantic_inputs(wl, dev(), seed=12)
+    cache = lsa.lsa_semantic_cache(inp["k_sem"], *prm)
+    assert cache["table"].shape[1] == 0
+    q_pos = torch.tensor([[499, 3], [0, -1]], dtype=torch.int32, device=dev())
+    q = inp["q_sem"].expand(2, 2, 64).contiguous()
+    idx, cnt = lsa.lsa_semantic_select(q, q_pos, cache, 100, 16, 4, 512)
+    torch.cuda.synchronize()
+    oc = _oracle_cache(inp["k_sem"][0], prm, n_blocks=0)
+    for b in range(2):
+        for i in range(2):
+            r = oracle.semantic_select_row(_f32(q[b, i]), oc, int(q_pos[b, i]), 100, 16, 4, 512)
+            assert np.array_equal(idx[b, i].cpu().numpy(), r["J"]) and int(cnt[b, i]) == r["count"]
+
+
 def test_select_in_chunks(lsa):
     """A workspace for one query per sequence: the call runs in chunks, same lists."""
     prm = (512, 4, 8, 32)
