@@ -900,7 +900,7 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
     } else {
       hipLaunchKernelGGL(sem_qnorm_kernel, dim3((rows + 255) / 256), dim3(256), 0, st,
                          static_cast<const unsigned short*>(a.q_idx), a.n_q, i0, nqc, rows, qn);
-      constexpr int QT = 8;
+      constexpr int QT = 16;
       const int bpw = 4;
       dim3 grid((a.NB + 4 * bpw - 1) / (4 * bpw), (nqc + QT - 1) / QT, a.B);
       hipLaunchKernelGGL(sem_score_kernel<QT>, grid, dim3(256), 0, st, qn, a.q_pos, a.n_q, i0, nqc,
