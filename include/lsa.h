@@ -193,6 +193,15 @@ lsa_status lsa_sparse_attn(const void* q, const void* k, const void* v, const in
                            float scale, int32_t n_split, void* out, float* lse,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* The same attention over shared K/V pools (paged caches): k_pool, v_pool bf16
+   [n_slots, d] hold every sequence's keys and idx entries are pool rows (entries outside
+   [0, n_slots) and -1 are skipped) -- the lists of lsa_forward or lsa_semantic_select_paged
+   with a page table.  Same support and workspace as lsa_sparse_attn. */
+lsa_status lsa_sparse_attn_pool(const void* q, const void* k_pool, const void* v_pool, const int32_t* idx,
+                                int32_t B, int32_t n_q, int64_t n_slots, int32_t H_q, int32_t d, int32_t k,
+                                float scale, int32_t n_split, void* out, float* lse, void* ws, size_t ws_bytes,
+                                void* stream);
+
 /*
  * The whole path in one call ([LSA] §2; [HISA] for two_stage):
  *   PREFILL flat:      per chunk of query rows: index_scores -> topk -> sparse_attn
@@ -365,6 +374,40 @@ lsa_status lsa_semantic_cluster(const void* k_idx, int32_t B, int32_t L_max, int
                                 int32_t n_update, void* centroids, int32_t* table, int32_t* offsets,
                                 void* stream);
 
+/*
+ * Paged storage for the semantic search (serving layout; [LSA] App. F.1 "Flat decode": a
+ * request's centroids lie in pages of the bucket cache and its keys in pages of the KV
+ * cache, read through its page tables).  Either part may be NULL.
+ *   block_table != NULL: the cache arrays of lsa_semantic_cluster/_select are pools of
+ *     n_bslots entries (centroids bf16 [n_bslots, 8, 64, 8], table int32
+ *     [n_bslots, n_cluster], offsets int32 [n_bslots, m + 1]) and block t of sequence b
+ *     lives in entry block_table[b * n_blocks + t] (int32 [B, n_blocks]).  Table entries
+ *     stay logical key positions.
+ *   page_table != NULL: index keys (and, for the attention, K and V) are pools of n_slots
+ *     rows, logical key j of sequence b at row page_table[b * max_pages + j / page_size]
+ *     * page_size + j % page_size (page_size a power of two >= 64, L_max = max_pages *
+ *     page_size, n_slots a multiple of page_size, at most 2^31); the index lists then hold
+ *     those pool rows, in ascending logical order -- what lsa_sparse_attn reads from pools.
+ * Ids outside their pools are clamped into them (no fault; the result is then
+ * unspecified).
+ */
+typedef struct lsa_semantic_pages {
+  const int32_t* block_table; /* int32 [B, n_blocks] or NULL */
+  int32_t n_bslots;
+  const int32_t* page_table;  /* int32 [B, max_pages] or NULL */
+  int32_t page_size;
+  int32_t max_pages;
+  int64_t n_slots;
+} lsa_semantic_pages;
+
+/* lsa_semantic_cluster over paged storage (pages != NULL; see lsa_semantic_pages): with a
+   page table, k_idx is the index-key pool bf16 [n_slots, 64] and L_max = max_pages *
+   page_size. */
+lsa_status lsa_semantic_cluster_paged(const void* k_idx, int32_t B, int32_t L_max, int32_t d_idx,
+                                      const lsa_semantic_params* prm, const lsa_semantic_pages* pages,
+                                      int32_t n_blocks, int32_t first_block, int32_t n_update, void* centroids,
+                                      int32_t* table, int32_t* offsets, void* stream);
+
 /* Workspace lsa_semantic_select needs to take all B * n_q queries in one pass: per
    query its normalised index query and one score-table row of n_blocks * m floats.
    Less (at least one query per sequence) is accepted: the call then runs in chunks of
@@ -389,6 +432,15 @@ lsa_status lsa_semantic_select(const void* q_idx, const int32_t* q_pos, int32_t 
                                const int32_t* table, const int32_t* offsets, int32_t k, int32_t p_top,
                                int32_t n_sink, int32_t n_w, int32_t* idx, int32_t* count, void* ws,
                                size_t ws_bytes, void* stream);
+
+/* lsa_semantic_select over paged storage (pages != NULL; see lsa_semantic_pages): the
+   cache is read through the block table, and with a page table the lists hold pool rows
+   (L_max = max_pages * page_size).  Same lists as the contiguous call, mapped. */
+lsa_status lsa_semantic_select_paged(const void* q_idx, const int32_t* q_pos, int32_t B, int32_t n_q, int32_t d_idx,
+                                     const lsa_semantic_params* prm, const lsa_semantic_pages* pages, int32_t L_max,
+                                     int32_t n_blocks, const void* centroids, const int32_t* table,
+                                     const int32_t* offsets, int32_t k, int32_t p_top, int32_t n_sink, int32_t n_w,
+                                     int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,7 @@ EXPORTED = [
     "lsa_topk", "lsa_sparse_attn_workspace_size", "lsa_sparse_attn",
     "lsa_forward_workspace_size", "lsa_forward", "lsa_forward_plan", "lsa_forward_stages",
     "lsa_semantic_cluster", "lsa_semantic_select_workspace_size", "lsa_semantic_select",
+    "lsa_semantic_cluster_paged", "lsa_semantic_select_paged", "lsa_sparse_attn_pool",
 ]
 
 STAGE_NAMES = {1: "block_reps", 2: "block_prefilter", 3: "index_select", 4: "index_scores", 5: "topk", 7: "sample",
@@ -81,6 +82,7 @@ def lib():
         L.lsa_topk.argtypes = [P, I64, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
         L.lsa_sparse_attn_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, C.POINTER(SZ)]
         L.lsa_sparse_attn.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, C.c_float, I32, P, P, P, SZ, P]
+        L.lsa_sparse_attn_pool.argtypes = [P, P, P, P, I32, I32, I64, I32, I32, I32, C.c_float, I32, P, P, P, SZ, P]
         L.lsa_forward_workspace_size.argtypes = [C.POINTER(ForwardArgs), C.POINTER(SZ)]
         L.lsa_forward.argtypes = [C.POINTER(ForwardArgs), P, SZ, P]
         L.lsa_forward_plan.argtypes = [C.POINTER(ForwardArgs), SZ, C.POINTER(I64), C.POINTER(I32)]
@@ -89,6 +91,10 @@ def lib():
         L.lsa_semantic_cluster.argtypes = [P, I32, I32, I32, SP, I32, I32, I32, P, P, P, P]
         L.lsa_semantic_select_workspace_size.argtypes = [I32, I32, I32, SP, C.POINTER(SZ)]
         L.lsa_semantic_select.argtypes = [P, P, I32, I32, I32, SP, I32, P, P, P, I32, I32, I32, I32, P, P, P, SZ, P]
+        SG = C.POINTER(SemanticPages)
+        L.lsa_semantic_cluster_paged.argtypes = [P, I32, I32, I32, SP, SG, I32, I32, I32, P, P, P, P]
+        L.lsa_semantic_select_paged.argtypes = [P, P, I32, I32, I32, SP, SG, I32, I32, P, P, P, I32, I32, I32, I32,
+                                                 P, P, P, SZ, P]
         for name in EXPORTED:
             if name not in ("lsa_status_string", "lsa_version"):
                 getattr(L, name).restype = C.c_int
@@ -248,14 +254,17 @@ def lsa_topk(scores, q_pos, k: int, L_max: int, kept_blocks=None, block_size: in
 
 
 def lsa_sparse_attn(q, k, v, idx, scale: Optional[float] = None, n_split: int = 0, return_lse: bool = True):
-    """Sparse attention: (out bf16 [B, n_q, H_q, d], lse fp32 [B, n_q, H_q] or None)."""
+    """Sparse attention: (out bf16 [B, n_q, H_q, d], lse fp32 [B, n_q, H_q] or None).
+    k, v bf16 [B, L_max, d], or pools [n_slots, d] shared by all sequences (paged caches;
+    idx then holds pool rows: lsa_sparse_attn_pool)."""
     dev = q.device
     _need(q, "q", torch.bfloat16)
     _need(k, "k", torch.bfloat16, dev)
     _need(v, "v", torch.bfloat16, dev)
     _need(idx, "idx", torch.int32, dev)
     B, n_q, H_q, d = q.shape
-    L = k.shape[1]
+    pool = k.dim() == 2
+    L = k.shape[0] if pool else k.shape[1]
     k_top = idx.shape[-1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -265,9 +274,10 @@ def lsa_sparse_attn(q, k, v, idx, scale: Optional[float] = None, n_split: int = 
     _check("lsa_sparse_attn_workspace_size",
            lib().lsa_sparse_attn_workspace_size(B, n_q, H_q, d, k_top, n_split, C.byref(nb)))
     ws = _workspace(nb.value, dev)
-    st = lib().lsa_sparse_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), B, n_q, L, H_q, d, k_top, float(scale),
-                               n_split, _ptr(out), _ptr(lse), _ptr(ws), nb.value, _stream(dev))
-    _check("lsa_sparse_attn", st)
+    fn = "lsa_sparse_attn_pool" if pool else "lsa_sparse_attn"
+    st = getattr(lib(), fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), B, n_q, L, H_q, d, k_top, float(scale),
+                            n_split, _ptr(out), _ptr(lse), _ptr(ws), nb.value, _stream(dev))
+    _check(fn, st)
     return out, lse
 
 
@@ -407,46 +417,90 @@ class SemanticParams(C.Structure):
     _fields_ = [("n_cluster", I32), ("n_pool", I32), ("n_bavg", I32), ("n_bmax", I32)]
 
 
+class SemanticPages(C.Structure):
+    """lsa_semantic_pages of include/lsa.h."""
+    _fields_ = [("block_table", P), ("n_bslots", I32), ("page_table", P), ("page_size", I32),
+                ("max_pages", I32), ("n_slots", I64)]
+
+
+def _sem_pages(paged: Optional[dict], cache: dict, n_slots: int = 0):
+    """SemanticPages from ``paged`` = dict(block_table=int32 [B, NB] or None,
+    page_table=int32 [B, max_pages] or None, page_size=int), and the logical L_max."""
+    bt, pt = paged.get("block_table"), paged.get("page_table")
+    P_ = int(paged.get("page_size", 0)) if pt is not None else 0
+    mp = pt.shape[1] if pt is not None else 0
+    nbs = cache["table"].shape[0] if bt is not None else 0
+    return SemanticPages(_ptr(bt), nbs, _ptr(pt), P_, mp, n_slots if pt is not None else 0), mp * P_
+
+
 def lsa_semantic_cache(k_idx, n_cluster: int = 512, n_pool: int = 4, n_bavg: int = 8, n_bmax: int = 32,
                        n_blocks: Optional[int] = None, cache: Optional[dict] = None, first_block: int = 0,
-                       n_update: Optional[int] = None) -> dict:
+                       n_update: Optional[int] = None, paged: Optional[dict] = None,
+                       n_bslots: Optional[int] = None) -> dict:
     """Bucket cache of the complete cluster blocks of k_idx (bf16 [B, L_max, 64]) through
     lsa_semantic_cluster.  With ``cache`` given, only blocks [first_block, first_block +
     n_update) are (re)clustered into it.  Returns dict(centroids bf16 [B, NB, 8, 64, 8],
-    table int32 [B, NB, n_cluster], offsets int32 [B, NB, m + 1], params)."""
+    table int32 [B, NB, n_cluster], offsets int32 [B, NB, m + 1], params).
+
+    ``paged`` (lsa_semantic_cluster_paged) = dict(block_table=int32 [B, NB] or None,
+    page_table=int32 [B, max_pages] or None, page_size): with a block table the cache is a
+    pool of ``n_bslots`` entries ([n_bslots, ...] arrays; NB = block_table.shape[1]); with a
+    page table k_idx is the key pool [n_slots, 64] and L_max = max_pages * page_size."""
     _need(k_idx, "k_idx", torch.bfloat16)
     dev = k_idx.device
-    B, L, d = k_idx.shape
     prm = SemanticParams(n_cluster, n_pool, n_bavg, n_bmax)
+    if paged is not None and paged.get("page_table") is not None:
+        B, mp = paged["page_table"].shape
+        L = mp * int(paged["page_size"])
+        d = k_idx.shape[-1]
+    else:
+        B, L, d = k_idx.shape
+    if paged is not None and paged.get("block_table") is not None:
+        B = paged["block_table"].shape[0]
     if cache is None:
-        NB = L // n_cluster if n_blocks is None else n_blocks
         m = n_cluster // n_bavg
-        cache = {"centroids": torch.zeros((B, NB, 8, 64, 8), dtype=torch.bfloat16, device=dev),
-                 "table": torch.empty((B, NB, n_cluster), dtype=torch.int32, device=dev),
-                 "offsets": torch.empty((B, NB, m + 1), dtype=torch.int32, device=dev),
-                 "params": (n_cluster, n_pool, n_bavg, n_bmax)}
+        if paged is not None and paged.get("block_table") is not None:
+            NB = paged["block_table"].shape[1]
+            lead = (n_bslots,)
+        else:
+            NB = L // n_cluster if n_blocks is None else n_blocks
+            lead = (B, NB)
+        cache = {"centroids": torch.zeros(lead + (8, 64, 8), dtype=torch.bfloat16, device=dev),
+                 "table": torch.empty(lead + (n_cluster,), dtype=torch.int32, device=dev),
+                 "offsets": torch.empty(lead + (m + 1,), dtype=torch.int32, device=dev),
+                 "params": (n_cluster, n_pool, n_bavg, n_bmax), "NB": NB}
     else:
         prm = SemanticParams(*cache["params"])
-    NB = cache["table"].shape[1]
+    NB = cache.get("NB", cache["table"].shape[1])
     if n_update is None:
         n_update = min(NB, L // prm.n_cluster) - first_block
-    _check("lsa_semantic_cluster",
-           lib().lsa_semantic_cluster(_ptr(k_idx), B, L, d, C.byref(prm), NB, first_block, n_update,
-                                      _ptr(cache["centroids"]), _ptr(cache["table"]), _ptr(cache["offsets"]),
-                                      _stream(dev)))
+    if paged is None:
+        _check("lsa_semantic_cluster",
+               lib().lsa_semantic_cluster(_ptr(k_idx), B, L, d, C.byref(prm), NB, first_block, n_update,
+                                          _ptr(cache["centroids"]), _ptr(cache["table"]), _ptr(cache["offsets"]),
+                                          _stream(dev)))
+    else:
+        sp, _ = _sem_pages(paged, cache, k_idx.shape[0] if paged.get("page_table") is not None else 0)
+        _check("lsa_semantic_cluster_paged",
+               lib().lsa_semantic_cluster_paged(_ptr(k_idx), B, L, d, C.byref(prm), C.byref(sp), NB, first_block,
+                                                n_update, _ptr(cache["centroids"]), _ptr(cache["table"]),
+                                                _ptr(cache["offsets"]), _stream(dev)))
     return cache
 
 
 def lsa_semantic_select(q_idx, q_pos, cache: dict, k: int, p_top: int, n_sink: int, n_w: int,
-                        idx=None, count=None, ws_bytes: Optional[int] = None, ws: Optional[torch.Tensor] = None):
+                        idx=None, count=None, ws_bytes: Optional[int] = None, ws: Optional[torch.Tensor] = None,
+                        paged: Optional[dict] = None):
     """Index lists of flat semantic search: (idx int32 [B, n_q, n_sink + k + n_w], count
-    int32 [B, n_q]).  q_idx bf16 [B, n_q, 64]; q_pos int32 [B, n_q]."""
+    int32 [B, n_q]).  q_idx bf16 [B, n_q, 64]; q_pos int32 [B, n_q].  ``paged``: as for
+    lsa_semantic_cache, plus n_slots (rows of the key pools) with a page table; the lists
+    then hold pool rows."""
     _need(q_idx, "q_idx", torch.bfloat16)
     dev = q_idx.device
     _need(q_pos, "q_pos", torch.int32, dev)
     B, n_q, d = q_idx.shape
     prm = SemanticParams(*cache["params"])
-    NB = cache["table"].shape[1]
+    NB = cache.get("NB", cache["table"].shape[1])
     W = n_sink + k + n_w
     if idx is None:
         idx = torch.empty((B, n_q, W), dtype=torch.int32, device=dev)
@@ -462,11 +516,19 @@ def lsa_semantic_select(q_idx, q_pos, cache: dict, k: int, p_top: int, n_sink: i
                    lib().lsa_semantic_select_workspace_size(B, n_q, NB, C.byref(prm), C.byref(nb)))
             ws_bytes = nb.value
         ws = _workspace(ws_bytes, dev)
-    _check("lsa_semantic_select",
-           lib().lsa_semantic_select(_ptr(q_idx), _ptr(q_pos), B, n_q, d, C.byref(prm), NB,
-                                     _ptr(cache["centroids"]), _ptr(cache["table"]), _ptr(cache["offsets"]),
-                                     k, p_top, n_sink, n_w, _ptr(idx), _ptr(count), _ptr(ws), ws_bytes,
-                                     _stream(dev)))
+    if paged is None:
+        _check("lsa_semantic_select",
+               lib().lsa_semantic_select(_ptr(q_idx), _ptr(q_pos), B, n_q, d, C.byref(prm), NB,
+                                         _ptr(cache["centroids"]), _ptr(cache["table"]), _ptr(cache["offsets"]),
+                                         k, p_top, n_sink, n_w, _ptr(idx), _ptr(count), _ptr(ws), ws_bytes,
+                                         _stream(dev)))
+    else:
+        sp, L = _sem_pages(paged, cache, int(paged.get("n_slots", 0)))
+        _check("lsa_semantic_select_paged",
+               lib().lsa_semantic_select_paged(_ptr(q_idx), _ptr(q_pos), B, n_q, d, C.byref(prm), C.byref(sp), L, NB,
+                                               _ptr(cache["centroids"]), _ptr(cache["table"]),
+                                               _ptr(cache["offsets"]), k, p_top, n_sink, n_w, _ptr(idx),
+                                               _ptr(count), _ptr(ws), ws_bytes, _stream(dev)))
     return idx, count
 
 
@@ -475,7 +537,8 @@ def lsa_semantic_workspace_size(B: int, n_q: int, cache: dict) -> int:
     nb = SZ(0)
     prm = SemanticParams(*cache["params"])
     _check("lsa_semantic_select_workspace_size",
-           lib().lsa_semantic_select_workspace_size(B, n_q, cache["table"].shape[1], C.byref(prm), C.byref(nb)))
+           lib().lsa_semantic_select_workspace_size(B, n_q, cache.get("NB", cache["table"].shape[1]), C.byref(prm),
+                                                    C.byref(nb)))
     return nb.value
 
 

@@ -312,6 +312,24 @@ LSA_API lsa_status lsa_sparse_attn(const void* q, const void* k, const void* v, 
   return run_attn(q, k, v, idx, B, n_q, L_max, H_q, d, k_top, scale, split, out, lse, ws, as_stream(stream));
 }
 
+LSA_API lsa_status lsa_sparse_attn_pool(const void* q, const void* k_pool, const void* v_pool, const int32_t* idx,
+                                        int32_t B, int32_t n_q, int64_t n_slots, int32_t H_q, int32_t d,
+                                        int32_t k_top, float scale, int32_t n_split, void* out, float* lse, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  if (B < 0 || n_q < 0 || n_slots < 0 || n_slots > (1LL << 31) || k_top < 1 || H_q < 1) return LSA_ERR_INVALID_ARG;
+  if (d != 128) return LSA_ERR_UNSUPPORTED;
+  if (H_q > 16 || k_top > 65536) return LSA_ERR_UNSUPPORTED;
+  if ((long long)B * n_q == 0) return LSA_OK;
+  if (!q || !k_pool || !v_pool || !idx || !out || n_slots < 1) return LSA_ERR_INVALID_ARG;
+  const int split = resolve_split(B, n_q, k_top, n_split);
+  const size_t need = attn_ws_bytes((long long)B * n_q, H_q, d, split);
+  if (ws_bytes < need || (need > 0 && !ws)) return LSA_ERR_WORKSPACE;
+  if (((uintptr_t)ws) % 16 != 0) return LSA_ERR_WORKSPACE;
+  const int32_t L_clip = n_slots > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int32_t)n_slots;
+  return run_attn(q, k_pool, v_pool, idx, B, n_q, L_clip, H_q, d, k_top, scale, split, out, lse, ws,
+                  as_stream(stream), n_slots);
+}
+
 // ------------------------------------------------------------------------------------------ forward
 namespace {
 
@@ -797,10 +815,33 @@ static lsa_status check_sem_params(const lsa_semantic_params* prm, int d_idx, ls
   return LSA_OK;
 }
 
-LSA_API lsa_status lsa_semantic_cluster(const void* k_idx, int32_t B, int32_t L_max, int32_t d_idx,
-                                        const lsa_semantic_params* prm, int32_t n_blocks, int32_t first_block,
-                                        int32_t n_update, void* centroids, int32_t* table, int32_t* offsets,
-                                        void* stream) {
+static lsa_status check_sem_pages(const lsa_semantic_pages* pg, int B, int L_max, int n_blocks, lsa::SemPages* out) {
+  *out = lsa::SemPages();
+  if (!pg) return LSA_OK;
+  if (pg->block_table) {
+    if (pg->n_bslots < 1) return LSA_ERR_INVALID_ARG;
+    out->block_table = pg->block_table;
+    out->n_bslots = pg->n_bslots;
+  }
+  if (pg->page_table) {
+    const int P = pg->page_size;
+    if (P < 64 || (P & (P - 1)) != 0 || pg->max_pages < 1 || (long long)pg->max_pages * P != L_max ||
+        pg->n_slots < P || pg->n_slots % P != 0 || pg->n_slots > (1LL << 31))
+      return LSA_ERR_INVALID_ARG;
+    out->page_table = pg->page_table;
+    out->page_size = P;
+    out->max_pages = pg->max_pages;
+    out->n_slots = pg->n_slots;
+  }
+  (void)B;
+  (void)n_blocks;
+  return LSA_OK;
+}
+
+static lsa_status sem_cluster(const void* k_idx, int32_t B, int32_t L_max, int32_t d_idx,
+                              const lsa_semantic_params* prm, const lsa_semantic_pages* pages, int32_t n_blocks,
+                              int32_t first_block, int32_t n_update, void* centroids, int32_t* table,
+                              int32_t* offsets, void* stream) {
   lsa::SemParams sp;
   if (B < 0 || L_max < 1 || n_blocks < 0 || first_block < 0 || n_update < 0) return LSA_ERR_INVALID_ARG;
   lsa_status st = check_sem_params(prm, d_idx, &sp);
@@ -808,10 +849,30 @@ LSA_API lsa_status lsa_semantic_cluster(const void* k_idx, int32_t B, int32_t L_
   if ((long long)first_block + n_update > n_blocks ||
       ((long long)first_block + n_update) * sp.n_cluster > L_max)
     return LSA_ERR_INVALID_ARG;
+  lsa::SemPages pg;
+  st = check_sem_pages(pages, B, L_max, n_blocks, &pg);
+  if (st != LSA_OK) return st;
   if ((long long)B * n_update == 0) return LSA_OK;
   if (!k_idx || !centroids || !table || !offsets) return LSA_ERR_INVALID_ARG;
   return hip_status(lsa::launch_sem_cluster(k_idx, B, L_max, sp, n_blocks, first_block, n_update, centroids, table,
-                                            offsets, as_stream(stream)));
+                                            offsets, pg, as_stream(stream)));
+}
+
+LSA_API lsa_status lsa_semantic_cluster(const void* k_idx, int32_t B, int32_t L_max, int32_t d_idx,
+                                        const lsa_semantic_params* prm, int32_t n_blocks, int32_t first_block,
+                                        int32_t n_update, void* centroids, int32_t* table, int32_t* offsets,
+                                        void* stream) {
+  return sem_cluster(k_idx, B, L_max, d_idx, prm, nullptr, n_blocks, first_block, n_update, centroids, table,
+                     offsets, stream);
+}
+
+LSA_API lsa_status lsa_semantic_cluster_paged(const void* k_idx, int32_t B, int32_t L_max, int32_t d_idx,
+                                              const lsa_semantic_params* prm, const lsa_semantic_pages* pages,
+                                              int32_t n_blocks, int32_t first_block, int32_t n_update,
+                                              void* centroids, int32_t* table, int32_t* offsets, void* stream) {
+  if (!pages) return LSA_ERR_INVALID_ARG;
+  return sem_cluster(k_idx, B, L_max, d_idx, prm, pages, n_blocks, first_block, n_update, centroids, table,
+                     offsets, stream);
 }
 
 LSA_API lsa_status lsa_semantic_select_workspace_size(int32_t B, int32_t n_q, int32_t n_blocks,
@@ -824,16 +885,19 @@ LSA_API lsa_status lsa_semantic_select_workspace_size(int32_t B, int32_t n_q, in
   return LSA_OK;
 }
 
-LSA_API lsa_status lsa_semantic_select(const void* q_idx, const int32_t* q_pos, int32_t B, int32_t n_q, int32_t d_idx,
-                                       const lsa_semantic_params* prm, int32_t n_blocks, const void* centroids,
-                                       const int32_t* table, const int32_t* offsets, int32_t k, int32_t p_top,
-                                       int32_t n_sink, int32_t n_w, int32_t* idx, int32_t* count, void* ws,
-                                       size_t ws_bytes, void* stream) {
+static lsa_status sem_select(const void* q_idx, const int32_t* q_pos, int32_t B, int32_t n_q, int32_t d_idx,
+                             const lsa_semantic_params* prm, const lsa_semantic_pages* pages, int32_t L_max,
+                             int32_t n_blocks, const void* centroids, const int32_t* table, const int32_t* offsets,
+                             int32_t k, int32_t p_top, int32_t n_sink, int32_t n_w, int32_t* idx, int32_t* count,
+                             void* ws, size_t ws_bytes, void* stream) {
   lsa::SemParams sp;
   if (B < 0 || n_q < 0 || n_blocks < 0 || k < 1 || p_top < 1 || n_sink < 0 || n_w < 0) return LSA_ERR_INVALID_ARG;
   lsa_status st = check_sem_params(prm, d_idx, &sp);
   if (st != LSA_OK) return st;
   if (k > lsa::SEM_MAX_K || p_top > lsa::SEM_MAX_P) return LSA_ERR_UNSUPPORTED;
+  lsa::SemPages pg;
+  st = check_sem_pages(pages, B, L_max, n_blocks, &pg);
+  if (st != LSA_OK) return st;
   if ((long long)n_sink + k + n_w > (1LL << 30)) return LSA_ERR_INVALID_ARG;
   if ((long long)B * n_q == 0) return LSA_OK;
   if (!q_idx || !q_pos || !idx || !count || (n_blocks > 0 && (!centroids || !table || !offsets)))
@@ -859,5 +923,26 @@ LSA_API lsa_status lsa_semantic_select(const void* q_idx, const int32_t* q_pos, 
   a.count = count;
   a.ws = ws;
   a.ws_bytes = ws_bytes;
+  a.pages = pg;
   return hip_status(lsa::launch_sem_select(a, as_stream(stream)));
+}
+
+LSA_API lsa_status lsa_semantic_select(const void* q_idx, const int32_t* q_pos, int32_t B, int32_t n_q, int32_t d_idx,
+                                       const lsa_semantic_params* prm, int32_t n_blocks, const void* centroids,
+                                       const int32_t* table, const int32_t* offsets, int32_t k, int32_t p_top,
+                                       int32_t n_sink, int32_t n_w, int32_t* idx, int32_t* count, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  return sem_select(q_idx, q_pos, B, n_q, d_idx, prm, nullptr, 0, n_blocks, centroids, table, offsets, k, p_top,
+                    n_sink, n_w, idx, count, ws, ws_bytes, stream);
+}
+
+LSA_API lsa_status lsa_semantic_select_paged(const void* q_idx, const int32_t* q_pos, int32_t B, int32_t n_q,
+                                             int32_t d_idx, const lsa_semantic_params* prm,
+                                             const lsa_semantic_pages* pages, int32_t L_max, int32_t n_blocks,
+                                             const void* centroids, const int32_t* table, const int32_t* offsets,
+                                             int32_t k, int32_t p_top, int32_t n_sink, int32_t n_w, int32_t* idx,
+                                             int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  if (!pages) return LSA_ERR_INVALID_ARG;
+  return sem_select(q_idx, q_pos, B, n_q, d_idx, prm, pages, L_max, n_blocks, centroids, table, offsets, k, p_top,
+                    n_sink, n_w, idx, count, ws, ws_bytes, stream);
 }

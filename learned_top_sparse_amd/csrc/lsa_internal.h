@@ -191,6 +191,13 @@ hipError_t launch_list_topk(const int32_t* q_pos, long long rows, int L_max, int
 struct SemParams {
   int n_cluster, n_pool, n_bavg, n_bmax;
 };
+struct SemPages {
+  const int32_t* block_table = nullptr;  // [B, NB] cache slot of each cluster block (null: b * NB + t)
+  int n_bslots = 0;
+  const int32_t* page_table = nullptr;   // [B, max_pages] pool page of each page of keys (null: contiguous)
+  int page_size = 0, max_pages = 0;
+  long long n_slots = 0;                 // rows of the key pools
+};
 struct SemSelectArgs {
   const void* q_idx;       // bf16 [B, n_q, 64]
   const int32_t* q_pos;    // [B, n_q]
@@ -205,13 +212,15 @@ struct SemSelectArgs {
   int32_t* count;          // [B, n_q]
   void* ws;
   size_t ws_bytes;
+  SemPages pages;
 };
 constexpr int SEM_MAX_POOL_KEYS = 128;  // pool keys of a cluster block
 constexpr int SEM_MAX_BUCKETS = 64;     // buckets of a cluster block
 constexpr int SEM_MAX_P = 2048;
 constexpr int SEM_MAX_K = 4096;
 hipError_t launch_sem_cluster(const void* k_idx, int B, int L_max, const SemParams& sp, int NB, int first_block,
-                              int n_update, void* cent, int32_t* table, int32_t* offs, hipStream_t st);
+                              int n_update, void* cent, int32_t* table, int32_t* offs, const SemPages& pages,
+                              hipStream_t st);
 size_t sem_select_row_bytes(int NB, int m);
 hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st);
 

@@ -51,6 +51,34 @@ __device__ __forceinline__ void unpack8(uint4 v, float* x) {
   x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
 }
 
+// Where a sequence's cluster block lives in the bucket cache, and where its logical key
+// lives in the index-key / K / V storage: identity for contiguous caches, through a
+// block table and a page table for pooled ones (ids clamped into their pools).
+struct SemPaging {
+  const int* bt;     // [B][NB] cache slot of each block, or null: slot b * NB + t
+  int n_bslots;
+  const int* pt;     // [B][max_pages] pool page of each page of keys, or null: contiguous
+  int plog2, max_pages;
+  long long n_pages;
+  __device__ __forceinline__ long long slot(int b, int NB, int blk) const {
+    if (!bt) return (long long)b * NB + blk;
+    int v = bt[(long long)b * NB + blk];
+    v = v < 0 ? 0 : (v >= n_bslots ? n_bslots - 1 : v);
+    return v;
+  }
+  // storage row of logical key j of sequence b (rows of L_max per sequence if contiguous)
+  __device__ __forceinline__ long long row(int b, long long L_max, int j) const {
+    if (!pt) return (long long)b * L_max + j;
+    int pi = j >> plog2;
+    pi = pi < max_pages ? pi : max_pages - 1;  // positions past the pages stay in the table
+    long long pg = pt[(long long)b * max_pages + pi];
+    pg = pg < 0 ? 0 : (pg >= n_pages ? n_pages - 1 : pg);
+    return (pg << plog2) | (j & ((1 << plog2) - 1));
+  }
+  // what the index list holds for logical key j: the key itself if contiguous, its pool row if paged
+  __device__ __forceinline__ int list_entry(int b, int j) const { return pt ? (int)row(b, 0, j) : j; }
+};
+
 // ---------------------------------------------------------------------------------
 // Clustering: one 1024-thread workgroup per (cluster block, sequence), 8 threads per
 // pool key / bucket row.  The block's pool keys (sums of its normalised keys), the
@@ -84,7 +112,8 @@ constexpr int CL_NT = 1024;            // threads of the clustering workgroup
 constexpr int CL_SLOTS = CL_NT / SEM_NPK;  // threads per pool key / bucket row
 
 __global__ __launch_bounds__(CL_NT) void sem_cluster_kernel(const unsigned short* __restrict__ kidx,
-                                                            long long seq_elems, SemGeom g, int first_block, int NB,
+                                                            long long L_max, SemPaging pg, SemGeom g,
+                                                            int first_block, int NB,
                                                             unsigned short* __restrict__ cent,
                                                             int* __restrict__ table, int* __restrict__ offs) {
   __shared__ float S[SEM_NPK][SEM_D + 1];
@@ -103,14 +132,14 @@ __global__ __launch_bounds__(CL_NT) void sem_cluster_kernel(const unsigned short
   const int b = blockIdx.y;
   const int npk = g.npk;
   const int row = t & (SEM_NPK - 1), slot = t >> 7;  // a bucket row and one of its CL_SLOTS threads
-  const unsigned short* kb = kidx + (long long)b * seq_elems + (long long)blk * g.n_cluster * SEM_D;
 
   // 1. pool keys: the block's keys normalised and summed n_pool at a time, in key order;
   //    each of a pool key's 8 threads divides its 8 dims (the norm needs all 64)
   if (row < npk) {
     float P[8];
     for (int i = 0; i < g.n_pool; ++i) {
-      const uint4* kr = reinterpret_cast<const uint4*>(kb + (long long)(row * g.n_pool + i) * SEM_D);
+      const int j = blk * g.n_cluster + row * g.n_pool + i;
+      const uint4* kr = reinterpret_cast<const uint4*>(kidx + pg.row(b, L_max, j) * SEM_D);
       float x[SEM_D];
 #pragma unroll
       for (int c = 0; c < 8; ++c) unpack8(kr[c], x + 8 * c);
@@ -273,7 +302,7 @@ __global__ __launch_bounds__(CL_NT) void sem_cluster_kernel(const unsigned short
     if (r < SEM_SLOTS) id_of_rank[r] = t;
   }
   __syncthreads();
-  const long long cb = (long long)b * NB + blk;
+  const long long cb = pg.slot(b, NB, blk);
   if (t < npk) {
     const int a = lab[t];
     int pos = 0;
@@ -352,6 +381,7 @@ __global__ __launch_bounds__(256) void sem_qnorm_kernel(const unsigned short* __
 // lanes, and the 64 rounded values are then wave-uniform -- so no separate launch.
 __global__ __launch_bounds__(256) void sem_score_decode_kernel(const unsigned short* __restrict__ q_idx,
                                                                const int* __restrict__ q_pos, int n_q, int i0,
+                                                               SemPaging pg,
                                                                const unsigned short* __restrict__ cent, int NB,
                                                                int m, int n_cluster, int bpw,
                                                                float* __restrict__ S, long long ld) {
@@ -366,10 +396,13 @@ __global__ __launch_bounds__(256) void sem_score_decode_kernel(const unsigned sh
   blk_end = blk_end < own ? blk_end : own;
   if (blk0 >= blk_end) return;
 
-  const uint4* cb = reinterpret_cast<const uint4*>(cent + ((long long)b * NB) * (SEM_D * SEM_SLOTS));
+  const uint4* c4 = reinterpret_cast<const uint4*>(cent);
   uint4 nxt[8];
+  {
+    const uint4* cb = c4 + pg.slot(b, NB, blk0) * (SEM_D * SEM_SLOTS / 8);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) nxt[c] = cb[(long long)blk0 * (SEM_D * SEM_SLOTS / 8) + c * SEM_SLOTS + lane];
+    for (int c = 0; c < 8; ++c) nxt[c] = cb[c * SEM_SLOTS + lane];
+  }
 
   const float x = __uint_as_float((unsigned)q_idx[((long long)b * n_q + i0) * SEM_D + lane] << 16);
   const float sq = x * x;
@@ -387,8 +420,9 @@ __global__ __launch_bounds__(256) void sem_score_decode_kernel(const unsigned sh
 #pragma unroll
     for (int c = 0; c < 8; ++c) unpack8(nxt[c], cv + 8 * c);
     if (blk + 1 < blk_end) {
+      const uint4* cb = c4 + pg.slot(b, NB, blk + 1) * (SEM_D * SEM_SLOTS / 8);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) nxt[c] = cb[(long long)(blk + 1) * (SEM_D * SEM_SLOTS / 8) + c * SEM_SLOTS + lane];
+      for (int c = 0; c < 8; ++c) nxt[c] = cb[c * SEM_SLOTS + lane];
     }
     float acc = 0.f;
 #pragma unroll
@@ -399,7 +433,7 @@ __global__ __launch_bounds__(256) void sem_score_decode_kernel(const unsigned sh
 
 template <int QT>
 __global__ __launch_bounds__(256) void sem_score_kernel(const float* __restrict__ qn, const int* __restrict__ q_pos,
-                                                        int n_q, int i0, int nqc,
+                                                        int n_q, int i0, int nqc, SemPaging pg,
                                                         const unsigned short* __restrict__ cent, int NB, int m,
                                                         int n_cluster, int bpw, float* __restrict__ S, long long ld) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -419,17 +453,21 @@ __global__ __launch_bounds__(256) void sem_score_kernel(const float* __restrict_
   blk_end = blk_end < own_max ? blk_end : own_max;
   if (blk0 >= blk_end) return;
 
-  const uint4* cb = reinterpret_cast<const uint4*>(cent + ((long long)b * NB) * (SEM_D * SEM_SLOTS));
+  const uint4* c4 = reinterpret_cast<const uint4*>(cent);
   uint4 nxt[8];
+  {
+    const uint4* cb = c4 + pg.slot(b, NB, blk0) * (SEM_D * SEM_SLOTS / 8);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) nxt[c] = cb[(long long)blk0 * (SEM_D * SEM_SLOTS / 8) + c * SEM_SLOTS + lane];
+    for (int c = 0; c < 8; ++c) nxt[c] = cb[c * SEM_SLOTS + lane];
+  }
   for (int blk = blk0; blk < blk_end; ++blk) {
     float cv[SEM_D];
 #pragma unroll
     for (int c = 0; c < 8; ++c) unpack8(nxt[c], cv + 8 * c);
     if (blk + 1 < blk_end) {
+      const uint4* cb = c4 + pg.slot(b, NB, blk + 1) * (SEM_D * SEM_SLOTS / 8);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) nxt[c] = cb[(long long)(blk + 1) * (SEM_D * SEM_SLOTS / 8) + c * SEM_SLOTS + lane];
+      for (int c = 0; c < 8; ++c) nxt[c] = cb[c * SEM_SLOTS + lane];
     }
     for (int qi = 0; qi < QT; ++qi) {
       const int i = q0 + qi;
@@ -458,6 +496,7 @@ constexpr int SEM_KMAX = 4096;
 
 __global__ __launch_bounds__(SEL_NT) void sem_select_stream_kernel(const float* __restrict__ S, long long ld,
                                                             const int* __restrict__ q_pos, int n_q, int i0, int nqc,
+                                                            SemPaging pg,
                                                             const int* __restrict__ table, const int* __restrict__ offs,
                                                             int NB, int m, int n_cluster, int k, int p_top, int n_sink,
                                                             int n_w, int W, int* __restrict__ idx,
@@ -567,11 +606,12 @@ __global__ __launch_bounds__(SEL_NT) void sem_select_stream_kernel(const float* 
   for (int r = t; r < nk; r += SEL_NT) {
     const int gid = (int)(0xFFFFFFFFu - (unsigned)(K[r] & 0xFFFFFFFFull));
     const int blk = gid / m, loc = gid - blk * m;
-    const int* ob = offs + ((long long)b * NB + blk) * (m + 1);
+    const long long sl = pg.slot(b, NB, blk);
+    const int* ob = offs + sl * (m + 1);
     const int o0 = ob[loc], o1 = ob[loc + 1];
     int av = o1 - o0;
     if (blk * n_cluster < n_sink || (blk + 1) * n_cluster > w0) {
-      const int* tb = table + ((long long)b * NB + blk) * n_cluster;
+      const int* tb = table + sl * n_cluster;
       av = 0;
       for (int x = o0; x < o1; ++x) {
         const int key = tb[x];
@@ -605,8 +645,9 @@ __global__ __launch_bounds__(SEL_NT) void sem_select_stream_kernel(const float* 
     const int take = avail[r] < k - e0 ? avail[r] : k - e0;
     const int gid = (int)(0xFFFFFFFFu - (unsigned)(K[r] & 0xFFFFFFFFull));
     const int blk = gid / m, loc = gid - blk * m;
-    const int* ob = offs + ((long long)b * NB + blk) * (m + 1);
-    const int* tb = table + ((long long)b * NB + blk) * n_cluster;
+    const long long sl = pg.slot(b, NB, blk);
+    const int* ob = offs + sl * (m + 1);
+    const int* tb = table + sl * n_cluster;
     int n = 0;
     for (int x = ob[loc]; x < ob[loc + 1] && n < take; ++x) {
       const int key = tb[x];
@@ -641,19 +682,23 @@ __global__ __launch_bounds__(SEL_NT) void sem_select_stream_kernel(const float* 
     if (j < n_s) v = j;
     else if (j < n_s + n_lr) v = LR[j - n_s];
     else if (j < cnt_all) v = w0 + (j - n_s - n_lr);
-    out[j] = v;
+    out[j] = v < 0 ? v : pg.list_entry(b, v);
   }
   if (t == 0) count[qrow] = cnt_all;
 }
 
 
-// Selection and expansion of rows of at most 1024 * C buckets whose long-range keys
-// lie below 32 * LBM(C) positions: one 1024-thread workgroup per query, the row's
-// order keys in registers (bucket c * 1024 + t in slot c of thread t).  The cut is a
+// Selection and expansion of rows of at most NT * C buckets whose long-range keys lie
+// below 32 * SelLbm<C>::WORDS positions: one NT-thread workgroup per query, the row's
+// order keys in registers (bucket c * NT + t in slot c of thread t).  The cut is a
 // radix select over them (11-bit digits below the bits all keys share; ties to the
-// lowest bucket id); each kept bucket's start in best-first order is the count of keys
-// the kept buckets with larger packed keys offer, and the long-range keys are marked
-// in an LDS bitmap of key positions, which yields them ascending.
+// lowest bucket id); the kept buckets' packed keys, appended from the registers, are
+// sorted best first (lane shuffles for exchanges under 64 apart, LDS above); each
+// bucket's offsets, eligible-key mask and long-range keys are handled by the thread
+// owning its run of that order, one scan giving every bucket's start; the long-range
+// keys are marked in an LDS bitmap of key positions, which yields them ascending.
+// MINW > 1 holds the kernel to the registers of MINW waves per SIMD (two workgroups
+// per compute unit when many rows run).
 template <int C>
 struct SelLbm {
   static constexpr int WORDS = 256 * C;  // positions < 8192 * C: n_bavg = 8 fills it
@@ -666,7 +711,7 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
                                                              const int* __restrict__ offs, int NB, int m,
                                                              int n_cluster, int n_bmax, int k, int p_top, int n_sink,
                                                              int n_w, int W, int* __restrict__ idx,
-                                                             int* __restrict__ count) {
+                                                             int* __restrict__ count, SemPaging pg) {
   constexpr int NWD = NT * C / 32;
   constexpr int LW = SelLbm<C>::WORDS;
   __shared__ unsigned long long K[SEM_PMAX];
@@ -777,14 +822,14 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
   //    its keys start and how many (one load), which of them lie outside the sink and
   //    the window (loads 8 at a time, a 64-bit mask kept in a register), and the
   //    running count of those in best-first order (one scan)
-  const long long tseq = (long long)b * NB * n_cluster;
   // long-range keys lie below both the window and the end of the scored blocks
   const int pos_lim = w0 < nb * n_cluster ? w0 : nb * n_cluster;
   const int nlw = (pos_lim + 31) >> 5;
   for (int wd = t; wd < nlw; wd += NT) lbm[wd] = 0u;
   constexpr int OWN = SEM_PMAX / NT;  // buckets a thread owns, at most
   const int per = (nk + NT - 1) / NT;
-  int o_start[OWN], o_size[OWN];
+  long long o_start[OWN];
+  int o_size[OWN];
   unsigned long long o_mask[OWN];
   int run = 0;
 #pragma unroll
@@ -796,11 +841,12 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
     if (e >= per || r >= nk) continue;
     const int gid = (int)(0xFFFFFFFFu - (unsigned)(K[r] & 0xFFFFFFFFull));
     const int blk = gid / m, loc = gid - blk * m;
-    const int* ob = offs + ((long long)b * NB + blk) * (m + 1);
+    const long long sl = pg.slot(b, NB, blk);
+    const int* ob = offs + sl * (m + 1);
     const int o0 = ob[loc], o1 = ob[loc + 1];
-    o_start[e] = blk * n_cluster + o0;
+    o_start[e] = sl * n_cluster + o0;
     o_size[e] = o1 - o0;
-    const int* tb = table + tseq + o_start[e];
+    const int* tb = table + o_start[e];
     unsigned long long msk = 0ull;
     for (int base = 0; base < o_size[e]; base += 8) {
       int v[8];
@@ -826,7 +872,7 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
     const int av = __popcll(msk);
     if (e0 < k && msk != 0ull) {
       const int take = av < k - e0 ? av : k - e0;
-      const int* tb = table + tseq + o_start[e];
+      const int* tb = table + o_start[e];
       for (int base = 0; base < o_size[e]; base += 8) {
         int v[8];
 #pragma unroll
@@ -843,12 +889,12 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
   }
   __syncthreads();
   const int n_s = n_sink < w0 ? n_sink : w0;
-  emit_marked<NT>(lbm, nlw, scan_tmp, [&](int r, int pos) { out[n_s + r] = pos; });
+  emit_marked<NT>(lbm, nlw, scan_tmp, [&](int r, int pos) { out[n_s + r] = pg.list_entry(b, pos); });
   const int n_win = p - w0 + 1;
   const int cnt_all = n_s + n_lr + n_win;
   for (int j = t; j < W; j += NT) {
-    if (j < n_s) out[j] = j;
-    else if (j >= n_s + n_lr) out[j] = j < cnt_all ? w0 + (j - n_s - n_lr) : -1;
+    if (j < n_s) out[j] = pg.list_entry(b, j);
+    else if (j >= n_s + n_lr) out[j] = j < cnt_all ? pg.list_entry(b, w0 + (j - n_s - n_lr)) : -1;
   }
   if (t == 0) count[qrow] = cnt_all;
 }
@@ -857,8 +903,21 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
 
 // ---------------------------------------------------------------------------------
 
+static SemPaging paging_of(const SemPages& p) {
+  SemPaging g;
+  g.bt = p.block_table;
+  g.n_bslots = p.n_bslots;
+  g.pt = p.page_table;
+  g.plog2 = 0;
+  while (p.page_size > 0 && (1 << g.plog2) < p.page_size) ++g.plog2;
+  g.max_pages = p.max_pages;
+  g.n_pages = p.page_size > 0 ? p.n_slots / p.page_size : 0;
+  return g;
+}
+
 hipError_t launch_sem_cluster(const void* k_idx, int B, int L_max, const SemParams& sp, int NB, int first_block,
-                              int n_update, void* cent, int32_t* table, int32_t* offs, hipStream_t st) {
+                              int n_update, void* cent, int32_t* table, int32_t* offs, const SemPages& pages,
+                              hipStream_t st) {
   SemGeom g;
   g.n_cluster = sp.n_cluster;
   g.n_pool = sp.n_pool;
@@ -867,7 +926,8 @@ hipError_t launch_sem_cluster(const void* k_idx, int B, int L_max, const SemPara
   g.cap = sp.n_bmax / sp.n_pool;
   dim3 grid(n_update, B);
   hipLaunchKernelGGL(sem_cluster_kernel, grid, dim3(CL_NT), 0, st, static_cast<const unsigned short*>(k_idx),
-                     (long long)L_max * SEM_D, g, first_block, NB, static_cast<unsigned short*>(cent), table, offs);
+                     (long long)L_max, paging_of(pages), g, first_block, NB, static_cast<unsigned short*>(cent), table,
+                     offs);
   return hipGetLastError();
 }
 
@@ -884,6 +944,7 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
   if (nqc_max > a.n_q) nqc_max = a.n_q;
   if (nqc_max < 1) return hipErrorInvalidValue;
   const int W = a.n_sink + a.k + a.n_w;
+  const SemPaging pg = paging_of(a.pages);
   for (int i0 = 0; i0 < a.n_q; i0 += (int)nqc_max) {
     const int nqc = (int)(a.n_q - i0 < nqc_max ? a.n_q - i0 : nqc_max);
     const int rows = a.B * nqc;
@@ -895,7 +956,7 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
       const int bpw = 4;
       dim3 grid((a.NB + 4 * bpw - 1) / (4 * bpw), 1, a.B);
       hipLaunchKernelGGL(sem_score_decode_kernel, grid, dim3(256), 0, st,
-                         static_cast<const unsigned short*>(a.q_idx), a.q_pos, a.n_q, i0,
+                         static_cast<const unsigned short*>(a.q_idx), a.q_pos, a.n_q, i0, pg,
                          static_cast<const unsigned short*>(a.cent), a.NB, m, a.sp.n_cluster, bpw, S, ld);
     } else {
       hipLaunchKernelGGL(sem_qnorm_kernel, dim3((rows + 255) / 256), dim3(256), 0, st,
@@ -903,7 +964,7 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
       constexpr int QT = 16;
       const int bpw = 4;
       dim3 grid((a.NB + 4 * bpw - 1) / (4 * bpw), (nqc + QT - 1) / QT, a.B);
-      hipLaunchKernelGGL(sem_score_kernel<QT>, grid, dim3(256), 0, st, qn, a.q_pos, a.n_q, i0, nqc,
+      hipLaunchKernelGGL(sem_score_kernel<QT>, grid, dim3(256), 0, st, qn, a.q_pos, a.n_q, i0, nqc, pg,
                          static_cast<const unsigned short*>(a.cent), a.NB, m, a.sp.n_cluster, bpw, S, ld);
     }
     // rows in registers: one 1024-thread workgroup per row; with enough rows to fill
@@ -917,7 +978,7 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
 #define LSA_SEM_SEL(NT, C, MINW)                                                                               \
   hipLaunchKernelGGL((sem_select_kernel<NT, C, MINW>), dim3(nqc, a.B), dim3(NT), 0, st, S, ld, a.q_pos, a.n_q,   \
                      i0, nqc, a.table, a.offs, a.NB, m, a.sp.n_cluster, a.sp.n_bmax, a.k, a.p_top, a.n_sink, a.n_w, \
-                     W, a.idx, a.count)
+                     W, a.idx, a.count, pg)
     if (many && fits(1024, 4)) LSA_SEM_SEL(1024, 4, 8);
     else if (many && fits(1024, 8)) LSA_SEM_SEL(1024, 8, 8);
     else if (many && fits(1024, 16)) LSA_SEM_SEL(1024, 16, 8);
@@ -927,7 +988,7 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
     else if (fits(1024, 32)) LSA_SEM_SEL(1024, 32, 1);
     else
       hipLaunchKernelGGL(sem_select_stream_kernel, dim3(nqc, a.B), dim3(SEL_NT), 0, st, S, ld, a.q_pos, a.n_q, i0,
-                         nqc, a.table, a.offs, a.NB, m, a.sp.n_cluster, a.k, a.p_top, a.n_sink, a.n_w, W, a.idx,
+                         nqc, pg, a.table, a.offs, a.NB, m, a.sp.n_cluster, a.k, a.p_top, a.n_sink, a.n_w, W, a.idx,
                          a.count);
 #undef LSA_SEM_SEL
     hipError_t e = hipGetLastError();

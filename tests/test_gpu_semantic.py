@@ -326,3 +326,61 @@ def test_semantic_decode_graph_replay(lsa):
         torch.cuda.synchronize()
         assert torch.equal(got[0], want_idx) and torch.equal(got[1], want_cnt), f"replay {trial}: lists"
         assert torch.equal(got[2], want_out) and torch.equal(got[3], want_lse), f"replay {trial}: attention"
+
+
+def _to_pool(t, pt, P, n_pages, fill_seed):
+    """t [B, L, d] scattered over a pool of pages: logical key j of sequence b at row
+    pt[b, j // P] * P + j % P; the other rows random."""
+    B, L, d = t.shape
+    gen = torch.Generator(dev()).manual_seed(fill_seed)
+    pool = torch.randn((n_pages * P, d), generator=gen, device=dev()).to(t.dtype)
+    j = torch.arange(L, device=dev())
+    rows = (pt.long()[:, j // P] * P + j % P).reshape(-1)
+    pool.index_copy_(0, rows, t.reshape(B * L, d))
+    return pool
+
+
+def test_semantic_paged(lsa):
+    """Paged storage: index keys, K and V in pools of 64-key pages behind a page table, the
+    bucket cache in a pool of entries behind a block table.  The cache entries equal the
+    contiguous ones slot for slot, the lists are the contiguous lists mapped to pool rows,
+    and attention over the pools equals attention over the contiguous caches."""
+    prm = (512, 4, 8, 32)
+    P, k, p_top = 64, 300, 64
+    L = 10 * 512
+    wl = synthetic.Workload("sem_paged", B=3, n_q=4, L=L, q_pos0=L - 4, H_I=1, d_I=64, k=k, H_q=16, semantic=True,
+                            p_top=p_top, n_sink=4)
+    g = synthetic.make_inputs(wl, dev())
+    g.update(synthetic.semantic_inputs(wl, dev(), seed=13))
+    g["q_pos"].copy_(torch.tensor([[L - 1, 4000, 513, 100], [L - 2, 2047, 3000, 5000], [1024, 1023, 5000, 4777]],
+                                  dtype=torch.int32, device=dev()))
+    B, NB, max_pages = 3, L // 512, L // P
+    gen = torch.Generator().manual_seed(21)
+    n_pages = B * max_pages + 17
+    pt = torch.randperm(n_pages, generator=gen)[: B * max_pages].view(B, max_pages).to(torch.int32).to(dev())
+    n_bslots = B * NB + 5
+    bt = torch.randperm(n_bslots, generator=gen)[: B * NB].view(B, NB).to(torch.int32).to(dev())
+    k_pool = _to_pool(g["k_sem"], pt, P, n_pages, 1)
+    kc_pool, vc_pool = _to_pool(g["k"], pt, P, n_pages, 2), _to_pool(g["v"], pt, P, n_pages, 3)
+    paged = {"block_table": bt, "page_table": pt, "page_size": P, "n_slots": n_pages * P}
+
+    cache = lsa.lsa_semantic_cache(g["k_sem"], *prm)
+    cache_p = lsa.lsa_semantic_cache(k_pool, *prm, paged=paged, n_bslots=n_bslots)
+    idx, cnt = lsa.lsa_semantic_select(g["q_sem"], g["q_pos"], cache, k, p_top, 4, 512)
+    idx_p, cnt_p = lsa.lsa_semantic_select(g["q_sem"], g["q_pos"], cache_p, k, p_top, 4, 512, paged=paged)
+    out, lse = lsa.lsa_sparse_attn(g["q"], g["k"], g["v"], idx, scale=wl.scale)
+    out_p, lse_p = lsa.lsa_sparse_attn(g["q"], kc_pool, vc_pool, idx_p, scale=wl.scale)
+    torch.cuda.synchronize()
+    for name in ("centroids", "table", "offsets"):
+        assert torch.equal(cache_p[name][bt.long()], cache[name]), name
+    mapped = torch.where(idx >= 0, pt.long().gather(1, (idx.clamp(min=0) // P).view(B, -1)).view_as(idx) * P
+                         + idx.clamp(min=0) % P, torch.full_like(idx, -1).long()).to(torch.int32)
+    assert torch.equal(idx_p, mapped) and torch.equal(cnt_p, cnt)
+    assert torch.equal(out_p, out) and torch.equal(lse_p, lse)
+    # the contiguous lists are the oracle's (checked here once more on one sequence)
+    oc = _oracle_cache(g["k_sem"][1], prm, n_blocks=NB)
+    for i in range(4):
+        r = oracle.semantic_select_row(_f32(g["q_sem"][1, i]), oc, int(g["q_pos"][1, i]), k, p_top, 4, 512)
+        assert np.array_equal(idx[1, i].cpu().numpy(), r["J"])
+        want = np.where(r["J"] >= 0, oracle.paged_rows(pt[1].cpu().numpy(), L, P)[np.maximum(r["J"], 0)], -1)
+        assert np.array_equal(idx_p[1, i].cpu().numpy(), want)
