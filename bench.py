@@ -54,7 +54,9 @@ def _describe_sem(wl):
             f"{wl.n_cluster} keys pooled {wl.n_pool}:1 into {wl.n_cluster // wl.n_bavg} Ward buckets "
             f"(cap {wl.n_bmax} keys), top {wl.p_top} buckets -> k={wl.k} long-range keys + {wl.n_sink} sinks + "
             f"a {wl.n_cluster}-key window; attention {wl.H_q} bf16 query heads / 1 KV head d={wl.d}; "
-            f"bucket cache built before timing")
+            f"bucket cache built before timing"
+            + (f"; paged storage: keys, K and V in pools of {wl.page_size}-token pages ({wl.spare_pages} spare), "
+               f"the bucket cache in a pool of entries behind a block table" if wl.page_size else ""))
 
 
 # Stage events are recorded on every EVENTS_EVERY-th timed step only: an event recorded
@@ -290,12 +292,13 @@ class SemStep:
             evs[e].record(st)
         if self.chunk_blocks:
             self.lsa.lsa_semantic_cache(self.inp["k_sem"], cache=self.cache, first_block=self.chunk_blocks[0],
-                                        n_update=self.chunk_blocks[1])
+                                        n_update=self.chunk_blocks[1], paged=self.inp.get("paged"))
             if record:
                 e += 1
                 evs[e].record(st)
         self.lsa.lsa_semantic_select(self.inp["q_sem"], self.inp["q_pos"], self.cache, wl.k, wl.p_top, wl.n_sink,
-                                     wl.n_cluster, idx=self.idx, count=self.count, ws=self.ws)
+                                     wl.n_cluster, idx=self.idx, count=self.count, ws=self.ws,
+                                     paged=self.inp.get("paged"))
         if record:
             e += 1
             evs[e].record(st)
@@ -327,19 +330,22 @@ def sem_algorithmic(wl):
 def measure_sem(lsa, torch, wl, steps, warmup):
     import synthetic
     dev = torch.device("cuda:0")
-    inp = synthetic.make_inputs(wl, dev)
+    inp = synthetic.make_inputs(wl.replace(page_size=0), dev)
     inp.update(synthetic.semantic_inputs(wl, dev))
     del inp["q_idx"], inp["k_idx"]
     prm = (wl.n_cluster, wl.n_pool, wl.n_bavg, wl.n_bmax)
+    if wl.page_size:
+        inp = synthetic.semantic_paged(inp, wl.page_size, wl.spare_pages, wl.L // wl.n_cluster)
+    paged = inp.get("paged")
     torch.cuda.synchronize()
     # the whole bucket cache once (every complete block of every sequence), then the
     # launch a decode step pays every n_cluster tokens: one new block per sequence
     e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     e[0].record()
-    cache = lsa.lsa_semantic_cache(inp["k_sem"], *prm)
+    cache = lsa.lsa_semantic_cache(inp["k_sem"], *prm, paged=paged, n_bslots=inp.get("n_bslots"))
     e[1].record()
-    nb = cache["table"].shape[1]
-    lsa.lsa_semantic_cache(inp["k_sem"], cache=cache, first_block=nb - 1, n_update=1)
+    nb = cache.get("NB", cache["table"].shape[1])
+    lsa.lsa_semantic_cache(inp["k_sem"], cache=cache, first_block=nb - 1, n_update=1, paged=paged)
     e[2].record()
     torch.cuda.synchronize()
     cluster = {"full_cache_ms": e[0].elapsed_time(e[1]), "blocks": wl.B * nb,
@@ -522,7 +528,8 @@ def main():
     torch.cuda.empty_cache()
 
     # ---- the pages' own method: flat semantic search at 128K, decode and a prefill chunk
-    for name, unit in (("decode_128k_lsa", "tok/s"), ("prefill_128k_lsa", "queries/s")):
+    for name, unit in (("decode_128k_lsa", "tok/s"), ("decode_128k_lsa_paged", "tok/s"),
+                       ("prefill_128k_lsa", "queries/s")):
         ws_ = synthetic.WORKLOADS[name]
         inp, step, ms_s, cluster = measure_sem(lsa, torch, ws_, args.steps, args.warmup)
         res[name] = {

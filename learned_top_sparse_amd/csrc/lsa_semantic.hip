@@ -391,15 +391,21 @@ __global__ __launch_bounds__(256) void sem_score_decode_kernel(const unsigned sh
   if (blk0 >= NB) return;
   const int p = q_pos[(long long)b * n_q + i0];
   const int own = p < 0 ? 0 : p / n_cluster;
-  int blk_end = blk0 + bpw;
+  int blk_end = blk0 + (bpw < 4 ? bpw : 4);
   blk_end = blk_end < NB ? blk_end : NB;
   blk_end = blk_end < own ? blk_end : own;
   if (blk0 >= blk_end) return;
 
+  // the wave's (at most 4) blocks: cache entries looked up before any centroid load,
+  // the next ones kept in three rotating registers
   const uint4* c4 = reinterpret_cast<const uint4*>(cent);
+  const long long s0 = pg.slot(b, NB, blk0);
+  long long s1 = blk0 + 1 < blk_end ? pg.slot(b, NB, blk0 + 1) : 0;
+  long long s2 = blk0 + 2 < blk_end ? pg.slot(b, NB, blk0 + 2) : 0;
+  long long s3 = blk0 + 3 < blk_end ? pg.slot(b, NB, blk0 + 3) : 0;
   uint4 nxt[8];
   {
-    const uint4* cb = c4 + pg.slot(b, NB, blk0) * (SEM_D * SEM_SLOTS / 8);
+    const uint4* cb = c4 + s0 * (SEM_D * SEM_SLOTS / 8);
 #pragma unroll
     for (int c = 0; c < 8; ++c) nxt[c] = cb[c * SEM_SLOTS + lane];
   }
@@ -415,15 +421,18 @@ __global__ __launch_bounds__(256) void sem_score_decode_kernel(const unsigned sh
 #pragma unroll
   for (int d = 0; d < SEM_D; ++d) q[d] = __shfl(y, d);
 
+#pragma unroll 1
   for (int blk = blk0; blk < blk_end; ++blk) {
     float cv[SEM_D];
 #pragma unroll
     for (int c = 0; c < 8; ++c) unpack8(nxt[c], cv + 8 * c);
     if (blk + 1 < blk_end) {
-      const uint4* cb = c4 + pg.slot(b, NB, blk + 1) * (SEM_D * SEM_SLOTS / 8);
+      const uint4* cb = c4 + s1 * (SEM_D * SEM_SLOTS / 8);
 #pragma unroll
       for (int c = 0; c < 8; ++c) nxt[c] = cb[c * SEM_SLOTS + lane];
     }
+    s1 = s2;
+    s2 = s3;
     float acc = 0.f;
 #pragma unroll
     for (int d = 0; d < SEM_D; ++d) acc = fmaf(q[d], cv[d], acc);
@@ -448,27 +457,36 @@ __global__ __launch_bounds__(256) void sem_score_kernel(const float* __restrict_
     const int o = p < 0 ? 0 : p / n_cluster;
     own_max = o > own_max ? o : own_max;
   }
-  int blk_end = blk0 + bpw;
+  int blk_end = blk0 + (bpw < 4 ? bpw : 4);
   blk_end = blk_end < NB ? blk_end : NB;
   blk_end = blk_end < own_max ? blk_end : own_max;
   if (blk0 >= blk_end) return;
 
+  // the wave's (at most 4) blocks: cache entries looked up before any centroid load,
+  // the next ones kept in three rotating registers
   const uint4* c4 = reinterpret_cast<const uint4*>(cent);
+  const long long s0 = pg.slot(b, NB, blk0);
+  long long s1 = blk0 + 1 < blk_end ? pg.slot(b, NB, blk0 + 1) : 0;
+  long long s2 = blk0 + 2 < blk_end ? pg.slot(b, NB, blk0 + 2) : 0;
+  long long s3 = blk0 + 3 < blk_end ? pg.slot(b, NB, blk0 + 3) : 0;
   uint4 nxt[8];
   {
-    const uint4* cb = c4 + pg.slot(b, NB, blk0) * (SEM_D * SEM_SLOTS / 8);
+    const uint4* cb = c4 + s0 * (SEM_D * SEM_SLOTS / 8);
 #pragma unroll
     for (int c = 0; c < 8; ++c) nxt[c] = cb[c * SEM_SLOTS + lane];
   }
+#pragma unroll 1
   for (int blk = blk0; blk < blk_end; ++blk) {
     float cv[SEM_D];
 #pragma unroll
     for (int c = 0; c < 8; ++c) unpack8(nxt[c], cv + 8 * c);
     if (blk + 1 < blk_end) {
-      const uint4* cb = c4 + pg.slot(b, NB, blk + 1) * (SEM_D * SEM_SLOTS / 8);
+      const uint4* cb = c4 + s1 * (SEM_D * SEM_SLOTS / 8);
 #pragma unroll
       for (int c = 0; c < 8; ++c) nxt[c] = cb[c * SEM_SLOTS + lane];
     }
+    s1 = s2;
+    s2 = s3;
     for (int qi = 0; qi < QT; ++qi) {
       const int i = q0 + qi;
       if (i >= nqc) break;
@@ -493,6 +511,7 @@ __global__ __launch_bounds__(256) void sem_score_kernel(const float* __restrict_
 
 constexpr int SEM_PMAX = 2048;
 constexpr int SEM_KMAX = 4096;
+constexpr int SEM_LPT = 4096;  // page-table entries of one sequence staged in LDS (256K keys of 64-key pages)
 
 __global__ __launch_bounds__(SEL_NT) void sem_select_stream_kernel(const float* __restrict__ S, long long ld,
                                                             const int* __restrict__ q_pos, int n_q, int i0, int nqc,
@@ -704,7 +723,7 @@ struct SelLbm {
   static constexpr int WORDS = 256 * C;  // positions < 8192 * C: n_bavg = 8 fills it
 };
 
-template <int NT, int C, int MINW>
+template <int NT, int C, int MINW, bool PAGED>
 __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __restrict__ S, long long ld,
                                                              const int* __restrict__ q_pos, int n_q, int i0, int nqc,
                                                              const int* __restrict__ table,
@@ -721,6 +740,7 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
   __shared__ int scan_tmp[NT / 64];
   __shared__ int sh[4];
   __shared__ unsigned long long shu[2];
+  __shared__ int lpt[PAGED ? SEM_LPT : 1];  // the sequence's page-table row (clamped), when it fits
 
   const int t = threadIdx.x;
   const int i = blockIdx.x, b = blockIdx.y;
@@ -737,6 +757,15 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
   const int N = nb * m;
   const float* row = S + ((long long)b * nqc + i) * ld;
   const int w0 = p - n_w + 1 > 0 ? p - n_w + 1 : 0;
+  const bool lds_pt = PAGED && pg.pt && pg.max_pages <= SEM_LPT;
+  const int pmask = (1 << pg.plog2) - 1;
+  auto entry = [&](int j) -> int {
+    if (!PAGED) return j;
+    if (!lds_pt) return pg.list_entry(b, j);
+    int pi = j >> pg.plog2;
+    pi = pi < pg.max_pages ? pi : pg.max_pages - 1;
+    return (lpt[pi] << pg.plog2) | (j & pmask);
+  };
 
   // 1. the kept buckets, marked in bm by bucket id
   unsigned long long key[C];
@@ -750,6 +779,13 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
       vmask |= 1u << c;
     }
   }
+  // the page-table row, staged for the list's pool rows at the end (read after the
+  // barriers of the steps below)
+  if (lds_pt)
+    for (int x = t; x < pg.max_pages; x += NT) {
+      long long v = pg.pt[(long long)b * pg.max_pages + x];
+      lpt[x] = (int)(v < 0 ? 0 : (v >= pg.n_pages ? pg.n_pages - 1 : v));
+    }
   if (N > p_top) {
     int need_eq;
     const unsigned long long T = radix_cut64<NT, C>(key, vmask, p_top, hist, scan_tmp, sh, shu, &need_eq);
@@ -841,7 +877,7 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
     if (e >= per || r >= nk) continue;
     const int gid = (int)(0xFFFFFFFFu - (unsigned)(K[r] & 0xFFFFFFFFull));
     const int blk = gid / m, loc = gid - blk * m;
-    const long long sl = pg.slot(b, NB, blk);
+    const long long sl = PAGED ? pg.slot(b, NB, blk) : (long long)b * NB + blk;
     const int* ob = offs + sl * (m + 1);
     const int o0 = ob[loc], o1 = ob[loc + 1];
     o_start[e] = sl * n_cluster + o0;
@@ -889,12 +925,12 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
   }
   __syncthreads();
   const int n_s = n_sink < w0 ? n_sink : w0;
-  emit_marked<NT>(lbm, nlw, scan_tmp, [&](int r, int pos) { out[n_s + r] = pg.list_entry(b, pos); });
+  emit_marked<NT>(lbm, nlw, scan_tmp, [&](int r, int pos) { out[n_s + r] = entry(pos); });
   const int n_win = p - w0 + 1;
   const int cnt_all = n_s + n_lr + n_win;
   for (int j = t; j < W; j += NT) {
-    if (j < n_s) out[j] = pg.list_entry(b, j);
-    else if (j >= n_s + n_lr) out[j] = j < cnt_all ? pg.list_entry(b, w0 + (j - n_s - n_lr)) : -1;
+    if (j < n_s) out[j] = entry(j);
+    else if (j >= n_s + n_lr) out[j] = j < cnt_all ? entry(w0 + (j - n_s - n_lr)) : -1;
   }
   if (t == 0) count[qrow] = cnt_all;
 }
@@ -975,10 +1011,18 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
     auto fits = [&](int nt, int C) {
       return n_max <= (long long)nt * C && pos_max <= 32LL * 256 * C && a.sp.n_bmax <= 64;
     };
-#define LSA_SEM_SEL(NT, C, MINW)                                                                               \
-  hipLaunchKernelGGL((sem_select_kernel<NT, C, MINW>), dim3(nqc, a.B), dim3(NT), 0, st, S, ld, a.q_pos, a.n_q,   \
-                     i0, nqc, a.table, a.offs, a.NB, m, a.sp.n_cluster, a.sp.n_bmax, a.k, a.p_top, a.n_sink, a.n_w, \
-                     W, a.idx, a.count, pg)
+    const bool paged = pg.bt || pg.pt;
+#define LSA_SEM_SEL1(NT, C, MINW, PG)                                                                          \
+  hipLaunchKernelGGL((sem_select_kernel<NT, C, MINW, PG>), dim3(nqc, a.B), dim3(NT), 0, st, S, ld, a.q_pos,      \
+                     a.n_q, i0, nqc, a.table, a.offs, a.NB, m, a.sp.n_cluster, a.sp.n_bmax, a.k, a.p_top, a.n_sink, \
+                     a.n_w, W, a.idx, a.count, pg)
+#define LSA_SEM_SEL(NT, C, MINW)           \
+  do {                                     \
+    if (paged)                             \
+      LSA_SEM_SEL1(NT, C, MINW, true);     \
+    else                                   \
+      LSA_SEM_SEL1(NT, C, MINW, false);    \
+  } while (0)
     if (many && fits(1024, 4)) LSA_SEM_SEL(1024, 4, 8);
     else if (many && fits(1024, 8)) LSA_SEM_SEL(1024, 8, 8);
     else if (many && fits(1024, 16)) LSA_SEM_SEL(1024, 16, 8);
@@ -991,6 +1035,7 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
                          nqc, pg, a.table, a.offs, a.NB, m, a.sp.n_cluster, a.k, a.p_top, a.n_sink, a.n_w, W, a.idx,
                          a.count);
 #undef LSA_SEM_SEL
+#undef LSA_SEM_SEL1
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -25,7 +25,7 @@ import torch
 
 IDS = {"q_idx": 1, "k_idx": 2, "w": 3, "q": 4, "k": 5, "v": 6,
        "pages": 7, "pool_k_idx": 8, "pool_k": 9, "pool_v": 10,
-       "sem_topics": 11, "k_sem": 12, "q_sem": 13}
+       "sem_topics": 11, "k_sem": 12, "q_sem": 13, "sem_blocks": 14, "pool_k_sem": 15}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -104,6 +104,11 @@ WORKLOADS = {
     # 512-key window
     "decode_128k_lsa": Workload("decode_128k_lsa", B=64, n_q=1, L=131073, q_pos0=131072,
                                 H_I=1, d_I=64, k=2048, H_q=16, semantic=True),
+    # decode_128k_lsa over paged storage: keys, K and V in pools of 64-token pages (4096
+    # spare pages), the bucket cache in a pool of entries behind a block table
+    "decode_128k_lsa_paged": Workload("decode_128k_lsa_paged", B=64, n_q=1, L=131073, q_pos0=131072,
+                                      H_I=1, d_I=64, k=2048, H_q=16, semantic=True, page_size=64,
+                                      spare_pages=4096),
     # the same search for the final 8192 queries of a 128K prefill
     "prefill_128k_lsa": Workload("prefill_128k_lsa", B=1, n_q=8192, L=131072, q_pos0=122880,
                                  H_I=1, d_I=64, k=2048, H_q=16, semantic=True),
@@ -235,6 +240,39 @@ def semantic_inputs(wl: Workload, device="cpu", seed: Optional[int] = None, n_to
     q_sem = (c[q_topic.to(device)] + noise * torch.randn((wl.B, wl.n_q, 64), generator=gq, device=device,
                                                          dtype=torch.float32)).to(torch.bfloat16)
     return {"k_sem": k_sem, "q_sem": q_sem, "q_pos": q_positions(wl, device)}
+
+
+def semantic_paged(inp: dict, page_size: int, spare_pages: int, n_blocks: int, seed: int = 0) -> dict:
+    """The semantic inputs of ``inp`` (k_sem, k, v: [B, L, .]) over paged storage: the
+    caches scattered over pools of pages in a seeded order (as paged_pool), and a block
+    table naming, in a seeded order, the bucket-cache entry of each of the n_blocks
+    cluster blocks of every sequence (a pool of B * n_blocks + 16 entries).  Returns a
+    copy with k_sem, k, v replaced by pools [n_slots, .] and paged = dict(block_table,
+    page_table, page_size, n_slots), n_bslots.  It moves data only."""
+    k_sem = inp["k_sem"]
+    device = k_sem.device
+    B, L, _ = k_sem.shape
+    max_pages = -(-L // page_size)
+    n_pages = B * max_pages + spare_pages
+    g = torch.Generator().manual_seed(seed * 16 + IDS["pages"])
+    page_table = torch.randperm(n_pages, generator=g)[: B * max_pages].to(torch.int32).view(B, max_pages)
+    page_table = page_table.contiguous().to(device)
+    n_slots = n_pages * page_size
+    j = torch.arange(L, device=device, dtype=torch.int64)
+    rows = (page_table.long()[:, j // page_size] * page_size + j % page_size).reshape(-1)
+    out = dict(inp)
+    for name, tid in (("k_sem", "pool_k_sem"), ("k", "pool_k"), ("v", "pool_v")):
+        t = inp[name]
+        pool = _randn_bf16((n_slots, t.shape[-1]), seed, IDS[tid], device)
+        pool.index_copy_(0, rows, t.reshape(B * L, t.shape[-1]))
+        out[name] = pool
+    gb = torch.Generator().manual_seed(seed * 16 + IDS["sem_blocks"])
+    n_bslots = B * n_blocks + 16
+    block_table = torch.randperm(n_bslots, generator=gb)[: B * n_blocks].to(torch.int32).view(B, n_blocks)
+    out["paged"] = {"block_table": block_table.contiguous().to(device), "page_table": page_table,
+                    "page_size": page_size, "n_slots": n_slots}
+    out["n_bslots"] = n_bslots
+    return out
 
 
 def checked_rows(wl: Workload, n_random: int = 56, seed: int = 0) -> list:

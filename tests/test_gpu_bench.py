@@ -27,6 +27,7 @@ def test_bench_headline_line():
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["value"] > 0
     r = d["roofline"]
     assert r["bound"] in ("hbm", "mfma", "alu") and 0 < r["frac"] < 1.5 and r["peak"] > 0
-    for wl in ("decode_128k_paged", "decode_128k_pool4", "prefill_128k", "decode_128k_lsa", "prefill_128k_lsa"):
+    for wl in ("decode_128k_paged", "decode_128k_pool4", "prefill_128k", "decode_128k_lsa", "decode_128k_lsa_paged",
+               "prefill_128k_lsa"):
         assert d[wl]["ms_per_step"] > 0 and d[wl]["kernel_ms"], wl
     assert 0 < d["prefill_128k"]["roofline"]["frac"] < 1.5
