@@ -416,10 +416,10 @@ __global__ __launch_bounds__(256) void sem_score_decode_kernel(const unsigned sh
 #pragma unroll
   for (int d = 0; d < SEM_D; ++d) ss = ss + __shfl(sq, d);
   const float nrm = sqrtf(ss);
-  const float y = __uint_as_float(to_bf16(nrm > 0.f ? x / nrm : 0.f) << 16);
-  float q[SEM_D];
+  const int yb = (int)(to_bf16(nrm > 0.f ? x / nrm : 0.f) << 16);
+  float q[SEM_D];  // wave-uniform: scalar registers
 #pragma unroll
-  for (int d = 0; d < SEM_D; ++d) q[d] = __shfl(y, d);
+  for (int d = 0; d < SEM_D; ++d) q[d] = __int_as_float(__builtin_amdgcn_readlane(yb, d));
 
 #pragma unroll 1
   for (int blk = blk0; blk < blk_end; ++blk) {
