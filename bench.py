@@ -529,7 +529,7 @@ def main():
 
     # ---- the pages' own method: flat semantic search at 128K, decode and a prefill chunk
     for name, unit in (("decode_128k_lsa", "tok/s"), ("decode_128k_lsa_paged", "tok/s"),
-                       ("prefill_128k_lsa", "queries/s")):
+                       ("prefill_128k_lsa", "queries/s"), ("decode_1m_lsa", "tok/s")):
         ws_ = synthetic.WORKLOADS[name]
         inp, step, ms_s, cluster = measure_sem(lsa, torch, ws_, args.steps, args.warmup)
         res[name] = {

@@ -511,7 +511,8 @@ __global__ __launch_bounds__(256) void sem_score_kernel(const float* __restrict_
 
 constexpr int SEM_PMAX = 2048;
 constexpr int SEM_KMAX = 4096;
-constexpr int SEM_LPT = 4096;  // page-table entries of one sequence staged in LDS (256K keys of 64-key pages)
+constexpr int SEM_LPT = 4096;
+constexpr int SEM_KC = 8192;   // candidates of a long row's chunks (chunks * p_top at most)  // page-table entries of one sequence staged in LDS (256K keys of 64-key pages)
 
 __global__ __launch_bounds__(SEL_NT) void sem_select_stream_kernel(const float* __restrict__ S, long long ld,
                                                             const int* __restrict__ q_pos, int n_q, int i0, int nqc,
@@ -707,6 +708,64 @@ __global__ __launch_bounds__(SEL_NT) void sem_select_stream_kernel(const float* 
 }
 
 
+// Long rows with few queries: one workgroup per (span of SPAN_B buckets, query) keeps the
+// span's top-p (registers, radix cut, ties to the lowest id) and writes them as packed
+// keys over the start of its own span of the score row, after a count: [count][keys...]
+// (the span is read whole before anything is written; spans are disjoint).
+constexpr int SPAN_B = 1024 * 16;
+__global__ __launch_bounds__(1024) void sem_span_topk_kernel(float* __restrict__ S, long long ld,
+                                                             const int* __restrict__ q_pos, int n_q, int i0, int nqc,
+                                                             int NB, int m, int n_cluster, int p_top) {
+  constexpr int NT = 1024, C = 16, NWD = NT * C / 32;
+  __shared__ int hist[2048];
+  __shared__ unsigned bm[NWD], eqm[NWD];
+  __shared__ int scan_tmp[NT / 64];
+  __shared__ int sh[4];
+  __shared__ unsigned long long shu[2];
+  const int t = threadIdx.x, span = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
+  const int p = q_pos[(long long)b * n_q + i0 + i];
+  if (p < 0) return;
+  int nb = p / n_cluster;
+  nb = nb < NB ? nb : NB;
+  const int N = nb * m, base = span * SPAN_B;
+  if (base >= N) return;
+  float* row = S + ((long long)b * nqc + i) * ld;
+  unsigned long long key[C];
+  unsigned vmask = 0u;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int j = base + c * NT + t;
+    key[c] = 0ull;
+    if (j < N) {
+      key[c] = order_key(row[j]);
+      vmask |= 1u << c;
+    }
+  }
+  const int Nc = N - base < SPAN_B ? N - base : SPAN_B;
+  if (Nc > p_top) {
+    int need_eq;
+    const unsigned long long T = radix_cut64<NT, C>(key, vmask, p_top, hist, scan_tmp, sh, shu, &need_eq);
+    mark_kept64<NT, C>(key, vmask, T, need_eq, bm, eqm, scan_tmp);
+  }
+  if (t == 0) sh[2] = 0;
+  __syncthreads();  // every score of the span is in registers before the span is overwritten
+  unsigned long long* out = reinterpret_cast<unsigned long long*>(row + base);
+  const int lane = t & 63;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int pos = c * NT + t;
+    const bool kept = ((vmask >> c) & 1u) && (Nc <= p_top || ((bm[pos >> 5] >> (pos & 31)) & 1u));
+    const unsigned long long ball = __ballot(kept);
+    if (ball == 0ull) continue;
+    int slot0 = 0;
+    if (lane == 0) slot0 = atomicAdd(&sh[2], __popcll(ball));
+    slot0 = __shfl(slot0, 0);
+    if (kept) out[1 + slot0 + lanes_below(ball)] = (key[c] << 32) | (0xFFFFFFFFu - (unsigned)(base + pos));
+  }
+  __syncthreads();
+  if (t == 0) out[0] = (unsigned long long)sh[2];
+}
+
 // Selection and expansion of rows of at most NT * C buckets whose long-range keys lie
 // below 32 * SelLbm<C>::WORDS positions: one NT-thread workgroup per query, the row's
 // order keys in registers (bucket c * NT + t in slot c of thread t).  The cut is a
@@ -723,20 +782,22 @@ struct SelLbm {
   static constexpr int WORDS = 256 * C;  // positions < 8192 * C: n_bavg = 8 fills it
 };
 
-template <int NT, int C, int MINW, bool PAGED>
+template <int NT, int C, int MINW, bool PAGED, bool LONG>
 __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __restrict__ S, long long ld,
                                                              const int* __restrict__ q_pos, int n_q, int i0, int nqc,
                                                              const int* __restrict__ table,
                                                              const int* __restrict__ offs, int NB, int m,
                                                              int n_cluster, int n_bmax, int k, int p_top, int n_sink,
                                                              int n_w, int W, int* __restrict__ idx,
-                                                             int* __restrict__ count, SemPaging pg) {
+                                                             int* __restrict__ count, SemPaging pg, int split) {
   constexpr int NWD = NT * C / 32;
   constexpr int LW = SelLbm<C>::WORDS;
   __shared__ unsigned long long K[SEM_PMAX];
   __shared__ int hist[2048];
   __shared__ unsigned bm[NWD], eqm[NWD];
-  __shared__ unsigned lbm[LW];
+  __shared__ unsigned lbm[LONG ? 1 : LW];
+  __shared__ unsigned long long Kc[LONG ? SEM_KC : 1];  // chunks' candidates (long rows)
+  __shared__ int LRs[LONG ? SEM_KMAX : 1];               // long-range keys to sort (long rows)
   __shared__ int scan_tmp[NT / 64];
   __shared__ int sh[4];
   __shared__ unsigned long long shu[2];
@@ -768,6 +829,100 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
   };
 
   // 1. the kept buckets, marked in bm by bucket id
+  int nk;
+  if constexpr (LONG) {
+    // rows longer than the registers hold: every chunk of NT * C buckets keeps its own
+    // top-p (the row's top-p is among them), as packed keys with the global bucket id
+    if (lds_pt)
+      for (int x = t; x < pg.max_pages; x += NT) {
+        long long v = pg.pt[(long long)b * pg.max_pages + x];
+        lpt[x] = (int)(v < 0 ? 0 : (v >= pg.n_pages ? pg.n_pages - 1 : v));
+      }
+    constexpr int CH = NT * C;
+    if (t == 0) sh[3] = 0;
+    const int lane = t & 63;
+    if (split) {
+      // the spans' candidates, left in the score row by sem_span_topk_kernel (every
+      // thread reads every count, so all keep the same running offset)
+      int off = 0;
+      for (int base = 0; base < N; base += SPAN_B) {
+        const unsigned long long* cin = reinterpret_cast<const unsigned long long*>(row + base);
+        const int cnt_s = (int)cin[0];
+        for (int x = t; x < cnt_s; x += NT) Kc[off + x] = cin[1 + x];
+        off += cnt_s;
+      }
+      __syncthreads();
+      if (t == 0) sh[3] = off;
+      __syncthreads();
+    }
+    for (int base = 0; base < (split ? 0 : N); base += CH) {
+      unsigned long long key[C];
+      unsigned vmask = 0u;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int j = base + c * NT + t;
+        key[c] = 0ull;
+        if (j < N) {
+          key[c] = order_key(row[j]);
+          vmask |= 1u << c;
+        }
+      }
+      const int Nc = N - base < CH ? N - base : CH;
+      if (Nc > p_top) {
+        int need_eq;
+        const unsigned long long T = radix_cut64<NT, C>(key, vmask, p_top, hist, scan_tmp, sh, shu, &need_eq);
+        mark_kept64<NT, C>(key, vmask, T, need_eq, bm, eqm, scan_tmp);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int pos = c * NT + t;
+        const bool kept = ((vmask >> c) & 1u) && (Nc <= p_top || ((bm[pos >> 5] >> (pos & 31)) & 1u));
+        const unsigned long long ball = __ballot(kept);
+        if (ball == 0ull) continue;
+        int slot0 = 0;
+        if (lane == 0) slot0 = atomicAdd(&sh[3], __popcll(ball));
+        slot0 = __shfl(slot0, 0);
+        if (kept) Kc[slot0 + lanes_below(ball)] = (key[c] << 32) | (0xFFFFFFFFu - (unsigned)(base + pos));
+      }
+      __syncthreads();
+    }
+    // the row's top-p among the candidates (packed keys are distinct: no ties)
+    const int ncand = sh[3];
+    if (ncand > p_top) {
+      constexpr int C2 = SEM_KC / NT;
+      unsigned long long k2[C2];
+      unsigned vm2 = 0u;
+#pragma unroll
+      for (int c = 0; c < C2; ++c) {
+        const int x = c * NT + t;
+        k2[c] = x < ncand ? Kc[x] : 0ull;
+        if (x < ncand) vm2 |= 1u << c;
+      }
+      int need_eq;
+      const unsigned long long T2 = radix_cut64<NT, C2>(k2, vm2, p_top, hist, scan_tmp, sh, shu, &need_eq);
+      mark_kept64<NT, C2>(k2, vm2, T2, need_eq, bm, eqm, scan_tmp);
+      if (t == 0) sh[2] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < C2; ++c) {
+        const int pos = c * NT + t;
+        const bool kept = ((vm2 >> c) & 1u) && ((bm[pos >> 5] >> (pos & 31)) & 1u);
+        const unsigned long long ball = __ballot(kept);
+        if (ball == 0ull) continue;
+        int slot0 = 0;
+        if (lane == 0) slot0 = atomicAdd(&sh[2], __popcll(ball));
+        slot0 = __shfl(slot0, 0);
+        if (kept) K[slot0 + lanes_below(ball)] = k2[c];
+      }
+      __syncthreads();
+      nk = sh[2];
+    } else {
+      for (int x = t; x < ncand; x += NT) K[x] = Kc[x];
+      __syncthreads();
+      nk = ncand;
+    }
+  } else {
   unsigned long long key[C];
   unsigned vmask = 0u;
 #pragma unroll
@@ -808,7 +963,8 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
     if (kept) K[base + lanes_below(ball)] = (key[c] << 32) | (0xFFFFFFFFu - (unsigned)pos);
   }
   __syncthreads();
-  const int nk = sh[2];
+  nk = sh[2];
+  }
 
   // 2. best first: bitonic sort of the packed keys, descending (padding 0 sorts last);
   //    one key per thread, exchanges under 64 apart by lane shuffles, wider ones
@@ -861,7 +1017,8 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
   // long-range keys lie below both the window and the end of the scored blocks
   const int pos_lim = w0 < nb * n_cluster ? w0 : nb * n_cluster;
   const int nlw = (pos_lim + 31) >> 5;
-  for (int wd = t; wd < nlw; wd += NT) lbm[wd] = 0u;
+  if constexpr (!LONG)
+    for (int wd = t; wd < nlw; wd += NT) lbm[wd] = 0u;
   constexpr int OWN = SEM_PMAX / NT;  // buckets a thread owns, at most
   const int per = (nk + NT - 1) / NT;
   long long o_start[OWN];
@@ -916,8 +1073,15 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           const int sl = base + x;
-          if (sl < o_size[e] && ((msk >> sl) & 1ull) && __popcll(msk & ((1ull << sl) - 1ull)) < take)
-            atomicOr(&lbm[v[x] >> 5], 1u << (v[x] & 31));
+          if (sl < o_size[e] && ((msk >> sl) & 1ull)) {
+            const int rank = __popcll(msk & ((1ull << sl) - 1ull));
+            if (rank < take) {
+              if constexpr (LONG)
+                LRs[e0 + rank] = v[x];
+              else
+                atomicOr(&lbm[v[x] >> 5], 1u << (v[x] & 31));
+            }
+          }
         }
       }
     }
@@ -925,7 +1089,31 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
   }
   __syncthreads();
   const int n_s = n_sink < w0 ? n_sink : w0;
-  emit_marked<NT>(lbm, nlw, scan_tmp, [&](int r, int pos) { out[n_s + r] = entry(pos); });
+  if constexpr (LONG) {
+    // the long-range keys ascending: bitonic sort in LDS (padding sorts last)
+    int Q2 = 1;
+    while (Q2 < n_lr) Q2 <<= 1;
+    for (int x = n_lr + t; x < Q2; x += NT) LRs[x] = 0x7FFFFFFF;
+    __syncthreads();
+    for (int kk = 2; kk <= Q2; kk <<= 1)
+      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+        for (int x = t; x < Q2; x += NT) {
+          const int y = x ^ jj;
+          if (y > x) {
+            const int a0 = LRs[x], a1 = LRs[y];
+            const bool asc = (x & kk) == 0;
+            if (asc ? (a0 > a1) : (a0 < a1)) {
+              LRs[x] = a1;
+              LRs[y] = a0;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    for (int r = t; r < n_lr; r += NT) out[n_s + r] = entry(LRs[r]);
+  } else {
+    emit_marked<NT>(lbm, nlw, scan_tmp, [&](int r, int pos) { out[n_s + r] = entry(pos); });
+  }
   const int n_win = p - w0 + 1;
   const int cnt_all = n_s + n_lr + n_win;
   for (int j = t; j < W; j += NT) {
@@ -967,7 +1155,14 @@ hipError_t launch_sem_cluster(const void* k_idx, int B, int L_max, const SemPara
   return hipGetLastError();
 }
 
-long long sem_ld(int NB, int m) { return (((long long)NB * m) + 3) / 4 * 4; }
+// Score-row stride: a row's buckets, and for rows that may exceed 32768 buckets (the
+// span path) room for the last span's candidates, which take 2 * (kept + 1) floats
+// where a short last span may hold fewer scores than that.
+long long sem_ld(int NB, int m) {
+  long long n = (long long)NB * m;
+  if (n > 32768) n += 2 * (SEM_MAX_P + 1);
+  return (n + 3) / 4 * 4;
+}
 
 size_t sem_select_row_bytes(int NB, int m) { return (size_t)SEM_D * 4 + (size_t)sem_ld(NB, m) * 4; }
 
@@ -1012,10 +1207,12 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
       return n_max <= (long long)nt * C && pos_max <= 32LL * 256 * C && a.sp.n_bmax <= 64;
     };
     const bool paged = pg.bt || pg.pt;
-#define LSA_SEM_SEL1(NT, C, MINW, PG)                                                                          \
-  hipLaunchKernelGGL((sem_select_kernel<NT, C, MINW, PG>), dim3(nqc, a.B), dim3(NT), 0, st, S, ld, a.q_pos,      \
+    int split = 0;
+#define LSA_SEM_SEL1(NT, C, MINW, PG)  LSA_SEM_SEL2(NT, C, MINW, PG, false)
+#define LSA_SEM_SEL2(NT, C, MINW, PG, LG)                                                                      \
+  hipLaunchKernelGGL((sem_select_kernel<NT, C, MINW, PG, LG>), dim3(nqc, a.B), dim3(NT), 0, st, S, ld, a.q_pos,  \
                      a.n_q, i0, nqc, a.table, a.offs, a.NB, m, a.sp.n_cluster, a.sp.n_bmax, a.k, a.p_top, a.n_sink, \
-                     a.n_w, W, a.idx, a.count, pg)
+                     a.n_w, W, a.idx, a.count, pg, split)
 #define LSA_SEM_SEL(NT, C, MINW)           \
   do {                                     \
     if (paged)                             \
@@ -1030,12 +1227,27 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
     else if (fits(1024, 8)) LSA_SEM_SEL(1024, 8, 1);
     else if (fits(1024, 16)) LSA_SEM_SEL(1024, 16, 1);
     else if (fits(1024, 32)) LSA_SEM_SEL(1024, 32, 1);
-    else
+    else if (a.sp.n_bmax <= 64 && (n_max + SPAN_B - 1) / SPAN_B * a.p_top <= SEM_KC) {
+      // long rows: spans of 16384 buckets in registers, their candidates merged; with
+      // few rows the spans run as workgroups of their own (sem_span_topk_kernel), with
+      // many each row's workgroup walks them
+      if (a.B * nqc < 256) {
+        split = 1;
+        const int n_spans = (int)((n_max + SPAN_B - 1) / SPAN_B);
+        hipLaunchKernelGGL(sem_span_topk_kernel, dim3(n_spans, nqc, a.B), dim3(1024), 0, st, S, ld, a.q_pos,
+                           a.n_q, i0, nqc, a.NB, m, a.sp.n_cluster, a.p_top);
+      }
+      if (paged)
+        LSA_SEM_SEL2(1024, 16, 1, true, true);
+      else
+        LSA_SEM_SEL2(1024, 16, 1, false, true);
+    } else
       hipLaunchKernelGGL(sem_select_stream_kernel, dim3(nqc, a.B), dim3(SEL_NT), 0, st, S, ld, a.q_pos, a.n_q, i0,
                          nqc, pg, a.table, a.offs, a.NB, m, a.sp.n_cluster, a.k, a.p_top, a.n_sink, a.n_w, W, a.idx,
                          a.count);
 #undef LSA_SEM_SEL
 #undef LSA_SEM_SEL1
+#undef LSA_SEM_SEL2
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

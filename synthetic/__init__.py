@@ -109,6 +109,9 @@ WORKLOADS = {
     "decode_128k_lsa_paged": Workload("decode_128k_lsa_paged", B=64, n_q=1, L=131073, q_pos0=131072,
                                       H_I=1, d_I=64, k=2048, H_q=16, semantic=True, page_size=64,
                                       spare_pages=4096),
+    # semantic decode at 1M context: 8 sequences of 1048576 cached keys (131072 buckets a row)
+    "decode_1m_lsa": Workload("decode_1m_lsa", B=8, n_q=1, L=1048577, q_pos0=1048576,
+                              H_I=1, d_I=64, k=2048, H_q=16, semantic=True),
     # the same search for the final 8192 queries of a 128K prefill
     "prefill_128k_lsa": Workload("prefill_128k_lsa", B=1, n_q=8192, L=131072, q_pos0=122880,
                                  H_I=1, d_I=64, k=2048, H_q=16, semantic=True),

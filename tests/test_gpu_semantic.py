@@ -115,6 +115,7 @@ def _select_case(lsa, wl, prm, positions, k, p_top, n_sink, n_w, seed, ws_bytes=
     ((256, 2, 4, 16), 100, 64, 0, 300),
     ((128, 1, 2, 8), 77, 2048, 9, 1),
     ((512, 4, 8, 32), 500, 128, 4, 1),
+    ((512, 4, 8, 128), 300, 80, 4, 512),   # buckets of up to 128 keys: the streaming selection
 ])
 def test_select_matches_oracle(lsa, prm, k, p_top, n_sink, n_w):
     n_c = prm[0]
@@ -231,9 +232,9 @@ def test_prefill_128k_lsa_sampled(lsa):
 
 @pytest.mark.slow
 def test_select_long_rows(lsa):
-    """Rows of more buckets than the register-held selection takes (37440 > 32768): the
-    streaming selection, bit for bit; and buckets of 16 keys (key positions beyond the
-    smaller bitmaps)."""
+    """Rows of more buckets than the registers hold (37440 > 32768): spans of 16384
+    buckets as workgroups of their own (few rows), their candidates merged, bit for
+    bit; and buckets of 16 keys (key positions beyond the smaller bitmaps)."""
     for prm, L in (((512, 4, 8, 32), 585 * 512 + 3), ((512, 4, 16, 32), 300 * 512 + 9)):
         wl = synthetic.WORKLOADS["decode_128k_lsa"].replace(B=1, L=L, q_pos0=L - 1)
         positions = [[L - 1, L - 600, 200 * 512 + 5, 3 * 512]]
@@ -244,6 +245,26 @@ def test_select_long_rows(lsa):
             r = oracle.semantic_select_row(_f32(q[0, i]), oc, p, 2048, 512, 4, 512)
             assert np.array_equal(idx[0, i].cpu().numpy(), r["J"]), f"p={p}"
             assert int(cnt[0, i]) == r["count"]
+
+
+@pytest.mark.slow
+def test_select_long_rows_many(lsa):
+    """256 queries on rows of 37440 buckets: each row's workgroup walks the spans itself
+    (the launch has enough rows); sampled rows bit for bit."""
+    prm = (512, 4, 8, 32)
+    L = 585 * 512 + 3
+    wl = synthetic.Workload("sem_long_many", B=1, n_q=256, L=L, q_pos0=L - 256, H_I=1, d_I=64, k=2048, H_q=16,
+                            semantic=True)
+    inp = synthetic.semantic_inputs(wl, dev(), seed=14)
+    cache = lsa.lsa_semantic_cache(inp["k_sem"], *prm)
+    idx, cnt = lsa.lsa_semantic_select(inp["q_sem"], inp["q_pos"], cache, 2048, 512, 4, 512)
+    torch.cuda.synchronize()
+    oc = _oracle_cache(inp["k_sem"][0], prm, n_blocks=cache["table"].shape[1])
+    for i in (0, 1, 100, 254, 255):
+        p = int(inp["q_pos"][0, i])
+        r = oracle.semantic_select_row(_f32(inp["q_sem"][0, i]), oc, p, 2048, 512, 4, 512)
+        assert np.array_equal(idx[0, i].cpu().numpy(), r["J"]), f"i={i}"
+        assert int(cnt[0, i]) == r["count"]
 
 
 @pytest.mark.slow
