@@ -166,6 +166,15 @@ def algorithmic(wl):
     }
 
 
+def _cpu_threads():
+    """Threads the oracle's BLAS uses (the CPU baselines' core count)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(wl, inp, budget_s=10.0):
     """The oracle as it stands, on a bounded sample of the same workload's rows."""
     import numpy as np
@@ -199,11 +208,7 @@ def cpu_baseline(wl, inp, budget_s=10.0):
         if t_work > budget_s:
             break
     rate = done / t_work
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
+    cores = _cpu_threads()
     unit = "tok/s" if wl.n_q == 1 else "queries/s"
     return {"value": rate, "unit": unit, "cores": cores, "kind": "oracle",
             "sample": f"{done} row evaluations cycling over {len(rows)} seeded rows of {wl.name} (incl. boundary "
@@ -234,6 +239,61 @@ def measured_traffic():
     for f in TRAFFIC_SOURCES:
         d.update(open(os.path.join(ROOT, f), "rb").read())
     return int(m.group(1)) if d.hexdigest() == h.group(1) else None
+
+
+SEM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_128k_lsa_scan_traffic.md")
+SEM_TRAFFIC_SOURCES = ["learned_top_sparse_amd/csrc/lsa_semantic.hip"]
+
+
+def sem_measured_traffic():
+    """HBM bytes per launch of the semantic decode scan from its committed counter runs,
+    or None if its source changed since they were taken."""
+    import hashlib
+    import re
+    try:
+        txt = open(SEM_TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    f = re.search(r"^\| FETCH_SIZE \|.*\| (\d+) \|$", txt, re.M)
+    w = re.search(r"^\| WRITE_SIZE \|.*\| (\d+) \|$", txt, re.M)
+    h = re.search(r"kernel_sources_sha256: ([0-9a-f]{64})", txt)
+    if not (f and w and h):
+        return None
+    d = hashlib.sha256()
+    for fn in SEM_TRAFFIC_SOURCES:
+        d.update(open(os.path.join(ROOT, fn), "rb").read())
+    return int(f.group(1)) + int(w.group(1)) if d.hexdigest() == h.group(1) else None
+
+
+def cpu_baseline_sem(wl, inp, budget_s=10.0):
+    """The oracle as it stands on a bounded sample of the semantic decode: one sequence's
+    bucket cache clustered by the oracle (its cost spread over the n_cluster tokens a
+    block takes to complete), then that sequence's query selected and attended to
+    repeatedly for about budget_s seconds."""
+    import numpy as np
+    import oracle
+    kb = inp["k_sem"][0].float().cpu().numpy()
+    q_row = inp["q_sem"][0, 0].float().cpu().numpy()
+    qa = inp["q"][0, 0].float().cpu().numpy().astype(np.float64)
+    kc = inp["k"][0].float().cpu().numpy().astype(np.float64)
+    vc = inp["v"][0].float().cpu().numpy().astype(np.float64)
+    p = int(inp["q_pos"][0, 0])
+    t0 = time.perf_counter()
+    cache = oracle.bucket_cache(kb, wl.n_cluster, wl.n_pool, wl.n_bavg, wl.n_bmax)
+    t_cluster = time.perf_counter() - t0
+    per_block = t_cluster / cache["table"].shape[0]
+    n, t1 = 0, time.perf_counter()
+    while True:
+        oracle.semantic_forward_row(q_row, cache, p, wl.k, wl.p_top, wl.n_sink, wl.n_cluster, q_row=qa, k_cache=kc,
+                                    v_cache=vc, scale=wl.scale)
+        n += 1
+        if time.perf_counter() - t1 > budget_s:
+            break
+    per_token = (time.perf_counter() - t1) / n + per_block / wl.n_cluster
+    return {"value": 1.0 / per_token, "unit": "tok/s", "cores": _cpu_threads(), "kind": "oracle",
+            "sample": f"sequence 0 of {wl.name}: its {cache['table'].shape[0]} cluster blocks clustered by the oracle "
+                      f"in {t_cluster:.1f}s (one block per {wl.n_cluster} tokens), then {n} selections + attentions "
+                      f"of its query in {budget_s:.0f}s; rate = 1 / (time per token + clustering per token)"}
 
 
 def copy_calibration(torch, nbytes=1 << 30, reps=5):
@@ -273,7 +333,11 @@ class SemStep:
             last = min(wl.L, wl.q_pos0 + wl.n_q) // wl.n_cluster
             if last > first:
                 self.chunk_blocks = (first, last - first)
-        self.names = (["cluster"] if self.chunk_blocks else []) + ["semantic_select", "sparse_attn"]
+        # with contiguous caches the selection call records its own events around the
+        # centroid scan (lsa_semantic_select_timed)
+        self.timed = "paged" not in inp
+        sel = ["centroid_scan", "select_expand"] if self.timed else ["semantic_select"]
+        self.names = (["cluster"] if self.chunk_blocks else []) + sel + ["sparse_attn"]
         self.pool, self.steps = [], []
 
     make_events = Step.make_events
@@ -296,12 +360,18 @@ class SemStep:
             if record:
                 e += 1
                 evs[e].record(st)
-        self.lsa.lsa_semantic_select(self.inp["q_sem"], self.inp["q_pos"], self.cache, wl.k, wl.p_top, wl.n_sink,
-                                     wl.n_cluster, idx=self.idx, count=self.count, ws=self.ws,
-                                     paged=self.inp.get("paged"))
-        if record:
-            e += 1
-            evs[e].record(st)
+        if record and self.timed:
+            self.lsa.lsa_semantic_select(self.inp["q_sem"], self.inp["q_pos"], self.cache, wl.k, wl.p_top,
+                                         wl.n_sink, wl.n_cluster, idx=self.idx, count=self.count, ws=self.ws,
+                                         stage_events=(evs[e], evs[e + 1], evs[e + 2]))
+            e += 2
+        else:
+            self.lsa.lsa_semantic_select(self.inp["q_sem"], self.inp["q_pos"], self.cache, wl.k, wl.p_top,
+                                         wl.n_sink, wl.n_cluster, idx=self.idx, count=self.count, ws=self.ws,
+                                         paged=self.inp.get("paged"))
+            if record:
+                e += 1
+                evs[e].record(st)
         self.out, _ = self.lsa.lsa_sparse_attn(self.inp["q"], self.inp["k"], self.inp["v"], self.idx,
                                                scale=wl.scale, return_lse=False)
         if record:
@@ -537,6 +607,16 @@ def main():
             "ms_per_step": ms_s, "kernel_ms": step.kernel_ms(), "cluster": cluster,
             "algorithmic": sem_algorithmic(ws_),
         }
+        if name == "decode_128k_lsa":
+            km = res[name]["kernel_ms"]
+            alg_b = res[name]["algorithmic"]["centroid_bytes"]
+            ach = alg_b / (km["centroid_scan"]["ms_per_step"] * 1e-3) / 1e9
+            res[name]["roofline"] = {"bound": "hbm", "kernel": "centroid scan (sem_score_decode_kernel)",
+                                     "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": ach / HBM_PEAK_GBS, "traffic": sem_measured_traffic(),
+                                     "algorithmic_bytes_per_launch": alg_b}
+            if not args.no_cpu_baseline:
+                res[name]["cpu_baseline"] = cpu_baseline_sem(ws_, inp)
         del inp, step
         torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)

@@ -433,6 +433,16 @@ lsa_status lsa_semantic_select(const void* q_idx, const int32_t* q_pos, int32_t 
                                int32_t n_sink, int32_t n_w, int32_t* idx, int32_t* count, void* ws,
                                size_t ws_bytes, void* stream);
 
+/* lsa_semantic_select that also records three caller-created HIP events (hipEvent_t,
+   passed as void*) on the stream: events[0] before the centroid scan of the last chunk of
+   queries, events[1] after it, events[2] after the whole call -- how a benchmark times
+   the scan and the selection live.  Same lists as lsa_semantic_select. */
+lsa_status lsa_semantic_select_timed(const void* q_idx, const int32_t* q_pos, int32_t B, int32_t n_q,
+                                     int32_t d_idx, const lsa_semantic_params* prm, int32_t n_blocks,
+                                     const void* centroids, const int32_t* table, const int32_t* offsets, int32_t k,
+                                     int32_t p_top, int32_t n_sink, int32_t n_w, int32_t* idx, int32_t* count,
+                                     void* ws, size_t ws_bytes, void* stream, void* const* events);
+
 /* lsa_semantic_select over paged storage (pages != NULL; see lsa_semantic_pages): the
    cache is read through the block table, and with a page table the lists hold pool rows
    (L_max = max_pages * page_size).  Same lists as the contiguous call, mapped. */

@@ -22,7 +22,7 @@ EXPORTED = [
     "lsa_topk", "lsa_sparse_attn_workspace_size", "lsa_sparse_attn",
     "lsa_forward_workspace_size", "lsa_forward", "lsa_forward_plan", "lsa_forward_stages",
     "lsa_semantic_cluster", "lsa_semantic_select_workspace_size", "lsa_semantic_select",
-    "lsa_semantic_cluster_paged", "lsa_semantic_select_paged", "lsa_sparse_attn_pool",
+    "lsa_semantic_cluster_paged", "lsa_semantic_select_paged", "lsa_sparse_attn_pool", "lsa_semantic_select_timed",
 ]
 
 STAGE_NAMES = {1: "block_reps", 2: "block_prefilter", 3: "index_select", 4: "index_scores", 5: "topk", 7: "sample",
@@ -91,6 +91,8 @@ def lib():
         L.lsa_semantic_cluster.argtypes = [P, I32, I32, I32, SP, I32, I32, I32, P, P, P, P]
         L.lsa_semantic_select_workspace_size.argtypes = [I32, I32, I32, SP, C.POINTER(SZ)]
         L.lsa_semantic_select.argtypes = [P, P, I32, I32, I32, SP, I32, P, P, P, I32, I32, I32, I32, P, P, P, SZ, P]
+        L.lsa_semantic_select_timed.argtypes = [P, P, I32, I32, I32, SP, I32, P, P, P, I32, I32, I32, I32, P, P, P,
+                                                 SZ, P, C.POINTER(P)]
         SG = C.POINTER(SemanticPages)
         L.lsa_semantic_cluster_paged.argtypes = [P, I32, I32, I32, SP, SG, I32, I32, I32, P, P, P, P]
         L.lsa_semantic_select_paged.argtypes = [P, P, I32, I32, I32, SP, SG, I32, I32, P, P, P, I32, I32, I32, I32,
@@ -490,11 +492,13 @@ def lsa_semantic_cache(k_idx, n_cluster: int = 512, n_pool: int = 4, n_bavg: int
 
 def lsa_semantic_select(q_idx, q_pos, cache: dict, k: int, p_top: int, n_sink: int, n_w: int,
                         idx=None, count=None, ws_bytes: Optional[int] = None, ws: Optional[torch.Tensor] = None,
-                        paged: Optional[dict] = None):
+                        paged: Optional[dict] = None, stage_events=None):
     """Index lists of flat semantic search: (idx int32 [B, n_q, n_sink + k + n_w], count
     int32 [B, n_q]).  q_idx bf16 [B, n_q, 64]; q_pos int32 [B, n_q].  ``paged``: as for
     lsa_semantic_cache, plus n_slots (rows of the key pools) with a page table; the lists
-    then hold pool rows."""
+    then hold pool rows.  ``stage_events``: three torch.cuda.Events (created and recorded
+    once beforehand) recorded before and after the centroid scan and at the end
+    (lsa_semantic_select_timed; contiguous caches)."""
     _need(q_idx, "q_idx", torch.bfloat16)
     dev = q_idx.device
     _need(q_pos, "q_pos", torch.int32, dev)
@@ -516,7 +520,14 @@ def lsa_semantic_select(q_idx, q_pos, cache: dict, k: int, p_top: int, n_sink: i
                    lib().lsa_semantic_select_workspace_size(B, n_q, NB, C.byref(prm), C.byref(nb)))
             ws_bytes = nb.value
         ws = _workspace(ws_bytes, dev)
-    if paged is None:
+    if paged is None and stage_events is not None:
+        evs = (P * 3)(*[C.c_void_p(e.cuda_event) for e in stage_events])
+        _check("lsa_semantic_select_timed",
+               lib().lsa_semantic_select_timed(_ptr(q_idx), _ptr(q_pos), B, n_q, d, C.byref(prm), NB,
+                                               _ptr(cache["centroids"]), _ptr(cache["table"]),
+                                               _ptr(cache["offsets"]), k, p_top, n_sink, n_w, _ptr(idx),
+                                               _ptr(count), _ptr(ws), ws_bytes, _stream(dev), evs))
+    elif paged is None:
         _check("lsa_semantic_select",
                lib().lsa_semantic_select(_ptr(q_idx), _ptr(q_pos), B, n_q, d, C.byref(prm), NB,
                                          _ptr(cache["centroids"]), _ptr(cache["table"]), _ptr(cache["offsets"]),

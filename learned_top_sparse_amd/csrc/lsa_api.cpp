@@ -889,7 +889,7 @@ static lsa_status sem_select(const void* q_idx, const int32_t* q_pos, int32_t B,
                              const lsa_semantic_params* prm, const lsa_semantic_pages* pages, int32_t L_max,
                              int32_t n_blocks, const void* centroids, const int32_t* table, const int32_t* offsets,
                              int32_t k, int32_t p_top, int32_t n_sink, int32_t n_w, int32_t* idx, int32_t* count,
-                             void* ws, size_t ws_bytes, void* stream) {
+                             void* ws, size_t ws_bytes, void* stream, void* const* events = nullptr) {
   lsa::SemParams sp;
   if (B < 0 || n_q < 0 || n_blocks < 0 || k < 1 || p_top < 1 || n_sink < 0 || n_w < 0) return LSA_ERR_INVALID_ARG;
   lsa_status st = check_sem_params(prm, d_idx, &sp);
@@ -924,6 +924,7 @@ static lsa_status sem_select(const void* q_idx, const int32_t* q_pos, int32_t B,
   a.ws = ws;
   a.ws_bytes = ws_bytes;
   a.pages = pg;
+  a.events = events;
   return hip_status(lsa::launch_sem_select(a, as_stream(stream)));
 }
 
@@ -945,4 +946,15 @@ LSA_API lsa_status lsa_semantic_select_paged(const void* q_idx, const int32_t* q
   if (!pages) return LSA_ERR_INVALID_ARG;
   return sem_select(q_idx, q_pos, B, n_q, d_idx, prm, pages, L_max, n_blocks, centroids, table, offsets, k, p_top,
                     n_sink, n_w, idx, count, ws, ws_bytes, stream);
+}
+
+LSA_API lsa_status lsa_semantic_select_timed(const void* q_idx, const int32_t* q_pos, int32_t B, int32_t n_q,
+                                             int32_t d_idx, const lsa_semantic_params* prm, int32_t n_blocks,
+                                             const void* centroids, const int32_t* table, const int32_t* offsets,
+                                             int32_t k, int32_t p_top, int32_t n_sink, int32_t n_w, int32_t* idx,
+                                             int32_t* count, void* ws, size_t ws_bytes, void* stream,
+                                             void* const* events) {
+  if (!events || !events[0] || !events[1] || !events[2]) return LSA_ERR_INVALID_ARG;
+  return sem_select(q_idx, q_pos, B, n_q, d_idx, prm, nullptr, 0, n_blocks, centroids, table, offsets, k, p_top,
+                    n_sink, n_w, idx, count, ws, ws_bytes, stream, events);
 }

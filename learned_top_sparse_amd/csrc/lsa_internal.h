@@ -213,6 +213,7 @@ struct SemSelectArgs {
   void* ws;
   size_t ws_bytes;
   SemPages pages;
+  void* const* events = nullptr;  // optional: 3 caller-made HIP events (scan start, scan end, end)
 };
 constexpr int SEM_MAX_POOL_KEYS = 128;  // pool keys of a cluster block
 constexpr int SEM_MAX_BUCKETS = 64;     // buckets of a cluster block

@@ -1181,6 +1181,7 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
     const int rows = a.B * nqc;
     float* qn = static_cast<float*>(a.ws);
     float* S = qn + (size_t)rows * SEM_D;
+    if (a.events) hipEventRecord(static_cast<hipEvent_t>(a.events[0]), st);
     if (a.NB == 0) {
       // an empty cache: nothing to score, every list is the sink and the window
     } else if (nqc == 1) {
@@ -1198,6 +1199,7 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(sem_score_kernel<QT>, grid, dim3(256), 0, st, qn, a.q_pos, a.n_q, i0, nqc, pg,
                          static_cast<const unsigned short*>(a.cent), a.NB, m, a.sp.n_cluster, bpw, S, ld);
     }
+    if (a.events) hipEventRecord(static_cast<hipEvent_t>(a.events[1]), st);
     // rows in registers: one 1024-thread workgroup per row; with enough rows to fill
     // the chip twice, a variant held to 64 VGPRs (8 waves per SIMD) runs two
     // workgroups per compute unit
@@ -1251,6 +1253,7 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (a.events) hipEventRecord(static_cast<hipEvent_t>(a.events[2]), st);
   return hipSuccess;
 }
 
