@@ -462,6 +462,8 @@ def lsa_semantic_cache(k_idx, n_cluster: int = 512, n_pool: int = 4, n_bavg: int
     if cache is None:
         m = n_cluster // n_bavg
         if paged is not None and paged.get("block_table") is not None:
+            if n_bslots is None or n_bslots < 1:
+                raise ValueError("a block-tabled cache needs n_bslots (entries of the cache pool)")
             NB = paged["block_table"].shape[1]
             lead = (n_bslots,)
         else:

@@ -405,3 +405,31 @@ def test_semantic_paged(lsa):
         assert np.array_equal(idx[1, i].cpu().numpy(), r["J"])
         want = np.where(r["J"] >= 0, oracle.paged_rows(pt[1].cpu().numpy(), L, P)[np.maximum(r["J"], 0)], -1)
         assert np.array_equal(idx_p[1, i].cpu().numpy(), want)
+
+
+def test_semantic_paged_many_rows(lsa):
+    """A 600-query chunk over paged storage (the two-workgroups-per-CU selection with
+    paging): the contiguous lists mapped to pool rows, bit for bit."""
+    prm = (512, 4, 8, 32)
+    P = 64
+    L = 12 * 512
+    wl = synthetic.Workload("sem_paged_chunk", B=1, n_q=600, L=L, q_pos0=L - 600, H_I=1, d_I=64, k=300, H_q=16,
+                            semantic=True, p_top=64, n_sink=4)
+    g = synthetic.semantic_inputs(wl, dev(), seed=15)
+    NB, max_pages = L // 512, L // P
+    gen = torch.Generator().manual_seed(23)
+    n_pages = max_pages + 9
+    pt = torch.randperm(n_pages, generator=gen)[:max_pages].view(1, max_pages).to(torch.int32).to(dev())
+    bt = torch.randperm(NB + 3, generator=gen)[:NB].view(1, NB).to(torch.int32).to(dev())
+    k_pool = _to_pool(g["k_sem"], pt, P, n_pages, 4)
+    paged = {"block_table": bt, "page_table": pt, "page_size": P, "n_slots": n_pages * P}
+    cache = lsa.lsa_semantic_cache(g["k_sem"], *prm)
+    cache_p = lsa.lsa_semantic_cache(k_pool, *prm, paged=paged, n_bslots=NB + 3)
+    idx, cnt = lsa.lsa_semantic_select(g["q_sem"], g["q_pos"], cache, wl.k, wl.p_top, 4, 512)
+    idx_p, cnt_p = lsa.lsa_semantic_select(g["q_sem"], g["q_pos"], cache_p, wl.k, wl.p_top, 4, 512, paged=paged)
+    torch.cuda.synchronize()
+    mapped = torch.where(idx >= 0, pt.long().gather(1, (idx.clamp(min=0) // P).view(1, -1)).view_as(idx) * P
+                         + idx.clamp(min=0) % P, torch.full_like(idx, -1).long()).to(torch.int32)
+    assert torch.equal(idx_p, mapped) and torch.equal(cnt_p, cnt)
+    with pytest.raises(ValueError):
+        lsa.lsa_semantic_cache(k_pool, *prm, paged=paged)
