@@ -1181,7 +1181,10 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
     const int rows = a.B * nqc;
     float* qn = static_cast<float*>(a.ws);
     float* S = qn + (size_t)rows * SEM_D;
-    if (a.events) hipEventRecord(static_cast<hipEvent_t>(a.events[0]), st);
+    if (a.events) {
+      const hipError_t er = hipEventRecord(static_cast<hipEvent_t>(a.events[0]), st);
+      if (er != hipSuccess) return er;
+    }
     if (a.NB == 0) {
       // an empty cache: nothing to score, every list is the sink and the window
     } else if (nqc == 1) {
@@ -1199,7 +1202,10 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(sem_score_kernel<QT>, grid, dim3(256), 0, st, qn, a.q_pos, a.n_q, i0, nqc, pg,
                          static_cast<const unsigned short*>(a.cent), a.NB, m, a.sp.n_cluster, bpw, S, ld);
     }
-    if (a.events) hipEventRecord(static_cast<hipEvent_t>(a.events[1]), st);
+    if (a.events) {
+      const hipError_t er = hipEventRecord(static_cast<hipEvent_t>(a.events[1]), st);
+      if (er != hipSuccess) return er;
+    }
     // rows in registers: one 1024-thread workgroup per row; with enough rows to fill
     // the chip twice, a variant held to 64 VGPRs (8 waves per SIMD) runs two
     // workgroups per compute unit
@@ -1224,7 +1230,7 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
   } while (0)
     if (many && fits(1024, 4)) LSA_SEM_SEL(1024, 4, 8);
     else if (many && fits(1024, 8)) LSA_SEM_SEL(1024, 8, 8);
-    else if (many && fits(1024, 16)) LSA_SEM_SEL(1024, 16, 8);
+    else if (many && fits(512, 32)) LSA_SEM_SEL(512, 32, 4);
     else if (fits(1024, 4)) LSA_SEM_SEL(1024, 4, 1);
     else if (fits(1024, 8)) LSA_SEM_SEL(1024, 8, 1);
     else if (fits(1024, 16)) LSA_SEM_SEL(1024, 16, 1);
@@ -1253,7 +1259,10 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.events) hipEventRecord(static_cast<hipEvent_t>(a.events[2]), st);
+  if (a.events) {
+    const hipError_t er = hipEventRecord(static_cast<hipEvent_t>(a.events[2]), st);
+    if (er != hipSuccess) return er;
+  }
   return hipSuccess;
 }
 
