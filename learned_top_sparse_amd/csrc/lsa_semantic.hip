@@ -1090,9 +1090,48 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
   __syncthreads();
   const int n_s = n_sink < w0 ? n_sink : w0;
   if constexpr (LONG) {
-    // the long-range keys ascending: bitonic sort in LDS (padding sorts last)
+    // the long-range keys ascending: bitonic sort (padding sorts last); up to 2 * NT keys
+    // two per thread (keys t and t + NT), exchanges within a thread or under 64 apart
+    // without LDS, wider ones through it
     int Q2 = 1;
     while (Q2 < n_lr) Q2 <<= 1;
+    if (Q2 <= 2 * NT && Q2 >= 128) {
+      int v0 = t < n_lr ? LRs[t] : 0x7FFFFFFF;
+      int v1 = t + NT < n_lr ? LRs[t + NT] : 0x7FFFFFFF;
+      const bool two = Q2 > NT;
+      for (int kk = 2; kk <= Q2; kk <<= 1)
+        for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+          if (jj == NT) {
+            // partners are the two keys of this thread: element t (lower) and t + NT
+            const bool asc = (t & kk) == 0;
+            const int lo = v0 < v1 ? v0 : v1, hi = v0 < v1 ? v1 : v0;
+            v0 = asc ? lo : hi;
+            v1 = asc ? hi : lo;
+            continue;
+          }
+          int p0, p1;
+          if (jj >= 64) {
+            __syncthreads();
+            LRs[t] = v0;
+            if (two) LRs[t + NT] = v1;
+            __syncthreads();
+            p0 = LRs[t ^ jj];
+            p1 = two ? LRs[(t + NT) ^ jj] : 0;
+          } else {
+            p0 = __shfl_xor(v0, jj);
+            p1 = __shfl_xor(v1, jj);
+          }
+          const int x0 = t, x1 = t + NT;
+          const bool asc0 = (x0 & kk) == 0, low0 = (x0 & jj) == 0;
+          const bool asc1 = (x1 & kk) == 0, low1 = (x1 & jj) == 0;
+          v0 = (asc0 == low0) ? (v0 < p0 ? v0 : p0) : (v0 > p0 ? v0 : p0);
+          if (two) v1 = (asc1 == low1) ? (v1 < p1 ? v1 : p1) : (v1 > p1 ? v1 : p1);
+        }
+      __syncthreads();
+      if (t < Q2) LRs[t] = v0;
+      if (two && t + NT < Q2) LRs[t + NT] = v1;
+      __syncthreads();
+    } else {
     for (int x = n_lr + t; x < Q2; x += NT) LRs[x] = 0x7FFFFFFF;
     __syncthreads();
     for (int kk = 2; kk <= Q2; kk <<= 1)
@@ -1110,6 +1149,7 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
         }
         __syncthreads();
       }
+    }
     for (int r = t; r < n_lr; r += NT) out[n_s + r] = entry(LRs[r]);
   } else {
     emit_marked<NT>(lbm, nlw, scan_tmp, [&](int r, int pos) { out[n_s + r] = entry(pos); });
