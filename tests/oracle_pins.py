@@ -623,6 +623,48 @@ def check_sem_select_hand(impl):
     return _all(r)
 
 
+def _bf16_bits(x):
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.int64)
+
+
+def check_sem_cluster_hand(impl):
+    """The cache entry of the hand-clustered block: merge rounds, bucket order, each
+    bucket's keys ascending, offsets, and the centroids' bf16 bit patterns."""
+    g = _load_golden()["semantic_cluster"]
+    keys = np.array(g["keys"], np.float32)
+    r = []
+    P = impl.sem_pool_keys(keys, g["n_pool"])
+    _, _, _, log = impl.sem_ward(P, g["m"], g["n_max"] // g["n_pool"])
+    r.append(_ok([[a, b, c] for a, b, c, _ in log] == g["merge_log"], f"merge rounds {log}"))
+    cent, table, off = impl.sem_cluster_block(keys, g["n_pool"], g["m"], g["n_max"])
+    r.append(_ok(np.asarray(table).tolist() == g["table"], f"table {np.asarray(table).tolist()}"))
+    r.append(_ok(np.asarray(off).tolist() == g["offsets"], f"offsets {np.asarray(off).tolist()}"))
+    want = [[int(h, 16) for h in row] for row in g["centroid_bf16_bits"]]
+    cent = np.asarray(cent, np.float32)
+    exact = cent.shape == (4, 4) and (cent.view(np.uint32) & 0xFFFF).max() == 0
+    r.append(_ok(exact and _bf16_bits(cent).tolist() == want, f"centroid bits {cent.tolist()}"))
+    # the same entry through the whole-sequence cache, its first key offset applied
+    c = impl.bucket_cache(np.vstack([keys, keys]), g["n_cluster"], g["n_pool"], g["n_bavg"], g["n_max"])
+    r.append(_ok(np.asarray(c["table"][1]).tolist() == [j + 16 for j in g["table"]], "second block's table"))
+    return _all(r)
+
+
+def check_sem_expand_cut_hand(impl):
+    """Expansion whose cut falls inside a multi-key bucket, over the hand-made cache."""
+    g = _load_golden()["semantic_cluster"]
+    e = g["expansion"]
+    keys = np.vstack([np.array(g["keys"], np.float32), np.eye(4, dtype=np.float32)[[0, 1, 2, 3, 0, 1, 2, 3]]])
+    c = impl.bucket_cache(keys, g["n_cluster"], g["n_pool"], g["n_bavg"], g["n_max"])
+    r = []
+    for cs in e["cases"]:
+        got = impl.semantic_select_row(np.array(e["q"], np.float32), c, e["p"], cs["k"], cs["p_top"],
+                                       cs["n_sink"], cs["n_w"])
+        want = cs["J"] + [-1] * (cs["n_sink"] + cs["k"] + cs["n_w"] - len(cs["J"]))
+        r.append(_ok(got["J"].tolist() == want and got["count"] == cs["count"],
+                     f"k={cs['k']} n_w={cs['n_w']}: {got['J'].tolist()}"))
+    return _all(r)
+
+
 def check_sem_token_reduction(impl, seed=23):
     """One key per bucket (n_pool = 1, m = n_cluster, no merge) and p = k: the long-range
     keys are the exact top-k of the cosine scores over the keys of the earlier cluster
@@ -704,4 +746,5 @@ ALL_CHECKS = [
     check_pooled_hand, check_pooled_dense,
     check_sem_normalize_pool, check_sem_ward_scipy, check_sem_ward_hand, check_sem_ward_invariants,
     check_sem_select_hand, check_sem_token_reduction, check_sem_invariants,
+    check_sem_cluster_hand, check_sem_expand_cut_hand,
 ]

@@ -256,6 +256,33 @@ def _sem_order_raw_bits(s):
     return np.asarray(s, np.float32).view(np.uint32).astype(np.uint64)
 
 
+_orig_sem_cluster_block = O.sem_cluster_block
+
+
+def _cluster_keys_descending(k_blk, n_pool, m, n_max, first_key=0):
+    # each bucket's keys listed from the highest position down
+    cent, table, off = _orig_sem_cluster_block(k_blk, n_pool, m, n_max, first_key)
+    table = table.copy()
+    for b in range(off.shape[0] - 1):
+        table[off[b]:off[b + 1]] = table[off[b]:off[b + 1]][::-1]
+    return cent, table, off
+
+
+def _cluster_centroids_unrounded(k_blk, n_pool, m, n_max, first_key=0):
+    # centroids left in fp32 instead of rounded to bf16
+    _, table, off = _orig_sem_cluster_block(k_blk, n_pool, m, n_max, first_key)
+    P = O.sem_pool_keys(k_blk, n_pool)
+    lab, S, _, _ = O.sem_ward(P, m, n_max // n_pool)
+    return O.sem_normalize(S[np.unique(lab)]), table, off
+
+
+def _cluster_buckets_reversed(k_blk, n_pool, m, n_max, first_key=0):
+    # a block's buckets listed in descending id order
+    cent, table, off = _orig_sem_cluster_block(k_blk, n_pool, m, n_max, first_key)
+    parts = [table[off[b]:off[b + 1]] for b in range(off.shape[0] - 1)][::-1]
+    return cent[::-1].copy(), np.concatenate(parts), np.concatenate([[0], np.cumsum([len(x) for x in parts])])
+
+
 MUTANTS = {
     "relu_after_sum": ("index_scores", _relu_after_sum),
     "no_relu": ("index_scores", _no_relu),
@@ -286,6 +313,9 @@ MUTANTS = {
     "sem_pool_raw_keys": ("sem_pool_keys", _sem_pool_raw),
     "sem_scores_last_dim_dropped": ("sem_scores", _short),
     "sem_order_raw_bits": ("sem_order_key", _sem_order_raw_bits),
+    "sem_cluster_keys_descending": ("sem_cluster_block", _cluster_keys_descending),
+    "sem_cluster_centroids_unrounded": ("sem_cluster_block", _cluster_centroids_unrounded),
+    "sem_cluster_buckets_reversed": ("sem_cluster_block", _cluster_buckets_reversed),
 }
 
 
