@@ -881,7 +881,7 @@ LSA_API lsa_status lsa_semantic_select_workspace_size(int32_t B, int32_t n_q, in
   if (!bytes || B < 0 || n_q < 0 || n_blocks < 0) return LSA_ERR_INVALID_ARG;
   lsa_status st = check_sem_params(prm, 64, &sp);
   if (st != LSA_OK) return st;
-  *bytes = (size_t)B * n_q * lsa::sem_select_row_bytes(n_blocks, sp.n_cluster / sp.n_bavg);
+  *bytes = (size_t)B * n_q * lsa::sem_select_row_bytes(n_blocks, sp.n_cluster / sp.n_bavg, sp.n_cluster, sp.n_bmax);
   return LSA_OK;
 }
 
@@ -903,7 +903,7 @@ static lsa_status sem_select(const void* q_idx, const int32_t* q_pos, int32_t B,
   if (!q_idx || !q_pos || !idx || !count || (n_blocks > 0 && (!centroids || !table || !offsets)))
     return LSA_ERR_INVALID_ARG;
   if (((uintptr_t)ws) % 16 != 0) return LSA_ERR_WORKSPACE;
-  const size_t row = lsa::sem_select_row_bytes(n_blocks, sp.n_cluster / sp.n_bavg);
+  const size_t row = lsa::sem_select_row_bytes(n_blocks, sp.n_cluster / sp.n_bavg, sp.n_cluster, sp.n_bmax);
   if (!ws || ws_bytes < (size_t)B * row) return LSA_ERR_WORKSPACE;
   lsa::SemSelectArgs a;
   a.q_idx = q_idx;

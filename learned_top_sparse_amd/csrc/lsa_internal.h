@@ -222,7 +222,7 @@ constexpr int SEM_MAX_K = 4096;
 hipError_t launch_sem_cluster(const void* k_idx, int B, int L_max, const SemParams& sp, int NB, int first_block,
                               int n_update, void* cent, int32_t* table, int32_t* offs, const SemPages& pages,
                               hipStream_t st);
-size_t sem_select_row_bytes(int NB, int m);
+size_t sem_select_row_bytes(int NB, int m, int n_cluster, int n_bmax);
 hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st);
 
 }  // namespace lsa

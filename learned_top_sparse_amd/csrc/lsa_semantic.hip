@@ -511,8 +511,8 @@ __global__ __launch_bounds__(256) void sem_score_kernel(const float* __restrict_
 
 constexpr int SEM_PMAX = 2048;
 constexpr int SEM_KMAX = 4096;
-constexpr int SEM_LPT = 4096;
-constexpr int SEM_KC = 8192;   // candidates of a long row's chunks (chunks * p_top at most)  // page-table entries of one sequence staged in LDS (256K keys of 64-key pages)
+constexpr int SEM_LPT = 4096;  // page-table entries of one sequence staged in LDS (256K keys of 64-key pages)
+constexpr int SEM_KC = 8192;   // candidates of a long row's chunks (chunks * p_top at most)
 
 __global__ __launch_bounds__(SEL_NT) void sem_select_stream_kernel(const float* __restrict__ S, long long ld,
                                                             const int* __restrict__ q_pos, int n_q, int i0, int nqc,
@@ -840,6 +840,7 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
       }
     constexpr int CH = NT * C;
     if (t == 0) sh[3] = 0;
+    __syncthreads();  // a row with no scored bucket reads sh[3] with no other barrier
     const int lane = t & 63;
     if (split) {
       // the spans' candidates, left in the score row by sem_span_topk_kernel (every
@@ -1195,21 +1196,36 @@ hipError_t launch_sem_cluster(const void* k_idx, int B, int L_max, const SemPara
   return hipGetLastError();
 }
 
-// Score-row stride: a row's buckets, and for rows that may exceed 32768 buckets (the
-// span path) room for the last span's candidates, which take 2 * (kept + 1) floats
-// where a short last span may hold fewer scores than that.
-long long sem_ld(int NB, int m) {
+// Whether a selection kernel with rows of nt * C buckets in registers (C per thread)
+// takes rows of n_max buckets whose long-range keys lie below pos_max: the bucket
+// count, the position bitmap (32 * SelLbm<C>::WORDS positions) and the bucket size.
+static bool sem_fits_registers(long long n_max, long long pos_max, int n_bmax, int nt, int C) {
+  return n_max <= (long long)nt * C && pos_max <= 32LL * 256 * C && n_bmax <= 64;
+}
+
+// Rows that no register instance takes go through the long-row path, whose span kernel
+// writes each span's candidates over the start of its own span of the score row.
+static bool sem_long_rows(int NB, int m, int n_cluster, int n_bmax) {
+  return !sem_fits_registers((long long)NB * m, (long long)NB * n_cluster, n_bmax, 1024, 32);
+}
+
+// Score-row stride: a row's buckets, and for rows of the long-row path room for the last
+// span's candidates, which take 2 * (kept + 1) floats where a short last span may hold
+// fewer scores than that.
+long long sem_ld(int NB, int m, int n_cluster, int n_bmax) {
   long long n = (long long)NB * m;
-  if (n > 32768) n += 2 * (SEM_MAX_P + 1);
+  if (sem_long_rows(NB, m, n_cluster, n_bmax)) n += 2 * (SEM_MAX_P + 1);
   return (n + 3) / 4 * 4;
 }
 
-size_t sem_select_row_bytes(int NB, int m) { return (size_t)SEM_D * 4 + (size_t)sem_ld(NB, m) * 4; }
+size_t sem_select_row_bytes(int NB, int m, int n_cluster, int n_bmax) {
+  return (size_t)SEM_D * 4 + (size_t)sem_ld(NB, m, n_cluster, n_bmax) * 4;
+}
 
 hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
   const int m = a.sp.n_cluster / a.sp.n_bavg;
-  const long long ld = sem_ld(a.NB, m);
-  const size_t row_bytes = sem_select_row_bytes(a.NB, m);
+  const long long ld = sem_ld(a.NB, m, a.sp.n_cluster, a.sp.n_bmax);
+  const size_t row_bytes = sem_select_row_bytes(a.NB, m, a.sp.n_cluster, a.sp.n_bmax);
   const long long rows_fit = (long long)(a.ws_bytes / row_bytes);
   long long nqc_max = rows_fit / a.B;
   if (nqc_max > a.n_q) nqc_max = a.n_q;
@@ -1251,9 +1267,7 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
     // workgroups per compute unit
     const bool many = (long long)a.B * nqc >= 512;
     const long long n_max = (long long)a.NB * m, pos_max = (long long)a.NB * a.sp.n_cluster;
-    auto fits = [&](int nt, int C) {
-      return n_max <= (long long)nt * C && pos_max <= 32LL * 256 * C && a.sp.n_bmax <= 64;
-    };
+    auto fits = [&](int nt, int C) { return sem_fits_registers(n_max, pos_max, a.sp.n_bmax, nt, C); };
     const bool paged = pg.bt || pg.pt;
     int split = 0;
 #define LSA_SEM_SEL1(NT, C, MINW, PG)  LSA_SEM_SEL2(NT, C, MINW, PG, false)
@@ -1280,6 +1294,9 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
       // few rows the spans run as workgroups of their own (sem_span_topk_kernel), with
       // many each row's workgroup walks them
       if (a.B * nqc < 256) {
+        // the last span's candidates end at most 2 * (p_top + 1) floats past its scores
+        if (!sem_long_rows(a.NB, m, a.sp.n_cluster, a.sp.n_bmax) || ld < n_max + 2LL * (a.p_top + 1))
+          return hipErrorInvalidValue;
         split = 1;
         const int n_spans = (int)((n_max + SPAN_B - 1) / SPAN_B);
         hipLaunchKernelGGL(sem_span_topk_kernel, dim3(n_spans, nqc, a.B), dim3(1024), 0, st, S, ld, a.q_pos,

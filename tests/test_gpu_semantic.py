@@ -256,15 +256,35 @@ def test_select_long_rows_many(lsa):
     wl = synthetic.Workload("sem_long_many", B=1, n_q=256, L=L, q_pos0=L - 256, H_I=1, d_I=64, k=2048, H_q=16,
                             semantic=True)
     inp = synthetic.semantic_inputs(wl, dev(), seed=14)
+    # rows with no scored bucket (inside the first cluster block, or padding) among them
+    q_pos = inp["q_pos"].clone()
+    q_pos[0, 2], q_pos[0, 3], q_pos[0, 4], q_pos[0, 5] = 100, -1, 0, 511
     cache = lsa.lsa_semantic_cache(inp["k_sem"], *prm)
-    idx, cnt = lsa.lsa_semantic_select(inp["q_sem"], inp["q_pos"], cache, 2048, 512, 4, 512)
+    idx, cnt = lsa.lsa_semantic_select(inp["q_sem"], q_pos, cache, 2048, 512, 4, 512)
     torch.cuda.synchronize()
     oc = _oracle_cache(inp["k_sem"][0], prm, n_blocks=cache["table"].shape[1])
-    for i in (0, 1, 100, 254, 255):
-        p = int(inp["q_pos"][0, i])
+    for i in (0, 1, 2, 3, 4, 5, 100, 254, 255):
+        p = int(q_pos[0, i])
         r = oracle.semantic_select_row(_f32(inp["q_sem"][0, i]), oc, p, 2048, 512, 4, 512)
         assert np.array_equal(idx[0, i].cpu().numpy(), r["J"]), f"i={i}"
         assert int(cnt[0, i]) == r["count"]
+
+
+@pytest.mark.slow
+def test_select_long_rows_past_bitmap(lsa):
+    """Rows of few buckets (32 a block, 16416 in all) whose key positions lie past the
+    largest position bitmap (513 blocks of 512 keys): the long-row path with spans as
+    workgroups of their own, the top-p of 2048 larger than the last span's scores."""
+    prm = (512, 4, 16, 64)
+    L = 513 * 512 + 9
+    wl = synthetic.WORKLOADS["decode_128k_lsa"].replace(B=1, L=L, q_pos0=L - 1)
+    positions = [[L - 1]]
+    print(f"[long rows past the bitmap {prm} L={L}]", flush=True)
+    inp, q, q_pos, cache, idx, cnt = _select_case(lsa, wl, prm, positions, 2048, 2048, 4, 512, seed=15)
+    oc = _oracle_cache(inp["k_sem"][0], prm, n_blocks=cache["table"].shape[1])
+    r = oracle.semantic_select_row(_f32(q[0, 0]), oc, L - 1, 2048, 2048, 4, 512)
+    assert np.array_equal(idx[0, 0].cpu().numpy(), r["J"])
+    assert int(cnt[0, 0]) == r["count"]
 
 
 @pytest.mark.slow

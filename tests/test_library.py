@@ -81,6 +81,31 @@ def test_semantic_validation_without_gpu():
                None, None, None, 0, None) == 0                                        # nothing to do
 
 
+def test_semantic_workspace_covers_span_candidates():
+    """Rows that take the long-row path (more buckets than the registers hold, key
+    positions beyond the largest bitmap, or buckets above 64 keys) get room for the last
+    span's candidates, 2 * (2048 + 1) floats past the row's scores; other rows do not."""
+    import learned_top_sparse_amd as lsa
+    L = lsa.lib()
+    P = lsa.SemanticParams
+
+    def row_bytes(prm, n_blocks):
+        nb = ctypes.c_size_t(0)
+        assert L.lsa_semantic_select_workspace_size(1, 1, n_blocks, ctypes.byref(prm), ctypes.byref(nb)) == 0
+        return nb.value
+
+    slack = 2 * (2048 + 1)
+    up4 = lambda n: (n + 3) // 4 * 4
+    # 32 buckets a block: 512 blocks put positions at the bitmap's end, 513 past it
+    assert row_bytes(P(512, 4, 16, 64), 512) == 4 * 64 + 4 * 512 * 32
+    assert row_bytes(P(512, 4, 16, 64), 513) == 4 * 64 + 4 * up4(513 * 32 + slack)
+    # 64 buckets a block: 512 blocks fill the registers, 513 exceed them
+    assert row_bytes(P(512, 4, 8, 32), 512) == 4 * 64 + 4 * 512 * 64
+    assert row_bytes(P(512, 4, 8, 32), 513) == 4 * 64 + 4 * up4(513 * 64 + slack)
+    # buckets of up to 128 keys
+    assert row_bytes(P(512, 4, 8, 128), 4) == 4 * 64 + 4 * up4(4 * 64 + slack)
+
+
 def _fake_inputs(B, n_q, L, H_I=64, d_I=128, H_q=16, d=128):
     """CPU tensors with the path's shapes: only their pointers reach the host-side planning."""
     import torch
