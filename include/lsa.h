@@ -289,6 +289,26 @@ enum { LSA_SELECT_AUTO = 0, LSA_SELECT_TABLE = 1, LSA_SELECT_FORCE_SHORT = 2, LS
    lsa_forward then uses whatever chunk fits the ws it gets. */
 lsa_status lsa_forward_workspace_size(const lsa_forward_args* a, size_t* bytes);
 lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_bytes, void* stream);
+/* Allocation-free lsa_forward, for callers that cannot allocate device memory: code
+   under HIP graph capture, serving loops and harnesses that forbid hipMalloc.  Same
+   arguments, results and stages as lsa_forward with ws_bytes = LSA_NOALLOC_SCRATCH_BYTES;
+   the workspace is a device array of that size inside the library, one per GPU, held
+   until the process ends.  The call allocates and frees nothing (device or host-pinned)
+   and calls no allocating routine.
+     Sizes: chunks are planned to fit the array (as lsa_forward_plan with that ws_bytes);
+       a call whose requested chunk_rows, or whose single row, needs more returns
+       LSA_ERR_WORKSPACE and launches nothing.  decode_128k (64 sequences of 131073 keys,
+       k_top 2048) needs 70.1 MiB and runs as one chunk.
+     Device: the current device; `stream` must belong to it.  The array's device address
+       is looked up on the first call on each device (one hipGetSymbolAddress), so make
+       that first call outside graph capture; later calls only launch kernels.
+     Sharing: every call on one GPU uses the same array, so calls that overlap on one GPU
+       (other streams, other host threads) race; order them on one stream.  The array
+       keeps the last call's contents; no kernel needs it cleared beforehand (each call
+       clears what it counts in).
+   Errors as lsa_forward; LSA_ERR_HIP also if the array's address cannot be found. */
+#define LSA_NOALLOC_SCRATCH_BYTES (128ull << 20)
+lsa_status lsa_forward_noalloc(const lsa_forward_args* a, void* stream);
 /* The launch plan lsa_forward uses with a workspace of ws_bytes: query rows per
    score chunk (sequences per chunk when n_q == 1) and the attention split count.
    Calling lsa_index_scores / lsa_topk / lsa_sparse_attn chunk by chunk with

@@ -14,6 +14,8 @@ from .binding import (  # noqa: F401
     lsa_block_prefilter,
     lsa_block_reps,
     lsa_forward,
+    lsa_forward_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     lsa_forward_plan,
     lsa_forward_stages,
     lsa_forward_workspace_size,

@@ -23,7 +23,11 @@ EXPORTED = [
     "lsa_forward_workspace_size", "lsa_forward", "lsa_forward_plan", "lsa_forward_stages",
     "lsa_semantic_cluster", "lsa_semantic_select_workspace_size", "lsa_semantic_select",
     "lsa_semantic_cluster_paged", "lsa_semantic_select_paged", "lsa_sparse_attn_pool", "lsa_semantic_select_timed",
+    "lsa_forward_noalloc",
 ]
+
+# size of the device array lsa_forward_noalloc works in (LSA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 STAGE_NAMES = {1: "block_reps", 2: "block_prefilter", 3: "index_select", 4: "index_scores", 5: "topk", 7: "sample",
                6: "sparse_attn", 8: "expand"}
@@ -85,6 +89,7 @@ def lib():
         L.lsa_sparse_attn_pool.argtypes = [P, P, P, P, I32, I32, I64, I32, I32, I32, C.c_float, I32, P, P, P, SZ, P]
         L.lsa_forward_workspace_size.argtypes = [C.POINTER(ForwardArgs), C.POINTER(SZ)]
         L.lsa_forward.argtypes = [C.POINTER(ForwardArgs), P, SZ, P]
+        L.lsa_forward_noalloc.argtypes = [C.POINTER(ForwardArgs), P]
         L.lsa_forward_plan.argtypes = [C.POINTER(ForwardArgs), SZ, C.POINTER(I64), C.POINTER(I32)]
         L.lsa_forward_stages.argtypes = [C.POINTER(ForwardArgs), SZ, C.POINTER(I32), I32, C.POINTER(I32)]
         SP = C.POINTER(SemanticParams)
@@ -364,7 +369,7 @@ def lsa_forward_stages(inp: dict, k_top: int, ws_bytes: int, two_stage=False, bl
 def lsa_forward(inp: dict, k_top: int, two_stage=False, block_size: int = 128, n_keep: int = 64,
                 scale: Optional[float] = None, attn_split: int = 0, chunk_rows: int = 0,
                 out: Optional[dict] = None, ws: Optional[torch.Tensor] = None, stage_events=None,
-                select: str = "auto") -> dict:
+                select: str = "auto", noalloc: bool = False) -> dict:
     """The whole path.  ``inp`` holds q_idx, k_idx, w, q_pos, q, k, v (device tensors).
     ``two_stage``: False (flat), True (block prefilter, then tokens) or "pooled" (the keys
     of the kept blocks; k_top = n_keep * block_size); ``inp["block_keys"]`` (optional,
@@ -373,7 +378,8 @@ def lsa_forward(inp: dict, k_top: int, two_stage=False, block_size: int = 128, n
     k_idx, k and v are then pools [n_slots, .] and idx receives pool rows.
     Returns dict(idx, count, out, lse[, kept]); pass ``out`` / ``ws`` to reuse buffers.
     ``stage_events``: optional torch.cuda.Event list (1 + len(lsa_forward_stages(...)));
-    each must have been recorded once (so its HIP event exists)."""
+    each must have been recorded once (so its HIP event exists).  ``noalloc``: run as
+    lsa_forward_noalloc (the library's device array as the workspace; ``ws`` must be None)."""
     q_idx, q = inp["q_idx"], inp["q"]
     dev = q_idx.device
     for name, dt in (("q_idx", torch.int8), ("k_idx", torch.int8), ("w", torch.int32), ("q_pos", torch.int32),
@@ -395,11 +401,15 @@ def lsa_forward(inp: dict, k_top: int, two_stage=False, block_size: int = 128, n
         if two_stage:
             out["kept"] = torch.empty((B, n_q, n_keep), dtype=torch.int32, device=dev)
     a = _forward_args(inp, k_top, two_stage, block_size, n_keep, scale, attn_split, chunk_rows, out, select)
-    if ws is None:
+    if noalloc:
+        if ws is not None:
+            raise LsaError("lsa_forward_noalloc: takes no workspace")
+    elif ws is None:
         nb = SZ(0)
         _check("lsa_forward_workspace_size", lib().lsa_forward_workspace_size(C.byref(a), C.byref(nb)))
         ws = _workspace(nb.value, dev)
     nbytes = 0 if ws is None else ws.numel()
+    handles = None
     if stage_events is not None:
         handles = (P * len(stage_events))()
         for i, e in enumerate(stage_events):
@@ -408,9 +418,20 @@ def lsa_forward(inp: dict, k_top: int, two_stage=False, block_size: int = 128, n
             handles[i] = e.cuda_event
         a.stage_events = C.cast(handles, P)
         a.n_stage_events = len(stage_events)
-    st = lib().lsa_forward(C.byref(a), _ptr(ws), nbytes, _stream(dev))
-    _check("lsa_forward", st)
+    if noalloc:
+        _check("lsa_forward_noalloc", lib().lsa_forward_noalloc(C.byref(a), _stream(dev)))
+    else:
+        _check("lsa_forward", lib().lsa_forward(C.byref(a), _ptr(ws), nbytes, _stream(dev)))
     return out
+
+
+def lsa_forward_noalloc(inp: dict, k_top: int, two_stage=False, block_size: int = 128, n_keep: int = 64,
+                        scale: Optional[float] = None, attn_split: int = 0, chunk_rows: int = 0,
+                        out: Optional[dict] = None, stage_events=None, select: str = "auto") -> dict:
+    """lsa_forward working in the library's own device array (no workspace argument; the
+    call allocates nothing -- pass ``out`` to keep torch from allocating the outputs)."""
+    return lsa_forward(inp, k_top, two_stage, block_size, n_keep, scale, attn_split, chunk_rows, out=out,
+                       stage_events=stage_events, select=select, noalloc=True)
 
 
 # --------------------------------------------------------------------------- flat semantic search
