@@ -43,7 +43,7 @@ namespace lsa {
 // PAGED: k_idx is a pool of pages of 2^page_log2 >= 64 keys; the pool pages of the
 // workgroup's keys (at most FLAT_PAGES of them: the launcher sizes the spans) are read
 // into LDS first, and each key's row is looked up there.
-// Grid: x = n_qtiles * n_spans (longest query tiles first), y = B.
+// Grid: x = 8 * ceil(n_qtiles / 8) * n_spans (XCD-aware order, below), y = B.
 constexpr int FLAT_PAGES = 4096;
 template <int D, int MT, int NW, bool SEL, bool PAGED>
 __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
@@ -61,11 +61,16 @@ __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.y;
-  const int qt_rev = blockIdx.x / n_spans;
-  // consecutive workgroups go to the XCDs in turn: rotating the span by the query
-  // tile spreads every span (the first one is the busiest under a causal mask) over
-  // all XCDs instead of pinning span s to XCD s % 8
-  const int s = (blockIdx.x + qt_rev) % n_spans;
+  // Workgroups are dealt to the 8 XCDs in turn (grid.x is a multiple of 8, so
+  // workgroup x runs on XCD x % 8).  XCD x takes the query tiles x, x + 8, ...
+  // (longest first, interleaved so causal work balances over the XCDs) and walks them
+  // span by span: the workgroups resident on one XCD at a time read the same span of
+  // keys, which its L2 then serves to all of them.
+  const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+  const int per_xcd = (n_qtiles + 7) >> 3;
+  const int s = kx / per_xcd;
+  const int qt_rev = (kx - s * per_xcd) * 8 + xcd;
+  if (qt_rev >= n_qtiles) return;
   const int qt = n_qtiles - 1 - qt_rev;
   const int i0 = qt * NW;
   const int32_t* qp = q_pos + (long long)b * n_q;
@@ -234,8 +239,10 @@ __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
 // slots).  The scan is bound by HBM, so each wave keeps a ring of RING groups of
 // fragments: RING-1 groups of loads are in flight while one group is multiplied
 // (2 waves/SIMD).
+// GB (KEPT with bs a multiple of 64): a 64-slot group lies in one kept block, so one
+// wave-uniform lookup of that block gives the keys of the whole group.
 // Grid: x = n_spans (1 for KEPT), y = B * n_q.
-template <int D, int MT, bool KEPT>
+template <int D, int MT, bool KEPT, bool GB>
 __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
     int w_per_query, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ kept, int bs,
@@ -248,7 +255,8 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
   constexpr int SBUF = KEPT ? 8192 : DIRECT_SPAN;
   __shared__ int kept_s[KEPT ? 256 : 1];
   __shared__ __attribute__((aligned(16))) int sbuf[SBUF];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long row = blockIdx.y;
   const int b = (int)blockIdx.y / n_q;
   // Flat rows: the span's keys are loaded (clamped to the cache) and scored whatever
@@ -303,14 +311,28 @@ __global__ __launch_bounds__(256, 2) void idx_direct_kernel(
   v4i ring[RING][4][KS];
   auto load_group = [&](int c0, int c1, int i, v4i (&Bf)[4][KS]) {
     const int sg = c0 + 64 * (wave + 4 * i);
+    if constexpr (GB) {
+      // groups past the chunk re-read its last group (chunks are multiples of 64 slots)
+      const int sgc = min(sg, c1 - 64);
+      const int bi = sgc / bs;
+      const int blk = kept_s[bi];
+      const int k0 = (blk >= 0 ? blk * bs + (sgc - bi * bs) : 0) + r16;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      // a slot past the chunk (or without a kept block) reads a fallback row: its
-      // score is never kept, and unconditional loads stay in flight together
-      const int s = min(sg + 16 * nt + r16, c1 - 1);
-      const int8_t* kr = kb + (long long)key_load(s) * D;
+      for (int nt = 0; nt < 4; ++nt) {
+        const int8_t* kr = kb + (long long)min(k0 + 16 * nt, L_max - 1) * D;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
+        for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        // a slot past the chunk (or without a kept block) reads a fallback row: its
+        // score is never kept, and unconditional loads stay in flight together
+        const int s = min(sg + 16 * nt + r16, c1 - 1);
+        const int8_t* kr = kb + (long long)key_load(s) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
+      }
     }
   };
   auto prologue = [&](int c0, int c1) {
@@ -718,6 +740,7 @@ __global__ void blk_cache_kernel(const int8_t* __restrict__ k_idx, int L_max, in
 // 2*D bytes; q.r = 128*(q.hi) + (q.lo) is exact in int32 (|q.r| < 2^29), then
 // ReLU and the weighted head sum accumulate in int64.  Block m is scored for a
 // query iff m < floor(q_pos / bs) (its own block is never scored).
+// Grid: x = 8 * ceil(n_qtiles / 8) * n_spans (the flat kernel's XCD-aware order), y = B.
 template <int D, int MT, int QW>
 __global__ __launch_bounds__(256, 2) void blk_scores_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ limbs, const int32_t* __restrict__ w,
@@ -730,11 +753,16 @@ __global__ __launch_bounds__(256, 2) void blk_scores_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
   const int b = blockIdx.y;
-  const int qt_rev = blockIdx.x / n_spans;
-  // consecutive workgroups go to the XCDs in turn: rotating the span by the query
-  // tile spreads every span (the first one is the busiest under a causal mask) over
-  // all XCDs instead of pinning span s to XCD s % 8
-  const int s = (blockIdx.x + qt_rev) % n_spans;
+  // Workgroups are dealt to the 8 XCDs in turn (grid.x is a multiple of 8, so
+  // workgroup x runs on XCD x % 8).  XCD x takes the query tiles x, x + 8, ...
+  // (longest first, interleaved so causal work balances over the XCDs) and walks them
+  // span by span: the workgroups resident on one XCD at a time read the same span of
+  // keys, which its L2 then serves to all of them.
+  const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+  const int per_xcd = (n_qtiles + 7) >> 3;
+  const int s = kx / per_xcd;
+  const int qt_rev = (kx - s * per_xcd) * 8 + xcd;
+  if (qt_rev >= n_qtiles) return;
   const int qt = n_qtiles - 1 - qt_rev;
   const int i0 = qt * QT;
   const int32_t* qp = q_pos + (long long)b * n_q;
@@ -986,7 +1014,7 @@ static hipError_t launch_flat_t(const IdxArgs& a, hipStream_t st) {
     span = (int)std::min<long long>(span, fit);
   }
   const int n_spans = (n_slots + span - 1) / span;
-  dim3 grid((unsigned)(n_qtiles * n_spans), (unsigned)a.B);
+  dim3 grid((unsigned)(8 * ((n_qtiles + 7) / 8) * n_spans), (unsigned)a.B);
   const bool sel = a.thr.theta != nullptr;
   if (sel && (a.thr.rstate == nullptr || a.thr.cnt == nullptr || a.thr.lslot == nullptr || a.thr.lscore == nullptr ||
               a.thr.cap < 1))
@@ -1037,9 +1065,14 @@ static hipError_t launch_direct_t(const IdxArgs& a, hipStream_t st) {
   if (!KEPT && a.span != DIRECT_SPAN) return hipErrorInvalidValue;
   const int n_spans = KEPT ? 1 : (a.L_max + a.span - 1) / a.span;
   dim3 grid((unsigned)n_spans, (unsigned)(a.B * a.n_q));
-  hipLaunchKernelGGL((idx_direct_kernel<D, MT, KEPT>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.w,
-                     a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I, a.span,
-                     a.scores, (long long)a.ld);
+  if (KEPT && a.block_size % 64 == 0)
+    hipLaunchKernelGGL((idx_direct_kernel<D, MT, KEPT, KEPT>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.w,
+                       a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I, a.span,
+                       a.scores, (long long)a.ld);
+  else
+    hipLaunchKernelGGL((idx_direct_kernel<D, MT, KEPT, false>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.w,
+                       a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I, a.span,
+                       a.scores, (long long)a.ld);
   return hipGetLastError();
 }
 
@@ -1125,7 +1158,8 @@ static hipError_t launch_blk_scores_t(const BlkArgs& a, hipStream_t st) {
   const int span = a.span;
   const int n_spans = (a.n_blocks + span - 1) / span;
   if (n_spans == 0) return hipSuccess;
-  dim3 grid((unsigned)(n_qtiles * n_spans), (unsigned)a.B);
+  // the kernel's XCD-aware order: 8 XCDs x ceil(n_qtiles / 8) query tiles x n_spans
+  dim3 grid((unsigned)(8 * ((n_qtiles + 7) / 8) * n_spans), (unsigned)a.B);
   hipLaunchKernelGGL((blk_scores_kernel<D, MT, 2>), grid, dim3(256), 0, st, a.q_idx, a.limbs, a.w,
                      a.w_per_query, a.q_pos, a.n_q, a.n_blocks, a.L_max, a.H_I, a.block_size, span,
                      n_spans, n_qtiles, a.bscores, (long long)a.ld);

@@ -88,10 +88,24 @@ struct RowView {
   bool vec;           // 16-byte aligned row: vector loads
   const int32_t* pt = nullptr;  // paged caches: the row's page table (page ids clamped to n_pages)
   int plog2 = 0, n_pages = 0;
+  // KEPT: the kept-table index of slot s is s / bs, taken without a division: a shift
+  // when bs is a power of two, else the high half of s * (floor(2^32 / bs) + 1), which
+  // is exact for 0 <= s < 2^16 (slots are fewer than 256 * 128)
+  int bs_log2 = -1;
+  unsigned bs_magic = 0;
 
+  __device__ __forceinline__ void set_block_size(int b) {
+    bs = b;
+    bs_log2 = (b & (b - 1)) == 0 ? __builtin_ctz((unsigned)b) : -1;
+    bs_magic = bs_log2 >= 0 ? 0u : (unsigned)(0xFFFFFFFFu / (unsigned)b) + 1u;
+  }
+  __device__ __forceinline__ int blk_of(int s) const {
+    return bs_log2 >= 0 ? (s >> bs_log2) : (int)__umulhi((unsigned)s, bs_magic);
+  }
   __device__ __forceinline__ int key_of(int s) const {
     if constexpr (KEPT) {
-      return kept_s[s / bs] * bs + s % bs;
+      const int bi = blk_of(s);
+      return kept_s[bi] * bs + (s - bi * bs);
     } else {
       if (pt == nullptr) return s;
       return (min(max(pt[s >> plog2], 0), n_pages - 1) << plog2) | (s & ((1 << plog2) - 1));
@@ -100,8 +114,9 @@ struct RowView {
   __device__ __forceinline__ bool valid(int s) const {
     if (s >= n_slots) return false;
     if constexpr (KEPT) {
-      const int blk = kept_s[s / bs];
-      return blk >= 0 && blk * bs + s % bs <= p;
+      const int bi = blk_of(s);
+      const int blk = kept_s[bi];
+      return blk >= 0 && blk * bs + (s - bi * bs) <= p;
     } else {
       return true;
     }
@@ -484,7 +499,7 @@ __device__ __forceinline__ RowView<KEPT> make_row(const int32_t* scores, long lo
   rv.p = min(q_pos[row], L_max - 1);
   rv.srow = scores + row * ld;
   rv.vec = (((uintptr_t)rv.srow) & 15u) == 0;
-  rv.bs = bs;
+  rv.set_block_size(bs);
   if constexpr (KEPT) {
     for (int t = threadIdx.x; t < n_keep; t += NT) kept_s[t] = kept[row * n_keep + t];
     __syncthreads();
@@ -588,7 +603,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(const int32_t* __restrict__ sc
 // ring, scores into LDS -- and then takes its exact top-k from those LDS scores with the
 // score-table kernel's row selection (select_row), so no score table is written or
 // read back.  Rows of at most KSEL_SLOTS slots (n_keep * bs).
-template <int D, int MT>
+// GB (bs a multiple of 64): a 64-slot group lies in one kept block, so one wave-uniform
+// lookup of that block gives the keys of the whole group (no per-slot division).
+template <int D, int MT, bool GB>
 __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
     int w_per_query, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ kept, int bs, int n_keep,
@@ -601,7 +618,8 @@ __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
   __shared__ int scan_tmp[NW + 1];
   __shared__ int h256[256];
   __shared__ int sh[8];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long row = blockIdx.x;
   const int b = (int)(row / n_q);
   int32_t* out = idx + row * (long long)k;
@@ -636,23 +654,41 @@ __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
   v4i ring[RING][4][KS];
   auto load_group = [&](int i, v4i (&Bf)[4][KS]) {
     const int sg = 64 * (wave + NW * i);
+    if constexpr (GB) {
+      // groups past the last slot re-read the last group (n_slots is a multiple of 64)
+      const int sgc = min(sg, n_slots - 64);
+      const int bi = sgc / bs;
+      const int blk = kept_s[bi];
+      const int base = blk >= 0 ? blk * bs + (sgc - bi * bs) : 0;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int8_t* kr = kb + (long long)key_load(min(sg + 16 * nt + r16, n_slots - 1)) * D;
+      for (int nt = 0; nt < 4; ++nt) {
+        const int8_t* kr = kb + (long long)min(base + 16 * nt + r16, L_max - 1) * D;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
+        for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int8_t* kr = kb + (long long)key_load(min(sg + 16 * nt + r16, n_slots - 1)) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
+      }
     }
   };
   const int n_groups = (n_slots + 63) / 64;
   const int n_iter = ((n_groups + NW - 1) / NW + RING - 1) / RING * RING;  // groups per wave, padded
+  // the prologue issues the slots in ring order (the loop's waits assume slot 0 is the
+  // oldest; a reordered prologue makes the compiler drain every load at the loop head)
 #pragma unroll
-  for (int r = 0; r < RING - 1; ++r) load_group(r, ring[r]);
+  for (int r = 0; r < RING; ++r) {
+    load_group(r, ring[r]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   int wt[MT][4];
   query_weights<MT>(wv, H_I, true, wt);
   for (int i0 = 0; i0 < n_iter; i0 += RING) {
 #pragma unroll
     for (int r = 0; r < RING; ++r) {
-      load_group(i0 + r + RING - 1, ring[(r + RING - 1) % RING]);
       const int sg = 64 * (wave + NW * (i0 + r));
       int part[4];
 #pragma unroll
@@ -671,6 +707,12 @@ __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
           for (int mt = 0; mt < MT; ++mt) ps = relu_mad24(acc[mt][e], wt[mt][e], ps);
         part[nt] = ps;
       }
+      // the slot just used takes the group RING ahead; the barrier keeps these loads
+      // here (left free, the scheduler sinks them towards their MFMAs, and every group
+      // then waits for its own loads)
+      __builtin_amdgcn_sched_barrier(0);
+      load_group(i0 + r + RING, ring[r]);
+      __builtin_amdgcn_sched_barrier(0);
       const int res = reduce_scatter4(part);
       const int sl = sg + 16 * g + r16;
       if (sl < n_slots) sbuf[sl] = res;
@@ -682,7 +724,7 @@ __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
   rv.kept_s = kept_s;
   rv.n_slots = n_slots;
   rv.p = p;
-  rv.bs = bs;
+  rv.set_block_size(bs);
   rv.vec = true;
   if (count != nullptr && tid == 0) count[row] = min(k, n_valid);
   select_row<NT, true>(rv, n_valid, k, out, lds_big, wcnt, scan_tmp, h256, sh);
@@ -691,8 +733,14 @@ __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
 template <int D, int MT>
 static hipError_t launch_kept_select_t(const IdxArgs& a, int k, int32_t* idx, int32_t* count, hipStream_t st) {
   const long long rows = (long long)a.B * a.n_q;
-  hipLaunchKernelGGL((idx_kept_select_kernel<D, MT>), dim3((unsigned)rows), dim3(256), 0, st, a.q_idx, a.k_idx, a.w,
-                     a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I, k, idx, count);
+  if (a.block_size % 64 == 0)
+    hipLaunchKernelGGL((idx_kept_select_kernel<D, MT, true>), dim3((unsigned)rows), dim3(256), 0, st, a.q_idx,
+                       a.k_idx, a.w, a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I, k,
+                       idx, count);
+  else
+    hipLaunchKernelGGL((idx_kept_select_kernel<D, MT, false>), dim3((unsigned)rows), dim3(256), 0, st, a.q_idx,
+                       a.k_idx, a.w, a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I, k,
+                       idx, count);
   return hipGetLastError();
 }
 

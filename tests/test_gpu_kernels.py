@@ -725,7 +725,7 @@ def test_forward_decode_fused_selection_concentrated(lsa, kind):
 
 
 @pytest.mark.parametrize("T,bs,n_keep,k", [(4096, 128, 8, 256), (2048, 16, 6, 40), (20000, 128, 64, 2048),
-                                           (20000, 128, 100, 2048)])
+                                           (20000, 128, 100, 2048), (5000, 64, 20, 300), (9000, 64, 150, 1000)])
 def test_forward_two_stage_small(lsa, T, bs, n_keep, k):
     """Two-stage lsa_forward against the oracle, and bit for bit against the separate calls
     (block prefilter, kept-slot scores, score-table top-k): with at most 8192 kept slots
