@@ -13,8 +13,13 @@ on its launch stream after every stage (lsa_forward_stages lists them), so every
 stage's kernels are timed live inside the timed region without an event gap in
 every step.
 
+The line also carries the other configurations of the path (the 1K, 32K and 256K-chunk
+prefills, decode over paged caches, the pooled 4:1 indexer, the semantic search), each
+with its dominant kernel against its roofline and the step against T_roof, and the
+machine's measured ceilings (lsa_peak_*), which every fraction is also given against.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-       [--no-cpu-baseline] [--copy-calibration]
+       [--no-cpu-baseline] [--no-peaks] [--peaks] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -166,6 +171,21 @@ def algorithmic(wl):
     }
 
 
+def t_roof_ms(wl):
+    """End-to-end lower bound of one step: max(sum of each contraction's ops at its dense
+    peak, compulsory HBM bytes at peak bandwidth).  Compulsory bytes: the index queries
+    and index keys read once, Q read and O written once, the K/V rows the lists touch
+    (at most the whole visible cache) and the lists written once."""
+    alg = algorithmic(wl)
+    ops_ms = ((alg.get("index_ops", 0) + alg.get("block_ops", 0)) / (INT8_PEAK_TOPS * 1e12)
+              + alg["attn_flops"] / (BF16_PEAK_TFLOPS * 1e12)) * 1e3
+    B, n_q = wl.B, wl.n_q
+    idx_keys = B * wl.L * wl.d_I if not wl.pooled else alg["block_bytes"]
+    kv = min(B * wl.L * wl.d * 2 * 2, alg["attn_gather_bytes"])
+    nbytes = B * n_q * wl.H_I * wl.d_I + idx_keys + B * n_q * wl.H_q * wl.d * 2 * 2 + kv + B * n_q * wl.k * 4
+    return max(ops_ms, nbytes / (HBM_PEAK_GBS * 1e9) * 1e3)
+
+
 def _cpu_threads():
     """Threads the oracle's BLAS uses (the CPU baselines' core count)."""
     try:
@@ -210,7 +230,7 @@ def cpu_baseline(wl, inp, budget_s=10.0):
     rate = done / t_work
     cores = _cpu_threads()
     unit = "tok/s" if wl.n_q == 1 else "queries/s"
-    return {"value": rate, "unit": unit, "cores": cores, "kind": "oracle",
+    return {"value": rate, "unit": unit, "cores": cores, "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{done} row evaluations cycling over {len(rows)} seeded rows of {wl.name} (incl. boundary "
                       f"rows), {t_work:.1f}s of oracle time "
                       f"(numpy fp64 BLAS, int64 scores); rate = rows / time"}
@@ -290,7 +310,8 @@ def cpu_baseline_sem(wl, inp, budget_s=10.0):
         if time.perf_counter() - t1 > budget_s:
             break
     per_token = (time.perf_counter() - t1) / n + per_block / wl.n_cluster
-    return {"value": 1.0 / per_token, "unit": "tok/s", "cores": _cpu_threads(), "kind": "oracle",
+    return {"value": 1.0 / per_token, "unit": "tok/s", "cores": _cpu_threads(), "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"sequence 0 of {wl.name}: its {cache['table'].shape[0]} cluster blocks clustered by the oracle "
                       f"in {t_cluster:.1f}s (one block per {wl.n_cluster} tokens), then {n} selections + attentions "
                       f"of its query in {budget_s:.0f}s; rate = 1 / (time per token + clustering per token)"}
@@ -306,6 +327,102 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's processor string."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _time_launches(torch, launch, reps=5, warm=2):
+    """Best of `reps` timed launches (ms), events on the current stream."""
+    for _ in range(warm):
+        launch()
+    best = float("inf")
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        launch()
+        b.record()
+        b.synchronize()
+        best = min(best, a.elapsed_time(b))
+    return best
+
+
+def measure_peaks(lsa, torch):
+    """The machine's reachable ceilings (lsa_peak_* microbenchmarks): int8 and bf16 MFMA
+    issue, HBM streaming read over 2 GiB, random 256-byte row gathers over a 2 GiB pool
+    after a 1 GiB read that evicts the caches (cold) and over a 64 MiB pool read just
+    before (cache-resident).  Best of 5 launches each."""
+    import ctypes as C
+    L = lsa.lib()
+    dev = torch.device("cuda:0")
+    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    res = {"compute_units": n_cu}
+
+    def sink_for(nb):
+        return torch.empty((L.lsa_peak_sink_ints(nb),), dtype=torch.int32, device=dev)
+
+    def check(rc, name):
+        if rc != 0:
+            raise RuntimeError(f"{name} failed: {rc}")
+
+    nb, iters = 8 * n_cu, 2048
+    sk = sink_for(nb)
+    for kind, key, ops in ((0, "int8_mfma_TOPs", 32768), (1, "bf16_mfma_TFLOPs", 16384)):
+        ms = _time_launches(torch, lambda: check(L.lsa_peak_mfma(kind, iters, nb, C.c_void_p(sk.data_ptr()), st),
+                                                 "lsa_peak_mfma"))
+        res[key] = nb * 4 * iters * 4 * ops / (ms * 1e-3) / 1e12
+    big = torch.ones((2 << 30,), dtype=torch.uint8, device=dev)
+    flush = torch.ones((1 << 30,), dtype=torch.uint8, device=dev)
+    nb = 16 * n_cu
+    sk = sink_for(nb)
+    ms = _time_launches(torch, lambda: check(L.lsa_peak_read(C.c_void_p(big.data_ptr()), big.numel(), nb,
+                                                             C.c_void_p(sk.data_ptr()), st), "lsa_peak_read"))
+    res["hbm_read_GBs"] = big.numel() / (ms * 1e-3) / 1e9
+    n_idx = 1 << 18  # 67 MB of 256-byte rows, the decode step's gather volume
+    g = torch.Generator(device=dev).manual_seed(0)
+    nbg = 4 * n_cu
+
+    def gather_ms(pool, n_rows, evict):
+        idx = torch.randint(0, n_rows, (n_idx,), dtype=torch.int32, device=dev, generator=g)
+        best = float("inf")
+        for _ in range(5):
+            if evict:
+                check(L.lsa_peak_read(C.c_void_p(flush.data_ptr()), flush.numel(), nb, C.c_void_p(sk.data_ptr()), st),
+                      "lsa_peak_read")
+            else:
+                check(L.lsa_peak_gather(C.c_void_p(pool.data_ptr()), n_rows, C.c_void_p(idx.data_ptr()), n_idx, nbg,
+                                        C.c_void_p(sk.data_ptr()), st), "lsa_peak_gather")
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            check(L.lsa_peak_gather(C.c_void_p(pool.data_ptr()), n_rows, C.c_void_p(idx.data_ptr()), n_idx, nbg,
+                                    C.c_void_p(sk.data_ptr()), st), "lsa_peak_gather")
+            b.record()
+            b.synchronize()
+            best = min(best, a.elapsed_time(b))
+        return best
+
+    res["gather_cold_GBs"] = n_idx * 256 / (gather_ms(big, big.numel() // 256, True) * 1e-3) / 1e9
+    warm = big[: 64 << 20]
+    res["gather_warm_GBs"] = n_idx * 256 / (gather_ms(warm, warm.numel() // 256, False) * 1e-3) / 1e9
+    l2 = big[: 2 << 20]
+    res["gather_l2_GBs"] = n_idx * 256 / (gather_ms(l2, l2.numel() // 256, False) * 1e-3) / 1e9
+    res["method"] = ("lsa_peak_* kernels (include/lsa_peaks.h): MFMA loops of 4 independent chains per wave over "
+                     f"{8 * n_cu} workgroups of 4 waves; 2 GiB streaming read; {n_idx} random 256-byte rows from a "
+                     "2 GiB pool after a 1 GiB read (cold), from a 64 MiB pool (Infinity Cache resident) and from a "
+                     "2 MiB pool (L2 resident), the warm pools read just before; best of 5")
+    del big, flush
+    torch.cuda.empty_cache()
+    return res
 
 
 class SemStep:
@@ -435,6 +552,40 @@ def measure_sem(lsa, torch, wl, steps, warmup):
     return inp, step, ms, cluster
 
 
+def prefill_object(lsa, torch, name, steps, warmup, peaks, with_cpu):
+    """One flat prefill configuration: throughput, the indexer scan's int8 MFMA roofline,
+    the step against T_roof, prefill attention's bf16 utilisation beside its gather rate,
+    and the oracle on a sample of its rows."""
+    import synthetic
+    wl = synthetic.WORKLOADS[name]
+    inp, step, ms = measure(lsa, torch, wl, steps, warmup)
+    km = step.kernel_ms()
+    alg = algorithmic(wl)
+    tr = t_roof_ms(wl)
+    obj = {"workload": _describe(wl), "value": wl.B * wl.n_q / (ms * 1e-3), "unit": "queries/s", "ms_per_step": ms,
+           "kernel_ms": km, "t_roof_ms": tr, "step_roofline_frac": tr / ms, "roofline": None}
+    stage = "index_select" if "index_select" in km else "index_scores"
+    scan_ms = km[stage]["ms_per_step"]
+    if wl.L > 4096:  # the tiny case is launch-bound: its time is reported, not a roofline
+        ach = alg["index_ops"] / (scan_ms * 1e-3) / 1e12
+        obj["roofline"] = {"bound": "mfma", "kernel": f"{stage} (flat indexer scan, idx_flat_kernel)",
+                           "achieved": ach, "peak": INT8_PEAK_TOPS, "unit": "TOP/s", "frac": ach / INT8_PEAK_TOPS,
+                           "frac_of_measured_peak": ach / peaks["int8_mfma_TOPs"] if peaks else None,
+                           "algorithmic_ops_per_step": alg["index_ops"], "launch_ms_per_step": scan_ms}
+    at_ms = km["sparse_attn"]["ms_per_step"]
+    gb = alg["attn_gather_bytes"] / (at_ms * 1e-3) / 1e9
+    tf = alg["attn_flops"] / (at_ms * 1e-3) / 1e12
+    obj["attention"] = {"bf16_TFLOPs": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS, "gather_GBs": gb,
+                        "frac_of_measured_warm_gather": gb / peaks["gather_warm_GBs"] if peaks else None,
+                        "frac_of_measured_l2_gather": gb / peaks["gather_l2_GBs"] if peaks else None,
+                        "gather_bytes": alg["attn_gather_bytes"]}
+    if with_cpu:
+        obj["cpu_baseline"] = cpu_baseline(wl, inp)
+    del inp, step
+    torch.cuda.empty_cache()
+    return obj
+
+
 def measure(lsa, torch, wl, steps, warmup):
     import synthetic
     inp = synthetic.make_inputs(wl, torch.device("cuda:0"))
@@ -465,6 +616,8 @@ def main():
     ap.add_argument("--workload", default=None, help="time only this workload (no headline line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--peaks", action="store_true", help="only measure the machine's ceilings")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the ceilings in the default run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); sharding the path "
@@ -477,6 +630,9 @@ def main():
     lsa.lib()
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.peaks:
+        print(json.dumps({"measured_peaks": measure_peaks(lsa, torch)}), flush=True)
         return
 
     if args.workload:
@@ -499,6 +655,8 @@ def main():
             torch.cuda.empty_cache()
         return
 
+    peaks = None if args.no_peaks else measure_peaks(lsa, torch)
+
     # ---- headline: decode at 128K
     wl = synthetic.WORKLOADS["decode_128k"]
     inp, step, ms = measure(lsa, torch, wl, args.steps, args.warmup)
@@ -509,7 +667,7 @@ def main():
     idx_ms = kms[idx_stage]["ms_per_launch"]
     launches = kms[idx_stage]["launches_per_step"]
     achieved = alg["index_bytes"] / launches / (idx_ms * 1e-3) / 1e9
-    roof_t_ms = max(alg["index_bytes"] + alg["attn_gather_bytes"], 0) / (HBM_PEAK_GBS * 1e9) * 1e3
+    roof_t_ms = t_roof_ms(wl)
     res = {
         "metric": METRIC,
         "value": tok_s,
@@ -529,15 +687,20 @@ def main():
             "bound": "hbm", "kernel": f"{idx_stage} (decode scan, idx_decode_kernel)",
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
             "traffic": measured_traffic(),
+            "frac_of_measured_peak": achieved / peaks["hbm_read_GBs"] if peaks else None,
             "algorithmic_bytes_per_launch": alg["index_bytes"] / launches, "launch_ms": idx_ms,
         },
         "kernel_ms": kms,
+        "t_roof_ms": roof_t_ms,
         "step_roofline_frac": roof_t_ms / ms,
         "decode_attn": {
             "achieved_GBs": alg["attn_gather_bytes"] / (kms["sparse_attn"]["ms_per_step"] * 1e-3) / 1e9,
             "frac_hbm": alg["attn_gather_bytes"] / (kms["sparse_attn"]["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "frac_of_measured_cold_gather": (alg["attn_gather_bytes"] / (kms["sparse_attn"]["ms_per_step"] * 1e-3)
+                                             / 1e9 / peaks["gather_cold_GBs"]) if peaks else None,
             "gather_bytes": alg["attn_gather_bytes"],
         },
+        "measured_peaks": peaks,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, inp)
@@ -581,21 +744,39 @@ def main():
     ts_stage = "index_select" if "index_select" in kp else "index_scores"
     ts_desc = ("index_select (token-stage scores in kept blocks + exact top-k, one kernel)"
                if ts_stage == "index_select" else "index_scores (token stage in kept blocks)")
+    ach_p = ap_["index_ops"] / (kp[ts_stage]["ms_per_step"] * 1e-3) / 1e12
+    at_p = kp["sparse_attn"]["ms_per_step"]
     res["prefill_128k"] = {
         "workload": _describe(wp),
         "value": wp.n_q / (ms_p * 1e-3), "unit": "queries/s", "ms_per_step": ms_p,
         "kernel_ms": kp,
         "roofline": {
             "bound": "mfma", "kernel": ts_desc,
-            "achieved": ap_["index_ops"] / (kp[ts_stage]["ms_per_step"] * 1e-3) / 1e12,
-            "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-            "frac": ap_["index_ops"] / (kp[ts_stage]["ms_per_step"] * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+            "achieved": ach_p, "peak": INT8_PEAK_TOPS, "unit": "TOP/s", "frac": ach_p / INT8_PEAK_TOPS,
+            "frac_of_measured_peak": ach_p / peaks["int8_mfma_TOPs"] if peaks else None,
+        },
+        "t_roof_ms": t_roof_ms(wp),
+        "step_roofline_frac": t_roof_ms(wp) / ms_p,
+        "attention": {
+            "bf16_TFLOPs": ap_["attn_flops"] / (at_p * 1e-3) / 1e12,
+            "frac_bf16_peak": ap_["attn_flops"] / (at_p * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "gather_GBs": ap_["attn_gather_bytes"] / (at_p * 1e-3) / 1e9,
+            "frac_of_measured_warm_gather": (ap_["attn_gather_bytes"] / (at_p * 1e-3) / 1e9
+                                             / peaks["gather_warm_GBs"]) if peaks else None,
+            "frac_of_measured_l2_gather": (ap_["attn_gather_bytes"] / (at_p * 1e-3) / 1e9
+                                           / peaks["gather_l2_GBs"]) if peaks else None,
         },
     }
     if not args.no_cpu_baseline:
         res["prefill_128k"]["cpu_baseline"] = cpu_baseline(wp, inp, budget_s=10.0)
     del inp, step
     torch.cuda.empty_cache()
+
+    # ---- the flat prefill configurations: tiny (parity size), 32K from position 0, and
+    # one GPU's 16384-query chunk of a 256K context
+    for name in ("tiny_prefill_1k", "prefill_32k", "chunk_256k"):
+        res[name] = prefill_object(lsa, torch, name, args.steps if name != "chunk_256k" else max(1, args.steps // 5),
+                                   args.warmup, peaks, not args.no_cpu_baseline)
 
     # ---- the pages' own method: flat semantic search at 128K, decode and a prefill chunk
     for name, unit in (("decode_128k_lsa", "tok/s"), ("decode_128k_lsa_paged", "tok/s"),

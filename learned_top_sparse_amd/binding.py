@@ -24,6 +24,7 @@ EXPORTED = [
     "lsa_semantic_cluster", "lsa_semantic_select_workspace_size", "lsa_semantic_select",
     "lsa_semantic_cluster_paged", "lsa_semantic_select_paged", "lsa_sparse_attn_pool", "lsa_semantic_select_timed",
     "lsa_forward_noalloc",
+    "lsa_peak_sink_ints", "lsa_peak_mfma", "lsa_peak_read", "lsa_peak_gather",
 ]
 
 # size of the device array lsa_forward_noalloc works in (LSA_NOALLOC_SCRATCH_BYTES)
@@ -90,6 +91,10 @@ def lib():
         L.lsa_forward_workspace_size.argtypes = [C.POINTER(ForwardArgs), C.POINTER(SZ)]
         L.lsa_forward.argtypes = [C.POINTER(ForwardArgs), P, SZ, P]
         L.lsa_forward_noalloc.argtypes = [C.POINTER(ForwardArgs), P]
+        L.lsa_peak_sink_ints.argtypes = [I32]
+        L.lsa_peak_mfma.argtypes = [I32, I64, I32, P, P]
+        L.lsa_peak_read.argtypes = [P, I64, I32, P, P]
+        L.lsa_peak_gather.argtypes = [P, I64, P, I64, I32, P, P]
         L.lsa_forward_plan.argtypes = [C.POINTER(ForwardArgs), SZ, C.POINTER(I64), C.POINTER(I32)]
         L.lsa_forward_stages.argtypes = [C.POINTER(ForwardArgs), SZ, C.POINTER(I32), I32, C.POINTER(I32)]
         SP = C.POINTER(SemanticParams)

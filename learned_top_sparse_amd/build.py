@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblsa.so")
-SOURCES = ["lsa_indexer.hip", "lsa_topk.hip", "lsa_attn.hip", "lsa_semantic.hip", "lsa_api.cpp", "lsa_noalloc.hip"]
+SOURCES = ["lsa_indexer.hip", "lsa_topk.hip", "lsa_attn.hip", "lsa_semantic.hip", "lsa_api.cpp", "lsa_noalloc.hip", "lsa_peaks.hip"]
 # sources whose arithmetic decides integers (merges, kept buckets): no fused multiply-add
 # unless written out, so every value is rounded in the order the source gives
 NO_CONTRACT = {"lsa_semantic.hip"}

@@ -28,6 +28,13 @@ def test_bench_headline_line():
     r = d["roofline"]
     assert r["bound"] in ("hbm", "mfma", "alu") and 0 < r["frac"] < 1.5 and r["peak"] > 0
     for wl in ("decode_128k_paged", "decode_128k_pool4", "prefill_128k", "decode_128k_lsa", "decode_128k_lsa_paged",
-               "prefill_128k_lsa"):
+               "prefill_128k_lsa", "tiny_prefill_1k", "prefill_32k", "chunk_256k"):
         assert d[wl]["ms_per_step"] > 0 and d[wl]["kernel_ms"], wl
     assert 0 < d["prefill_128k"]["roofline"]["frac"] < 1.5
+    for wl in ("prefill_32k", "chunk_256k"):
+        assert 0 < d[wl]["roofline"]["frac"] < 1.5 and 0 < d[wl]["step_roofline_frac"] <= 1.0, wl
+        assert d[wl]["attention"]["gather_GBs"] > 0, wl
+    pk = d["measured_peaks"]
+    # measured ceilings below the published ones (8 TB/s, 5.0 POPS int8, 2.5 PFLOP/s bf16)
+    assert 0 < pk["hbm_read_GBs"] < 8000 and 0 < pk["int8_mfma_TOPs"] < 5100 and 0 < pk["bf16_mfma_TFLOPs"] < 2600
+    assert 0 < pk["gather_cold_GBs"] < pk["gather_l2_GBs"]
