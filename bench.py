@@ -592,7 +592,8 @@ def measure(lsa, torch, wl, steps, warmup):
     if wl.pooled:
         # the block-key cache is kept with the caches (a serving loop updates one block per
         # block_size tokens), so it is built before the timed steps
-        inp["block_keys"] = lsa.lsa_block_cache(inp["k_idx"], wl.block_size)
+        inp["block_keys"] = lsa.lsa_block_cache(inp["k_idx"], wl.block_size, page_table=inp.get("page_table"),
+                                                page_size=wl.page_size)
     torch.cuda.synchronize()
     step = Step(lsa, torch, wl, inp)
     step.make_events((steps + EVENTS_EVERY - 1) // EVENTS_EVERY)
@@ -733,6 +734,15 @@ def main():
     }
     del inp, step
     torch.cuda.empty_cache()
+
+    # ---- the block modes over paged caches (pools of 64-token pages, seeded page order)
+    for name, unit in (("decode_128k_pool4_paged", "tok/s"), ("two_stage_128k_paged", "queries/s")):
+        wx = synthetic.WORKLOADS[name]
+        inp, step, ms_x = measure(lsa, torch, wx, args.steps, args.warmup)
+        res[name] = {"workload": _describe(wx), "value": wx.B * wx.n_q / (ms_x * 1e-3), "unit": unit,
+                     "ms_per_step": ms_x, "kernel_ms": step.kernel_ms()}
+        del inp, step
+        torch.cuda.empty_cache()
 
     # ---- prefill at 128K (two-stage chunk)
     wp = synthetic.WORKLOADS["two_stage_128k"]

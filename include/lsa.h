@@ -129,6 +129,18 @@ lsa_status lsa_block_reps(const int8_t* k_idx, int32_t B, int32_t L_max, int32_t
 lsa_status lsa_block_cache(const int8_t* k_idx, int32_t B, int32_t L_max, int32_t d_I, int32_t block_size,
                            int32_t n_blocks, int32_t first_block, int32_t n_update, int8_t* block_keys,
                            void* stream);
+/* The same cache for index keys in a paged pool ([LSA] App. F.1 "Attention kernels":
+ * caches are read through page tables; reading as lsa_forward_args.page_table below):
+ * k_idx_pool int8 [n_slots, d_I], page_table int32 [B, max_pages], pages of page_size
+ * keys (a power of two >= 64; n_slots a multiple of it, at most 2^31).  Logical key j
+ * of sequence b is pool row page_table[b][j / page_size] * page_size + j % page_size;
+ * page ids outside [0, n_slots / page_size) are clamped into it.  The cache itself is
+ * per sequence, [B, n_blocks, 2, d_I] as above; the blocks cover logical keys, so
+ * (first_block + n_update) * block_size <= max_pages * page_size. */
+lsa_status lsa_block_cache_paged(const int8_t* k_idx_pool, int64_t n_slots, const int32_t* page_table,
+                                 int32_t page_size, int32_t max_pages, int32_t B, int32_t d_I, int32_t block_size,
+                                 int32_t n_blocks, int32_t first_block, int32_t n_update, int8_t* block_keys,
+                                 void* stream);
 
 /*
  * Two-stage block prefilter ([HISA]; [LSA] §2.2 "Related Work": score blocks
@@ -262,10 +274,13 @@ typedef struct lsa_forward_args {
      n_slots a multiple of it (at most 2^31).  Page ids outside [0, n_slots / page_size)
      are clamped into that range (no fault; the result is then unspecified).  Selection
      runs on logical keys (ties: lower logical index) and idx receives the pool rows of
-     the kept keys, in ascending logical order, -1 padded.  Supported for flat calls
-     (two_stage = 0, else LSA_ERR_UNSUPPORTED): decode and prefill chunks alike; a chunk
-     of fewer than 8 queries per sequence must fit its decode selection state in the
-     workspace (else LSA_ERR_WORKSPACE).  Sequences of different lengths share a call through q_pos;
+     the kept keys, in ascending logical order, -1 padded.  Flat calls: decode and
+     prefill chunks alike; a chunk of fewer than 8 queries per sequence must fit its
+     decode selection state in the workspace (else LSA_ERR_WORKSPACE).  Block modes:
+     the block-key cache covers logical blocks (block_keys from lsa_block_cache_paged,
+     or built here through the page table) and kept_blocks holds logical block ids;
+     the two-stage token stage must take its one-kernel form (n_keep <= 256 and
+     n_keep * block_size <= 8192, else LSA_ERR_UNSUPPORTED).  Sequences of different lengths share a call through q_pos;
      with L_max fixed (one per range of context lengths) the launches keep one shape,
      so a captured HIP graph replays for any positions and page tables.
      page_table == NULL: contiguous caches [B, L_max, ...]. */

@@ -23,7 +23,7 @@ EXPORTED = [
     "lsa_forward_workspace_size", "lsa_forward", "lsa_forward_plan", "lsa_forward_stages",
     "lsa_semantic_cluster", "lsa_semantic_select_workspace_size", "lsa_semantic_select",
     "lsa_semantic_cluster_paged", "lsa_semantic_select_paged", "lsa_sparse_attn_pool", "lsa_semantic_select_timed",
-    "lsa_forward_noalloc",
+    "lsa_forward_noalloc", "lsa_block_cache_paged",
     "lsa_peak_sink_ints", "lsa_peak_mfma", "lsa_peak_read", "lsa_peak_gather",
 ]
 
@@ -81,6 +81,7 @@ def lib():
         L.lsa_index_scores.argtypes = [P, P, P, I32, P, P, I32, I32, I32, I32, I32, I32, I32, P, I64, P]
         L.lsa_block_reps.argtypes = [P, I32, I32, I32, I32, I32, P, P]
         L.lsa_block_cache.argtypes = [P, I32, I32, I32, I32, I32, I32, I32, P, P]
+        L.lsa_block_cache_paged.argtypes = [P, I64, P, I32, I32, I32, I32, I32, I32, I32, I32, P, P]
         L.lsa_block_prefilter_workspace_size.argtypes = [I32, I32, I32, I32, C.POINTER(SZ)]
         L.lsa_block_prefilter.argtypes = [P, P, P, I32, P, I32, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
         L.lsa_topk_workspace_size.argtypes = [I32, I32, I32, I32, C.POINTER(SZ)]
@@ -201,12 +202,19 @@ def lsa_block_reps(k_idx, block_size: int, n_blocks: Optional[int] = None):
 
 
 def lsa_block_cache(k_idx, block_size: int, n_blocks: Optional[int] = None, out: Optional[torch.Tensor] = None,
-                    first_block: int = 0, n_update: Optional[int] = None):
+                    first_block: int = 0, n_update: Optional[int] = None, page_table=None, page_size: int = 0):
     """Block-key cache int8 [B, n_blocks, 2, d_I] (hi, lo parts of each block's key sum);
-    with ``out`` given, only blocks [first_block, first_block + n_update) are (re)written."""
+    with ``out`` given, only blocks [first_block, first_block + n_update) are (re)written.
+    With ``page_table`` (int32 [B, max_pages]) and ``page_size``, k_idx is a pool
+    [n_slots, d_I] read through the page table (lsa_block_cache_paged)."""
     dev = k_idx.device
     _need(k_idx, "k_idx", torch.int8)
-    B, L, d_I = k_idx.shape
+    if page_table is not None:
+        _need(page_table, "page_table", torch.int32, dev)
+        B, max_pages = page_table.shape
+        L, d_I = max_pages * page_size, k_idx.shape[1]
+    else:
+        B, L, d_I = k_idx.shape
     if n_blocks is None:
         n_blocks = L // block_size
     if out is None:
@@ -214,6 +222,11 @@ def lsa_block_cache(k_idx, block_size: int, n_blocks: Optional[int] = None, out:
     _need(out, "block_keys", torch.int8, dev)
     if n_update is None:
         n_update = n_blocks - first_block
+    if page_table is not None:
+        st = lib().lsa_block_cache_paged(_ptr(k_idx), k_idx.shape[0], _ptr(page_table), page_size, max_pages, B,
+                                         d_I, block_size, n_blocks, first_block, n_update, _ptr(out), _stream(dev))
+        _check("lsa_block_cache_paged", st)
+        return out
     st = lib().lsa_block_cache(_ptr(k_idx), B, L, d_I, block_size, n_blocks, first_block, n_update, _ptr(out),
                                _stream(dev))
     _check("lsa_block_cache", st)

@@ -209,6 +209,31 @@ LSA_API lsa_status lsa_block_cache(const int8_t* k_idx, int32_t B, int32_t L_max
                                             block_keys, as_stream(stream)));
 }
 
+LSA_API lsa_status lsa_block_cache_paged(const int8_t* k_idx_pool, int64_t n_slots, const int32_t* page_table,
+                                         int32_t page_size, int32_t max_pages, int32_t B, int32_t d_I,
+                                         int32_t block_size, int32_t n_blocks, int32_t first_block, int32_t n_update,
+                                         int8_t* block_keys, void* stream) {
+  if (page_size < 64 || (page_size & (page_size - 1)) != 0 || max_pages < 1 ||
+      (long long)max_pages * page_size > 0x7FFFFFFFLL || n_slots < page_size || n_slots % page_size != 0 ||
+      n_slots > (1LL << 31))
+    return LSA_ERR_INVALID_ARG;
+  const int32_t L_max = max_pages * page_size;
+  if (B < 0 || block_size < 1 || n_blocks < 0 || first_block < 0 || n_update < 0 ||
+      (long long)first_block + n_update > n_blocks || ((long long)first_block + n_update) * block_size > L_max)
+    return LSA_ERR_INVALID_ARG;
+  if (d_I != 64 && d_I != 128) return LSA_ERR_UNSUPPORTED;
+  if (block_size > 128) return LSA_ERR_UNSUPPORTED;
+  if ((long long)B * n_update == 0) return LSA_OK;
+  if (!k_idx_pool || !page_table || !block_keys) return LSA_ERR_INVALID_ARG;
+  lsa::Pages pg{};
+  pg.page_table = page_table;
+  pg.page_log2 = __builtin_ctz((unsigned)page_size);
+  pg.max_pages = max_pages;
+  pg.n_pages = (int)(n_slots / page_size);
+  return hip_status(lsa::launch_block_cache(k_idx_pool, B, L_max, d_I, block_size, n_blocks, first_block, n_update,
+                                            block_keys, as_stream(stream), pg));
+}
+
 LSA_API lsa_status lsa_topk_workspace_size(int32_t B, int32_t n_q, int32_t L_max, int32_t k, size_t* bytes) {
   if (!bytes || B < 0 || n_q < 0 || L_max < 0 || k < 0) return LSA_ERR_INVALID_ARG;
   *bytes = lsa::topk_ws_bytes((long long)B * n_q, L_max);
@@ -365,7 +390,9 @@ lsa_status check_forward(const lsa_forward_args* a) {
         (long long)a->max_pages * a->page_size != a->L_max || a->n_slots < a->page_size ||
         a->n_slots % a->page_size != 0 || a->n_slots > (1ll << 31))
       return LSA_ERR_INVALID_ARG;
-    if (a->two_stage) return LSA_ERR_UNSUPPORTED;
+    // block modes over paged caches: the token stage's scores and top-k in one kernel
+    if (a->two_stage == 1 && !(a->n_keep <= 256 && (long long)a->n_keep * a->block_size <= lsa::KSEL_SLOTS))
+      return LSA_ERR_UNSUPPORTED;
   }
   if ((long long)a->B * a->n_q == 0) return LSA_OK;
   if (!a->q_idx || !a->k_idx || !a->w || !a->q_pos || !a->q || !a->k || !a->v || !a->idx || !a->out)
@@ -558,8 +585,8 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
   if (a->stage_events != nullptr &&
       (long long)a->n_stage_events < 1 + (long long)forward_stages(a, p, rows).size())
     return LSA_ERR_INVALID_ARG;
-  if (a->page_table) {
-    // paged caches: chunks of fewer than 8 queries per sequence must take the decode selection
+  if (a->page_table && !a->two_stage) {
+    // paged caches: flat chunks of fewer than 8 queries per sequence must take the decode selection
     const size_t tws = topk_ws_for(a, rows);
     bool ok = true;
     for_each_chunk(a, rows, [&](int32_t, int32_t nb, int32_t, int32_t ni) {
@@ -627,8 +654,8 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
   // one split count for every chunk, so no chunk needs more attention workspace than sized
   const int split = resolve_split(1, (int32_t)rows, kt, a->attn_split);
   if (a->two_stage && p.n_blocks > 0 && limbs_ws) {
-    if (lsa::launch_block_cache(a->k_idx, a->B, L, d_I, a->block_size, p.n_blocks, 0, p.n_blocks, limbs_ws, s) !=
-            hipSuccess ||
+    if (lsa::launch_block_cache(a->k_idx, a->B, L, d_I, a->block_size, p.n_blocks, 0, p.n_blocks, limbs_ws, s,
+                                chunk_pages(a, 0)) != hipSuccess ||
         !mark())
       return LSA_ERR_HIP;
   }
@@ -677,13 +704,15 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
         hipError_t e;
         if (a->two_stage == 2) {
           // pooled blocks: the list is every key of the kept blocks the query may see
-          e = lsa::launch_expand(kept, qp, (long long)nb * ni, a->block_size, a->n_keep, kt, ix, cnt, s);
+          e = lsa::launch_expand(kept, qp, (long long)nb * ni, a->block_size, a->n_keep, kt, ix, cnt, s,
+                                 chunk_pages(a, b0), ni);
         } else {
           // the token stage and its top-k in one kernel
           e = lsa::launch_kept_select(ia, kt, ix, cnt, s);
         }
         if (e != hipSuccess || !mark()) return LSA_ERR_HIP;
-        lsa_status sa = run_attn(qq, kk, vv, ix, nb, ni, L, H_q, d, kt, a->scale, split, oo, ls, attn_ws, s);
+        lsa_status sa = run_attn(qq, kk, vv, ix, nb, ni, L, H_q, d, kt, a->scale, split, oo, ls, attn_ws, s,
+                                 paged ? (long long)a->n_slots : 0ll);
         if (sa != LSA_OK) return sa;
         return mark() ? LSA_OK : LSA_ERR_HIP;
       }

@@ -718,18 +718,30 @@ __global__ void blk_limbs_kernel(const int32_t* __restrict__ reps, int D, long l
 
 // Block-key cache: blocks [m0, m0 + n_upd) of every sequence, each written as the
 // two int8 limbs of its representative (the sum of its bs keys), rows laid out as
-// blk_limbs_kernel writes them.  Thread e: one byte column c of block m.
+// blk_limbs_kernel writes them.  Thread e: one byte column c of block m.  With a page
+// table (pg.page_table set) k_idx is a pool and key j of sequence b is pool row
+// page_table[b][j >> page_log2] << page_log2 | (j & mask) (page ids clamped).
 __global__ void blk_cache_kernel(const int8_t* __restrict__ k_idx, int L_max, int D, int bs, int n_blocks, int m0,
-                                 int n_upd, long long total, int8_t* __restrict__ limbs) {
+                                 int n_upd, long long total, int8_t* __restrict__ limbs, Pages pg) {
   const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= total) return;
   const int c = (int)(e % D);
   const long long bm = e / D;
   const int m = m0 + (int)(bm % n_upd);
   const long long b = bm / n_upd;
-  const int8_t* src = k_idx + (b * L_max + (long long)m * bs) * D + c;
   int r = 0;
-  for (int t = 0; t < bs; ++t) r += src[(long long)t * D];
+  if (pg.page_table != nullptr) {
+    const int32_t* pt = pg.page_table + b * pg.max_pages;
+    const int pmask = (1 << pg.page_log2) - 1;
+    for (int t = 0; t < bs; ++t) {
+      const int j = m * bs + t;
+      const long long page = min(max(pt[j >> pg.page_log2], 0), pg.n_pages - 1);
+      r += k_idx[((page << pg.page_log2) | (j & pmask)) * D + c];
+    }
+  } else {
+    const int8_t* src = k_idx + (b * L_max + (long long)m * bs) * D + c;
+    for (int t = 0; t < bs; ++t) r += src[(long long)t * D];
+  }
   const int hi = (r + 64) >> 7;
   int8_t* dst = limbs + (b * n_blocks + m) * 2 * D;
   dst[c] = (int8_t)hi;
@@ -1142,12 +1154,15 @@ hipError_t launch_block_limbs(const int32_t* reps, int B, int n_blocks, int d_I,
 }
 
 hipError_t launch_block_cache(const int8_t* k_idx, int B, int L_max, int d_I, int bs, int n_blocks, int m0,
-                              int n_upd, int8_t* limbs, hipStream_t st) {
+                              int n_upd, int8_t* limbs, hipStream_t st, const Pages& pg) {
   const long long total = (long long)B * n_upd * d_I;
   if (total == 0) return hipSuccess;
   if (m0 < 0 || n_upd < 0 || m0 + n_upd > n_blocks || (long long)(m0 + n_upd) * bs > L_max) return hipErrorInvalidValue;
+  if (pg.page_table != nullptr &&
+      (pg.page_log2 < 6 || pg.page_log2 > 30 || pg.n_pages < 1 || (long long)pg.max_pages << pg.page_log2 < L_max))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(blk_cache_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, k_idx, L_max, d_I,
-                     bs, n_blocks, m0, n_upd, total, limbs);
+                     bs, n_blocks, m0, n_upd, total, limbs, pg);
   return hipGetLastError();
 }
 

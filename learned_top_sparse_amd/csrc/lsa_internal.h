@@ -138,10 +138,10 @@ bool blk_cand_layout(long long rows, int n_q, int n_blocks, int n_keep, void* re
                      BlkCand* c);
 // block-key cache (the limbs of the representatives) of blocks [m0, m0 + n_upd)
 hipError_t launch_block_cache(const int8_t* k_idx, int B, int L_max, int d_I, int bs, int n_blocks, int m0,
-                              int n_upd, int8_t* limbs, hipStream_t st);
+                              int n_upd, int8_t* limbs, hipStream_t st, const Pages& pg = Pages{});
 // pooled blocks: index lists = the keys of the kept blocks a query may see
 hipError_t launch_expand(const int32_t* kept, const int32_t* q_pos, long long rows, int bs, int n_keep, int k,
-                         int32_t* idx, int32_t* count, hipStream_t st);
+                         int32_t* idx, int32_t* count, hipStream_t st, const Pages& pg = Pages{}, int n_q = 1);
 hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 // two-stage token stage and its top-k in one kernel (rows of at most KSEL_SLOTS kept slots)

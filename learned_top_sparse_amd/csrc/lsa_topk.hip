@@ -79,7 +79,7 @@ __device__ __forceinline__ unsigned radix_select32(int n, int need, int* h256, i
 // One query row as seen by the selection: candidate slots [0, n_slots), their
 // scores in global memory, and (two-stage mode) the kept-block table in LDS.  The
 // written list holds key_of(slot): the key (two-stage: through the kept blocks), or
-// with paged caches (flat rows, pt set) the key's pool row.
+// with paged caches (pt set) the key's pool row.
 template <bool KEPT>
 struct RowView {
   const int32_t* srow;
@@ -103,13 +103,13 @@ struct RowView {
     return bs_log2 >= 0 ? (s >> bs_log2) : (int)__umulhi((unsigned)s, bs_magic);
   }
   __device__ __forceinline__ int key_of(int s) const {
+    int key = s;
     if constexpr (KEPT) {
       const int bi = blk_of(s);
-      return kept_s[bi] * bs + (s - bi * bs);
-    } else {
-      if (pt == nullptr) return s;
-      return (min(max(pt[s >> plog2], 0), n_pages - 1) << plog2) | (s & ((1 << plog2) - 1));
+      key = kept_s[bi] * bs + (s - bi * bs);
     }
+    if (pt == nullptr) return key;
+    return (min(max(pt[key >> plog2], 0), n_pages - 1) << plog2) | (key & ((1 << plog2) - 1));
   }
   __device__ __forceinline__ bool valid(int s) const {
     if (s >= n_slots) return false;
@@ -605,11 +605,13 @@ __global__ __launch_bounds__(NT) void topk_kernel(const int32_t* __restrict__ sc
 // read back.  Rows of at most KSEL_SLOTS slots (n_keep * bs).
 // GB (bs a multiple of 64): a 64-slot group lies in one kept block, so one wave-uniform
 // lookup of that block gives the keys of the whole group (no per-slot division).
-template <int D, int MT, bool GB>
+// PAGED: k_idx is a pool of pages of 2^page_log2 >= 64 keys behind the sequence's page
+// table (a 64-aligned group of keys lies in one page); the list receives pool rows.
+template <int D, int MT, bool GB, bool PAGED>
 __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
     int w_per_query, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ kept, int bs, int n_keep,
-    int n_q, int L_max, int H_I, int k, int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+    int n_q, int L_max, int H_I, int k, int32_t* __restrict__ idx, int32_t* __restrict__ count, Pages pg) {
   constexpr int NT = 256, NW = NT / 64, KS = D / 64, RING = 4;
   __shared__ int kept_s[256];
   __shared__ __attribute__((aligned(16))) int sbuf[KSEL_SLOTS];
@@ -644,12 +646,23 @@ __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
     }
     (void)block_exclusive_scan<NT>(c, scan_tmp, &n_valid);
   }
-  const int8_t* kb = k_idx + (long long)b * L_max * D;
+  const int8_t* kb = k_idx + (PAGED ? 0ll : (long long)b * L_max * D);
+  const int32_t* pt = PAGED ? pg.page_table + (long long)b * pg.max_pages : nullptr;
+  const int pmask = PAGED ? (1 << pg.page_log2) - 1 : 0;
+  // pool row of logical key j (paged caches; page ids clamped into the pool).  The own
+  // block may run past the last page (its keys there are never candidates): the page
+  // index is clamped into the sequence's table.
+  auto pool_row = [&](int j) -> long long {
+    const int pi = min(j >> pg.page_log2, pg.max_pages - 1);
+    return ((long long)min(max(pt[pi], 0), pg.n_pages - 1) << pg.page_log2) | (j & pmask);
+  };
   // a slot without a kept block, or past the cache, reads a fallback row: its score is
   // never a candidate, and the loads stay unconditional
-  auto key_load = [&](int sl) -> int {
+  auto key_load = [&](int sl) -> long long {
     const int blk = kept_s[sl / bs];
-    return blk >= 0 ? min(blk * bs + sl % bs, L_max - 1) : 0;
+    const int j = blk >= 0 ? min(blk * bs + sl % bs, L_max - 1) : 0;
+    if constexpr (PAGED) return pool_row(j);
+    return j;
   };
   v4i ring[RING][4][KS];
   auto load_group = [&](int i, v4i (&Bf)[4][KS]) {
@@ -660,16 +673,20 @@ __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
       const int bi = sgc / bs;
       const int blk = kept_s[bi];
       const int base = blk >= 0 ? blk * bs + (sgc - bi * bs) : 0;
+      // paged: the group's 64 keys lie in the page of its first key (base and the page
+      // size are multiples of 64)
+      const long long rbase = PAGED ? pool_row(base) : (long long)base;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const int8_t* kr = kb + (long long)min(base + 16 * nt + r16, L_max - 1) * D;
+        const int8_t* kr =
+            kb + (PAGED ? rbase + 16 * nt + r16 : (long long)min(base + 16 * nt + r16, L_max - 1)) * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
       }
     } else {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const int8_t* kr = kb + (long long)key_load(min(sg + 16 * nt + r16, n_slots - 1)) * D;
+        const int8_t* kr = kb + key_load(min(sg + 16 * nt + r16, n_slots - 1)) * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
       }
@@ -726,6 +743,11 @@ __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
   rv.p = p;
   rv.set_block_size(bs);
   rv.vec = true;
+  if constexpr (PAGED) {  // the list receives pool rows
+    rv.pt = pt;
+    rv.plog2 = pg.page_log2;
+    rv.n_pages = pg.n_pages;
+  }
   if (count != nullptr && tid == 0) count[row] = min(k, n_valid);
   select_row<NT, true>(rv, n_valid, k, out, lds_big, wcnt, scan_tmp, h256, sh);
 }
@@ -733,14 +755,16 @@ __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
 template <int D, int MT>
 static hipError_t launch_kept_select_t(const IdxArgs& a, int k, int32_t* idx, int32_t* count, hipStream_t st) {
   const long long rows = (long long)a.B * a.n_q;
-  if (a.block_size % 64 == 0)
-    hipLaunchKernelGGL((idx_kept_select_kernel<D, MT, true>), dim3((unsigned)rows), dim3(256), 0, st, a.q_idx,
-                       a.k_idx, a.w, a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I, k,
-                       idx, count);
-  else
-    hipLaunchKernelGGL((idx_kept_select_kernel<D, MT, false>), dim3((unsigned)rows), dim3(256), 0, st, a.q_idx,
-                       a.k_idx, a.w, a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I, k,
-                       idx, count);
+  const bool gb = a.block_size % 64 == 0, paged = a.pages.page_table != nullptr;
+#define LSA_KSEL(GB, PG)                                                                                             \
+  hipLaunchKernelGGL((idx_kept_select_kernel<D, MT, GB, PG>), dim3((unsigned)rows), dim3(256), 0, st, a.q_idx,       \
+                     a.k_idx, a.w, a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I, k, \
+                     idx, count, a.pages)
+  if (gb && paged) LSA_KSEL(true, true);
+  else if (gb) LSA_KSEL(true, false);
+  else if (paged) LSA_KSEL(false, true);
+  else LSA_KSEL(false, false);
+#undef LSA_KSEL
   return hipGetLastError();
 }
 
@@ -1877,18 +1901,23 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
 template <int NT>
 __global__ __launch_bounds__(NT) void expand_kernel(const int32_t* __restrict__ kept, const int32_t* __restrict__ q_pos,
                                                     int bs, int n_keep, int k, int32_t* __restrict__ idx,
-                                                    int32_t* __restrict__ count) {
+                                                    int32_t* __restrict__ count, Pages pg, int n_q) {
   __shared__ int scan_tmp[NT / 64 + 1];
   const long long row = blockIdx.x;
   const int p = q_pos[row];
   const int32_t* kr = kept + row * (long long)n_keep;
   int32_t* out = idx + row * (long long)k;
+  // paged caches: the list holds pool rows (row / n_q is the row's sequence)
+  const int32_t* pt = pg.page_table != nullptr ? pg.page_table + (row / n_q) * pg.max_pages : nullptr;
+  const int pmask = (1 << pg.page_log2) - 1;
   int n = 0;
   for (int r = threadIdx.x; r < k; r += NT) {
     const int blk = r / bs < n_keep ? kr[r / bs] : -1;
     const int key = blk * bs + r % bs;
     const bool ok = blk >= 0 && key <= p;
-    out[r] = ok ? key : -1;
+    int v = ok ? key : -1;
+    if (ok && pt != nullptr) v = (min(max(pt[key >> pg.page_log2], 0), pg.n_pages - 1) << pg.page_log2) | (key & pmask);
+    out[r] = v;
     n += ok ? 1 : 0;
   }
   if (count != nullptr) {
@@ -1899,11 +1928,12 @@ __global__ __launch_bounds__(NT) void expand_kernel(const int32_t* __restrict__ 
 }
 
 hipError_t launch_expand(const int32_t* kept, const int32_t* q_pos, long long rows, int bs, int n_keep, int k,
-                         int32_t* idx, int32_t* count, hipStream_t st) {
+                         int32_t* idx, int32_t* count, hipStream_t st, const Pages& pg, int n_q) {
   if (rows == 0) return hipSuccess;
-  if (bs < 1 || n_keep < 1 || k < 1) return hipErrorInvalidValue;
+  if (bs < 1 || n_keep < 1 || k < 1 || n_q < 1) return hipErrorInvalidValue;
+  if (pg.page_table != nullptr && (pg.page_log2 < 6 || pg.page_log2 > 30 || pg.n_pages < 1)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(expand_kernel<256>, dim3((unsigned)rows), dim3(256), 0, st, kept, q_pos, bs, n_keep, k, idx,
-                     count);
+                     count, pg, n_q);
   return hipGetLastError();
 }
 
@@ -1913,6 +1943,10 @@ hipError_t launch_kept_select(const IdxArgs& a, int k, int32_t* idx, int32_t* co
   if (a.kept == nullptr || a.block_size < 1 || a.n_keep < 1 || a.n_keep > 256 ||
       (long long)a.n_keep * a.block_size > KSEL_SLOTS || k < 1 || (a.d_I != 64 && a.d_I != 128) || a.H_I < 1 ||
       a.H_I > 64)
+    return hipErrorInvalidValue;
+  if (a.pages.page_table != nullptr &&
+      (a.pages.page_log2 < 6 || a.pages.page_log2 > 30 || a.pages.n_pages < 1 ||
+       (long long)a.pages.max_pages << a.pages.page_log2 != a.L_max))
     return hipErrorInvalidValue;
   const int mt = (a.H_I + 15) / 16;
   if (a.d_I == 128) {

@@ -224,18 +224,20 @@ def paged_rows(page_table_row, n_keys: int, page_size: int) -> np.ndarray:
 
 
 def forward_row_paged(q_idx_row, k_idx_pool, w, p: int, k: int, page_table_row, page_size: int,
-                      q_row=None, k_pool=None, v_pool=None, scale: float | None = None):
-    """The flat path for one query row of a sequence whose caches are paged.
+                      q_row=None, k_pool=None, v_pool=None, scale: float | None = None, **modes):
+    """The path for one query row of a sequence whose caches are paged.
 
     The sequence's logical caches are the pool rows its page table names
-    (paged_rows); scores, top-k and attention are those of forward_row on them,
-    and J then names the pool rows of the chosen logical keys (ascending logical
-    order, -1 padded).  J_logical keeps the logical keys.
+    (paged_rows); blocks, scores, top-k and attention are those of forward_row on
+    them (``modes``: its two_stage / block_size / n_keep / pooled arguments, so blocks
+    are blocks of logical keys and kept holds logical block ids), and J then names
+    the pool rows of the chosen logical keys (ascending logical order, -1 padded).
+    J_logical keeps the logical keys.
     """
     rows = paged_rows(page_table_row, len(page_table_row) * page_size, page_size)
     res = forward_row(q_idx_row, np.asarray(k_idx_pool)[rows], w, p, k, q_row=q_row,
                       k_cache=None if k_pool is None else np.asarray(k_pool)[rows],
-                      v_cache=None if v_pool is None else np.asarray(v_pool)[rows], scale=scale)
+                      v_cache=None if v_pool is None else np.asarray(v_pool)[rows], scale=scale, **modes)
     J = res["J"]
     res["J_logical"] = J
     res["J"] = np.where(J >= 0, rows[np.maximum(J, 0)], -1)

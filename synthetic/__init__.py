@@ -95,10 +95,18 @@ WORKLOADS = {
     "decode_128k_pool4": Workload("decode_128k_pool4", B=64, n_q=1, L=131073, q_pos0=131072,
                                   H_I=64, d_I=128, k=2048, H_q=16, two_stage=True, pooled=True,
                                   block_size=4, n_keep=512),
+    # decode_128k_pool4 over the page pool of decode_128k_paged
+    "decode_128k_pool4_paged": Workload("decode_128k_pool4_paged", B=64, n_q=1, L=131073, q_pos0=131072,
+                                        H_I=64, d_I=128, k=2048, H_q=16, two_stage=True, pooled=True,
+                                        block_size=4, n_keep=512, page_size=64, spare_pages=4096),
     # two-stage (block prefilter, then tokens) on the final 8192 queries of 128K
     "two_stage_128k": Workload("two_stage_128k", B=1, n_q=8192, L=131072, q_pos0=122880,
                                H_I=64, d_I=128, k=2048, H_q=16, two_stage=True,
                                block_size=128, n_keep=64),
+    # two_stage_128k with its caches in a pool of 64-token pages (1024 spare pages)
+    "two_stage_128k_paged": Workload("two_stage_128k_paged", B=1, n_q=8192, L=131072, q_pos0=122880,
+                                     H_I=64, d_I=128, k=2048, H_q=16, two_stage=True,
+                                     block_size=128, n_keep=64, page_size=64, spare_pages=1024),
     # flat semantic search (bucket cache of 512-key blocks, 64 buckets each): decode of 64
     # sequences at 128K, 2048 long-range keys from the best 512 buckets + 4 sinks + a
     # 512-key window

@@ -430,16 +430,25 @@ def _paged_case(rng, n_pages_seq, page_size, spare, d_I=16, d=8, H=4):
     return L, k_idx, kc, vc, perm, pool_k_idx, pool_kc, pool_vc, q_idx, w, q
 
 
+# the path's modes over paged caches: flat, two-stage (blocks of 4, 3 kept), pooled blocks
+PAGED_MODES = ({}, {"two_stage": True, "block_size": 4, "n_keep": 3},
+               {"two_stage": True, "block_size": 4, "n_keep": 3, "pooled": True})
+
+
 def check_paged_identity(impl, seed=10):
-    """An identity page table is the contiguous cache itself."""
+    """An identity page table is the contiguous cache itself (every mode of the path)."""
     rng = np.random.default_rng(seed)
     L, k_idx, kc, vc, _, _, _, _, q_idx, w, q = _paged_case(rng, 6, 8, 0)
     r = []
-    for p, k in ((L - 1, 12), (20, 30), (0, 4)):
-        a = impl.forward_row(q_idx, k_idx, w, p, k, q_row=q, k_cache=kc, v_cache=vc)
-        b = impl.forward_row_paged(q_idx, k_idx, w, p, k, np.arange(6), 8, q_row=q, k_pool=kc, v_pool=vc)
-        r.append(_ok(np.array_equal(a["J"], b["J"]) and np.array_equal(a["out"], b["out"])
-                     and np.array_equal(a["lse"], b["lse"]), f"identity pages p={p}"))
+    for modes in PAGED_MODES:
+        for p, k in ((L - 1, 12), (20, 30), (0, 4)):
+            if modes.get("pooled"):
+                k = modes["n_keep"] * modes["block_size"]
+            a = impl.forward_row(q_idx, k_idx, w, p, k, q_row=q, k_cache=kc, v_cache=vc, **modes)
+            b = impl.forward_row_paged(q_idx, k_idx, w, p, k, np.arange(6), 8, q_row=q, k_pool=kc, v_pool=vc,
+                                       **modes)
+            r.append(_ok(np.array_equal(a["J"], b["J"]) and np.array_equal(a["out"], b["out"])
+                         and np.array_equal(a["lse"], b["lse"]), f"identity pages p={p} {modes}"))
     return _all(r)
 
 
@@ -450,14 +459,21 @@ def check_paged_permutation(impl, seed=11):
     r = []
     for page_size, n_pages, spare in ((4, 9, 5), (16, 5, 3)):
         L, k_idx, kc, vc, perm, pk, pkc, pvc, q_idx, w, q = _paged_case(rng, n_pages, page_size, spare)
-        for p, k in ((L - 1, 10), (L // 2, 7), (3, 9)):
-            a = impl.forward_row(q_idx, k_idx, w, p, k, q_row=q, k_cache=kc, v_cache=vc)
-            b = impl.forward_row_paged(q_idx, pk, w, p, k, perm, page_size, q_row=q, k_pool=pkc, v_pool=pvc)
-            Ja = a["J"]
-            want = np.where(Ja >= 0, perm[np.maximum(Ja, 0) // page_size] * page_size + np.maximum(Ja, 0) % page_size, -1)
-            r.append(_ok(np.array_equal(b["J_logical"], Ja) and np.array_equal(b["J"], want)
-                         and np.array_equal(a["out"], b["out"]) and np.array_equal(a["lse"], b["lse"]),
-                         f"scattered pages P={page_size} p={p}"))
+        for modes in PAGED_MODES:
+            for p, k in ((L - 1, 10), (L // 2, 7), (3, 9)):
+                if modes.get("pooled"):
+                    k = modes["n_keep"] * modes["block_size"]
+                a = impl.forward_row(q_idx, k_idx, w, p, k, q_row=q, k_cache=kc, v_cache=vc, **modes)
+                b = impl.forward_row_paged(q_idx, pk, w, p, k, perm, page_size, q_row=q, k_pool=pkc, v_pool=pvc,
+                                           **modes)
+                Ja = a["J"]
+                want = np.where(Ja >= 0, perm[np.maximum(Ja, 0) // page_size] * page_size
+                                + np.maximum(Ja, 0) % page_size, -1)
+                ok = (np.array_equal(b["J_logical"], Ja) and np.array_equal(b["J"], want)
+                      and np.array_equal(a["out"], b["out"]) and np.array_equal(a["lse"], b["lse"]))
+                if "kept" in a:
+                    ok = ok and np.array_equal(a["kept"], b["kept"])
+                r.append(_ok(ok, f"scattered pages P={page_size} p={p} {modes}"))
     return _all(r)
 
 

@@ -633,6 +633,60 @@ def test_forward_prefill_paged(lsa, page_size):
         assert torch.equal(res["lse"], ref["lse"]), mode
 
 
+@pytest.mark.parametrize("mode,B,n_q,L,bs,nk,k,P", [
+    ("two_stage", 5, 1, 20480, 128, 64, 2048, 64),   # decode rows, the one-kernel token stage
+    ("two_stage", 2, 40, 9024, 128, 20, 600, 64),    # prefill rows; own blocks run past the last page
+    ("two_stage", 2, 30, 3072, 16, 6, 40, 64),       # blocks of 16: slots looked up one by one
+    ("pooled", 5, 1, 9216, 4, 512, 2048, 64),        # decode rows, 4:1 pooled keys
+    ("pooled", 2, 40, 3072, 4, 64, 256, 256),        # prefill rows
+])
+def test_forward_block_modes_paged(lsa, mode, B, n_q, L, bs, nk, k, P):
+    """Block modes over paged caches: the block-key cache built through the page table
+    equals the contiguous one; kept blocks, counts, outputs and LSE equal the
+    contiguous call's bit for bit and the lists are its lists mapped through the page
+    table (also with the caller's paged block-key cache); the oracle's paged definition
+    agrees on sampled rows."""
+    two = "pooled" if mode == "pooled" else True
+    wl = synthetic.Workload("pgblk", B=B, n_q=n_q, L=L, q_pos0=0, H_I=64, d_I=128, k=k, H_q=16)
+    if n_q == 1:
+        pos = [L - 1, L - 2, L // 2 + 3, 4 * nk * bs // 4 - 1, 3][:B]
+    else:
+        pos = np.sort(np.random.default_rng(17).integers(0, L, (B, n_q)), axis=1)
+        pos[:, 0], pos[:, 1], pos[:, -1] = 0, bs - 1, L - 1
+        pos = pos.reshape(-1).tolist()
+    inp, g = _inputs(wl, seed=41, pos=pos)
+    ref = lsa.lsa_forward(g, k_top=k, two_stage=two, block_size=bs, n_keep=nk, attn_split=1)
+    pg = synthetic.paged_pool(g, P, spare_pages=23, seed=9)
+    res = lsa.lsa_forward(pg, k_top=k, two_stage=two, block_size=bs, n_keep=nk, attn_split=1)
+    torch.cuda.synchronize()
+    assert torch.equal(res["kept"], ref["kept"])
+    assert torch.equal(res["idx"].long(), _map_pages(ref["idx"], pg["page_table"], P))
+    for name in ("count", "out", "lse"):
+        assert torch.equal(res[name], ref[name]), name
+    # the block-key cache through the page table, and the call that takes it
+    bk = lsa.lsa_block_cache(pg["k_idx"], bs, page_table=pg["page_table"], page_size=P)
+    assert torch.equal(bk[:, : L // bs], lsa.lsa_block_cache(g["k_idx"], bs))
+    res_c = lsa.lsa_forward(dict(pg, block_keys=bk), k_top=k, two_stage=two, block_size=bs, n_keep=nk, attn_split=1)
+    torch.cuda.synchronize()
+    for name in ("idx", "count", "kept", "out", "lse"):
+        assert torch.equal(res_c[name], res[name]), name
+    # the oracle over the pool itself
+    pt = pg["page_table"].cpu().numpy()
+    pki, pk, pv = pg["k_idx"].cpu().numpy(), np64(pg["k"].cpu()), np64(pg["v"].cpu())
+    qi, w, q = inp["q_idx"].numpy(), inp["w"].numpy(), np64(inp["q"])
+    J, kept, out = res["idx"].cpu().numpy(), res["kept"].cpu().numpy(), np64(res["out"])
+    err = AttnErr()
+    for b, i in [(0, 0), (B - 1, n_q - 1), (B // 2, n_q // 2)]:
+        p = int(inp["q_pos"][b, i])
+        r = oracle.forward_row_paged(qi[b, i], pki, w, p, k, pt[b], P, q_row=q[b, i], k_pool=pk, v_pool=pv,
+                                     scale=1.0 / math.sqrt(128), two_stage=True, block_size=bs, n_keep=nk,
+                                     pooled=mode == "pooled")
+        assert np.array_equal(kept[b, i], r["kept"]), (b, i)
+        assert np.array_equal(J[b, i], r["J"]), (b, i)
+        err.add(out[b, i], r["out"], (b, i))
+    err.check()
+
+
 def test_forward_decode_paged_graph_replay(lsa):
     """A paged decode step captured once in a HIP graph (one graph per range of context
     lengths: the page-table width fixes L_max and so every launch shape) replays for

@@ -83,6 +83,31 @@ def test_prefill_32k(lsa):
     _certificate_flat(lsa, wl, g, res, row_chunk=2048)
 
 
+def _pool_rows(J, page_table, P):
+    """Logical keys [B, n_q, k] (or -1) -> pool rows through page_table [B, max_pages]."""
+    J = J.long()
+    Jc = J.clamp(min=0)
+    rows = torch.gather(page_table.long(), 1, (Jc // P).reshape(J.shape[0], -1)).reshape(J.shape) * P + Jc % P
+    return torch.where(J >= 0, rows, torch.full_like(J, -1))
+
+
+def _paged_equal(lsa, name, g, res, **kw):
+    """The benchmark's paged variant of a workload (its caches scattered over a pool of
+    pages) gives the contiguous step bit for bit, the lists naming pool rows."""
+    wp = synthetic.WORKLOADS[name]
+    pg = synthetic.paged_pool(g, wp.page_size, wp.spare_pages, wp.seed)
+    if wp.pooled:
+        pg["block_keys"] = lsa.lsa_block_cache(pg["k_idx"], wp.block_size, page_table=pg["page_table"],
+                                               page_size=wp.page_size)
+    rp = lsa.lsa_forward(pg, k_top=wp.k, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(rp["idx"].long(), _pool_rows(res["idx"], pg["page_table"], wp.page_size))
+    for n in ("count", "out", "lse", "kept"):
+        if n in res:
+            assert torch.equal(rp[n], res[n]), n
+    print(f"[{name}] equal to the contiguous step", flush=True)
+
+
 def test_decode_128k(lsa):
     wl, g, res = _run(lsa, "decode_128k")
     _check_rows(wl, g, res, synthetic.checked_rows(wl, n_random=10))
@@ -150,6 +175,8 @@ def test_two_stage_128k(lsa):
     max_oth = torch.where(oth, packed_lo, torch.full_like(packed_lo, -big - 1)).max(1).values
     assert bool(((min_sel >= max_oth) | (oth.sum(1) == 0)).all())
     assert bool((sel.sum(1) == torch.clamp(own, max=nk - 1)).all())
+    del S, bsc, hits
+    _paged_equal(lsa, "two_stage_128k_paged", g, res, two_stage=True, block_size=bs, n_keep=nk)
 
 
 def test_decode_128k_pool4(lsa):
@@ -176,3 +203,6 @@ def test_decode_128k_pool4(lsa):
         assert int(res["count"][b, 0]) == r["count"]
         err.add(np64(res["out"][b, 0]), r["out"], b)
     err.check()
+    del g["block_keys"]
+    _paged_equal(lsa, "decode_128k_pool4_paged", g, res, two_stage="pooled", block_size=wl.block_size,
+                 n_keep=wl.n_keep)

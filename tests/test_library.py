@@ -180,7 +180,8 @@ def _fake_paged(B, n_q, max_pages, page_size, n_pages, H_I=64, d_I=128, H_q=16, 
 def test_forward_paged_arguments():
     """Paged caches (host checks only): decode calls plan the decode selection and
     prefill calls the flat stages; page sizes below 64 or not powers of two, and pools
-    not made of whole pages, are invalid; two-stage calls are unsupported."""
+    not made of whole pages, are invalid; block modes plan their stages, and a two-stage
+    call whose kept slots exceed the one-kernel token stage is unsupported."""
     import learned_top_sparse_amd as lsa
     from learned_top_sparse_amd.binding import LsaError
     inp = _fake_paged(64, 1, 2049, 64, 64 * 2049 + 100)
@@ -197,8 +198,15 @@ def test_forward_paged_arguments():
     pre = _fake_paged(1, 64, 512, 64, 600)   # 32768-key prefill rows: thresholded selection
     ws = lsa.lsa_forward_workspace_size(pre, 2048)
     assert lsa.lsa_forward_stages(pre, 2048, ws) == ["sample", "index_select", "topk", "sparse_attn"]
+    two = _fake_paged(4, 1, 16, 64, 80)
+    ws = lsa.lsa_forward_workspace_size(two, 256, two_stage=True)
+    assert lsa.lsa_forward_stages(two, 256, ws, two_stage=True) == [
+        "block_reps", "block_prefilter", "index_select", "sparse_attn"]
+    ws = lsa.lsa_forward_workspace_size(two, 256, two_stage="pooled", block_size=4, n_keep=64)
+    assert lsa.lsa_forward_stages(two, 256, ws, two_stage="pooled", block_size=4, n_keep=64) == [
+        "block_reps", "block_prefilter", "expand", "sparse_attn"]
     with pytest.raises(LsaError, match="UNSUPPORTED"):
-        lsa.lsa_forward_workspace_size(_fake_paged(4, 1, 16, 64, 80), 256, two_stage=True)
+        lsa.lsa_forward_workspace_size(two, 256, two_stage=True, n_keep=100)
 
 
 def test_forward_rejects_too_few_stage_events():
