@@ -735,6 +735,26 @@ def main():
     del inp, step
     torch.cuda.empty_cache()
 
+    # ---- the pooled (4:1) indexer on the prefill configurations (block-key cache resident)
+    for name in ("prefill_32k_pool4", "chunk_256k_pool4"):
+        wx = synthetic.WORKLOADS[name]
+        inp, step, ms_x = measure(lsa, torch, wx, args.steps if wx.L <= 32768 else max(1, args.steps // 5),
+                                  args.warmup)
+        kx = step.kernel_ms()
+        ax = algorithmic(wx)
+        ach = ax["block_ops"] / (kx["block_prefilter"]["ms_per_step"] * 1e-3) / 1e12
+        res[name] = {
+            "workload": _describe(wx), "value": wx.B * wx.n_q / (ms_x * 1e-3), "unit": "queries/s",
+            "ms_per_step": ms_x, "kernel_ms": kx, "t_roof_ms": t_roof_ms(wx),
+            "step_roofline_frac": t_roof_ms(wx) / ms_x,
+            "roofline": {"bound": "mfma", "kernel": "block_prefilter (blk_scores_kernel + blk_select_kernel)",
+                         "achieved": ach, "peak": INT8_PEAK_TOPS, "unit": "TOP/s", "frac": ach / INT8_PEAK_TOPS,
+                         "frac_of_measured_peak": ach / peaks["int8_mfma_TOPs"] if peaks else None,
+                         "ops": "pooled-key scores, two int8 parts per block key"},
+        }
+        del inp, step
+        torch.cuda.empty_cache()
+
     # ---- the block modes over paged caches (pools of 64-token pages, seeded page order)
     for name, unit in (("decode_128k_pool4_paged", "tok/s"), ("two_stage_128k_paged", "queries/s")):
         wx = synthetic.WORKLOADS[name]

@@ -99,6 +99,14 @@ WORKLOADS = {
     "decode_128k_pool4_paged": Workload("decode_128k_pool4_paged", B=64, n_q=1, L=131073, q_pos0=131072,
                                         H_I=64, d_I=128, k=2048, H_q=16, two_stage=True, pooled=True,
                                         block_size=4, n_keep=512, page_size=64, spare_pages=4096),
+    # the 32K prefill and the 256K chunk with the 4:1 pooled indexer (the best 512 blocks
+    # of 4 keys, own block included, give the 2048-key list)
+    "prefill_32k_pool4": Workload("prefill_32k_pool4", B=1, n_q=32768, L=32768, q_pos0=0,
+                                  H_I=64, d_I=128, k=2048, H_q=16, two_stage=True, pooled=True,
+                                  block_size=4, n_keep=512),
+    "chunk_256k_pool4": Workload("chunk_256k_pool4", B=1, n_q=16384, L=262144, q_pos0=245760,
+                                 H_I=64, d_I=128, k=2048, H_q=16, two_stage=True, pooled=True,
+                                 block_size=4, n_keep=512),
     # two-stage (block prefilter, then tokens) on the final 8192 queries of 128K
     "two_stage_128k": Workload("two_stage_128k", B=1, n_q=8192, L=131072, q_pos0=122880,
                                H_I=64, d_I=128, k=2048, H_q=16, two_stage=True,

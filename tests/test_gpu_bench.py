@@ -29,7 +29,7 @@ def test_bench_headline_line():
     assert r["bound"] in ("hbm", "mfma", "alu") and 0 < r["frac"] < 1.5 and r["peak"] > 0
     for wl in ("decode_128k_paged", "decode_128k_pool4", "prefill_128k", "decode_128k_lsa", "decode_128k_lsa_paged",
                "prefill_128k_lsa", "tiny_prefill_1k", "prefill_32k", "chunk_256k", "decode_128k_pool4_paged",
-               "two_stage_128k_paged"):
+               "two_stage_128k_paged", "prefill_32k_pool4", "chunk_256k_pool4"):
         assert d[wl]["ms_per_step"] > 0 and d[wl]["kernel_ms"], wl
     assert 0 < d["prefill_128k"]["roofline"]["frac"] < 1.5
     for wl in ("prefill_32k", "chunk_256k"):

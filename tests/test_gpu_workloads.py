@@ -179,6 +179,36 @@ def test_two_stage_128k(lsa):
     _paged_equal(lsa, "two_stage_128k_paged", g, res, two_stage=True, block_size=bs, n_keep=nk)
 
 
+@pytest.mark.parametrize("name", ["prefill_32k_pool4", "chunk_256k_pool4"])
+def test_prefill_pool4(lsa, name):
+    """The pooled (4:1) indexer on the prefill workloads at full size, with the block-key
+    cache built beforehand as the benchmark does: seeded sampled rows (boundary rows
+    included) against the oracle -- lists, kept blocks and counts exact, attention within
+    tolerance."""
+    wl = synthetic.WORKLOADS[name]
+    g = synthetic.make_inputs(wl, dev())
+    g["block_keys"] = lsa.lsa_block_cache(g["k_idx"], wl.block_size)
+    t0 = time.time()
+    res = lsa.lsa_forward(g, k_top=wl.k, two_stage="pooled", block_size=wl.block_size, n_keep=wl.n_keep)
+    torch.cuda.synchronize()
+    print(f"[{wl.name}] forward {time.time() - t0:.3f}s", flush=True)
+    w = g["w"].cpu().numpy()
+    ki = g["k_idx"][0].cpu().numpy()
+    kc, vc = np64(g["k"][0].cpu()), np64(g["v"][0].cpu())
+    reps = oracle.block_reps(ki, wl.block_size)
+    err = AttnErr()
+    for b, i in synthetic.checked_rows(wl, n_random=12):
+        p = int(g["q_pos"][b, i])
+        r = oracle.forward_row(g["q_idx"][b, i].cpu().numpy(), ki, w, p, wl.k, q_row=np64(g["q"][b, i]),
+                               k_cache=kc, v_cache=vc, scale=wl.scale, two_stage=True, block_size=wl.block_size,
+                               n_keep=wl.n_keep, pooled=True, reps=reps)
+        assert np.array_equal(res["kept"][b, i].cpu().numpy(), r["kept"]), f"kept {(b, i)}"
+        assert np.array_equal(res["idx"][b, i].cpu().numpy(), r["J"]), f"row {(b, i)}"
+        assert int(res["count"][b, i]) == r["count"]
+        err.add(np64(res["out"][b, i]), r["out"], (b, i))
+    err.check()
+
+
 def test_decode_128k_pool4(lsa):
     """The pooled (4:1) decode workload at full size, with the block-key cache built
     beforehand as the benchmark does: sampled rows against the oracle (lists, kept
