@@ -12,53 +12,19 @@ from typing import Optional
 
 import torch
 
+from .abi import EXPORTED, I32, I64, NOALLOC_SCRATCH_BYTES, P, SZ, ForwardArgs, SemanticPages, SemanticParams, declare
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
-# every symbol include/lsa.h declares
-EXPORTED = [
-    "lsa_status_string", "lsa_version", "lsa_index_scores", "lsa_block_reps", "lsa_block_cache",
-    "lsa_block_prefilter_workspace_size", "lsa_block_prefilter", "lsa_topk_workspace_size",
-    "lsa_topk", "lsa_sparse_attn_workspace_size", "lsa_sparse_attn",
-    "lsa_forward_workspace_size", "lsa_forward", "lsa_forward_plan", "lsa_forward_stages",
-    "lsa_semantic_cluster", "lsa_semantic_select_workspace_size", "lsa_semantic_select",
-    "lsa_semantic_cluster_paged", "lsa_semantic_select_paged", "lsa_sparse_attn_pool", "lsa_semantic_select_timed",
-    "lsa_forward_noalloc", "lsa_block_cache_paged",
-    "lsa_peak_sink_ints", "lsa_peak_mfma", "lsa_peak_read", "lsa_peak_gather",
-]
-
-# size of the device array lsa_forward_noalloc works in (LSA_NOALLOC_SCRATCH_BYTES)
-NOALLOC_SCRATCH_BYTES = 128 << 20
-
 STAGE_NAMES = {1: "block_reps", 2: "block_prefilter", 3: "index_select", 4: "index_scores", 5: "topk", 7: "sample",
                6: "sparse_attn", 8: "expand"}
-
-P = C.c_void_p
-I32 = C.c_int32
-I64 = C.c_int64
-SZ = C.c_size_t
 
 
 class LsaError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn} failed: {status} ({lsa_status_string(status)})")
         self.status = status
-
-
-class ForwardArgs(C.Structure):
-    _fields_ = [
-        ("mode", I32), ("two_stage", I32),
-        ("q_idx", P), ("k_idx", P), ("w", P), ("w_per_query", I32),
-        ("q_pos", P), ("q", P), ("k", P), ("v", P),
-        ("B", I32), ("n_q", I32), ("L_max", I32), ("H_I", I32), ("d_I", I32), ("H_q", I32),
-        ("d", I32), ("k_top", I32), ("block_size", I32), ("n_keep", I32),
-        ("scale", C.c_float), ("attn_split", I32), ("chunk_rows", I64),
-        ("idx", P), ("count", P), ("out", P), ("lse", P), ("kept_blocks", P),
-        ("stage_events", P), ("n_stage_events", I32),
-        ("select_mode", I32),
-        ("page_table", P), ("page_size", I32), ("max_pages", I32), ("n_slots", I64),
-        ("block_keys", P),
-    ]
 
 
 def lib_path() -> str:
@@ -74,43 +40,7 @@ def lib():
             raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
                                "(hipcc --offload-arch=gfx950); there is no fallback path")
         L = C.CDLL(path)
-        L.lsa_status_string.restype = C.c_char_p
-        L.lsa_status_string.argtypes = [C.c_int]
-        L.lsa_version.restype = C.c_int
-        L.lsa_version.argtypes = []
-        L.lsa_index_scores.argtypes = [P, P, P, I32, P, P, I32, I32, I32, I32, I32, I32, I32, P, I64, P]
-        L.lsa_block_reps.argtypes = [P, I32, I32, I32, I32, I32, P, P]
-        L.lsa_block_cache.argtypes = [P, I32, I32, I32, I32, I32, I32, I32, P, P]
-        L.lsa_block_cache_paged.argtypes = [P, I64, P, I32, I32, I32, I32, I32, I32, I32, I32, P, P]
-        L.lsa_block_prefilter_workspace_size.argtypes = [I32, I32, I32, I32, C.POINTER(SZ)]
-        L.lsa_block_prefilter.argtypes = [P, P, P, I32, P, I32, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
-        L.lsa_topk_workspace_size.argtypes = [I32, I32, I32, I32, C.POINTER(SZ)]
-        L.lsa_topk.argtypes = [P, I64, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
-        L.lsa_sparse_attn_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, C.POINTER(SZ)]
-        L.lsa_sparse_attn.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, C.c_float, I32, P, P, P, SZ, P]
-        L.lsa_sparse_attn_pool.argtypes = [P, P, P, P, I32, I32, I64, I32, I32, I32, C.c_float, I32, P, P, P, SZ, P]
-        L.lsa_forward_workspace_size.argtypes = [C.POINTER(ForwardArgs), C.POINTER(SZ)]
-        L.lsa_forward.argtypes = [C.POINTER(ForwardArgs), P, SZ, P]
-        L.lsa_forward_noalloc.argtypes = [C.POINTER(ForwardArgs), P]
-        L.lsa_peak_sink_ints.argtypes = [I32]
-        L.lsa_peak_mfma.argtypes = [I32, I64, I32, P, P]
-        L.lsa_peak_read.argtypes = [P, I64, I32, P, P]
-        L.lsa_peak_gather.argtypes = [P, I64, P, I64, I32, P, P]
-        L.lsa_forward_plan.argtypes = [C.POINTER(ForwardArgs), SZ, C.POINTER(I64), C.POINTER(I32)]
-        L.lsa_forward_stages.argtypes = [C.POINTER(ForwardArgs), SZ, C.POINTER(I32), I32, C.POINTER(I32)]
-        SP = C.POINTER(SemanticParams)
-        L.lsa_semantic_cluster.argtypes = [P, I32, I32, I32, SP, I32, I32, I32, P, P, P, P]
-        L.lsa_semantic_select_workspace_size.argtypes = [I32, I32, I32, SP, C.POINTER(SZ)]
-        L.lsa_semantic_select.argtypes = [P, P, I32, I32, I32, SP, I32, P, P, P, I32, I32, I32, I32, P, P, P, SZ, P]
-        L.lsa_semantic_select_timed.argtypes = [P, P, I32, I32, I32, SP, I32, P, P, P, I32, I32, I32, I32, P, P, P,
-                                                 SZ, P, C.POINTER(P)]
-        SG = C.POINTER(SemanticPages)
-        L.lsa_semantic_cluster_paged.argtypes = [P, I32, I32, I32, SP, SG, I32, I32, I32, P, P, P, P]
-        L.lsa_semantic_select_paged.argtypes = [P, P, I32, I32, I32, SP, SG, I32, I32, P, P, P, I32, I32, I32, I32,
-                                                 P, P, P, SZ, P]
-        for name in EXPORTED:
-            if name not in ("lsa_status_string", "lsa_version"):
-                getattr(L, name).restype = C.c_int
+        declare(L)
         _LIB = L
     return _LIB
 
@@ -453,17 +383,6 @@ def lsa_forward_noalloc(inp: dict, k_top: int, two_stage=False, block_size: int 
 
 
 # --------------------------------------------------------------------------- flat semantic search
-class SemanticParams(C.Structure):
-    """lsa_semantic_params of include/lsa.h."""
-    _fields_ = [("n_cluster", I32), ("n_pool", I32), ("n_bavg", I32), ("n_bmax", I32)]
-
-
-class SemanticPages(C.Structure):
-    """lsa_semantic_pages of include/lsa.h."""
-    _fields_ = [("block_table", P), ("n_bslots", I32), ("page_table", P), ("page_size", I32),
-                ("max_pages", I32), ("n_slots", I64)]
-
-
 def _sem_pages(paged: Optional[dict], cache: dict, n_slots: int = 0):
     """SemanticPages from ``paged`` = dict(block_table=int32 [B, NB] or None,
     page_table=int32 [B, max_pages] or None, page_size=int), and the logical L_max."""
