@@ -356,11 +356,38 @@ def _time_launches(torch, launch, reps=5, warm=2):
     return best
 
 
+RESIDENT_POOLS_MIB = (16, 64, 128)
+
+
+def resident_ceiling(peaks, wl):
+    """(GB/s, pool MiB): the measured cache-resident gather rate over the smallest pool
+    that holds the workload's K and V caches."""
+    kv_mib = wl.B * wl.L * 128 * 2 * 2 / (1 << 20)
+    fits = [m for m in RESIDENT_POOLS_MIB if m >= kv_mib] or [RESIDENT_POOLS_MIB[-1]]
+    return peaks["gather_resident_GBs"][str(fits[0])], fits[0]
+
+
+def attention_object(alg, at_ms, peaks, wl):
+    """Prefill attention: bf16 utilisation beside its gather rate and the measured
+    cache-resident gather ceiling for a pool of its K+V size."""
+    gb = alg["attn_gather_bytes"] / (at_ms * 1e-3) / 1e9
+    tf = alg["attn_flops"] / (at_ms * 1e-3) / 1e12
+    obj = {"bf16_TFLOPs": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS, "gather_GBs": gb,
+           "gather_bytes": alg["attn_gather_bytes"]}
+    if peaks:
+        ceil, mib = resident_ceiling(peaks, wl)
+        obj.update({"resident_pool_MiB": mib, "frac_of_measured_resident_gather": gb / ceil,
+                    "frac_of_measured_l2_gather": gb / peaks["gather_l2_GBs"]})
+    return obj
+
+
 def measure_peaks(lsa, torch):
     """The machine's reachable ceilings (lsa_peak_* microbenchmarks): int8 and bf16 MFMA
     issue, HBM streaming read over 2 GiB, random 256-byte row gathers over a 2 GiB pool
-    after a 1 GiB read that evicts the caches (cold) and over a 64 MiB pool read just
-    before (cache-resident).  Best of 5 launches each."""
+    after a 1 GiB read that evicts the caches (cold: the decode step's 67 MB, one
+    launch timed with events like the step's stages), and steady-state gathers of 4.3 GB
+    from a 64 MiB pool (Infinity Cache resident) and from a 2 MiB pool (L2 resident).
+    Best of 5 launches each."""
     import ctypes as C
     L = lsa.lib()
     dev = torch.device("cuda:0")
@@ -390,36 +417,47 @@ def measure_peaks(lsa, torch):
     res["hbm_read_GBs"] = big.numel() / (ms * 1e-3) / 1e9
     n_idx = 1 << 18  # 67 MB of 256-byte rows, the decode step's gather volume
     g = torch.Generator(device=dev).manual_seed(0)
-    nbg = 4 * n_cu
+    nbg = 8 * n_cu  # many waves with few rows in flight each: the fastest launch shape for random rows
+    sk = sink_for(max(nb, nbg))
 
-    def gather_ms(pool, n_rows, evict):
-        idx = torch.randint(0, n_rows, (n_idx,), dtype=torch.int32, device=dev, generator=g)
+    def gather_ms(pool, n_rows, evict, n):
+        idx = torch.randint(0, n_rows, (n,), dtype=torch.int32, device=dev, generator=g)
         best = float("inf")
         for _ in range(5):
             if evict:
                 check(L.lsa_peak_read(C.c_void_p(flush.data_ptr()), flush.numel(), nb, C.c_void_p(sk.data_ptr()), st),
                       "lsa_peak_read")
             else:
-                check(L.lsa_peak_gather(C.c_void_p(pool.data_ptr()), n_rows, C.c_void_p(idx.data_ptr()), n_idx, nbg,
+                check(L.lsa_peak_gather(C.c_void_p(pool.data_ptr()), n_rows, C.c_void_p(idx.data_ptr()), n, nbg,
                                         C.c_void_p(sk.data_ptr()), st), "lsa_peak_gather")
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            check(L.lsa_peak_gather(C.c_void_p(pool.data_ptr()), n_rows, C.c_void_p(idx.data_ptr()), n_idx, nbg,
+            check(L.lsa_peak_gather(C.c_void_p(pool.data_ptr()), n_rows, C.c_void_p(idx.data_ptr()), n, nbg,
                                     C.c_void_p(sk.data_ptr()), st), "lsa_peak_gather")
             b.record()
             b.synchronize()
             best = min(best, a.elapsed_time(b))
+        del idx
         return best
 
-    res["gather_cold_GBs"] = n_idx * 256 / (gather_ms(big, big.numel() // 256, True) * 1e-3) / 1e9
-    warm = big[: 64 << 20]
-    res["gather_warm_GBs"] = n_idx * 256 / (gather_ms(warm, warm.numel() // 256, False) * 1e-3) / 1e9
+    res["gather_cold_GBs"] = n_idx * 256 / (gather_ms(big, big.numel() // 256, True, n_idx) * 1e-3) / 1e9
+    n_steady = 1 << 24  # 4.3 GB of rows: long enough that launch and ramp do not count
+    # cache-resident pools the size of the prefill workloads' K and V caches (the share
+    # an XCD's L2 holds decides the rate); gather_warm_GBs is the 64 MiB one
+    res["gather_resident_GBs"] = {}
+    for mib in RESIDENT_POOLS_MIB:
+        pool = big[: mib << 20]
+        res["gather_resident_GBs"][str(mib)] = (n_steady * 256 / (gather_ms(pool, pool.numel() // 256, False, n_steady)
+                                                                  * 1e-3) / 1e9)
+    res["gather_warm_GBs"] = res["gather_resident_GBs"]["64"]
     l2 = big[: 2 << 20]
-    res["gather_l2_GBs"] = n_idx * 256 / (gather_ms(l2, l2.numel() // 256, False) * 1e-3) / 1e9
+    res["gather_l2_GBs"] = n_steady * 256 / (gather_ms(l2, l2.numel() // 256, False, n_steady) * 1e-3) / 1e9
     res["method"] = ("lsa_peak_* kernels (include/lsa_peaks.h): MFMA loops of 4 independent chains per wave over "
-                     f"{8 * n_cu} workgroups of 4 waves; 2 GiB streaming read; {n_idx} random 256-byte rows from a "
-                     "2 GiB pool after a 1 GiB read (cold), from a 64 MiB pool (Infinity Cache resident) and from a "
-                     "2 MiB pool (L2 resident), the warm pools read just before; best of 5")
+                     f"{8 * n_cu} workgroups of 4 waves; 2 GiB streaming read; random 256-byte rows over {nbg} "
+                     f"workgroups: {n_idx} rows from a 2 GiB pool after a 1 GiB read (cold, the decode step's volume), "
+                     f"{n_steady} rows from pools of {', '.join(str(m) for m in RESIDENT_POOLS_MIB)} MiB (the "
+                     "prefill workloads' K+V sizes, Infinity Cache resident) and from a 2 MiB pool (L2 resident), "
+                     "the warm pools read just before; best of 5")
     del big, flush
     torch.cuda.empty_cache()
     return res
@@ -572,13 +610,7 @@ def prefill_object(lsa, torch, name, steps, warmup, peaks, with_cpu):
                            "achieved": ach, "peak": INT8_PEAK_TOPS, "unit": "TOP/s", "frac": ach / INT8_PEAK_TOPS,
                            "frac_of_measured_peak": ach / peaks["int8_mfma_TOPs"] if peaks else None,
                            "algorithmic_ops_per_step": alg["index_ops"], "launch_ms_per_step": scan_ms}
-    at_ms = km["sparse_attn"]["ms_per_step"]
-    gb = alg["attn_gather_bytes"] / (at_ms * 1e-3) / 1e9
-    tf = alg["attn_flops"] / (at_ms * 1e-3) / 1e12
-    obj["attention"] = {"bf16_TFLOPs": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS, "gather_GBs": gb,
-                        "frac_of_measured_warm_gather": gb / peaks["gather_warm_GBs"] if peaks else None,
-                        "frac_of_measured_l2_gather": gb / peaks["gather_l2_GBs"] if peaks else None,
-                        "gather_bytes": alg["attn_gather_bytes"]}
+    obj["attention"] = attention_object(alg, km["sparse_attn"]["ms_per_step"], peaks, wl)
     if with_cpu:
         obj["cpu_baseline"] = cpu_baseline(wl, inp)
     del inp, step
@@ -787,15 +819,7 @@ def main():
         },
         "t_roof_ms": t_roof_ms(wp),
         "step_roofline_frac": t_roof_ms(wp) / ms_p,
-        "attention": {
-            "bf16_TFLOPs": ap_["attn_flops"] / (at_p * 1e-3) / 1e12,
-            "frac_bf16_peak": ap_["attn_flops"] / (at_p * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "gather_GBs": ap_["attn_gather_bytes"] / (at_p * 1e-3) / 1e9,
-            "frac_of_measured_warm_gather": (ap_["attn_gather_bytes"] / (at_p * 1e-3) / 1e9
-                                             / peaks["gather_warm_GBs"]) if peaks else None,
-            "frac_of_measured_l2_gather": (ap_["attn_gather_bytes"] / (at_p * 1e-3) / 1e9
-                                           / peaks["gather_l2_GBs"]) if peaks else None,
-        },
+        "attention": attention_object(ap_, at_p, peaks, wp),
     }
     if not args.no_cpu_baseline:
         res["prefill_128k"]["cpu_baseline"] = cpu_baseline(wp, inp, budget_s=10.0)

@@ -28,16 +28,17 @@ inline int flat_span(int32_t L_max, bool direct) {
   return L_max > 65536 ? 8192 : 4096;
 }
 
-// automatic split count of the sparse attention: with few rows, cut each list so the
-// launch holds about 1024 waves (one per SIMD; each wave pipelines its tiles, so
-// more, shorter waves only add merge work), at least one 32-key tile per wave
+// automatic split count of the sparse attention.  Rows enough to give every CU a
+// workgroup (256 and up) are not split: each wave pipelines its tiles.  Fewer rows
+// are cut into splits of at most 8 32-key tiles -- one tile per wave in the one-tile
+// form, two such workgroups per CU -- and into at least 256 units, so every CU holds
+// a workgroup.
 inline int attn_split_auto(long long rows, int32_t k_top) {
-  constexpr long long kWaves = 1024;
+  constexpr long long kUnits = 256;
   const long long n_tiles = (k_top + 31) / 32;
-  const long long max_split = std::max<long long>(1, n_tiles / lsa::ATTN_WAVES);
-  if (rows * lsa::ATTN_WAVES >= kWaves) return 1;
-  const long long s = (kWaves + rows * lsa::ATTN_WAVES - 1) / (rows * lsa::ATTN_WAVES);
-  return (int)std::max<long long>(1, std::min<long long>(s, max_split));
+  if (rows >= kUnits) return 1;
+  const long long s = std::max((n_tiles + 7) / 8, (kUnits + rows - 1) / std::max<long long>(rows, 1));
+  return (int)std::max<long long>(1, std::min<long long>(s, std::min<long long>(n_tiles, 64)));
 }
 
 lsa_status check_index_args(const int8_t* q_idx, const int8_t* k_idx, const int32_t* w, const int32_t* q_pos,

@@ -7,7 +7,7 @@
 // no key.  The split form (J_i cut into n_split parts merged by log-sum-exp) is
 // the split-KV decode kernel the same appendix mentions.
 //
-// One wave per (query row, split).  Per tile of 32 listed keys:
+// Per tile of 32 listed keys, in one wave:
 //   * the 32 K rows are gathered straight into MFMA A fragments and multiplied by
 //     the query's heads (B fragments, loaded once): S^T[key][head] = K Q^T with
 //     v_mfma_f32_16x16x32_bf16 -- lane l then owns head (l & 15);
@@ -77,8 +77,17 @@ constexpr int WAVE_LDS = D * RSD;  // dwords of LDS per wave: the transposed V t
 // dealt to the waves round-robin, each wave keeps an online-softmax state for the 16
 // heads, and at the end the NW states are merged through LDS.  n_split == 1 writes
 // the bf16 output and LSE; otherwise a normalised fp32 partial and its LSE go to ws.
-template <int NW>
-__global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
+//
+// Two forms.  PIPE: a wave walks many tiles with the next tile's gathers in flight
+// (two register sets; rows of many queries, where the grid alone fills the chip).
+// !PIPE: a wave takes at most one tile (the launch keeps the split's tiles <= NW), so
+// the code is straight-line, O is born after the gathers and 16 waves fit on a CU
+// (128 VGPRs) -- the split-KV decode form.  Random 256-byte row gathers reach a
+// higher rate from many waves with few loads in flight each than from few waves with
+// many: a wave's loads return in order, so one slow row holds back every later load
+// of that wave.
+template <int NW, bool PIPE>
+__global__ __launch_bounds__(64 * NW, PIPE ? 2 : 16 / NW) void sparse_attn_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ idx, int n_q, long long kv_rows, long long j_lim, int H_q, int k_top,
     float scale_log2, int n_split, __bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws) {
@@ -96,17 +105,16 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
   const __bf16* vb = v + (long long)b * kv_rows * D;
   u32* vt = lds + wave * WAVE_LDS;
 
-  // query heads as B fragments: lane (h = l&15, g) holds d = 32s + 8g .. +8 at step s
+  // query heads as B fragments: lane (h = l&15, g) holds d = 32s + 8g .. +8 at step s.
+  // Lanes of heads past H_q repeat head 0 (their results are never stored).  Loaded
+  // after the first index entries and used as loaded: a wave's loads complete in
+  // order, so the first gathers (which wait for the entries) do not wait for the query.
   Frag8 Qb[4];
-  {
-    const bool hv = r16 < H_q;
-    const __bf16* qr = q + (row * H_q + (hv ? r16 : 0)) * D + 8 * g;
+  auto load_q = [&]() {
+    const __bf16* qr = q + (row * H_q + (r16 < H_q ? r16 : 0)) * D + 8 * g;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (hv) Qb[s].u = *(const v4u*)(qr + 32 * s);
-      else Qb[s].u = v4u{0u, 0u, 0u, 0u};
-    }
-  }
+    for (int s = 0; s < 4; ++s) Qb[s].u = *(const v4u*)(qr + 32 * s);
+  };
 
   v4f O[8];
 #pragma unroll
@@ -122,8 +130,9 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
 
   // Software pipeline over the wave's tiles: index entries two tiles ahead, K/V
   // gathers one tile ahead, ping-pong register sets (no copies).  Every load is
-  // unconditional -- tiles past the wave's last one re-read that tile and are not
-  // computed -- so the compiler's wait counts stay exact.
+  // unconditional, so the compiler's wait counts stay exact: a tile past the wave's
+  // last one lists no key, so its gather reads one row (a single 64-byte piece per
+  // load instruction), and it is not computed.
   struct Idx {
     int jA, jB, j0, j1;
   };
@@ -131,10 +140,12 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     Frag8 Ka[2][4];
     v4u V0[4], V1[4];
     unsigned long long vA, vB;
+    bool v0ok, v1ok;
   };
   auto load_idx = [&](int i) -> Idx {
     const int base = (first + NW * min(i, n_my - 1)) * KT;
-    auto e = [&](int pos) -> int { return jrow[min(pos, k_top - 1)] | (pos < k_top ? 0 : -1); };
+    const int none = i < n_my ? 0 : -1;
+    auto e = [&](int pos) -> int { return jrow[min(pos, k_top - 1)] | (pos < k_top ? none : -1); };
     return Idx{e(base + r16), e(base + 16 + r16), e(base + 2 * r16), e(base + 2 * r16 + 1)};
   };
   auto gather = [&](Idx x, Gat& G) {
@@ -142,16 +153,19 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     G.vA = __ballot(ok(x.jA));
     G.vB = __ballot(ok(x.jB));
     // Entries without a key read the rows of a listed key of this tile instead (row 0
-    // if none is listed; the tile is then skipped): its score is masked to -inf, so
-    // its weight is exactly 0 and the borrowed V row (finite, or listed anyway) adds
-    // nothing.
+    // if none is listed): the score is masked to -inf and its weight set to exactly 0,
+    // and the borrowed V row is replaced by zeros, so it adds nothing whatever it
+    // holds.  No tile is skipped: a branch on the entries would let the compiler
+    // move the tile's other loads behind the wait for them.
     int jfill = 0;
     if (G.vA | G.vB) {
       const int src = G.vA ? __ffsll((long long)G.vA) - 1 : __ffsll((long long)G.vB) - 1;
       jfill = G.vA ? __shfl(x.jA, src) : __shfl(x.jB, src);
     }
     const int jA = ok(x.jA) ? x.jA : jfill, jB = ok(x.jB) ? x.jB : jfill;
-    const int j0 = ok(x.j0) ? x.j0 : jfill, j1 = ok(x.j1) ? x.j1 : jfill;
+    G.v0ok = ok(x.j0);
+    G.v1ok = ok(x.j1);
+    const int j0 = G.v0ok ? x.j0 : jfill, j1 = G.v1ok ? x.j1 : jfill;
     // every load instruction reads whole 64-byte pieces of 16 rows
     const __bf16* ra = kb + (long long)jA * D + 8 * g;
     const __bf16* rb = kb + (long long)jB * D + 8 * g;
@@ -169,7 +183,6 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     }
   };
   auto compute = [&](const Gat& G) {
-    if ((G.vA | G.vB) == 0ull) return;
     // S^T = K Q^T : lane holds keys 16*mt + 4g + i for head r16
     v4f S[2];
 #pragma unroll
@@ -185,7 +198,7 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
       for (int w2 = 0; w2 < 4; ++w2) {
-        const u32 a = G.V0[m][w2], c = G.V1[m][w2];
+        const u32 a = G.v0ok ? G.V0[m][w2] : 0u, c = G.v1ok ? G.V1[m][w2] : 0u;
         const int d = 8 * g + 32 * m + 2 * w2;
         vt[d * RSD + r16] = __builtin_amdgcn_perm(c, a, 0x05040100u);        // low halves
         vt[(d + 1) * RSD + r16] = __builtin_amdgcn_perm(c, a, 0x07060302u);  // high halves
@@ -223,7 +236,9 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pp = exp2f(sv[mt][i] - m_run);
+          // masked keys weigh exactly 0 (also while m_run is still -inf)
+          const bool okk = ((mt ? G.vB : G.vA) >> (4 * g + i)) & 1ull;
+          const float pp = okk ? exp2f(sv[mt][i] - m_run) : 0.f;
           pv[4 * mt + i] = pp;
           l_part += pp;
         }
@@ -244,19 +259,29 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
     }
   };
 
-  if (n_my > 0) {
-    Idx x0 = load_idx(0), x1 = load_idx(1);
-    Gat G0, G1;
-    gather(x0, G0);
-    x0 = load_idx(2);
-    for (int i = 0; i < n_my; i += 2) {
-      gather(x1, G1);  // tile i+1
-      x1 = load_idx(i + 3);
-      compute(G0);     // tile i
-      gather(x0, G0);  // tile i+2
-      x0 = load_idx(i + 4);
-      if (i + 1 < n_my) compute(G1);
+  if constexpr (PIPE) {
+    if (n_my > 0) {
+      Idx x0 = load_idx(0), x1 = load_idx(1);
+      load_q();
+      Gat G0, G1;
+      gather(x0, G0);
+      x0 = load_idx(2);
+      for (int i = 0; i < n_my; i += 2) {
+        gather(x1, G1);  // tile i+1
+        x1 = load_idx(i + 3);
+        compute(G0);     // tile i
+        gather(x0, G0);  // tile i+2
+        x0 = load_idx(i + 4);
+        if (i + 1 < n_my) compute(G1);
+      }
     }
+  } else if (n_my > 0) {
+    const Idx x = load_idx(0);
+    load_q();
+    __builtin_amdgcn_sched_barrier(0);  // all entries and the query in flight before the first wait
+    Gat G;
+    gather(x, G);
+    compute(G);
   }
 
   // ---- merge the NW wave states through LDS: region of wave w = O[16][OSTR] | m[16] | l[16]
@@ -312,45 +337,67 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_attn_kernel(
   }
 }
 
-// Merge of the n_split partial results of each row by log-sum-exp: one workgroup
-// per row, 8 outputs per thread, weights computed once per (split, head) in LDS.
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ ws, long long n_units,
-                                                          int n_split, int H_q, __bf16* __restrict__ out,
-                                                          float* __restrict__ lse) {
-  __shared__ float wgt[64 * 16];
-  __shared__ float Mh[16], inv_den[16];
-  const long long row = blockIdx.x;
-  const float* pl = ws + n_units * H_q * D + row * n_split * H_q;  // lse parts of this row [split][h]
-  const int tid = threadIdx.x;
-  if (tid < H_q) {
-    float M = -INFINITY;
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, pl[s * H_q + tid]);
-    float den = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      const float ls = pl[s * H_q + tid];
-      const float w = (M > -INFINITY && ls > -INFINITY) ? expf(ls - M) : 0.f;
-      wgt[s * 16 + tid] = w;
-      den += w;
-    }
-    Mh[tid] = M;
-    inv_den[tid] = den > 0.f ? 1.f / den : 0.f;
-    if (lse != nullptr) lse[row * H_q + tid] = den > 0.f ? M + logf(den) : -INFINITY;
-  }
-  __syncthreads();
+// Merge of the n_split partial results of each row by log-sum-exp.  The merge is a
+// handful of flops per loaded value, so its time is the latency of its loads: every
+// thread owns 4 outputs of one head and issues the loads of all its splits' partials
+// and LSEs before the first use (CS splits per batch of loads), and the grid spreads a
+// row over H_q * D / 1024 workgroups.  Per head: M = max_s lse_s, w_s = e^(lse_s - M),
+// out = (sum_s w_s x_s) / sum_s w_s, lse = M + log(sum_s w_s).
+constexpr int CMB_NT = 256;  // threads per combine workgroup (4 outputs each)
+constexpr int CMB_CS = 16;   // splits loaded per batch
+
+__global__ __launch_bounds__(CMB_NT) void attn_combine_kernel(const float* __restrict__ ws, long long n_units,
+                                                             int n_split, int H_q, __bf16* __restrict__ out,
+                                                             float* __restrict__ lse) {
   const int n_out = H_q * D;
-  for (int e0 = tid * 4; e0 < n_out; e0 += 256 * 4) {
-    const int h = e0 / D;
-    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < n_split; ++s) {
-      const v4f x = *(const v4f*)(ws + (row * n_split + s) * n_out + e0);
-      acc += x * wgt[s * 16 + h];
+  const int per_row = (n_out + 4 * CMB_NT - 1) / (4 * CMB_NT);
+  const long long row = blockIdx.x / per_row;
+  const int e0 = ((int)(blockIdx.x % per_row) * CMB_NT + (int)threadIdx.x) * 4;
+  if (e0 >= n_out) return;
+  const int h = e0 / D;
+  const float* pl = ws + n_units * n_out + row * n_split * H_q + h;  // lse part of split s: pl[s * H_q]
+  const float* px = ws + row * n_split * n_out + e0;                 // partial of split s: px[s * n_out]
+
+  float M = -INFINITY, den = 0.f;
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  auto load = [&](int s0, float (&ls)[CMB_CS], v4f (&x)[CMB_CS]) {
+#pragma unroll
+    for (int s = 0; s < CMB_CS; ++s) {
+      const bool in = s0 + s < n_split;
+      ls[s] = in ? pl[(s0 + s) * H_q] : -INFINITY;
+      x[s] = in ? *(const v4f*)(px + (long long)(s0 + s) * n_out) : v4f{0.f, 0.f, 0.f, 0.f};
     }
-    acc *= inv_den[h];
-    v2u pk;
-    pk[0] = pack_bf16(acc[0], acc[1]);
-    pk[1] = pack_bf16(acc[2], acc[3]);
-    *(v2u*)(out + row * n_out + e0) = pk;
+  };
+  auto accumulate = [&](const float (&ls)[CMB_CS], const v4f (&x)[CMB_CS]) {
+#pragma unroll
+    for (int s = 0; s < CMB_CS; ++s) {
+      const float w = (M > -INFINITY && ls[s] > -INFINITY) ? expf(ls[s] - M) : 0.f;
+      den += w;
+      acc += x[s] * w;
+    }
+  };
+  if (n_split <= CMB_CS) {  // one batch: M from the loaded LSEs
+    float ls[CMB_CS];
+    v4f x[CMB_CS];
+    load(0, ls, x);
+#pragma unroll
+    for (int s = 0; s < CMB_CS; ++s) M = fmaxf(M, ls[s]);
+    accumulate(ls, x);
+  } else {  // M over all splits first, then the batches
+    for (int s = 0; s < n_split; ++s) M = fmaxf(M, pl[s * H_q]);
+    for (int s0 = 0; s0 < n_split; s0 += CMB_CS) {
+      float ls[CMB_CS];
+      v4f x[CMB_CS];
+      load(s0, ls, x);
+      accumulate(ls, x);
+    }
   }
+  acc *= den > 0.f ? 1.f / den : 0.f;
+  v2u pk;
+  pk[0] = pack_bf16(acc[0], acc[1]);
+  pk[1] = pack_bf16(acc[2], acc[3]);
+  *(v2u*)(out + row * n_out + e0) = pk;
+  if (lse != nullptr && e0 % D == 0) lse[row * H_q + h] = den > 0.f ? M + logf(den) : -INFINITY;
 }
 
 }  // namespace
@@ -360,14 +407,26 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   if (a.n_split < 1 || a.n_split > 64) return hipErrorInvalidValue;  // the merges hold 64 splits
   const long long units = rows * a.n_split;
-  hipLaunchKernelGGL((sparse_attn_kernel<ATTN_WAVES>), dim3((unsigned)units), dim3(64 * ATTN_WAVES), 0, st,
-                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.idx, a.n_q,
-                     a.kv_pool > 0 ? 0ll : (long long)a.L_max, a.kv_pool > 0 ? a.kv_pool : (long long)a.L_max,
-                     a.H_q, a.k_top, a.scale * LOG2E, a.n_split, (__bf16*)a.out, a.lse, a.ws);
+  // one (row, split) unit per workgroup; split rows whose splits hold at most 16 tiles
+  // take the one-tile form with the fewest waves that give each wave one tile
+  const int tiles = (a.k_top + KT - 1) / KT;
+  const int per_split = (tiles + a.n_split - 1) / a.n_split;
+  const long long kv_rows = a.kv_pool > 0 ? 0ll : (long long)a.L_max;
+  const long long j_lim = a.kv_pool > 0 ? a.kv_pool : (long long)a.L_max;
+  auto go = [&](auto kern, int nw) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)units), dim3(64 * nw), 0, st, (const __bf16*)a.q, (const __bf16*)a.k,
+                       (const __bf16*)a.v, a.idx, a.n_q, kv_rows, j_lim, a.H_q, a.k_top, a.scale * LOG2E, a.n_split,
+                       (__bf16*)a.out, a.lse, a.ws);
+  };
+  if (a.n_split == 1 || per_split > 16) go(sparse_attn_kernel<ATTN_WAVES, true>, ATTN_WAVES);
+  else if (per_split <= 4) go(sparse_attn_kernel<4, false>, 4);
+  else if (per_split <= 8) go(sparse_attn_kernel<8, false>, 8);
+  else go(sparse_attn_kernel<16, false>, 16);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)rows), dim3(256), 0, st, a.ws, units, a.n_split, a.H_q,
-                     (__bf16*)a.out, a.lse);
+  const long long per_row = ((long long)a.H_q * D + 4 * CMB_NT - 1) / (4 * CMB_NT);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(rows * per_row)), dim3(CMB_NT), 0, st, a.ws, units,
+                     a.n_split, a.H_q, (__bf16*)a.out, a.lse);
   return hipGetLastError();
 }
 

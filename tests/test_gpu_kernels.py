@@ -310,6 +310,29 @@ def test_sparse_attn_random_lists(lsa, H, n_split):
     assert np.all(np64(out)[empty] == 0)
 
 
+@pytest.mark.parametrize("n_split", [1, 2, 3, 5, 12, 0])
+def test_sparse_attn_split_forms(lsa, n_split):
+    """Every launch form on one list length (35 tiles, the last one ragged): one unit per
+    row with pipelined waves (1), split units of more than 16 tiles, pipelined (2), and
+    the one-tile form with 16, 8 and 4 waves (3, 5, 12 splits), plus the automatic count."""
+    B, n_q, L, H, k = 3, 2, 5000, 16, 1100
+    q, k_, v = _attn_inputs(B, n_q, L, H, seed=40 + n_split)
+    rng = np.random.default_rng(n_split)
+    J = np.full((B, n_q, k), -1, np.int32)
+    for b in range(B):
+        for i in range(n_q):
+            n = k if (b + i) % 2 == 0 else int(rng.integers(1, k))
+            J[b, i, :n] = rng.choice(L, size=n, replace=False)
+    Jt = torch.from_numpy(J)
+    scale = 1 / math.sqrt(128)
+    out, lse = lsa.lsa_sparse_attn(q.to(dev()), k_.to(dev()), v.to(dev()), Jt.to(dev()), scale, n_split=n_split)
+    want, want_lse = _attn_oracle(q, k_, v, Jt, scale)
+    err = AttnErr()
+    err.add(np64(out), want)
+    err.check()
+    assert np.max(np.abs(lse.cpu().numpy() - want_lse)) < 1e-3
+
+
 def test_sparse_attn_degenerate_lists(lsa):
     B, n_q, L, H = 1, 6, 500, 16
     q, k, v = _attn_inputs(B, n_q, L, H, seed=1)
