@@ -365,6 +365,7 @@ struct FwdPlan {
   size_t fixed;         // workspace bytes independent of the chunk
   int64_t ld;           // score row stride
   int32_t n_blocks;
+  size_t il_bytes;      // the token stage's interleaved key copy (part of fixed), 0 = none
 };
 
 lsa_status check_forward(const lsa_forward_args* a) {
@@ -438,7 +439,17 @@ bool kept_fused(const lsa_forward_args* a) {
   return a->two_stage == 1 && a->n_keep <= 256 && (long long)a->n_keep * a->block_size <= lsa::KSEL_SLOTS;
 }
 
-FwdPlan plan_forward(const lsa_forward_args* a) {
+// The one-kernel token stage reads its keys from a chunk-interleaved copy, built at the
+// start of the call, where the copy pays: block sizes a multiple of 64 and at least 8
+// kept-key reads per cached key (many queries per sequence: prefill).
+bool kept_il(const lsa_forward_args* a) {
+  if (!kept_fused(a) || a->block_size % 64 != 0) return false;
+  const double reads = (double)a->B * a->n_q * a->n_keep * a->block_size;
+  return reads >= 8.0 * (double)a->B * a->L_max;
+}
+
+// with_il = false: the plan without the interleaved copy (a workspace too small for it)
+FwdPlan plan_forward(const lsa_forward_args* a, bool with_il = true) {
   FwdPlan p{};
   p.decode_like = a->n_q == 1;
   if (a->two_stage) {
@@ -448,6 +459,8 @@ FwdPlan plan_forward(const lsa_forward_args* a) {
     p.per_row = p.ld * 4 + (long long)p.n_blocks * 8 + (a->kept_blocks ? 0 : (long long)a->n_keep * 4) + 64;
     // the block-key cache, unless the caller keeps one
     p.fixed = a->block_keys ? 0 : align_up((size_t)a->B * p.n_blocks * 2 * a->d_I);
+    p.il_bytes = with_il && kept_il(a) ? align_up(lsa::kidx_interleave_bytes(a->B, a->L_max, a->d_I)) : 0;
+    p.fixed += p.il_bytes;
   } else {
     p.n_blocks = 0;
     p.ld = score_ld(a->L_max);
@@ -489,6 +502,20 @@ long long total_rows(const lsa_forward_args* a) { return a->n_q == 1 ? (long lon
 constexpr long long kChunkBudget = 8ll << 30;  // default chunk budget (bytes)
 
 // rows per chunk for a workspace of ws_bytes (0 if even one row does not fit)
+long long plan_rows(const lsa_forward_args* a, const FwdPlan& p, size_t ws_bytes);
+
+// the plan and rows per chunk for a workspace of ws_bytes: with the interleaved key copy
+// where it fits, else without it (rows 0: not even one row fits)
+FwdPlan plan_for(const lsa_forward_args* a, size_t ws_bytes, long long* rows) {
+  FwdPlan p = plan_forward(a);
+  *rows = plan_rows(a, p, ws_bytes);
+  if (*rows == 0 && p.il_bytes > 0) {
+    p = plan_forward(a, false);
+    *rows = plan_rows(a, p, ws_bytes);
+  }
+  return p;
+}
+
 long long plan_rows(const lsa_forward_args* a, const FwdPlan& p, size_t ws_bytes) {
   const long long n_rows = total_rows(a);
   long long rows = a->chunk_rows > 0 ? std::min<long long>(a->chunk_rows, n_rows) : n_rows;
@@ -535,7 +562,7 @@ void for_each_chunk(const lsa_forward_args* a, long long rows, F f) {
 // stage codes of lsa_forward in launch order (rows per chunk already planned)
 std::vector<int32_t> forward_stages(const lsa_forward_args* a, const FwdPlan& p, long long rows) {
   std::vector<int32_t> st;
-  if (a->two_stage && p.n_blocks > 0 && !a->block_keys) st.push_back(LSA_STAGE_BLOCK_REPS);
+  if (a->two_stage && ((p.n_blocks > 0 && !a->block_keys) || p.il_bytes > 0)) st.push_back(LSA_STAGE_BLOCK_REPS);
   const size_t topk_ws_size = a->two_stage ? 0 : topk_ws_for(a, rows);
   for_each_chunk(a, rows, [&](int32_t, int32_t nb, int32_t, int32_t ni) {
     if (a->two_stage) st.push_back(LSA_STAGE_BLOCK_PREFILTER);
@@ -575,12 +602,12 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
   if (st != LSA_OK) return st;
   if ((long long)a->B * a->n_q == 0) return LSA_OK;
   if (((uintptr_t)ws) % 16 != 0) return LSA_ERR_WORKSPACE;
-  const FwdPlan p = plan_forward(a);
   hipStream_t s = as_stream(stream);
   const long long n_rows = total_rows(a);
 
   // rows per chunk: requested, else the most that fit
-  const long long rows = plan_rows(a, p, ws_bytes);
+  long long rows = 0;
+  const FwdPlan p = plan_for(a, ws_bytes, &rows);
   if (rows == 0 || (!ws && chunk_bytes(a, p, rows) > 0)) return LSA_ERR_WORKSPACE;
   (void)n_rows;
   if (a->stage_events != nullptr &&
@@ -612,6 +639,11 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
     limbs_ws = reinterpret_cast<int8_t*>(base + off);
     limbs = limbs_ws;
     off += align_up((size_t)a->B * p.n_blocks * 2 * a->d_I);
+  }
+  int8_t* k_il = nullptr;  // the token stage's interleaved keys
+  if (p.il_bytes > 0) {
+    k_il = reinterpret_cast<int8_t*>(base + off);
+    off += p.il_bytes;
   }
   int32_t* sc = reinterpret_cast<int32_t*>(base + off);
   off += align_up((size_t)rows * p.ld * 4);
@@ -654,12 +686,14 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
   const int32_t d_I = a->d_I, H_I = a->H_I, H_q = a->H_q, d = a->d, L = a->L_max, kt = a->k_top;
   // one split count for every chunk, so no chunk needs more attention workspace than sized
   const int split = resolve_split(1, (int32_t)rows, kt, a->attn_split);
-  if (a->two_stage && p.n_blocks > 0 && limbs_ws) {
-    if (lsa::launch_block_cache(a->k_idx, a->B, L, d_I, a->block_size, p.n_blocks, 0, p.n_blocks, limbs_ws, s,
-                                chunk_pages(a, 0)) != hipSuccess ||
-        !mark())
-      return LSA_ERR_HIP;
-  }
+  // caches derived from the keys, one stage: the block-key cache and the interleaved keys
+  const bool build_limbs = a->two_stage && p.n_blocks > 0 && limbs_ws;
+  if (build_limbs && lsa::launch_block_cache(a->k_idx, a->B, L, d_I, a->block_size, p.n_blocks, 0, p.n_blocks,
+                                             limbs_ws, s, chunk_pages(a, 0)) != hipSuccess)
+    return LSA_ERR_HIP;
+  if (k_il && lsa::launch_kidx_interleave(a->k_idx, a->B, L, d_I, chunk_pages(a, 0), k_il, s) != hipSuccess)
+    return LSA_ERR_HIP;
+  if ((build_limbs || k_il) && !mark()) return LSA_ERR_HIP;
 
   // one chunk: sequences [b0, b0+nb) x queries [i0, i0+ni) (either nb == 1 or ni == n_q == 1)
   auto run_chunk = [&](int32_t b0, int32_t nb, int32_t i0, int32_t ni) -> lsa_status {
@@ -709,6 +743,7 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
                                  chunk_pages(a, b0), ni);
         } else {
           // the token stage and its top-k in one kernel
+          ia.k_il = k_il ? k_il + (long long)b0 * ((L + 63) / 64) * 64 * d_I : nullptr;
           e = lsa::launch_kept_select(ia, kt, ix, cnt, s);
         }
         if (e != hipSuccess || !mark()) return LSA_ERR_HIP;
@@ -797,8 +832,8 @@ LSA_API lsa_status lsa_forward_stages(const lsa_forward_args* a, size_t ws_bytes
   if (st != LSA_OK) return st;
   *n_stages = 0;
   if ((long long)a->B * a->n_q == 0) return LSA_OK;
-  const FwdPlan p = plan_forward(a);
-  const long long rows = plan_rows(a, p, ws_bytes);
+  long long rows = 0;
+  const FwdPlan p = plan_for(a, ws_bytes, &rows);
   if (rows == 0) return LSA_ERR_WORKSPACE;
   const std::vector<int32_t> v = forward_stages(a, p, rows);
   for (size_t i = 0; codes != nullptr && i < v.size() && (long long)i < max_codes; ++i) codes[i] = v[i];
@@ -816,8 +851,8 @@ LSA_API lsa_status lsa_forward_plan(const lsa_forward_args* a, size_t ws_bytes, 
     *attn_split = 1;
     return LSA_OK;
   }
-  const FwdPlan p = plan_forward(a);
-  const long long rows = plan_rows(a, p, ws_bytes);
+  long long rows = 0;
+  (void)plan_for(a, ws_bytes, &rows);
   if (rows == 0) return LSA_ERR_WORKSPACE;
   *chunk_rows = rows;
   *attn_split = resolve_split(1, (int32_t)rows, a->k_top, a->attn_split);

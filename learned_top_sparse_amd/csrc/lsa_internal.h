@@ -56,6 +56,9 @@ struct IdxArgs {
   // paged caches (decode selection only): k_idx is a pool of n_pages pages of
   // 2^page_log2 keys; key j of sequence b is in page page_table[b * max_pages + (j >> page_log2)]
   Pages pages;
+  // two-stage token stage (block sizes a multiple of 64): the chunk-interleaved copy of
+  // k_idx (launch_kidx_interleave), or nullptr to read k_idx itself
+  const int8_t* k_il;
 };
 
 // Block candidates of decode-shaped rows: the scoring workgroup of span s (span blocks)
@@ -144,6 +147,11 @@ hipError_t launch_expand(const int32_t* kept, const int32_t* q_pos, long long ro
                          int32_t* idx, int32_t* count, hipStream_t st, const Pages& pg = Pages{}, int n_q = 1);
 hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+// chunk-interleaved copy of the index keys of B sequences for the token stage: bytes, and
+// the kernel that writes it (paged caches through pg)
+size_t kidx_interleave_bytes(int B, int L_max, int d_I);
+hipError_t launch_kidx_interleave(const int8_t* k_idx, int B, int L_max, int d_I, const Pages& pg, int8_t* out,
+                                  hipStream_t st);
 // two-stage token stage and its top-k in one kernel (rows of at most KSEL_SLOTS kept slots)
 constexpr int KSEL_SLOTS = 8192;
 hipError_t launch_kept_select(const IdxArgs& a, int k, int32_t* idx, int32_t* count, hipStream_t st);

@@ -21,6 +21,9 @@
 // If bins >= b* hold more than the LDS list can take (heavy ties, adversarial
 // distributions), the row falls back to exact 8-bit radix passes and a final
 // stable compaction over the row in global memory.  Every path is exact.
+#include <algorithm>
+#include <atomic>
+
 #include "lsa_device.h"
 #include "lsa_internal.h"
 #include "lsa_idx_tiles.h"
@@ -607,12 +610,18 @@ __global__ __launch_bounds__(NT) void topk_kernel(const int32_t* __restrict__ sc
 // lookup of that block gives the keys of the whole group (no per-slot division).
 // PAGED: k_idx is a pool of pages of 2^page_log2 >= 64 keys behind the sequence's page
 // table (a 64-aligned group of keys lies in one page); the list receives pool rows.
-template <int D, int MT, bool GB, bool PAGED>
+// IL (with GB): the keys are read from their chunk-interleaved copy kil (one per
+// sequence, kidx_interleave_kernel), whose fragment loads move whole 64-byte pieces per
+// quad of lanes (at the token stage's 16 MiB of keys the reads are then bound by the
+// Infinity Cache rather than by the texture data path).
+template <int D, int MT, bool GB, bool PAGED, bool IL>
 __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
-    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w,
-    int w_per_query, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ kept, int bs, int n_keep,
-    int n_q, int L_max, int H_I, int k, int32_t* __restrict__ idx, int32_t* __restrict__ count, Pages pg) {
+    const int8_t* __restrict__ q_idx, const int8_t* __restrict__ k_idx, const int8_t* __restrict__ kil,
+    const int32_t* __restrict__ w, int w_per_query, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ kept, int bs, int n_keep, int n_q, int L_max, int H_I, int k,
+    int32_t* __restrict__ idx, int32_t* __restrict__ count, Pages pg) {
   constexpr int NT = 256, NW = NT / 64, KS = D / 64, RING = 4;
+  static_assert(!IL || GB, "the interleaved keys are read a 64-key group at a time");
   __shared__ int kept_s[256];
   __shared__ __attribute__((aligned(16))) int sbuf[KSEL_SLOTS];
   __shared__ int lds_big[NBINS];
@@ -647,6 +656,7 @@ __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
     (void)block_exclusive_scan<NT>(c, scan_tmp, &n_valid);
   }
   const int8_t* kb = k_idx + (PAGED ? 0ll : (long long)b * L_max * D);
+  const int8_t* kil_b = IL ? kil + (long long)b * ((L_max + 63) >> 6) * 64 * D : nullptr;
   const int32_t* pt = PAGED ? pg.page_table + (long long)b * pg.max_pages : nullptr;
   const int pmask = PAGED ? (1 << pg.page_log2) - 1 : 0;
   // pool row of logical key j (paged caches; page ids clamped into the pool).  The own
@@ -664,6 +674,8 @@ __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
     if constexpr (PAGED) return pool_row(j);
     return j;
   };
+  const int n_groups = (n_slots + 63) / 64;
+  const int n_iter = ((n_groups + NW - 1) / NW + RING - 1) / RING * RING;  // groups per wave, padded
   v4i ring[RING][4][KS];
   auto load_group = [&](int i, v4i (&Bf)[4][KS]) {
     const int sg = 64 * (wave + NW * i);
@@ -673,15 +685,25 @@ __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
       const int bi = sgc / bs;
       const int blk = kept_s[bi];
       const int base = blk >= 0 ? blk * bs + (sgc - bi * bs) : 0;
-      // paged: the group's 64 keys lie in the page of its first key (base and the page
-      // size are multiples of 64)
-      const long long rbase = PAGED ? pool_row(base) : (long long)base;
+      if constexpr (IL) {
+        // group base / 64 of the interleaved copy: piece c of key 16 nt + r16 at
+        // ((group * D / 16 + c) * 64 + 16 nt + r16) * 16
+        const int8_t* kg = kil_b + (long long)(base >> 6) * 64 * D + 16 * r16;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int8_t* kr =
-            kb + (PAGED ? rbase + 16 * nt + r16 : (long long)min(base + 16 * nt + r16, L_max - 1)) * D;
+        for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
+          for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kg + (kchunk<D>(g, ks) * 64 + 16 * nt) * 16);
+      } else {
+        // paged: the group's 64 keys lie in the page of its first key (base and the page
+        // size are multiples of 64)
+        const long long rbase = PAGED ? pool_row(base) : (long long)base;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int8_t* kr =
+              kb + (PAGED ? rbase + 16 * nt + r16 : (long long)min(base + 16 * nt + r16, L_max - 1)) * D;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) Bf[nt][ks] = *(const v4i*)(kr + 16 * kchunk<D>(g, ks));
+        }
       }
     } else {
 #pragma unroll
@@ -692,8 +714,6 @@ __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
       }
     }
   };
-  const int n_groups = (n_slots + 63) / 64;
-  const int n_iter = ((n_groups + NW - 1) / NW + RING - 1) / RING * RING;  // groups per wave, padded
   // the prologue issues the slots in ring order (the loop's waits assume slot 0 is the
   // oldest; a reordered prologue makes the compiler drain every load at the loop head)
 #pragma unroll
@@ -752,20 +772,70 @@ __global__ __launch_bounds__(256, 2) void idx_kept_select_kernel(
   select_row<NT, true>(rv, n_valid, k, out, lds_big, wcnt, scan_tmp, h256, sh);
 }
 
+// compute units of the current device (cached per device)
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 template <int D, int MT>
 static hipError_t launch_kept_select_t(const IdxArgs& a, int k, int32_t* idx, int32_t* count, hipStream_t st) {
   const long long rows = (long long)a.B * a.n_q;
-  const bool gb = a.block_size % 64 == 0, paged = a.pages.page_table != nullptr;
-#define LSA_KSEL(GB, PG)                                                                                             \
-  hipLaunchKernelGGL((idx_kept_select_kernel<D, MT, GB, PG>), dim3((unsigned)rows), dim3(256), 0, st, a.q_idx,       \
-                     a.k_idx, a.w, a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, a.H_I, k, \
-                     idx, count, a.pages)
-  if (gb && paged) LSA_KSEL(true, true);
-  else if (gb) LSA_KSEL(true, false);
-  else if (paged) LSA_KSEL(false, true);
-  else LSA_KSEL(false, false);
+  const bool gb = a.block_size % 64 == 0, paged = a.pages.page_table != nullptr, il = gb && a.k_il != nullptr;
+#define LSA_KSEL(GB, PG, IL)                                                                                        \
+  hipLaunchKernelGGL((idx_kept_select_kernel<D, MT, GB, PG, IL>), dim3((unsigned)rows), dim3(256), 0, st, a.q_idx, \
+                     a.k_idx, a.k_il, a.w, a.w_per_query, a.q_pos, a.kept, a.block_size, a.n_keep, a.n_q, a.L_max, \
+                     a.H_I, k, idx, count, a.pages)
+  if (il && paged) LSA_KSEL(true, true, true);
+  else if (il) LSA_KSEL(true, false, true);
+  else if (gb && paged) LSA_KSEL(true, true, false);
+  else if (gb) LSA_KSEL(true, false, false);
+  else if (paged) LSA_KSEL(false, true, false);
+  else LSA_KSEL(false, false, false);
 #undef LSA_KSEL
   return hipGetLastError();
+}
+
+// Chunk-interleaved index keys for the token stage.  An MFMA fragment of 16 keys takes
+// 16 bytes of each key per lane, lanes 0..15 on 16 different keys; loaded from key rows,
+// every quad of lanes touches four rows, and such loads deliver about a quarter of the
+// bytes per cycle that loads of contiguous lanes do.  Here group G of 64 keys of a
+// sequence stores, for each 16-byte piece c of the key rows, the 64 keys' pieces side by
+// side -- il[b][G][c][jj] = k_idx[b][64 G + jj][16 c .. 16 c + 15] -- so the 16 keys of a
+// fragment are 256 contiguous bytes per piece.  Keys at or past L_max are zero.  One
+// thread per 16-byte piece, in output order (coalesced writes).
+template <int D>
+__global__ __launch_bounds__(256) void kidx_interleave_kernel(const int8_t* __restrict__ k_idx, int L_max,
+                                                              long long n_grp, long long total, Pages pg,
+                                                              v4i* __restrict__ out) {
+  constexpr int CH = D / 16;
+  for (long long t = (long long)blockIdx.x * 256 + threadIdx.x; t < total; t += (long long)gridDim.x * 256) {
+    const int jj = (int)(t & 63);
+    const long long q = t >> 6;
+    const int c = (int)(q % CH);
+    const long long gq = q / CH;
+    const long long b = gq / n_grp;
+    const long long j = (gq - b * n_grp) * 64 + jj;
+    v4i v = v4i{0, 0, 0, 0};
+    if (j < L_max) {
+      long long r;
+      if (pg.page_table != nullptr) {  // page ids clamped into the pool
+        const int pi = (int)(j >> pg.page_log2);
+        const int page = min(max(pg.page_table[b * pg.max_pages + pi], 0), pg.n_pages - 1);
+        r = ((long long)page << pg.page_log2) | (j & ((1 << pg.page_log2) - 1));
+      } else {
+        r = b * L_max + j;
+      }
+      v = *(const v4i*)(k_idx + r * D + 16 * c);
+    }
+    out[t] = v;
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -1934,6 +2004,28 @@ hipError_t launch_expand(const int32_t* kept, const int32_t* q_pos, long long ro
   if (pg.page_table != nullptr && (pg.page_log2 < 6 || pg.page_log2 > 30 || pg.n_pages < 1)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(expand_kernel<256>, dim3((unsigned)rows), dim3(256), 0, st, kept, q_pos, bs, n_keep, k, idx,
                      count, pg, n_q);
+  return hipGetLastError();
+}
+
+size_t kidx_interleave_bytes(int B, int L_max, int d_I) {
+  return (size_t)B * (size_t)((L_max + 63) / 64) * 64 * (size_t)d_I;
+}
+
+hipError_t launch_kidx_interleave(const int8_t* k_idx, int B, int L_max, int d_I, const Pages& pg, int8_t* out,
+                                  hipStream_t st) {
+  if (B < 1 || L_max < 1 || (d_I != 64 && d_I != 128) || !k_idx || !out) return hipErrorInvalidValue;
+  if (pg.page_table != nullptr &&
+      (pg.page_log2 < 6 || pg.page_log2 > 30 || pg.n_pages < 1 || (long long)pg.max_pages << pg.page_log2 != L_max))
+    return hipErrorInvalidValue;
+  const long long n_grp = (L_max + 63) / 64;
+  const long long total = (long long)B * n_grp * 64 * (d_I / 16);
+  const unsigned grid = (unsigned)std::min<long long>((total + 255) / 256, 16LL * device_cus());
+  if (d_I == 128)
+    hipLaunchKernelGGL(kidx_interleave_kernel<128>, dim3(grid), dim3(256), 0, st, k_idx, L_max, n_grp, total, pg,
+                       reinterpret_cast<v4i*>(out));
+  else
+    hipLaunchKernelGGL(kidx_interleave_kernel<64>, dim3(grid), dim3(256), 0, st, k_idx, L_max, n_grp, total, pg,
+                       reinterpret_cast<v4i*>(out));
   return hipGetLastError();
 }
 
