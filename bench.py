@@ -261,6 +261,33 @@ def measured_traffic():
     return int(m.group(1)) if d.hexdigest() == h.group(1) else None
 
 
+COUNTER_FILE = os.path.join(ROOT, "profiles", "compute_counters.md")
+COUNTER_SOURCES = ["learned_top_sparse_amd/csrc/lsa_topk.hip", "learned_top_sparse_amd/csrc/lsa_indexer.hip",
+                   "learned_top_sparse_amd/csrc/lsa_attn.hip", "learned_top_sparse_amd/csrc/lsa_device.h",
+                   "learned_top_sparse_amd/csrc/lsa_select.h", "learned_top_sparse_amd/csrc/lsa_idx_tiles.h",
+                   "learned_top_sparse_amd/csrc/lsa_internal.h"]
+
+
+def counter_mfma_busy(workload, stage):
+    """Matrix-core busy share (SQ_VALU_MFMA_BUSY_CYCLES over the SIMDs' cycles) of a stage's
+    kernel from the committed rocprofv3 counter runs, or None if the kernel sources
+    changed since they were taken (or the stage was not profiled)."""
+    import hashlib
+    import re
+    try:
+        txt = open(COUNTER_FILE).read()
+    except OSError:
+        return None
+    h = re.search(r"^kernel_sources_sha256: ([0-9a-f]{64})$", txt, re.M)
+    m = re.search(rf"^counter_mfma_busy: {re.escape(workload)} {re.escape(stage)} ([0-9.]+)$", txt, re.M)
+    if not (h and m):
+        return None
+    d = hashlib.sha256()
+    for f in COUNTER_SOURCES:
+        d.update(open(os.path.join(ROOT, f), "rb").read())
+    return float(m.group(1)) if d.hexdigest() == h.group(1) else None
+
+
 SEM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_128k_lsa_scan_traffic.md")
 SEM_TRAFFIC_SOURCES = ["learned_top_sparse_amd/csrc/lsa_semantic.hip"]
 
@@ -378,6 +405,7 @@ def attention_object(alg, at_ms, peaks, wl):
         ceil, mib = resident_ceiling(peaks, wl)
         obj.update({"resident_pool_MiB": mib, "frac_of_measured_resident_gather": gb / ceil,
                     "frac_of_measured_l2_gather": gb / peaks["gather_l2_GBs"]})
+    obj["counter_mfma_busy"] = counter_mfma_busy(wl.name, "sparse_attn")
     return obj
 
 
@@ -609,6 +637,7 @@ def prefill_object(lsa, torch, name, steps, warmup, peaks, with_cpu):
         obj["roofline"] = {"bound": "mfma", "kernel": f"{stage} (flat indexer scan, idx_flat_kernel)",
                            "achieved": ach, "peak": INT8_PEAK_TOPS, "unit": "TOP/s", "frac": ach / INT8_PEAK_TOPS,
                            "frac_of_measured_peak": ach / peaks["int8_mfma_TOPs"] if peaks else None,
+                           "counter_mfma_busy": counter_mfma_busy(wl.name, stage),
                            "algorithmic_ops_per_step": alg["index_ops"], "launch_ms_per_step": scan_ms}
     obj["attention"] = attention_object(alg, km["sparse_attn"]["ms_per_step"], peaks, wl)
     if with_cpu:
@@ -816,6 +845,7 @@ def main():
             "bound": "mfma", "kernel": ts_desc,
             "achieved": ach_p, "peak": INT8_PEAK_TOPS, "unit": "TOP/s", "frac": ach_p / INT8_PEAK_TOPS,
             "frac_of_measured_peak": ach_p / peaks["int8_mfma_TOPs"] if peaks else None,
+            "counter_mfma_busy": counter_mfma_busy(wp.name, ts_stage),
         },
         "t_roof_ms": t_roof_ms(wp),
         "step_roofline_frac": t_roof_ms(wp) / ms_p,
