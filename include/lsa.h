@@ -388,7 +388,30 @@ typedef struct lsa_semantic_params {
   int32_t n_pool;    /* keys summed into one pool key; divides n_cluster and n_bmax */
   int32_t n_bavg;    /* average keys per bucket; divides n_cluster (m = n_cluster / n_bavg) */
   int32_t n_bmax;    /* largest bucket, in keys; at least 2 * n_bavg (so exactly m buckets form) */
+  /* How lsa_semantic_select finds the top-p buckets of decode rows (one query per
+   * sequence); the result is the exact top-p in every mode, and prefill rows always rank
+   * their whole score row.
+   *   LSA_SEM_SELECT_ROW (0): every row ranks its whole score row (one workgroup holds
+   *     rows of up to 32768 buckets in registers; longer rows merge spans' top-p).
+   *   LSA_SEM_SELECT_THRESHOLD (1): the threshold list of [LSA] App. F.1 "Selection by
+   *     threshold", "Flat decode", for rows of more than LSA_SEM_LIST_CAP buckets with
+   *     p_top <= LSA_SEM_LIST_CAP / 4: a threshold is set from a sample of the row
+   *     (about 2 p_top buckets reach it), the scan lists every bucket at or above it, and
+   *     only the list is ranked; a row whose list falls short of p_top or overflows its
+   *     LSA_SEM_LIST_CAP entries ranks its whole score row instead.
+   *   LSA_SEM_SELECT_FORCE_SHORT (2), LSA_SEM_SELECT_FORCE_OVERFLOW (3): as THRESHOLD,
+   *     with the threshold above / below every score, so every such row falls back
+   *     (tests). */
+  int32_t select_mode;
 } lsa_semantic_params;
+
+#define LSA_SEM_LIST_CAP 4096 /* entries of a decode row's threshold list */
+enum {
+  LSA_SEM_SELECT_ROW = 0,
+  LSA_SEM_SELECT_THRESHOLD = 1,
+  LSA_SEM_SELECT_FORCE_SHORT = 2,
+  LSA_SEM_SELECT_FORCE_OVERFLOW = 3
+};
 
 /*
  * Bucket cache of blocks [first_block, first_block + n_update) of every sequence
@@ -444,9 +467,10 @@ lsa_status lsa_semantic_cluster_paged(const void* k_idx, int32_t B, int32_t L_ma
                                       int32_t* table, int32_t* offsets, void* stream);
 
 /* Workspace lsa_semantic_select needs to take all B * n_q queries in one pass: per
-   query its normalised index query and one score-table row of n_blocks * m floats.
-   Less (at least one query per sequence) is accepted: the call then runs in chunks of
-   queries. */
+   query its normalised index query and one score-table row of n_blocks * m floats, and
+   for decode (n_q == 1) rows of more than LSA_SEM_LIST_CAP buckets the threshold list
+   (LSA_SEM_LIST_CAP 8-byte entries, a count and the threshold).  Less (at least one
+   query per sequence) is accepted: the call then runs in chunks of queries. */
 lsa_status lsa_semantic_select_workspace_size(int32_t B, int32_t n_q, int32_t n_blocks,
                                               const lsa_semantic_params* prm, size_t* bytes);
 

@@ -44,7 +44,7 @@ class ForwardArgs(C.Structure):
 
 class SemanticParams(C.Structure):
     """lsa_semantic_params of include/lsa.h."""
-    _fields_ = [("n_cluster", I32), ("n_pool", I32), ("n_bavg", I32), ("n_bmax", I32)]
+    _fields_ = [("n_cluster", I32), ("n_pool", I32), ("n_bavg", I32), ("n_bmax", I32), ("select_mode", I32)]
 
 
 class SemanticPages(C.Structure):

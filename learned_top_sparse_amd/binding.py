@@ -238,6 +238,8 @@ def lsa_sparse_attn(q, k, v, idx, scale: Optional[float] = None, n_split: int = 
 
 # selection of flat prefill rows (lsa_forward_args.select_mode)
 SELECT_MODES = {"auto": 0, "table": 1, "force_short": 2, "force_overflow": 3}
+# selection of semantic decode rows (lsa_semantic_params.select_mode)
+SEM_SELECT_MODES = {"row": 0, "threshold": 1, "force_short": 2, "force_overflow": 3}
 
 
 def _forward_args(inp: dict, k_top: int, two_stage, block_size: int, n_keep: int, scale, attn_split: int,
@@ -452,18 +454,19 @@ def lsa_semantic_cache(k_idx, n_cluster: int = 512, n_pool: int = 4, n_bavg: int
 
 def lsa_semantic_select(q_idx, q_pos, cache: dict, k: int, p_top: int, n_sink: int, n_w: int,
                         idx=None, count=None, ws_bytes: Optional[int] = None, ws: Optional[torch.Tensor] = None,
-                        paged: Optional[dict] = None, stage_events=None):
+                        paged: Optional[dict] = None, stage_events=None, select: str = "row"):
     """Index lists of flat semantic search: (idx int32 [B, n_q, n_sink + k + n_w], count
     int32 [B, n_q]).  q_idx bf16 [B, n_q, 64]; q_pos int32 [B, n_q].  ``paged``: as for
     lsa_semantic_cache, plus n_slots (rows of the key pools) with a page table; the lists
     then hold pool rows.  ``stage_events``: three torch.cuda.Events (created and recorded
     once beforehand) recorded before and after the centroid scan and at the end
-    (lsa_semantic_select_timed; contiguous caches)."""
+    (lsa_semantic_select_timed; contiguous caches).  ``select``: how decode rows find their
+    top-p buckets (lsa_semantic_params.select_mode; a key of SEM_SELECT_MODES)."""
     _need(q_idx, "q_idx", torch.bfloat16)
     dev = q_idx.device
     _need(q_pos, "q_pos", torch.int32, dev)
     B, n_q, d = q_idx.shape
-    prm = SemanticParams(*cache["params"])
+    prm = SemanticParams(*cache["params"], SEM_SELECT_MODES[select])
     NB = cache.get("NB", cache["table"].shape[1])
     W = n_sink + k + n_w
     if idx is None:
@@ -514,10 +517,10 @@ def lsa_semantic_workspace_size(B: int, n_q: int, cache: dict) -> int:
 
 
 def lsa_semantic_forward(inp: dict, cache: dict, k: int, p_top: int, n_sink: int, n_w: int,
-                         scale: Optional[float] = None, attn_split: int = 0) -> dict:
+                         scale: Optional[float] = None, attn_split: int = 0, select: str = "row") -> dict:
     """Flat semantic search then sparse attention over its lists: lsa_semantic_select
     and lsa_sparse_attn.  inp: q_sem bf16 [B, n_q, 64], q_pos, q / k / v as for
     lsa_sparse_attn.  Returns dict(idx, count, out, lse)."""
-    idx, count = lsa_semantic_select(inp["q_sem"], inp["q_pos"], cache, k, p_top, n_sink, n_w)
+    idx, count = lsa_semantic_select(inp["q_sem"], inp["q_pos"], cache, k, p_top, n_sink, n_w, select=select)
     out, lse = lsa_sparse_attn(inp["q"], inp["k"], inp["v"], idx, scale=scale, n_split=attn_split)
     return {"idx": idx, "count": count, "out": out, "lse": lse}

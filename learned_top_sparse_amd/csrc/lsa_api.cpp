@@ -74,7 +74,7 @@ LSA_API const char* lsa_status_string(lsa_status s) {
   }
 }
 
-LSA_API int lsa_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+LSA_API int lsa_version(void) { return 1 * 10000 + 1 * 100 + 0; }
 
 LSA_API lsa_status lsa_index_scores(const int8_t* q_idx, const int8_t* k_idx, const int32_t* w,
                                     int32_t w_per_query, const int32_t* q_pos, const int32_t* kept_blocks,
@@ -870,6 +870,7 @@ static lsa_status check_sem_params(const lsa_semantic_params* prm, int d_idx, ls
       p.n_cluster % p.n_bavg != 0 || p.n_bmax % p.n_pool != 0 || p.n_bmax < 2 * p.n_bavg ||
       p.n_bavg < p.n_pool)
     return LSA_ERR_INVALID_ARG;
+  if (p.select_mode < LSA_SEM_SELECT_ROW || p.select_mode > LSA_SEM_SELECT_FORCE_OVERFLOW) return LSA_ERR_INVALID_ARG;
   if (d_idx != 64) return LSA_ERR_UNSUPPORTED;
   if (p.n_cluster / p.n_pool > lsa::SEM_MAX_POOL_KEYS || p.n_cluster / p.n_bavg > lsa::SEM_MAX_BUCKETS)
     return LSA_ERR_UNSUPPORTED;
@@ -877,6 +878,7 @@ static lsa_status check_sem_params(const lsa_semantic_params* prm, int d_idx, ls
   sp->n_pool = p.n_pool;
   sp->n_bavg = p.n_bavg;
   sp->n_bmax = p.n_bmax;
+  sp->select_mode = p.select_mode;
   return LSA_OK;
 }
 
@@ -946,7 +948,8 @@ LSA_API lsa_status lsa_semantic_select_workspace_size(int32_t B, int32_t n_q, in
   if (!bytes || B < 0 || n_q < 0 || n_blocks < 0) return LSA_ERR_INVALID_ARG;
   lsa_status st = check_sem_params(prm, 64, &sp);
   if (st != LSA_OK) return st;
-  *bytes = (size_t)B * n_q * lsa::sem_select_row_bytes(n_blocks, sp.n_cluster / sp.n_bavg, sp.n_cluster, sp.n_bmax);
+  *bytes = (size_t)B * n_q *
+           lsa::sem_select_row_bytes(n_blocks, sp.n_cluster / sp.n_bavg, sp.n_cluster, sp.n_bmax, n_q == 1);
   return LSA_OK;
 }
 
@@ -968,7 +971,7 @@ static lsa_status sem_select(const void* q_idx, const int32_t* q_pos, int32_t B,
   if (!q_idx || !q_pos || !idx || !count || (n_blocks > 0 && (!centroids || !table || !offsets)))
     return LSA_ERR_INVALID_ARG;
   if (((uintptr_t)ws) % 16 != 0) return LSA_ERR_WORKSPACE;
-  const size_t row = lsa::sem_select_row_bytes(n_blocks, sp.n_cluster / sp.n_bavg, sp.n_cluster, sp.n_bmax);
+  const size_t row = lsa::sem_select_row_bytes(n_blocks, sp.n_cluster / sp.n_bavg, sp.n_cluster, sp.n_bmax, n_q == 1);
   if (!ws || ws_bytes < (size_t)B * row) return LSA_ERR_WORKSPACE;
   lsa::SemSelectArgs a;
   a.q_idx = q_idx;

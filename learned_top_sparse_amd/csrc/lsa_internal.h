@@ -198,6 +198,7 @@ hipError_t launch_list_topk(const int32_t* q_pos, long long rows, int L_max, int
 // ---- flat semantic search (Ward bucket cache, centroid scoring, top-p, expansion)
 struct SemParams {
   int n_cluster, n_pool, n_bavg, n_bmax;
+  int select_mode;  // lsa_semantic_params.select_mode
 };
 struct SemPages {
   const int32_t* block_table = nullptr;  // [B, NB] cache slot of each cluster block (null: b * NB + t)
@@ -230,7 +231,7 @@ constexpr int SEM_MAX_K = 4096;
 hipError_t launch_sem_cluster(const void* k_idx, int B, int L_max, const SemParams& sp, int NB, int first_block,
                               int n_update, void* cent, int32_t* table, int32_t* offs, const SemPages& pages,
                               hipStream_t st);
-size_t sem_select_row_bytes(int NB, int m, int n_cluster, int n_bmax);
+size_t sem_select_row_bytes(int NB, int m, int n_cluster, int n_bmax, bool decode);
 hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st);
 
 }  // namespace lsa

@@ -376,15 +376,123 @@ __global__ __launch_bounds__(256) void sem_qnorm_kernel(const unsigned short* __
 // that query's row of the score table; the next block's centroids are loaded while
 // the current one is scored.
 
+// ---------------------------------------------------------------------------------
+// Selection by threshold, decode rows ("Latent Sparse Attention (LSA)", App. F.1
+// "Selection by threshold", "Flat decode").  Before the scan, a threshold theta_i is set
+// for each query from a sample of its row; the scan then appends every bucket scoring
+// at or above theta_i to the query's list L_i (one comparison per score, whatever the
+// span), and the selection ranks only L_i.  When L_i holds every such bucket (it did not
+// overflow) and at least p of them, the row's top-p all score >= theta_i and are in it;
+// otherwise the row falls back to the scores the scan wrote.  Either way the result is
+// the exact top-p: the threshold only sets how many buckets are listed.
+constexpr int SEM_LCAP = 4096;     // list entries per row
+constexpr int SEM_THR_NT = 1024;   // threads of the threshold workgroup
+constexpr int SEM_THR_C = 16;      // sampled buckets per thread (16384 at most)
+
+struct SemList {
+  unsigned long long* keys;  // [rows][SEM_LCAP]: order key of the score << 32 | ~bucket
+  int* cnt;                  // [rows]: buckets at or above theta (may exceed SEM_LCAP)
+  unsigned* theta;           // [rows]: order key of theta
+};
+
+// The query normalised as the scan does it (each wave on its own, the same roundings):
+// the 64 values wave-uniform.
+__device__ __forceinline__ void sem_decode_query(const unsigned short* __restrict__ q_idx, long long qrow, int lane,
+                                                 float (&q)[SEM_D]) {
+  const float x = __uint_as_float((unsigned)q_idx[qrow * SEM_D + lane] << 16);
+  const float sq = x * x;
+  float ss = 0.f;
+#pragma unroll
+  for (int d = 0; d < SEM_D; ++d) ss = ss + __shfl(sq, d);
+  const float nrm = sqrtf(ss);
+  const int yb = (int)(to_bf16(nrm > 0.f ? x / nrm : 0.f) << 16);
+#pragma unroll
+  for (int d = 0; d < SEM_D; ++d) q[d] = __int_as_float(__builtin_amdgcn_readlane(yb, d));
+}
+
+// One workgroup per decode row: theta_i and a cleared list counter.  The sample is
+// n_s = N / 8 buckets (2048 to 16384), in runs of 8 neighbouring buckets spread evenly
+// over the row, scored exactly as the scan scores them; theta_i is the n_theta-th best
+// sampled score with n_theta = 2 p n_s / N, so about 2 p buckets of the row reach it
+// (room for the sample's noise on both sides: p below, SEM_LCAP - 2 p above).  Rows of
+// at most SEM_LCAP buckets list every bucket.  mode 2 / 3 set theta above / below every
+// score, so that every row falls back (tests).
+__global__ __launch_bounds__(SEM_THR_NT) void sem_theta_kernel(const unsigned short* __restrict__ q_idx,
+                                                               const int* __restrict__ q_pos, int n_q, int i0,
+                                                               SemPaging pg, const unsigned short* __restrict__ cent,
+                                                               int NB, int m, int n_cluster, int p_top, int mode,
+                                                               SemList L) {
+  constexpr int NT = SEM_THR_NT, C = SEM_THR_C;
+  __shared__ int hist[2048];
+  __shared__ int scan_tmp[NT / 64];
+  __shared__ int sh[4];
+  __shared__ unsigned long long shu[2];
+  const int t = threadIdx.x, lane = t & 63, b = blockIdx.x;
+  const long long qrow = (long long)b * n_q + i0;
+  const int p = q_pos[qrow];
+  int nb = p < 0 ? 0 : p / n_cluster;
+  nb = nb < NB ? nb : NB;
+  const int N = nb * m;
+  unsigned theta = 0u;  // every bucket
+  if (mode == 2) {
+    theta = 0xFFFFFFFFu;
+  } else if (mode == 0 && N > SEM_LCAP) {
+    float q[SEM_D];
+    sem_decode_query(q_idx, qrow, lane, q);
+    int n_s = N / 8;
+    n_s = n_s < 2048 ? 2048 : (n_s > NT * C ? NT * C : n_s);
+    n_s &= ~7;
+    const int runs = n_s / 8;
+    int n_theta = (int)((2LL * p_top * n_s + N / 2) / N);
+    n_theta = n_theta < 1 ? 1 : (n_theta > n_s ? n_s : n_theta);
+    const uint4* c4 = reinterpret_cast<const uint4*>(cent);
+    unsigned long long key[C];
+    unsigned vmask = 0u;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int e = c * NT + t;
+      key[c] = 0ull;
+      if (e < n_s) {
+        int j = (int)((long long)(e >> 3) * N / runs) + (e & 7);
+        j = j < N ? j : N - 1;
+        const int blk = j / m, sl = j - blk * m;
+        const uint4* cb = c4 + pg.slot(b, NB, blk) * (SEM_D * SEM_SLOTS / 8) + sl;
+        uint4 v[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g) v[g] = cb[g * SEM_SLOTS];
+        float acc = 0.f;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          float cv[8];
+          unpack8(v[g], cv);
+#pragma unroll
+          for (int d = 0; d < 8; ++d) acc = fmaf(q[8 * g + d], cv[d], acc);
+        }
+        key[c] = ((unsigned long long)order_key(acc) << 32) | (0xFFFFFFFFu - (unsigned)e);
+        vmask |= 1u << c;
+      }
+    }
+    int need_eq;
+    const unsigned long long T = radix_cut64<NT, C>(key, vmask, n_theta, hist, scan_tmp, sh, shu, &need_eq);
+    theta = (unsigned)(T >> 32);
+  }
+  if (t == 0) {  // decode rows: one query per sequence, row b
+    L.cnt[b] = 0;
+    L.theta[b] = theta;
+  }
+}
+
 // Decode (one query per sequence): the same scores, with the query normalised inside
 // each wave -- lane d holds x_d, the sum of squares is taken d = 0, 1, ... across the
 // lanes, and the 64 rounded values are then wave-uniform -- so no separate launch.
+// With a list (L.keys), every bucket scoring at or above the row's theta is also appended
+// to the row's list: one ballot and one counter atomic per wave and block.
 __global__ __launch_bounds__(256) void sem_score_decode_kernel(const unsigned short* __restrict__ q_idx,
                                                                const int* __restrict__ q_pos, int n_q, int i0,
                                                                SemPaging pg,
                                                                const unsigned short* __restrict__ cent, int NB,
                                                                int m, int n_cluster, int bpw,
-                                                               float* __restrict__ S, long long ld) {
+                                                               float* __restrict__ S, long long ld, SemList L) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int b = blockIdx.z;
   const int blk0 = (blockIdx.x * 4 + w) * bpw;
@@ -410,16 +518,9 @@ __global__ __launch_bounds__(256) void sem_score_decode_kernel(const unsigned sh
     for (int c = 0; c < 8; ++c) nxt[c] = cb[c * SEM_SLOTS + lane];
   }
 
-  const float x = __uint_as_float((unsigned)q_idx[((long long)b * n_q + i0) * SEM_D + lane] << 16);
-  const float sq = x * x;
-  float ss = 0.f;
-#pragma unroll
-  for (int d = 0; d < SEM_D; ++d) ss = ss + __shfl(sq, d);
-  const float nrm = sqrtf(ss);
-  const int yb = (int)(to_bf16(nrm > 0.f ? x / nrm : 0.f) << 16);
   float q[SEM_D];  // wave-uniform: scalar registers
-#pragma unroll
-  for (int d = 0; d < SEM_D; ++d) q[d] = __int_as_float(__builtin_amdgcn_readlane(yb, d));
+  sem_decode_query(q_idx, (long long)b * n_q + i0, lane, q);
+  const unsigned theta = L.keys ? L.theta[b] : 0u;
 
 #pragma unroll 1
   for (int blk = blk0; blk < blk_end; ++blk) {
@@ -437,6 +538,20 @@ __global__ __launch_bounds__(256) void sem_score_decode_kernel(const unsigned sh
 #pragma unroll
     for (int d = 0; d < SEM_D; ++d) acc = fmaf(q[d], cv[d], acc);
     if (lane < m) S[(long long)b * ld + (long long)blk * m + lane] = acc;
+    if (L.keys) {
+      const unsigned ok = order_key(acc);
+      const bool pass = lane < m && ok >= theta;
+      const unsigned long long ball = __ballot(pass);
+      if (ball != 0ull) {
+        int slot0 = 0;
+        if (lane == 0) slot0 = atomicAdd(&L.cnt[b], __popcll(ball));
+        slot0 = __shfl(slot0, 0);
+        const int sl = slot0 + lanes_below(ball);
+        if (pass && sl < SEM_LCAP)
+          L.keys[(long long)b * SEM_LCAP + sl] =
+              ((unsigned long long)ok << 32) | (0xFFFFFFFFu - (unsigned)(blk * m + lane));
+      }
+    }
   }
 }
 
@@ -789,7 +904,8 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
                                                              const int* __restrict__ offs, int NB, int m,
                                                              int n_cluster, int n_bmax, int k, int p_top, int n_sink,
                                                              int n_w, int W, int* __restrict__ idx,
-                                                             int* __restrict__ count, SemPaging pg, int split) {
+                                                             int* __restrict__ count, SemPaging pg, int split,
+                                                             SemList lst) {
   constexpr int NWD = NT * C / 32;
   constexpr int LW = SelLbm<C>::WORDS;
   __shared__ unsigned long long K[SEM_PMAX];
@@ -842,7 +958,21 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
     if (t == 0) sh[3] = 0;
     __syncthreads();  // a row with no scored bucket reads sh[3] with no other barrier
     const int lane = t & 63;
-    if (split) {
+    // the row's threshold list, when it holds every bucket at or above theta and at least
+    // p_top of them (then the row's top-p is in it); otherwise the whole row below
+    bool listed = false;
+    if (lst.keys) {
+      const long long lr = (long long)b * nqc + i;
+      const int c = lst.cnt[lr];
+      if (c >= p_top && c <= SEM_LCAP) {
+        for (int x = t; x < c; x += NT) Kc[x] = lst.keys[lr * SEM_LCAP + x];
+        __syncthreads();
+        if (t == 0) sh[3] = c;
+        __syncthreads();
+        listed = true;
+      }
+    }
+    if (split && !listed) {
       // the spans' candidates, left in the score row by sem_span_topk_kernel (every
       // thread reads every count, so all keep the same running offset)
       int off = 0;
@@ -856,7 +986,7 @@ __global__ __launch_bounds__(NT, MINW) void sem_select_kernel(const float* __res
       if (t == 0) sh[3] = off;
       __syncthreads();
     }
-    for (int base = 0; base < (split ? 0 : N); base += CH) {
+    for (int base = 0; base < (split || listed ? 0 : N); base += CH) {
       unsigned long long key[C];
       unsigned vmask = 0u;
 #pragma unroll
@@ -1218,14 +1348,20 @@ long long sem_ld(int NB, int m, int n_cluster, int n_bmax) {
   return (n + 3) / 4 * 4;
 }
 
-size_t sem_select_row_bytes(int NB, int m, int n_cluster, int n_bmax) {
-  return (size_t)SEM_D * 4 + (size_t)sem_ld(NB, m, n_cluster, n_bmax) * 4;
+// Rows that may take the threshold list: decode rows longer than the list.  Each gets
+// the list, its count and its threshold after the score rows.
+static bool sem_list_rows(int NB, int m, bool decode) { return decode && (long long)NB * m > SEM_LCAP; }
+
+size_t sem_select_row_bytes(int NB, int m, int n_cluster, int n_bmax, bool decode) {
+  const size_t lst = sem_list_rows(NB, m, decode) ? (size_t)SEM_LCAP * 8 + 8 : 0;
+  return (size_t)SEM_D * 4 + (size_t)sem_ld(NB, m, n_cluster, n_bmax) * 4 + lst;
 }
 
 hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
   const int m = a.sp.n_cluster / a.sp.n_bavg;
   const long long ld = sem_ld(a.NB, m, a.sp.n_cluster, a.sp.n_bmax);
-  const size_t row_bytes = sem_select_row_bytes(a.NB, m, a.sp.n_cluster, a.sp.n_bmax);
+  const bool decode = a.n_q == 1;
+  const size_t row_bytes = sem_select_row_bytes(a.NB, m, a.sp.n_cluster, a.sp.n_bmax, decode);
   const long long rows_fit = (long long)(a.ws_bytes / row_bytes);
   long long nqc_max = rows_fit / a.B;
   if (nqc_max > a.n_q) nqc_max = a.n_q;
@@ -1237,6 +1373,21 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
     const int rows = a.B * nqc;
     float* qn = static_cast<float*>(a.ws);
     float* S = qn + (size_t)rows * SEM_D;
+    // the threshold list (decode rows longer than the list; the long-row selection ranks
+    // it), when asked for: p_top <= SEM_LCAP / 4 (2 p_top expected in the list, room for
+    // the noise on both sides), rows the long-row selection takes.  Not the default: the
+    // selection's time is the ordering and expansion of the kept buckets, whatever it
+    // ranks, so the threshold's extra launch costs more than ranking the whole row here.
+    const long long n_max = (long long)a.NB * m, pos_max = (long long)a.NB * a.sp.n_cluster;
+    const bool use_list = sem_list_rows(a.NB, m, decode) && a.sp.select_mode != 0 && 4 * a.p_top <= SEM_LCAP &&
+                          a.sp.n_bmax <= 64 && (n_max + SPAN_B - 1) / SPAN_B * a.p_top <= SEM_KC;
+    SemList L{};
+    if (sem_list_rows(a.NB, m, decode)) {
+      L.keys = reinterpret_cast<unsigned long long*>(S + (size_t)rows * ld);
+      L.cnt = reinterpret_cast<int*>(L.keys + (size_t)rows * SEM_LCAP);
+      L.theta = reinterpret_cast<unsigned*>(L.cnt + rows);
+    }
+    const SemList none{};
     if (a.events) {
       const hipError_t er = hipEventRecord(static_cast<hipEvent_t>(a.events[0]), st);
       if (er != hipSuccess) return er;
@@ -1244,11 +1395,18 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
     if (a.NB == 0) {
       // an empty cache: nothing to score, every list is the sink and the window
     } else if (nqc == 1) {
+      if (use_list) {
+        hipLaunchKernelGGL(sem_theta_kernel, dim3(a.B), dim3(SEM_THR_NT), 0, st,
+                           static_cast<const unsigned short*>(a.q_idx), a.q_pos, a.n_q, i0, pg,
+                           static_cast<const unsigned short*>(a.cent), a.NB, m, a.sp.n_cluster, a.p_top,
+                           a.sp.select_mode == 2 ? 2 : a.sp.select_mode == 3 ? 3 : 0, L);  // 0: sampled
+      }
       const int bpw = 4;
       dim3 grid((a.NB + 4 * bpw - 1) / (4 * bpw), 1, a.B);
       hipLaunchKernelGGL(sem_score_decode_kernel, grid, dim3(256), 0, st,
                          static_cast<const unsigned short*>(a.q_idx), a.q_pos, a.n_q, i0, pg,
-                         static_cast<const unsigned short*>(a.cent), a.NB, m, a.sp.n_cluster, bpw, S, ld);
+                         static_cast<const unsigned short*>(a.cent), a.NB, m, a.sp.n_cluster, bpw, S, ld,
+                         use_list ? L : none);
     } else {
       hipLaunchKernelGGL(sem_qnorm_kernel, dim3((rows + 255) / 256), dim3(256), 0, st,
                          static_cast<const unsigned short*>(a.q_idx), a.n_q, i0, nqc, rows, qn);
@@ -1266,7 +1424,6 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
     // the chip twice, a variant held to 64 VGPRs (8 waves per SIMD) runs two
     // workgroups per compute unit
     const bool many = (long long)a.B * nqc >= 512;
-    const long long n_max = (long long)a.NB * m, pos_max = (long long)a.NB * a.sp.n_cluster;
     auto fits = [&](int nt, int C) { return sem_fits_registers(n_max, pos_max, a.sp.n_bmax, nt, C); };
     const bool paged = pg.bt || pg.pt;
     int split = 0;
@@ -1274,7 +1431,7 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
 #define LSA_SEM_SEL2(NT, C, MINW, PG, LG)                                                                      \
   hipLaunchKernelGGL((sem_select_kernel<NT, C, MINW, PG, LG>), dim3(nqc, a.B), dim3(NT), 0, st, S, ld, a.q_pos,  \
                      a.n_q, i0, nqc, a.table, a.offs, a.NB, m, a.sp.n_cluster, a.sp.n_bmax, a.k, a.p_top, a.n_sink, \
-                     a.n_w, W, a.idx, a.count, pg, split)
+                     a.n_w, W, a.idx, a.count, pg, split, LG && use_list ? L : none)
 #define LSA_SEM_SEL(NT, C, MINW)           \
   do {                                     \
     if (paged)                             \
@@ -1282,7 +1439,14 @@ hipError_t launch_sem_select(const SemSelectArgs& a, hipStream_t st) {
     else                                   \
       LSA_SEM_SEL1(NT, C, MINW, false);    \
   } while (0)
-    if (many && fits(1024, 4)) LSA_SEM_SEL(1024, 4, 8);
+    if (use_list && a.NB > 0) {
+      // the threshold list, ranked by the long-row selection (which takes the whole row
+      // where the list missed)
+      if (paged)
+        LSA_SEM_SEL2(1024, 16, 1, true, true);
+      else
+        LSA_SEM_SEL2(1024, 16, 1, false, true);
+    } else if (many && fits(1024, 4)) LSA_SEM_SEL(1024, 4, 8);
     else if (many && fits(1024, 8)) LSA_SEM_SEL(1024, 8, 8);
     else if (many && fits(512, 32)) LSA_SEM_SEL(512, 32, 4);
     else if (fits(1024, 4)) LSA_SEM_SEL(1024, 4, 1);

@@ -132,6 +132,76 @@ def test_select_matches_oracle(lsa, prm, k, p_top, n_sink, n_w):
             assert int(cnt[b, i]) == r["count"], f"count b={b} p={p}"
 
 
+def test_select_threshold_modes(lsa):
+    """Decode rows (one query per sequence) through the threshold list: a sampled
+    threshold, the buckets at or above it listed by the scan, the list ranked; rows whose
+    list falls short or overflows rank their whole row.  Rows of 5120 and 4480 buckets
+    (listed), of 3840 (at most the list: every bucket listed), inside the first block and
+    padding.  Every mode -- the list, the whole row, and both forced fall-backs -- gives
+    the same lists bit for bit, paged storage the same lists mapped to pool rows, and
+    sampled rows equal the oracle's."""
+    prm = (512, 4, 8, 32)
+    L = 80 * 512
+    P = 64
+    positions = [L - 1, 70 * 512 + 5, 60 * 512, 300, -1, 79 * 512 + 17]
+    B = len(positions)
+    wl = synthetic.Workload("sem_thr", B=B, n_q=1, L=L, q_pos0=L - 1, H_I=1, d_I=64, k=2048, H_q=16, semantic=True,
+                            p_top=512, n_sink=4)
+    inp = synthetic.semantic_inputs(wl, dev(), seed=31)
+    q_pos = torch.tensor(positions, dtype=torch.int32, device=dev()).view(B, 1)
+    cache = lsa.lsa_semantic_cache(inp["k_sem"], *prm)
+    res = {}
+    for mode in ("threshold", "row", "force_short", "force_overflow"):
+        print(f"[threshold modes: {mode}]", flush=True)
+        res[mode] = lsa.lsa_semantic_select(inp["q_sem"], q_pos, cache, 2048, 512, 4, 512, select=mode)
+    torch.cuda.synchronize()
+    for mode in ("threshold", "force_short", "force_overflow"):
+        assert torch.equal(res[mode][0], res["row"][0]), mode
+        assert torch.equal(res[mode][1], res["row"][1]), mode
+    # paged storage: the same lists as pool rows
+    NB, max_pages = L // 512, L // P
+    gen = torch.Generator().manual_seed(32)
+    n_pages = B * max_pages + 9
+    pt = torch.randperm(n_pages, generator=gen)[: B * max_pages].view(B, max_pages).to(torch.int32).to(dev())
+    n_bslots = B * NB + 3
+    bt = torch.randperm(n_bslots, generator=gen)[: B * NB].view(B, NB).to(torch.int32).to(dev())
+    paged = {"block_table": bt, "page_table": pt, "page_size": P, "n_slots": n_pages * P}
+    cache_p = lsa.lsa_semantic_cache(_to_pool(inp["k_sem"], pt, P, n_pages, 4), *prm, paged=paged, n_bslots=n_bslots)
+    idx_p, cnt_p = lsa.lsa_semantic_select(inp["q_sem"], q_pos, cache_p, 2048, 512, 4, 512, paged=paged,
+                                           select="threshold")
+    idx = res["threshold"][0]
+    mapped = torch.where(idx >= 0, pt.long().gather(1, (idx.clamp(min=0) // P).view(B, -1)).view_as(idx) * P
+                         + idx.clamp(min=0) % P, torch.full_like(idx, -1).long()).to(torch.int32)
+    assert torch.equal(idx_p, mapped) and torch.equal(cnt_p, res["threshold"][1])
+    for b in (0, 2, 3, 5):
+        oc = _oracle_cache(inp["k_sem"][b], prm, n_blocks=NB)
+        r = oracle.semantic_select_row(_f32(inp["q_sem"][b, 0]), oc, positions[b], 2048, 512, 4, 512)
+        assert np.array_equal(idx[b, 0].cpu().numpy(), r["J"]), f"b={b}"
+        assert int(res["threshold"][1][b, 0]) == r["count"]
+
+
+@pytest.mark.slow
+def test_select_threshold_long_rows(lsa):
+    """Decode rows of 70400 buckets (1100 blocks) through the threshold list, with a
+    sample of N / 8 buckets: the same lists as the whole-row ranking and both forced
+    fall-backs, bit for bit."""
+    prm = (512, 4, 8, 32)
+    L = 1100 * 512 + 7
+    positions = [L - 1, L - 5000, 900 * 512 + 11]
+    B = len(positions)
+    wl = synthetic.Workload("sem_thr_long", B=B, n_q=1, L=L, q_pos0=L - 1, H_I=1, d_I=64, k=2048, H_q=16,
+                            semantic=True, p_top=512, n_sink=4)
+    inp = synthetic.semantic_inputs(wl, dev(), seed=33)
+    q_pos = torch.tensor(positions, dtype=torch.int32, device=dev()).view(B, 1)
+    cache = lsa.lsa_semantic_cache(inp["k_sem"], *prm)
+    res = {mode: lsa.lsa_semantic_select(inp["q_sem"], q_pos, cache, 2048, 512, 4, 512, select=mode)
+           for mode in ("threshold", "row", "force_short", "force_overflow")}
+    torch.cuda.synchronize()
+    for mode in ("threshold", "force_short", "force_overflow"):
+        assert torch.equal(res[mode][0], res["row"][0]), mode
+        assert torch.equal(res[mode][1], res["row"][1]), mode
+
+
 def test_select_empty_cache(lsa):
     """A cache of no blocks (contexts shorter than one cluster block): every list is the
     sink and the window, as the oracle's."""

@@ -61,8 +61,13 @@ def test_semantic_validation_without_gpu():
     ok = P(512, 4, 8, 32)
     nb = ctypes.c_size_t(0)
     assert L.lsa_semantic_select_workspace_size(64, 1, 256, ctypes.byref(ok), ctypes.byref(nb)) == 0
+    # decode rows of 16384 buckets: the score row and the threshold list (4096 entries,
+    # count, threshold); prefill rows only the score row
+    assert nb.value == 64 * (64 * 4 + 256 * 64 * 4 + 4096 * 8 + 8)
+    assert L.lsa_semantic_select_workspace_size(1, 64, 256, ctypes.byref(ok), ctypes.byref(nb)) == 0
     assert nb.value == 64 * (64 * 4 + 256 * 64 * 4)
-    for bad in (P(512, 4, 8, 15), P(512, 3, 8, 32), P(512, 4, 7, 32), P(512, 8, 4, 32), P(0, 1, 1, 2)):
+    for bad in (P(512, 4, 8, 15), P(512, 3, 8, 32), P(512, 4, 7, 32), P(512, 8, 4, 32), P(0, 1, 1, 2),
+                P(512, 4, 8, 32, 4)):
         assert L.lsa_semantic_cluster(None, 1, 4096, 64, ctypes.byref(bad), 8, 0, 8, None, None, None, None) == -1
     assert L.lsa_semantic_cluster(None, 1, 4096, 128, ctypes.byref(ok), 8, 0, 8, None, None, None, None) == -2
     # 512 pool keys per block, or more than 64 buckets: beyond the compiled limits
@@ -99,14 +104,15 @@ def test_semantic_workspace_covers_span_candidates():
         return nb.value
 
     slack = 2 * (2048 + 1)
+    lst = 4096 * 8 + 8  # a decode row's threshold list, for rows of more than 4096 buckets
     up4 = lambda n: (n + 3) // 4 * 4
     # 32 buckets a block: 512 blocks put positions at the bitmap's end, 513 past it
-    assert row_bytes(P(512, 4, 16, 64), 512) == 4 * 64 + 4 * 512 * 32
-    assert row_bytes(P(512, 4, 16, 64), 513) == 4 * 64 + 4 * up4(513 * 32 + slack)
+    assert row_bytes(P(512, 4, 16, 64), 512) == 4 * 64 + 4 * 512 * 32 + lst
+    assert row_bytes(P(512, 4, 16, 64), 513) == 4 * 64 + 4 * up4(513 * 32 + slack) + lst
     # 64 buckets a block: 512 blocks fill the registers, 513 exceed them
-    assert row_bytes(P(512, 4, 8, 32), 512) == 4 * 64 + 4 * 512 * 64
-    assert row_bytes(P(512, 4, 8, 32), 513) == 4 * 64 + 4 * up4(513 * 64 + slack)
-    # buckets of up to 128 keys
+    assert row_bytes(P(512, 4, 8, 32), 512) == 4 * 64 + 4 * 512 * 64 + lst
+    assert row_bytes(P(512, 4, 8, 32), 513) == 4 * 64 + 4 * up4(513 * 64 + slack) + lst
+    # buckets of up to 128 keys (4 blocks: 256 buckets, no list)
     assert row_bytes(P(512, 4, 8, 128), 4) == 4 * 64 + 4 * up4(4 * 64 + slack)
 
 
