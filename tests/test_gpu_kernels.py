@@ -834,6 +834,26 @@ def test_forward_two_stage_small(lsa, T, bs, n_keep, k):
     err.check()
 
 
+def test_forward_two_stage_without_key_copy(lsa):
+    """A prefill-shaped two-stage forward whose workspace cannot hold the token stage's
+    interleaved key copy reads the key rows instead (in chunks of the rows that fit): the
+    same kept blocks, lists, counts and outputs bit for bit."""
+    T, bs, n_keep, k, n_q = 20000, 128, 64, 2048, 64
+    wl = synthetic.Workload("ts_nocopy", B=1, n_q=n_q, L=T, q_pos0=T - n_q, H_I=64, d_I=128, k=k, H_q=16,
+                            two_stage=True, block_size=bs, n_keep=n_keep)
+    inp, g = _inputs(wl, seed=8)
+    ref = lsa.lsa_forward(g, k_top=k, two_stage=True, block_size=bs, n_keep=n_keep)
+    small = (T + 63) // 64 * 64 * 128 - (1 << 16)
+    rows, split = lsa.lsa_forward_plan(g, k, small, two_stage=True, block_size=bs, n_keep=n_keep)
+    assert 0 < rows < n_q and split == lsa.lsa_forward_plan(g, k, 1 << 30, two_stage=True, block_size=bs,
+                                                             n_keep=n_keep)[1]
+    ws = torch.empty((small,), dtype=torch.uint8, device=dev())
+    res = lsa.lsa_forward(g, k_top=k, two_stage=True, block_size=bs, n_keep=n_keep, ws=ws)
+    torch.cuda.synchronize()
+    for name in ("kept", "idx", "count", "out", "lse"):
+        assert torch.equal(res[name], ref[name]), name
+
+
 def test_forward_two_stage_reduces_to_flat(lsa):
     """When every causal block is kept (own < n_keep) the two-stage lists equal the flat ones."""
     wl = synthetic.Workload("red", B=1, n_q=128, L=1024, q_pos0=896, H_I=64, d_I=128, k=200, H_q=16)

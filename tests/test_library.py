@@ -172,6 +172,29 @@ def test_forward_stages_listing():
     assert st == ["block_reps"] + ["block_prefilter", "index_scores", "topk", "sparse_attn"] * 2
 
 
+def test_two_stage_interleaved_key_copy_sizing():
+    """Prefill-shaped two-stage forwards (every index key read at least 8 times) reserve the
+    token stage's chunk-interleaved key copy -- ceil(L / 64) * 64 keys of d_I bytes per
+    sequence -- in the workspace; a workspace too small for the copy plans without it (in
+    chunks of the rows that fit) instead of failing; decode-shaped forwards never reserve it."""
+    import learned_top_sparse_amd as lsa
+    L = 20000
+    il = (L + 63) // 64 * 64 * 128
+    pre = _fake_inputs(1, 64, L)
+    ws = lsa.lsa_forward_workspace_size(pre, 2048, two_stage=True)
+    flat_blocks = lsa.lsa_forward_workspace_size(pre, 2048, two_stage=True, block_size=16, n_keep=6)  # no copy: bs % 64
+    assert ws >= il
+    assert lsa.lsa_forward_plan(pre, 2048, ws, two_stage=True)[0] == 64
+    small = il - (1 << 16)
+    assert small < ws
+    rows, _ = lsa.lsa_forward_plan(pre, 2048, small, two_stage=True)
+    assert 0 < rows < 64   # without the copy, in chunks
+    dec = _fake_inputs(4, 1, L)
+    ws_dec = lsa.lsa_forward_workspace_size(dec, 2048, two_stage=True)
+    assert ws_dec < il   # per-row buffers of 4 rows and the block cache only
+    assert flat_blocks > 0
+
+
 def _fake_paged(B, n_q, max_pages, page_size, n_pages, H_I=64, d_I=128, H_q=16, d=128):
     import torch
     inp = _fake_inputs(B, n_q, 1, H_I, d_I, H_q, d)
