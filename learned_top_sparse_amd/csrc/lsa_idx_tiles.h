@@ -86,4 +86,15 @@ __device__ __forceinline__ int relu_mad24(int x, int w, int acc) {
   return acc;
 }
 
+// acc + max(x, 0) * w in 64 bits as one v_mad_i64_i32 (signed 32 x 32 -> 64-bit product
+// plus a 64-bit add): the block scores' epilogue.  Written out because the compiler
+// forms the widened product from two v_mad_u64_u32 and register moves, doubling the
+// epilogue's VALU issue.  The instruction's carry-out goes to an SGPR pair nobody reads.
+__device__ __forceinline__ long long relu_mad64(int x, int w, long long acc) {
+  const int r = max(x, 0);
+  unsigned long long carry;
+  asm("v_mad_i64_i32 %0, %1, %2, %3, %0" : "+v"(acc), "=s"(carry) : "v"(w), "v"(r));
+  return acc;
+}
+
 }  // namespace lsa

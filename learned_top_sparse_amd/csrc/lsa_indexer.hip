@@ -857,7 +857,7 @@ __global__ __launch_bounds__(256, 2) void blk_scores_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int x = (ah[e] << 7) + al[e];
-            ps += (long long)wt[q][mt][e] * (long long)max(x, 0);
+            ps = relu_mad64(x, wt[q][mt][e], ps);
           }
         }
         part[4 * q + nt] = ps;
@@ -952,7 +952,7 @@ __global__ __launch_bounds__(256, 2) void blk_decode_kernel(
           al = mfma_i8(A[mt][ks], Bf[nt][1][ks], al);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ps += (long long)wt[mt][e] * (long long)max((ah[e] << 7) + al[e], 0);
+        for (int e = 0; e < 4; ++e) ps = relu_mad64((ah[e] << 7) + al[e], wt[mt][e], ps);
       }
       part[nt] = ps;
     }
