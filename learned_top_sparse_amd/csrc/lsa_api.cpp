@@ -516,6 +516,14 @@ FwdPlan plan_for(const lsa_forward_args* a, size_t ws_bytes, long long* rows) {
   return p;
 }
 
+// Chunks of equal size for n_rows rows in chunks of at most fit rows: as many chunks as
+// fit requires, none of them a short tail (a tail of a few rows would run the
+// decode-shaped kernels and pay every stage's launches for little work).
+long long balanced_rows(long long n_rows, long long fit) {
+  const long long n_chunks = (n_rows + fit - 1) / fit;
+  return (n_rows + n_chunks - 1) / n_chunks;
+}
+
 long long plan_rows(const lsa_forward_args* a, const FwdPlan& p, size_t ws_bytes) {
   const long long n_rows = total_rows(a);
   long long rows = a->chunk_rows > 0 ? std::min<long long>(a->chunk_rows, n_rows) : n_rows;
@@ -527,7 +535,7 @@ long long plan_rows(const lsa_forward_args* a, const FwdPlan& p, size_t ws_bytes
     if (chunk_bytes(a, p, mid) <= ws_bytes) lo = mid;
     else hi = mid - 1;
   }
-  return lo;
+  return balanced_rows(n_rows, lo);
 }
 
 }  // namespace
@@ -591,8 +599,9 @@ LSA_API lsa_status lsa_forward_workspace_size(const lsa_forward_args* a, size_t*
     return LSA_OK;
   }
   const FwdPlan p = plan_forward(a);
-  long long rows = a->chunk_rows > 0 ? a->chunk_rows : std::max<long long>(1, kChunkBudget / p.per_row);
-  rows = std::min(rows, total_rows(a));
+  const long long n_rows = total_rows(a);
+  long long rows = a->chunk_rows > 0 ? std::min<long long>(a->chunk_rows, n_rows)
+                                     : balanced_rows(n_rows, std::max<long long>(1, kChunkBudget / p.per_row));
   *bytes = chunk_bytes(a, p, rows);
   return LSA_OK;
 }

@@ -21,6 +21,17 @@ __device__ __forceinline__ int coarse_bin(int s) {
   return (gv ^ sign) + 4096;
 }
 
+// The same layout for 64-bit scores with 6 mantissa bits: u = s folded (s ^ sign),
+// shift = max(0, 57 - clz(u)), g = (shift << 6) + (u >> shift) < 3712 (u itself below 128,
+// 64 bins per power of two above), bin = 4096 + g for s >= 0 and 4095 - g below.
+__device__ __forceinline__ int coarse_bin64(long long s) {
+  const long long sign = s >> 63;
+  const unsigned long long u = (unsigned long long)(s ^ sign);
+  const int shift = max(0, 57 - (int)__clzll((long long)(u | 1ull)));
+  const int gv = (shift << 6) + (int)(u >> shift);
+  return (gv ^ (int)sign) + 4096;
+}
+
 // Bin b* holding the k-th best entry of `hist` (NBINS counters, LDS or global):
 // writes sh[4] = b*, sh[5] = entries in bins above b*, sh[6] = entries in b*.
 template <int NT>
@@ -294,6 +305,37 @@ __device__ __forceinline__ unsigned long long radix_cut64(const unsigned long lo
   return pref;
 }
 
+// Adds to the LDS bitmap bm the need_eq lowest positions set in eqm (nwd words each):
+// the keys equal to the cut that the keep takes.  All threads call, with eqm complete;
+// bm is complete when this returns.
+template <int NT>
+__device__ __forceinline__ void keep_first_ties(unsigned* bm, const unsigned* eqm, int nwd, int need_eq,
+                                                int* scan_tmp) {
+  const int tid = threadIdx.x;
+  // each thread takes whole words in order: the rank of its first equal key among all
+  const int wpt = (nwd + NT - 1) / NT;
+  int n_eq = 0;
+  for (int j = 0; j < wpt; ++j) {
+    const int wd = wpt * tid + j;
+    if (wd < nwd) n_eq += __popc(eqm[wd]);
+  }
+  int tot;
+  int before = block_exclusive_scan<NT>(n_eq, scan_tmp, &tot);
+  for (int j = 0; j < wpt; ++j) {
+    const int wd = wpt * tid + j;
+    if (wd >= nwd) break;
+    unsigned e = eqm[wd], keep = 0u;
+    while (e != 0u && before < need_eq) {
+      const unsigned low = e & (0u - e);
+      keep |= low;
+      e ^= low;
+      ++before;
+    }
+    bm[wd] |= keep;
+  }
+  __syncthreads();
+}
+
 // Marks, in an LDS bitmap of positions (bm: NT * C / 32 words), the keys kept by the cut:
 // key > T, and the first need_eq keys equal to T in position order (the lowest
 // positions win ties).  eqm: another NT * C / 32 words of LDS.  The bitmap is complete
@@ -319,28 +361,7 @@ __device__ __forceinline__ void mark_kept64(const unsigned long long (&key)[C], 
     else if (key[c] == T) atomicOr(&eqm[pos >> 5], 1u << (pos & 31));
   }
   __syncthreads();
-  // each thread takes whole words in order: the rank of its first equal key among all
-  constexpr int WPT = (NWD + NT - 1) / NT;
-  int n_eq = 0;
-  for (int j = 0; j < WPT; ++j) {
-    const int wd = WPT * tid + j;
-    if (wd < NWD) n_eq += __popc(eqm[wd]);
-  }
-  int tot;
-  int before = block_exclusive_scan<NT>(n_eq, scan_tmp, &tot);
-  for (int j = 0; j < WPT; ++j) {
-    const int wd = WPT * tid + j;
-    if (wd >= NWD) break;
-    unsigned e = eqm[wd], keep = 0u;
-    while (e != 0u && before < need_eq) {
-      const unsigned low = e & (0u - e);
-      keep |= low;
-      e ^= low;
-      ++before;
-    }
-    bm[wd] |= keep;
-  }
-  __syncthreads();
+  keep_first_ties<NT>(bm, eqm, NWD, need_eq, scan_tmp);
 }
 
 // Writes the marked positions in ascending order: emit(rank, pos) for each; returns

@@ -1603,19 +1603,108 @@ __global__ __launch_bounds__(NT) void list_topk_kernel(const int32_t* __restrict
   }
 }
 
+// The best n_sel of a row's n_sc > n_sel scored blocks by (int64 score desc, block asc),
+// written ascending to out[0..n_sel): one pass for the keys' max and min, one per 8-bit
+// radix digit below the prefix they share, one to rank the blocks equal to the cut and
+// one to write; every pass re-reads the row.  Returns n_sel.  All threads call.
+template <int NT>
+__device__ int blk_cut_passes(const long long* __restrict__ br, int n_sc, int n_sel, int32_t* __restrict__ out) {
+  constexpr int V = 4;
+  __shared__ int wcnt[2 * V * (NT / 64)];
+  __shared__ int scan_tmp[NT / 64 + 1];
+  __shared__ int h256[256];
+  __shared__ unsigned long long shu[4];
+  __shared__ int sh[4];
+  __shared__ int drop_from;
+  const int tid = threadIdx.x;
+  auto key64 = [&](int m) -> unsigned long long {
+    return (unsigned long long)br[m] ^ 0x8000000000000000ull;
+  };
+  // max / min of the keys -> bits they all share -> first digit to examine
+  unsigned long long mx = 0, mn = ~0ull;
+  for (int m = tid; m < n_sc; m += NT) {
+    const unsigned long long u = key64(m);
+    mx = u > mx ? u : mx;
+    mn = u < mn ? u : mn;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long a = __shfl_xor(mx, o), b = __shfl_xor(mn, o);
+    mx = a > mx ? a : mx;
+    mn = b < mn ? b : mn;
+  }
+  if (tid == 0) { shu[0] = 0; shu[1] = ~0ull; }
+  __syncthreads();
+  if ((tid & 63) == 0) {
+    atomicMax(&shu[0], mx);
+    atomicMin(&shu[1], mn);
+  }
+  __syncthreads();
+  mx = shu[0];
+  mn = shu[1];
+  __syncthreads();
+  int need = n_sel;
+  unsigned long long pref, pmask;
+  int shift;
+  if (mx == mn) {
+    pref = mx;
+    pmask = ~0ull;
+    shift = -8;
+  } else {
+    const int hb = 63 - __clzll((long long)(mx ^ mn));  // highest differing bit
+    shift = (hb / 8) * 8;
+    pmask = (shift + 8 >= 64) ? 0ull : ~((1ull << (shift + 8)) - 1ull);
+    pref = mx & pmask;
+  }
+  for (; shift >= 0; shift -= 8) {
+    for (int t = tid; t < 256; t += NT) h256[t] = 0;
+    __syncthreads();
+    for (int m = tid; m < n_sc; m += NT) {
+      const unsigned long long u = key64(m);
+      if ((u & pmask) == pref) atomicAdd(&h256[(int)((u >> shift) & 255ull)], 1);
+    }
+    __syncthreads();
+    const int c = tid < 256 ? h256[255 - tid] : 0;
+    int tot;
+    const int excl = block_exclusive_scan<NT>(c, scan_tmp, &tot);
+    if (tid < 256 && excl < need && excl + c >= need) {
+      sh[0] = 255 - tid;
+      sh[1] = excl;
+    }
+    __syncthreads();
+    need -= sh[1];
+    pref |= (unsigned long long)sh[0] << shift;
+    pmask |= 255ull << shift;
+    __syncthreads();
+  }
+  const unsigned long long T = pref;
+  const int need_eq = need;
+  // blocks equal to T beyond the first need_eq are dropped; rank them in order
+  if (tid == 0) drop_from = n_sc;
+  __syncthreads();
+  ordered_compact<NT, V>(n_sc, wcnt, [&](int m, int&) { return key64(m) == T; },
+                         [&](int r, int m, int) {
+                           if (r == need_eq) drop_from = m;
+                         });
+  const int df = drop_from;
+  return ordered_compact<NT, V>(
+      n_sc, wcnt,
+      [&](int m, int&) {
+        const unsigned long long u = key64(m);
+        return u > T || (u == T && m < df);
+      },
+      [&](int r, int m, int) {
+        if (r < n_sel) out[r] = m;
+      });
+}
+
 // Block keep of the two-stage indexer: own block + the best n_keep-1 earlier blocks
 // by (int64 score desc, block asc), ascending, -1 padded.
 template <int NT>
 __global__ __launch_bounds__(NT) void blk_select_kernel(const long long* __restrict__ bscores, long long ld,
                                                         const int32_t* __restrict__ q_pos, int n_blocks,
                                                         int bs, int n_keep, int32_t* __restrict__ kept) {
-  constexpr int NW = NT / 64;
   constexpr int V = 4;
-  __shared__ int wcnt[2 * V * NW];
-  __shared__ int scan_tmp[NW + 1];
-  __shared__ int h256[256];
-  __shared__ unsigned long long shu[4];
-  __shared__ int sh[4];
+  __shared__ int wcnt[2 * V * (NT / 64)];
   const long long row = blockIdx.x;
   const int tid = threadIdx.x;
   const int p = q_pos[row];
@@ -1627,93 +1716,139 @@ __global__ __launch_bounds__(NT) void blk_select_kernel(const long long* __restr
   const int own = p / bs;
   const int n_sc = min(own, n_blocks);  // scored earlier blocks
   const long long* br = bscores + row * ld;
-  auto key64 = [&](int m) -> unsigned long long {
-    return (unsigned long long)br[m] ^ 0x8000000000000000ull;
-  };
   const int n_sel = min(n_keep - 1, n_sc);
   int written = 0;
-  if (n_sel >= n_sc) {
+  if (n_sel >= n_sc)
     written = ordered_compact<NT, V>(n_sc, wcnt, [&](int, int&) { return true; },
                                      [&](int r, int m, int) {
                                        if (r < n_keep - 1) out[r] = m;
                                      });
-  } else if (n_sel > 0) {
-    // max / min of the keys -> bits they all share -> first digit to examine
-    unsigned long long mx = 0, mn = ~0ull;
-    for (int m = tid; m < n_sc; m += NT) {
-      const unsigned long long u = key64(m);
-      mx = u > mx ? u : mx;
-      mn = u < mn ? u : mn;
-    }
-    for (int o = 32; o > 0; o >>= 1) {
-      const unsigned long long a = __shfl_xor(mx, o), b = __shfl_xor(mn, o);
-      mx = a > mx ? a : mx;
-      mn = b < mn ? b : mn;
-    }
-    if (tid == 0) { shu[0] = 0; shu[1] = ~0ull; }
+  else if (n_sel > 0)
+    written = blk_cut_passes<NT>(br, n_sc, n_sel, out);
+  written = min(written, n_keep - 1);
+  if (tid == 0) out[written] = own;
+  for (int t = written + 1 + tid; t < n_keep; t += NT) out[t] = -1;
+}
+
+// Block keep of long prefill-shaped rows (up to BLK_LONG_MAXB blocks): the result of
+// blk_select_kernel from two reads of the row instead of about eight.  The first counts
+// the keys per coarse bin (coarse_bin64, monotone in the score) and finds the bin b*
+// holding the cut; the second marks the blocks of higher bins in an LDS bitmap of
+// positions and gathers b*'s members (key, position) into LDS, where the exact cut, the
+// ties it keeps (lowest positions) and the bitmap's remaining bits are settled; the
+// bitmap is then written out in position order.  Rows of up to MAXB blocks; a row whose
+// b* holds more than MCAP members (heavy ties) takes blk_cut_passes instead.
+// Measured on MI355X: rows of 1024 blocks are faster with blk_select_kernel (its
+// passes hit the cache), rows of 4K-16K blocks with the 256-thread form (three
+// workgroups per compute unit), longer rows with the 1024-thread form.
+constexpr int BLK_LONG_MAXB = 131072;
+constexpr int BLK_MED_MIN = 4096, BLK_MED_MAXB = 16384;
+template <int NT, int MAXB, int MCAP>
+__global__ __launch_bounds__(NT) void blk_select_long_kernel(const long long* __restrict__ bscores, long long ld,
+                                                             const int32_t* __restrict__ q_pos, int n_blocks,
+                                                             int bs, int n_keep, int32_t* __restrict__ kept) {
+  constexpr int V = 8, MC = MCAP / NT, NWD = MAXB / 32;
+  static_assert(MCAP % NT == 0 && NBINS % NT == 0 && MC <= 32, "whole member and bin ranges per thread");
+  __shared__ int hist[NBINS];
+  __shared__ unsigned bm[NWD], eqm[NWD];
+  __shared__ unsigned long long mkey[MCAP];
+  __shared__ int mpos[MCAP];
+  __shared__ int scan_tmp[NT / 64 + 1], sh[8], mcnt;
+  __shared__ unsigned long long shu[2];
+  const long long row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int p = q_pos[row];
+  int32_t* out = kept + row * (long long)n_keep;
+  if (p < 0) {
+    for (int t = tid; t < n_keep; t += NT) out[t] = -1;
+    return;
+  }
+  const int own = p / bs;
+  const int n_sc = min(own, n_blocks);  // scored earlier blocks
+  const int n_sel = min(n_keep - 1, n_sc);
+  const long long* br = bscores + row * ld;
+  int written;
+  if (n_sel >= n_sc) {
+    for (int m = tid; m < n_sc; m += NT) out[m] = m;
+    written = n_sc;
+  } else {
+    for (int t = tid; t < NBINS; t += NT) hist[t] = 0;
     __syncthreads();
-    if ((tid & 63) == 0) {
-      atomicMax(&shu[0], mx);
-      atomicMin(&shu[1], mn);
+    for (int base = 0; base < n_sc; base += V * NT) {
+      long long s[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int m = base + v * NT + tid;
+        s[v] = m < n_sc ? br[m] : 0ll;
+      }
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (base + v * NT + tid < n_sc) atomicAdd(&hist[coarse_bin64(s[v])], 1);
     }
     __syncthreads();
-    mx = shu[0];
-    mn = shu[1];
-    __syncthreads();
-    int need = n_sel;
-    unsigned long long pref, pmask;
-    int shift;
-    if (mx == mn) {
-      pref = mx;
-      pmask = ~0ull;
-      shift = -8;
+    find_cut_bin<NT>(hist, n_sel, scan_tmp, sh);
+    const int bstar = sh[4], cnt = sh[6];
+    const int need = n_sel - sh[5];  // 1 .. cnt of b*'s members are kept
+    if (cnt <= MCAP) {
+      const int nwd = (n_sc + 31) >> 5;
+      for (int t = tid; t < nwd; t += NT) eqm[t] = 0u;
+      if (tid == 0) mcnt = 0;
+      __syncthreads();
+      for (int base = 0; base < n_sc; base += V * NT) {
+        long long s[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const int m = base + v * NT + tid;
+          s[v] = m < n_sc ? br[m] : 0ll;
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const int m = base + v * NT + tid;
+          const int b = m < n_sc ? coarse_bin64(s[v]) : -1;
+          // the wave's 64 positions are two whole bitmap words, each written once
+          const unsigned long long gt = __ballot(b > bstar);
+          const int w0 = (base + v * NT + wave * 64) >> 5;
+          if (lane < 2 && w0 + lane < nwd) bm[w0 + lane] = (unsigned)(gt >> (32 * lane));
+          const unsigned long long in = __ballot(b == bstar);
+          if (in != 0ull) {
+            int slot0 = 0;
+            if (lane == 0) slot0 = atomicAdd(&mcnt, __popcll(in));
+            slot0 = __shfl(slot0, 0);
+            if (b == bstar) {
+              const int j = slot0 + lanes_below(in);
+              mkey[j] = (unsigned long long)s[v] ^ 0x8000000000000000ull;
+              mpos[j] = m;
+            }
+          }
+        }
+      }
+      __syncthreads();
+      unsigned long long key[MC];
+      int pos[MC];
+      unsigned vmask = 0u;
+#pragma unroll
+      for (int c = 0; c < MC; ++c) {
+        const int j = c * NT + tid;
+        key[c] = j < cnt ? mkey[j] : 0ull;
+        pos[c] = j < cnt ? mpos[j] : 0;
+        vmask |= (j < cnt ? 1u : 0u) << c;
+      }
+      int need_eq;
+      const unsigned long long T = radix_cut64<NT, MC>(key, vmask, need, hist, scan_tmp, sh, shu, &need_eq);
+#pragma unroll
+      for (int c = 0; c < MC; ++c) {
+        if (!((vmask >> c) & 1u)) continue;
+        if (key[c] > T) atomicOr(&bm[pos[c] >> 5], 1u << (pos[c] & 31));
+        else if (key[c] == T) atomicOr(&eqm[pos[c] >> 5], 1u << (pos[c] & 31));
+      }
+      __syncthreads();
+      keep_first_ties<NT>(bm, eqm, nwd, need_eq, scan_tmp);
+      written = emit_marked<NT>(bm, nwd, scan_tmp, [&](int r, int q) {
+        if (r < n_sel) out[r] = q;
+      });
     } else {
-      const int hb = 63 - __clzll((long long)(mx ^ mn));  // highest differing bit
-      shift = (hb / 8) * 8;
-      pmask = (shift + 8 >= 64) ? 0ull : ~((1ull << (shift + 8)) - 1ull);
-      pref = mx & pmask;
+      written = blk_cut_passes<NT>(br, n_sc, n_sel, out);
     }
-    for (; shift >= 0; shift -= 8) {
-      for (int t = tid; t < 256; t += NT) h256[t] = 0;
-      __syncthreads();
-      for (int m = tid; m < n_sc; m += NT) {
-        const unsigned long long u = key64(m);
-        if ((u & pmask) == pref) atomicAdd(&h256[(int)((u >> shift) & 255ull)], 1);
-      }
-      __syncthreads();
-      const int c = tid < 256 ? h256[255 - tid] : 0;
-      int tot;
-      const int excl = block_exclusive_scan<NT>(c, scan_tmp, &tot);
-      if (tid < 256 && excl < need && excl + c >= need) {
-        sh[0] = 255 - tid;
-        sh[1] = excl;
-      }
-      __syncthreads();
-      need -= sh[1];
-      pref |= (unsigned long long)sh[0] << shift;
-      pmask |= 255ull << shift;
-      __syncthreads();
-    }
-    const unsigned long long T = pref;
-    const int need_eq = need;
-    // blocks equal to T beyond the first need_eq are dropped; rank them in order
-    __shared__ int drop_from;
-    if (tid == 0) drop_from = n_sc;
-    __syncthreads();
-    ordered_compact<NT, V>(n_sc, wcnt, [&](int m, int&) { return key64(m) == T; },
-                           [&](int r, int m, int) {
-                             if (r == need_eq) drop_from = m;
-                           });
-    const int df = drop_from;
-    written = ordered_compact<NT, V>(
-        n_sc, wcnt,
-        [&](int m, int&) {
-          const unsigned long long u = key64(m);
-          return u > T || (u == T && m < df);
-        },
-        [&](int r, int m, int) {
-          if (r < n_keep - 1) out[r] = m;
-        });
   }
   written = min(written, n_keep - 1);
   if (tid == 0) out[written] = own;
@@ -2072,6 +2207,17 @@ hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st) {
     // few long rows (decode): the row's scores in registers of one workgroup
     hipLaunchKernelGGL((blk_keep_rows_kernel<1024, 32>), dim3((unsigned)rows), dim3(1024), 0, st, a.bscores, a.ld,
                        a.q_pos, a.n_blocks, a.block_size, a.n_keep, a.kept);
+    return hipGetLastError();
+  }
+  if (a.n_blocks > BLK_MED_MAXB && a.n_blocks <= BLK_LONG_MAXB) {
+    // long prefill-shaped rows: two reads of each row
+    hipLaunchKernelGGL((blk_select_long_kernel<1024, BLK_LONG_MAXB, 4096>), dim3((unsigned)rows), dim3(1024), 0, st,
+                       a.bscores, a.ld, a.q_pos, a.n_blocks, a.block_size, a.n_keep, a.kept);
+    return hipGetLastError();
+  }
+  if (a.n_blocks > BLK_MED_MIN && a.n_blocks <= BLK_MED_MAXB) {
+    hipLaunchKernelGGL((blk_select_long_kernel<256, BLK_MED_MAXB, 1024>), dim3((unsigned)rows), dim3(256), 0, st,
+                       a.bscores, a.ld, a.q_pos, a.n_blocks, a.block_size, a.n_keep, a.kept);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(blk_select_kernel<256>, dim3((unsigned)rows), dim3(256), 0, st, a.bscores, a.ld,

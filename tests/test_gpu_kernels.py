@@ -258,6 +258,60 @@ def test_block_reps_and_prefilter(lsa, case):
         assert np.array_equal(kept[i], padded), f"kept row {i}"
 
 
+@pytest.mark.parametrize("T", [24576, 98304])
+@pytest.mark.parametrize("mode", ["random", "signed", "ties", "zeros", "bigw", "extreme"])
+def test_block_prefilter_long_rows(lsa, mode, T):
+    """Prefill-shaped rows over more than 4096 blocks (the keep that reads each row's
+    scores twice: a coarse histogram, then the cut's bin gathered into LDS; 6144 blocks
+    take its 256-thread form, 24576 its 1024-thread form).  Kept blocks equal the
+    oracle's for rows whose cut bin holds a few members (random), scores of both signs
+    (signed weights), heavily tied scores (q, k in {-1, 0, 1}), and every score equal
+    (rows whose tie outgrows the LDS member list then take the multi-pass fallback,
+    shorter ones settle all their ties in LDS).  Block scores equal the oracle's at
+    the extremes of their int64 sums too: q = k = -128 with w = 16 over 64 heads (every
+    block 2^33) and weights near 2^20."""
+    bs, n_keep, d = 4, 256, 128
+    H = 64 if mode == "extreme" else 8
+    rng = np.random.default_rng({"random": 1, "signed": 2, "ties": 3, "zeros": 4, "bigw": 5, "extreme": 6}[mode] + T)
+    n_q = 24
+    vr = 1 if mode == "ties" else 64
+    q = rng.integers(-vr, vr + 1, size=(1, n_q, H, d)).astype(np.int8)
+    if mode == "zeros":
+        q[:] = 0
+    k = rng.integers(-vr, vr + 1, size=(1, T, d)).astype(np.int8)
+    if mode == "extreme":
+        q[:] = -128
+        k[:] = -128
+    if mode == "signed":
+        w = rng.integers(-16, 17, size=H)
+    elif mode == "bigw":
+        w = rng.integers(2 ** 20, 2 ** 21, size=H)
+    elif mode == "extreme":
+        w = np.full(H, 16)
+    else:
+        w = rng.integers(1, 17, size=H)
+    w = w.astype(np.int32)
+    pos = np.sort(rng.integers(4 * 4096, T, size=n_q)).astype(np.int32)
+    pos[:4] = [0, 4 * n_keep - 1, 4 * n_keep + 5, 4 * 3000 + 1]  # all kept, one to cut, a short row
+    pos[-1] = T - 1
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+    reps = lsa.lsa_block_reps(t(k), bs, T // bs)
+    R = oracle.block_reps(k[0], bs)
+    kept, bsc = lsa.lsa_block_prefilter(t(q), reps, t(w), t(pos.reshape(1, n_q)), bs, n_keep, return_scores=True)
+    kept, bsc = kept.cpu().numpy()[0], bsc.cpu().numpy()[0]
+    for i in range(n_q):
+        want, want_bs = oracle.block_keep(q[0, i], R, w, int(pos[i]), bs, n_keep)
+        own = int(pos[i]) // bs
+        assert np.array_equal(bsc[i, :own], want_bs), f"block scores row {i}"
+        padded = np.full(n_keep, -1)
+        padded[: want.size] = want
+        assert np.array_equal(kept[i], padded), f"kept row {i} (p = {pos[i]})"
+    if mode == "signed":
+        assert (bsc < 0).any() and (bsc > 0).any()
+    if mode == "extreme":
+        assert bsc[-1, 0] == H * 16 * d * 128 * 512
+
+
 # ----------------------------------------------------------------------------- attention
 def _attn_inputs(B, n_q, L, H, seed):
     g = torch.Generator().manual_seed(seed)
