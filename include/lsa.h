@@ -260,6 +260,14 @@ typedef struct lsa_forward_args {
        top-k is taken from those; a row whose kept entries fall short of k_top or
        overflow 4*k_top goes through the score table instead.  Other rows use the
        score table.  The results are the same either way.
+     Block modes (two_stage > 0, chunks of at least 8 queries per sequence) choose the
+     block keep the same way: with AUTO, rows over max(8*n_keep, 16384) blocks (n_keep
+     from 257 to 2048, at most 131072 blocks) take the thresholded keep -- every
+     (2*(n_keep-1)/32)-th block scored as a sample gives each row a threshold, the
+     block scan lists the blocks that reach it, and the kept blocks are taken from the
+     list; a row whose list falls short of n_keep-1 or overflows 4*n_keep is scored
+     again into the block score table.  Other rows use the table.  The results are the
+     same either way.
      LSA_SELECT_TABLE (1): every row through the score table.
      LSA_SELECT_FORCE_SHORT (2), LSA_SELECT_FORCE_OVERFLOW (3): as AUTO, but every
        thresholded row's threshold is set above (below) all of its scores, so every

@@ -130,10 +130,19 @@ LSA_API lsa_status lsa_block_prefilter_workspace_size(int32_t B, int32_t n_q, in
 // block scores + keep for rows whose limbs are already in `limbs`
 // Block scores and kept blocks.  scores_private: bscores is workspace nobody reads back,
 // so decode-shaped rows may keep span candidates there instead of the score table.
+// Thresholded keep of a prefill-shaped chunk (BlkThr): where its workspace was carved.
+struct BlkThrWs {
+  long long* samp = nullptr;  // sampled scores, ld_s per row
+  long long ld_s = 0;
+  lsa::BlkThr thr{};
+  int stride = 1, row_min = 0, mode = 0;
+};
+
 static lsa_status run_prefilter(const int8_t* q_idx, const int8_t* limbs, const int32_t* w, int32_t w_per_query,
                                 const int32_t* q_pos, int32_t B, int32_t n_q, int32_t n_blocks, int32_t H_I,
                                 int32_t d_I, int32_t block_size, int32_t n_keep, int32_t* kept,
-                                long long* bscores, hipStream_t s, bool scores_private = false) {
+                                long long* bscores, hipStream_t s, bool scores_private = false,
+                                const BlkThrWs* tw = nullptr) {
   lsa::BlkCand cand{};
   if (scores_private && !lsa::blk_cand_layout((long long)B * n_q, n_q, n_blocks, n_keep, bscores,
                                               (size_t)B * n_q * n_blocks * 8, &cand))
@@ -155,8 +164,31 @@ static lsa_status run_prefilter(const int8_t* q_idx, const int8_t* limbs, const 
   ba.ld = n_blocks;
   ba.span = 512;
   ba.cand = cand;
+  const long long rows = (long long)B * n_q;
+  const bool thr = tw != nullptr && n_q >= 8 && cand.key == nullptr;
+  if (thr) {
+    // sample -> thresholds -> scan appending to the lists (table rows to the table)
+    lsa::BlkArgs sm = ba;
+    sm.stride = tw->stride;
+    sm.bscores = tw->samp;
+    sm.ld = tw->ld_s;
+    if (lsa::launch_block_scores(sm, s) != hipSuccess ||
+        lsa::launch_blk_thresholds(tw->samp, tw->ld_s, q_pos, B, n_q, n_blocks, block_size, n_keep, tw->stride,
+                                   tw->row_min, tw->mode, tw->thr, s) != hipSuccess)
+      return LSA_ERR_HIP;
+    ba.mode = 1;
+    ba.thr = tw->thr;
+  }
   hipError_t e = lsa::launch_block_scores(ba, s);
   if (e != hipSuccess) return LSA_ERR_HIP;
+  if (thr) {
+    // the list rows' keep; rows whose list fell short or overflowed are scored again
+    // into the table, which then serves them and the table rows
+    if (lsa::launch_blk_list_keep(q_pos, B, n_q, n_blocks, block_size, n_keep, tw->thr, kept, s) != hipSuccess)
+      return LSA_ERR_HIP;
+    ba.mode = 2;
+    if (lsa::launch_block_scores(ba, s) != hipSuccess) return LSA_ERR_HIP;
+  }
   lsa::BlkSelArgs sa{};
   sa.bscores = bscores;
   sa.ld = n_blocks;
@@ -168,6 +200,7 @@ static lsa_status run_prefilter(const int8_t* q_idx, const int8_t* limbs, const 
   sa.n_keep = n_keep;
   sa.kept = kept;
   sa.cand = cand;
+  sa.rstate = thr ? tw->thr.rstate : nullptr;
   return hip_status(lsa::launch_block_select(sa, s));
 }
 
@@ -433,6 +466,31 @@ size_t thr_ws_bytes(const lsa_forward_args* a, long long rows) {
          2 * align_up((size_t)rows * cap * 4);
 }
 
+// Thresholded block keep (block modes, prefill-shaped chunks): rows of more than
+// blk_thr_row_min(n_keep) blocks, where the sample costs at most 1/BLK_THR_MIN_STRIDE
+// of the scan and fits the threshold kernel.
+bool blk_thr_applies(const lsa_forward_args* a) {
+  if (!a->two_stage || a->select_mode == LSA_SELECT_TABLE || a->n_q < 8 || a->n_keep < 2 || a->n_keep > 2048)
+    return false;
+  const int nb = a->L_max / a->block_size, st = lsa::blk_thr_stride(a->n_keep);
+  return st >= lsa::BLK_THR_MIN_STRIDE && nb > lsa::blk_thr_row_min(a->n_keep) && nb <= lsa::BLK_THR_MAX_B &&
+         (nb + st - 1) / st <= lsa::BLK_THR_MAX_SAMPLES;
+}
+// sampled scores per row (leading dimension, a multiple of 8: 64-byte rows)
+int64_t blk_thr_ld(const lsa_forward_args* a) {
+  const int st = lsa::blk_thr_stride(a->n_keep);
+  return ((int64_t)(a->L_max / a->block_size + st - 1) / st + 7) / 8 * 8;
+}
+// its workspace for a chunk of `rows` rows: samples, threshold, state, count, lists, and
+// the fallback tile marks, list and count (a tile per row at most)
+size_t blk_thr_ws_bytes(const lsa_forward_args* a, long long rows) {
+  if (!blk_thr_applies(a)) return 0;
+  const size_t cap = (size_t)lsa::blk_thr_cap(a->n_keep);
+  return align_up((size_t)rows * blk_thr_ld(a) * 8) + align_up((size_t)rows * 8) + 2 * align_up((size_t)rows * 4) +
+         align_up((size_t)rows * cap * 4) + align_up((size_t)rows * cap * 8) + 2 * align_up((size_t)rows * 4) +
+         align_up(4);
+}
+
 // Two-stage rows whose kept slots fit one workgroup's LDS: the token stage and its top-k
 // run as one kernel, with no token score table.
 bool kept_fused(const lsa_forward_args* a) {
@@ -457,6 +515,7 @@ FwdPlan plan_forward(const lsa_forward_args* a, bool with_il = true) {
     // the token stage's score rows (pooled blocks have none)
     p.ld = (a->two_stage == 2 || kept_fused(a)) ? 0 : (int64_t)a->n_keep * a->block_size;
     p.per_row = p.ld * 4 + (long long)p.n_blocks * 8 + (a->kept_blocks ? 0 : (long long)a->n_keep * 4) + 64;
+    if (blk_thr_applies(a)) p.per_row += blk_thr_ld(a) * 8 + 24 + (long long)lsa::blk_thr_cap(a->n_keep) * 12;
     // the block-key cache, unless the caller keeps one
     p.fixed = a->block_keys ? 0 : align_up((size_t)a->B * p.n_blocks * 2 * a->d_I);
     p.il_bytes = with_il && kept_il(a) ? align_up(lsa::kidx_interleave_bytes(a->B, a->L_max, a->d_I)) : 0;
@@ -494,6 +553,7 @@ size_t chunk_bytes(const lsa_forward_args* a, const FwdPlan& p, long long rows) 
   s += attn_ws_bytes(rows, a->H_q, a->d, split);
   if (!a->two_stage) s += align_up(topk_ws_for(a, rows));
   s += thr_ws_bytes(a, rows);
+  s += blk_thr_ws_bytes(a, rows);
   return s;
 }
 
@@ -691,6 +751,34 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
     thr.lscore = reinterpret_cast<int32_t*>(base + off);
     off += align_up((size_t)rows * thr.cap * 4);
   }
+  // thresholded block keep: sampled block scores, per-row threshold / state / count, lists
+  BlkThrWs bt;
+  const bool use_bt = blk_thr_applies(a);
+  if (use_bt) {
+    bt.stride = lsa::blk_thr_stride(a->n_keep);
+    bt.row_min = lsa::blk_thr_row_min(a->n_keep);
+    bt.mode = a->select_mode == LSA_SELECT_FORCE_SHORT ? 1 : a->select_mode == LSA_SELECT_FORCE_OVERFLOW ? 2 : 0;
+    bt.ld_s = blk_thr_ld(a);
+    bt.thr.cap = lsa::blk_thr_cap(a->n_keep);
+    bt.samp = reinterpret_cast<long long*>(base + off);
+    off += align_up((size_t)rows * bt.ld_s * 8);
+    bt.thr.theta = reinterpret_cast<long long*>(base + off);
+    off += align_up((size_t)rows * 8);
+    bt.thr.rstate = reinterpret_cast<int32_t*>(base + off);
+    off += align_up((size_t)rows * 4);
+    bt.thr.cnt = reinterpret_cast<int32_t*>(base + off);
+    off += align_up((size_t)rows * 4);
+    bt.thr.lblk = reinterpret_cast<int32_t*>(base + off);
+    off += align_up((size_t)rows * bt.thr.cap * 4);
+    bt.thr.lscore = reinterpret_cast<long long*>(base + off);
+    off += align_up((size_t)rows * bt.thr.cap * 8);
+    bt.thr.tflag = reinterpret_cast<int32_t*>(base + off);
+    off += align_up((size_t)rows * 4);
+    bt.thr.tlist = reinterpret_cast<int32_t*>(base + off);
+    off += align_up((size_t)rows * 4);
+    bt.thr.tcnt = reinterpret_cast<int32_t*>(base + off);
+    off += align_up(4);
+  }
 
   const int32_t d_I = a->d_I, H_I = a->H_I, H_q = a->H_q, d = a->d, L = a->L_max, kt = a->k_top;
   // one split count for every chunk, so no chunk needs more attention workspace than sized
@@ -737,7 +825,8 @@ LSA_API lsa_status lsa_forward(const lsa_forward_args* a, void* ws, size_t ws_by
     if (a->two_stage) {
       int32_t* kout = a->kept_blocks ? a->kept_blocks + r0 * a->n_keep : kept_ws;
       lsa_status st2 = run_prefilter(qi, limbs + (long long)b0 * p.n_blocks * 2 * d_I, wq, a->w_per_query, qp, nb,
-                                     ni, p.n_blocks, H_I, d_I, a->block_size, a->n_keep, kout, bsc, s, true);
+                                     ni, p.n_blocks, H_I, d_I, a->block_size, a->n_keep, kout, bsc, s, true,
+                                     use_bt ? &bt : nullptr);
       if (st2 != LSA_OK) return st2;
       kept = kout;
       ia.kept = kept;

@@ -752,131 +752,218 @@ __global__ void blk_cache_kernel(const int8_t* __restrict__ k_idx, int L_max, in
 // 2*D bytes; q.r = 128*(q.hi) + (q.lo) is exact in int32 (|q.r| < 2^29), then
 // ReLU and the weighted head sum accumulate in int64.  Block m is scored for a
 // query iff m < floor(q_pos / bs) (its own block is never scored).
-// Grid: x = 8 * ceil(n_qtiles / 8) * n_spans (the flat kernel's XCD-aware order), y = B.
-template <int D, int MT, int QW>
+// stride > 1 scores only blocks 0, stride, 2 stride, ... (column m of a row holds
+// block m * stride): the thresholded keep's sample.  MODE 0 writes every scored block
+// to the table.  MODE 1 (thresholded scan) writes table rows (state 1) to the table and
+// appends each list row's blocks whose score reaches its threshold to its list: one
+// atomic per wave, query and tile reserves the slots, and the tile's entries are
+// written after the next tile's products, so the atomic's round trip hides behind
+// them.  MODE 2 scores the tiles of the fallback list (tiles holding a row in state 2)
+// and writes only those rows, on a grid of BLK_THR_FB_SLOTS x n_spans workgroups.
+// Grid (MODE 0, 1): x = 8 * ceil(n_qtiles / 8) * n_spans (the flat kernel's XCD-aware
+// order), y = B.
+template <int D, int MT, int QW, int MODE>
 __global__ __launch_bounds__(256, 2) void blk_scores_kernel(
     const int8_t* __restrict__ q_idx, const int8_t* __restrict__ limbs, const int32_t* __restrict__ w,
     int w_per_query, const int32_t* __restrict__ q_pos, int n_q, int n_blocks, int L_max, int H_I,
-    int bs, int span, int n_spans, int n_qtiles, long long* __restrict__ bscores, long long ld) {
+    int bs, int span, int n_spans, int n_qtiles, long long* __restrict__ bscores, long long ld, int stride,
+    BlkThr thr) {
   static_assert(QW == 2, "reduce_scatter8_64 assumes two queries per wave");
   constexpr int KS = D / 64, KT = 64, QT = 4 * QW, RB = 2 * D, CH = RB / 16;
   constexpr int LOADS = KT * CH / 256;
+  static_assert(QT == BLK_THR_QT, "the fallback list's tiles");
   __shared__ __attribute__((aligned(16))) int8_t tile[2][KT * RB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
-  const int b = blockIdx.y;
-  // Workgroups are dealt to the 8 XCDs in turn (grid.x is a multiple of 8, so
-  // workgroup x runs on XCD x % 8).  XCD x takes the query tiles x, x + 8, ...
-  // (longest first, interleaved so causal work balances over the XCDs) and walks them
-  // span by span: the workgroups resident on one XCD at a time read the same span of
-  // keys, which its L2 then serves to all of them.
-  const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
-  const int per_xcd = (n_qtiles + 7) >> 3;
-  const int s = kx / per_xcd;
-  const int qt_rev = (kx - s * per_xcd) * 8 + xcd;
-  if (qt_rev >= n_qtiles) return;
-  const int qt = n_qtiles - 1 - qt_rev;
-  const int i0 = qt * QT;
-  const int32_t* qp = q_pos + (long long)b * n_q;
+  const int nv = (n_blocks + stride - 1) / stride;  // columns: blocks 0, stride, ...
+  // columns [0, own_col(p)) are scored for a query at position p
+  auto own_col = [&](int pp) { return (min(pp / bs, n_blocks) + stride - 1) / stride; };
 
-  int omax = 0;  // blocks [0, omax) are scored by some query of the tile
+  // query tile qt of sequence b over span s of columns
+  auto body = [&](int b, int qt, int s) {
+    const int i0 = qt * QT;
+    const int32_t* qp = q_pos + (long long)b * n_q;
+    // MODE 2: rows in state 2 only
+    auto takes = [&](int i) { return MODE != 2 || thr.rstate[(long long)b * n_q + i] == 2; };
+    int omax = 0;  // columns [0, omax) are scored for some query of the tile
 #pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    const int i = i0 + t;
-    if (i < n_q) {
-      const int pp = min(qp[i], L_max - 1);
-      if (pp >= 0) omax = max(omax, min(pp / bs, n_blocks));
-    }
-  }
-  const int m_begin = s * span;
-  if (m_begin >= omax) return;
-  const int m_end = min(m_begin + span, omax);
-
-  v4i A[QW][MT][KS];
-  int wt[QW][MT][4];
-  int own[QW];
-  long long srow[QW];
-#pragma unroll
-  for (int q = 0; q < QW; ++q) {
-    const int i = i0 + wave * QW + q;
-    const bool valid = i < n_q;
-    const long long row = (long long)b * n_q + (valid ? i : 0);
-    const int pp = valid ? min(qp[i], L_max - 1) : -1;
-    own[q] = pp >= 0 ? min(pp / bs, n_blocks) : 0;
-    srow[q] = row * ld;
-    load_query<D, MT>(q_idx, w, w_per_query, row, H_I, valid, A[q], wt[q]);
-  }
-
-  const int8_t* lb = limbs + (long long)b * n_blocks * RB;
-  v4i stage[LOADS];
-  auto gload = [&](int m0) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int cid = tid + 256 * u, r = cid / CH, c = cid % CH, m = min(m0 + r, n_blocks - 1);
-      stage[u] = *(const v4i*)(lb + (long long)m * RB + 16 * c);
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int cid = tid + 256 * u, r = cid / CH, c = cid % CH;
-      *(v4i*)(&tile[buf][r * RB + 16 * swz<RB>(r, c)]) = stage[u];
-    }
-  };
-
-  const int n_tiles = (m_end - m_begin + KT - 1) / KT;
-  gload(m_begin);
-  swrite(0);
-  __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const int m0 = m_begin + t * KT;
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) gload(m0 + KT);
-    long long part[8];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      v4i Bh[KS], Bl[KS];
-      const int r = 16 * nt + r16;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int c = kchunk<D>(g, ks);
-        Bh[ks] = *(const v4i*)(&tile[buf][r * RB + 16 * swz<RB>(r, c)]);
-        Bl[ks] = *(const v4i*)(&tile[buf][r * RB + 16 * swz<RB>(r, c + D / 16)]);
+    for (int t = 0; t < QT; ++t) {
+      const int i = i0 + t;
+      if (i < n_q) {
+        const int pp = min(qp[i], L_max - 1);
+        if (pp >= 0 && takes(i)) omax = max(omax, own_col(pp));
       }
+    }
+    const int m_begin = s * span;
+    if (m_begin >= omax) return;
+    const int m_end = min(m_begin + span, omax);
+
+    v4i A[QW][MT][KS];
+    int wt[QW][MT][4];
+    int own[QW];
+    long long srow[QW];
+    long long rid[QW];  // flattened row
+    long long th[QW];   // MODE 1: threshold of a list row
+    bool lst[QW];       // MODE 1: the row appends to its list
 #pragma unroll
-      for (int q = 0; q < QW; ++q) {
-        long long ps = 0;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          v4i ah = v4i{0, 0, 0, 0}, al = v4i{0, 0, 0, 0};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            ah = mfma_i8(A[q][mt][ks], Bh[ks], ah);
-            al = mfma_i8(A[q][mt][ks], Bl[ks], al);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int x = (ah[e] << 7) + al[e];
-            ps = relu_mad64(x, wt[q][mt][e], ps);
-          }
+    for (int q = 0; q < QW; ++q) {
+      const int i = i0 + wave * QW + q;
+      const bool valid = i < n_q;
+      const long long row = (long long)b * n_q + (valid ? i : 0);
+      const int pp = valid ? min(qp[i], L_max - 1) : -1;
+      own[q] = pp >= 0 && takes(i) ? own_col(pp) : 0;
+      srow[q] = row * ld;
+      rid[q] = row;
+      th[q] = 0;
+      lst[q] = false;
+      if constexpr (MODE == 1) {
+        if (valid && pp >= 0 && thr.rstate[row] == 0) {
+          lst[q] = true;
+          th[q] = thr.theta[row];
         }
-        part[4 * q + nt] = ps;
       }
+      load_query<D, MT>(q_idx, w, w_per_query, row, H_I, valid, A[q], wt[q]);
     }
-    long long res[2];
-    reduce_scatter8_64(part, res);
-    {
-      const int q = g >> 1;
-      const int o = q ? own[1] : own[0];
-      const long long base = q ? srow[1] : srow[0];
+
+    const int8_t* lb = limbs + (long long)b * n_blocks * RB;
+    v4i stage[LOADS];
+    auto gload = [&](int m0) {
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) {
+        const int cid = tid + 256 * u, r = cid / CH, c = cid % CH, m = min(m0 + r, nv - 1);
+        stage[u] = *(const v4i*)(lb + (long long)m * stride * RB + 16 * c);
+      }
+    };
+    auto swrite = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) {
+        const int cid = tid + 256 * u, r = cid / CH, c = cid % CH;
+        *(v4i*)(&tile[buf][r * RB + 16 * swz<RB>(r, c)]) = stage[u];
+      }
+    };
+
+    // lanes 0-31 hold query 0 of the wave, lanes 32-63 query 1
+    const int lq = g >> 1;
+    const unsigned long long half = lq ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;
+    // MODE 1: the previous tile's entries waiting for their slots
+    long long pv[2] = {0, 0};
+    int pm[2] = {0, 0};
+    unsigned long long pb[2] = {0ull, 0ull};
+    int psb = 0;
+    auto flush = [&]() {
+      const int sb = __shfl(psb, lane & 32);
+      const long long row = lq ? rid[1] : rid[0];
+      const int n0 = __popcll(pb[0]);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int m = m0 + 16 * (2 * (g & 1) + e) + r16;
-        if (m < o) bscores[base + m] = res[e];
+        if (!((pb[e] >> lane) & 1ull)) continue;
+        const int slot = sb + (e ? n0 + lanes_below(pb[1]) : lanes_below(pb[0]));
+        if (slot < thr.cap) {
+          thr.lblk[row * thr.cap + slot] = pm[e];
+          thr.lscore[row * thr.cap + slot] = pv[e];
+        }
       }
-    }
-    if (t + 1 < n_tiles) swrite(buf ^ 1);
+    };
+
+    const int n_tiles = (m_end - m_begin + KT - 1) / KT;
+    gload(m_begin);
+    swrite(0);
     __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+      const int m0 = m_begin + t * KT;
+      const int buf = t & 1;
+      if (t + 1 < n_tiles) gload(m0 + KT);
+      long long part[8];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        v4i Bh[KS], Bl[KS];
+        const int r = 16 * nt + r16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int c = kchunk<D>(g, ks);
+          Bh[ks] = *(const v4i*)(&tile[buf][r * RB + 16 * swz<RB>(r, c)]);
+          Bl[ks] = *(const v4i*)(&tile[buf][r * RB + 16 * swz<RB>(r, c + D / 16)]);
+        }
+#pragma unroll
+        for (int q = 0; q < QW; ++q) {
+          long long ps = 0;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            v4i ah = v4i{0, 0, 0, 0}, al = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              ah = mfma_i8(A[q][mt][ks], Bh[ks], ah);
+              al = mfma_i8(A[q][mt][ks], Bl[ks], al);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int x = (ah[e] << 7) + al[e];
+              ps = relu_mad64(x, wt[q][mt][e], ps);
+            }
+          }
+          part[4 * q + nt] = ps;
+        }
+      }
+      long long res[2];
+      reduce_scatter8_64(part, res);
+      {
+        const int o = lq ? own[1] : own[0];
+        const long long base = lq ? srow[1] : srow[0];
+        if constexpr (MODE == 1) {
+          if (t > 0) flush();
+          const bool ls = lq ? lst[1] : lst[0];
+          const long long tq = lq ? th[1] : th[0];
+          bool pass[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int m = m0 + 16 * (2 * (g & 1) + e) + r16;
+            pass[e] = ls && m < o && res[e] >= tq;
+            if (!ls && m < o) bscores[base + m] = res[e];
+            pv[e] = res[e];
+            pm[e] = m;
+          }
+          pb[0] = __ballot(pass[0]) & half;
+          pb[1] = __ballot(pass[1]) & half;
+          const int n = __popcll(pb[0]) + __popcll(pb[1]);
+          psb = 0;
+          if ((lane & 31) == 0 && n > 0) psb = atomicAdd(&thr.cnt[lq ? rid[1] : rid[0]], n);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int m = m0 + 16 * (2 * (g & 1) + e) + r16;
+            if (m < o) bscores[base + m] = res[e];
+          }
+        }
+      }
+      if (t + 1 < n_tiles) swrite(buf ^ 1);
+      __syncthreads();
+    }
+    if constexpr (MODE == 1) {
+      if (n_tiles > 0) flush();
+    }
+  };
+
+  if constexpr (MODE == 2) {
+    // the listed tiles, BLK_THR_FB_SLOTS at a time
+    const int s = blockIdx.x % n_spans;
+    const int n_fb = *thr.tcnt;
+    for (int j = blockIdx.x / n_spans; j < n_fb; j += BLK_THR_FB_SLOTS) {
+      const int tl = thr.tlist[j];
+      body(tl / n_qtiles, tl % n_qtiles, s);
+      __syncthreads();
+    }
+  } else {
+    // Workgroups are dealt to the 8 XCDs in turn (grid.x is a multiple of 8, so
+    // workgroup x runs on XCD x % 8).  XCD x takes the query tiles x, x + 8, ...
+    // (longest first, interleaved so causal work balances over the XCDs) and walks them
+    // span by span: the workgroups resident on one XCD at a time read the same span of
+    // keys, which its L2 then serves to all of them.
+    const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+    const int per_xcd = (n_qtiles + 7) >> 3;
+    const int s = kx / per_xcd;
+    const int qt_rev = (kx - s * per_xcd) * 8 + xcd;
+    if (qt_rev >= n_qtiles) return;
+    body(blockIdx.y, n_qtiles - 1 - qt_rev, s);
   }
 }
 
@@ -1171,13 +1258,30 @@ static hipError_t launch_blk_scores_t(const BlkArgs& a, hipStream_t st) {
   const int QT = 8;
   const int n_qtiles = (a.n_q + QT - 1) / QT;
   const int span = a.span;
-  const int n_spans = (a.n_blocks + span - 1) / span;
+  if (a.mode < 0 || a.mode > 2 || (a.mode != 0 && (a.thr.rstate == nullptr || a.stride > 1)) ||
+      (a.mode == 1 && (a.thr.theta == nullptr || a.thr.cnt == nullptr || a.thr.lblk == nullptr ||
+                       a.thr.lscore == nullptr || a.thr.cap < 1)) ||
+      (a.mode == 2 && (a.thr.tlist == nullptr || a.thr.tcnt == nullptr)))
+    return hipErrorInvalidValue;
+  // columns: blocks 0, stride, 2 stride, ...
+  const int n_cols = a.stride > 1 ? (a.n_blocks + a.stride - 1) / a.stride : a.n_blocks;
+  const int n_spans = (n_cols + span - 1) / span;
   if (n_spans == 0) return hipSuccess;
   // the kernel's XCD-aware order: 8 XCDs x ceil(n_qtiles / 8) query tiles x n_spans
   dim3 grid((unsigned)(8 * ((n_qtiles + 7) / 8) * n_spans), (unsigned)a.B);
-  hipLaunchKernelGGL((blk_scores_kernel<D, MT, 2>), grid, dim3(256), 0, st, a.q_idx, a.limbs, a.w,
-                     a.w_per_query, a.q_pos, a.n_q, a.n_blocks, a.L_max, a.H_I, a.block_size, span,
-                     n_spans, n_qtiles, a.bscores, (long long)a.ld);
+  const int stride = a.stride > 1 ? a.stride : 1;
+  if (a.mode == 0)
+    hipLaunchKernelGGL((blk_scores_kernel<D, MT, 2, 0>), grid, dim3(256), 0, st, a.q_idx, a.limbs, a.w,
+                       a.w_per_query, a.q_pos, a.n_q, a.n_blocks, a.L_max, a.H_I, a.block_size, span,
+                       n_spans, n_qtiles, a.bscores, (long long)a.ld, stride, a.thr);
+  else if (a.mode == 1)
+    hipLaunchKernelGGL((blk_scores_kernel<D, MT, 2, 1>), grid, dim3(256), 0, st, a.q_idx, a.limbs, a.w,
+                       a.w_per_query, a.q_pos, a.n_q, a.n_blocks, a.L_max, a.H_I, a.block_size, span,
+                       n_spans, n_qtiles, a.bscores, (long long)a.ld, 1, a.thr);
+  else
+    hipLaunchKernelGGL((blk_scores_kernel<D, MT, 2, 2>), dim3((unsigned)(BLK_THR_FB_SLOTS * n_spans)), dim3(256), 0,
+                       st, a.q_idx, a.limbs, a.w, a.w_per_query, a.q_pos, a.n_q, a.n_blocks, a.L_max, a.H_I,
+                       a.block_size, span, n_spans, n_qtiles, a.bscores, (long long)a.ld, 1, a.thr);
   return hipGetLastError();
 }
 
@@ -1221,6 +1325,7 @@ static hipError_t launch_blk_decode_t(const BlkArgs& a, hipStream_t st) {
 
 hipError_t launch_block_scores(const BlkArgs& a, hipStream_t st) {
   if (a.n_q < 8) {  // decode-shaped rows: one query per workgroup
+    if (a.mode != 0 || a.stride > 1) return hipErrorInvalidValue;  // prefill-shaped rows only
     if (a.d_I == 128) {
 #define C(MT) launch_blk_decode_t<128, MT>(a, st)
       LSA_DISPATCH_MT(a.H_I, C)

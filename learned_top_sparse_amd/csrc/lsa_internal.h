@@ -71,6 +71,43 @@ struct BlkCand {
   int spans, span, cap;
 };
 
+// Thresholded keep of long block rows (block modes, chunks of at least 8 queries per
+// sequence), the flat rows' thresholded selection over int64 block scores: a sample of
+// every blk_thr_stride(n_keep)-th block gives each row a threshold that about
+// 2 (n_keep - 1) of its blocks reach (about BLK_THR_ABOVE samples lie above it); the
+// block scan appends those blocks to the row's list (at most blk_thr_cap(n_keep)); the
+// exact keep is taken from the list, and rows whose list fell short of n_keep - 1 or
+// overflowed are scored again into the score table and kept from there.
+struct BlkThr {
+  long long* theta;   // [rows]
+  int32_t* rstate;    // [rows] 0 list row, 1 table row, 2 list fell short or overflowed
+  int32_t* cnt;       // [rows] blocks appended to the list (may exceed cap)
+  int32_t* lblk;      // [rows][cap]
+  long long* lscore;  // [rows][cap]
+  int cap;
+  // query tiles (8 queries of one sequence: b * n_qtiles + i / 8) holding a row in
+  // state 2, each once: tflag [n_tiles] marks them, tlist [n_tiles] lists them, tcnt [1]
+  int32_t* tflag;
+  int32_t* tlist;
+  int32_t* tcnt;
+};
+constexpr int BLK_THR_QT = 8;          // queries per tile of the block scoring
+constexpr int BLK_THR_FB_SLOTS = 64;   // tiles the fallback scoring takes at once
+constexpr int BLK_THR_ABOVE = 32;
+constexpr int BLK_THR_MAX_SAMPLES = 8192;  // a row's samples, in registers of one workgroup
+constexpr int BLK_THR_MAX_B = 131072;      // the list keep's bitmaps of block positions
+constexpr int BLK_THR_MIN_STRIDE = 16;     // sampling costs at most 1/16 of the scan
+inline int blk_thr_cap(int n_keep) { return 4 * n_keep; }
+inline int blk_thr_stride(int n_keep) {
+  const int st = 2 * (n_keep - 1) / BLK_THR_ABOVE;
+  return st > 1 ? st : 1;
+}
+// Rows of at most this many scored blocks keep the score table: below it the table's
+// round trip (8 bytes written and 16 read per block) costs less than the list path's
+// fixed share per row (measured on MI355X at n_keep = 512: rows of 4K-8K blocks ran
+// slower through lists, rows of 62K blocks 7 % faster per step).
+inline int blk_thr_row_min(int n_keep) { return 8 * n_keep > 16384 ? 8 * n_keep : 16384; }
+
 struct BlkArgs {
   const int8_t* q_idx;
   const int8_t* limbs;
@@ -82,6 +119,10 @@ struct BlkArgs {
   long long ld;
   int span;
   BlkCand cand;  // decode-shaped rows: candidates instead of the score table (key == nullptr: table)
+  // prefill-shaped rows only:
+  int stride;    // > 1: score blocks 0, stride, 2 stride, ... into column m / stride (the sample)
+  int mode;      // 0 every row into the table; 1 thresholded scan (thr); 2 rows in state 2 only
+  BlkThr thr;
 };
 
 struct TopkArgs {
@@ -107,6 +148,7 @@ struct BlkSelArgs {
   int B, n_q, n_blocks, block_size, n_keep;
   int32_t* kept;
   BlkCand cand;  // key != nullptr: merge the scoring workgroups' candidates instead
+  const int32_t* rstate;  // non-null: rows in state 0 (kept from their lists) are skipped
 };
 
 // waves per sparse-attention workgroup (each with its own 32-key tile state)
@@ -146,6 +188,15 @@ hipError_t launch_block_cache(const int8_t* k_idx, int B, int L_max, int d_I, in
 hipError_t launch_expand(const int32_t* kept, const int32_t* q_pos, long long rows, int bs, int n_keep, int k,
                          int32_t* idx, int32_t* count, hipStream_t st, const Pages& pg = Pages{}, int n_q = 1);
 hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st);
+// thresholded block keep: each row's threshold from its sampled scores (samp: ld_s per
+// row; mode 0 sampled quantile, 1 above every score, 2 below every score) ...
+hipError_t launch_blk_thresholds(const long long* samp, long long ld_s, const int32_t* q_pos, int B, int n_q,
+                                 int n_blocks, int bs, int n_keep, int stride, int row_min, int mode,
+                                 const BlkThr& t, hipStream_t st);
+// ... and the exact keep of the list rows (rows whose list fell short or overflowed: state 2,
+// their tiles listed for the fallback scoring)
+hipError_t launch_blk_list_keep(const int32_t* q_pos, int B, int n_q, int n_blocks, int bs, int n_keep,
+                                const BlkThr& t, int32_t* kept, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 // chunk-interleaved copy of the index keys of B sequences for the token stage: bytes, and
 // the kernel that writes it (paged caches through pg)

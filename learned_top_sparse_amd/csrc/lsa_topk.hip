@@ -23,6 +23,7 @@
 // stable compaction over the row in global memory.  Every path is exact.
 #include <algorithm>
 #include <atomic>
+#include <climits>
 
 #include "lsa_device.h"
 #include "lsa_internal.h"
@@ -1702,10 +1703,12 @@ __device__ int blk_cut_passes(const long long* __restrict__ br, int n_sc, int n_
 template <int NT>
 __global__ __launch_bounds__(NT) void blk_select_kernel(const long long* __restrict__ bscores, long long ld,
                                                         const int32_t* __restrict__ q_pos, int n_blocks,
-                                                        int bs, int n_keep, int32_t* __restrict__ kept) {
+                                                        int bs, int n_keep, int32_t* __restrict__ kept,
+    const int32_t* __restrict__ rstate) {
   constexpr int V = 4;
   __shared__ int wcnt[2 * V * (NT / 64)];
   const long long row = blockIdx.x;
+  if (rstate != nullptr && rstate[row] == 0) return;  // kept from its list
   const int tid = threadIdx.x;
   const int p = q_pos[row];
   int32_t* out = kept + row * (long long)n_keep;
@@ -1746,7 +1749,8 @@ constexpr int BLK_MED_MIN = 4096, BLK_MED_MAXB = 16384;
 template <int NT, int MAXB, int MCAP>
 __global__ __launch_bounds__(NT) void blk_select_long_kernel(const long long* __restrict__ bscores, long long ld,
                                                              const int32_t* __restrict__ q_pos, int n_blocks,
-                                                             int bs, int n_keep, int32_t* __restrict__ kept) {
+                                                             int bs, int n_keep, int32_t* __restrict__ kept,
+    const int32_t* __restrict__ rstate) {
   constexpr int V = 8, MC = MCAP / NT, NWD = MAXB / 32;
   static_assert(MCAP % NT == 0 && NBINS % NT == 0 && MC <= 32, "whole member and bin ranges per thread");
   __shared__ int hist[NBINS];
@@ -1756,6 +1760,7 @@ __global__ __launch_bounds__(NT) void blk_select_long_kernel(const long long* __
   __shared__ int scan_tmp[NT / 64 + 1], sh[8], mcnt;
   __shared__ unsigned long long shu[2];
   const long long row = blockIdx.x;
+  if (rstate != nullptr && rstate[row] == 0) return;  // kept from its list
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int p = q_pos[row];
   int32_t* out = kept + row * (long long)n_keep;
@@ -1862,13 +1867,15 @@ __global__ __launch_bounds__(NT) void blk_select_long_kernel(const long long* __
 template <int NT, int C>
 __global__ __launch_bounds__(NT) void blk_keep_rows_kernel(const long long* __restrict__ bscores, long long ld,
                                                            const int32_t* __restrict__ q_pos, int n_blocks, int bs,
-                                                           int n_keep, int32_t* __restrict__ kept) {
+                                                           int n_keep, int32_t* __restrict__ kept,
+    const int32_t* __restrict__ rstate) {
   constexpr int NW = NT / 64, NWD = NT * C / 32;
   __shared__ int hist[2048];
   __shared__ unsigned bm[NWD], eqm[NWD];
   __shared__ int scan_tmp[NW + 1], sh[2];
   __shared__ unsigned long long shu[2];
   const long long row = blockIdx.x;
+  if (rstate != nullptr && rstate[row] == 0) return;  // kept from its list
   const int tid = threadIdx.x;
   const int p = q_pos[row];
   int32_t* out = kept + row * (long long)n_keep;
@@ -2099,6 +2106,173 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   return a.kept != nullptr ? launch_topk_t<true>(a, st, rows) : launch_topk_t<false>(a, st, rows);
 }
 
+// Threshold of each block row for the thresholded keep (one workgroup per row).  A row
+// with at most row_min scored blocks (or no position) keeps the score table (state 1).
+// Otherwise its threshold is the t-th best of its m sampled scores (blocks 0, stride,
+// 2 stride, ... below its own block), t = ceil(2 n_sel m / n_sc) (at most m), so about
+// 2 n_sel of its blocks are expected to reach it; the keep stays exact whatever the
+// sample shows (lists that fall short or overflow take the table).  The m samples sit
+// in registers, C per thread (the launcher checks m <= NT * C).
+// It also clears the fallback tile list (row 0) and its row's tile mark (first row of a tile).
+template <int NT, int C>
+__global__ __launch_bounds__(NT) void blk_thr_kernel(const long long* __restrict__ samp, long long ld_s,
+                                                     const int32_t* __restrict__ q_pos, int n_q, int n_blocks,
+                                                     int bs, int n_keep, int stride, int row_min, int mode,
+                                                     BlkThr t) {
+  __shared__ int hist[2048];
+  __shared__ int scan_tmp[NT / 64 + 1], sh[8];
+  __shared__ unsigned long long shu[2];
+  const long long row = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    const int i = (int)(row % n_q);
+    if (i % BLK_THR_QT == 0)
+      t.tflag[(row / n_q) * ((n_q + BLK_THR_QT - 1) / BLK_THR_QT) + i / BLK_THR_QT] = 0;
+    if (row == 0) *t.tcnt = 0;
+  }
+  const int p = q_pos[row];
+  const int n_sc = p >= 0 ? min(p / bs, n_blocks) : 0;  // scored blocks
+  if (p < 0 || n_sc <= row_min) {
+    if (tid == 0) {
+      t.theta[row] = LLONG_MIN;
+      t.rstate[row] = 1;
+      t.cnt[row] = 0;
+    }
+    return;
+  }
+  const int n_sel = min(n_keep - 1, n_sc);
+  long long th;
+  if (mode == 1) {
+    th = LLONG_MAX;
+  } else if (mode == 2) {
+    th = LLONG_MIN;
+  } else {
+    const int m = (n_sc + stride - 1) / stride;
+    const long long tt = (2LL * n_sel * m + n_sc - 1) / n_sc;
+    const int need = (int)min<long long>(m, max<long long>(1, tt));
+    const long long* sr = samp + row * ld_s;
+    unsigned long long key[C];
+    unsigned vmask = 0u;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int j = c * NT + tid;
+      key[c] = j < m ? (unsigned long long)sr[j] ^ 0x8000000000000000ull : 0ull;
+      vmask |= (j < m ? 1u : 0u) << c;
+    }
+    int need_eq;
+    const unsigned long long T = radix_cut64<NT, C>(key, vmask, need, hist, scan_tmp, sh, shu, &need_eq);
+    th = (long long)(T ^ 0x8000000000000000ull);
+  }
+  if (tid == 0) {
+    t.theta[row] = th;
+    t.rstate[row] = 0;
+    t.cnt[row] = 0;
+  }
+}
+
+// Exact keep of a list row (one workgroup per row, rows in state 0): every scored
+// block whose score reaches the row's threshold is in its list, and there are at least
+// n_sel of them, so the row's best n_sel blocks by (score desc, block asc) are the
+// list's.  The list (at most NT * C entries) sits in registers: the cut over it
+// (radix_cut64), the blocks above the cut and the lowest-numbered ones equal to it
+// (an LDS bitmap of block positions), written ascending, then the own block and -1s.
+// A list that fell short of n_sel or overflowed marks its row (state 2) for the table.
+template <int NT, int C>
+__global__ __launch_bounds__(NT) void blk_list_keep_kernel(const int32_t* __restrict__ q_pos, int n_q, int n_blocks,
+                                                           int bs, int n_keep, BlkThr t,
+                                                           int32_t* __restrict__ kept) {
+  constexpr int NWD = BLK_THR_MAX_B / 32;
+  __shared__ int hist[2048];
+  __shared__ unsigned bm[NWD], eqm[NWD];
+  __shared__ int scan_tmp[NT / 64 + 1], sh[8];
+  __shared__ unsigned long long shu[2];
+  const long long row = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (t.rstate[row] != 0) return;
+  const int own = q_pos[row] / bs;  // a list row has a position and more than row_min scored blocks
+  const int n_sc = min(own, n_blocks);
+  const int n_sel = min(n_keep - 1, n_sc);
+  const int c = t.cnt[row];
+  if (c < n_sel || c > t.cap) {
+    if (tid == 0) {
+      t.rstate[row] = 2;
+      // the row's tile, listed once for the fallback scoring
+      const int tile = (int)((row / n_q) * ((n_q + BLK_THR_QT - 1) / BLK_THR_QT) + (row % n_q) / BLK_THR_QT);
+      if (atomicExch(&t.tflag[tile], 1) == 0) t.tlist[atomicAdd(t.tcnt, 1)] = tile;
+    }
+    return;
+  }
+  const int32_t* lb = t.lblk + row * t.cap;
+  const long long* ls = t.lscore + row * t.cap;
+  unsigned long long key[C];
+  int pos[C];
+  unsigned vmask = 0u;
+#pragma unroll
+  for (int cc = 0; cc < C; ++cc) {
+    const int j = cc * NT + tid;
+    key[cc] = j < c ? (unsigned long long)ls[j] ^ 0x8000000000000000ull : 0ull;
+    pos[cc] = j < c ? lb[j] : 0;
+    vmask |= (j < c ? 1u : 0u) << cc;
+  }
+  int need_eq;
+  const unsigned long long T = radix_cut64<NT, C>(key, vmask, n_sel, hist, scan_tmp, sh, shu, &need_eq);
+  const int nwd = (n_sc + 31) >> 5;
+  for (int wd = tid; wd < nwd; wd += NT) {
+    bm[wd] = 0u;
+    eqm[wd] = 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int cc = 0; cc < C; ++cc) {
+    if (!((vmask >> cc) & 1u)) continue;
+    if (key[cc] > T) atomicOr(&bm[pos[cc] >> 5], 1u << (pos[cc] & 31));
+    else if (key[cc] == T) atomicOr(&eqm[pos[cc] >> 5], 1u << (pos[cc] & 31));
+  }
+  __syncthreads();
+  keep_first_ties<NT>(bm, eqm, nwd, need_eq, scan_tmp);
+  int32_t* out = kept + row * (long long)n_keep;
+  const int written = emit_marked<NT>(bm, nwd, scan_tmp, [&](int r, int q) {
+    if (r < n_sel) out[r] = q;
+  });
+  const int wr = min(written, n_sel);
+  if (tid == 0) out[wr] = own;
+  for (int tt = wr + 1 + tid; tt < n_keep; tt += NT) out[tt] = -1;
+}
+
+hipError_t launch_blk_thresholds(const long long* samp, long long ld_s, const int32_t* q_pos, int B, int n_q,
+                                 int n_blocks, int bs, int n_keep, int stride, int row_min, int mode,
+                                 const BlkThr& t, hipStream_t st) {
+  const long long rows = (long long)B * n_q;
+  if (rows == 0) return hipSuccess;
+  constexpr int NT = 256, C = BLK_THR_MAX_SAMPLES / 256;
+  if (samp == nullptr || t.theta == nullptr || t.rstate == nullptr || t.cnt == nullptr || t.tflag == nullptr ||
+      t.tcnt == nullptr || stride < 1 || bs < 1 || n_keep < 2 || mode < 0 || mode > 2 ||
+      (long long)(n_blocks + stride - 1) / stride > (long long)NT * C || ld_s < (n_blocks + stride - 1) / stride)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((blk_thr_kernel<NT, C>), dim3((unsigned)rows), dim3(NT), 0, st, samp, ld_s, q_pos, n_q,
+                     n_blocks, bs, n_keep, stride, row_min, mode, t);
+  return hipGetLastError();
+}
+
+hipError_t launch_blk_list_keep(const int32_t* q_pos, int B, int n_q, int n_blocks, int bs, int n_keep,
+                                const BlkThr& t, int32_t* kept, hipStream_t st) {
+  const long long rows = (long long)B * n_q;
+  if (rows == 0) return hipSuccess;
+  constexpr int NT = 256;
+  if (t.lblk == nullptr || t.lscore == nullptr || t.cap < 1 || t.tflag == nullptr || t.tlist == nullptr ||
+      t.tcnt == nullptr || n_blocks > BLK_THR_MAX_B || n_keep < 2 || kept == nullptr)
+    return hipErrorInvalidValue;
+  if (t.cap <= NT * 8)
+    hipLaunchKernelGGL((blk_list_keep_kernel<NT, 8>), dim3((unsigned)rows), dim3(NT), 0, st, q_pos, n_q, n_blocks,
+                       bs, n_keep, t, kept);
+  else if (t.cap <= NT * 32)
+    hipLaunchKernelGGL((blk_list_keep_kernel<NT, 32>), dim3((unsigned)rows), dim3(NT), 0, st, q_pos, n_q,
+                       n_blocks, bs, n_keep, t, kept);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 // Pooled blocks: the index list of a query is every key of its kept blocks that it
 // may see, idx[r] = kept[r / bs] * bs + r % bs if that block is kept and the key is
 // <= the query's position, else -1.  kept is ascending with the own block last, so
@@ -2206,22 +2380,22 @@ hipError_t launch_block_select(const BlkSelArgs& a, hipStream_t st) {
   if (a.n_q < 8 && a.n_blocks > 4096 && a.n_blocks <= 1024 * 32) {
     // few long rows (decode): the row's scores in registers of one workgroup
     hipLaunchKernelGGL((blk_keep_rows_kernel<1024, 32>), dim3((unsigned)rows), dim3(1024), 0, st, a.bscores, a.ld,
-                       a.q_pos, a.n_blocks, a.block_size, a.n_keep, a.kept);
+                       a.q_pos, a.n_blocks, a.block_size, a.n_keep, a.kept, a.rstate);
     return hipGetLastError();
   }
   if (a.n_blocks > BLK_MED_MAXB && a.n_blocks <= BLK_LONG_MAXB) {
     // long prefill-shaped rows: two reads of each row
     hipLaunchKernelGGL((blk_select_long_kernel<1024, BLK_LONG_MAXB, 4096>), dim3((unsigned)rows), dim3(1024), 0, st,
-                       a.bscores, a.ld, a.q_pos, a.n_blocks, a.block_size, a.n_keep, a.kept);
+                       a.bscores, a.ld, a.q_pos, a.n_blocks, a.block_size, a.n_keep, a.kept, a.rstate);
     return hipGetLastError();
   }
   if (a.n_blocks > BLK_MED_MIN && a.n_blocks <= BLK_MED_MAXB) {
     hipLaunchKernelGGL((blk_select_long_kernel<256, BLK_MED_MAXB, 1024>), dim3((unsigned)rows), dim3(256), 0, st,
-                       a.bscores, a.ld, a.q_pos, a.n_blocks, a.block_size, a.n_keep, a.kept);
+                       a.bscores, a.ld, a.q_pos, a.n_blocks, a.block_size, a.n_keep, a.kept, a.rstate);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(blk_select_kernel<256>, dim3((unsigned)rows), dim3(256), 0, st, a.bscores, a.ld,
-                     a.q_pos, a.n_blocks, a.block_size, a.n_keep, a.kept);
+                     a.q_pos, a.n_blocks, a.block_size, a.n_keep, a.kept, a.rstate);
   return hipGetLastError();
 }
 

@@ -621,6 +621,60 @@ def test_forward_pooled_blocks(lsa, case):
     err.check()
 
 
+@pytest.mark.parametrize("case", [
+    # (two_stage, L, block_size, n_keep, k_top, values)
+    ("pooled", 72000, 4, 300, 1200, "random"),
+    ("pooled", 72000, 4, 300, 1200, "ties3"),
+    ("pooled", 72000, 4, 300, 1200, "zeros"),
+    ("pooled", 70002, 4, 300, 1200, "d64"),  # d_I = 64, 20 heads (a partial head tile), ragged L
+])
+def test_forward_block_threshold_keep(lsa, case):
+    """Prefill-shaped pooled block rows over max(8 * n_keep, 16384) blocks take the
+    thresholded keep: a sample of every 18th block sets each row's threshold, the block scan lists the
+    blocks that reach it, and the keep comes from the list (rows whose list falls short
+    or overflows are scored again into the table).  Lists, kept blocks, counts and
+    outputs equal the score-table path's bit for bit with sampled thresholds, with every
+    list short and with every list overflowing, and the oracle's on sampled rows.  Rows
+    of at most 16384 blocks (the table) and heavily tied or all-equal scores (lists that
+    overflow by themselves) mix in."""
+    mode, L, bs, nk, k, vals = case
+    two = "pooled" if mode == "pooled" else True
+    n_q = 40
+    H_I, d_I = (20, 64) if vals == "d64" else (64, 128)
+    wl = synthetic.Workload("bthr", B=1, n_q=n_q, L=L, q_pos0=0, H_I=H_I, d_I=d_I, k=k, H_q=16)
+    gen = np.random.default_rng(11)
+    row_min = max(8 * nk, 16384)
+    pos = np.sort(gen.integers(row_min * bs, L, n_q))
+    pos[:4] = [0, bs * nk, row_min * bs, row_min * bs + bs]  # short rows (table), then the first list row
+    pos[-1] = L - 1
+    inp, g = _inputs(wl, seed=31, pos=pos.tolist())
+    if vals == "zeros":
+        inp["q_idx"].zero_()
+    elif vals == "ties3":
+        tg = torch.Generator().manual_seed(5)
+        inp["q_idx"] = torch.randint(-1, 2, inp["q_idx"].shape, generator=tg).to(torch.int8)
+        inp["k_idx"] = torch.randint(-1, 2, inp["k_idx"].shape, generator=tg).to(torch.int8)
+    g = {n: v.to(dev()) for n, v in inp.items()}
+    kw = dict(k_top=k, two_stage=two, block_size=bs, n_keep=nk, attn_split=1)
+    ref = lsa.lsa_forward(g, select="table", **kw)
+    for sel in ("auto", "force_short", "force_overflow"):
+        res = lsa.lsa_forward(g, select=sel, **kw)
+        for n in ("idx", "count", "kept", "out", "lse"):
+            assert torch.equal(res[n], ref[n]), (sel, n)
+    qi, ki, w = inp["q_idx"].numpy(), inp["k_idx"].numpy(), inp["w"].numpy()
+    q, kk, vv = np64(inp["q"]), np64(inp["k"]), np64(inp["v"])
+    J, kept, out = ref["idx"].cpu().numpy(), ref["kept"].cpu().numpy(), np64(ref["out"])
+    err = AttnErr()
+    for i in (2, 3, n_q // 2, n_q - 1):
+        r = oracle.forward_row(qi[0, i], ki[0], w, int(pos[i]), k, q_row=q[0, i], k_cache=kk[0], v_cache=vv[0],
+                               scale=1.0 / math.sqrt(128), two_stage=True, block_size=bs, n_keep=nk,
+                               pooled=mode == "pooled")
+        assert np.array_equal(J[0, i], r["J"]), f"row {i}"
+        assert np.array_equal(kept[0, i], r["kept"]), f"kept {i}"
+        err.add(out[0, i], r["out"], i)
+    err.check()
+
+
 @pytest.mark.parametrize("mode", ["two_stage", "pooled"])
 def test_forward_block_modes_short_context(lsa, mode):
     """Contexts shorter than one block (no complete block to score): every query keeps

@@ -195,6 +195,45 @@ def test_two_stage_interleaved_key_copy_sizing():
     assert flat_blocks > 0
 
 
+def test_block_threshold_keep_sizing():
+    """Block modes reserve the thresholded keep's buffers -- per row the sampled scores
+    (every (2 (n_keep - 1) // 32)-th block, 8 bytes, padded to 8 per row), threshold,
+    state, count, a list of 4 n_keep (block, score) pairs and a fallback tile mark and
+    list entry, plus the list's count -- only for prefill-shaped calls with rows over
+    max(8 n_keep, 16384) blocks and a sampling stride of at least 16 (n_keep >= 257),
+    and not with the score table asked for."""
+    import learned_top_sparse_amd as lsa
+    A = 256
+
+    def al(x):
+        return (x + A - 1) // A * A
+
+    def thr_bytes(rows, n_blocks, nk):
+        st = 2 * (nk - 1) // 32
+        ld = ((n_blocks + st - 1) // st + 7) // 8 * 8
+        cap = 4 * nk
+        return (al(rows * ld * 8) + al(rows * 8) + 2 * al(rows * 4) + al(rows * cap * 4) + al(rows * cap * 8)
+                + 2 * al(rows * 4) + al(4))
+
+    pre = _fake_inputs(1, 64, 72000)
+    kw = dict(two_stage="pooled", block_size=4, n_keep=300)
+    auto = lsa.lsa_forward_workspace_size(pre, 1200, **kw)
+    table = lsa.lsa_forward_workspace_size(pre, 1200, select="table", **kw)
+    assert auto - table == thr_bytes(64, 18000, 300)
+    for sel in ("force_short", "force_overflow"):
+        assert lsa.lsa_forward_workspace_size(pre, 1200, select=sel, **kw) == auto
+    # rows of at most 16384 blocks, sampling strides below 16, decode-shaped calls: none
+    short = _fake_inputs(1, 64, 65536)
+    assert (lsa.lsa_forward_workspace_size(short, 1200, **kw) ==
+            lsa.lsa_forward_workspace_size(short, 1200, select="table", **kw))
+    kw2 = dict(two_stage="pooled", block_size=4, n_keep=256)
+    assert (lsa.lsa_forward_workspace_size(pre, 1024, **kw2) ==
+            lsa.lsa_forward_workspace_size(pre, 1024, select="table", **kw2))
+    dec = _fake_inputs(4, 1, 72000)
+    assert (lsa.lsa_forward_workspace_size(dec, 1200, **kw) ==
+            lsa.lsa_forward_workspace_size(dec, 1200, select="table", **kw))
+
+
 def _fake_paged(B, n_q, max_pages, page_size, n_pages, H_I=64, d_I=128, H_q=16, d=128):
     import torch
     inp = _fake_inputs(B, n_q, 1, H_I, d_I, H_q, d)
