@@ -2249,8 +2249,17 @@ hipError_t launch_blk_thresholds(const long long* samp, long long ld_s, const in
       t.tcnt == nullptr || stride < 1 || bs < 1 || n_keep < 2 || mode < 0 || mode > 2 ||
       (long long)(n_blocks + stride - 1) / stride > (long long)NT * C || ld_s < (n_blocks + stride - 1) / stride)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL((blk_thr_kernel<NT, C>), dim3((unsigned)rows), dim3(NT), 0, st, samp, ld_s, q_pos, n_q,
-                     n_blocks, bs, n_keep, stride, row_min, mode, t);
+  // samples per thread: as few registers as the longest row needs
+  const int m_max = (n_blocks + stride - 1) / stride;
+  if (m_max <= NT * 8)
+    hipLaunchKernelGGL((blk_thr_kernel<NT, 8>), dim3((unsigned)rows), dim3(NT), 0, st, samp, ld_s, q_pos, n_q,
+                       n_blocks, bs, n_keep, stride, row_min, mode, t);
+  else if (m_max <= NT * 16)
+    hipLaunchKernelGGL((blk_thr_kernel<NT, 16>), dim3((unsigned)rows), dim3(NT), 0, st, samp, ld_s, q_pos, n_q,
+                       n_blocks, bs, n_keep, stride, row_min, mode, t);
+  else
+    hipLaunchKernelGGL((blk_thr_kernel<NT, C>), dim3((unsigned)rows), dim3(NT), 0, st, samp, ld_s, q_pos, n_q,
+                       n_blocks, bs, n_keep, stride, row_min, mode, t);
   return hipGetLastError();
 }
 
