@@ -808,9 +808,13 @@ def main():
             "workload": _describe(wx), "value": wx.B * wx.n_q / (ms_x * 1e-3), "unit": "queries/s",
             "ms_per_step": ms_x, "kernel_ms": kx, "t_roof_ms": t_roof_ms(wx),
             "step_roofline_frac": t_roof_ms(wx) / ms_x,
-            "roofline": {"bound": "mfma", "kernel": "block_prefilter (blk_scores_kernel + blk_select_kernel)",
+            "roofline": {"bound": "mfma",
+                         "kernel": "block_prefilter (blk_scores_kernel and the block keep: the score table and "
+                                   "blk_select_long_kernel for rows up to 16384 blocks; a sampled threshold, the "
+                                   "thresholded scan and blk_list_keep_kernel above)",
                          "achieved": ach, "peak": INT8_PEAK_TOPS, "unit": "TOP/s", "frac": ach / INT8_PEAK_TOPS,
                          "frac_of_measured_peak": ach / peaks["int8_mfma_TOPs"] if peaks else None,
+                         "counter_mfma_busy": counter_mfma_busy(name, "block_prefilter"),
                          "ops": "pooled-key scores, two int8 parts per block key"},
         }
         del inp, step
