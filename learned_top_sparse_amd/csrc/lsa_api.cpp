@@ -127,9 +127,6 @@ LSA_API lsa_status lsa_block_prefilter_workspace_size(int32_t B, int32_t n_q, in
   return LSA_OK;
 }
 
-// block scores + keep for rows whose limbs are already in `limbs`
-// Block scores and kept blocks.  scores_private: bscores is workspace nobody reads back,
-// so decode-shaped rows may keep span candidates there instead of the score table.
 // Thresholded keep of a prefill-shaped chunk (BlkThr): where its workspace was carved.
 struct BlkThrWs {
   long long* samp = nullptr;  // sampled scores, ld_s per row
@@ -138,6 +135,11 @@ struct BlkThrWs {
   int stride = 1, row_min = 0, mode = 0;
 };
 
+// Block scores and kept blocks for rows whose limbs are already in `limbs`.
+// scores_private: bscores is workspace nobody reads back, so decode-shaped rows may keep
+// span candidates there instead of the score table.  tw: prefill-shaped chunks take the
+// thresholded keep (sample, thresholds, listing scan, list keep, fallback tiles into the
+// table, table keep of the rest).
 static lsa_status run_prefilter(const int8_t* q_idx, const int8_t* limbs, const int32_t* w, int32_t w_per_query,
                                 const int32_t* q_pos, int32_t B, int32_t n_q, int32_t n_blocks, int32_t H_I,
                                 int32_t d_I, int32_t block_size, int32_t n_keep, int32_t* kept,
