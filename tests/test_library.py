@@ -195,6 +195,31 @@ def test_two_stage_interleaved_key_copy_sizing():
     assert flat_blocks > 0
 
 
+def test_forward_chunks_equal_size():
+    """Automatic chunking splits the rows into chunks of equal size (the last one at most
+    one row per chunk short), as few as the workspace allows, instead of full chunks and
+    a short tail; each planned chunk fits the workspace and an explicit chunk_rows is
+    kept as given."""
+    import math
+    import learned_top_sparse_amd as lsa
+    n, k = 1000, 2048
+    inp = _fake_inputs(1, n, 20000)
+    full = lsa.lsa_forward_workspace_size(inp, k)
+    assert lsa.lsa_forward_plan(inp, k, full)[0] == n
+    for f in (0.3, 0.45, 0.7, 0.97):
+        ws = int(full * f)
+        rows, _ = lsa.lsa_forward_plan(inp, k, ws)
+        n_chunks = math.ceil(n / rows)
+        assert rows == math.ceil(n / n_chunks), (f, rows)
+        assert lsa.lsa_forward_workspace_size(inp, k, chunk_rows=rows) <= ws
+        # one row more per chunk would not have saved a chunk: the most that fit needs as many
+        fit = rows
+        while lsa.lsa_forward_workspace_size(inp, k, chunk_rows=fit + 1) <= ws:
+            fit += 1
+        assert math.ceil(n / fit) == n_chunks, (f, rows, fit)
+    assert lsa.lsa_forward_plan(inp, k, full, chunk_rows=333)[0] == 333
+
+
 def test_block_threshold_keep_sizing():
     """Block modes reserve the thresholded keep's buffers -- per row the sampled scores
     (every (2 (n_keep - 1) // 32)-th block, 8 bytes, padded to 8 per row), threshold,
