@@ -85,6 +85,14 @@ __device__ __forceinline__ int relu_mad24(int x, int w, int acc) {
   asm("v_mad_i32_i24 %0, %1, %2, %0" : "+v"(acc) : "v"(r), "v"(w));
   return acc;
 }
+// max(x, 0) * w as one v_mul_i32_i24: the first term of a chain, so no register has
+// to be set to zero for it.
+__device__ __forceinline__ int relu_mul24(int x, int w) {
+  const int r = max(x, 0);
+  int p;
+  asm("v_mul_i32_i24 %0, %1, %2" : "=v"(p) : "v"(r), "v"(w));
+  return p;
+}
 
 // acc + max(x, 0) * w in 64 bits as one v_mad_i64_i32 (signed 32 x 32 -> 64-bit product
 // plus a 64-bit add): the block scores' epilogue.  Written out because the compiler
@@ -95,6 +103,14 @@ __device__ __forceinline__ long long relu_mad64(int x, int w, long long acc) {
   unsigned long long carry;
   asm("v_mad_i64_i32 %0, %1, %2, %3, %0" : "+v"(acc), "=s"(carry) : "v"(w), "v"(r));
   return acc;
+}
+// max(x, 0) * w in 64 bits: the first term of a chain (the addend is the constant 0).
+__device__ __forceinline__ long long relu_mul64(int x, int w) {
+  const int r = max(x, 0);
+  long long p;
+  unsigned long long carry;
+  asm("v_mad_i64_i32 %0, %1, %2, %3, 0" : "=v"(p), "=s"(carry) : "v"(w), "v"(r));
+  return p;
 }
 
 }  // namespace lsa

@@ -55,8 +55,8 @@ __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
   constexpr int R = 3;  // register stages of key tiles
   constexpr int WBUF = 512;  // SEL: candidates a wave buffers in LDS
   static_assert(KT * CH <= 64 * NW, "one 16-byte chunk of a key tile per thread");
-  __shared__ __attribute__((aligned(16))) int8_t tile[2][KT * D];
-  __shared__ int wb_slot[SEL ? NW : 1][WBUF], wb_score[SEL ? NW : 1][WBUF];
+  __shared__ __attribute__((aligned(16))) int8_t tile[R][KT * D];
+  __shared__ int wb[SEL ? NW : 1][2][WBUF];  // SEL: per wave, slots then scores
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -105,11 +105,12 @@ __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
   load_query<D, MT>(q_idx, w, w_per_query, row, H_I, valid, A, wt);
   // SEL: this wave's row kind and threshold (a table row, or an invalid query, keeps
   // the plain stores)
-  bool list_row = false;
+  // (kept in scalar registers: the row kind is tested once per tile)
+  int list_row = 0;
   int th = 0;
   if constexpr (SEL) {
-    list_row = valid && thr.rstate[row] == 0;
-    th = thr.theta[row];
+    list_row = __builtin_amdgcn_readfirstlane((valid && thr.rstate[row] == 0) ? 1 : 0);
+    th = __builtin_amdgcn_readfirstlane(thr.theta[row]);
   }
   int wn = 0;  // SEL: candidates in this wave's LDS buffer (wave-uniform)
   auto flush = [&]() {
@@ -123,8 +124,8 @@ __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
     int32_t* lsc = thr.lscore + row * thr.cap;
     for (int e = lane; e < wn; e += 64) {
       if (base + e < thr.cap) {
-        lsl[base + e] = wb_slot[wave][e];
-        lsc[base + e] = wb_score[wave][e];
+        lsl[base + e] = wb[wave][0][e];
+        lsc[base + e] = wb[wave][1][e];
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -150,15 +151,30 @@ __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
     for (int t = tid; t <= pg1 - pg0; t += 64 * NW) span_pages[t] = min(max(pt[pg0 + t], 0), pg.n_pages - 1);
     __syncthreads();
   }
+  // Contiguous caches: a tile's keys come through a buffer resource based at the tile's
+  // first key, so the only per-tile address arithmetic is scalar; a lane's offset in the
+  // tile is fixed, and keys past the cache's end read as zero (the resource's range
+  // check), where no stored or listed score looks.
+  const long long key_bytes = (long long)L_max * D;
+  const int lane_koff = cr * stride * D + 16 * cc;
   auto gload = [&](int t) -> v4i {
-    const int js = min(j_begin + min(t, n_tiles - 1) * KT + cr, smax);
-    long long key = (long long)js * stride;
-    if constexpr (PAGED)
+    const int js0 = j_begin + min(t, n_tiles - 1) * KT;
+    if constexpr (PAGED) {
+      const int js = min(js0 + cr, smax);
+      long long key = (long long)js * stride;
       key = ((long long)span_pages[(int)(key >> pg.page_log2) - pg0] << pg.page_log2) |
             (key & ((1ll << pg.page_log2) - 1));
-    return *(const v4i*)(kb + key * D + 16 * cc);
+      return *(const v4i*)(kb + key * D + 16 * cc);
+    } else {
+      const long long off0 = (long long)js0 * stride * D;
+      const long long rem = key_bytes - off0;  // > 0: the tile's first slot has a key
+      const int n_rec = (unsigned)(rem >> 31) != 0u ? 0x7fffffff : (int)rem;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(kb + off0), (short)0, n_rec, BUF_RSRC_WORD3);
+      return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, lane_koff, 0, 0));
+    }
   };
-  // dot products of the query's heads with the 16 keys of group nt
+  // dot products of the query's heads with the 16 keys of group nt of LDS tile buf
   auto mfmas = [&](int buf, int nt, v4i (&acc)[MT]) {
     v4i Bf[KS];
     const int r = 16 * nt + r16;
@@ -174,11 +190,12 @@ __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
   };
   // this lane's share of sum_h w_h * max(0, dot_h) for its key column
   auto epilogue = [&](const v4i (&acc)[MT]) -> int {
-    int ps = 0;
+    int ps = relu_mul24(acc[0][0], wt[0][0]);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) ps = relu_mad24(acc[mt][e], wt[mt][e], ps);
+      for (int mt = 0; mt < MT; ++mt)
+        if (e + mt > 0) ps = relu_mad24(acc[mt][e], wt[mt][e], ps);
     return ps;
   };
   auto compute = [&](int buf) -> int {
@@ -195,6 +212,8 @@ __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
     return reduce_scatter4(part);  // lane l: key l of the tile
   };
 
+  // R register stages and R LDS tiles: in the loop unrolled by R, tile t sits in stage
+  // and LDS tile t % R = u, so every LDS address is fixed at compile time
   v4i st[R];
 #pragma unroll
   for (int u = 0; u < R; ++u) st[u] = gload(u);
@@ -204,27 +223,27 @@ __global__ __launch_bounds__(64 * NW, 4) void idx_flat_kernel(
   for (int t0 = 0; t0 < n_pad; t0 += R) {
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-      const int t = t0 + u, buf = t & 1;
+      const int t = t0 + u;
       st[u] = gload(t + R);  // stage u held tile t, already in LDS
       int res = 0;
-      if (t < n_tiles) res = compute(buf);
-      const int js = j_begin + t * KT + lane;
-      if (!SEL || !list_row) {
-        __builtin_amdgcn_raw_buffer_store_b32(res, row_rsrc, js * 4, 0, 0);
+      if (t < n_tiles) res = compute(u);
+      const int jt = j_begin + t * KT;  // slot of the tile's first key
+      if (!SEL || list_row == 0) {
+        __builtin_amdgcn_raw_buffer_store_b32(res, row_rsrc, 4 * (jt + lane), 0, 0);
       } else {
-        const bool pass = js < lim && res >= th;
-        const unsigned long long bal = __ballot(pass);
+        const bool pass = lane < lim - jt && res >= th;
+        const unsigned long long bal = __builtin_amdgcn_ballot_w64(pass);
         if (bal != 0ull) {  // wave-uniform
           const int r = wn + lanes_below(bal);
           if (pass) {
-            wb_slot[wave][r] = js;
-            wb_score[wave][r] = res;
+            wb[wave][0][r] = jt + lane;
+            wb[wave][1][r] = res;
           }
           wn += __popcll(bal);
           if (wn > WBUF - 64) flush();
         }
       }
-      *(v4i*)(&tile[buf ^ 1][tile_off]) = st[(u + 1) % R];  // tile t+1
+      *(v4i*)(&tile[(u + 1) % R][tile_off]) = st[(u + 1) % R];  // tile t+1
       __syncthreads();
     }
   }
@@ -825,13 +844,22 @@ __global__ __launch_bounds__(256, 2) void blk_scores_kernel(
       load_query<D, MT>(q_idx, w, w_per_query, row, H_I, valid, A[q], wt[q]);
     }
 
+    // Column rows come through buffer resources based at the rows a load instruction
+    // starts on, so the per-tile address arithmetic is scalar; a lane's offset is fixed,
+    // and columns past the last block read as zero (the resource's range check), where
+    // no stored or listed score looks.
     const int8_t* lb = limbs + (long long)b * n_blocks * RB;
+    // (n_blocks <= 65536 rows of RB bytes: every offset here fits in 32 bits)
+    const int limb_bytes = n_blocks * RB;
+    const int lane_loff = (tid / CH) * stride * RB + 16 * (tid % CH);
     v4i stage[LOADS];
     auto gload = [&](int m0) {
 #pragma unroll
       for (int u = 0; u < LOADS; ++u) {
-        const int cid = tid + 256 * u, r = cid / CH, c = cid % CH, m = min(m0 + r, nv - 1);
-        stage[u] = *(const v4i*)(lb + (long long)m * stride * RB + 16 * c);
+        const int off0 = (m0 + u * (256 / CH)) * stride * RB;  // row of thread 0
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(lb + off0), (short)0, max(limb_bytes - off0, 0), BUF_RSRC_WORD3);
+        stage[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, lane_loff, 0, 0));
       }
     };
     auto swrite = [&](int buf) {
@@ -898,7 +926,7 @@ __global__ __launch_bounds__(256, 2) void blk_scores_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int x = (ah[e] << 7) + al[e];
-              ps = relu_mad64(x, wt[q][mt][e], ps);
+              ps = (mt == 0 && e == 0) ? relu_mul64(x, wt[q][mt][e]) : relu_mad64(x, wt[q][mt][e], ps);
             }
           }
           part[4 * q + nt] = ps;
