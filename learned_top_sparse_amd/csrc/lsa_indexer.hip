@@ -737,34 +737,57 @@ __global__ void blk_limbs_kernel(const int32_t* __restrict__ reps, int D, long l
 
 // Block-key cache: blocks [m0, m0 + n_upd) of every sequence, each written as the
 // two int8 limbs of its representative (the sum of its bs keys), rows laid out as
-// blk_limbs_kernel writes them.  Thread e: one byte column c of block m.  With a page
-// table (pg.page_table set) k_idx is a pool and key j of sequence b is pool row
-// page_table[b][j >> page_log2] << page_log2 | (j & mask) (page ids clamped).
-__global__ void blk_cache_kernel(const int8_t* __restrict__ k_idx, int L_max, int D, int bs, int n_blocks, int m0,
-                                 int n_upd, long long total, int8_t* __restrict__ limbs, Pages pg) {
-  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= total) return;
-  const int c = (int)(e % D);
-  const long long bm = e / D;
-  const int m = m0 + (int)(bm % n_upd);
-  const long long b = bm / n_upd;
-  int r = 0;
-  if (pg.page_table != nullptr) {
-    const int32_t* pt = pg.page_table + b * pg.max_pages;
-    const int pmask = (1 << pg.page_log2) - 1;
-    for (int t = 0; t < bs; ++t) {
+// blk_limbs_kernel writes them.  One workgroup per block: thread t reads 16-byte chunk
+// t % CH of every (256 / CH)-th key row of the block (all its loads issued before the
+// first sum), keeps 16 column sums, and the sums of the threads sharing a chunk meet in
+// LDS.  With a page table (pg.page_table set) k_idx is a pool and key j of sequence b
+// is pool row page_table[b][j >> page_log2] << page_log2 | (j & mask) (page ids
+// clamped).  Grid: x = B * n_upd (workgroup x: sequence x / n_upd, block m0 + x % n_upd).
+template <int D>
+__global__ __launch_bounds__(256) void blk_cache_kernel(const int8_t* __restrict__ k_idx, int L_max, int bs,
+                                                        int n_blocks, int m0, int n_upd,
+                                                        int8_t* __restrict__ limbs, Pages pg) {
+  constexpr int CH = D / 16, NG = 256 / CH, KPT = (128 + NG - 1) / NG;  // bs <= 128 keys
+  __shared__ int part[NG][D + 1];
+  const int tid = threadIdx.x, c = tid % CH, kg = tid / CH;
+  const int m = m0 + (int)(blockIdx.x % n_upd);
+  const long long b = blockIdx.x / n_upd;
+  v4i x[KPT];
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const int t = kg + u * NG;
+    x[u] = v4i{0, 0, 0, 0};
+    if (t < bs) {
       const int j = m * bs + t;
-      const long long page = min(max(pt[j >> pg.page_log2], 0), pg.n_pages - 1);
-      r += k_idx[((page << pg.page_log2) | (j & pmask)) * D + c];
+      long long rowk;
+      if (pg.page_table != nullptr) {
+        const long long page = min(max(pg.page_table[b * pg.max_pages + (j >> pg.page_log2)], 0), pg.n_pages - 1);
+        rowk = (page << pg.page_log2) | (j & ((1 << pg.page_log2) - 1));
+      } else {
+        rowk = b * L_max + j;
+      }
+      x[u] = *(const v4i*)(k_idx + rowk * D + 16 * c);
     }
-  } else {
-    const int8_t* src = k_idx + (b * L_max + (long long)m * bs) * D + c;
-    for (int t = 0; t < bs; ++t) r += src[(long long)t * D];
   }
-  const int hi = (r + 64) >> 7;
-  int8_t* dst = limbs + (b * n_blocks + m) * 2 * D;
-  dst[c] = (int8_t)hi;
-  dst[D + c] = (int8_t)(r - (hi << 7));
+  int sum[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sum[i] = 0;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum[i] += (int)(signed char)(x[u][i >> 2] >> (8 * (i & 3)));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) part[kg][16 * c + i] = sum[i];
+  __syncthreads();
+  if (tid < D) {
+    int r = 0;
+#pragma unroll 8
+    for (int g2 = 0; g2 < NG; ++g2) r += part[g2][tid];
+    const int hi = (r + 64) >> 7;
+    int8_t* dst = limbs + (b * n_blocks + m) * 2 * D;
+    dst[tid] = (int8_t)hi;
+    dst[D + tid] = (int8_t)(r - (hi << 7));
+  }
 }
 
 // Block scores with the flat kernel's tiling: the "keys" are block limb rows of
@@ -1276,8 +1299,14 @@ hipError_t launch_block_cache(const int8_t* k_idx, int B, int L_max, int d_I, in
   if (pg.page_table != nullptr &&
       (pg.page_log2 < 6 || pg.page_log2 > 30 || pg.n_pages < 1 || (long long)pg.max_pages << pg.page_log2 < L_max))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(blk_cache_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, k_idx, L_max, d_I,
-                     bs, n_blocks, m0, n_upd, total, limbs, pg);
+  if (bs < 1 || bs > 128 || (d_I != 64 && d_I != 128)) return hipErrorInvalidValue;
+  if (total / d_I > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (d_I == 128)
+    hipLaunchKernelGGL(blk_cache_kernel<128>, dim3((unsigned)(total / d_I)), dim3(256), 0, st, k_idx, L_max, bs,
+                       n_blocks, m0, n_upd, limbs, pg);
+  else
+    hipLaunchKernelGGL(blk_cache_kernel<64>, dim3((unsigned)(total / d_I)), dim3(256), 0, st, k_idx, L_max, bs,
+                       n_blocks, m0, n_upd, limbs, pg);
   return hipGetLastError();
 }
 
