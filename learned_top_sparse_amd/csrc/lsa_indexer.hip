@@ -735,14 +735,45 @@ __global__ void blk_limbs_kernel(const int32_t* __restrict__ reps, int D, long l
   limbs[rowi * 2 * D + D + c] = (int8_t)lo;
 }
 
+// Blocks of few keys (the pooled 4:1 cache): thread e sums byte column e % D of one
+// block, one byte load per key.
+__global__ void blk_cache_cols_kernel(const int8_t* __restrict__ k_idx, int L_max, int D, int bs, int n_blocks,
+                                      int m0, int n_upd, long long total, int8_t* __restrict__ limbs, Pages pg) {
+  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  const int c = (int)(e % D);
+  const long long bm = e / D;
+  const int m = m0 + (int)(bm % n_upd);
+  const long long b = bm / n_upd;
+  int r = 0;
+  if (pg.page_table != nullptr) {
+    const int32_t* pt = pg.page_table + b * pg.max_pages;
+    const int pmask = (1 << pg.page_log2) - 1;
+    for (int t = 0; t < bs; ++t) {
+      const int j = m * bs + t;
+      const long long page = min(max(pt[j >> pg.page_log2], 0), pg.n_pages - 1);
+      r += k_idx[((page << pg.page_log2) | (j & pmask)) * D + c];
+    }
+  } else {
+    const int8_t* src = k_idx + (b * L_max + (long long)m * bs) * D + c;
+    for (int t = 0; t < bs; ++t) r += src[(long long)t * D];
+  }
+  const int hi = (r + 64) >> 7;
+  int8_t* dst = limbs + (b * n_blocks + m) * 2 * D;
+  dst[c] = (int8_t)hi;
+  dst[D + c] = (int8_t)(r - (hi << 7));
+}
+
 // Block-key cache: blocks [m0, m0 + n_upd) of every sequence, each written as the
 // two int8 limbs of its representative (the sum of its bs keys), rows laid out as
-// blk_limbs_kernel writes them.  One workgroup per block: thread t reads 16-byte chunk
+// blk_limbs_kernel writes them.  Blocks of at least BLK_CACHE_WG_MIN keys take one
+// workgroup per block: thread t reads 16-byte chunk
 // t % CH of every (256 / CH)-th key row of the block (all its loads issued before the
 // first sum), keeps 16 column sums, and the sums of the threads sharing a chunk meet in
 // LDS.  With a page table (pg.page_table set) k_idx is a pool and key j of sequence b
 // is pool row page_table[b][j >> page_log2] << page_log2 | (j & mask) (page ids
 // clamped).  Grid: x = B * n_upd (workgroup x: sequence x / n_upd, block m0 + x % n_upd).
+constexpr int BLK_CACHE_WG_MIN = 32;
 template <int D>
 __global__ __launch_bounds__(256) void blk_cache_kernel(const int8_t* __restrict__ k_idx, int L_max, int bs,
                                                         int n_blocks, int m0, int n_upd,
@@ -1300,6 +1331,11 @@ hipError_t launch_block_cache(const int8_t* k_idx, int B, int L_max, int d_I, in
       (pg.page_log2 < 6 || pg.page_log2 > 30 || pg.n_pages < 1 || (long long)pg.max_pages << pg.page_log2 < L_max))
     return hipErrorInvalidValue;
   if (bs < 1 || bs > 128 || (d_I != 64 && d_I != 128)) return hipErrorInvalidValue;
+  if (bs < BLK_CACHE_WG_MIN) {
+    hipLaunchKernelGGL(blk_cache_cols_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, k_idx, L_max,
+                       d_I, bs, n_blocks, m0, n_upd, total, limbs, pg);
+    return hipGetLastError();
+  }
   if (total / d_I > 0x7fffffffLL) return hipErrorInvalidValue;
   if (d_I == 128)
     hipLaunchKernelGGL(blk_cache_kernel<128>, dim3((unsigned)(total / d_I)), dim3(256), 0, st, k_idx, L_max, bs,
