@@ -537,17 +537,22 @@ def test_forward_decode_fused_selection(lsa, H_I):
     err.check()
 
 
-def test_block_cache(lsa):
+@pytest.mark.parametrize("d_I", [128, 64])
+def test_block_cache(lsa, d_I):
     """The block-key cache: hi, lo int8 parts with 128 * hi + lo = the block's key sum
-    (lsa_block_reps) and lo in [-64, 63]; a cache built in two partial updates over a
-    stale buffer equals one built whole."""
-    wl = synthetic.Workload("bc", B=3, n_q=1, L=1000, q_pos0=999, H_I=4, d_I=128, k=16, H_q=8)
-    _, g = _inputs(wl, seed=23)
-    for bs in (4, 16, 128):
+    (lsa_block_reps, and the oracle's block_reps) and lo in [-64, 63]; a cache built in
+    two partial updates over a stale buffer equals one built whole.  Block sizes on both
+    sides of the per-block workgroup's threshold (32 keys), odd ones included."""
+    wl = synthetic.Workload("bc", B=3, n_q=1, L=1000, q_pos0=999, H_I=4, d_I=d_I, k=16, H_q=8)
+    inp, g = _inputs(wl, seed=23)
+    for bs in (1, 4, 16, 31, 32, 48, 100, 128):
         full = lsa.lsa_block_cache(g["k_idx"], bs)
         reps = lsa.lsa_block_reps(g["k_idx"], bs)
         hi, lo = full[:, :, 0].long(), full[:, :, 1].long()
         assert torch.equal(128 * hi + lo, reps.long()), f"bs={bs}"
+        for b in range(wl.B):
+            want = oracle.block_reps(inp["k_idx"][b].numpy(), bs)
+            assert np.array_equal((128 * hi + lo)[b].cpu().numpy(), want), f"bs={bs} b={b}"
         assert int(lo.min()) >= -64 and int(lo.max()) <= 63
         n = full.shape[1]
         part = torch.full_like(full, 77)
