@@ -735,33 +735,50 @@ __global__ void blk_limbs_kernel(const int32_t* __restrict__ reps, int D, long l
   limbs[rowi * 2 * D + D + c] = (int8_t)lo;
 }
 
-// Blocks of few keys (the pooled 4:1 cache): thread e sums byte column e % D of one
-// block, one byte load per key.
-__global__ void blk_cache_cols_kernel(const int8_t* __restrict__ k_idx, int L_max, int D, int bs, int n_blocks,
-                                      int m0, int n_upd, long long total, int8_t* __restrict__ limbs, Pages pg) {
-  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+// Blocks of few keys (the pooled 4:1 cache): thread e owns 16-byte chunk e % (D / 16)
+// of one block -- it reads that chunk of each of the block's key rows (16-byte loads,
+// four rows in flight at a time), keeps the 16 byte-column sums in registers and writes
+// the chunk of both limb rows with one 16-byte store each.  total = B * n_upd * D / 16.
+template <int D>
+__global__ __launch_bounds__(256) void blk_cache_chunks_kernel(const int8_t* __restrict__ k_idx, int L_max, int bs,
+                                                               int n_blocks, int m0, int n_upd, long long total,
+                                                               int8_t* __restrict__ limbs, Pages pg) {
+  constexpr int CH = D / 16;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
   if (e >= total) return;
-  const int c = (int)(e % D);
-  const long long bm = e / D;
+  const int c = (int)(e % CH);
+  const long long bm = e / CH;
   const int m = m0 + (int)(bm % n_upd);
   const long long b = bm / n_upd;
-  int r = 0;
-  if (pg.page_table != nullptr) {
-    const int32_t* pt = pg.page_table + b * pg.max_pages;
-    const int pmask = (1 << pg.page_log2) - 1;
-    for (int t = 0; t < bs; ++t) {
-      const int j = m * bs + t;
-      const long long page = min(max(pt[j >> pg.page_log2], 0), pg.n_pages - 1);
-      r += k_idx[((page << pg.page_log2) | (j & pmask)) * D + c];
-    }
-  } else {
-    const int8_t* src = k_idx + (b * L_max + (long long)m * bs) * D + c;
-    for (int t = 0; t < bs; ++t) r += src[(long long)t * D];
+  auto key_row = [&](int j) -> long long {
+    if (pg.page_table == nullptr) return b * L_max + j;
+    const long long page = min(max(pg.page_table[b * pg.max_pages + (j >> pg.page_log2)], 0), pg.n_pages - 1);
+    return (page << pg.page_log2) | (j & ((1 << pg.page_log2) - 1));
+  };
+  int sum[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sum[i] = 0;
+  for (int t0 = 0; t0 < bs; t0 += 4) {
+    v4i x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      x[u] = t0 + u < bs ? *(const v4i*)(k_idx + key_row(m * bs + t0 + u) * D + 16 * c) : v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum[i] += (int)(signed char)(x[u][i >> 2] >> (8 * (i & 3)));
   }
-  const int hi = (r + 64) >> 7;
-  int8_t* dst = limbs + (b * n_blocks + m) * 2 * D;
-  dst[c] = (int8_t)hi;
-  dst[D + c] = (int8_t)(r - (hi << 7));
+  v4i hw = v4i{0, 0, 0, 0}, lw = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int hi = (sum[i] + 64) >> 7;
+    const int lo = sum[i] - (hi << 7);
+    hw[i >> 2] |= (hi & 0xff) << (8 * (i & 3));
+    lw[i >> 2] |= (lo & 0xff) << (8 * (i & 3));
+  }
+  int8_t* dst = limbs + (b * n_blocks + m) * 2 * D + 16 * c;
+  *(v4i*)dst = hw;
+  *(v4i*)(dst + D) = lw;
 }
 
 // Block-key cache: blocks [m0, m0 + n_upd) of every sequence, each written as the
@@ -1332,8 +1349,15 @@ hipError_t launch_block_cache(const int8_t* k_idx, int B, int L_max, int d_I, in
     return hipErrorInvalidValue;
   if (bs < 1 || bs > 128 || (d_I != 64 && d_I != 128)) return hipErrorInvalidValue;
   if (bs < BLK_CACHE_WG_MIN) {
-    hipLaunchKernelGGL(blk_cache_cols_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, k_idx, L_max,
-                       d_I, bs, n_blocks, m0, n_upd, total, limbs, pg);
+    const long long chunks = total / 16;  // one thread per 16-byte chunk of a block
+    if ((chunks + 255) / 256 > 0x7fffffffLL) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((chunks + 255) / 256));
+    if (d_I == 128)
+      hipLaunchKernelGGL(blk_cache_chunks_kernel<128>, grid, dim3(256), 0, st, k_idx, L_max, bs, n_blocks, m0, n_upd,
+                         chunks, limbs, pg);
+    else
+      hipLaunchKernelGGL(blk_cache_chunks_kernel<64>, grid, dim3(256), 0, st, k_idx, L_max, bs, n_blocks, m0, n_upd,
+                         chunks, limbs, pg);
     return hipGetLastError();
   }
   if (total / d_I > 0x7fffffffLL) return hipErrorInvalidValue;
