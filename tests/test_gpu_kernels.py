@@ -261,9 +261,9 @@ def test_block_reps_and_prefilter(lsa, case):
 @pytest.mark.parametrize("T", [24576, 98304])
 @pytest.mark.parametrize("mode", ["random", "signed", "ties", "zeros", "bigw", "extreme"])
 def test_block_prefilter_long_rows(lsa, mode, T):
-    """Prefill-shaped rows over more than 4096 blocks (the keep that reads each row's
-    scores twice: a coarse histogram, then the cut's bin gathered into LDS; 6144 blocks
-    take its 256-thread form, 24576 its 1024-thread form).  Kept blocks equal the
+    """Prefill-shaped rows over more than 4096 blocks: 6144 blocks take the keep that
+    holds the row in registers (read once), 24576 the keep that reads each row's scores
+    twice (a coarse histogram, then the cut's bin gathered into LDS).  Kept blocks equal the
     oracle's for rows whose cut bin holds a few members (random), scores of both signs
     (signed weights), heavily tied scores (q, k in {-1, 0, 1}), and every score equal
     (rows whose tie outgrows the LDS member list then take the multi-pass fallback,
