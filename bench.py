@@ -453,8 +453,9 @@ def measure_peaks(lsa, torch):
         best = float("inf")
         for _ in range(5):
             if evict:
-                check(L.lsa_peak_read(C.c_void_p(flush.data_ptr()), flush.numel(), nb, C.c_void_p(sk.data_ptr()), st),
-                      "lsa_peak_read")
+                # a 1 GiB read with ordinary loads displaces the caches and leaves them clean
+                # (the streaming probe's non-temporal loads would leave them as they were)
+                flush.sum()
             else:
                 check(L.lsa_peak_gather(C.c_void_p(pool.data_ptr()), n_rows, C.c_void_p(idx.data_ptr()), n, nbg,
                                         C.c_void_p(sk.data_ptr()), st), "lsa_peak_gather")
@@ -481,8 +482,8 @@ def measure_peaks(lsa, torch):
     l2 = big[: 2 << 20]
     res["gather_l2_GBs"] = n_steady * 256 / (gather_ms(l2, l2.numel() // 256, False, n_steady) * 1e-3) / 1e9
     res["method"] = ("lsa_peak_* kernels (include/lsa_peaks.h): MFMA loops of 4 independent chains per wave over "
-                     f"{8 * n_cu} workgroups of 4 waves; 2 GiB streaming read; random 256-byte rows over {nbg} "
-                     f"workgroups: {n_idx} rows from a 2 GiB pool after a 1 GiB read (cold, the decode step's volume), "
+                     f"{8 * n_cu} workgroups of 4 waves; 2 GiB streaming read (one contiguous span per workgroup, non-temporal loads); random 256-byte rows over {nbg} "
+                     f"workgroups: {n_idx} rows from a 2 GiB pool after a 1 GiB read with ordinary loads (cold, the decode step's volume), "
                      f"{n_steady} rows from pools of {', '.join(str(m) for m in RESIDENT_POOLS_MIB)} MiB (the "
                      "prefill workloads' K+V sizes, Infinity Cache resident) and from a 2 MiB pool (L2 resident), "
                      "the warm pools read just before; best of 5")

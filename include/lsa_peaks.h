@@ -32,7 +32,8 @@ int32_t lsa_peak_sink_ints(int32_t n_blocks);
 int lsa_peak_mfma(int32_t kind, int64_t iters, int32_t n_blocks, int32_t* sink, void* stream);
 
 /* Streaming read of `bytes` (a multiple of 16, 16-byte aligned) of device memory,
-   each byte once, coalesced 16-byte loads. */
+   each byte once: workgroup x reads one contiguous span of about bytes / n_blocks
+   with coalesced 16-byte non-temporal loads, eight in flight per thread. */
 int lsa_peak_read(const void* src, int64_t bytes, int32_t n_blocks, int32_t* sink, void* stream);
 
 /* Random gather of 256-byte rows: rows[idx[e]] for e < n_idx (indices clamped into
