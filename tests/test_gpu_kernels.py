@@ -258,12 +258,13 @@ def test_block_reps_and_prefilter(lsa, case):
         assert np.array_equal(kept[i], padded), f"kept row {i}"
 
 
-@pytest.mark.parametrize("T", [24576, 98304])
+@pytest.mark.parametrize("T", [24576, 49152, 98304])
 @pytest.mark.parametrize("mode", ["random", "signed", "ties", "zeros", "bigw", "extreme"])
 def test_block_prefilter_long_rows(lsa, mode, T):
     """Prefill-shaped rows over more than 4096 blocks: 6144 blocks take the keep that
-    holds the row in registers (read once), 24576 the keep that reads each row's scores
-    twice (a coarse histogram, then the cut's bin gathered into LDS).  Kept blocks equal the
+    holds the row in registers (read once), 12288 and 24576 the keep that reads each
+    row's scores twice (a coarse histogram, then the cut's bin gathered into LDS; its
+    256- and 1024-thread forms).  Kept blocks equal the
     oracle's for rows whose cut bin holds a few members (random), scores of both signs
     (signed weights), heavily tied scores (q, k in {-1, 0, 1}), and every score equal
     (rows whose tie outgrows the LDS member list then take the multi-pass fallback,
